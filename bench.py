@@ -1,0 +1,231 @@
+"""Benchmark of the OSDN forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1.3b-apf]
+                    [--no-cpu-baseline] [--only forward|phases]
+
+A step is one osdn_forward call (preconditioner walk + chunkwise pass) over
+the whole workload, inputs already resident in HBM.  Several input copies
+rotate so the working set exceeds the 256 MB last-level cache.  Prints ONE
+JSON line (rank 0).  Besides the end-to-end figure it times the standalone
+phases (osdn_precond_scan, osdn_chunk_fwd) and the plain delta rule
+(OSDN_PRECOND_OFF), reports the dominant kernel against the HBM roofline,
+and times the fp64 CPU oracle on the host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "OSDN fwd tokens/s (scan+chunk WY), H=16 dk=dv=128 T=4096; % of roofline"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, GB/s
+CACHE_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="1.3b-apf")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "forward", "phases"], default="all")
+    return ap.parse_args()
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "delta_rule_recurrent_precond_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, path: str) -> int:
+    """Bytes a launch must move at minimum (inputs read once, outputs written once).
+
+    Per token-head: q, k, v reads (dk+dk+dv elements), beta (4 B), r (4 B with
+    APF), o write (dv elements); per head: S_final (dv*dk fp32) and d_final
+    (dk fp32).  The two-launch chunk pass also reads k~ (dk elements) and does
+    not handle r or d.
+    """
+    e = 2 if w.dtype == "bf16" else 4
+    th = w.B * w.H * w.T
+    heads = w.B * w.H
+    if path == "chunk":
+        per = (3 * w.dk + w.dv) * e + 4 + w.dv * e
+        return th * per + heads * w.dv * w.dk * 4
+    if path == "scan":
+        per = w.dk * e + 4 + (4 if w.apf else 0) + w.dk * e
+        return th * per + heads * w.dk * 4
+    per = (2 * w.dk + w.dv) * e + 4 + (4 if w.apf else 0) + w.dv * e
+    return th * per + heads * (w.dv * w.dk * 4 + w.dk * 4)
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
+    for the current kernel sources (profiles/traffic.json)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get("%s|%s" % (kernel, workload))
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("sources") != kernel_sources_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Average ms per call of fn(i) over `steps` calls, HIP events on the
+    current stream (the library launches on that stream)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, inp):
+    from oracle import oracle
+    heads = list(range(w.B * w.H))
+    threads = min(oracle.default_threads(), len(heads))
+    t0 = time.perf_counter()
+    oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, eta=inp.eta, heads=heads,
+                   want=("o", "S", "d"), threads=threads)
+    dt = time.perf_counter() - t0
+    tokens = len(heads) * w.T / w.H
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "whole workload: %d (b,h) sequences x T=%d, fp64 token-serial, %.2f s wall"
+                      % (len(heads), w.T, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (b,h) sequence is independent; see the sharding notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import delta_rule_recurrent_precond_amd as osdn
+    from delta_rule_recurrent_precond_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm device"
+    osdn.load()
+    w = W.CONFIGS[args.workload]
+    code = 0 if w.dtype == "bf16" else 1
+    print("[bench] generating %s" % w.name, file=sys.stderr, flush=True)
+    host = W.generate(w)
+    per_copy = sum(t.numel() * t.element_size() for t in (host.q, host.k, host.v, host.beta)
+                   if t is not None)
+    copies = max(2, -(-2 * CACHE_BYTES // per_copy))
+    devs = [host.to("cuda") for _ in range(copies)]
+    B, H, T, dk, dv, C = w.B, w.H, w.T, w.dk, w.dv, w.chunk
+    path = osdn.forward_path(B, H, T, dk, dv, C, code)
+    outs = [{
+        "o": torch.empty_like(d.v),
+        "S_final": torch.empty((B, H, dv, dk), dtype=torch.float32, device="cuda"),
+        "d_final": torch.empty((B, H, dk), dtype=torch.float32, device="cuda"),
+        "log_ratio_sum": torch.empty((B, H), dtype=torch.float32, device="cuda"),
+    } for d in devs]
+    ws_n = osdn.forward_workspace_bytes(B, H, T, dk, dv, C, code)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda") if ws_n else None
+
+    def fwd(i, precond=True):
+        d = devs[i % copies]
+        o = outs[i % copies]
+        osdn.forward(d.q, d.k, d.v, d.beta, d.r, eta=d.eta, chunk=C, precond=precond,
+                     out=o if precond else {**o, "d_final": None}, workspace=ws)
+
+    print("[bench] path=%s copies=%d" % (path, copies), file=sys.stderr, flush=True)
+    ms = time_launches(fwd, args.steps, args.warmup, torch)
+    tokens = B * T
+    result = {
+        "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if (path == "fused" and w.dtype == "bf16") else "f32",
+        "data": "synthetic (seeded generator; shapes and distributions of the workload)",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C,
+                   "eta": w.eta, "apf": w.apf, "storage": w.dtype, "path": path},
+    }
+    print("[bench] forward %.4f ms/step" % ms, file=sys.stderr, flush=True)
+
+    phases = {}
+    if args.only in ("all", "phases"):
+        ms_dn = time_launches(lambda i: fwd(i, precond=False), args.steps, args.warmup, torch)
+        kts = [torch.empty_like(d.k) for d in devs]
+        dfin = torch.empty((B, H, dk), dtype=torch.float32, device="cuda")
+        lib = osdn.load()
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def scan(i):
+            d = devs[i % copies]
+            st = lib.osdn_precond_scan(d.k.data_ptr(), d.beta.data_ptr(),
+                                       None if d.r is None else d.r.data_ptr(), None,
+                                       float(d.eta), B, H, T, dk, code, kts[i % copies].data_ptr(),
+                                       dfin.data_ptr(), None, None, stream)
+            assert st == 0, st
+
+        def chunk(i):
+            d = devs[i % copies]
+            o = outs[i % copies]
+            st = lib.osdn_chunk_fwd(d.q.data_ptr(), d.k.data_ptr(), kts[i % copies].data_ptr(),
+                                    d.v.data_ptr(), d.beta.data_ptr(), None, B, H, T, dk, dv, C,
+                                    code, o["o"].data_ptr(), o["S_final"].data_ptr(), stream)
+            assert st == 0, st
+
+        ms_scan = time_launches(scan, args.steps, args.warmup, torch)
+        ms_chunk = time_launches(chunk, args.steps, args.warmup, torch)
+        phases = {
+            "precond_scan": {"ms": ms_scan, "tokens_per_s": tokens / (ms_scan * 1e-3),
+                             "hbm_frac": algorithmic_bytes(w, "scan") / (ms_scan * 1e-3)
+                             / (HBM_PEAK_GBS * 1e9)},
+            "chunk_fwd": {"ms": ms_chunk, "tokens_per_s": tokens / (ms_chunk * 1e-3),
+                          "hbm_frac": algorithmic_bytes(w, "chunk") / (ms_chunk * 1e-3)
+                          / (HBM_PEAK_GBS * 1e9)},
+            "deltanet_mode": {"ms": ms_dn, "tokens_per_s": tokens / (ms_dn * 1e-3)},
+            "precond_overhead": (ms - ms_dn) / ms,
+            "two_launch_scan_share": ms_scan / (ms_scan + ms_chunk),
+        }
+        result["phases"] = phases
+        print("[bench] scan %.4f ms, chunk %.4f ms, deltanet %.4f ms" % (ms_scan, ms_chunk, ms_dn),
+              file=sys.stderr, flush=True)
+
+    # Dominant kernel against the HBM roofline.  The fused path is one kernel per
+    # osdn_forward; the two-launch path is dominated by the chunkwise pass.
+    if path == "fused":
+        kname, kms, kbytes = "osdn_fused_forward", ms, algorithmic_bytes(w, "fused")
+    else:
+        kname = "chunk_generic"
+        kms = phases["chunk_fwd"]["ms"] if phases else ms
+        kbytes = algorithmic_bytes(w, "chunk")
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    result["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                          "traffic": stored_traffic(kname, args.workload),
+                          "kernel": kname, "algorithmic_bytes": kbytes, "kernel_ms": kms}
+
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, host)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

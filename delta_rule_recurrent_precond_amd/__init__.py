@@ -1,0 +1,163 @@
+"""OSDN (Online Scaled DeltaNet) forward hot path for AMD MI355X (gfx950).
+
+Python face of libosdn.so.  The functions mirror the C ABI of include/osdn.h:
+
+  precond_scan(k, beta, r, d0, eta)            phase 1: the preconditioner walk
+  chunk_fwd(q, k, k_tilde, v, beta, S0, chunk)  phase 2: chunkwise pass with k~
+  forward(q, k, v, beta, r, d0, S0, eta, chunk) both phases
+
+Tensors are torch tensors on a ROCm device, contiguous, in the [B,H,T,D]
+layout; q/k/v/k~/o are bfloat16 or float32, gates and states float32.  Outputs
+are allocated with torch on the inputs' device and the work is enqueued on the
+current stream.  Source of the method: gist.science technical summary of
+"OSDN: Improving Delta Rule with Provable Online Preconditioning in Linear
+Attention" (arXiv 2605.13473).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import OsdnError, load  # noqa: F401
+
+__all__ = ["precond_scan", "chunk_fwd", "forward", "forward_workspace_bytes", "forward_path",
+           "OsdnError", "load"]
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.OSDN_BF16
+    if t.dtype == torch.float32:
+        return _lib.OSDN_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, shape=None, dtype=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a ROCm device (got %s); there is no CPU path" %
+                         (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def precond_scan(k, beta, r=None, d0=None, eta=0.05, *, want_d_all=False, want_log_ratio=False):
+    """Phase 1.  Returns dict(k_tilde, d_final[, d_all][, log_ratio])."""
+    _dev(k, "k")
+    B, H, T, dk = k.shape
+    dev = k.device
+    _dev(beta, "beta", (B, H, T), torch.float32, dev)
+    _dev(r, "r", (B, H, T), torch.float32, dev)
+    _dev(d0, "d0", (B, H, dk), torch.float32, dev)
+    out = {
+        "k_tilde": torch.empty_like(k),
+        "d_final": torch.empty((B, H, dk), dtype=torch.float32, device=dev),
+    }
+    if want_d_all:
+        out["d_all"] = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev)
+    if want_log_ratio:
+        out["log_ratio"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    st = _lib.load().osdn_precond_scan(
+        _ptr(k), _ptr(beta), _ptr(r), _ptr(d0), float(eta), B, H, T, dk, _dtype_code(k),
+        _ptr(out["k_tilde"]), _ptr(out["d_final"]), _ptr(out.get("d_all")),
+        _ptr(out.get("log_ratio")), _stream(dev))
+    _lib.check("osdn_precond_scan", st)
+    return out
+
+
+def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64):
+    """Phase 2 with a given write key k~.  Returns (o, S_final)."""
+    _dev(q, "q")
+    B, H, T, dk = q.shape
+    dev = q.device
+    _dev(k, "k", q.shape, q.dtype, dev)
+    _dev(k_tilde, "k_tilde", q.shape, q.dtype, dev)
+    _dev(v, "v", None, q.dtype, dev)
+    if v.shape[:3] != (B, H, T):
+        raise ValueError("v has shape %s, expected [%d,%d,%d,dv]" % (tuple(v.shape), B, H, T))
+    dv = v.shape[3]
+    _dev(beta, "beta", (B, H, T), torch.float32, dev)
+    _dev(S0, "S0", (B, H, dv, dk), torch.float32, dev)
+    o = torch.empty_like(v)
+    S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    st = _lib.load().osdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(k_tilde), _ptr(v), _ptr(beta),
+                                    _ptr(S0), B, H, T, dk, dv, int(chunk), _dtype_code(q),
+                                    _ptr(o), _ptr(S_final), _stream(dev))
+    _lib.check("osdn_chunk_fwd", st)
+    return o, S_final
+
+
+def forward_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code, precond=True) -> int:
+    flags = 0 if precond else _lib.OSDN_PRECOND_OFF
+    n = _lib.load().osdn_forward_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code, flags)
+    if n == (1 << 64) - 1:
+        raise ValueError("invalid arguments for osdn_forward")
+    return int(n)
+
+
+def forward_path(B, H, T, dk, dv, chunk, dtype_code, precond=True) -> str:
+    flags = 0 if precond else _lib.OSDN_PRECOND_OFF
+    return _lib.load().osdn_forward_path(B, H, T, dk, dv, chunk, dtype_code, flags).decode()
+
+
+def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond=True,
+            *, out=None, workspace=None):
+    """Both phases.  Returns dict(o, S_final, d_final, log_ratio_sum).
+
+    ``out`` may pass preallocated outputs (same keys) to keep the call free of
+    allocations; ``workspace`` a uint8 device tensor of at least
+    forward_workspace_bytes(...) bytes.
+    """
+    _dev(q, "q")
+    B, H, T, dk = q.shape
+    dev = q.device
+    _dev(k, "k", q.shape, q.dtype, dev)
+    _dev(v, "v", None, q.dtype, dev)
+    if v.shape[:3] != (B, H, T):
+        raise ValueError("v has shape %s, expected [%d,%d,%d,dv]" % (tuple(v.shape), B, H, T))
+    dv = v.shape[3]
+    _dev(beta, "beta", (B, H, T), torch.float32, dev)
+    _dev(r, "r", (B, H, T), torch.float32, dev)
+    _dev(d0, "d0", (B, H, dk), torch.float32, dev)
+    _dev(S0, "S0", (B, H, dv, dk), torch.float32, dev)
+    code = _dtype_code(q)
+    flags = 0 if precond else _lib.OSDN_PRECOND_OFF
+    if out is None:
+        out = {
+            "o": torch.empty_like(v),
+            "S_final": torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev),
+            "d_final": (torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+                        if precond else None),
+            "log_ratio_sum": torch.empty((B, H), dtype=torch.float32, device=dev),
+        }
+    need = forward_workspace_bytes(B, H, T, dk, dv, chunk, code, precond)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.load().osdn_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(d0), _ptr(S0), float(eta),
+        B, H, T, dk, dv, int(chunk), code, flags, _ptr(out["o"]), _ptr(out.get("S_final")),
+        _ptr(out.get("d_final")), _ptr(out.get("log_ratio_sum")), _ptr(workspace), ws_bytes,
+        _stream(dev))
+    _lib.check("osdn_forward", st)
+    return out

@@ -1,0 +1,196 @@
+// Phase 2 of OSDN, any supported shape and dtype: the chunkwise delta-rule
+// pass with the preconditioned write key, in fp32 vector arithmetic.
+//
+// Source: gist.science technical summary of "OSDN: Improving Delta Rule with
+// Provable Online Preconditioning in Linear Attention", §2.1: replacing the
+// write key k by kt = d (.) k keeps DeltaNet's chunkwise pipeline, with kt in
+// the chunk gram and the intra-chunk scores.  For a chunk with entry state S
+// (rows t = 0..L-1):
+//   A  = strict_lower(diag(beta) K Kt^T)          mixed gram (read key K, write key Kt)
+//   (I + A) X = diag(beta) (V - K S^T)            pseudo-values x_t = beta_t (v_t - S_{t-1} k_t)
+//   O  = Q S^T + lower(Q Kt^T) X                  o_t = S_t q_t (scores include t = s)
+//   S <- S + X^T Kt
+// This is the correctness path (used for fp32 data and for shapes the
+// matrix-core kernel does not cover).  One workgroup per (b, h, dv tile),
+// serial over chunks, everything of a chunk staged in LDS as fp32.
+#include "device.h"
+#include "launch.h"
+
+namespace osdn {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T, int DK, int DVT, int C>
+__global__ void __launch_bounds__(kThreads)
+chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ kt,
+              const T *__restrict__ v, const float *__restrict__ beta,
+              const float *__restrict__ S0, int T_, int dv, T *__restrict__ o,
+              float *__restrict__ S_final) {
+  constexpr int DKP = DK + 1;          // padded rows (bank spread)
+  constexpr int CP = C + 1;
+  constexpr int XP = DVT + 1;
+  constexpr int PARTS = kThreads / DVT;  // lanes cooperating on one column of X
+  static_assert(PARTS <= 64 && (PARTS & (PARTS - 1)) == 0, "group must fit a wave");
+
+  __shared__ float sK[C * DKP];   // K, then Q
+  __shared__ float sKt[C * DKP];
+  __shared__ float sS[DVT * DKP];
+  __shared__ float sA[C * CP];    // A, then the scores P
+  __shared__ float sX[C * XP];    // V - K S^T scaled (R), then X
+  __shared__ float sV[C * DVT];
+  __shared__ float sB[C];
+
+  const int tid = threadIdx.x;
+  const long bh = blockIdx.x;
+  const int j0 = blockIdx.y * DVT;  // first value channel of this tile
+
+  const long tok0 = bh * (long)T_;
+  for (int idx = tid; idx < DVT * DK; idx += kThreads) {
+    const int j = idx / DK, i = idx % DK;
+    sS[j * DKP + i] = S0 ? S0[(bh * dv + j0 + j) * DK + i] : 0.0f;
+  }
+
+  for (int c0 = 0; c0 < T_; c0 += C) {
+    const int L = min(C, T_ - c0);
+    // 1. stage the chunk
+    for (int idx = tid; idx < C * DK; idx += kThreads) {
+      const int t = idx / DK, i = idx % DK;
+      const bool ok = t < L;
+      const long g = (tok0 + c0 + t) * DK + i;
+      sK[t * DKP + i] = ok ? Elem<T>::load(k + g) : 0.0f;
+      sKt[t * DKP + i] = ok ? Elem<T>::load(kt + g) : 0.0f;
+    }
+    for (int idx = tid; idx < C * DVT; idx += kThreads) {
+      const int t = idx / DVT, j = idx % DVT;
+      sV[idx] = t < L ? Elem<T>::load(v + (tok0 + c0 + t) * (long)dv + j0 + j) : 0.0f;
+    }
+    for (int t = tid; t < C; t += kThreads) sB[t] = t < L ? beta[tok0 + c0 + t] : 0.0f;
+    __syncthreads();
+
+    // 2. mixed gram A and right-hand side R = diag(beta)(V - K S^T)
+    for (int idx = tid; idx < C * C; idx += kThreads) {
+      const int t = idx / C, s = idx % C;
+      float acc = 0.0f;
+      if (s < t) {
+        for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sKt[s * DKP + i];
+        acc *= sB[t];
+      }
+      sA[t * CP + s] = acc;
+    }
+    for (int idx = tid; idx < C * DVT; idx += kThreads) {
+      const int t = idx / DVT, j = idx % DVT;
+      float acc = 0.0f;
+      for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sS[j * DKP + i];
+      sX[t * XP + j] = sB[t] * (sV[idx] - acc);
+    }
+    __syncthreads();
+
+    // Q replaces K (K is no longer read in this chunk)
+    for (int idx = tid; idx < C * DK; idx += kThreads) {
+      const int t = idx / DK, i = idx % DK;
+      sK[t * DKP + i] = t < L ? Elem<T>::load(q + (tok0 + c0 + t) * DK + i) : 0.0f;
+    }
+
+    // 3. forward substitution (I + A) X = R, one column per group of PARTS lanes.
+    //    Lane `part` owns rows s = part (mod PARTS); it alone writes and later
+    //    reads those rows of X, so no cross-lane LDS ordering is needed.
+    {
+      const int j = tid / PARTS, part = tid % PARTS;
+      for (int t = 0; t < L; ++t) {
+        const float rhs = sX[t * XP + j];
+        float acc = 0.0f;
+        for (int s = part; s < t; s += PARTS) acc += sA[t * CP + s] * sX[s * XP + j];
+        acc = group_sum<PARTS>(acc);
+        if (part == (t % PARTS)) sX[t * XP + j] = rhs - acc;
+      }
+    }
+    __syncthreads();
+
+    // 4. intra-chunk scores P = lower(Q Kt^T) (diagonal included) into sA
+    for (int idx = tid; idx < C * C; idx += kThreads) {
+      const int t = idx / C, s = idx % C;
+      float acc = 0.0f;
+      if (s <= t)
+        for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sKt[s * DKP + i];
+      sA[t * CP + s] = acc;
+    }
+    __syncthreads();
+
+    // 5. output O = Q S^T + P X
+    for (int idx = tid; idx < C * DVT; idx += kThreads) {
+      const int t = idx / DVT, j = idx % DVT;
+      if (t < L) {
+        float acc = 0.0f;
+        for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sS[j * DKP + i];
+        for (int s = 0; s <= t; ++s) acc += sA[t * CP + s] * sX[s * XP + j];
+        Elem<T>::store(o + (tok0 + c0 + t) * (long)dv + j0 + j, acc);
+      }
+    }
+    __syncthreads();
+
+    // 6. state update S += X^T Kt
+    for (int idx = tid; idx < DVT * DK; idx += kThreads) {
+      const int j = idx / DK, i = idx % DK;
+      float acc = sS[j * DKP + i];
+      for (int s = 0; s < L; ++s) acc += sX[s * XP + j] * sKt[s * DKP + i];
+      sS[j * DKP + i] = acc;
+    }
+    __syncthreads();
+  }
+
+  if (S_final) {
+    for (int idx = tid; idx < DVT * DK; idx += kThreads) {
+      const int j = idx / DK, i = idx % DK;
+      S_final[(bh * dv + j0 + j) * DK + i] = sS[j * DKP + i];
+    }
+  }
+}
+
+template <typename T, int DK, int DVT>
+hipError_t launch_c(const ChunkArgs &a, hipStream_t s, dim3 grid) {
+  const dim3 block(kThreads);
+#define OSDN_GEN_CASE(C_)                                                                      \
+  case C_:                                                                                     \
+    hipLaunchKernelGGL((chunk_generic<T, DK, DVT, C_>), grid, block, 0, s, (const T *)a.q,   \
+                       (const T *)a.k, (const T *)a.k_tilde, (const T *)a.v, a.beta, a.S0,   \
+                       a.T, a.dv, (T *)a.o, a.S_final);                                       \
+    break;
+  switch (a.chunk) {
+    OSDN_GEN_CASE(16)
+    OSDN_GEN_CASE(32)
+    OSDN_GEN_CASE(64)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef OSDN_GEN_CASE
+  return hipGetLastError();
+}
+
+template <typename T, int DVT>
+hipError_t launch_dk(const ChunkArgs &a, hipStream_t s, dim3 grid) {
+  switch (a.dk) {
+    case 16: return launch_c<T, 16, DVT>(a, s, grid);
+    case 32: return launch_c<T, 32, DVT>(a, s, grid);
+    case 64: return launch_c<T, 64, DVT>(a, s, grid);
+    case 128: return launch_c<T, 128, DVT>(a, s, grid);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const ChunkArgs &a, hipStream_t s) {
+  const int dvt = a.dv >= 32 ? 32 : 16;
+  const dim3 grid((unsigned)(a.B * a.H), (unsigned)(a.dv / dvt));
+  return dvt == 32 ? launch_dk<T, 32>(a, s, grid) : launch_dk<T, 16>(a, s, grid);
+}
+
+}  // namespace
+
+hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t s) {
+  if ((long)a.B * a.H == 0) return hipSuccess;
+  return a.dtype == 0 ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
+}
+
+}  // namespace osdn

@@ -1,0 +1,55 @@
+// Device helpers shared by the OSDN kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace osdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Element access for the two storage types of q, k, v, k~, o.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float *p) { return *p; }
+  static __device__ __forceinline__ void store(float *p, float x) { *p = x; }
+};
+template <> struct Elem<bf16> {
+  static __device__ __forceinline__ float load(const bf16 *p) { return (float)(*p); }
+  // round to nearest even (the hardware conversion on gfx950)
+  static __device__ __forceinline__ void store(bf16 *p, float x) { *p = (bf16)x; }
+};
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+// Quad butterflies and row mirrors via DPP, then the four 16-lane rows are
+// combined through lane reads (gfx9 DPP cannot cross rows symmetrically).
+__device__ __forceinline__ float wave_sum(float v) {
+  // DPP controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+  // row_half_mirror = 0x141, row_mirror = 0x140.
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  const int iv = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Sum over aligned groups of G lanes (G = 2..64, power of two) with xor
+// shuffles; every lane of the group receives the group's total.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+}  // namespace osdn

@@ -1,0 +1,48 @@
+// Internal launchers behind the C ABI (not exported).  Arguments are
+// validated by the caller (osdn_api.hip) before any of these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace osdn {
+
+struct ScanArgs {
+  const void *k;
+  const float *beta, *r, *d0;
+  float eta;
+  int B, H, T, dk, dtype;
+  int mode_off;          // 1: plain delta rule (only the residual-ratio sums are produced)
+  void *k_tilde;         // [B,H,T,dk] dtype (unused when mode_off)
+  float *d_final, *d_all, *log_ratio, *log_ratio_sum;  // optional
+};
+
+struct ChunkArgs {
+  const void *q, *k, *k_tilde, *v;
+  const float *beta, *S0;
+  int B, H, T, dk, dv, chunk, dtype;
+  void *o;
+  float *S_final;
+};
+
+struct FusedArgs {
+  const void *q, *k, *v;
+  const float *beta, *r, *d0, *S0;
+  float eta;
+  int B, H, T, dk, dv, chunk, dtype;
+  int precond_off;
+  void *o;
+  float *S_final, *d_final, *log_ratio_sum;
+};
+
+// Token-serial preconditioner walk, one wave per (b,h).
+hipError_t launch_precond_scan_serial(const ScanArgs &a, hipStream_t s);
+
+// Chunkwise state pass with fp32 vector arithmetic; any supported shape/dtype.
+hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t s);
+
+// Fused single-kernel forward on matrix cores (bf16, dk = dv = 128, chunk = 64).
+bool fused_supported(int dk, int dv, int chunk, int dtype);
+hipError_t launch_fused_forward(const FusedArgs &a, hipStream_t s);
+
+}  // namespace osdn

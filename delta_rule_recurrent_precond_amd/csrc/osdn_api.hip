@@ -1,0 +1,136 @@
+// C ABI of libosdn.so: argument checks, path selection and launches.
+// Declarations and the meaning of every argument: include/osdn.h.
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/osdn.h"
+#include "launch.h"
+
+#define OSDN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+size_t elem_bytes(int dtype) { return dtype == OSDN_BF16 ? 2 : 4; }
+
+// Sizes common to every entry point.
+int check_sizes(int B, int H, int T, int dk, int dv, int chunk, int dtype, bool need_dv,
+                bool need_chunk) {
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_SHAPE;
+  if (dtype != OSDN_BF16 && dtype != OSDN_F32) return OSDN_ERR_UNSUPPORTED;
+  if (!dim_ok(dk)) return OSDN_ERR_UNSUPPORTED;
+  if (need_dv && !dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
+  if (need_chunk && !chunk_ok(chunk)) return OSDN_ERR_UNSUPPORTED;
+  const long long heads = (long long)B * H;
+  if (heads > INT_MAX / 8) return OSDN_ERR_SHAPE;  // grid size; also bounds the products below
+  const long long per_head = (long long)T * 128;
+  if (heads > 0 && per_head > (LLONG_MAX / 8) / heads) return OSDN_ERR_SHAPE;
+  return OSDN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? OSDN_OK : OSDN_ERR_HIP; }
+
+bool use_fused(int dk, int dv, int chunk, int dtype) {
+  return osdn::fused_supported(dk, dv, chunk, dtype);
+}
+
+size_t ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype, unsigned flags) {
+  if ((flags & OSDN_PRECOND_OFF) || use_fused(dk, dv, chunk, dtype)) return 0;
+  const size_t n = (size_t)B * H * T * dk * elem_bytes(dtype);
+  return (n + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+OSDN_EXPORT const char *osdn_status_str(int status) {
+  switch (status) {
+    case OSDN_OK: return "ok";
+    case OSDN_ERR_NULL: return "a required pointer is NULL";
+    case OSDN_ERR_SHAPE: return "a size is negative or the sizes overflow";
+    case OSDN_ERR_UNSUPPORTED: return "dtype, dk, dv or chunk outside the supported set";
+    case OSDN_ERR_WORKSPACE: return "workspace is NULL or smaller than required";
+    case OSDN_ERR_HIP: return "the HIP runtime rejected a launch";
+    default: return "unknown status";
+  }
+}
+
+OSDN_EXPORT int osdn_precond_scan(const void *k, const float *beta, const float *r,
+                                  const float *d0, float eta, int B, int H, int T, int dk,
+                                  int dtype, void *k_tilde, float *d_final, float *d_all,
+                                  float *log_ratio, void *stream) {
+  int st = check_sizes(B, H, T, dk, 16, 16, dtype, false, false);
+  if (st != OSDN_OK) return st;
+  if ((long long)B * H == 0) return OSDN_OK;
+  if (T > 0 && (!k || !beta || !k_tilde)) return OSDN_ERR_NULL;
+  osdn::ScanArgs a{k, beta, r, d0, eta, B, H, T, dk, dtype, 0, k_tilde,
+                   d_final, d_all, log_ratio, nullptr};
+  return hip_status(osdn::launch_precond_scan_serial(a, (hipStream_t)stream));
+}
+
+OSDN_EXPORT int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde, const void *v,
+                               const float *beta, const float *S0, int B, int H, int T, int dk,
+                               int dv, int chunk, int dtype, void *o, float *S_final,
+                               void *stream) {
+  int st = check_sizes(B, H, T, dk, dv, chunk, dtype, true, true);
+  if (st != OSDN_OK) return st;
+  if ((long long)B * H == 0) return OSDN_OK;
+  if (T > 0 && (!q || !k || !k_tilde || !v || !beta || !o)) return OSDN_ERR_NULL;
+  osdn::ChunkArgs a{q, k, k_tilde, v, beta, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
+  return hip_status(osdn::launch_chunk_generic(a, (hipStream_t)stream));
+}
+
+OSDN_EXPORT size_t osdn_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
+                                                int dtype, unsigned flags) {
+  if (check_sizes(B, H, T, dk, dv, chunk, dtype, true, true) != OSDN_OK) return (size_t)-1;
+  if (flags & ~OSDN_PRECOND_OFF) return (size_t)-1;
+  return ws_bytes(B, H, T, dk, dv, chunk, dtype, flags);
+}
+
+OSDN_EXPORT const char *osdn_forward_path(int B, int H, int T, int dk, int dv, int chunk,
+                                          int dtype, unsigned flags) {
+  if (check_sizes(B, H, T, dk, dv, chunk, dtype, true, true) != OSDN_OK) return "invalid";
+  if (flags & ~OSDN_PRECOND_OFF) return "invalid";
+  if ((long long)B * H == 0) return "none";
+  return use_fused(dk, dv, chunk, dtype) ? "fused" : "two-phase";
+}
+
+OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
+                             const float *r, const float *d0, const float *S0, float eta, int B,
+                             int H, int T, int dk, int dv, int chunk, int dtype, unsigned flags,
+                             void *o, float *S_final, float *d_final, float *log_ratio_sum,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_sizes(B, H, T, dk, dv, chunk, dtype, true, true);
+  if (st != OSDN_OK) return st;
+  if (flags & ~OSDN_PRECOND_OFF) return OSDN_ERR_UNSUPPORTED;
+  if ((long long)B * H == 0) return OSDN_OK;
+  if (T > 0 && (!q || !k || !v || !beta || !o)) return OSDN_ERR_NULL;
+  const bool off = (flags & OSDN_PRECOND_OFF) != 0;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (use_fused(dk, dv, chunk, dtype)) {
+    osdn::FusedArgs a{q, k, v, beta, r, d0, S0, eta, B, H, T, dk, dv, chunk, dtype,
+                      off ? 1 : 0, o, S_final, d_final, log_ratio_sum};
+    return hip_status(osdn::launch_fused_forward(a, s));
+  }
+
+  // Two launches: the preconditioner walk writes kt into the workspace, then
+  // the chunkwise pass reads it.
+  const size_t need = ws_bytes(B, H, T, dk, dv, chunk, dtype, flags);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return OSDN_ERR_WORKSPACE;
+  const void *kt = k;
+  if (!off) {
+    osdn::ScanArgs sa{k, beta, r, d0, eta, B, H, T, dk, dtype, 0, workspace,
+                      d_final, nullptr, nullptr, log_ratio_sum};
+    st = hip_status(osdn::launch_precond_scan_serial(sa, s));
+    if (st != OSDN_OK) return st;
+    kt = workspace;
+  } else if (log_ratio_sum) {
+    osdn::ScanArgs sa{k, beta, nullptr, nullptr, 0.0f, B, H, T, dk, dtype, 1, nullptr,
+                      nullptr, nullptr, nullptr, log_ratio_sum};
+    st = hip_status(osdn::launch_precond_scan_serial(sa, s));
+    if (st != OSDN_OK) return st;
+  }
+  osdn::ChunkArgs ca{q, k, kt, v, beta, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
+  return hip_status(osdn::launch_chunk_generic(ca, s));
+}

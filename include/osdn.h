@@ -1,0 +1,144 @@
+/*
+ * osdn.h -- C ABI of the OSDN forward library (libosdn.so, AMD gfx950).
+ *
+ * Online Scaled DeltaNet (OSDN) is the delta rule with a diagonal
+ * preconditioner d_t on the write side, learned online by descent on a
+ * closed-form hypergradient surrogate.  Source of every definition below: the
+ * gist.science technical summary of "OSDN: Improving Delta Rule with Provable
+ * Online Preconditioning in Linear Attention" (arXiv 2605.13473), cited as
+ * [summary §N].
+ *
+ * Per (batch b, head h), tokens t = 0..T-1, keys/queries in R^dk, values in
+ * R^dv, state S in R^{dv x dk}, preconditioner d in R^dk:
+ *   kt_t    = d_t (.) k_t                                   [summary §2.1]
+ *   S_t     = S_{t-1} + beta_t (v_t - S_{t-1} k_t) kt_t^T    [summary §2.1]
+ *   o_t     = S_t q_t           (readout after the write; the pages give none)
+ *   a_t     = <d_t, k_t (.) k_t>,  rho_t = (1 - beta_t a_t)^2  [summary §2.2, §3]
+ *   d_{t+1} = r_t d_t + eta beta_t (1 - beta_t a_t) (k_t (.) k_t) / ||k_t||^2
+ *             (descent on the surrogate of [summary §2.2]; r_t = 1 without the
+ *              APF retention gate of [summary §2.3]; the step is 0 when k_t = 0)
+ * Phase 1 (osdn_precond_scan) is the O(dk) walk over the key stream that
+ * produces kt; phase 2 (osdn_chunk_fwd) is the chunkwise delta-rule pass with
+ * kt in place of k in the chunk gram, the intra-chunk scores and the state
+ * update [summary §2.2, two-phase implementation].  osdn_forward does both.
+ *
+ * Conventions shared by every entry point
+ *  - Layout: every tensor is dense, row-major, contiguous:
+ *      q, k, kt  [B][H][T][dk]     v, o [B][H][T][dv]
+ *      beta, r   [B][H][T]  fp32   d0, d_final [B][H][dk] fp32
+ *      S0, S_final [B][H][dv][dk] fp32 (row j of S is value channel j)
+ *  - dtype (q, k, v, kt, o): OSDN_BF16 (bfloat16) or OSDN_F32.  beta, r, d and
+ *    S are always fp32; arithmetic is fp32 on the device.
+ *  - Pointers are device pointers (any memory the GPU can address) except where
+ *    stated.  The caller owns every buffer; the library never allocates, frees
+ *    or synchronises on these calls.  Outputs must not overlap inputs.
+ *  - stream is a hipStream_t (NULL = the default stream).  Work is enqueued on
+ *    it and the call returns; device faults surface at the caller's next sync.
+ *  - Sizes: B, H, T >= 0 (any zero makes the call a no-op apart from copying
+ *    the initial state to the final-state outputs when T = 0); dk, dv in
+ *    {16, 32, 64, 128}; chunk in {16, 32, 64}.  T need not be a multiple of
+ *    chunk (the last chunk is short).
+ *  - Errors: every argument is checked before anything is enqueued; on error
+ *    nothing is enqueued and a negative OSDN_ERR_* code is returned.
+ *  - Results are deterministic run to run (no floating-point atomics).
+ *  - Non-finite inputs propagate; they are not checked.
+ */
+#ifndef OSDN_H
+#define OSDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSDN_OK 0
+#define OSDN_ERR_NULL (-1)        /* a required pointer is NULL */
+#define OSDN_ERR_SHAPE (-2)       /* a size is negative or the sizes overflow */
+#define OSDN_ERR_UNSUPPORTED (-3) /* dtype, dk, dv or chunk outside the supported set */
+#define OSDN_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than required */
+#define OSDN_ERR_HIP (-5)         /* the HIP runtime rejected a launch */
+
+#define OSDN_BF16 0
+#define OSDN_F32 1
+
+/* osdn_forward flag: run the plain delta rule (kt = k, [summary §1]); d0, r and
+ * eta are ignored, d_final is not written, rho_t = (1 - beta_t ||k_t||^2)^2. */
+#define OSDN_PRECOND_OFF 1u
+
+/*
+ * Phase 1: the preconditioner scan over the key stream [summary §2.2 phase 1,
+ * §2.3 APF].
+ *   k         [B,H,T,dk] dtype   keys (required if T > 0)
+ *   beta      [B,H,T]    fp32    write gates (required if T > 0)
+ *   r         [B,H,T]    fp32    APF retention gates; NULL means r = 1
+ *   d0        [B,H,dk]   fp32    initial preconditioner; NULL means all ones
+ *   eta                          meta step size
+ *   k_tilde   [B,H,T,dk] dtype   out: kt_t = d_t (.) k_t, rounded to dtype
+ *                                (required if T > 0)
+ *   d_final   [B,H,dk]   fp32    out: d_T (optional, NULL to skip)
+ *   d_all     [B,H,T,dk] fp32    out: d_t, the value used at token t (optional)
+ *   log_ratio [B,H,T]    fp32    out: log rho_t (optional; -inf where rho_t = 0)
+ */
+int osdn_precond_scan(const void *k, const float *beta, const float *r, const float *d0,
+                      float eta, int B, int H, int T, int dk, int dtype,
+                      void *k_tilde, float *d_final, float *d_all, float *log_ratio,
+                      void *stream);
+
+/*
+ * Phase 2: the chunkwise delta-rule pass with a given write key kt
+ * [summary §2.1: kt replaces k in the chunk gram and intra-chunk scores].
+ * Within a chunk with entry state S, A = strict_lower(diag(beta) K Kt^T),
+ * (I + A) X = diag(beta) (V - K S^T), O = Q S^T + lower(Q Kt^T) X,
+ * S <- S + X^T Kt.  Same result as the token recurrence up to rounding.
+ *   q, k      [B,H,T,dk] dtype   queries; read-side keys (required if T > 0)
+ *   k_tilde   [B,H,T,dk] dtype   write-side keys (required if T > 0)
+ *   v         [B,H,T,dv] dtype   values (required if T > 0)
+ *   beta      [B,H,T]    fp32    (required if T > 0)
+ *   S0        [B,H,dv,dk] fp32   initial state; NULL means zero
+ *   chunk                        chunk length
+ *   o         [B,H,T,dv] dtype   out: o_t = S_t q_t (required if T > 0)
+ *   S_final   [B,H,dv,dk] fp32   out: S_T (optional)
+ */
+int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde, const void *v,
+                   const float *beta, const float *S0, int B, int H, int T, int dk, int dv,
+                   int chunk, int dtype, void *o, float *S_final, void *stream);
+
+/*
+ * Both phases end to end [summary §2.2 two-phase implementation].
+ *   q, k, v, beta, r, d0, S0, eta   as above
+ *   flags          0 or OSDN_PRECOND_OFF
+ *   o              [B,H,T,dv] dtype out (required if T > 0)
+ *   S_final        [B,H,dv,dk] fp32 out (optional)
+ *   d_final        [B,H,dk] fp32 out (optional)
+ *   log_ratio_sum  [B,H] fp32 out: sum_t log rho_t (optional) -- the per-head
+ *                  log of the product of token-local residual ratios of
+ *                  [summary §3]; its mean over tokens gives log q_geo [summary §4.2]
+ *   workspace      device scratch of at least osdn_forward_workspace_bytes(...)
+ *                  bytes (may be NULL when that is 0)
+ */
+int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
+                 const float *r, const float *d0, const float *S0, float eta, int B, int H,
+                 int T, int dk, int dv, int chunk, int dtype, unsigned flags, void *o,
+                 float *S_final, float *d_final, float *log_ratio_sum, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* Scratch bytes osdn_forward needs for these arguments (0 when the fused
+ * single-kernel path applies); (size_t)-1 if the arguments are invalid. */
+size_t osdn_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                                    unsigned flags);
+
+/* Static, NUL-terminated description of a status code (host pointer). */
+const char *osdn_status_str(int status);
+
+/* Name of the kernel family osdn_forward would launch for these arguments
+ * ("fused", "two-phase" or "none"); static host string, "invalid" on bad
+ * arguments.  Lets callers and tests know which path they exercised. */
+const char *osdn_forward_path(int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                              unsigned flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSDN_H */

@@ -1,0 +1,311 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Error metric: per (b,h,t) vector, ||gpu - oracle||_inf / ||oracle||_inf, max
+over vectors; the state uses the per-(b,h) matrix max-abs relative error.
+Tolerances (the path's stated bar): fp32 data -- d and k~ 1e-5, o and S 1e-4;
+bf16 data with fp32 accumulation -- o and S 2e-2.  d is compared at 1e-5 in
+bf16 cases too (identical inputs, fp32 arithmetic); k~ in bf16 cases at the
+bf16 rounding bound 2^-8.
+
+Every input comes from the seeded generators (delta_rule_recurrent_precond_amd
+.workloads) or from the oracle; no expected value comes from the HIP path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import delta_rule_recurrent_precond_amd as osdn
+from delta_rule_recurrent_precond_amd import workloads as W
+from oracle import oracle
+
+from _helpers import as_f64, matrix_rel, rowwise_rel
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(d=1e-5, kt=1e-5, o=1e-4, S=1e-4),
+       "bf16": dict(d=1e-5, kt=2.0 ** -8, o=2e-2, S=2e-2)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    osdn.load()  # fails loudly when libosdn.so is missing
+    torch.cuda.init()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _to_dev(inp):
+    return inp.to("cuda")
+
+
+def _heads(w, n):
+    """A deterministic sample of n flattened heads (all when n >= B*H)."""
+    total = w.B * w.H
+    if n >= total:
+        return list(range(total))
+    g = np.random.default_rng(w.seed + 17)
+    return sorted(g.choice(total, size=n, replace=False).tolist())
+
+
+def _select(x, heads, w):
+    x = as_f64(x)
+    return x.reshape((w.B * w.H,) + x.shape[2:])[heads]
+
+
+def _log_ratio_tol(rho, eps_a=2e-5):
+    """Per-token bound on |log rho_gpu - log rho_oracle| for an fp32 error of at
+    most eps_a (relative to O(1)) in a_t = <d_t, k_t^2>."""
+    g = np.sqrt(np.maximum(rho, 1e-300))
+    return 2.0 * eps_a / g + 1e-6
+
+
+def _check_forward(w, inp, heads, precond=True, d0=None, S0=None, tol=None, label=""):
+    tol = tol or TOL[w.dtype]
+    dev = _to_dev(inp)
+    _log("forward %s heads=%d path=%s" % (label or w.name, len(heads),
+                                         osdn.forward_path(w.B, w.H, w.T, w.dk, w.dv, w.chunk,
+                                                           0 if w.dtype == "bf16" else 1,
+                                                           precond)))
+    out = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r,
+                       None if d0 is None else d0.cuda(), None if S0 is None else S0.cuda(),
+                       eta=inp.eta, chunk=w.chunk, precond=precond)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, d0, S0, eta=inp.eta,
+                         mode="osdn" if precond else "deltanet", heads=heads,
+                         want=("o", "S", "d", "rho"))
+    errs = {
+        "o": rowwise_rel(_select(out["o"], heads, w), _select(ref["o"], heads, w)),
+        "S": matrix_rel(_select(out["S_final"], heads, w), _select(ref["S"], heads, w)),
+    }
+    if precond:
+        errs["d"] = rowwise_rel(_select(out["d_final"], heads, w), _select(ref["d"], heads, w))
+    # sum_t log rho_t per head (fp32 accumulation of T terms)
+    rho = _select(ref["rho"], heads, w)
+    lrs_ref = np.log(rho).sum(axis=-1)
+    lrs_gpu = _select(out["log_ratio_sum"], heads, w)
+    lrs_tol = _log_ratio_tol(rho).sum(axis=-1) + 1e-6 * np.abs(lrs_ref)
+    errs["log_ratio_sum"] = float(np.max(np.abs(lrs_gpu - lrs_ref) / lrs_tol))
+    _log("  errors %s" % {k: "%.3g" % v for k, v in errs.items()})
+    assert errs["o"] <= tol["o"], errs
+    assert errs["S"] <= tol["S"], errs
+    if precond:
+        assert errs["d"] <= tol["d"], errs
+    assert errs["log_ratio_sum"] <= 1.0, errs   # in units of the conditioning bound
+    return out, ref, errs
+
+
+# ---------------------------------------------------------------------------
+# phase 1 alone
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("apf", [False, True])
+def test_precond_scan_parity(dtype, dk, apf):
+    w = W.custom(2, 3, 203, dk, 16, 16, dtype=dtype, eta=0.1, apf=apf, seed=100 + dk)
+    inp = W.generate(w)
+    d0 = (0.5 + torch.rand(w.B, w.H, dk, generator=torch.Generator().manual_seed(5)))
+    dev = _to_dev(inp)
+    _log("scan %s" % w.name)
+    out = osdn.precond_scan(dev.k, dev.beta, dev.r, d0.cuda(), inp.eta, want_d_all=True,
+                            want_log_ratio=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, d0, None, eta=inp.eta,
+                         want=("d", "d_all", "k_tilde", "rho"))
+    tol = TOL[dtype]
+    assert rowwise_rel(out["d_all"], ref["d_all"]) <= tol["d"]
+    assert rowwise_rel(out["d_final"], ref["d"]) <= tol["d"]
+    assert rowwise_rel(out["k_tilde"], ref["k_tilde"]) <= tol["kt"]
+    # log rho_t = 2 log|1 - beta a_t| is ill-conditioned where rho_t -> 0: an error
+    # eps in a_t moves it by about 2 beta eps / |1 - beta a_t|.
+    lr = as_f64(out["log_ratio"])
+    assert np.all(np.abs(lr - np.log(ref["rho"])) <= _log_ratio_tol(ref["rho"]))
+
+
+def test_precond_scan_empty_sequence_copies_d0():
+    d0 = torch.rand(2, 2, 64) + 0.5
+    k = torch.zeros(2, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    beta = torch.zeros(2, 2, 0, device="cuda")
+    out = osdn.precond_scan(k, beta, None, d0.cuda(), 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(out["d_final"].cpu(), d0)
+
+
+# ---------------------------------------------------------------------------
+# phase 2 alone, with the oracle's write keys rounded to the data type
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv,chunk,T", [(16, 16, 16, 100), (32, 64, 32, 77), (64, 32, 16, 150),
+                                           (128, 128, 64, 300), (128, 64, 32, 97),
+                                           (64, 128, 64, 129), (128, 128, 16, 33)])
+def test_chunk_fwd_parity_given_ktilde(dtype, dk, dv, chunk, T):
+    w = W.custom(2, 2, T, dk, dv, chunk, dtype=dtype, eta=0.1, apf=True, seed=dk + dv + T)
+    inp = W.generate(w)
+    S0 = 0.1 * torch.randn(w.B, w.H, dv, dk, generator=torch.Generator().manual_seed(3))
+    kt_ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, eta=inp.eta,
+                            want=("k_tilde",))["k_tilde"]
+    kt = torch.from_numpy(kt_ref).to(inp.k.dtype)   # the stored write keys of both sides
+    dev = _to_dev(inp)
+    _log("chunk %s" % w.name)
+    o, S = osdn.chunk_fwd(dev.q, dev.k, kt.cuda(), dev.v, dev.beta, S0.cuda(), chunk)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, None, None, S0, mode="given",
+                         k_given=kt, want=("o", "S"))
+    tol = TOL[dtype]
+    assert rowwise_rel(o, ref["o"]) <= tol["o"]
+    assert matrix_rel(S, ref["S"]) <= tol["S"]
+
+
+# ---------------------------------------------------------------------------
+# end to end, reduced sizes spanning several chunks with ragged tails
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv,chunk,T,apf", [(16, 16, 16, 256, False), (32, 32, 32, 203, True),
+                                               (64, 64, 64, 190, True), (128, 128, 64, 333, True),
+                                               (128, 128, 64, 256, False), (128, 64, 16, 71, True),
+                                               (64, 128, 32, 64, False)])
+def test_forward_parity_small(dtype, dk, dv, chunk, T, apf):
+    w = W.custom(2, 3, T, dk, dv, chunk, dtype=dtype, eta=0.1, apf=apf, seed=T + dk)
+    inp = W.generate(w)
+    _check_forward(w, inp, _heads(w, 6))
+
+
+@pytest.mark.parametrize("precond", [True, False])
+def test_forward_with_initial_state(precond):
+    w = W.custom(1, 4, 200, 128, 128, 64, dtype="bf16", eta=0.05, apf=True, seed=42)
+    inp = W.generate(w)
+    g = torch.Generator().manual_seed(9)
+    S0 = 0.05 * torch.randn(w.B, w.H, w.dv, w.dk, generator=g)
+    d0 = 0.5 + torch.rand(w.B, w.H, w.dk, generator=g)
+    _check_forward(w, inp, _heads(w, 4), precond=precond, d0=d0, S0=S0)
+
+
+def test_forward_deltanet_mode_small():
+    w = W.custom(2, 2, 150, 64, 64, 32, dtype="f32", eta=0.1, apf=True, seed=3)
+    _check_forward(w, W.generate(w), _heads(w, 4), precond=False)
+
+
+@pytest.mark.parametrize("T", [0, 1, 5, 64, 65])
+def test_forward_short_and_empty(T):
+    w = W.custom(1, 2, T, 128, 128, 64, dtype="bf16", eta=0.1, apf=True, seed=11)
+    inp = W.generate(w)
+    g = torch.Generator().manual_seed(1)
+    S0 = 0.1 * torch.randn(1, 2, 128, 128, generator=g)
+    d0 = 0.5 + torch.rand(1, 2, 128, generator=g)
+    dev = _to_dev(inp)
+    out = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, d0.cuda(), S0.cuda(), eta=inp.eta,
+                       chunk=64)
+    torch.cuda.synchronize()
+    if T == 0:
+        assert torch.equal(out["S_final"].cpu(), S0)
+        assert torch.equal(out["d_final"].cpu(), d0)
+        assert torch.all(out["log_ratio_sum"].cpu() == 0)
+    else:
+        _check_forward(w, inp, [0, 1], d0=d0, S0=S0)
+
+
+def test_eta_zero_equals_deltanet_mode_bitwise():
+    w = W.custom(2, 2, 200, 128, 128, 64, dtype="bf16", eta=0.0, apf=False, seed=21)
+    dev = _to_dev(W.generate(w))
+    a = osdn.forward(dev.q, dev.k, dev.v, dev.beta, None, eta=0.0, chunk=64, precond=True)
+    b = osdn.forward(dev.q, dev.k, dev.v, dev.beta, None, eta=0.0, chunk=64, precond=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["S_final"], b["S_final"])
+    assert torch.all(a["d_final"] == 1.0)
+
+
+def test_deterministic_bitwise():
+    w = W.custom(2, 4, 300, 128, 128, 64, dtype="bf16", eta=0.05, apf=True, seed=8)
+    dev = _to_dev(W.generate(w))
+    runs = [osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=0.05, chunk=64)
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    for key in ("o", "S_final", "d_final", "log_ratio_sum"):
+        assert torch.equal(runs[0][key], runs[1][key]), key
+
+
+@pytest.mark.parametrize("split", [128, 100])
+def test_continuation_through_state(split):
+    """forward(0:T) vs forward(split:T) started from forward(0:split)'s (S, d)."""
+    w = W.custom(1, 2, 256, 128, 128, 64, dtype="bf16", eta=0.05, apf=True, seed=31)
+    inp = W.generate(w)
+    dev = _to_dev(inp)
+    whole = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=0.05, chunk=64)
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    first = osdn.forward(sl(dev.q, 0, split), sl(dev.k, 0, split), sl(dev.v, 0, split),
+                         sl(dev.beta, 0, split), sl(dev.r, 0, split), eta=0.05, chunk=64)
+    second = osdn.forward(sl(dev.q, split, 256), sl(dev.k, split, 256), sl(dev.v, split, 256),
+                          sl(dev.beta, split, 256), sl(dev.r, split, 256), first["d_final"],
+                          first["S_final"], eta=0.05, chunk=64)
+    torch.cuda.synchronize()
+    o = torch.cat([first["o"], second["o"]], dim=2)
+    if split % 64 == 0:   # same chunk boundaries: identical operations
+        assert torch.equal(o, whole["o"]) and torch.equal(second["S_final"], whole["S_final"])
+    else:
+        assert rowwise_rel(o, whole["o"]) <= 2e-2
+        assert matrix_rel(second["S_final"], whole["S_final"]) <= 2e-2
+    assert rowwise_rel(second["d_final"], whole["d_final"]) <= 1e-5
+
+
+def test_basis_keys_closed_form():
+    """Keys e_j (exact in bf16): column j of S is a gated EMA towards v and
+    d_{t+1} = r d_t + eta beta (1 - beta d_j) e_j -- derived by hand from the
+    recurrence; checked here against that closed form, not the oracle."""
+    B, H, T, dk, dv = 1, 1, 96, 16, 16
+    g = np.random.default_rng(5)
+    j = g.integers(0, dk, size=T)
+    K = np.eye(dk)[j]
+    Q = g.standard_normal((T, dk))
+    V = g.standard_normal((T, dv))
+    beta = g.random(T).astype(np.float32)
+    r = (0.8 + 0.2 * g.random(T)).astype(np.float32)
+    eta = 0.5
+    t32 = lambda x: torch.from_numpy(np.asarray(x, np.float32))[None, None].contiguous()
+    out = osdn.forward(t32(Q).cuda(), t32(K).cuda(), t32(V).cuda(), t32(beta).cuda(),
+                       t32(r).cuda(), eta=eta, chunk=16)
+    torch.cuda.synchronize()
+    d = np.ones(dk)
+    S = np.zeros((dv, dk))
+    o = np.zeros((T, dv))
+    Qf, Vf = t32(Q)[0, 0].double().numpy(), t32(V)[0, 0].double().numpy()
+    for t in range(T):
+        jj = j[t]
+        wgt = float(beta[t]) * d[jj]
+        S[:, jj] = (1 - wgt) * S[:, jj] + wgt * Vf[t]
+        o[t] = S @ Qf[t]
+        step = eta * float(beta[t]) * (1 - float(beta[t]) * d[jj])
+        d = float(r[t]) * d
+        d[jj] += step
+    assert rowwise_rel(out["o"][0, 0], o) <= 1e-4
+    assert matrix_rel(out["S_final"][0, 0][None], S[None]) <= 1e-4
+    assert rowwise_rel(out["d_final"][0, 0], d) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# the five measured workloads at full size (sampled heads)
+# ---------------------------------------------------------------------------
+
+FULL = [("tiny", 1), ("340m", 4), ("340m-apf", 4), ("1.3b-apf", 4), ("recall", 3),
+        ("recall-apf", 3)]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,nheads", FULL)
+def test_workload_full_size(name, nheads):
+    w = W.CONFIGS[name]
+    inp = W.generate(w)
+    out, ref, errs = _check_forward(w, inp, _heads(w, nheads), label=name)
+    if name.startswith("recall") or name == "1.3b-apf":
+        # q_geo over the sampled heads agrees with the oracle's
+        heads = _heads(w, nheads)
+        lrs = _select(out["log_ratio_sum"], heads, w)
+        q_gpu = float(np.exp(lrs.sum() / (len(heads) * w.T)))
+        q_ref = oracle.q_geo(_select(ref["rho"], heads, w))
+        _log("  q_geo gpu %.6f oracle %.6f" % (q_gpu, q_ref))
+        tol = _log_ratio_tol(_select(ref["rho"], heads, w)).sum() / (len(heads) * w.T)
+        assert abs(np.log(q_gpu) - np.log(q_ref)) <= tol + 1e-6
