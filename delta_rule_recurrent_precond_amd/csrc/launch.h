@@ -44,5 +44,7 @@ hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t s);
 // Fused single-kernel forward on matrix cores (bf16, dk = dv = 128, chunk = 64).
 bool fused_supported(int dk, int dv, int chunk, int dtype);
 hipError_t launch_fused_forward(const FusedArgs &a, hipStream_t s);
+// The same kernel with the write keys read from memory (phase 2 alone).
+hipError_t launch_fused_chunk(const ChunkArgs &a, hipStream_t s);
 
 }  // namespace osdn

@@ -77,6 +77,8 @@ OSDN_EXPORT int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde
   if ((long long)B * H == 0) return OSDN_OK;
   if (T > 0 && (!q || !k || !k_tilde || !v || !beta || !o)) return OSDN_ERR_NULL;
   osdn::ChunkArgs a{q, k, k_tilde, v, beta, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
+  if (use_fused(dk, dv, chunk, dtype))
+    return hip_status(osdn::launch_fused_chunk(a, (hipStream_t)stream));
   return hip_status(osdn::launch_chunk_generic(a, (hipStream_t)stream));
 }
 
@@ -132,5 +134,5 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
     if (st != OSDN_OK) return st;
   }
   osdn::ChunkArgs ca{q, k, kt, v, beta, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
-  return hip_status(osdn::launch_chunk_generic(ca, s));
+  return hip_status(osdn::launch_chunk_generic(ca, s));  // only shapes the fused kernel lacks
 }
