@@ -5,34 +5,52 @@
 // Source: gist.science technical summary of "OSDN: Improving Delta Rule with
 // Provable Online Preconditioning in Linear Attention" -- §2.1 (the write key
 // kt = d (.) k replaces k in the chunk gram, the intra-chunk scores and the
-// state update; nothing else in the chunkwise pipeline changes), §2.2 (the
-// closed-form surrogate whose gradient drives d, depending on k and beta
-// only, which is what lets the preconditioner walk run ahead of the state
-// pass), §2.3 (APF retention acts on d only and keeps the d recurrence
-// affine), §3 (token-local residual ratio rho_t = (1 - beta_t a_t)^2).
+// state update), §2.2 (closed-form surrogate depending on k and beta only, so
+// the preconditioner walk runs ahead of the state pass), §2.3 (APF retention
+// acts on d only; the d recurrence stays affine), §3 (token-local residual
+// ratio rho_t = (1 - beta_t a_t)^2).
 //
-// One workgroup (4 waves) per (b, h, 32-wide tile of value channels), serial
-// over chunks.  Per chunk of C = 64 tokens with entry state S and entry
-// preconditioner d0:
+// Organisation.  One workgroup of 8 waves per (b, h, 32-wide tile of value
+// channels).  Waves 0-5 ("prep") prepare chunk c+1 while waves 6-7 ("state")
+// run the state pass of chunk c, each on 16 value channels, and take a share
+// of the prep work in the phases where the state pass has nothing to do.
+// Only the prep waves read HBM; everything passed from prep to state is
+// double-buffered in LDS.  Every wave meets the same 9 workgroup barriers per
+// chunk, so no wave ever spins.
 //
-//  preconditioner walk (affine in d, unrolled over the chunk):
-//    p_t = k_t (.) k_t, n_t = ||k_t||^2, alpha_t = eta beta_t / n_t (0 if n_t = 0)
-//    Gamma_t = prod_{m<t} r_m, R_{t,s} = prod_{s<m<t} r_m
-//    e_j <- <d0, p_j>; for t = 0..C-1:  g_t = 1 - beta_t e_t,  c_t = alpha_t g_t,
-//                                        e_j <- r_t e_j + c_t <p_j, p_t>
-//      (e_t at step t equals a_t = <d_t, p_t>; the inner products <p_j, p_t>
-//       form a gram computed on matrix cores)
-//    d_t = Gamma_t d0 + sum_{s<t} R_{t,s} c_s p_s     (matrix cores, for kt only)
-//    d_next = Gamma_C d0 + sum_s R_{C,s} c_s p_s      (fp32)
-//    log rho_t = log g_t^2
-//  state pass (mixed keys: K on the read side, Kt on the write side):
-//    A = strict_lower(diag(beta) K Kt^T),  Tinv = (I + A)^-1 (blocked, 16x16 blocks)
-//    R = diag(beta) (V - K S^T),  X = Tinv R
-//    O = Q S^T + lower(Q Kt^T) X,  S <- S + X^T Kt
+// Prep of a chunk (entry preconditioner d0, p_t = k_t (.) k_t):
+//   stats      n_t = ||k_t||^2, b_t = <d0, p_t>, alpha_t = eta beta_t / n_t (0 if n_t = 0)
+//   G = P P^T  (matrix cores); M_{t,s} = beta_t alpha_s R_{t,s} G_{t,s} for s < t,
+//              R_{t,s} = prod_{s<m<t} r_m, Gamma_t = prod_{m<t} r_m
+//   walk       (I + M) g = 1 - beta (.) Gamma (.) b, by 16x16 blocks; c = alpha (.) g.
+//              g_t = 1 - beta_t a_t with a_t = <d_t, p_t>, so log rho_t = log g_t^2
+//   write keys d_t = Gamma_t d0 + sum_{s<t} R_{t,s} c_s p_s (matrix cores);
+//              kt = d (.) k / ds, ds a power of two >= max(d0) (exact rescaling)
+//   next d     Gamma_L d0 + sum_s R_{L,s} c_s p_s in fp32
+//   grams      A = strict_lower(diag(beta) K Kt^T) ds, P = lower(Q Kt^T) ds
+//   Tinv       (I + A)^-1: fp32 16x16 diagonal blocks, then off-diagonal blocks
+//              T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj by distance from the diagonal
+// State pass of a chunk (entry state S, fp32 master S^T in registers):
+//   R = diag(beta)(V - K S^T), X = Tinv R, O = Q S^T + P X, S^T += ds Kt^T X
+// K S^T and Q S^T of a chunk are formed at the end of the iteration that
+// prepared it, from the prep copies of K and Q, right after the state update
+// of the chunk before it.
 //
-// The write keys enter fp16 scaled by a power of two ds (exact) chosen from
-// the chunk's entry preconditioner, and every product with them is scaled
-// back in fp32, so small preconditioners (APF) stay in fp16's normal range.
+// Iteration schedule (prep of chunk c+1 | state pass of chunk c):
+//   1  stage k, q, v, beta, r; entry d          | R = diag(beta)(V - K S^T)
+//   2  stats, log-gate prefix, ds, key gram G    | X = Tinv R; values of c+1 -> registers
+//   3  M blocks, diagonal inverses, rhs; loads   | O = Q S^T + P X, store o
+//   4  substitution (wave 0) | R factors         | S^T update
+//   5  write keys, 6 i tiles; next d partials    | write keys, 2 i tiles
+//   6  diagonal A blocks + inverses; off-diag A  | score tiles P
+//   7-9 off-diagonal blocks of Tinv              | K S^T, Q S^T of chunk c+1
+//
+// Layout trick: in a 16x16 MFMA result a lane holds 4 consecutive rows of one
+// column; a 16x16x32 operand whose 32 k slots are rows 4g..4g+3 of two
+// consecutive 16-row tiles has exactly that shape.  Contraction order is
+// free, so results feed the next product from registers, with the partner
+// operand read in the same "paired" k order.  Transposes are products with
+// the identity (exact with fp32 accumulation).
 #include "device.h"
 #include "launch.h"
 
@@ -43,38 +61,40 @@ namespace {
 typedef _Float16 f16;
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int C = 64;       // chunk length
-constexpr int DK = 128;     // key dimension
+constexpr int DK = 128;     // key dimension (= value dimension)
 constexpr int DVT = 32;     // value channels per workgroup
-constexpr int NTH = 256;    // threads per workgroup
+constexpr int NTH = 512;    // threads per workgroup
+constexpr int NPREP = 6;    // prep waves
+constexpr int PTH = NPREP * 64;
 constexpr int KP = 136;     // padded row (halves) of [C][DK] tiles
-constexpr int CP = 72;      // padded row (halves) of [*][C] tiles
-constexpr int AP = 68;      // padded row (floats) of fp32 [C][C] tiles
-constexpr int VP = 68;      // padded row (bf16) of the transposed value tile
+constexpr int CP = 72;      // padded row (halves) of [C][C] tiles
+constexpr int AP = 68;      // padded row (floats) of the fp32 [C][C] scratch
 
 enum Mode { kOsdn = 0, kDeltaNet = 1, kGiven = 2 };
 
 struct Smem {
-  f16 K[C * KP];        // chunk keys [t][i]
-  f16 KT[DK * CP];      // chunk keys transposed [i][t]; in the preconditioned
-                        // modes it is overwritten by the scaled write keys [i][t]
-  f16 Q[C * KP];        // chunk queries [t][i]
-  f16 Kt[C * KP];       // scaled write keys [t][i]
-  f16 S[DVT * KP];      // state tile [j][i] (fp16 copy of the fp32 master)
-  f16 Tm[C * CP];       // (I + A)^-1 [t][s]; the preconditioner walk's L first
-  f16 P[C * CP];        // lower(Q Kt^T) [t][s]
-  f16 RT[DVT * CP];     // R^T [j][t]
-  f16 XT[DVT * CP];     // X^T [j][t]
-  unsigned short VT[DVT * VP];  // value tile transposed [j][t], bf16 bits
-  float A[C * AP];      // gram A [t][s] (also the walk's key gram)
-  float d[2][DK];       // preconditioner at chunk entry (ping-pong)
-  float dpart[2][DK];   // partial sums of the next entry preconditioner
-  float beta[C], r[C], n[C], b[C], alpha[C], c[C], w[C];
-  float lg[C + 1];      // lg[t] = sum_{m<t} log r_m
-  float red[8];
+  f16 Kp[C * KP];           // keys of the chunk being prepared [t][i]
+  f16 Qp[C * KP];           // queries [t][i]
+  f16 Kt[C * KP];           // scaled write keys [t][i] (gram operand); before them,
+                            // the chunk's value tile [t][j < 32] passes through here
+  f16 KtF[2][8][2][64][8];  // write keys as S-update operands [buf][i tile][t pair][lane][8]
+  f16 Tm[2][C * CP];        // (I + A)^-1 [buf][t][s]; the walk's R factors occupy the
+                            // buffer being prepared until the inverse overwrites them
+  f16 P[2][C * CP];         // scores lower(Q Kt^T) ds [buf][t][s]
+  float F[C * AP];          // fp32 scratch: key gram -> M, then the gram A
+  float Td[4][16][16];      // the walk's 16x16 diagonal-block inverses
+  float d_in[DK];           // entry preconditioner of the chunk being prepared
+  float dpart[3][DK];       // partial sums of the next entry preconditioner
+  float beta[2][C];         // write gates [buf][t]
+  float dsb[4];             // write-key scale [buf] (padded to keep 16-byte alignment)
+  float r[C], n[C], bv[C], alpha[C], g[C], cc[C], w[C], rhs[C], acc[C];
+  float lg[C + 4];          // lg[t] = sum_{m<t} log2 r_m
+  float lgC;                // lg[L] of the chunk prepared last
+  float red[15];
 };
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget of one workgroup");
 
 __device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -82,31 +102,78 @@ __device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mma16(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f16x8 ld8(const f16 *p) { return *(const f16x8 *)p; }
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// fp32 -> fp16, rounding a materialised fp32 value to nearest even.  The empty
-// asm keeps the compiler from fusing the conversion into the producing FMA
-// (a mixed-precision FMA would round once, straight to fp16), so equal fp32
-// values always give equal fp16 values whichever code path produced them --
-// which is what makes results bitwise reproducible across call boundaries.
+// fp32 -> fp16 rounding a materialised fp32 value.  The empty asm keeps the
+// compiler from fusing the conversion into the producing FMA (a mixed-precision
+// FMA rounds once, straight to fp16), so equal fp32 values give equal fp16
+// values on every code path -- needed for bitwise-reproducible continuation.
 __device__ __forceinline__ f16 h(float x) {
   asm volatile("" : "+v"(x));
   return (f16)x;
 }
-
+__device__ __forceinline__ f16x4 h4(f32x4 v) { return f16x4{h(v[0]), h(v[1]), h(v[2]), h(v[3])}; }
+__device__ __forceinline__ f16x8 cat(f16x4 a, f16x4 b) {
+  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 __device__ __forceinline__ float bf2f(unsigned short u) {
   return __builtin_bit_cast(float, ((unsigned)u) << 16);
 }
+__device__ __forceinline__ f16x4 ld4(const f16 *p) { return *(const f16x4 *)p; }
+__device__ __forceinline__ f16x8 ld8(const f16 *p) { return *(const f16x8 *)p; }
+// 16x16x32 operand in the paired k order from a row-major f16 row:
+// halves kb + 4g .. +3 and kb + 16 + 4g .. +3.
+__device__ __forceinline__ f16x8 ldpk(const f16 *row, int kb, int g) {
+  return cat(ld4(row + kb + 4 * g), ld4(row + kb + 16 + 4 * g));
+}
+// 8 bf16 (16 bytes) as fp16 (exact for |x| in fp16's normal range)
+__device__ __forceinline__ f16x8 cvt8(const uint4 &u) {
+  const unsigned short *s = (const unsigned short *)&u;
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = h(bf2f(s[e]));
+  return r;
+}
+// hardware 2^x and log2 x (about 1 ulp)
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+// Lanes of one wave exchange data through LDS between the two sides of this
+// call; it keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_wave_barrier(); }
 
-// Lower-triangular 16x16 tile list of a 64x64 matrix (row tile, col tile).
+// Lower-triangular 16x16 tile list of a 64x64 matrix (10 tiles).
 __device__ __forceinline__ void tri_tile(int idx, int &rt, int &ct) {
-  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
   rt = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
   ct = idx - (rt * (rt + 1)) / 2;
 }
+// Off-diagonal lower tiles (row tile > col tile), 6 of them:
+// (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+__device__ __forceinline__ void off_tile(int idx, int &rt, int &ct) {
+  rt = idx >= 3 ? 3 : idx >= 1 ? 2 : 1;
+  ct = idx - (rt * (rt - 1)) / 2;
+}
+
+// Column `col` of (I + N)^-1 for a 16x16 strictly-lower N, row-major fp32 in
+// LDS with row stride `ld` (16-byte aligned rows); forward substitution.
+__device__ __forceinline__ void tri16_inverse_column(const float *N, int ld, int col,
+                                                     float (&x)[16]) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    float a0 = (t == col) ? 1.f : 0.f, a1 = 0.f;
+#pragma unroll
+    for (int s = 0; s < t; s += 4) {
+      const float4 nv = *(const float4 *)&N[t * ld + s];
+      a0 = fmaf(-nv.x, x[s], a0);
+      if (s + 1 < t) a1 = fmaf(-nv.y, x[s + 1], a1);
+      if (s + 2 < t) a0 = fmaf(-nv.z, x[s + 2], a0);
+      if (s + 3 < t) a1 = fmaf(-nv.w, x[s + 3], a1);
+    }
+    x[t] = a0 + a1;
+  }
+}
 
 template <int MODE>
-__global__ void __launch_bounds__(NTH, 1)
+__global__ void __launch_bounds__(NTH)
 osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const bf16 *__restrict__ kt_in, const bf16 *__restrict__ v,
                    const float *__restrict__ beta, const float *__restrict__ r,
@@ -119,12 +186,12 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform role
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
 
-  // Workgroup -> (head, value tile).  Consecutive workgroup ids are spread over
-  // the 8 XCDs; keep the tiles of one head on one XCD so they share its L2.
+  // Workgroup -> (head, value tile); consecutive workgroup ids go to different
+  // XCDs, so the tiles of one head are kept on one XCD to share its L2.
   int bh, tile;
   {
     const int b = blockIdx.x;
@@ -139,520 +206,628 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
   const int j0 = tile * DVT;
   const long tok0 = (long)bh * T_;
+  const int nch = (T_ + C - 1) / C;
   const bool writer = tile == 0;  // writes the per-head outputs (d, log-ratio sum)
 
-  // ---- zero the upper triangles that the triangular products read as zero ----
+  // identity as a 16x16x16 operand: lane (col c16, k 4g+e)
+  f16x4 ident;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ident[e] = (4 * g + e == c16) ? (f16)1.0f : (f16)0.0f;
+
+  // ------------- prep work any wave can take (chunk in buffer nb) -------------
+  // Write keys of i tile n (OSDN): D = Gamma d0 + R (c (.) P), kt = D (.) k / ds,
+  // stored as S-update operands (KtF) and row-major (Kt).
+  auto write_keys_itile = [&](int n, int nb) {
+    const float inv = 1.0f / sm.dsb[nb];
+    f32x4 kT[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      kT[j] = mma16(ld4(&sm.Kp[(16 * j + c16) * KP + 16 * n + 4 * g]), ident, zero4());
+    f16x8 cP[2];
+    {
+      f16x4 cpj[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 c4 = *(const float4 *)&sm.cc[16 * j + 4 * g];
+        const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cpj[j][e] = h(kT[j][e] * kT[j][e] * cv[e]);
+      }
+      cP[0] = cat(cpj[0], cpj[1]);
+      cP[1] = cat(cpj[2], cpj[3]);
+    }
+    const float dbase = sm.d_in[16 * n + c16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float4 l4 = *(const float4 *)&sm.lg[16 * m + 4 * g];
+      f32x4 acc = {fexp2(l4.x) * dbase, fexp2(l4.y) * dbase, fexp2(l4.z) * dbase,
+                   fexp2(l4.w) * dbase};
+      const f16 *row = &sm.Tm[nb][(16 * m + c16) * CP];
+#pragma unroll
+      for (int qq = 0; qq <= (m >> 1); ++qq) acc = mma32(ldpk(row, 32 * qq, g), cP[qq], acc);
+      f32x4 ktv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ktv[e] = acc[e] * kT[m][e] * inv;
+      const f16x4 kt4 = h4(ktv);
+      *(f16x4 *)&sm.KtF[nb][n][m >> 1][lane][4 * (m & 1)] = kt4;
+      const f32x4 tr = mma16(kt4, ident, zero4());
+      *(f16x4 *)&sm.Kt[(16 * m + c16) * KP + 16 * n + 4 * g] = h4(tr);
+    }
+  };
+  // Write keys held row-major in `src` (the keys, or given write keys):
+  // 16x16 tile (m, n) transposed through the identity into the S-update operand.
+  auto write_keys_copy = [&](int job, const f16 *src, int nb) {
+    const int m = job >> 3, n = job & 7;
+    const f32x4 tr = mma16(ld4(&src[(16 * m + c16) * KP + 16 * n + 4 * g]), ident, zero4());
+    *(f16x4 *)&sm.KtF[nb][n][m >> 1][lane][4 * (m & 1)] = h4(tr);
+  };
+  // Lower tile idx of the scores P = lower(Q Kt^T) ds.
+  auto score_tile = [&](int idx, const f16 *Bsrc, int nb) {
+    int rt, ct;
+    tri_tile(idx, rt, ct);
+    const float ds = sm.dsb[nb];
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      acc = mma32(ld8(&sm.Qp[(16 * rt + c16) * KP + 32 * kk + 8 * g]),
+                  ld8(&Bsrc[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + 4 * g + e, col = 16 * ct + c16;
+      sm.P[nb][row * CP + col] = h(col <= row ? ds * acc[e] : 0.f);
+    }
+  };
+
+  // ---------------- initialisation ----------------
   for (int idx = tid; idx < C * CP; idx += NTH) {
-    sm.Tm[idx] = h(0.0f);
-    sm.P[idx] = h(0.0f);
+    sm.P[0][idx] = (f16)0.0f;
+    sm.P[1][idx] = (f16)0.0f;
+    sm.Tm[0][idx] = (f16)0.0f;
+    sm.Tm[1][idx] = (f16)0.0f;
   }
-  for (int i = tid; i < DK; i += NTH) sm.d[0][i] = (MODE == kOsdn && d0) ? d0[(long)bh * DK + i] : 1.0f;
+  for (int i = tid; i < DK; i += NTH)
+    sm.d_in[i] = (MODE == kOsdn && d0) ? d0[(long)bh * DK + i] : 1.0f;
+  if (tid == 0) sm.lgC = 0.f;
 
-  // ---- state: fp32 master S^T tiles in registers, wave w owns i-tiles 2w, 2w+1 ----
-  f32x4 Sacc[2][2];  // [i sub-tile][j tile]
+  if (wave < NPREP) {
+    // =====================================================================
+    //                              prep waves
+    // =====================================================================
+    const int ptid = tid;
+    uint4 pk[3], pq[3], pkt[3], pv;
+    float pb = 0.f, pr = 1.f;
+    float lr_sum = 0.f;  // wave 0: sum over tokens of log rho_t
+    auto prep_load = [&](int cc_) {
+      const int c0 = cc_ * C;
+      const int L = min(C, T_ - c0);
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int i0 = 16 * (2 * wave + mi) + 4 * g4;
-      const int j = 16 * n + l16;
-      if (S0) {
-        const float4 s4 = *(const float4 *)(S0 + ((long)bh * 128 + j0 + j) * DK + i0);
-        Sacc[mi][n] = f32x4{s4.x, s4.y, s4.z, s4.w};
-      } else {
-        Sacc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < 3; ++u) {
+        const int p = ptid + PTH * u;
+        const int t = p >> 4, piece = p & 15;
+        const bool ok = p < 16 * C && t < L;
+        const long off = (tok0 + c0 + t) * DK + piece * 8;
+        pk[u] = ok ? *(const uint4 *)(k + off) : uint4{0, 0, 0, 0};
+        pq[u] = ok ? *(const uint4 *)(q + off) : uint4{0, 0, 0, 0};
+        if (MODE == kGiven) pkt[u] = ok ? *(const uint4 *)(kt_in + off) : uint4{0, 0, 0, 0};
       }
-    }
-  auto write_state_f16 = [&]() {
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int i0 = 16 * (2 * wave + mi) + 4 * g4;
-        const int j = 16 * n + l16;
-        const f16x4 hs = {h(Sacc[mi][n][0]), h(Sacc[mi][n][1]), h(Sacc[mi][n][2]),
-                          h(Sacc[mi][n][3])};
-        *(f16x4 *)&sm.S[j * KP + i0] = hs;
+      {
+        // value tile: 64 rows x 4 pieces of 8 channels
+        const int t = ptid >> 2, piece = ptid & 3;
+        const bool ok = ptid < 4 * C && t < L;
+        pv = ok ? *(const uint4 *)(v + (tok0 + c0 + t) * 128 + j0 + piece * 8)
+                : uint4{0, 0, 0, 0};
       }
-  };
-  write_state_f16();
-
-  // ---- global -> register staging of one chunk (issued a chunk ahead) ----
-  // K, Q, (k~ in the given-key mode): 64 rows x 16 pieces of 16 B; thread tid
-  // takes rows tid/16 + 16 m, piece tid%16.  V tile: 64 rows x 4 pieces.
-  uint4 pk[4], pq[4], pkt[4], pv;
-  float pb = 0.f, pr = 1.f;
-  auto load_chunk = [&](int c0) {
-    const int L = min(C, T_ - c0);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = tid / 16 + 16 * m, piece = tid % 16;
-      const bool ok = t < L;
-      const long off = (tok0 + c0 + t) * DK + piece * 8;
-      pk[m] = ok ? *(const uint4 *)(k + off) : uint4{0, 0, 0, 0};
-      pq[m] = ok ? *(const uint4 *)(q + off) : uint4{0, 0, 0, 0};
-      if (MODE == kGiven) pkt[m] = ok ? *(const uint4 *)(kt_in + off) : uint4{0, 0, 0, 0};
-    }
-    {
-      const int t = tid / 4, piece = tid % 4;
-      pv = t < L ? *(const uint4 *)(v + (tok0 + c0 + t) * 128 + j0 + piece * 8)
-                 : uint4{0, 0, 0, 0};
-    }
-    if (tid < C) {
-      const bool ok = tid < L;
-      pb = ok ? beta[tok0 + c0 + tid] : 0.f;
-      pr = (ok && r) ? r[tok0 + c0 + tid] : 1.f;
-    }
-  };
-
-  float lr_sum = 0.f;  // wave 0 of the writer accumulates sum_t log rho_t
-  int dcur = 0;
-  if (T_ > 0) load_chunk(0);
-
-  for (int c0 = 0; c0 < T_; c0 += C) {
-    const int L = min(C, T_ - c0);
-    // ================= P1: staging registers -> LDS =================
-    __syncthreads();  // previous chunk is done with every buffer
-    float kmax = 0.f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = tid / 16 + 16 * m, i0 = (tid % 16) * 8;
-      const unsigned short *uk = (const unsigned short *)&pk[m];
-      const unsigned short *uq = (const unsigned short *)&pq[m];
-      f16x8 hk, hq;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hk[e] = h(bf2f(uk[e]));
-        hq[e] = h(bf2f(uq[e]));
-        if (MODE != kGiven) sm.KT[(i0 + e) * CP + t] = hk[e];
+      if (ptid < C) {
+        const bool ok = ptid < L;
+        pb = ok ? beta[tok0 + c0 + ptid] : 0.f;
+        pr = (ok && r) ? r[tok0 + c0 + ptid] : 1.f;
       }
-      *(f16x8 *)&sm.K[t * KP + i0] = hk;
-      *(f16x8 *)&sm.Q[t * KP + i0] = hq;
-      if (MODE == kGiven) {
-        const unsigned short *ut = (const unsigned short *)&pkt[m];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kmax = fmaxf(kmax, fabsf(bf2f(ut[e])));
-      }
-    }
-    {
-      const int t = tid / 4, jj = (tid % 4) * 8;
-      const unsigned short *uv = (const unsigned short *)&pv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm.VT[(jj + e) * VP + t] = uv[e];
-    }
-    if (tid < C) {
-      sm.beta[tid] = pb;
-      sm.r[tid] = pr;
-    }
-    float ds = 1.0f;  // power-of-two scale of the fp16 write keys
-    if (MODE == kGiven) {
-      kmax = fmaxf(kmax, __shfl_xor(kmax, 1));
-      kmax = fmaxf(kmax, __shfl_xor(kmax, 2));
-      kmax = fmaxf(kmax, __shfl_xor(kmax, 4));
-      kmax = fmaxf(kmax, __shfl_xor(kmax, 8));
-      kmax = fmaxf(kmax, __shfl_xor(kmax, 16));
-      kmax = fmaxf(kmax, __shfl_xor(kmax, 32));
-      if (lane == 0) sm.red[wave] = kmax;
-    }
+    };
+    if (nch > 0) prep_load(0);
     __syncthreads();
 
-    if (MODE == kGiven) {
-      const float km = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
-      ds = km > 0.f ? exp2f(ceilf(log2f(km))) : 1.0f;
-      const float inv = 1.0f / ds;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int t = tid / 16 + 16 * m, i0 = (tid % 16) * 8;
-        const unsigned short *ut = (const unsigned short *)&pkt[m];
-        f16x8 hv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hv[e] = h(bf2f(ut[e]) * inv);
-          sm.KT[(i0 + e) * CP + t] = hv[e];
-        }
-        *(f16x8 *)&sm.Kt[t * KP + i0] = hv;
-      }
-    }
-    // prefetch the next chunk (the staging registers are consumed) while this one runs
-    if (c0 + C < T_) load_chunk(c0 + C);
+    for (int it = 0; it <= nch; ++it) {
+      const int pc = it;  // chunk being prepared
+      const int nb = pc & 1;
+      const bool act = pc < nch;
+      const int pL = act ? min(C, T_ - pc * C) : 0;
 
-    const f16 *Kt = (MODE == kDeltaNet) ? sm.K : sm.Kt;
-    const f16 *KtT = sm.KT;
-
-    // ================= P2: key statistics =================
-    // wave w, tokens 16w + l16, dims 32 g4 .. +31
-    if (MODE != kGiven) {
-      const int t = 16 * wave + l16;
-      const float *dv = sm.d[dcur];
-      float pn = 0.f, pa = 0.f, dmx = 0.f;
+      // ------------------------------ phase 1 ------------------------------
+      if (act) {
+        if (MODE == kOsdn && pc > 0 && ptid < DK)
+          sm.d_in[ptid] = fexp2(sm.lgC) * sm.d_in[ptid] + sm.dpart[0][ptid] +
+                          sm.dpart[1][ptid] + sm.dpart[2][ptid];
+        float kmax = 0.f;
 #pragma unroll
-      for (int q8 = 0; q8 < 4; ++q8) {
-        const int i0 = 32 * g4 + 8 * q8;
-        const f16x8 kk = ld8(&sm.K[t * KP + i0]);
+        for (int u = 0; u < 3; ++u) {
+          const int p = ptid + PTH * u;
+          if (p < 16 * C) {
+            const int t = p >> 4, i0 = (p & 15) * 8;
+            *(f16x8 *)&sm.Kp[t * KP + i0] = cvt8(pk[u]);
+            *(f16x8 *)&sm.Qp[t * KP + i0] = cvt8(pq[u]);
+            if (MODE == kGiven) {
+              const unsigned short *ut = (const unsigned short *)&pkt[u];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (float)kk[e];
-          const float p = x * x;
-          pn += p;
-          pa += dv[i0 + e] * p;
-          dmx = fmaxf(dmx, dv[i0 + e]);
-        }
-      }
-      pn += __shfl_xor(pn, 16);
-      pn += __shfl_xor(pn, 32);
-      pa += __shfl_xor(pa, 16);
-      pa += __shfl_xor(pa, 32);
-      dmx = fmaxf(dmx, __shfl_xor(dmx, 16));
-      dmx = fmaxf(dmx, __shfl_xor(dmx, 32));
-      if (g4 == 0) {
-        const float bt = sm.beta[t];
-        sm.n[t] = pn;
-        sm.b[t] = pa;
-        sm.alpha[t] = (MODE == kOsdn && pn > 0.f) ? eta * bt / pn : 0.f;
-      }
-      if (lane == 0) sm.red[wave] = dmx;
-      // prefix sums of log r (wave 0, lanes = tokens)
-      if (wave == 0 && MODE == kOsdn) {
-        const float lr = fmaxf(logf(sm.r[lane]), -80.f);
-        float incl = lr;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(incl, off);
-          if (lane >= off) incl += y;
-        }
-        sm.lg[lane + 1] = incl;
-        if (lane == 0) sm.lg[0] = 0.f;
-      }
-    }
-    __syncthreads();
-
-    if (MODE == kOsdn) {
-      const float dmax = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
-      ds = dmax > 0.f ? exp2f(ceilf(log2f(dmax))) : 1.0f;
-
-      // ---- key gram G = strict_lower(P P^T), P = k (.) k in fp16 -> sm.A ----
-      for (int job = wave; job < 10; job += 4) {
-        int rt, ct;
-        tri_tile(job, rt, ct);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          f16x8 a = ld8(&sm.K[(16 * rt + l16) * KP + 32 * kk + 8 * g4]);
-          f16x8 b = ld8(&sm.K[(16 * ct + l16) * KP + 32 * kk + 8 * g4]);
-          acc = mma32(a * a, b * b, acc);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * rt + 4 * g4 + e, col = 16 * ct + l16;
-          sm.A[row * AP + col] = col < row ? acc[e] : 0.f;
-        }
-      }
-      // zero the strictly upper tiles of the gram (read by the walk)
-      for (int idx = tid; idx < C * C; idx += NTH) {
-        const int row = idx / C, col = idx % C;
-        if ((col >> 4) > (row >> 4)) sm.A[row * AP + col] = 0.f;
-      }
-      __syncthreads();
-
-      // ---- the walk proper: one wave, lanes = tokens of the chunk ----
-      if (wave == 0) {
-        const int j = lane;
-        float G[C];
-#pragma unroll
-        for (int q4 = 0; q4 < C / 4; ++q4) {
-          const float4 g = *(const float4 *)&sm.A[j * AP + 4 * q4];
-          G[4 * q4 + 0] = g.x;
-          G[4 * q4 + 1] = g.y;
-          G[4 * q4 + 2] = g.z;
-          G[4 * q4 + 3] = g.w;
-        }
-        const float bj = sm.beta[j];
-        const float al = sm.alpha[j];
-        const float rj = sm.r[j];
-        float e = sm.b[j];
-        float ckeep = 0.f, gkeep = 1.f;
-#pragma unroll
-        for (int t = 0; t < C; ++t) {
-          const float g = fmaf(-bj, e, 1.0f);
-          const float cl = al * g;
-          const float ct = __builtin_bit_cast(
-              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cl), t));
-          const float rt = __builtin_bit_cast(
-              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rj), t));
-          if (j == t) {
-            ckeep = cl;
-            gkeep = g;
-          }
-          e = fmaf(ct, G[t], rt * e);
-        }
-        sm.c[j] = ckeep;
-        // weight of c_s p_s in the next entry preconditioner: R_{L,s}
-        sm.w[j] = j < L ? expf(sm.lg[L] - sm.lg[j + 1]) * ckeep : 0.f;
-        const float lr = j < L ? logf(gkeep * gkeep) : 0.f;
-        lr_sum += wave_sum(lr);
-      }
-      __syncthreads();
-
-      // ---- L[t][s] = R_{t,s} c_s (s < t) into sm.Tm (fp16) ----
-      for (int idx = tid; idx < C * C; idx += NTH) {
-        const int t = idx / C, s = idx % C;
-        const float val = s < t ? expf(sm.lg[t] - sm.lg[s + 1]) * sm.c[s] : 0.f;
-        sm.Tm[t * CP + s] = h(val);
-      }
-      // ---- next entry preconditioner (fp32): partial sums over halves of s ----
-      {
-        const int i = tid & 127, h = tid >> 7;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int s = 32 * h; s < 32 * h + 32; ++s) {
-          const float x = (float)sm.KT[i * CP + s];
-          acc = fmaf(sm.w[s], x * x, acc);
-        }
-        sm.dpart[h][i] = acc;
-      }
-      __syncthreads();
-      if (tid < DK) {
-        sm.d[dcur ^ 1][tid] =
-            expf(sm.lg[L]) * sm.d[dcur][tid] + sm.dpart[0][tid] + sm.dpart[1][tid];
-      }
-
-      // ---- d_t for the chunk: D = Gamma d0^T + L P (matrix cores), kt = D (.) k / ds ----
-      // Wave w owns i tiles 2w, 2w+1: it alone reads and then rewrites those rows of KT.
-      {
-        const float inv = 1.0f / ds;
-        f16x4 kto[2][4];
-#pragma unroll
-        for (int nn = 0; nn < 2; ++nn) {
-          const int n = 2 * wave + nn;  // i tile
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {  // t tile
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int nk = m < 2 ? 1 : 2;
-            for (int kk = 0; kk < nk; ++kk) {
-              const f16x8 a = ld8(&sm.Tm[(16 * m + l16) * CP + 32 * kk + 8 * g4]);
-              const f16x8 b = ld8(&sm.KT[(16 * n + l16) * CP + 32 * kk + 8 * g4]);
-              acc = mma32(a, b * b, acc);
+              for (int e = 0; e < 8; ++e) kmax = fmaxf(kmax, fabsf(bf2f(ut[e])));
             }
-            const int i = 16 * n + l16;
-            const int t0 = 16 * m + 4 * g4;
-            const f16x4 kv = *(const f16x4 *)&sm.KT[i * CP + t0];
-            const float dbase = sm.d[dcur][i];
+          }
+        }
+        if (ptid < 4 * C) {
+          const int t = ptid >> 2, j = (ptid & 3) * 8;
+          *(f16x8 *)&sm.Kt[t * KP + j] = cvt8(pv);
+        }
+        if (ptid < C) {
+          sm.beta[nb][ptid] = pb;
+          sm.r[ptid] = pr;
+        }
+        if (MODE == kGiven) {
+#pragma unroll
+          for (int m_ = 1; m_ < 64; m_ <<= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, m_));
+          if (lane == 0) sm.red[wave] = kmax;
+        }
+      }
+      __syncthreads();
+
+      // ------------------------------ phase 2 ------------------------------
+      if (act && MODE != kGiven) {
+        if (wave < 4) {
+          // token statistics: wave w owns tokens 16w..16w+15, lane quarter g 32 dims
+          const int t = 16 * wave + c16;
+          float pn = 0.f, pa = 0.f;
+#pragma unroll
+          for (int q8 = 0; q8 < 4; ++q8) {
+            const int i0 = 32 * g + 8 * q8;
+            const f16x8 kk = ld8(&sm.Kp[t * KP + i0]);
+            const float4 da = *(const float4 *)&sm.d_in[i0];
+            const float4 db = *(const float4 *)&sm.d_in[i0 + 4];
+            const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = (float)kk[e];
+              const float p = x * x;
+              pn += p;
+              pa = fmaf(dd[e], p, pa);
+            }
+          }
+          pn += __shfl_xor(pn, 16);
+          pn += __shfl_xor(pn, 32);
+          pa += __shfl_xor(pa, 16);
+          pa += __shfl_xor(pa, 32);
+          if (g == 0) {
+            sm.n[t] = pn;
+            sm.bv[t] = pa;
+            sm.alpha[t] = (MODE == kOsdn && pn > 0.f) ? eta * sm.beta[nb][t] / pn : 0.f;
+          }
+        } else if (wave == 4) {
+          if (MODE == kOsdn) {
+            // lg[t] = sum_{m<t} log2 r_m (clamped so that r = 0 stays finite)
+            const float lr = fmaxf(flog2(sm.r[lane]), -126.f);
+            float incl = lr;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+              const float y = __shfl_up(incl, off);
+              if (lane >= off) incl += y;
+            }
+            sm.lg[lane + 1] = incl;
+            if (lane == 0) sm.lg[0] = 0.f;
+          }
+        } else {
+          float dm = fmaxf(sm.d_in[lane], sm.d_in[lane + 64]);
+#pragma unroll
+          for (int m_ = 1; m_ < 64; m_ <<= 1) dm = fmaxf(dm, __shfl_xor(dm, m_));
+          if (lane == 0)
+            sm.dsb[nb] = (MODE == kOsdn && dm > 0.f) ? fexp2(ceilf(flog2(dm))) : 1.0f;
+        }
+        if (MODE == kOsdn) {
+          // key gram G = P P^T (P = k (.) k in fp16), lower tiles -> F (raw)
+          for (int job = wave; job < 10; job += NPREP) {
+            int rt, ct;
+            tri_tile(job, rt, ct);
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              const f16x8 a = ld8(&sm.Kp[(16 * rt + c16) * KP + 32 * kk + 8 * g]);
+              const f16x8 b = ld8(&sm.Kp[(16 * ct + c16) * KP + 32 * kk + 8 * g]);
+              acc = mma32(a * a, b * b, acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sm.F[(16 * rt + 4 * g + e) * AP + 16 * ct + c16] = acc[e];
+          }
+        }
+      }
+      __syncthreads();
+
+      // ------------------------------ phase 3 ------------------------------
+      if (act) {
+        if (MODE == kGiven) {
+          // given write keys, rescaled by a power of two into fp16 range
+          float km = 0.f;
+#pragma unroll
+          for (int w_ = 0; w_ < NPREP; ++w_) km = fmaxf(km, sm.red[w_]);
+          const float ds = km > 0.f ? fexp2(ceilf(flog2(km))) : 1.0f;
+          const float inv = 1.0f / ds;
+          if (ptid == 0) sm.dsb[nb] = ds;
+#pragma unroll
+          for (int u = 0; u < 3; ++u) {
+            const int p = ptid + PTH * u;
+            if (p < 16 * C) {
+              const int t = p >> 4, i0 = (p & 15) * 8;
+              const unsigned short *ut = (const unsigned short *)&pkt[u];
+              f16x8 hv;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) hv[e] = h(bf2f(ut[e]) * inv);
+              *(f16x8 *)&sm.Kt[t * KP + i0] = hv;
+            }
+          }
+        } else if (MODE == kOsdn) {
+          if (wave < 4) {
+            // diagonal block b of M, scaled in place, then its inverse
+            const int b = wave;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int idx = lane + 64 * u;
+              const int tt = idx >> 4, ss = idx & 15;
+              const int t = 16 * b + tt, s = 16 * b + ss;
+              float val = 0.f;
+              if (ss < tt)
+                val = sm.beta[nb][t] * sm.alpha[s] * fexp2(sm.lg[t] - sm.lg[s + 1]) *
+                      sm.F[t * AP + s];
+              sm.F[t * AP + s] = val;
+            }
+            wave_lds_sync();
+            if (lane < 16) {
+              float x[16];
+              tri16_inverse_column(&sm.F[(16 * b) * AP + 16 * b], AP, lane, x);
+#pragma unroll
+              for (int t = 0; t < 16; ++t) sm.Td[b][t][lane] = x[t];
+            }
+          } else {
+            // off-diagonal blocks of M (a thread keeps one column s), and the rhs
+            const int l2 = ptid - 256;  // 0..127
+#pragma unroll
+            for (int u = 0; u < 12; ++u) {
+              const int idx = l2 + 128 * u;  // < 1536
+              int rt, ct;
+              off_tile(idx >> 8, rt, ct);
+              const int t = 16 * rt + ((idx >> 4) & 15), s = 16 * ct + (idx & 15);
+              sm.F[t * AP + s] *= sm.beta[nb][t] * sm.alpha[s] * fexp2(sm.lg[t] - sm.lg[s + 1]);
+            }
+            if (l2 < C) sm.rhs[l2] = 1.0f - sm.beta[nb][l2] * fexp2(sm.lg[l2]) * sm.bv[l2];
+          }
+        }
+        // prefetch the next chunk (every staging register has been consumed)
+        if (pc + 1 < nch) prep_load(pc + 1);
+      }
+      __syncthreads();
+
+      // ------------------------------ phase 4 ------------------------------
+      if (act) {
+        if (wave == 0) {
+          if (MODE == kOsdn) {
+            // blocked forward substitution of (I + M) g = rhs, lanes = tokens
+            const int t = lane;
+            float a = sm.rhs[t];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              sm.acc[t] = a;
+              wave_lds_sync();
+              if ((t >> 4) == b) {
+                const float *row = &sm.Td[b][t & 15][0];
+                float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+                for (int u = 0; u < 16; u += 4) {
+                  const float4 tv = *(const float4 *)&row[u];
+                  const float4 av = *(const float4 *)&sm.acc[16 * b + u];
+                  y0 = fmaf(tv.x, av.x, y0);
+                  y1 = fmaf(tv.y, av.y, y1);
+                  y0 = fmaf(tv.z, av.z, y0);
+                  y1 = fmaf(tv.w, av.w, y1);
+                }
+                a = y0 + y1;
+                sm.g[t] = a;
+              }
+              wave_lds_sync();
+              if ((t >> 4) > b) {
+                float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+                for (int u = 0; u < 16; u += 4) {
+                  const float4 mv = *(const float4 *)&sm.F[t * AP + 16 * b + u];
+                  const float4 gv = *(const float4 *)&sm.g[16 * b + u];
+                  y0 = fmaf(mv.x, gv.x, y0);
+                  y1 = fmaf(mv.y, gv.y, y1);
+                  y0 = fmaf(mv.z, gv.z, y0);
+                  y1 = fmaf(mv.w, gv.w, y1);
+                }
+                a -= y0 + y1;
+              }
+              wave_lds_sync();
+            }
+            // a == g_t == 1 - beta_t a_t
+            const float cct = sm.alpha[t] * a;
+            sm.cc[t] = cct;
+            sm.w[t] = t < pL ? fexp2(sm.lg[pL] - sm.lg[t + 1]) * cct : 0.f;
+            if (lane == 0) sm.lgC = sm.lg[pL];
+            lr_sum += wave_sum(t < pL ? logf(a * a) : 0.f);
+          } else if (MODE == kDeltaNet) {
+            const float gd = 1.0f - sm.beta[nb][lane] * sm.n[lane];
+            lr_sum += wave_sum(lane < pL ? logf(gd * gd) : 0.f);
+          }
+        } else if (MODE == kOsdn) {
+          // R_{t,s} (s < t) for the write keys, into the inverse buffer being
+          // prepared; a thread keeps one column s
+          f16 *R16 = sm.Tm[nb];
+          const int l5 = ptid - 64;  // 0..319
+          for (int idx = l5; idx < C * C; idx += 320) {
+            const int t = idx >> 6, s = idx & 63;
+            R16[t * CP + s] = h(s < t ? fexp2(sm.lg[t] - sm.lg[s + 1]) : 0.f);
+          }
+        }
+      }
+      __syncthreads();
+
+      // ------------------------------ phase 5 ------------------------------
+      if (act) {
+        if (MODE == kOsdn) {
+          write_keys_itile(wave, nb);  // i tiles 0..5; the state waves take 6 and 7
+          // next entry preconditioner, partial sums over thirds of the chunk
+          const int i = ptid & 127, part = ptid >> 7;
+          const int s_lo = part == 0 ? 0 : part == 1 ? 22 : 43;
+          const int s_hi = part == 0 ? 22 : part == 1 ? 43 : 64;
+          float a0 = 0.f, a1 = 0.f;
+          for (int s = s_lo; s < s_hi; s += 2) {
+            const float x0 = (float)sm.Kp[s * KP + i];
+            a0 = fmaf(sm.w[s], x0 * x0, a0);
+            if (s + 1 < s_hi) {
+              const float x1 = (float)sm.Kp[(s + 1) * KP + i];
+              a1 = fmaf(sm.w[s + 1], x1 * x1, a1);
+            }
+          }
+          sm.dpart[part][i] = a0 + a1;
+        } else {
+          const f16 *src = (MODE == kDeltaNet) ? sm.Kp : sm.Kt;
+          for (int job = wave; job < 32; job += 8) write_keys_copy(job, src, nb);
+        }
+      }
+      __syncthreads();
+
+      // ------------------------------ phase 6 ------------------------------
+      if (act) {
+        const float ds = sm.dsb[nb];
+        const f16 *Bsrc = (MODE == kDeltaNet) ? sm.Kp : sm.Kt;
+        if (wave < 4) {
+          // diagonal tile of A, then its inverse (a diagonal block of Tinv)
+          const int b = wave;
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            acc = mma32(ld8(&sm.Kp[(16 * b + c16) * KP + 32 * kk + 8 * g]),
+                        ld8(&Bsrc[(16 * b + c16) * KP + 32 * kk + 8 * g]), acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * b + 4 * g + e, col = 16 * b + c16;
+            sm.F[row * AP + col] = col < row ? sm.beta[nb][row] * ds * acc[e] : 0.f;
+          }
+          wave_lds_sync();
+          if (lane < 16) {
+            float x[16];
+            tri16_inverse_column(&sm.F[(16 * b) * AP + 16 * b], AP, lane, x);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) sm.Tm[nb][(16 * b + t) * CP + 16 * b + lane] = h(x[t]);
+          }
+        } else {
+          // off-diagonal tiles of A (the state waves form the scores)
+          for (int job = wave - 4; job < 6; job += 2) {
+            int rt, ct;
+            off_tile(job, rt, ct);
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+              acc = mma32(ld8(&sm.Kp[(16 * rt + c16) * KP + 32 * kk + 8 * g]),
+                          ld8(&Bsrc[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float dt = fmaf(expf(sm.lg[t0 + e]), dbase, acc[e]);
-              kto[nn][m][e] = h(dt * (float)kv[e] * inv);
+              const int row = 16 * rt + 4 * g + e, col = 16 * ct + c16;
+              sm.F[row * AP + col] = sm.beta[nb][row] * ds * acc[e];
             }
           }
         }
+      }
+      __syncthreads();
+
+      // ----------------- phases 7-9: off-diagonal blocks of Tinv -----------------
+      // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, blocks at distance 1, 2, 3
 #pragma unroll
-        for (int nn = 0; nn < 2; ++nn)
+      for (int dist = 1; dist < 4; ++dist) {
+        if (act && wave < 4 - dist) {
+          const int bj = wave, bi = wave + dist;
+          f16 *Tn = sm.Tm[nb];
+          f32x4 y = zero4();
+          for (int bk = bj; bk < bi; ++bk) {
+            f16x4 a, b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a[e] = h(sm.F[(16 * bi + c16) * AP + 16 * bk + 4 * g + e]);
+              b[e] = Tn[(16 * bk + 4 * g + e) * CP + 16 * bj + c16];
+            }
+            y = mma16(a, b, y);
+          }
+          const f32x4 z = mma16(ld4(&Tn[(16 * bi + c16) * CP + 16 * bi + 4 * g]), h4(y), zero4());
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Tn[(16 * bi + 4 * g + e) * CP + 16 * bj + c16] = h(-z[e]);
+        }
+        __syncthreads();
+      }
+    }
+
+    if (writer) {
+      if (MODE == kOsdn && d_final && ptid < DK) {
+        const float dv = nch > 0 ? fexp2(sm.lgC) * sm.d_in[ptid] + sm.dpart[0][ptid] +
+                                       sm.dpart[1][ptid] + sm.dpart[2][ptid]
+                                 : sm.d_in[ptid];
+        d_final[(long)bh * DK + ptid] = dv;
+      }
+      if (MODE != kGiven && log_ratio_sum && ptid == 0) log_ratio_sum[bh] = lr_sum;
+    }
+  } else {
+    // =====================================================================
+    //                              state waves
+    // =====================================================================
+    const int sn = wave - NPREP;          // 16-channel sub-tile
+    const int jcol = j0 + 16 * sn + c16;  // value channel of this lane
+    f32x4 Sacc[8];                        // S^T tiles: rows i = 16 i8 + 4g + e, col jcol
+    f16x8 Sb[4];                          // S^T in the paired k order (K S^T, Q S^T operand)
+#pragma unroll
+    for (int i8 = 0; i8 < 8; ++i8) Sacc[i8] = zero4();
+    if (S0) {
+#pragma unroll
+      for (int i8 = 0; i8 < 8; ++i8) {
+        const float4 s4 = *(const float4 *)(S0 + ((long)bh * 128 + jcol) * DK + 16 * i8 + 4 * g);
+        Sacc[i8] = f32x4{s4.x, s4.y, s4.z, s4.w};
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
+    __syncthreads();
+
+    // Carried from the iteration that prepared the chunk to the one that runs
+    // it: K S^T, Q S^T and the values, all in the result layout (lane: column
+    // jcol, rows 16m + 4g + e).
+    f32x4 KS[4], O[4];
+    f16x4 V[4];
+    f16x8 Rb[2], Xb[2];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      KS[m] = O[m] = zero4();
+      V[m] = f16x4{0, 0, 0, 0};
+    }
+
+    for (int it = 0; it <= nch; ++it) {
+      const int sc = it - 1;       // chunk in the state pass
+      const int cb = sc & 1;
+      const bool act = sc >= 0;
+      const int sL = act ? min(C, T_ - sc * C) : 0;
+      const int nb = it & 1;       // buffer the prep waves are filling
+      const bool pact = it < nch;  // a chunk is being prepared
+
+      // ------------------------------ phase 1 ------------------------------
+      if (act) {
+        // R = diag(beta)(V - K S^T), in the paired k order for Tinv R
+        f16x4 rr[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float4 b4 = *(const float4 *)&sm.beta[cb][16 * m + 4 * g];
+          const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rr[m][e] = h(bb[e] * ((float)V[m][e] - KS[m][e]));
+        }
+        Rb[0] = cat(rr[0], rr[1]);
+        Rb[1] = cat(rr[2], rr[3]);
+      }
+      __syncthreads();
+
+      // ------------------------------ phase 2 ------------------------------
+      if (act) {
+        // X = Tinv R (row blocks m need t pairs 0..m/2), in the paired k order
+        f32x4 X[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 acc = zero4();
+          const f16 *row = &sm.Tm[cb][(16 * m + c16) * CP];
+#pragma unroll
+          for (int qq = 0; qq <= (m >> 1); ++qq) acc = mma32(ldpk(row, 32 * qq, g), Rb[qq], acc);
+          X[m] = acc;
+        }
+        Xb[0] = cat(h4(X[0]), h4(X[1]));
+        Xb[1] = cat(h4(X[2]), h4(X[3]));
+      }
+      if (pact) {
+        // values of the chunk being prepared (staged row-major in Kt), transposed
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          V[m] = h4(mma16(ld4(&sm.Kt[(16 * m + c16) * KP + 16 * sn + 4 * g]), ident, zero4()));
+      }
+      __syncthreads();
+
+      // ------------------------------ phase 3 ------------------------------
+      if (act) {
+        // O = Q S^T + P X, then store o
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f16 *row = &sm.P[cb][(16 * m + c16) * CP];
+#pragma unroll
+          for (int qq = 0; qq <= (m >> 1); ++qq) O[m] = mma32(ldpk(row, 32 * qq, g), Xb[qq], O[m]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * m + 4 * g + e;
+            if (t < sL) o[(tok0 + (long)sc * C + t) * 128 + jcol] = (bf16)O[m][e];
+          }
+        }
+      }
+      __syncthreads();
+
+      // ------------------------------ phase 4 ------------------------------
+      if (act) {
+        // S^T += ds Kt^T X, then the fp16 copy for the next products
+        const float ds = sm.dsb[cb];
+#pragma unroll
+        for (int i8 = 0; i8 < 8; ++i8) {
+          f32x4 u = zero4();
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) u = mma32(ld8(&sm.KtF[cb][i8][qq][lane][0]), Xb[qq], u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Sacc[i8][e] = fmaf(ds, u[e], Sacc[i8][e]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
+      }
+      __syncthreads();
+
+      // ------------------------------ phase 5 ------------------------------
+      if (pact) {
+        if (MODE == kOsdn) {
+          write_keys_itile(6 + sn, nb);
+        } else {
+          const f16 *src = (MODE == kDeltaNet) ? sm.Kp : sm.Kt;
+          for (int job = wave; job < 32; job += 8) write_keys_copy(job, src, nb);
+        }
+      }
+      __syncthreads();
+
+      // ------------------------------ phase 6 ------------------------------
+      if (pact) {
+        const f16 *Bsrc = (MODE == kDeltaNet) ? sm.Kp : sm.Kt;
+        for (int idx = sn; idx < 10; idx += 2) score_tile(idx, Bsrc, nb);
+      }
+      __syncthreads();
+
+      // ------------------------------ phases 7-9 ------------------------------
+      // K S^T (phase 7) and Q S^T (phase 8) of the chunk being prepared, from
+      // the prep copies of K and Q and the state after this iteration's update.
+#pragma unroll
+      for (int dist = 1; dist < 4; ++dist) {
+        if (pact && dist < 3) {
+          const f16 *src = dist == 1 ? sm.Kp : sm.Qp;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const int i = 16 * (2 * wave + nn) + l16;
-            const int t0 = 16 * m + 4 * g4;
-            *(f16x4 *)&sm.KT[i * CP + t0] = kto[nn][m];
+            f32x4 acc = zero4();
+            const f16 *row = &src[(16 * m + c16) * KP];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.Kt[(t0 + e) * KP + i] = kto[nn][m][e];
-          }
-      }
-      __syncthreads();
-      dcur ^= 1;
-    } else if (MODE == kDeltaNet) {
-      // residual ratio of the plain delta rule: rho_t = (1 - beta_t ||k_t||^2)^2
-      if (wave == 0) {
-        const float g = 1.0f - sm.beta[lane] * sm.n[lane];
-        lr_sum += wave_sum(lane < L ? logf(g * g) : 0.f);
-      }
-    } else {
-      __syncthreads();
-    }
-
-    // ================= P3: grams A = beta K Kt^T (strict), P = Q Kt^T (incl.) =================
-    for (int job = wave; job < 20; job += 4) {
-      const bool isA = job < 10;
-      int rt, ct;
-      tri_tile(isA ? job : job - 10, rt, ct);
-      const f16 *src = isA ? sm.K : sm.Q;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const f16x8 a = ld8(&src[(16 * rt + l16) * KP + 32 * kk + 8 * g4]);
-        const f16x8 b = ld8(&Kt[(16 * ct + l16) * KP + 32 * kk + 8 * g4]);
-        acc = mma32(a, b, acc);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * rt + 4 * g4 + e, col = 16 * ct + l16;
-        if (isA) {
-          sm.A[row * AP + col] = col < row ? sm.beta[row] * ds * acc[e] : 0.f;
-        } else {
-          sm.P[row * CP + col] = h(col <= row ? ds * acc[e] : 0.f);
-        }
-      }
-    }
-    __syncthreads();
-
-    // ================= P4: Tinv = (I + A)^-1, 16x16 blocks =================
-    // diagonal blocks: wave w inverts block w, lane c (< 16) solves column c
-    if (lane < 16) {
-      const int base = 16 * wave;
-      float x[16];
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        float acc = (t == lane) ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < t; ++s) acc = fmaf(-sm.A[(base + t) * AP + base + s], x[s], acc);
-        x[t] = acc;
-      }
-#pragma unroll
-      for (int t = 0; t < 16; ++t) sm.Tm[(base + t) * CP + base + lane] = h(x[t]);
-    }
-    __syncthreads();
-    // off-diagonal blocks, by distance from the diagonal:
-    //   T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj
-    auto a_op = [&](int bi, int bk) {  // A block (bi, bk) as 16x16x16 A operand
-      f16x4 a;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = h(sm.A[(16 * bi + l16) * AP + 16 * bk + 4 * g4 + e]);
-      return a;
-    };
-    auto t_bop = [&](int bk, int bj) {  // T block (bk, bj) as B operand (k = row)
-      f16x4 b;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b[e] = sm.Tm[(16 * bk + 4 * g4 + e) * CP + 16 * bj + l16];
-      return b;
-    };
-    auto t_aop = [&](int bi) {  // diagonal T block (bi, bi) as A operand
-      return *(const f16x4 *)&sm.Tm[(16 * bi + l16) * CP + 16 * bi + 4 * g4];
-    };
-    auto finish_block = [&](int bi, int bj, f32x4 y) {
-      const f16x4 yb = {h(y[0]), h(y[1]), h(y[2]), h(y[3])};
-      f32x4 z = mma16(t_aop(bi), yb, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.Tm[(16 * bi + 4 * g4 + e) * CP + 16 * bj + l16] = h(-z[e]);
-    };
-#pragma unroll
-    for (int dist = 1; dist < 4; ++dist) {
-      if (wave < 4 - dist) {
-        const int bj = wave, bi = wave + dist;
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        for (int bk = bj; bk < bi; ++bk) y = mma16(a_op(bi, bk), t_bop(bk, bj), y);
-        finish_block(bi, bj, y);
-      }
-      __syncthreads();
-    }
-
-    // ================= P5: K S^T, Q S^T; R = diag(beta)(V - K S^T) =================
-    f32x4 O[2];
-    {
-      f32x4 KS[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      O[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      O[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const f16x8 ak = ld8(&sm.K[(16 * wave + l16) * KP + 32 * kk + 8 * g4]);
-        const f16x8 aq = ld8(&sm.Q[(16 * wave + l16) * KP + 32 * kk + 8 * g4]);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const f16x8 b = ld8(&sm.S[(16 * n + l16) * KP + 32 * kk + 8 * g4]);
-          KS[n] = mma32(ak, b, KS[n]);
-          O[n] = mma32(aq, b, O[n]);
-        }
-      }
-      const int t0 = 16 * wave + 4 * g4;
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int j = 16 * n + l16;
-        const ushort4 vv = *(const ushort4 *)&sm.VT[j * VP + t0];
-        const float va[4] = {bf2f(vv.x), bf2f(vv.y), bf2f(vv.z), bf2f(vv.w)};
-        f16x4 rr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rr[e] = h(sm.beta[t0 + e] * (va[e] - KS[n][e]));
-        *(f16x4 *)&sm.RT[j * CP + t0] = rr;
-      }
-    }
-    __syncthreads();
-
-    // ================= P6: X = Tinv R =================
-    {
-      const int nk = wave < 2 ? 1 : 2;
-      f32x4 X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      for (int kk = 0; kk < nk; ++kk) {
-        const f16x8 a = ld8(&sm.Tm[(16 * wave + l16) * CP + 32 * kk + 8 * g4]);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const f16x8 b = ld8(&sm.RT[(16 * n + l16) * CP + 32 * kk + 8 * g4]);
-          X[n] = mma32(a, b, X[n]);
-        }
-      }
-      const int t0 = 16 * wave + 4 * g4;
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int j = 16 * n + l16;
-        const f16x4 xx = {h(X[n][0]), h(X[n][1]), h(X[n][2]), h(X[n][3])};
-        *(f16x4 *)&sm.XT[j * CP + t0] = xx;
-      }
-    }
-    __syncthreads();
-
-    // ================= P7: O += P X, store o; S += ds Kt^T X =================
-    {
-      const int nk = wave < 2 ? 1 : 2;
-      for (int kk = 0; kk < nk; ++kk) {
-        const f16x8 a = ld8(&sm.P[(16 * wave + l16) * CP + 32 * kk + 8 * g4]);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const f16x8 b = ld8(&sm.XT[(16 * n + l16) * CP + 32 * kk + 8 * g4]);
-          O[n] = mma32(a, b, O[n]);
-        }
-      }
-      const int t0 = 16 * wave + 4 * g4;
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int j = j0 + 16 * n + l16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (t0 + e < L) o[(tok0 + c0 + t0 + e) * 128 + j] = (bf16)O[n][e];
-      }
-      // state update on this wave's i tiles
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int itile = 2 * wave + mi;
-        f32x4 U[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const f16x8 a = ld8(&KtT[(16 * itile + l16) * CP + 32 * kk + 8 * g4]);
-#pragma unroll
-          for (int n = 0; n < 2; ++n) {
-            const f16x8 b = ld8(&sm.XT[(16 * n + l16) * CP + 32 * kk + 8 * g4]);
-            U[n] = mma32(a, b, U[n]);
+            for (int kk = 0; kk < 4; ++kk) acc = mma32(ldpk(row, 32 * kk, g), Sb[kk], acc);
+            if (dist == 1) KS[m] = acc;
+            else O[m] = acc;
           }
         }
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Sacc[mi][n][e] = fmaf(ds, U[n][e], Sacc[mi][n][e]);
+        __syncthreads();
       }
-      write_state_f16();
     }
-  }
 
-  // ================= outputs after the last chunk =================
-  if (S_final) {
+    if (S_final) {
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int i0 = 16 * (2 * wave + mi) + 4 * g4;
-        const int j = 16 * n + l16;
-        *(float4 *)(S_final + ((long)bh * 128 + j0 + j) * DK + i0) =
-            float4{Sacc[mi][n][0], Sacc[mi][n][1], Sacc[mi][n][2], Sacc[mi][n][3]};
-      }
-  }
-  __syncthreads();
-  if (writer) {
-    if (MODE == kOsdn && d_final && tid < DK) d_final[(long)bh * DK + tid] = sm.d[dcur][tid];
-    if (MODE != kGiven && log_ratio_sum && tid == 0) log_ratio_sum[bh] = lr_sum;
+      for (int i8 = 0; i8 < 8; ++i8)
+        *(float4 *)(S_final + ((long)bh * 128 + jcol) * DK + 16 * i8 + 4 * g) =
+            float4{Sacc[i8][0], Sacc[i8][1], Sacc[i8][2], Sacc[i8][3]};
+    }
   }
 }
 
