@@ -86,7 +86,7 @@ struct Smem {
   float F[C * AP];          // fp32 scratch: key gram -> M, then the gram A
   float Td[4][16][16];      // the walk's 16x16 diagonal-block inverses
   float d_in[DK];           // entry preconditioner of the chunk being prepared
-  float dpart[3][DK];       // partial sums of the next entry preconditioner
+  float dpart[4][DK];       // partial sums of the next entry preconditioner
   float beta[2][C];         // write gates [buf][t]
   float dsb[4];             // write-key scale [buf] (padded to keep 16-byte alignment)
   float r[C], n[C], bv[C], alpha[C], g[C], cc[C], w[C], rhs[C], acc[C];
@@ -102,6 +102,9 @@ __device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mma16(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mma16bf(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // fp32 -> fp16 rounding a materialised fp32 value.  The empty asm keeps the
@@ -109,7 +112,7 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // FMA rounds once, straight to fp16), so equal fp32 values give equal fp16
 // values on every code path -- needed for bitwise-reproducible continuation.
 __device__ __forceinline__ f16 h(float x) {
-  asm volatile("" : "+v"(x));
+  asm("" : "+v"(x));
   return (f16)x;
 }
 __device__ __forceinline__ f16x4 h4(f32x4 v) { return f16x4{h(v[0]), h(v[1]), h(v[2]), h(v[3])}; }
@@ -131,7 +134,7 @@ __device__ __forceinline__ f16x8 cvt8(const uint4 &u) {
   const unsigned short *s = (const unsigned short *)&u;
   f16x8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = h(bf2f(s[e]));
+  for (int e = 0; e < 8; ++e) r[e] = (f16)bf2f(s[e]);
   return r;
 }
 // hardware 2^x and log2 x (about 1 ulp)
@@ -153,42 +156,82 @@ __device__ __forceinline__ void off_tile(int idx, int &rt, int &ct) {
   ct = idx - (rt * (rt - 1)) / 2;
 }
 
-// Column `col` of (I + N)^-1 for a 16x16 strictly-lower N, row-major fp32 in
-// LDS with row stride `ld` (16-byte aligned rows); forward substitution.
-__device__ __forceinline__ void tri16_inverse_column(const float *N, int ld, int col,
-                                                     float (&x)[16]) {
+// Sum over the 4 lanes of an aligned quad (DPP quad permutations); all four
+// lanes receive the same bits.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  return v;
+}
+__device__ __forceinline__ float readlane(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// (I + N)^-1 for a strictly lower 16x16 fp32 block N in LDS (row stride ld;
+// entries on and above the diagonal must be zero), by one wave.  Lanes
+// 4c..4c+3 solve column c by forward substitution: lane q keeps rows q, q+4,
+// q+8, q+12 and their share of each dot product, and quad sums join the
+// shares.  On return x[j] holds row q + 4j of column c.
+__device__ __forceinline__ void tri16_inverse_quad(const float *N, int ld, int lane,
+                                                   float (&x)[4]) {
+  const int col = lane >> 2, q = lane & 3;
+  float nv[16][4];
+#pragma unroll
+  for (int t = 1; t < 16; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nv[t][j] = N[t * ld + q + 4 * j];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = 0.f;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    float a0 = (t == col) ? 1.f : 0.f, a1 = 0.f;
-#pragma unroll
-    for (int s = 0; s < t; s += 4) {
-      const float4 nv = *(const float4 *)&N[t * ld + s];
-      a0 = fmaf(-nv.x, x[s], a0);
-      if (s + 1 < t) a1 = fmaf(-nv.y, x[s + 1], a1);
-      if (s + 2 < t) a0 = fmaf(-nv.z, x[s + 2], a0);
-      if (s + 3 < t) a1 = fmaf(-nv.w, x[s + 3], a1);
+    float p = 0.f;
+    if (t > 0) {
+      const float p0 = fmaf(nv[t][0], x[0], nv[t][1] * x[1]);
+      const float p1 = fmaf(nv[t][2], x[2], nv[t][3] * x[3]);
+      p = quad_sum(p0 + p1);
     }
-    x[t] = a0 + a1;
+    const float xt = (t == col ? 1.f : 0.f) - p;
+    if (q == (t & 3)) x[t >> 2] = xt;
   }
 }
 
+// The kernel body.  Every LDS array comes in through its own restrict
+// pointer, which tells the compiler that a store to one array cannot change
+// another, so loads can be issued ahead of unrelated stores.
 template <int MODE>
-__global__ void __launch_bounds__(NTH)
-osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+__device__ __forceinline__ void fused_body(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const bf16 *__restrict__ kt_in, const bf16 *__restrict__ v,
                    const float *__restrict__ beta, const float *__restrict__ r,
                    const float *__restrict__ d0, const float *__restrict__ S0, float eta,
                    int BH, int T_, bf16 *__restrict__ o, float *__restrict__ S_final,
-                   float *__restrict__ d_final, float *__restrict__ log_ratio_sum) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+                   float *__restrict__ d_final, float *__restrict__ log_ratio_sum,
+    f16 *__restrict__ LKp, f16 *__restrict__ LQp, f16 *__restrict__ LKt,
+           f16 (*__restrict__ LKtF)[8][2][64][8], f16 (*__restrict__ LTm)[C * CP],
+           f16 (*__restrict__ LP)[C * CP], float *__restrict__ LF,
+           float (*__restrict__ LTd)[16][16], float *__restrict__ Ld_in,
+           float (*__restrict__ Ldpart)[DK], float (*__restrict__ Lbeta)[C],
+           float *__restrict__ Ldsb, float *__restrict__ Lr, float *__restrict__ Ln,
+           float *__restrict__ Lbv, float *__restrict__ Lalpha, float *__restrict__ Lg,
+           float *__restrict__ Lcc, float *__restrict__ Lw, float *__restrict__ Lrhs,
+           float *__restrict__ Lacc, float *__restrict__ Llg, float *__restrict__ LlgC,
+           float *__restrict__ Lred) {
   constexpr int NTILE = 128 / DVT;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform role
-  const int c16 = lane & 15;
-  const int g = lane >> 4;
+  // Lane coordinates.  They are re-derived from an opaque copy of the thread
+  // index at the top of every chunk iteration, so that the compiler recomputes
+  // the many lane-dependent LDS addresses and masks of an iteration instead of
+  // hoisting them all out of the loop and running out of registers.
+  int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+  auto refresh_lane = [&]() {
+    int x = tid;
+    asm volatile("" : "+v"(x));
+    lane = x & 63;
+    c16 = lane & 15;
+    g = lane >> 4;
+  };
 
   // Workgroup -> (head, value tile); consecutive workgroup ids go to different
   // XCDs, so the tiles of one head are kept on one XCD to share its L2.
@@ -211,47 +254,66 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   // identity as a 16x16x16 operand: lane (col c16, k 4g+e)
   f16x4 ident;
+  bf16x4 identb;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) ident[e] = (4 * g + e == c16) ? (f16)1.0f : (f16)0.0f;
+  for (int e = 0; e < 4; ++e) {
+    ident[e] = (4 * g + e == c16) ? (f16)1.0f : (f16)0.0f;
+    identb[e] = (4 * g + e == c16) ? (bf16)1.0f : (bf16)0.0f;
+  }
 
   // ------------- prep work any wave can take (chunk in buffer nb) -------------
   // Write keys of i tile n (OSDN): D = Gamma d0 + R (c (.) P), kt = D (.) k / ds,
   // stored as S-update operands (KtF) and row-major (Kt).
   auto write_keys_itile = [&](int n, int nb) {
-    const float inv = 1.0f / sm.dsb[nb];
+    // every LDS operand first, then the products, then the stores
+    const float inv = 1.0f / Ldsb[nb];
+    const float dbase = Ld_in[16 * n + c16];
+    f16x4 kin[4];
+    float4 c4[4], l4[4];
+    f16x8 rrow[6];  // R rows of block m for t pairs 0..m/2
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kin[j] = ld4(&LKp[(16 * j + c16) * KP + 16 * n + 4 * g]);
+      c4[j] = *(const float4 *)&Lcc[16 * j + 4 * g];
+      l4[j] = *(const float4 *)&Llg[16 * j + 4 * g];
+    }
+#pragma unroll
+    for (int m = 0, x = 0; m < 4; ++m)
+#pragma unroll
+      for (int qq = 0; qq <= (m >> 1); ++qq, ++x)
+        rrow[x] = ldpk(&LTm[nb][(16 * m + c16) * CP], 32 * qq, g);
     f32x4 kT[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      kT[j] = mma16(ld4(&sm.Kp[(16 * j + c16) * KP + 16 * n + 4 * g]), ident, zero4());
+    for (int j = 0; j < 4; ++j) kT[j] = mma16(kin[j], ident, zero4());
     f16x8 cP[2];
     {
       f16x4 cpj[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 c4 = *(const float4 *)&sm.cc[16 * j + 4 * g];
-        const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+        const float cv[4] = {c4[j].x, c4[j].y, c4[j].z, c4[j].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) cpj[j][e] = h(kT[j][e] * kT[j][e] * cv[e]);
       }
       cP[0] = cat(cpj[0], cpj[1]);
       cP[1] = cat(cpj[2], cpj[3]);
     }
-    const float dbase = sm.d_in[16 * n + c16];
+    f16x4 kt4[4], kr4[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float4 l4 = *(const float4 *)&sm.lg[16 * m + 4 * g];
-      f32x4 acc = {fexp2(l4.x) * dbase, fexp2(l4.y) * dbase, fexp2(l4.z) * dbase,
-                   fexp2(l4.w) * dbase};
-      const f16 *row = &sm.Tm[nb][(16 * m + c16) * CP];
+    for (int m = 0, x = 0; m < 4; ++m) {
+      f32x4 acc = {fexp2(l4[m].x) * dbase, fexp2(l4[m].y) * dbase, fexp2(l4[m].z) * dbase,
+                   fexp2(l4[m].w) * dbase};
 #pragma unroll
-      for (int qq = 0; qq <= (m >> 1); ++qq) acc = mma32(ldpk(row, 32 * qq, g), cP[qq], acc);
+      for (int qq = 0; qq <= (m >> 1); ++qq, ++x) acc = mma32(rrow[x], cP[qq], acc);
       f32x4 ktv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ktv[e] = acc[e] * kT[m][e] * inv;
-      const f16x4 kt4 = h4(ktv);
-      *(f16x4 *)&sm.KtF[nb][n][m >> 1][lane][4 * (m & 1)] = kt4;
-      const f32x4 tr = mma16(kt4, ident, zero4());
-      *(f16x4 *)&sm.Kt[(16 * m + c16) * KP + 16 * n + 4 * g] = h4(tr);
+      kt4[m] = h4(ktv);
+      kr4[m] = h4(mma16(kt4[m], ident, zero4()));
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      *(f16x4 *)&LKtF[nb][n][m >> 1][lane][4 * (m & 1)] = kt4[m];
+      *(f16x4 *)&LKt[(16 * m + c16) * KP + 16 * n + 4 * g] = kr4[m];
     }
   };
   // Write keys held row-major in `src` (the keys, or given write keys):
@@ -259,50 +321,85 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   auto write_keys_copy = [&](int job, const f16 *src, int nb) {
     const int m = job >> 3, n = job & 7;
     const f32x4 tr = mma16(ld4(&src[(16 * m + c16) * KP + 16 * n + 4 * g]), ident, zero4());
-    *(f16x4 *)&sm.KtF[nb][n][m >> 1][lane][4 * (m & 1)] = h4(tr);
+    *(f16x4 *)&LKtF[nb][n][m >> 1][lane][4 * (m & 1)] = h4(tr);
   };
   // Lower tile idx of the scores P = lower(Q Kt^T) ds.
   auto score_tile = [&](int idx, const f16 *Bsrc, int nb) {
     int rt, ct;
     tri_tile(idx, rt, ct);
-    const float ds = sm.dsb[nb];
+    const float ds = Ldsb[nb];
     f32x4 acc = zero4();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      acc = mma32(ld8(&sm.Qp[(16 * rt + c16) * KP + 32 * kk + 8 * g]),
+      acc = mma32(ld8(&LQp[(16 * rt + c16) * KP + 32 * kk + 8 * g]),
                   ld8(&Bsrc[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * rt + 4 * g + e, col = 16 * ct + c16;
-      sm.P[nb][row * CP + col] = h(col <= row ? ds * acc[e] : 0.f);
+      LP[nb][row * CP + col] = h(col <= row ? ds * acc[e] : 0.f);
+    }
+  };
+
+  // Lower tile `job` of the key gram G = P P^T (P = k (.) k in fp16), raw, into F.
+  auto key_gram_tile = [&](int job) {
+    int rt, ct;
+    tri_tile(job, rt, ct);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const f16x8 a = ld8(&LKp[(16 * rt + c16) * KP + 32 * kk + 8 * g]);
+      const f16x8 b = ld8(&LKp[(16 * ct + c16) * KP + 32 * kk + 8 * g]);
+      acc = mma32(a * a, b * b, acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) LF[(16 * rt + 4 * g + e) * AP + 16 * ct + c16] = acc[e];
+  };
+  // Off-diagonal tile `job` of A = strict_lower(diag(beta) K Kt^T) ds, into F.
+  auto gram_a_off_tile = [&](int job, const f16 *Bsrc, int nb) {
+    int rt, ct;
+    off_tile(job, rt, ct);
+    const float ds = Ldsb[nb];
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      acc = mma32(ld8(&LKp[(16 * rt + c16) * KP + 32 * kk + 8 * g]),
+                  ld8(&Bsrc[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + 4 * g + e, col = 16 * ct + c16;
+      LF[row * AP + col] = Lbeta[nb][row] * ds * acc[e];
     }
   };
 
   // ---------------- initialisation ----------------
   for (int idx = tid; idx < C * CP; idx += NTH) {
-    sm.P[0][idx] = (f16)0.0f;
-    sm.P[1][idx] = (f16)0.0f;
-    sm.Tm[0][idx] = (f16)0.0f;
-    sm.Tm[1][idx] = (f16)0.0f;
+    LP[0][idx] = (f16)0.0f;
+    LP[1][idx] = (f16)0.0f;
+    LTm[0][idx] = (f16)0.0f;
+    LTm[1][idx] = (f16)0.0f;
   }
   for (int i = tid; i < DK; i += NTH)
-    sm.d_in[i] = (MODE == kOsdn && d0) ? d0[(long)bh * DK + i] : 1.0f;
-  if (tid == 0) sm.lgC = 0.f;
+    Ld_in[i] = (MODE == kOsdn && d0) ? d0[(long)bh * DK + i] : 1.0f;
+  if (tid == 0) (*LlgC) = 0.f;
 
   if (wave < NPREP) {
     // =====================================================================
     //                              prep waves
     // =====================================================================
     const int ptid = tid;
-    uint4 pk[3], pq[3], pkt[3], pv;
+    const int lt = ptid - 64;  // loader index of waves 1-5 (0..319)
+    uint4 pk[4], pq[4], pkt[4], pv;
     float pb = 0.f, pr = 1.f;
     float lr_sum = 0.f;  // wave 0: sum over tokens of log rho_t
+    // Global loads of a chunk, by waves 1-5 (wave 0 runs the walk's substitution
+    // meanwhile): k and q (and given write keys) as 1024 pieces of 8 elements,
+    // the value tile as 256 pieces, beta and r.
     auto prep_load = [&](int cc_) {
       const int c0 = cc_ * C;
       const int L = min(C, T_ - c0);
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        const int p = ptid + PTH * u;
+      for (int u = 0; u < 4; ++u) {
+        const int p = lt + 320 * u;
         const int t = p >> 4, piece = p & 15;
         const bool ok = p < 16 * C && t < L;
         const long off = (tok0 + c0 + t) * DK + piece * 8;
@@ -311,22 +408,23 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         if (MODE == kGiven) pkt[u] = ok ? *(const uint4 *)(kt_in + off) : uint4{0, 0, 0, 0};
       }
       {
-        // value tile: 64 rows x 4 pieces of 8 channels
-        const int t = ptid >> 2, piece = ptid & 3;
-        const bool ok = ptid < 4 * C && t < L;
+        const int t = lt >> 2, piece = lt & 3;
+        const bool ok = lt < 4 * C && t < L;
         pv = ok ? *(const uint4 *)(v + (tok0 + c0 + t) * 128 + j0 + piece * 8)
                 : uint4{0, 0, 0, 0};
       }
-      if (ptid < C) {
-        const bool ok = ptid < L;
-        pb = ok ? beta[tok0 + c0 + ptid] : 0.f;
-        pr = (ok && r) ? r[tok0 + c0 + ptid] : 1.f;
+      if (lt < C) {
+        const bool ok = lt < L;
+        pb = ok ? beta[tok0 + c0 + lt] : 0.f;
+        pr = (ok && r) ? r[tok0 + c0 + lt] : 1.f;
       }
     };
-    if (nch > 0) prep_load(0);
+    if (nch > 0 && wave > 0) prep_load(0);
     __syncthreads();
 
     for (int it = 0; it <= nch; ++it) {
+      refresh_lane();
+      const int lt = tid - 64 + (lane - (tid & 63));  // == tid - 64, opaque per iteration
       const int pc = it;  // chunk being prepared
       const int nb = pc & 1;
       const bool act = pc < nch;
@@ -334,36 +432,44 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
       // ------------------------------ phase 1 ------------------------------
       if (act) {
-        if (MODE == kOsdn && pc > 0 && ptid < DK)
-          sm.d_in[ptid] = fexp2(sm.lgC) * sm.d_in[ptid] + sm.dpart[0][ptid] +
-                          sm.dpart[1][ptid] + sm.dpart[2][ptid];
-        float kmax = 0.f;
+        if (wave == 0) {
+          if (MODE == kOsdn && pc > 0) {
+            // entry preconditioner: Gamma_L d of the previous chunk plus its sums
+            const float gL = fexp2((*LlgC));
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
-          const int p = ptid + PTH * u;
-          if (p < 16 * C) {
-            const int t = p >> 4, i0 = (p & 15) * 8;
-            *(f16x8 *)&sm.Kp[t * KP + i0] = cvt8(pk[u]);
-            *(f16x8 *)&sm.Qp[t * KP + i0] = cvt8(pq[u]);
-            if (MODE == kGiven) {
-              const unsigned short *ut = (const unsigned short *)&pkt[u];
+            for (int i = lane; i < DK; i += 64)
+              Ld_in[i] = gL * Ld_in[i] + Ldpart[0][i] + Ldpart[1][i] + Ldpart[2][i] +
+                         Ldpart[3][i];
+          }
+        } else {
+          float kmax = 0.f;
 #pragma unroll
-              for (int e = 0; e < 8; ++e) kmax = fmaxf(kmax, fabsf(bf2f(ut[e])));
+          for (int u = 0; u < 4; ++u) {
+            const int p = lt + 320 * u;
+            if (p < 16 * C) {
+              const int t = p >> 4, i0 = (p & 15) * 8;
+              *(f16x8 *)&LKp[t * KP + i0] = cvt8(pk[u]);
+              *(f16x8 *)&LQp[t * KP + i0] = cvt8(pq[u]);
+              if (MODE == kGiven) {
+                const unsigned short *ut = (const unsigned short *)&pkt[u];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kmax = fmaxf(kmax, fabsf(bf2f(ut[e])));
+              }
             }
           }
-        }
-        if (ptid < 4 * C) {
-          const int t = ptid >> 2, j = (ptid & 3) * 8;
-          *(f16x8 *)&sm.Kt[t * KP + j] = cvt8(pv);
-        }
-        if (ptid < C) {
-          sm.beta[nb][ptid] = pb;
-          sm.r[ptid] = pr;
-        }
-        if (MODE == kGiven) {
+          if (lt < 4 * C) {  // the value tile passes through Kt
+            const int t = lt >> 2, j = (lt & 3) * 8;
+            *(f16x8 *)&LKt[t * KP + j] = cvt8(pv);
+          }
+          if (lt < C) {
+            Lbeta[nb][lt] = pb;
+            Lr[lt] = pr;
+          }
+          if (MODE == kGiven) {
 #pragma unroll
-          for (int m_ = 1; m_ < 64; m_ <<= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, m_));
-          if (lane == 0) sm.red[wave] = kmax;
+            for (int m_ = 1; m_ < 64; m_ <<= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, m_));
+            if (lane == 0) Lred[wave] = kmax;
+          }
         }
       }
       __syncthreads();
@@ -377,9 +483,9 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
           for (int q8 = 0; q8 < 4; ++q8) {
             const int i0 = 32 * g + 8 * q8;
-            const f16x8 kk = ld8(&sm.Kp[t * KP + i0]);
-            const float4 da = *(const float4 *)&sm.d_in[i0];
-            const float4 db = *(const float4 *)&sm.d_in[i0 + 4];
+            const f16x8 kk = ld8(&LKp[t * KP + i0]);
+            const float4 da = *(const float4 *)&Ld_in[i0];
+            const float4 db = *(const float4 *)&Ld_in[i0 + 4];
             const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -394,45 +500,38 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           pa += __shfl_xor(pa, 16);
           pa += __shfl_xor(pa, 32);
           if (g == 0) {
-            sm.n[t] = pn;
-            sm.bv[t] = pa;
-            sm.alpha[t] = (MODE == kOsdn && pn > 0.f) ? eta * sm.beta[nb][t] / pn : 0.f;
+            Ln[t] = pn;
+            Lbv[t] = pa;
+            Lalpha[t] = (MODE == kOsdn && pn > 0.f) ? eta * Lbeta[nb][t] / pn : 0.f;
           }
         } else if (wave == 4) {
           if (MODE == kOsdn) {
             // lg[t] = sum_{m<t} log2 r_m (clamped so that r = 0 stays finite)
-            const float lr = fmaxf(flog2(sm.r[lane]), -126.f);
+            const float lr = fmaxf(flog2(Lr[lane]), -126.f);
             float incl = lr;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
               const float y = __shfl_up(incl, off);
               if (lane >= off) incl += y;
             }
-            sm.lg[lane + 1] = incl;
-            if (lane == 0) sm.lg[0] = 0.f;
+            Llg[lane + 1] = incl;
+            if (lane == 0) Llg[0] = 0.f;
           }
         } else {
-          float dm = fmaxf(sm.d_in[lane], sm.d_in[lane + 64]);
+          float dm = fmaxf(Ld_in[lane], Ld_in[lane + 64]);
 #pragma unroll
           for (int m_ = 1; m_ < 64; m_ <<= 1) dm = fmaxf(dm, __shfl_xor(dm, m_));
           if (lane == 0)
-            sm.dsb[nb] = (MODE == kOsdn && dm > 0.f) ? fexp2(ceilf(flog2(dm))) : 1.0f;
+            Ldsb[nb] = (MODE == kOsdn && dm > 0.f) ? fexp2(ceilf(flog2(dm))) : 1.0f;
         }
         if (MODE == kOsdn) {
-          // key gram G = P P^T (P = k (.) k in fp16), lower tiles -> F (raw)
-          for (int job = wave; job < 10; job += NPREP) {
-            int rt, ct;
-            tri_tile(job, rt, ct);
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-              const f16x8 a = ld8(&sm.Kp[(16 * rt + c16) * KP + 32 * kk + 8 * g]);
-              const f16x8 b = ld8(&sm.Kp[(16 * ct + c16) * KP + 32 * kk + 8 * g]);
-              acc = mma32(a * a, b * b, acc);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              sm.F[(16 * rt + 4 * g + e) * AP + 16 * ct + c16] = acc[e];
+          // key gram tiles 0-7 (the state waves take 8 and 9)
+          if (wave < 4) key_gram_tile(wave);
+          else if (wave == 4) key_gram_tile(4);
+          else {
+            key_gram_tile(5);
+            key_gram_tile(6);
+            key_gram_tile(7);
           }
         }
       }
@@ -444,60 +543,95 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           // given write keys, rescaled by a power of two into fp16 range
           float km = 0.f;
 #pragma unroll
-          for (int w_ = 0; w_ < NPREP; ++w_) km = fmaxf(km, sm.red[w_]);
+          for (int w_ = 1; w_ < NPREP; ++w_) km = fmaxf(km, Lred[w_]);
           const float ds = km > 0.f ? fexp2(ceilf(flog2(km))) : 1.0f;
           const float inv = 1.0f / ds;
-          if (ptid == 0) sm.dsb[nb] = ds;
+          if (ptid == 0) Ldsb[nb] = ds;
 #pragma unroll
-          for (int u = 0; u < 3; ++u) {
-            const int p = ptid + PTH * u;
-            if (p < 16 * C) {
+          for (int u = 0; u < 4; ++u) {
+            const int p = lt + 320 * u;
+            if (wave > 0 && p < 16 * C) {
               const int t = p >> 4, i0 = (p & 15) * 8;
               const unsigned short *ut = (const unsigned short *)&pkt[u];
               f16x8 hv;
 #pragma unroll
               for (int e = 0; e < 8; ++e) hv[e] = h(bf2f(ut[e]) * inv);
-              *(f16x8 *)&sm.Kt[t * KP + i0] = hv;
+              *(f16x8 *)&LKt[t * KP + i0] = hv;
             }
           }
         } else if (MODE == kOsdn) {
           if (wave < 4) {
-            // diagonal block b of M, scaled in place, then its inverse
-            const int b = wave;
+            // diagonal block b of M, scaled in place (a lane keeps column s and
+            // rows 16b + g + 4u), then its inverse
+            const int b = wave, s = 16 * b + c16;
+            const float as = Lalpha[s], ls = Llg[s + 1];
+            float bt[4], lt[4], fv[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              const int idx = lane + 64 * u;
-              const int tt = idx >> 4, ss = idx & 15;
-              const int t = 16 * b + tt, s = 16 * b + ss;
-              float val = 0.f;
-              if (ss < tt)
-                val = sm.beta[nb][t] * sm.alpha[s] * fexp2(sm.lg[t] - sm.lg[s + 1]) *
-                      sm.F[t * AP + s];
-              sm.F[t * AP + s] = val;
+              const int t = 16 * b + g + 4 * u;
+              bt[u] = Lbeta[nb][t];
+              lt[u] = Llg[t];
+              fv[u] = LF[t * AP + s];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int t = 16 * b + g + 4 * u;
+              LF[t * AP + s] = c16 < g + 4 * u ? bt[u] * as * fexp2(lt[u] - ls) * fv[u] : 0.f;
             }
             wave_lds_sync();
-            if (lane < 16) {
-              float x[16];
-              tri16_inverse_column(&sm.F[(16 * b) * AP + 16 * b], AP, lane, x);
+            float x[4];
+            tri16_inverse_quad(&LF[(16 * b) * AP + 16 * b], AP, lane, x);
 #pragma unroll
-              for (int t = 0; t < 16; ++t) sm.Td[b][t][lane] = x[t];
-            }
+            for (int j = 0; j < 4; ++j) LTd[b][(lane & 3) + 4 * j][lane >> 2] = x[j];
           } else {
-            // off-diagonal blocks of M (a thread keeps one column s), and the rhs
+            // off-diagonal blocks of M: a thread keeps column sc of each tile and
+            // rows r0, r0 + 8; and the rhs
             const int l2 = ptid - 256;  // 0..127
+            const int sc = l2 & 15, r0 = l2 >> 4;
+            float as[3], ls[3], bt[12], lt[12], fv[12];
+#pragma unroll
+            for (int ct = 0; ct < 3; ++ct) {
+              as[ct] = Lalpha[16 * ct + sc];
+              ls[ct] = Llg[16 * ct + sc + 1];
+            }
 #pragma unroll
             for (int u = 0; u < 12; ++u) {
-              const int idx = l2 + 128 * u;  // < 1536
               int rt, ct;
-              off_tile(idx >> 8, rt, ct);
-              const int t = 16 * rt + ((idx >> 4) & 15), s = 16 * ct + (idx & 15);
-              sm.F[t * AP + s] *= sm.beta[nb][t] * sm.alpha[s] * fexp2(sm.lg[t] - sm.lg[s + 1]);
+              off_tile(u >> 1, rt, ct);
+              const int t = 16 * rt + r0 + 8 * (u & 1), s = 16 * ct + sc;
+              bt[u] = Lbeta[nb][t];
+              lt[u] = Llg[t];
+              fv[u] = LF[t * AP + s];
             }
-            if (l2 < C) sm.rhs[l2] = 1.0f - sm.beta[nb][l2] * fexp2(sm.lg[l2]) * sm.bv[l2];
+            float rb = 0.f, rl = 0.f, rv = 0.f;
+            if (l2 < C) {
+              rb = Lbeta[nb][l2];
+              rl = Llg[l2];
+              rv = Lbv[l2];
+            }
+#pragma unroll
+            for (int u = 0; u < 12; ++u) {
+              int rt, ct;
+              off_tile(u >> 1, rt, ct);
+              const int t = 16 * rt + r0 + 8 * (u & 1), s = 16 * ct + sc;
+              LF[t * AP + s] = fv[u] * (bt[u] * as[ct] * fexp2(lt[u] - ls[ct]));
+            }
+            if (l2 < C) Lrhs[l2] = 1.0f - rb * fexp2(rl) * rv;
+            // R_{t,s} = 2^(lg_t - lg_{s+1}) (s < t) for the write keys, into the
+            // inverse buffer being prepared; a thread keeps column s
+            f16 *R16 = LTm[nb];
+            const int s = l2 & 63;
+            const float lgs = Llg[s + 1];
+            float lgt[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) lgt[u] = Llg[(l2 >> 6) + 2 * u];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+              const int t = (l2 >> 6) + 2 * u;
+              R16[t * CP + s] = h(s < t ? fexp2(lgt[u] - lgs) : 0.f);
+            }
           }
         }
-        // prefetch the next chunk (every staging register has been consumed)
-        if (pc + 1 < nch) prep_load(pc + 1);
       }
       __syncthreads();
 
@@ -505,63 +639,55 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (act) {
         if (wave == 0) {
           if (MODE == kOsdn) {
-            // blocked forward substitution of (I + M) g = rhs, lanes = tokens
-            const int t = lane;
-            float a = sm.rhs[t];
+            // blocked forward substitution of (I + M) g = rhs, lanes = tokens;
+            // the 16 values of a block reach every lane through lane reads
+            const int t = lane, bt = t >> 4;
+            float tdrow[16], mrow[3][16];
+#pragma unroll
+            for (int u = 0; u < 16; u += 4) {
+              const float4 tv = *(const float4 *)&LTd[bt][t & 15][u];
+              tdrow[u] = tv.x, tdrow[u + 1] = tv.y, tdrow[u + 2] = tv.z, tdrow[u + 3] = tv.w;
+#pragma unroll
+              for (int b = 0; b < 3; ++b) {
+                const float4 mv = *(const float4 *)&LF[t * AP + 16 * b + u];
+                mrow[b][u] = mv.x, mrow[b][u + 1] = mv.y, mrow[b][u + 2] = mv.z,
+                mrow[b][u + 3] = mv.w;
+              }
+            }
+            const float alpha_t = Lalpha[t], lg_next = Llg[t + 1], lg_end = Llg[pL];
+            float a = Lrhs[t];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-              sm.acc[t] = a;
-              wave_lds_sync();
-              if ((t >> 4) == b) {
-                const float *row = &sm.Td[b][t & 15][0];
-                float y0 = 0.f, y1 = 0.f;
+              float y0 = 0.f, y1 = 0.f;
 #pragma unroll
-                for (int u = 0; u < 16; u += 4) {
-                  const float4 tv = *(const float4 *)&row[u];
-                  const float4 av = *(const float4 *)&sm.acc[16 * b + u];
-                  y0 = fmaf(tv.x, av.x, y0);
-                  y1 = fmaf(tv.y, av.y, y1);
-                  y0 = fmaf(tv.z, av.z, y0);
-                  y1 = fmaf(tv.w, av.w, y1);
-                }
-                a = y0 + y1;
-                sm.g[t] = a;
+              for (int j = 0; j < 16; j += 2) {
+                y0 = fmaf(tdrow[j], readlane(a, 16 * b + j), y0);
+                y1 = fmaf(tdrow[j + 1], readlane(a, 16 * b + j + 1), y1);
               }
-              wave_lds_sync();
-              if ((t >> 4) > b) {
-                float y0 = 0.f, y1 = 0.f;
+              if (bt == b) a = y0 + y1;
+              if (b < 3) {
+                float z0 = 0.f, z1 = 0.f;
 #pragma unroll
-                for (int u = 0; u < 16; u += 4) {
-                  const float4 mv = *(const float4 *)&sm.F[t * AP + 16 * b + u];
-                  const float4 gv = *(const float4 *)&sm.g[16 * b + u];
-                  y0 = fmaf(mv.x, gv.x, y0);
-                  y1 = fmaf(mv.y, gv.y, y1);
-                  y0 = fmaf(mv.z, gv.z, y0);
-                  y1 = fmaf(mv.w, gv.w, y1);
+                for (int j = 0; j < 16; j += 2) {
+                  z0 = fmaf(mrow[b][j], readlane(a, 16 * b + j), z0);
+                  z1 = fmaf(mrow[b][j + 1], readlane(a, 16 * b + j + 1), z1);
                 }
-                a -= y0 + y1;
+                if (bt > b) a -= z0 + z1;
               }
-              wave_lds_sync();
             }
             // a == g_t == 1 - beta_t a_t
-            const float cct = sm.alpha[t] * a;
-            sm.cc[t] = cct;
-            sm.w[t] = t < pL ? fexp2(sm.lg[pL] - sm.lg[t + 1]) * cct : 0.f;
-            if (lane == 0) sm.lgC = sm.lg[pL];
+            const float cct = alpha_t * a;
+            Lcc[t] = cct;
+            Lw[t] = t < pL ? fexp2(lg_end - lg_next) * cct : 0.f;
+            if (lane == 0) (*LlgC) = lg_end;
             lr_sum += wave_sum(t < pL ? logf(a * a) : 0.f);
           } else if (MODE == kDeltaNet) {
-            const float gd = 1.0f - sm.beta[nb][lane] * sm.n[lane];
+            const float gd = 1.0f - Lbeta[nb][lane] * Ln[lane];
             lr_sum += wave_sum(lane < pL ? logf(gd * gd) : 0.f);
           }
-        } else if (MODE == kOsdn) {
-          // R_{t,s} (s < t) for the write keys, into the inverse buffer being
-          // prepared; a thread keeps one column s
-          f16 *R16 = sm.Tm[nb];
-          const int l5 = ptid - 64;  // 0..319
-          for (int idx = l5; idx < C * C; idx += 320) {
-            const int t = idx >> 6, s = idx & 63;
-            R16[t * CP + s] = h(s < t ? fexp2(sm.lg[t] - sm.lg[s + 1]) : 0.f);
-          }
+        } else if (pc + 1 < nch) {
+          // prefetch the next chunk (every staging register has been consumed)
+          prep_load(pc + 1);
         }
       }
       __syncthreads();
@@ -570,22 +696,31 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (act) {
         if (MODE == kOsdn) {
           write_keys_itile(wave, nb);  // i tiles 0..5; the state waves take 6 and 7
-          // next entry preconditioner, partial sums over thirds of the chunk
-          const int i = ptid & 127, part = ptid >> 7;
-          const int s_lo = part == 0 ? 0 : part == 1 ? 22 : 43;
-          const int s_hi = part == 0 ? 22 : part == 1 ? 43 : 64;
-          float a0 = 0.f, a1 = 0.f;
-          for (int s = s_lo; s < s_hi; s += 2) {
-            const float x0 = (float)sm.Kp[s * KP + i];
-            a0 = fmaf(sm.w[s], x0 * x0, a0);
-            if (s + 1 < s_hi) {
-              const float x1 = (float)sm.Kp[(s + 1) * KP + i];
-              a1 = fmaf(sm.w[s + 1], x1 * x1, a1);
+          // next entry preconditioner: waves 0-3 sum quarters of the chunk, a
+          // thread keeps two dimensions
+          if (wave < 4) {
+            const int i = 2 * lane, part = wave;
+            float4 w4[4];
+            typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+            f16x2 kx[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) kx[u] = *(const f16x2 *)&LKp[(16 * part + u) * KP + i];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) w4[u] = *(const float4 *)&Lw[16 * part + 4 * u];
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+              const float ws = u % 4 == 0 ? w4[u / 4].x : u % 4 == 1 ? w4[u / 4].y
+                             : u % 4 == 2 ? w4[u / 4].z : w4[u / 4].w;
+              const float x0 = (float)kx[u][0], x1 = (float)kx[u][1];
+              a0 = fmaf(ws, x0 * x0, a0);
+              a1 = fmaf(ws, x1 * x1, a1);
             }
+            Ldpart[part][i] = a0;
+            Ldpart[part][i + 1] = a1;
           }
-          sm.dpart[part][i] = a0 + a1;
         } else {
-          const f16 *src = (MODE == kDeltaNet) ? sm.Kp : sm.Kt;
+          const f16 *src = (MODE == kDeltaNet) ? LKp : LKt;
           for (int job = wave; job < 32; job += 8) write_keys_copy(job, src, nb);
         }
       }
@@ -593,61 +728,54 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
       // ------------------------------ phase 6 ------------------------------
       if (act) {
-        const float ds = sm.dsb[nb];
-        const f16 *Bsrc = (MODE == kDeltaNet) ? sm.Kp : sm.Kt;
+        const float ds = Ldsb[nb];
+        const f16 *Bsrc = (MODE == kDeltaNet) ? LKp : LKt;
         if (wave < 4) {
           // diagonal tile of A, then its inverse (a diagonal block of Tinv)
           const int b = wave;
           f32x4 acc = zero4();
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
-            acc = mma32(ld8(&sm.Kp[(16 * b + c16) * KP + 32 * kk + 8 * g]),
+            acc = mma32(ld8(&LKp[(16 * b + c16) * KP + 32 * kk + 8 * g]),
                         ld8(&Bsrc[(16 * b + c16) * KP + 32 * kk + 8 * g]), acc);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = 16 * b + 4 * g + e, col = 16 * b + c16;
-            sm.F[row * AP + col] = col < row ? sm.beta[nb][row] * ds * acc[e] : 0.f;
+            LF[row * AP + col] = col < row ? Lbeta[nb][row] * ds * acc[e] : 0.f;
           }
           wave_lds_sync();
-          if (lane < 16) {
-            float x[16];
-            tri16_inverse_column(&sm.F[(16 * b) * AP + 16 * b], AP, lane, x);
+          float x[4];
+          tri16_inverse_quad(&LF[(16 * b) * AP + 16 * b], AP, lane, x);
 #pragma unroll
-            for (int t = 0; t < 16; ++t) sm.Tm[nb][(16 * b + t) * CP + 16 * b + lane] = h(x[t]);
-          }
+          for (int j = 0; j < 4; ++j)
+            LTm[nb][(16 * b + (lane & 3) + 4 * j) * CP + 16 * b + (lane >> 2)] = h(x[j]);
         } else {
-          // off-diagonal tiles of A (the state waves form the scores)
-          for (int job = wave - 4; job < 6; job += 2) {
-            int rt, ct;
-            off_tile(job, rt, ct);
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-              acc = mma32(ld8(&sm.Kp[(16 * rt + c16) * KP + 32 * kk + 8 * g]),
-                          ld8(&Bsrc[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int row = 16 * rt + 4 * g + e, col = 16 * ct + c16;
-              sm.F[row * AP + col] = sm.beta[nb][row] * ds * acc[e];
-            }
-          }
+          // score tiles 0-3 (the state waves form the off-diagonal tiles of A)
+          score_tile(2 * (wave - 4), Bsrc, nb);
+          score_tile(2 * (wave - 4) + 1, Bsrc, nb);
         }
       }
       __syncthreads();
 
       // ----------------- phases 7-9: off-diagonal blocks of Tinv -----------------
-      // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, blocks at distance 1, 2, 3
+      // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, blocks at distance 1, 2, 3; the
+      // waves a level leaves idle form score tiles 4-9
 #pragma unroll
       for (int dist = 1; dist < 4; ++dist) {
+        if (act && wave >= 4 - dist) {
+          const f16 *Bsrc = (MODE == kDeltaNet) ? LKp : LKt;
+          if (dist == 1) score_tile(1 + wave, Bsrc, nb);                  // waves 3-5
+          if (dist == 2 && wave <= 4) score_tile(5 + wave, Bsrc, nb);     // waves 2-4
+        }
         if (act && wave < 4 - dist) {
           const int bj = wave, bi = wave + dist;
-          f16 *Tn = sm.Tm[nb];
+          f16 *Tn = LTm[nb];
           f32x4 y = zero4();
           for (int bk = bj; bk < bi; ++bk) {
             f16x4 a, b;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              a[e] = h(sm.F[(16 * bi + c16) * AP + 16 * bk + 4 * g + e]);
+              a[e] = h(LF[(16 * bi + c16) * AP + 16 * bk + 4 * g + e]);
               b[e] = Tn[(16 * bk + 4 * g + e) * CP + 16 * bj + c16];
             }
             y = mma16(a, b, y);
@@ -662,9 +790,9 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
     if (writer) {
       if (MODE == kOsdn && d_final && ptid < DK) {
-        const float dv = nch > 0 ? fexp2(sm.lgC) * sm.d_in[ptid] + sm.dpart[0][ptid] +
-                                       sm.dpart[1][ptid] + sm.dpart[2][ptid]
-                                 : sm.d_in[ptid];
+        const float dv = nch > 0 ? fexp2((*LlgC)) * Ld_in[ptid] + Ldpart[0][ptid] +
+                                       Ldpart[1][ptid] + Ldpart[2][ptid] + Ldpart[3][ptid]
+                                 : Ld_in[ptid];
         d_final[(long)bh * DK + ptid] = dv;
       }
       if (MODE != kGiven && log_ratio_sum && ptid == 0) log_ratio_sum[bh] = lr_sum;
@@ -703,6 +831,8 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
 
     for (int it = 0; it <= nch; ++it) {
+      refresh_lane();
+      const int jcol = j0 + 16 * sn + c16;
       const int sc = it - 1;       // chunk in the state pass
       const int cb = sc & 1;
       const bool act = sc >= 0;
@@ -716,7 +846,7 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         f16x4 rr[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float4 b4 = *(const float4 *)&sm.beta[cb][16 * m + 4 * g];
+          const float4 b4 = *(const float4 *)&Lbeta[cb][16 * m + 4 * g];
           const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) rr[m][e] = h(bb[e] * ((float)V[m][e] - KS[m][e]));
@@ -733,7 +863,7 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           f32x4 acc = zero4();
-          const f16 *row = &sm.Tm[cb][(16 * m + c16) * CP];
+          const f16 *row = &LTm[cb][(16 * m + c16) * CP];
 #pragma unroll
           for (int qq = 0; qq <= (m >> 1); ++qq) acc = mma32(ldpk(row, 32 * qq, g), Rb[qq], acc);
           X[m] = acc;
@@ -741,27 +871,30 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         Xb[0] = cat(h4(X[0]), h4(X[1]));
         Xb[1] = cat(h4(X[2]), h4(X[3]));
       }
+      if (pact && MODE == kOsdn) key_gram_tile(8 + sn);
       if (pact) {
         // values of the chunk being prepared (staged row-major in Kt), transposed
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          V[m] = h4(mma16(ld4(&sm.Kt[(16 * m + c16) * KP + 16 * sn + 4 * g]), ident, zero4()));
+          V[m] = h4(mma16(ld4(&LKt[(16 * m + c16) * KP + 16 * sn + 4 * g]), ident, zero4()));
       }
       __syncthreads();
 
       // ------------------------------ phase 3 ------------------------------
       if (act) {
-        // O = Q S^T + P X, then store o
+        // O = Q S^T + P X, rounded to bf16, then turned through the identity so
+        // that a lane holds 4 consecutive channels of one token (8-byte stores)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const f16 *row = &sm.P[cb][(16 * m + c16) * CP];
+          const f16 *row = &LP[cb][(16 * m + c16) * CP];
 #pragma unroll
           for (int qq = 0; qq <= (m >> 1); ++qq) O[m] = mma32(ldpk(row, 32 * qq, g), Xb[qq], O[m]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = 16 * m + 4 * g + e;
-            if (t < sL) o[(tok0 + (long)sc * C + t) * 128 + jcol] = (bf16)O[m][e];
-          }
+          const bf16x4 ob = {(bf16)O[m][0], (bf16)O[m][1], (bf16)O[m][2], (bf16)O[m][3]};
+          const f32x4 ot = mma16bf(ob, identb, zero4());
+          const int t = 16 * m + c16;
+          if (t < sL)
+            *(bf16x4 *)(o + (tok0 + (long)sc * C + t) * 128 + j0 + 16 * sn + 4 * g) =
+                bf16x4{(bf16)ot[0], (bf16)ot[1], (bf16)ot[2], (bf16)ot[3]};
         }
       }
       __syncthreads();
@@ -769,12 +902,12 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       // ------------------------------ phase 4 ------------------------------
       if (act) {
         // S^T += ds Kt^T X, then the fp16 copy for the next products
-        const float ds = sm.dsb[cb];
+        const float ds = Ldsb[cb];
 #pragma unroll
         for (int i8 = 0; i8 < 8; ++i8) {
           f32x4 u = zero4();
 #pragma unroll
-          for (int qq = 0; qq < 2; ++qq) u = mma32(ld8(&sm.KtF[cb][i8][qq][lane][0]), Xb[qq], u);
+          for (int qq = 0; qq < 2; ++qq) u = mma32(ld8(&LKtF[cb][i8][qq][lane][0]), Xb[qq], u);
 #pragma unroll
           for (int e = 0; e < 4; ++e) Sacc[i8][e] = fmaf(ds, u[e], Sacc[i8][e]);
         }
@@ -788,7 +921,7 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         if (MODE == kOsdn) {
           write_keys_itile(6 + sn, nb);
         } else {
-          const f16 *src = (MODE == kDeltaNet) ? sm.Kp : sm.Kt;
+          const f16 *src = (MODE == kDeltaNet) ? LKp : LKt;
           for (int job = wave; job < 32; job += 8) write_keys_copy(job, src, nb);
         }
       }
@@ -796,8 +929,8 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
       // ------------------------------ phase 6 ------------------------------
       if (pact) {
-        const f16 *Bsrc = (MODE == kDeltaNet) ? sm.Kp : sm.Kt;
-        for (int idx = sn; idx < 10; idx += 2) score_tile(idx, Bsrc, nb);
+        const f16 *Bsrc = (MODE == kDeltaNet) ? LKp : LKt;
+        for (int job = sn; job < 6; job += 2) gram_a_off_tile(job, Bsrc, nb);
       }
       __syncthreads();
 
@@ -807,7 +940,7 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
       for (int dist = 1; dist < 4; ++dist) {
         if (pact && dist < 3) {
-          const f16 *src = dist == 1 ? sm.Kp : sm.Qp;
+          const f16 *src = dist == 1 ? LKp : LQp;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             f32x4 acc = zero4();
@@ -829,6 +962,22 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             float4{Sacc[i8][0], Sacc[i8][1], Sacc[i8][2], Sacc[i8][3]};
     }
   }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(NTH)
+osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+                   const bf16 *__restrict__ kt_in, const bf16 *__restrict__ v,
+                   const float *__restrict__ beta, const float *__restrict__ r,
+                   const float *__restrict__ d0, const float *__restrict__ S0, float eta,
+                   int BH, int T_, bf16 *__restrict__ o, float *__restrict__ S_final,
+                   float *__restrict__ d_final, float *__restrict__ log_ratio_sum) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+  fused_body<MODE>(q, k, kt_in, v, beta, r, d0, S0, eta, BH, T_, o, S_final, d_final,
+                   log_ratio_sum, sm.Kp, sm.Qp, sm.Kt, sm.KtF, sm.Tm, sm.P, sm.F, sm.Td, sm.d_in,
+                   sm.dpart, sm.beta, sm.dsb, sm.r, sm.n, sm.bv, sm.alpha, sm.g, sm.cc, sm.w,
+                   sm.rhs, sm.acc, sm.lg, &sm.lgC, sm.red);
 }
 
 template <int MODE>
