@@ -72,7 +72,11 @@ constexpr int KP = 136;     // padded row (halves) of [C][DK] tiles
 constexpr int CP = 72;      // padded row (halves) of [C][C] tiles
 constexpr int AP = 68;      // padded row (floats) of the fp32 [C][C] scratch
 
-enum Mode { kOsdn = 0, kDeltaNet = 1, kGiven = 2 };
+// kOsdn: the whole forward; kDeltaNet: the same with kt = k; kGiven: the
+// chunkwise pass with kt read from memory; kScan: the preconditioner walk
+// alone, writing kt (and optionally d_t and log rho_t) to memory.
+enum Mode { kOsdn = 0, kDeltaNet = 1, kGiven = 2, kScan = 3 };
+constexpr bool walk_mode(int m) { return m == kOsdn || m == kScan; }
 
 struct Smem {
   f16 Kp[C * KP];           // keys of the chunk being prepared [t][i]
@@ -205,7 +209,8 @@ __device__ __forceinline__ void fused_body(
                    const float *__restrict__ beta, const float *__restrict__ r,
                    const float *__restrict__ d0, const float *__restrict__ S0, float eta,
                    int BH, int T_, bf16 *__restrict__ o, float *__restrict__ S_final,
-                   float *__restrict__ d_final, float *__restrict__ log_ratio_sum,
+                   float *__restrict__ d_final, float *__restrict__ log_ratio_sum, bf16 *__restrict__ kt_out,
+    float *__restrict__ d_all, float *__restrict__ log_ratio,
     f16 *__restrict__ LKp, f16 *__restrict__ LQp, f16 *__restrict__ LKt,
            f16 (*__restrict__ LKtF)[8][2][64][8], f16 (*__restrict__ LTm)[C * CP],
            f16 (*__restrict__ LP)[C * CP], float *__restrict__ LF,
@@ -216,7 +221,7 @@ __device__ __forceinline__ void fused_body(
            float *__restrict__ Lcc, float *__restrict__ Lw, float *__restrict__ Lrhs,
            float *__restrict__ Lacc, float *__restrict__ Llg, float *__restrict__ LlgC,
            float *__restrict__ Lred) {
-  constexpr int NTILE = 128 / DVT;
+  constexpr int NTILE = MODE == kScan ? 1 : 128 / DVT;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform role
@@ -379,7 +384,7 @@ __device__ __forceinline__ void fused_body(
     LTm[1][idx] = (f16)0.0f;
   }
   for (int i = tid; i < DK; i += NTH)
-    Ld_in[i] = (MODE == kOsdn && d0) ? d0[(long)bh * DK + i] : 1.0f;
+    Ld_in[i] = (walk_mode(MODE) && d0) ? d0[(long)bh * DK + i] : 1.0f;
   if (tid == 0) (*LlgC) = 0.f;
 
   if (wave < NPREP) {
@@ -404,10 +409,10 @@ __device__ __forceinline__ void fused_body(
         const bool ok = p < 16 * C && t < L;
         const long off = (tok0 + c0 + t) * DK + piece * 8;
         pk[u] = ok ? *(const uint4 *)(k + off) : uint4{0, 0, 0, 0};
-        pq[u] = ok ? *(const uint4 *)(q + off) : uint4{0, 0, 0, 0};
+        if (MODE != kScan) pq[u] = ok ? *(const uint4 *)(q + off) : uint4{0, 0, 0, 0};
         if (MODE == kGiven) pkt[u] = ok ? *(const uint4 *)(kt_in + off) : uint4{0, 0, 0, 0};
       }
-      {
+      if (MODE != kScan) {
         const int t = lt >> 2, piece = lt & 3;
         const bool ok = lt < 4 * C && t < L;
         pv = ok ? *(const uint4 *)(v + (tok0 + c0 + t) * 128 + j0 + piece * 8)
@@ -449,7 +454,7 @@ __device__ __forceinline__ void fused_body(
             if (p < 16 * C) {
               const int t = p >> 4, i0 = (p & 15) * 8;
               *(f16x8 *)&LKp[t * KP + i0] = cvt8(pk[u]);
-              *(f16x8 *)&LQp[t * KP + i0] = cvt8(pq[u]);
+              if (MODE != kScan) *(f16x8 *)&LQp[t * KP + i0] = cvt8(pq[u]);
               if (MODE == kGiven) {
                 const unsigned short *ut = (const unsigned short *)&pkt[u];
 #pragma unroll
@@ -457,7 +462,7 @@ __device__ __forceinline__ void fused_body(
               }
             }
           }
-          if (lt < 4 * C) {  // the value tile passes through Kt
+          if (MODE != kScan && lt < 4 * C) {  // the value tile passes through Kt
             const int t = lt >> 2, j = (lt & 3) * 8;
             *(f16x8 *)&LKt[t * KP + j] = cvt8(pv);
           }
@@ -502,10 +507,10 @@ __device__ __forceinline__ void fused_body(
           if (g == 0) {
             Ln[t] = pn;
             Lbv[t] = pa;
-            Lalpha[t] = (MODE == kOsdn && pn > 0.f) ? eta * Lbeta[nb][t] / pn : 0.f;
+            Lalpha[t] = (walk_mode(MODE) && pn > 0.f) ? eta * Lbeta[nb][t] / pn : 0.f;
           }
         } else if (wave == 4) {
-          if (MODE == kOsdn) {
+          if (walk_mode(MODE)) {
             // lg[t] = sum_{m<t} log2 r_m (clamped so that r = 0 stays finite)
             const float lr = fmaxf(flog2(Lr[lane]), -126.f);
             float incl = lr;
@@ -524,7 +529,7 @@ __device__ __forceinline__ void fused_body(
           if (lane == 0)
             Ldsb[nb] = (MODE == kOsdn && dm > 0.f) ? fexp2(ceilf(flog2(dm))) : 1.0f;
         }
-        if (MODE == kOsdn) {
+        if (walk_mode(MODE)) {
           // key gram tiles 0-7 (the state waves take 8 and 9)
           if (wave < 4) key_gram_tile(wave);
           else if (wave == 4) key_gram_tile(4);
@@ -559,7 +564,7 @@ __device__ __forceinline__ void fused_body(
               *(f16x8 *)&LKt[t * KP + i0] = hv;
             }
           }
-        } else if (MODE == kOsdn) {
+        } else if (walk_mode(MODE)) {
           if (wave < 4) {
             // diagonal block b of M, scaled in place (a lane keeps column s and
             // rows 16b + g + 4u), then its inverse
@@ -617,6 +622,7 @@ __device__ __forceinline__ void fused_body(
               LF[t * AP + s] = fv[u] * (bt[u] * as[ct] * fexp2(lt[u] - ls[ct]));
             }
             if (l2 < C) Lrhs[l2] = 1.0f - rb * fexp2(rl) * rv;
+            if (MODE == kOsdn) {
             // R_{t,s} = 2^(lg_t - lg_{s+1}) (s < t) for the write keys, into the
             // inverse buffer being prepared; a thread keeps column s
             f16 *R16 = LTm[nb];
@@ -630,6 +636,7 @@ __device__ __forceinline__ void fused_body(
               const int t = (l2 >> 6) + 2 * u;
               R16[t * CP + s] = h(s < t ? fexp2(lgt[u] - lgs) : 0.f);
             }
+            }
           }
         }
       }
@@ -638,7 +645,7 @@ __device__ __forceinline__ void fused_body(
       // ------------------------------ phase 4 ------------------------------
       if (act) {
         if (wave == 0) {
-          if (MODE == kOsdn) {
+          if (walk_mode(MODE)) {
             // blocked forward substitution of (I + M) g = rhs, lanes = tokens;
             // the 16 values of a block reach every lane through lane reads
             const int t = lane, bt = t >> 4;
@@ -680,7 +687,9 @@ __device__ __forceinline__ void fused_body(
             Lcc[t] = cct;
             Lw[t] = t < pL ? fexp2(lg_end - lg_next) * cct : 0.f;
             if (lane == 0) (*LlgC) = lg_end;
-            lr_sum += wave_sum(t < pL ? logf(a * a) : 0.f);
+            const float lrt = logf(a * a);  // log rho_t
+            if (MODE == kScan && log_ratio && t < pL) log_ratio[tok0 + (long)pc * C + t] = lrt;
+            lr_sum += wave_sum(t < pL ? lrt : 0.f);
           } else if (MODE == kDeltaNet) {
             const float gd = 1.0f - Lbeta[nb][lane] * Ln[lane];
             lr_sum += wave_sum(lane < pL ? logf(gd * gd) : 0.f);
@@ -719,6 +728,32 @@ __device__ __forceinline__ void fused_body(
             Ldpart[part][i] = a0;
             Ldpart[part][i + 1] = a1;
           }
+        } else if (MODE == kScan) {
+          // d_t token by token from the walk's c_t, d_{t+1} = r_t d_t + c_t p_t,
+          // a lane per dimension (waves 0-1): write keys kt_t = d_t (.) k_t and,
+          // if asked, d_t itself; d after the chunk is the next entry value
+          if (wave < 2) {
+            const int i = wave * 64 + lane;
+            float d = Ld_in[i];
+            const long base = (tok0 + (long)pc * C) * DK + i;
+#pragma unroll
+            for (int t0 = 0; t0 < C; t0 += 4) {
+              const float4 c4 = *(const float4 *)&Lcc[t0];
+              const float4 r4 = *(const float4 *)&Lr[t0];
+              const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int t = t0 + e;
+                if (t < pL) {
+                  const float kv = (float)LKp[t * KP + i];
+                  kt_out[base + (long)t * DK] = (bf16)(d * kv);
+                  if (d_all) d_all[base + (long)t * DK] = d;
+                  d = fmaf(cv[e], kv * kv, rv[e] * d);
+                }
+              }
+            }
+            Ld_in[i] = d;
+          }
         } else {
           const f16 *src = (MODE == kDeltaNet) ? LKp : LKt;
           for (int job = wave; job < 32; job += 8) write_keys_copy(job, src, nb);
@@ -727,7 +762,8 @@ __device__ __forceinline__ void fused_body(
       __syncthreads();
 
       // ------------------------------ phase 6 ------------------------------
-      if (act) {
+      // (the walk alone ends with phase 5)
+      if (MODE != kScan && act) {
         const float ds = Ldsb[nb];
         const f16 *Bsrc = (MODE == kDeltaNet) ? LKp : LKt;
         if (wave < 4) {
@@ -755,13 +791,13 @@ __device__ __forceinline__ void fused_body(
           score_tile(2 * (wave - 4) + 1, Bsrc, nb);
         }
       }
-      __syncthreads();
+      if (MODE != kScan) __syncthreads();
 
       // ----------------- phases 7-9: off-diagonal blocks of Tinv -----------------
       // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, blocks at distance 1, 2, 3; the
       // waves a level leaves idle form score tiles 4-9
 #pragma unroll
-      for (int dist = 1; dist < 4; ++dist) {
+      for (int dist = 1; dist < (MODE == kScan ? 1 : 4); ++dist) {
         if (act && wave >= 4 - dist) {
           const f16 *Bsrc = (MODE == kDeltaNet) ? LKp : LKt;
           if (dist == 1) score_tile(1 + wave, Bsrc, nb);                  // waves 3-5
@@ -795,6 +831,7 @@ __device__ __forceinline__ void fused_body(
                                  : Ld_in[ptid];
         d_final[(long)bh * DK + ptid] = dv;
       }
+      if (MODE == kScan && d_final && ptid < DK) d_final[(long)bh * DK + ptid] = Ld_in[ptid];
       if (MODE != kGiven && log_ratio_sum && ptid == 0) log_ratio_sum[bh] = lr_sum;
     }
   } else {
@@ -835,7 +872,7 @@ __device__ __forceinline__ void fused_body(
       const int jcol = j0 + 16 * sn + c16;
       const int sc = it - 1;       // chunk in the state pass
       const int cb = sc & 1;
-      const bool act = sc >= 0;
+      const bool act = MODE != kScan && sc >= 0;
       const int sL = act ? min(C, T_ - sc * C) : 0;
       const int nb = it & 1;       // buffer the prep waves are filling
       const bool pact = it < nch;  // a chunk is being prepared
@@ -871,8 +908,8 @@ __device__ __forceinline__ void fused_body(
         Xb[0] = cat(h4(X[0]), h4(X[1]));
         Xb[1] = cat(h4(X[2]), h4(X[3]));
       }
-      if (pact && MODE == kOsdn) key_gram_tile(8 + sn);
-      if (pact) {
+      if (pact && walk_mode(MODE)) key_gram_tile(8 + sn);
+      if (pact && MODE != kScan) {
         // values of the chunk being prepared (staged row-major in Kt), transposed
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -917,7 +954,7 @@ __device__ __forceinline__ void fused_body(
       __syncthreads();
 
       // ------------------------------ phase 5 ------------------------------
-      if (pact) {
+      if (pact && MODE != kScan) {
         if (MODE == kOsdn) {
           write_keys_itile(6 + sn, nb);
         } else {
@@ -928,17 +965,17 @@ __device__ __forceinline__ void fused_body(
       __syncthreads();
 
       // ------------------------------ phase 6 ------------------------------
-      if (pact) {
+      if (MODE != kScan && pact) {
         const f16 *Bsrc = (MODE == kDeltaNet) ? LKp : LKt;
         for (int job = sn; job < 6; job += 2) gram_a_off_tile(job, Bsrc, nb);
       }
-      __syncthreads();
+      if (MODE != kScan) __syncthreads();
 
       // ------------------------------ phases 7-9 ------------------------------
       // K S^T (phase 7) and Q S^T (phase 8) of the chunk being prepared, from
       // the prep copies of K and Q and the state after this iteration's update.
 #pragma unroll
-      for (int dist = 1; dist < 4; ++dist) {
+      for (int dist = 1; dist < (MODE == kScan ? 1 : 4); ++dist) {
         if (pact && dist < 3) {
           const f16 *src = dist == 1 ? LKp : LQp;
 #pragma unroll
@@ -971,11 +1008,13 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const float *__restrict__ beta, const float *__restrict__ r,
                    const float *__restrict__ d0, const float *__restrict__ S0, float eta,
                    int BH, int T_, bf16 *__restrict__ o, float *__restrict__ S_final,
-                   float *__restrict__ d_final, float *__restrict__ log_ratio_sum) {
+                   float *__restrict__ d_final, float *__restrict__ log_ratio_sum,
+                   bf16 *__restrict__ kt_out, float *__restrict__ d_all,
+                   float *__restrict__ log_ratio) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
   fused_body<MODE>(q, k, kt_in, v, beta, r, d0, S0, eta, BH, T_, o, S_final, d_final,
-                   log_ratio_sum, sm.Kp, sm.Qp, sm.Kt, sm.KtF, sm.Tm, sm.P, sm.F, sm.Td, sm.d_in,
+                   log_ratio_sum, kt_out, d_all, log_ratio, sm.Kp, sm.Qp, sm.Kt, sm.KtF, sm.Tm, sm.P, sm.F, sm.Td, sm.d_in,
                    sm.dpart, sm.beta, sm.dsb, sm.r, sm.n, sm.bv, sm.alpha, sm.g, sm.cc, sm.w,
                    sm.rhs, sm.acc, sm.lg, &sm.lgC, sm.red);
 }
@@ -991,7 +1030,8 @@ hipError_t launch_mode(const FusedArgs &a, const void *kt, hipStream_t s) {
   hipLaunchKernelGGL(osdn_fused_forward<MODE>, grid, block, shm, s, (const bf16 *)a.q,
                      (const bf16 *)a.k, (const bf16 *)kt, (const bf16 *)a.v, a.beta,
                      MODE == kOsdn ? a.r : nullptr, a.d0, a.S0, a.eta, BH, a.T, (bf16 *)a.o,
-                     a.S_final, a.d_final, a.log_ratio_sum);
+                     a.S_final, a.d_final, a.log_ratio_sum, (bf16 *)nullptr, (float *)nullptr,
+                     (float *)nullptr);
   return hipGetLastError();
 }
 
@@ -1004,6 +1044,23 @@ bool fused_supported(int dk, int dv, int chunk, int dtype) {
 hipError_t launch_fused_forward(const FusedArgs &a, hipStream_t s) {
   if ((long)a.B * a.H == 0) return hipSuccess;
   return a.precond_off ? launch_mode<kDeltaNet>(a, nullptr, s) : launch_mode<kOsdn>(a, nullptr, s);
+}
+
+bool fused_scan_supported(int dk, int dtype) { return dtype == 0 && dk == DK; }
+
+hipError_t launch_fused_scan(const ScanArgs &a, hipStream_t s) {
+  const int BH = a.B * a.H;
+  if (BH == 0) return hipSuccess;
+  const size_t shm = sizeof(Smem);
+  hipError_t e = hipFuncSetAttribute((const void *)osdn_fused_forward<kScan>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(osdn_fused_forward<kScan>, dim3((unsigned)BH), dim3(NTH), shm, s,
+                     (const bf16 *)nullptr, (const bf16 *)a.k, (const bf16 *)nullptr,
+                     (const bf16 *)nullptr, a.beta, a.r, a.d0, (const float *)nullptr, a.eta, BH,
+                     a.T, (bf16 *)nullptr, (float *)nullptr, a.d_final, a.log_ratio_sum,
+                     (bf16 *)a.k_tilde, a.d_all, a.log_ratio);
+  return hipGetLastError();
 }
 
 hipError_t launch_fused_chunk(const ChunkArgs &a, hipStream_t s) {

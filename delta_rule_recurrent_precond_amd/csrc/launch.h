@@ -46,5 +46,8 @@ bool fused_supported(int dk, int dv, int chunk, int dtype);
 hipError_t launch_fused_forward(const FusedArgs &a, hipStream_t s);
 // The same kernel with the write keys read from memory (phase 2 alone).
 hipError_t launch_fused_chunk(const ChunkArgs &a, hipStream_t s);
+// The same kernel's chunked preconditioner walk alone (bf16, dk = 128).
+bool fused_scan_supported(int dk, int dtype);
+hipError_t launch_fused_scan(const ScanArgs &a, hipStream_t s);
 
 }  // namespace osdn

@@ -65,6 +65,8 @@ OSDN_EXPORT int osdn_precond_scan(const void *k, const float *beta, const float 
   if (T > 0 && (!k || !beta || !k_tilde)) return OSDN_ERR_NULL;
   osdn::ScanArgs a{k, beta, r, d0, eta, B, H, T, dk, dtype, 0, k_tilde,
                    d_final, d_all, log_ratio, nullptr};
+  if (osdn::fused_scan_supported(dk, dtype))
+    return hip_status(osdn::launch_fused_scan(a, (hipStream_t)stream));
   return hip_status(osdn::launch_precond_scan_serial(a, (hipStream_t)stream));
 }
 
@@ -124,7 +126,8 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   if (!off) {
     osdn::ScanArgs sa{k, beta, r, d0, eta, B, H, T, dk, dtype, 0, workspace,
                       d_final, nullptr, nullptr, log_ratio_sum};
-    st = hip_status(osdn::launch_precond_scan_serial(sa, s));
+    st = hip_status(osdn::fused_scan_supported(dk, dtype) ? osdn::launch_fused_scan(sa, s)
+                                                          : osdn::launch_precond_scan_serial(sa, s));
     if (st != OSDN_OK) return st;
     kt = workspace;
   } else if (log_ratio_sum) {

@@ -125,13 +125,53 @@ def test_precond_scan_parity(dtype, dk, apf):
     assert np.all(np.abs(lr - np.log(ref["rho"])) <= _log_ratio_tol(ref["rho"]))
 
 
-def test_precond_scan_empty_sequence_copies_d0():
-    d0 = torch.rand(2, 2, 64) + 0.5
-    k = torch.zeros(2, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+@pytest.mark.parametrize("dk", [64, 128])
+def test_precond_scan_empty_sequence_copies_d0(dk):
+    d0 = torch.rand(2, 2, dk) + 0.5
+    k = torch.zeros(2, 2, 0, dk, dtype=torch.bfloat16, device="cuda")
     beta = torch.zeros(2, 2, 0, device="cuda")
     out = osdn.precond_scan(k, beta, None, d0.cuda(), 0.1)
     torch.cuda.synchronize()
     assert torch.equal(out["d_final"].cpu(), d0)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130])
+def test_precond_scan_chunk_boundaries(T):
+    """The chunked walk (bf16, dk = 128) around chunk boundaries, APF gates."""
+    w = W.custom(1, 2, T, 128, 128, 64, dtype="bf16", eta=0.2, apf=True, seed=300 + T)
+    inp = W.generate(w)
+    dev = _to_dev(inp)
+    _log("scan chunk boundaries T=%d" % T)
+    out = osdn.precond_scan(dev.k, dev.beta, dev.r, None, inp.eta, want_d_all=True,
+                            want_log_ratio=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, None, None, eta=inp.eta,
+                         want=("d", "d_all", "k_tilde", "rho"))
+    assert rowwise_rel(out["d_all"], ref["d_all"]) <= 1e-5
+    assert rowwise_rel(out["d_final"], ref["d"]) <= 1e-5
+    assert rowwise_rel(out["k_tilde"], ref["k_tilde"]) <= 2.0 ** -8
+    lr = as_f64(out["log_ratio"])
+    assert np.all(np.abs(lr - np.log(ref["rho"])) <= _log_ratio_tol(ref["rho"]))
+
+
+@pytest.mark.parametrize("name", ["1.3b-apf", "recall-apf"])
+def test_precond_scan_full_size_sampled_heads(name):
+    """The standalone walk at a workload's full size, checked on sampled heads."""
+    w = W.CONFIGS[name]
+    inp = W.generate(w)
+    heads = _heads(w, 3)
+    dev = _to_dev(inp)
+    _log("scan full size %s heads=%s" % (name, heads))
+    out = osdn.precond_scan(dev.k, dev.beta, dev.r, None, inp.eta, want_log_ratio=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, None, None, eta=inp.eta,
+                         heads=heads, want=("d", "k_tilde", "rho"))
+    assert rowwise_rel(_select(out["d_final"], heads, w), _select(ref["d"], heads, w)) <= 1e-5
+    assert rowwise_rel(_select(out["k_tilde"], heads, w),
+                       _select(ref["k_tilde"], heads, w)) <= 2.0 ** -8
+    rho = _select(ref["rho"], heads, w)
+    lr = _select(out["log_ratio"], heads, w)
+    assert np.all(np.abs(lr - np.log(rho)) <= _log_ratio_tol(rho))
 
 
 # ---------------------------------------------------------------------------
