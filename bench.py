@@ -14,8 +14,6 @@ and times the fp64 CPU oracle on the host as a reported baseline.
 from __future__ import annotations
 
 import argparse
-import hashlib
-import glob
 import json
 import os
 import sys
@@ -41,10 +39,8 @@ def parse():
 
 
 def kernel_sources_hash() -> str:
-    h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "delta_rule_recurrent_precond_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
-    return h.hexdigest()[:16]
+    from delta_rule_recurrent_precond_amd.profiling import kernel_sources_hash as h
+    return h()
 
 
 def algorithmic_bytes(w, path: str) -> int:
@@ -100,17 +96,34 @@ def time_launches(fn, steps, warmup, torch):
 
 
 def cpu_baseline(w, inp):
+    """The fp64 oracle on the host: the whole workload, repeated until about
+    10 s of CPU time (threads x wall) have been spent."""
     from oracle import oracle
     heads = list(range(w.B * w.H))
     threads = min(oracle.default_threads(), len(heads))
-    t0 = time.perf_counter()
-    oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, eta=inp.eta, heads=heads,
-                   want=("o", "S", "d"), threads=threads)
-    dt = time.perf_counter() - t0
+    reps, wall = 0, 0.0
+    while reps < 1 or (wall * threads < 10.0 and reps < 20):
+        t0 = time.perf_counter()
+        oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, eta=inp.eta, heads=heads,
+                       want=("o", "S", "d"), threads=threads)
+        wall += time.perf_counter() - t0
+        reps += 1
     tokens = len(heads) * w.T / w.H
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "whole workload: %d (b,h) sequences x T=%d, fp64 token-serial, %.2f s wall"
-                      % (len(heads), w.T, dt)}
+    return {"value": reps * tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "whole workload (%d (b,h) sequences x T=%d), fp64 token-serial, %d runs, "
+                      "%.2f s wall on %d threads" % (len(heads), w.T, reps, wall, threads)}
+
+
+def gpu_clocks():
+    """Current sclk/mclk as rocm-smi reports them (best effort, informational)."""
+    import subprocess
+    try:
+        p = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        card = next(iter(json.loads(p.stdout).values()))
+        return {k: v for k, v in card.items() if "sclk" in k or "mclk" in k}
+    except Exception:  # noqa: BLE001 - purely informational
+        return None
 
 
 def main():
@@ -194,11 +207,14 @@ def main():
         phases = {
             "precond_scan": {"ms": ms_scan, "tokens_per_s": tokens / (ms_scan * 1e-3),
                              "hbm_frac": algorithmic_bytes(w, "scan") / (ms_scan * 1e-3)
-                             / (HBM_PEAK_GBS * 1e9)},
+                             / (HBM_PEAK_GBS * 1e9),
+                             "traffic": stored_traffic("osdn_fused_scan", args.workload)},
             "chunk_fwd": {"ms": ms_chunk, "tokens_per_s": tokens / (ms_chunk * 1e-3),
                           "hbm_frac": algorithmic_bytes(w, "chunk") / (ms_chunk * 1e-3)
-                          / (HBM_PEAK_GBS * 1e9)},
-            "deltanet_mode": {"ms": ms_dn, "tokens_per_s": tokens / (ms_dn * 1e-3)},
+                          / (HBM_PEAK_GBS * 1e9),
+                          "traffic": stored_traffic("osdn_fused_chunk", args.workload)},
+            "deltanet_mode": {"ms": ms_dn, "tokens_per_s": tokens / (ms_dn * 1e-3),
+                              "traffic": stored_traffic("osdn_fused_deltanet", args.workload)},
             "precond_overhead": (ms - ms_dn) / ms,
             "two_launch_scan_share": ms_scan / (ms_scan + ms_chunk),
         }
@@ -220,6 +236,7 @@ def main():
                           "traffic": stored_traffic(kname, args.workload),
                           "kernel": kname, "algorithmic_bytes": kbytes, "kernel_ms": kms}
 
+    result["gpu_clocks"] = gpu_clocks()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, host)
