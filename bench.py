@@ -194,16 +194,22 @@ def main():
                                        dfin.data_ptr(), None, None, stream)
             assert st == 0, st
 
-        def chunk(i):
+        cws_n = osdn.chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, code)
+        cws = torch.empty(max(cws_n, 1), dtype=torch.uint8, device="cuda")
+
+        def chunk(i, use_ws=True):
             d = devs[i % copies]
             o = outs[i % copies]
             st = lib.osdn_chunk_fwd(d.q.data_ptr(), d.k.data_ptr(), kts[i % copies].data_ptr(),
                                     d.v.data_ptr(), d.beta.data_ptr(), None, B, H, T, dk, dv, C,
-                                    code, o["o"].data_ptr(), o["S_final"].data_ptr(), stream)
+                                    code, o["o"].data_ptr(), o["S_final"].data_ptr(),
+                                    cws.data_ptr() if (use_ws and cws_n) else None,
+                                    cws_n if use_ws else 0, stream)
             assert st == 0, st
 
         ms_scan = time_launches(scan, args.steps, args.warmup, torch)
         ms_chunk = time_launches(chunk, args.steps, args.warmup, torch)
+        ms_chunk_single = time_launches(lambda i: chunk(i, False), args.steps, args.warmup, torch)
         phases = {
             "precond_scan": {"ms": ms_scan, "tokens_per_s": tokens / (ms_scan * 1e-3),
                              "hbm_frac": algorithmic_bytes(w, "scan") / (ms_scan * 1e-3)
@@ -213,6 +219,7 @@ def main():
                           "hbm_frac": algorithmic_bytes(w, "chunk") / (ms_chunk * 1e-3)
                           / (HBM_PEAK_GBS * 1e9),
                           "traffic": stored_traffic("osdn_fused_chunk", args.workload)},
+            "chunk_fwd_single_kernel": {"ms": ms_chunk_single},
             "deltanet_mode": {"ms": ms_dn, "tokens_per_s": tokens / (ms_dn * 1e-3),
                               "traffic": stored_traffic("osdn_fused_deltanet", args.workload)},
             "precond_overhead": (ms - ms_dn) / ms,

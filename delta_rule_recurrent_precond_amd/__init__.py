@@ -85,8 +85,19 @@ def precond_scan(k, beta, r=None, d0=None, eta=0.05, *, want_d_all=False, want_l
     return out
 
 
-def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64):
-    """Phase 2 with a given write key k~.  Returns (o, S_final)."""
+def chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code) -> int:
+    n = _lib.load().osdn_chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code)
+    if n == (1 << 64) - 1:
+        raise ValueError("invalid arguments for osdn_chunk_fwd")
+    return int(n)
+
+
+def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64, *, workspace=True):
+    """Phase 2 with a given write key k~.  Returns (o, S_final).
+
+    ``workspace``: True allocates the scratch that selects the chunk-parallel
+    path (when one exists for these shapes), a uint8 device tensor passes one,
+    None runs the single-kernel pass."""
     _dev(q, "q")
     B, H, T, dk = q.shape
     dev = q.device
@@ -100,9 +111,14 @@ def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64):
     _dev(S0, "S0", (B, H, dv, dk), torch.float32, dev)
     o = torch.empty_like(v)
     S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if workspace is True:
+        n = chunk_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), _dtype_code(q))
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+    ws_bytes = 0 if workspace is None else workspace.numel()
     st = _lib.load().osdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(k_tilde), _ptr(v), _ptr(beta),
                                     _ptr(S0), B, H, T, dk, dv, int(chunk), _dtype_code(q),
-                                    _ptr(o), _ptr(S_final), _stream(dev))
+                                    _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes,
+                                    _stream(dev))
     _lib.check("osdn_chunk_fwd", st)
     return o, S_final
 

@@ -1,0 +1,473 @@
+// Two-kernel chunkwise pass for bf16 data, dk = dv = 128, chunk length 64.
+//
+// Source: gist.science technical summary of "OSDN: Improving Delta Rule with
+// Provable Online Preconditioning in Linear Attention" -- §2.1 and the
+// two-phase implementation of §2.2: given the write keys kt, the chunkwise
+// delta-rule pass is DeltaNet's, with kt in place of k in the chunk gram, the
+// intra-chunk scores and the state update.
+//
+// Within a chunk with entry state S (rows of S are value channels):
+//   A = strict_lower(diag(beta) K Kt^T),  T = (I + A)^-1,  P = lower(Q Kt^T)
+//   X = T diag(beta) (V - K S^T),  O = Q S^T + P X,  S <- S + X^T Kt
+// Everything except the three products with S depends on one chunk only, so a
+// chunk-parallel kernel (chunk_prep) forms it for all chunks at once and
+// writes, per (b, h, chunk), the operands the sequential pass needs; the state
+// kernel (chunk_state) then runs the pass, one wave per (b, h, 16 value
+// channels), streaming those operands and q, k, v.  Numerically it follows the
+// fused kernel step for step (the same fp16 operands, the same accumulation
+// order), so both paths agree to rounding.
+//
+// Record of one (b, h, chunk) in the caller's workspace (REC bytes):
+//   KtF  fp16 [8 i tiles][2 t pairs][64 lanes][8]  kt^T / ds as S-update operands
+//   TmA  fp16 [6 ops][64 lanes][8]  rows of T as 16x16x32 A operands, paired k order
+//   PA   fp16 [6 ops][64 lanes][8]  rows of P ds as A operands, paired k order
+//   ds   fp32 write-key scale: kt is stored divided by ds, a power of two
+// op x = 0..5 is (row block m, t pair qq) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
+#include "device.h"
+#include "launch.h"
+#include "mfma.h"
+
+namespace osdn {
+
+namespace {
+
+enum PrepMode { kDeltaNet = 1, kGiven = 2 };  // kt = k, or kt read from memory
+
+constexpr int C = 64;
+constexpr int DK = 128;
+constexpr size_t REC = 32768;
+constexpr size_t OFF_KTF = 0;
+constexpr size_t OFF_TM = 16384;
+constexpr size_t OFF_P = 22528;
+constexpr size_t OFF_DS = 28672;
+constexpr int LDT = 24;  // padded row (halves) of the 16x16 fp16 blocks in LDS
+constexpr int LDF = 20;  // padded row (floats) of the 16x16 fp32 blocks in LDS
+
+__device__ __forceinline__ int op_index(int m, int qq) { return m < 2 ? m : 2 * m - 2 + qq; }
+
+// ---------------------------------------------------------------------------
+// chunk_prep: one workgroup of 4 waves per (b, h, chunk).  k, kt and q are
+// loaded with all loads in flight at once, staged in LDS as fp16, and every
+// product reads its operands from there.
+// ---------------------------------------------------------------------------
+constexpr int KP = 136;  // padded row (halves) of the staged [64][128] tiles
+
+template <int MODE>  // kGiven: kt from memory; kDeltaNet: kt = k
+__global__ void __launch_bounds__(256)
+chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+           const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
+           unsigned char *__restrict__ ws) {
+  __shared__ __align__(16) f16 Ks[C * KP];          // k
+  __shared__ __align__(16) f16 Kts[C * KP];         // kt / ds (kt = k: unused)
+  __shared__ __align__(16) f16 Qs[C * KP];          // q
+  __shared__ __align__(16) float Fd[4][16][LDF];   // diagonal blocks of A (fp32)
+  __shared__ __align__(16) f16 Aoff[6][16][LDT];   // off-diagonal blocks of A (fp16)
+  __shared__ __align__(16) f16 Tdg[4][16][LDT];    // diagonal blocks of T (fp16)
+  __shared__ float bs[C];
+  __shared__ float red[4];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+  const long tok0 = (long)bh * T_ + (long)c * C;
+  const int L = min(C, T_ - c * C);
+  unsigned char *rec = ws + ((long)bh * NC + c) * REC;
+  const f16 *Ktp = (MODE == kGiven) ? Kts : Ks;
+
+  // ---- loads: 1024 pieces of 8 elements per tensor, 4 per thread
+  uint4 rk[4], rq[4], rt[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int p = tid + 256 * u, t = p >> 4;
+    const long off = (tok0 + t) * DK + (p & 15) * 8;
+    const bool ok = t < L;
+    rk[u] = ok ? *(const uint4 *)(k + off) : uint4{0, 0, 0, 0};
+    rq[u] = ok ? *(const uint4 *)(q + off) : uint4{0, 0, 0, 0};
+    if (MODE == kGiven) rt[u] = ok ? *(const uint4 *)(kt_in + off) : uint4{0, 0, 0, 0};
+  }
+  if (tid < C) bs[tid] = tid < L ? beta[tok0 + tid] : 0.f;
+
+  // write-key scale: a power of two >= max |kt| (given keys), 1 for kt = k
+  float ds = 1.0f;
+  if (MODE == kGiven) {
+    float km = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const unsigned short *s = (const unsigned short *)&rt[u];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) km = fmaxf(km, fabsf(bf2f(s[e])));
+    }
+#pragma unroll
+    for (int m_ = 1; m_ < 64; m_ <<= 1) km = fmaxf(km, __shfl_xor(km, m_));
+    if (lane == 0) red[wave] = km;
+    __syncthreads();
+    km = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    ds = km > 0.f ? fexp2(ceilf(flog2(km))) : 1.0f;
+  }
+  const float inv = 1.0f / ds;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
+    *(f16x8 *)&Ks[t * KP + i0] = cvt8(rk[u]);
+    *(f16x8 *)&Qs[t * KP + i0] = cvt8(rq[u]);
+    if (MODE == kGiven) {
+      const unsigned short *s = (const unsigned short *)&rt[u];
+      f16x8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = h(bf2f(s[e]) * inv);
+      *(f16x8 *)&Kts[t * KP + i0] = hv;
+    }
+  }
+  __syncthreads();
+
+  f16x4 ident;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ident[e] = (4 * g + e == c16) ? (f16)1.0f : (f16)0.0f;
+
+  // product tile (rt, ct) of X Kt^T over the 128 key dimensions
+  auto gram = [&](const f16 *xs, int rt_, int ct) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      acc = mma32(ld8(&xs[(16 * rt_ + c16) * KP + 32 * kk + 8 * g]),
+                  ld8(&Ktp[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
+    return acc;
+  };
+  auto beta4 = [&](int rt_) { return *(const f32x4 *)&bs[16 * rt_ + 4 * g]; };
+
+  // ---- A: diagonal block `wave` (then its inverse) and off-diagonal blocks
+  {
+    const f32x4 acc = gram(Ks, wave, wave);
+    const f32x4 b4 = beta4(wave);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * g + e;
+      Fd[wave][row][c16] = c16 < row ? b4[e] * ds * acc[e] : 0.f;
+    }
+  }
+  for (int job = wave; job < 6; job += 4) {
+    int rt_, ct;
+    off_tile(job, rt_, ct);
+    const f32x4 acc = gram(Ks, rt_, ct);
+    const f32x4 b4 = beta4(rt_);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Aoff[job][4 * g + e][c16] = h(b4[e] * ds * acc[e]);
+  }
+  wave_lds_sync();
+  {
+    float x[4];
+    tri16_inverse_quad(&Fd[wave][0][0], LDF, lane, x);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Tdg[wave][(lane & 3) + 4 * j][lane >> 2] = h(x[j]);
+  }
+
+  // ---- scores P = lower(Q Kt^T) ds, emitted as A operands (transposed tiles)
+  for (int idx = wave; idx < 10; idx += 4) {
+    int rt_, ct;
+    tri_tile(idx, rt_, ct);
+    const f32x4 acc = gram(Qs, rt_, ct);
+    f32x4 pv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = (16 * ct + c16 <= 16 * rt_ + 4 * g + e) ? ds * acc[e] : 0.f;
+    const f16x4 pt = h4(mma16(h4(pv), ident, zero4()));
+    *(f16x4 *)(rec + OFF_P + ((op_index(rt_, ct >> 1) * 64 + lane) * 8 + 4 * (ct & 1)) * 2) = pt;
+  }
+  // the two zero halves of P and T: blocks (0,1) and (2,3)
+  if (wave == 0) {
+    const f16x4 z = {0, 0, 0, 0};
+    *(f16x4 *)(rec + OFF_P + ((op_index(0, 0) * 64 + lane) * 8 + 4) * 2) = z;
+    *(f16x4 *)(rec + OFF_P + ((op_index(2, 1) * 64 + lane) * 8 + 4) * 2) = z;
+    *(f16x4 *)(rec + OFF_TM + ((op_index(0, 0) * 64 + lane) * 8 + 4) * 2) = z;
+    *(f16x4 *)(rec + OFF_TM + ((op_index(2, 1) * 64 + lane) * 8 + 4) * 2) = z;
+  }
+
+  // ---- write keys as S-update operands: i tiles 2w, 2w+1
+#pragma unroll
+  for (int nn = 0; nn < 2; ++nn) {
+    const int n = 2 * wave + nn;
+    f16x4 tr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      tr[m] = h4(mma16(ld4(&Ktp[(16 * m + c16) * KP + 16 * n + 4 * g]), ident, zero4()));
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+      *(f16x8 *)(rec + OFF_KTF + (((n * 2 + qq) * 64 + lane) * 8) * 2) = cat(tr[2 * qq], tr[2 * qq + 1]);
+  }
+  if (tid == 0) *(float *)(rec + OFF_DS) = ds;
+
+  __syncthreads();  // Tdg and Aoff complete
+
+  // ---- T: the diagonal block of row block `wave` as an A-operand half, then
+  // column `wave` below the diagonal: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+  {
+    const int m = wave;
+    *(f16x4 *)(rec + OFF_TM + ((op_index(m, m >> 1) * 64 + lane) * 8 + 4 * (m & 1)) * 2) =
+        ld4(&Tdg[m][c16][4 * g]);
+  }
+  if (wave < 3) {
+    const int bj = wave;
+    f16x4 tcol[4];  // T_{bk, bj} in the result layout (lane: column, rows 4g..4g+3)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tcol[bj][e] = Tdg[bj][4 * g + e][c16];
+#pragma unroll
+    for (int bi = 1; bi < 4; ++bi) {
+      if (bi <= bj) continue;
+      f32x4 y = zero4();
+#pragma unroll
+      for (int bk = 0; bk < 3; ++bk)
+        if (bk >= bj && bk < bi) {
+          const int ofj = bi == 1 ? 0 : bi == 2 ? 1 + bk : 3 + bk;  // off-diagonal index of (bi, bk)
+          y = mma16(ld4(&Aoff[ofj][c16][4 * g]), tcol[bk], y);
+        }
+      const f32x4 z = mma16(ld4(&Tdg[bi][c16][4 * g]), h4(y), zero4());
+      f32x4 nz;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nz[e] = -z[e];
+      tcol[bi] = h4(nz);
+      const f16x4 tt = h4(mma16(tcol[bi], ident, zero4()));
+      *(f16x4 *)(rec + OFF_TM + ((op_index(bi, bj >> 1) * 64 + lane) * 8 + 4 * (bj & 1)) * 2) = tt;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chunk_state: one workgroup of 8 waves per (b, h, 32 value channels),
+// sequential over chunks.  Waves 0 and 1 run the pass on channels 16w..16w+15
+// of the tile from one LDS buffer while waves 2-7 load the operands of the
+// next chunk and store them into the other (the loads are spread over six
+// waves so that enough of them are in flight).  One barrier per chunk.
+// ---------------------------------------------------------------------------
+constexpr int ST = 512;  // threads
+constexpr int VP = 40;   // padded row (halves) of the staged [64][32] value tile
+
+struct StateSmem {
+  f16 K[2][C * KP];
+  f16 Q[2][C * KP];
+  f16 V[2][C * VP];
+  unsigned char rec[2][OFF_DS + 16];  // KtF, TmA, PA, ds of the chunk
+  float b[2][C];
+};
+static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
+
+__global__ void __launch_bounds__(ST)
+chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+            const float *__restrict__ beta, const float *__restrict__ S0, int BH, int T_, int NC,
+            const unsigned char *__restrict__ ws, bf16 *__restrict__ o,
+            float *__restrict__ S_final) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  StateSmem &sm = *reinterpret_cast<StateSmem *>(smem_raw);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+  // (head, 32-channel tile); the four tiles of a head share one XCD (and its L2)
+  int bh, tile;
+  {
+    const int b = blockIdx.x;
+    if ((BH & 7) == 0) {
+      bh = 8 * (b >> 5) + (b & 7);
+      tile = (b >> 3) & 3;
+    } else {
+      bh = b >> 2;
+      tile = b & 3;
+    }
+  }
+  const int j0 = 32 * tile;            // first channel of the tile
+  const int jcol = j0 + 16 * wave + c16;
+
+  f16x4 ident;
+  bf16x4 identb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ident[e] = (4 * g + e == c16) ? (f16)1.0f : (f16)0.0f;
+    identb[e] = (4 * g + e == c16) ? (bf16)1.0f : (bf16)0.0f;
+  }
+
+  // loader registers (waves 2-7, index lt): k and q as 2048 pieces of 8
+  // elements, the value tile as 256, the record as OFF_DS/16 + 1 = 1793 pieces
+  // of 16 bytes, beta
+  constexpr int NL = ST - 128;
+  constexpr int RECP = OFF_DS / 16 + 1;
+  constexpr int NKQ = (2048 + NL - 1) / NL, NR = (RECP + NL - 1) / NL;
+  const int lt = tid - 128;
+  // Loads are unconditional (a masked lane reads a valid address) and masked
+  // values are zeroed when stored: a conditional load makes the compiler wait
+  // for it at the end of its branch.
+  uint4 lkq[NKQ], lv, lr[NR];
+  float lb = 0.f;
+  int lL = 0;  // valid rows of the chunk in the registers
+  auto load = [&](int cc) {
+    const long t0 = (long)bh * T_ + (long)cc * C;
+    const int L = min(C, T_ - cc * C);
+    lL = L;
+#pragma unroll
+    for (int u = 0; u < NKQ; ++u) {
+      const int p = min(lt + NL * u, 2047), pp = p & 1023, t = min(pp >> 4, L - 1);
+      lkq[u] = *(const uint4 *)((p < 1024 ? k : q) + (t0 + t) * DK + (pp & 15) * 8);  // k or q
+    }
+    {
+      const int t = min((lt & 255) >> 2, L - 1);
+      lv = *(const uint4 *)(v + (t0 + t) * 128 + j0 + (lt & 3) * 8);
+    }
+    const uint4 *rs = (const uint4 *)(ws + ((long)bh * NC + cc) * REC);
+#pragma unroll
+    for (int u = 0; u < NR; ++u) lr[u] = rs[min(lt + NL * u, RECP - 1)];
+    lb = beta[t0 + min(lt & 63, L - 1)];
+  };
+  auto stash = [&](int buf) {
+    const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < NKQ; ++u) {
+      const int p = lt + NL * u, pp = p & 1023, t = pp >> 4, i0 = (pp & 15) * 8;
+      if (p < 2048) *(f16x8 *)&(p < 1024 ? sm.K : sm.Q)[buf][t * KP + i0] = t < lL ? cvt8(lkq[u]) : z8;
+    }
+    if (lt < 256) *(f16x8 *)&sm.V[buf][(lt >> 2) * VP + (lt & 3) * 8] = (lt >> 2) < lL ? cvt8(lv) : z8;
+    uint4 *rd = (uint4 *)sm.rec[buf];
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int p = lt + NL * u;
+      if (p < RECP) rd[p] = lr[u];
+    }
+    if (lt < C) sm.b[buf][lt] = lt < lL ? lb : 0.f;
+  };
+
+  f32x4 Sacc[8];
+  f16x8 Sb[4];
+#pragma unroll
+  for (int i8 = 0; i8 < 8; ++i8) Sacc[i8] = zero4();
+  if (S0 && wave < 2) {
+#pragma unroll
+    for (int i8 = 0; i8 < 8; ++i8) {
+      const float4 s4 = *(const float4 *)(S0 + ((long)bh * 128 + jcol) * DK + 16 * i8 + 4 * g);
+      Sacc[i8] = f32x4{s4.x, s4.y, s4.z, s4.w};
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
+
+  if (NC > 0 && wave >= 2) {
+    load(0);
+    stash(0);
+  }
+  __syncthreads();
+
+  for (int c = 0; c < NC; ++c) {
+    const int cb = c & 1;
+    if (wave >= 2 && c + 1 < NC) load(c + 1);
+    if (wave < 2) {
+    const long tok0 = (long)bh * T_ + (long)c * C;
+    const int L = min(C, T_ - c * C);
+    const f16 *Kc = sm.K[cb], *Qc = sm.Q[cb];
+    const f16x8 *KtF = (const f16x8 *)(sm.rec[cb] + OFF_KTF);
+    const f16x8 *TmA = (const f16x8 *)(sm.rec[cb] + OFF_TM);
+    const f16x8 *PA = (const f16x8 *)(sm.rec[cb] + OFF_P);
+    const float ds = *(const float *)(sm.rec[cb] + OFF_DS);
+
+    // K S^T and Q S^T
+    f32x4 KS[4], O[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f16 *kr = &Kc[(16 * m + c16) * KP], *qr = &Qc[(16 * m + c16) * KP];
+      f32x4 a = zero4(), b = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        a = mma32(ldpk(kr, 32 * kk, g), Sb[kk], a);
+        b = mma32(ldpk(qr, 32 * kk, g), Sb[kk], b);
+      }
+      KS[m] = a;
+      O[m] = b;
+    }
+    // R = diag(beta)(V - K S^T), values turned into the result layout
+    f16x4 rr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f16x4 vv =
+          h4(mma16(ld4(&sm.V[cb][(16 * m + c16) * VP + 16 * wave + 4 * g]), ident, zero4()));
+      const f32x4 b4 = *(const f32x4 *)&sm.b[cb][16 * m + 4 * g];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rr[m][e] = h(b4[e] * ((float)vv[e] - KS[m][e]));
+    }
+    const f16x8 Rb[2] = {cat(rr[0], rr[1]), cat(rr[2], rr[3])};
+    // X = T R
+    f32x4 X[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int qq = 0; qq <= (m >> 1); ++qq)
+        acc = mma32(TmA[op_index(m, qq) * 64 + lane], Rb[qq], acc);
+      X[m] = acc;
+    }
+    const f16x8 Xb[2] = {cat(h4(X[0]), h4(X[1])), cat(h4(X[2]), h4(X[3]))};
+    // S^T += ds Kt^T X
+#pragma unroll
+    for (int i8 = 0; i8 < 8; ++i8) {
+      f32x4 u = zero4();
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) u = mma32(KtF[(i8 * 2 + qq) * 64 + lane], Xb[qq], u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Sacc[i8][e] = fmaf(ds, u[e], Sacc[i8][e]);
+    }
+    // O = Q S^T + P X, stored as bf16 through an identity transpose
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int qq = 0; qq <= (m >> 1); ++qq)
+        O[m] = mma32(PA[op_index(m, qq) * 64 + lane], Xb[qq], O[m]);
+      const bf16x4 ob = {(bf16)O[m][0], (bf16)O[m][1], (bf16)O[m][2], (bf16)O[m][3]};
+      const f32x4 ot = mma16bf(ob, identb, zero4());
+      const int t = 16 * m + c16;
+      if (t < L)
+        *(bf16x4 *)(o + (tok0 + t) * 128 + j0 + 16 * wave + 4 * g) =
+            bf16x4{(bf16)ot[0], (bf16)ot[1], (bf16)ot[2], (bf16)ot[3]};
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
+    }
+
+    if (wave >= 2 && c + 1 < NC) stash(cb ^ 1);
+    __syncthreads();
+  }
+
+  if (S_final && wave < 2) {
+#pragma unroll
+    for (int i8 = 0; i8 < 8; ++i8)
+      *(float4 *)(S_final + ((long)bh * 128 + jcol) * DK + 16 * i8 + 4 * g) =
+          float4{Sacc[i8][0], Sacc[i8][1], Sacc[i8][2], Sacc[i8][3]};
+  }
+}
+
+}  // namespace
+
+size_t split_workspace_bytes(int B, int H, int T) {
+  const long nc = (T + C - 1) / C;
+  return (size_t)B * H * nc * REC;
+}
+
+hipError_t launch_split_chunk(const ChunkArgs &a, bool given, void *ws, hipStream_t s) {
+  const int BH = a.B * a.H;
+  if (BH == 0) return hipSuccess;
+  const int NC = (a.T + C - 1) / C;
+  if (NC > 0) {
+    if (given)
+      hipLaunchKernelGGL(chunk_prep<kGiven>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.k_tilde, a.beta,
+                         a.T, NC, (unsigned char *)ws);
+    else
+      hipLaunchKernelGGL(chunk_prep<kDeltaNet>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
+                         a.T, NC, (unsigned char *)ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const size_t shm = sizeof(StateSmem);
+  hipError_t e = hipFuncSetAttribute((const void *)chunk_state,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_state, dim3((unsigned)(BH * 4)), dim3(ST), shm, s, (const bf16 *)a.q,
+                     (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.S0, BH, a.T, NC,
+                     (const unsigned char *)ws, (bf16 *)a.o, a.S_final);
+  return hipGetLastError();
+}
+
+}  // namespace osdn

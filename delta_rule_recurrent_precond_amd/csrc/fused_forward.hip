@@ -53,14 +53,12 @@
 // the identity (exact with fp32 accumulation).
 #include "device.h"
 #include "launch.h"
+#include "mfma.h"
 
 namespace osdn {
 
 namespace {
 
-typedef _Float16 f16;
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int C = 64;       // chunk length
 constexpr int DK = 128;     // key dimension (= value dimension)
@@ -99,105 +97,6 @@ struct Smem {
   float red[15];
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget of one workgroup");
-
-__device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16(f16x4 a, f16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16bf(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// fp32 -> fp16 rounding a materialised fp32 value.  The empty asm keeps the
-// compiler from fusing the conversion into the producing FMA (a mixed-precision
-// FMA rounds once, straight to fp16), so equal fp32 values give equal fp16
-// values on every code path -- needed for bitwise-reproducible continuation.
-__device__ __forceinline__ f16 h(float x) {
-  asm("" : "+v"(x));
-  return (f16)x;
-}
-__device__ __forceinline__ f16x4 h4(f32x4 v) { return f16x4{h(v[0]), h(v[1]), h(v[2]), h(v[3])}; }
-__device__ __forceinline__ f16x8 cat(f16x4 a, f16x4 b) {
-  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-__device__ __forceinline__ float bf2f(unsigned short u) {
-  return __builtin_bit_cast(float, ((unsigned)u) << 16);
-}
-__device__ __forceinline__ f16x4 ld4(const f16 *p) { return *(const f16x4 *)p; }
-__device__ __forceinline__ f16x8 ld8(const f16 *p) { return *(const f16x8 *)p; }
-// 16x16x32 operand in the paired k order from a row-major f16 row:
-// halves kb + 4g .. +3 and kb + 16 + 4g .. +3.
-__device__ __forceinline__ f16x8 ldpk(const f16 *row, int kb, int g) {
-  return cat(ld4(row + kb + 4 * g), ld4(row + kb + 16 + 4 * g));
-}
-// 8 bf16 (16 bytes) as fp16 (exact for |x| in fp16's normal range)
-__device__ __forceinline__ f16x8 cvt8(const uint4 &u) {
-  const unsigned short *s = (const unsigned short *)&u;
-  f16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (f16)bf2f(s[e]);
-  return r;
-}
-// hardware 2^x and log2 x (about 1 ulp)
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
-// Lanes of one wave exchange data through LDS between the two sides of this
-// call; it keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_wave_barrier(); }
-
-// Lower-triangular 16x16 tile list of a 64x64 matrix (10 tiles).
-__device__ __forceinline__ void tri_tile(int idx, int &rt, int &ct) {
-  rt = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
-  ct = idx - (rt * (rt + 1)) / 2;
-}
-// Off-diagonal lower tiles (row tile > col tile), 6 of them:
-// (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-__device__ __forceinline__ void off_tile(int idx, int &rt, int &ct) {
-  rt = idx >= 3 ? 3 : idx >= 1 ? 2 : 1;
-  ct = idx - (rt * (rt - 1)) / 2;
-}
-
-// Sum over the 4 lanes of an aligned quad (DPP quad permutations); all four
-// lanes receive the same bits.
-__device__ __forceinline__ float quad_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-  return v;
-}
-__device__ __forceinline__ float readlane(float v, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-
-// (I + N)^-1 for a strictly lower 16x16 fp32 block N in LDS (row stride ld;
-// entries on and above the diagonal must be zero), by one wave.  Lanes
-// 4c..4c+3 solve column c by forward substitution: lane q keeps rows q, q+4,
-// q+8, q+12 and their share of each dot product, and quad sums join the
-// shares.  On return x[j] holds row q + 4j of column c.
-__device__ __forceinline__ void tri16_inverse_quad(const float *N, int ld, int lane,
-                                                   float (&x)[4]) {
-  const int col = lane >> 2, q = lane & 3;
-  float nv[16][4];
-#pragma unroll
-  for (int t = 1; t < 16; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) nv[t][j] = N[t * ld + q + 4 * j];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] = 0.f;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    float p = 0.f;
-    if (t > 0) {
-      const float p0 = fmaf(nv[t][0], x[0], nv[t][1] * x[1]);
-      const float p1 = fmaf(nv[t][2], x[2], nv[t][3] * x[3]);
-      p = quad_sum(p0 + p1);
-    }
-    const float xt = (t == col ? 1.f : 0.f) - p;
-    if (q == (t & 3)) x[t >> 2] = xt;
-  }
-}
 
 // The kernel body.  Every LDS array comes in through its own restrict
 // pointer, which tells the compiler that a store to one array cannot change
@@ -392,44 +291,40 @@ __device__ __forceinline__ void fused_body(
     //                              prep waves
     // =====================================================================
     const int ptid = tid;
-    const int lt = ptid - 64;  // loader index of waves 1-5 (0..319)
-    uint4 pk[4], pq[4], pkt[4], pv;
+    uint4 pk[3], pq[3], pkt[3], pv;
     float pb = 0.f, pr = 1.f;
     float lr_sum = 0.f;  // wave 0: sum over tokens of log rho_t
-    // Global loads of a chunk, by waves 1-5 (wave 0 runs the walk's substitution
-    // meanwhile): k and q (and given write keys) as 1024 pieces of 8 elements,
-    // the value tile as 256 pieces, beta and r.
+    // Global loads of a chunk by all prep waves: k and q (and given write keys)
+    // as 1024 pieces of 8 elements, the value tile as 256 pieces, beta and r.
+    // The loads are unconditional -- rows past the end read the last row and
+    // are zeroed when staged, and the chunk after the last reloads the last --
+    // because a load under a condition makes the compiler wait for it where the
+    // branches join, which would expose its latency.
     auto prep_load = [&](int cc_) {
       const int c0 = cc_ * C;
       const int L = min(C, T_ - c0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int p = lt + 320 * u;
-        const int t = p >> 4, piece = p & 15;
-        const bool ok = p < 16 * C && t < L;
+      for (int u = 0; u < 3; ++u) {
+        const int p = min(ptid + PTH * u, 16 * C - 1);
+        const int t = min(p >> 4, L - 1), piece = p & 15;
         const long off = (tok0 + c0 + t) * DK + piece * 8;
-        pk[u] = ok ? *(const uint4 *)(k + off) : uint4{0, 0, 0, 0};
-        if (MODE != kScan) pq[u] = ok ? *(const uint4 *)(q + off) : uint4{0, 0, 0, 0};
-        if (MODE == kGiven) pkt[u] = ok ? *(const uint4 *)(kt_in + off) : uint4{0, 0, 0, 0};
+        pk[u] = *(const uint4 *)(k + off);
+        if (MODE != kScan) pq[u] = *(const uint4 *)(q + off);
+        if (MODE == kGiven) pkt[u] = *(const uint4 *)(kt_in + off);
       }
       if (MODE != kScan) {
-        const int t = lt >> 2, piece = lt & 3;
-        const bool ok = lt < 4 * C && t < L;
-        pv = ok ? *(const uint4 *)(v + (tok0 + c0 + t) * 128 + j0 + piece * 8)
-                : uint4{0, 0, 0, 0};
+        const int t = min((ptid & 255) >> 2, L - 1), piece = ptid & 3;
+        pv = *(const uint4 *)(v + (tok0 + c0 + t) * 128 + j0 + piece * 8);
       }
-      if (lt < C) {
-        const bool ok = lt < L;
-        pb = ok ? beta[tok0 + c0 + lt] : 0.f;
-        pr = (ok && r) ? r[tok0 + c0 + lt] : 1.f;
-      }
+      const int tb = min(ptid & 63, L - 1);
+      pb = beta[tok0 + c0 + tb];
+      pr = (r ? r : beta)[tok0 + c0 + tb];  // replaced by 1 when staged if r is absent
     };
-    if (nch > 0 && wave > 0) prep_load(0);
+    if (nch > 0) prep_load(0);
     __syncthreads();
 
-    for (int it = 0; it <= nch; ++it) {
+    for (int it = 0; nch > 0 && it <= nch; ++it) {
       refresh_lane();
-      const int lt = tid - 64 + (lane - (tid & 63));  // == tid - 64, opaque per iteration
       const int pc = it;  // chunk being prepared
       const int nb = pc & 1;
       const bool act = pc < nch;
@@ -437,38 +332,40 @@ __device__ __forceinline__ void fused_body(
 
       // ------------------------------ phase 1 ------------------------------
       if (act) {
-        if (wave == 0) {
-          if (MODE == kOsdn && pc > 0) {
-            // entry preconditioner: Gamma_L d of the previous chunk plus its sums
-            const float gL = fexp2((*LlgC));
+        if (wave == 0 && MODE == kOsdn && pc > 0) {
+          // entry preconditioner: Gamma_L d of the previous chunk plus its sums
+          const float gL = fexp2((*LlgC));
 #pragma unroll
-            for (int i = lane; i < DK; i += 64)
-              Ld_in[i] = gL * Ld_in[i] + Ldpart[0][i] + Ldpart[1][i] + Ldpart[2][i] +
-                         Ldpart[3][i];
-          }
-        } else {
+          for (int i = lane; i < DK; i += 64)
+            Ld_in[i] = gL * Ld_in[i] + Ldpart[0][i] + Ldpart[1][i] + Ldpart[2][i] +
+                       Ldpart[3][i];
+        }
+        {
           float kmax = 0.f;
+          const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int p = lt + 320 * u;
+          for (int u = 0; u < 3; ++u) {
+            const int p = ptid + PTH * u;
             if (p < 16 * C) {
               const int t = p >> 4, i0 = (p & 15) * 8;
-              *(f16x8 *)&LKp[t * KP + i0] = cvt8(pk[u]);
-              if (MODE != kScan) *(f16x8 *)&LQp[t * KP + i0] = cvt8(pq[u]);
+              const bool ok = t < pL;
+              *(f16x8 *)&LKp[t * KP + i0] = ok ? cvt8(pk[u]) : z8;
+              if (MODE != kScan) *(f16x8 *)&LQp[t * KP + i0] = ok ? cvt8(pq[u]) : z8;
               if (MODE == kGiven) {
+                if (!ok) pkt[u] = uint4{0, 0, 0, 0};
                 const unsigned short *ut = (const unsigned short *)&pkt[u];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) kmax = fmaxf(kmax, fabsf(bf2f(ut[e])));
               }
             }
           }
-          if (MODE != kScan && lt < 4 * C) {  // the value tile passes through Kt
-            const int t = lt >> 2, j = (lt & 3) * 8;
-            *(f16x8 *)&LKt[t * KP + j] = cvt8(pv);
+          if (MODE != kScan && ptid < 4 * C) {  // the value tile passes through Kt
+            const int t = ptid >> 2, j = (ptid & 3) * 8;
+            *(f16x8 *)&LKt[t * KP + j] = t < pL ? cvt8(pv) : z8;
           }
-          if (lt < C) {
-            Lbeta[nb][lt] = pb;
-            Lr[lt] = pr;
+          if (ptid < C) {
+            Lbeta[nb][ptid] = ptid < pL ? pb : 0.f;
+            Lr[ptid] = (r && ptid < pL) ? pr : 1.f;
           }
           if (MODE == kGiven) {
 #pragma unroll
@@ -548,14 +445,14 @@ __device__ __forceinline__ void fused_body(
           // given write keys, rescaled by a power of two into fp16 range
           float km = 0.f;
 #pragma unroll
-          for (int w_ = 1; w_ < NPREP; ++w_) km = fmaxf(km, Lred[w_]);
+          for (int w_ = 0; w_ < NPREP; ++w_) km = fmaxf(km, Lred[w_]);
           const float ds = km > 0.f ? fexp2(ceilf(flog2(km))) : 1.0f;
           const float inv = 1.0f / ds;
           if (ptid == 0) Ldsb[nb] = ds;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int p = lt + 320 * u;
-            if (wave > 0 && p < 16 * C) {
+          for (int u = 0; u < 3; ++u) {
+            const int p = ptid + PTH * u;
+            if (p < 16 * C) {
               const int t = p >> 4, i0 = (p & 15) * 8;
               const unsigned short *ut = (const unsigned short *)&pkt[u];
               f16x8 hv;
@@ -694,14 +591,14 @@ __device__ __forceinline__ void fused_body(
             const float gd = 1.0f - Lbeta[nb][lane] * Ln[lane];
             lr_sum += wave_sum(lane < pL ? logf(gd * gd) : 0.f);
           }
-        } else if (pc + 1 < nch) {
-          // prefetch the next chunk (every staging register has been consumed)
-          prep_load(pc + 1);
         }
       }
       __syncthreads();
 
       // ------------------------------ phase 5 ------------------------------
+      // the next chunk's loads: at the start of the phase in the walk alone
+      // (whose iteration ends here), else at its end
+      if (MODE == kScan) prep_load(min(pc + 1, nch - 1));
       if (act) {
         if (MODE == kOsdn) {
           write_keys_itile(wave, nb);  // i tiles 0..5; the state waves take 6 and 7
@@ -759,6 +656,7 @@ __device__ __forceinline__ void fused_body(
           for (int job = wave; job < 32; job += 8) write_keys_copy(job, src, nb);
         }
       }
+      if (MODE != kScan) prep_load(min(pc + 1, nch - 1));
       __syncthreads();
 
       // ------------------------------ phase 6 ------------------------------
@@ -867,7 +765,7 @@ __device__ __forceinline__ void fused_body(
       V[m] = f16x4{0, 0, 0, 0};
     }
 
-    for (int it = 0; it <= nch; ++it) {
+    for (int it = 0; nch > 0 && it <= nch; ++it) {
       refresh_lane();
       const int jcol = j0 + 16 * sn + c16;
       const int sc = it - 1;       // chunk in the state pass

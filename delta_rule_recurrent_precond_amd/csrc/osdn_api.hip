@@ -70,18 +70,28 @@ OSDN_EXPORT int osdn_precond_scan(const void *k, const float *beta, const float 
   return hip_status(osdn::launch_precond_scan_serial(a, (hipStream_t)stream));
 }
 
+OSDN_EXPORT size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
+                                                  int dtype) {
+  if (check_sizes(B, H, T, dk, dv, chunk, dtype, true, true) != OSDN_OK) return (size_t)-1;
+  return use_fused(dk, dv, chunk, dtype) ? osdn::split_workspace_bytes(B, H, T) : 0;
+}
+
 OSDN_EXPORT int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde, const void *v,
                                const float *beta, const float *S0, int B, int H, int T, int dk,
                                int dv, int chunk, int dtype, void *o, float *S_final,
-                               void *stream) {
+                               void *workspace, size_t workspace_bytes, void *stream) {
   int st = check_sizes(B, H, T, dk, dv, chunk, dtype, true, true);
   if (st != OSDN_OK) return st;
   if ((long long)B * H == 0) return OSDN_OK;
   if (T > 0 && (!q || !k || !k_tilde || !v || !beta || !o)) return OSDN_ERR_NULL;
   osdn::ChunkArgs a{q, k, k_tilde, v, beta, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
-  if (use_fused(dk, dv, chunk, dtype))
-    return hip_status(osdn::launch_fused_chunk(a, (hipStream_t)stream));
-  return hip_status(osdn::launch_chunk_generic(a, (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  if (use_fused(dk, dv, chunk, dtype)) {
+    if (workspace && workspace_bytes >= osdn::split_workspace_bytes(B, H, T))
+      return hip_status(osdn::launch_split_chunk(a, true, workspace, s));
+    return hip_status(osdn::launch_fused_chunk(a, s));
+  }
+  return hip_status(osdn::launch_chunk_generic(a, s));
 }
 
 OSDN_EXPORT size_t osdn_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,

@@ -99,10 +99,20 @@ int osdn_precond_scan(const void *k, const float *beta, const float *r, const fl
  *   chunk                        chunk length
  *   o         [B,H,T,dv] dtype   out: o_t = S_t q_t (required if T > 0)
  *   S_final   [B,H,dv,dk] fp32   out: S_T (optional)
+ *   workspace  optional device scratch.  When it holds at least
+ *              osdn_chunk_fwd_workspace_bytes(...) bytes (a positive number),
+ *              the per-chunk work runs chunk-parallel ahead of the sequential
+ *              pass (faster); NULL selects the single-kernel pass.
  */
 int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde, const void *v,
                    const float *beta, const float *S0, int B, int H, int T, int dk, int dv,
-                   int chunk, int dtype, void *o, float *S_final, void *stream);
+                   int chunk, int dtype, void *o, float *S_final, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* Scratch bytes that let osdn_chunk_fwd run its chunk-parallel path (0 when
+ * no path for these arguments uses scratch); (size_t)-1 if the arguments are
+ * invalid. */
+size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
 
 /*
  * Both phases end to end [summary §2.2 two-phase implementation].

@@ -200,6 +200,35 @@ def test_chunk_fwd_parity_given_ktilde(dtype, dk, dv, chunk, T):
     assert matrix_rel(S, ref["S"]) <= tol["S"]
 
 
+@pytest.mark.parametrize("T", [1, 64, 65, 200, 300])
+def test_chunk_fwd_split_matches_single_kernel_bitwise(T):
+    """The chunk-parallel prep + state pass takes the single-kernel pass's
+    steps in the same order on the same fp16 operands: identical bits."""
+    w = W.custom(2, 4, T, 128, 128, 64, dtype="bf16", eta=0.1, apf=True, seed=500 + T)
+    inp = W.generate(w)
+    S0 = 0.1 * torch.randn(w.B, w.H, 128, 128, generator=torch.Generator().manual_seed(4))
+    kt = (3.0 * inp.k.float()).to(torch.bfloat16)  # a scale that exercises the power-of-two ds
+    dev = _to_dev(inp)
+    _log("chunk split vs single T=%d" % T)
+    o1, S1 = osdn.chunk_fwd(dev.q, dev.k, kt.cuda(), dev.v, dev.beta, S0.cuda(), 64)
+    o2, S2 = osdn.chunk_fwd(dev.q, dev.k, kt.cuda(), dev.v, dev.beta, S0.cuda(), 64,
+                            workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(S1, S2)
+
+
+def test_chunk_fwd_workspace_too_small_uses_single_kernel():
+    w = W.custom(1, 2, 130, 128, 128, 64, dtype="bf16", seed=9)
+    inp = W.generate(w)
+    dev = _to_dev(inp)
+    small = torch.empty(100, dtype=torch.uint8, device="cuda")
+    o1, S1 = osdn.chunk_fwd(dev.q, dev.k, dev.k, dev.v, dev.beta, None, 64, workspace=small)
+    o2, S2 = osdn.chunk_fwd(dev.q, dev.k, dev.k, dev.v, dev.beta, None, 64, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
 # ---------------------------------------------------------------------------
 # end to end, reduced sizes spanning several chunks with ragged tails
 # ---------------------------------------------------------------------------
