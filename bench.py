@@ -114,6 +114,26 @@ def cpu_baseline(w, inp):
                       "%.2f s wall on %d threads" % (len(heads), w.T, reps, wall, threads)}
 
 
+def bench_step(args, torch, osdn, W):
+    """osdn_step on the decode batch: S and d updated in place each call."""
+    w = W.DECODE
+    dev = W.generate(w).to("cuda")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    S = 0.1 * torch.randn(w.B, w.H, w.dv, w.dk, device="cuda", generator=g)
+    d = 0.5 + torch.rand(w.B, w.H, w.dk, device="cuda", generator=g)
+    tok = [t[:, :, 0].contiguous() for t in (dev.q, dev.k, dev.v, dev.beta, dev.r)]
+    o = torch.empty_like(tok[2])
+    ms = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S, d, tok[4],
+                                           eta=w.eta, o=o), args.steps, args.warmup, torch)
+    heads = w.B * w.H
+    # S read and written (fp32), d read and written, q, k, v read and o written
+    # (bf16), beta and r read
+    nbytes = heads * (2 * w.dv * w.dk * 4 + 2 * w.dk * 4 + (2 * w.dk + 2 * w.dv) * 2 + 8)
+    return {"workload": w.name, "ms": ms, "tokens_per_s": w.B / (ms * 1e-3),
+            "algorithmic_bytes": nbytes,
+            "hbm_frac": nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+
+
 def gpu_clocks():
     """Current sclk/mclk as rocm-smi reports them (best effort, informational)."""
     import subprocess
@@ -242,6 +262,9 @@ def main():
                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                           "traffic": stored_traffic(kname, args.workload),
                           "kernel": kname, "algorithmic_bytes": kbytes, "kernel_ms": kms}
+
+    if args.only in ("all", "phases"):
+        result["decode_step"] = bench_step(args, torch, osdn, W)
 
     result["gpu_clocks"] = gpu_clocks()
     if not args.no_cpu_baseline:

@@ -123,6 +123,34 @@ def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64, *, workspace=True):
     return o, S_final
 
 
+def step(q, k, v, beta, S, d, r=None, eta=0.05, *, o=None, want_log_ratio=False):
+    """One decoding step.  q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), beta, r
+    [B,H] fp32; S [B,H,dv,dk] and d [B,H,dk] fp32 are updated in place.
+    Returns dict(o[, log_ratio])."""
+    _dev(q, "q")
+    B, H, dk = q.shape
+    dev = q.device
+    _dev(k, "k", q.shape, q.dtype, dev)
+    _dev(v, "v", None, q.dtype, dev)
+    if v.dim() != 3 or v.shape[:2] != (B, H):
+        raise ValueError("v has shape %s, expected [%d,%d,dv]" % (tuple(v.shape), B, H))
+    dv = v.shape[2]
+    _dev(beta, "beta", (B, H), torch.float32, dev)
+    _dev(r, "r", (B, H), torch.float32, dev)
+    _dev(S, "S", (B, H, dv, dk), torch.float32, dev)
+    _dev(d, "d", (B, H, dk), torch.float32, dev)
+    o = torch.empty_like(v) if o is None else o
+    lr = torch.empty((B, H), dtype=torch.float32, device=dev) if want_log_ratio else None
+    st = _lib.load().osdn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), float(eta), B, H,
+                               dk, dv, _dtype_code(q), _ptr(S), _ptr(d), _ptr(o), _ptr(lr),
+                               _stream(dev))
+    _lib.check("osdn_step", st)
+    out = {"o": o}
+    if want_log_ratio:
+        out["log_ratio"] = lr
+    return out
+
+
 def forward_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code, precond=True) -> int:
     flags = 0 if precond else _lib.OSDN_PRECOND_OFF
     n = _lib.load().osdn_forward_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code, flags)

@@ -244,6 +244,22 @@ __device__ __forceinline__ void fused_body(
     }
   };
 
+  // R_{t,s} = 2^(lg_t - lg_{s+1}) (s < t) for the write keys, into the inverse
+  // buffer being prepared: rows t = r0 + 4u and r0 + 1 + 4u, thread x (0..127)
+  // keeping column x & 63 of one of the two row sets.
+  auto r_factor_rows = [&](int x, int r0, int nb) {
+    f16 *R16 = LTm[nb];
+    const int s = x & 63, t0 = r0 + (x >> 6);
+    const float lgs = Llg[s + 1];
+    float lgt[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) lgt[u] = Llg[t0 + 4 * u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = t0 + 4 * u;
+      R16[t * CP + s] = h(s < t ? fexp2(lgt[u] - lgs) : 0.f);
+    }
+  };
   // Lower tile `job` of the key gram G = P P^T (P = k (.) k in fp16), raw, into F.
   auto key_gram_tile = [&](int job) {
     int rt, ct;
@@ -519,21 +535,7 @@ __device__ __forceinline__ void fused_body(
               LF[t * AP + s] = fv[u] * (bt[u] * as[ct] * fexp2(lt[u] - ls[ct]));
             }
             if (l2 < C) Lrhs[l2] = 1.0f - rb * fexp2(rl) * rv;
-            if (MODE == kOsdn) {
-            // R_{t,s} = 2^(lg_t - lg_{s+1}) (s < t) for the write keys, into the
-            // inverse buffer being prepared; a thread keeps column s
-            f16 *R16 = LTm[nb];
-            const int s = l2 & 63;
-            const float lgs = Llg[s + 1];
-            float lgt[32];
-#pragma unroll
-            for (int u = 0; u < 32; ++u) lgt[u] = Llg[(l2 >> 6) + 2 * u];
-#pragma unroll
-            for (int u = 0; u < 32; ++u) {
-              const int t = (l2 >> 6) + 2 * u;
-              R16[t * CP + s] = h(s < t ? fexp2(lgt[u] - lgs) : 0.f);
-            }
-            }
+            if (MODE == kOsdn) r_factor_rows(l2, 0, nb);  // rows 4u, 4u + 1
           }
         }
       }
@@ -816,6 +818,7 @@ __device__ __forceinline__ void fused_body(
       __syncthreads();
 
       // ------------------------------ phase 3 ------------------------------
+      if (pact && MODE == kOsdn) r_factor_rows(tid - 384, 2, nb);  // rows 4u + 2, 4u + 3
       if (act) {
         // O = Q S^T + P X, rounded to bf16, then turned through the identity so
         // that a lane holds 4 consecutive channels of one token (8-byte stores)

@@ -35,6 +35,19 @@ struct FusedArgs {
   float *S_final, *d_final, *log_ratio_sum;
 };
 
+struct StepArgs {
+  const void *q, *k, *v;
+  const float *beta, *r;
+  float eta;
+  int B, H, dk, dv, dtype;
+  float *S, *d;   // updated in place
+  void *o;
+  float *log_ratio;  // optional
+};
+
+// One decoding step with persistent (S, d), one workgroup per (b,h).
+hipError_t launch_step(const StepArgs &a, hipStream_t s);
+
 // Token-serial preconditioner walk, one wave per (b,h).
 hipError_t launch_precond_scan_serial(const ScanArgs &a, hipStream_t s);
 

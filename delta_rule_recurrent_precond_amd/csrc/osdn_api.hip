@@ -70,6 +70,17 @@ OSDN_EXPORT int osdn_precond_scan(const void *k, const float *beta, const float 
   return hip_status(osdn::launch_precond_scan_serial(a, (hipStream_t)stream));
 }
 
+OSDN_EXPORT int osdn_step(const void *q, const void *k, const void *v, const float *beta,
+                          const float *r, float eta, int B, int H, int dk, int dv, int dtype,
+                          float *S, float *d, void *o, float *log_ratio, void *stream) {
+  int st = check_sizes(B, H, 1, dk, dv, 16, dtype, true, false);
+  if (st != OSDN_OK) return st;
+  if ((long long)B * H == 0) return OSDN_OK;
+  if (!q || !k || !v || !beta || !S || !d || !o) return OSDN_ERR_NULL;
+  osdn::StepArgs a{q, k, v, beta, r, eta, B, H, dk, dv, dtype, S, d, o, log_ratio};
+  return hip_status(osdn::launch_step(a, (hipStream_t)stream));
+}
+
 OSDN_EXPORT size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
                                                   int dtype) {
   if (check_sizes(B, H, T, dk, dv, chunk, dtype, true, true) != OSDN_OK) return (size_t)-1;

@@ -79,6 +79,11 @@ CONFIGS = {
 # The throughput metric is quoted on the 1.3B-style layer (H=16, dk=dv=128, T=4096).
 METRIC_WORKLOAD = L13B_APF
 
+# One decoding step of a batch of 64 sequences on the same layer shape (the
+# persistent-state update): q, k, v of one token per (b, h), APF gates.
+DECODE = Workload("decode step B64 H16 d128 bf16 APF", 64, 16, 1, 128, 128, 64, "bf16", 0.05,
+                  True, seed=1006)
+
 
 def custom(B, H, T, dk, dv, chunk, dtype="bf16", eta=0.05, apf=False, seed=7, **kw) -> Workload:
     name = "custom B%d H%d T%d dk%d dv%d C%d %s%s" % (B, H, T, dk, dv, chunk, dtype,

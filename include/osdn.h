@@ -133,6 +133,28 @@ int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
                  float *S_final, float *d_final, float *log_ratio_sum, void *workspace,
                  size_t workspace_bytes, void *stream);
 
+/*
+ * One decoding step with persistent state [summary §2.1-§2.3, §3; the
+ * efficiency claims concern this per-token update]: for one token per (b,h),
+ *   kt = d (.) k,  S <- S + beta (v - S k) kt^T,  o = S q  (after the write),
+ *   rho = (1 - beta <d, k (.) k>)^2,
+ *   d <- r d + eta beta (1 - beta <d, k (.) k>) (k (.) k) / ||k||^2  (0 if k = 0).
+ * Running it for t = 0..T-1 gives the same o, S and d as osdn_forward over the
+ * T tokens, up to rounding.
+ *   q, k      [B,H,dk] dtype     query and key of the token (required)
+ *   v         [B,H,dv] dtype     value (required)
+ *   beta      [B,H]    fp32      write gate (required)
+ *   r         [B,H]    fp32      APF retention gate; NULL means r = 1
+ *   S         [B,H,dv,dk] fp32   state, read and updated in place (required)
+ *   d         [B,H,dk] fp32      preconditioner, read and updated in place (required)
+ *   o         [B,H,dv] dtype     out: the readout (required)
+ *   log_ratio [B,H]    fp32      out: log rho (optional)
+ * S, d and o must not overlap each other or the inputs.
+ */
+int osdn_step(const void *q, const void *k, const void *v, const float *beta, const float *r,
+              float eta, int B, int H, int dk, int dv, int dtype, float *S, float *d, void *o,
+              float *log_ratio, void *stream);
+
 /* Scratch bytes osdn_forward needs for these arguments (0 when the fused
  * single-kernel path applies); (size_t)-1 if the arguments are invalid. */
 size_t osdn_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype,

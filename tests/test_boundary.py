@@ -107,6 +107,18 @@ def test_scan_and_chunk_reject(lib):
                               None, 0, None) == _lib.OSDN_ERR_SHAPE
 
 
+def test_step_rejects(lib):
+    p = 1
+    assert lib.osdn_step(None, None, None, None, None, 0.1, 0, 4, 16, 16, 0, None, None, None,
+                         None, None) == _lib.OSDN_OK
+    assert lib.osdn_step(p, p, p, p, None, 0.1, 1, 1, 16, 16, 0, None, p, p, None,
+                         None) == _lib.OSDN_ERR_NULL
+    assert lib.osdn_step(p, p, p, p, None, 0.1, 1, 1, 24, 16, 0, p, p, p, None,
+                         None) == _lib.OSDN_ERR_UNSUPPORTED
+    assert lib.osdn_step(p, p, p, p, None, 0.1, 1, -2, 16, 16, 0, p, p, p, None,
+                         None) == _lib.OSDN_ERR_SHAPE
+
+
 def test_chunk_workspace_bytes(lib):
     # one 32 KB record per (b, h, chunk of 64) on the bf16 dk = dv = 128 shapes
     assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 128, 128, 64, 0) == 2 * 3 * 3 * 32768
