@@ -13,8 +13,10 @@ from __future__ import annotations
 from fractions import Fraction as F
 
 
-def run(q, k, v, beta, r=None, d0=None, S0=None, eta=F(0), deltanet=False):
-    """Sequences of rationals: q,k [T][dk], v [T][dv], beta,r [T], d0 [dk], S0 [dv][dk].
+def run(q, k, v, beta, r=None, d0=None, S0=None, eta=F(0), deltanet=False, alpha=None):
+    """Sequences of rationals: q,k [T][dk], v [T][dv], beta,r,alpha [T], d0 [dk],
+    S0 [dv][dk].  alpha is the optional state gate (the state is scaled by
+    alpha_t before token t reads and writes it).
     Returns dict(o [T][dv], S [dv][dk], d [dk], k_tilde [T][dk], rho [T])."""
     T = len(k)
     dk = len(k[0]) if T else (len(d0) if d0 is not None else 0)
@@ -32,7 +34,10 @@ def run(q, k, v, beta, r=None, d0=None, S0=None, eta=F(0), deltanet=False):
         a = sum((di * si for di, si in zip(d, sq)), F(0))
         w = list(kt_vec) if deltanet else [di * ki for di, ki in zip(d, kt_vec)]
         kts.append(w)
-        # state read with S_{t-1}, then rank-one write
+        if alpha is not None:
+            at = F(alpha[t])
+            S = [[at * x for x in row] for row in S]
+        # state read with (the gated) S_{t-1}, then rank-one write
         resid = [F(v[t][j]) - sum((S[j][i] * kt_vec[i] for i in range(dk)), F(0)) for j in range(dv)]
         for j in range(dv):
             for i in range(dk):

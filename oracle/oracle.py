@@ -64,7 +64,7 @@ def _load():
             lib.oracle_forward.argtypes = [
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 ctypes.c_int, ctypes.c_double,
-                P, P, P, P, P, P, P, P,   # q k v beta r d0 S0 k_given
+                P, P, P, P, P, P, P, P, P,  # q k v beta r d0 S0 k_given alpha
                 P, P, P, P, P, P,         # o S_final d_final k_tilde d_all rho
                 P, ctypes.c_long, ctypes.c_int]
             _lib = lib
@@ -92,8 +92,11 @@ def default_threads() -> int:
 
 def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.0, mode="osdn",
             k_given=None, heads=None, want=("o", "S", "d", "k_tilde", "rho"),
-            threads=None):
+            threads=None, alpha=None):
     """Token-serial fp64 OSDN forward.
+
+    ``alpha`` [B,H,T] is the optional state gate (Gated DeltaNet backbone):
+    S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) kt_t^T.
 
     Arrays are [B,H,T,dk] (q, k, k_given), [B,H,T,dv] (v), [B,H,T] (beta, r),
     [B,H,dk] (d0), [B,H,dv,dk] (S0); anything convertible (numpy, torch CPU)
@@ -113,7 +116,10 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.0, mode="osdn",
     d0 = _f64(d0)
     S0 = _f64(S0)
     k_given = _f64(k_given)
+    alpha = _f64(alpha)
     assert v.shape == (B, H, T, dv) and beta.shape == (B, H, T)
+    if alpha is not None:
+        assert alpha.shape == (B, H, T)
     if q is not None:
         assert q.shape == (B, H, T, dk)
     if r is not None:
@@ -141,7 +147,7 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.0, mode="osdn",
     nthr = threads if threads is not None else min(default_threads(), max(1, n_heads))
     rc = lib.oracle_forward(B, H, T, dk, dv, MODES[mode], float(eta),
                             _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(d0),
-                            _ptr(S0), _ptr(k_given),
+                            _ptr(S0), _ptr(k_given), _ptr(alpha),
                             _ptr(o), _ptr(Sf), _ptr(df), _ptr(kt), _ptr(da), _ptr(rho),
                             _ptr(hv), n_heads, int(nthr))
     if rc != 0:
@@ -193,7 +199,7 @@ def surrogate_grad(d, k, beta):
 # Chunkwise form of the state pass with K~  [summary §2.1]
 # ---------------------------------------------------------------------------
 
-def chunked_state_pass(q, k, k_tilde, v, beta, S0=None, C=64):
+def chunked_state_pass(q, k, k_tilde, v, beta, S0=None, C=64, alpha=None):
     """One (b,h) sequence, fp64, chunk length C (last chunk may be short).
 
     The summary states that the only change to DeltaNet's chunkwise pipeline is
@@ -204,22 +210,32 @@ def chunked_state_pass(q, k, k_tilde, v, beta, S0=None, C=64):
         (I + A) X = diag(beta) (V - K S^T),   A = strict_lower(diag(beta) K K~^T)
         O  = Q S^T + lower_incl_diag(Q K~^T) X
         S' = S + X^T K~
-    Inputs: q, k, k_tilde [T,dk]; v [T,dv]; beta [T]; S0 [dv,dk].
+    With the state gate alpha (S_t = alpha_t S_{t-1} + x_t k~_t^T, x_t =
+    beta_t (v_t - alpha_t S_{t-1} k_t)) and gamma_t = prod_{m<=t} alpha_m within
+    the chunk, S_t = gamma_t S + sum_{s<=t} (gamma_t / gamma_s) x_s k~_s^T, so
+        A_ts = beta_t (gamma_t/gamma_s) k_t . k~_s (s < t),
+        (I + A) X = diag(beta) (V - diag(gamma) K S^T),
+        O_t = gamma_t S q_t + sum_{s<=t} (gamma_t/gamma_s) (q_t . k~_s) x_s,
+        S' = gamma_L S + sum_s (gamma_L/gamma_s) x_s k~_s^T.
+    Inputs: q, k, k_tilde [T,dk]; v [T,dv]; beta, alpha [T]; S0 [dv,dk].
     Returns (o [T,dv], S_final [dv,dk]).
     """
     q, k, kt, v, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, k_tilde, v, beta))
     T, dk = k.shape
     dv = v.shape[1]
+    al = np.ones(T) if alpha is None else np.asarray(alpha, dtype=np.float64)
     S = np.zeros((dv, dk)) if S0 is None else np.array(S0, dtype=np.float64)
     o = np.zeros((T, dv))
     for c0 in range(0, T, C):
         sl = slice(c0, min(T, c0 + C))
         Q, K, Kt, V, bt = q[sl], k[sl], kt[sl], v[sl], beta[sl]
-        A = np.tril(bt[:, None] * (K @ Kt.T), k=-1)
-        rhs = bt[:, None] * (V - K @ S.T)
+        gam = np.cumprod(al[sl])
+        ratio = gam[:, None] / gam[None, :]          # gamma_t / gamma_s
+        A = np.tril(bt[:, None] * ratio * (K @ Kt.T), k=-1)
+        rhs = bt[:, None] * (V - gam[:, None] * (K @ S.T))
         X = np.linalg.solve(np.eye(len(bt)) + A, rhs)
-        o[sl] = Q @ S.T + np.tril(Q @ Kt.T) @ X
-        S = S + X.T @ Kt
+        o[sl] = gam[:, None] * (Q @ S.T) + np.tril(ratio * (Q @ Kt.T)) @ X
+        S = gam[-1] * S + (X * (gam[-1] / gam)[:, None]).T @ Kt
     return o, S
 
 

@@ -31,6 +31,14 @@
  * [summary §1]) and GIVEN_KTILDE (kt read from an input; isolates the state
  * pass).  In every mode rho_t = (1 - beta_t <kt, k_t>)^2, which equals the
  * OSDN formula because <d (.) k, k> = <d, k (.) k>.
+ *
+ * Optional state gate alpha_t (Gated DeltaNet backbone, [summary §4] lists it
+ * among the evaluated backbones but prints no formula; the plainest reading):
+ * the state decays before the token's read and write,
+ *     S <- alpha_t S,  then u = v_t - S k_t and S += beta_t u kt^T as above,
+ * i.e. S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) kt^T.  The
+ * preconditioner walk and rho_t do not involve S and are unchanged.  NULL
+ * alpha is alpha = 1.
  */
 #include <math.h>
 #include <pthread.h>
@@ -42,7 +50,7 @@ enum { ORACLE_OSDN = 0, ORACLE_DELTANET = 1, ORACLE_GIVEN_KTILDE = 2 };
 typedef struct {
   int B, H, T, dk, dv, mode;
   double eta;
-  const double *q, *k, *v, *beta, *r, *d0, *S0, *k_given;
+  const double *q, *k, *v, *beta, *r, *d0, *S0, *k_given, *alpha;
   double *o, *S_final, *d_final, *k_tilde, *d_all, *rho;
   const long *heads; /* which flattened (b,h) indices to run */
   long n_heads;
@@ -92,6 +100,12 @@ static int run_head(const oracle_job *J, long bh) {
     }
     if (J->k_tilde) memcpy(J->k_tilde + row * dk, kt, sizeof(double) * (size_t)dk);
     if (J->d_all) memcpy(J->d_all + row * dk, d, sizeof(double) * (size_t)dk);
+
+    /* state gate: the decay acts before the token's read and write */
+    if (J->alpha) {
+      const double at = J->alpha[row];
+      for (long x = 0; x < (long)dv * dk; ++x) S[x] *= at;
+    }
 
     /* residual against the state before this token's write */
     for (int j = 0; j < dv; ++j) {
@@ -158,14 +172,14 @@ static void *worker(void *arg) {
  * Run the recurrence over the heads listed in `heads` (flattened b*H+h; NULL
  * means all B*H heads) with up to n_threads threads (one head per task).
  * Shapes: q,k,k_given,k_tilde,d_all [B,H,T,dk]; v,o [B,H,T,dv];
- * beta,r,rho [B,H,T]; d0,d_final [B,H,dk]; S0,S_final [B,H,dv,dk].
+ * beta,r,alpha,rho [B,H,T]; d0,d_final [B,H,dk]; S0,S_final [B,H,dv,dk].
  * Optional pointers may be NULL.  Returns 0, or -1 on bad arguments or
  * allocation failure.
  */
 int oracle_forward(int B, int H, int T, int dk, int dv, int mode, double eta,
                    const double *q, const double *k, const double *v,
                    const double *beta, const double *r, const double *d0,
-                   const double *S0, const double *k_given,
+                   const double *S0, const double *k_given, const double *alpha,
                    double *o, double *S_final, double *d_final,
                    double *k_tilde, double *d_all, double *rho,
                    const long *heads, long n_heads, int n_threads) {
@@ -182,7 +196,7 @@ int oracle_forward(int B, int H, int T, int dk, int dv, int mode, double eta,
   memset(&J, 0, sizeof(J));
   J.B = B; J.H = H; J.T = T; J.dk = dk; J.dv = dv; J.mode = mode; J.eta = eta;
   J.q = q; J.k = k; J.v = v; J.beta = beta; J.r = r; J.d0 = d0; J.S0 = S0;
-  J.k_given = k_given; J.o = o; J.S_final = S_final; J.d_final = d_final;
+  J.k_given = k_given; J.alpha = alpha; J.o = o; J.S_final = S_final; J.d_final = d_final;
   J.k_tilde = k_tilde; J.d_all = d_all; J.rho = rho;
   J.heads = heads; J.n_heads = n_heads; J.next = 0; J.failed = 0;
   pthread_mutex_init(&J.lock, NULL);
