@@ -14,6 +14,7 @@ and times the fp64 CPU oracle on the host as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -162,7 +163,8 @@ def main():
     w = W.CONFIGS[args.workload]
     code = 0 if w.dtype == "bf16" else 1
     print("[bench] generating %s" % w.name, file=sys.stderr, flush=True)
-    host = W.generate(w)
+    # the gated draw adds the state gate alpha and leaves every other input as is
+    host = W.generate(dataclasses.replace(w, gated=True))
     per_copy = sum(t.numel() * t.element_size() for t in (host.q, host.k, host.v, host.beta)
                    if t is not None)
     copies = max(2, -(-2 * CACHE_BYTES // per_copy))
@@ -178,10 +180,11 @@ def main():
     ws_n = osdn.forward_workspace_bytes(B, H, T, dk, dv, C, code)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda") if ws_n else None
 
-    def fwd(i, precond=True):
+    def fwd(i, precond=True, gated=False):
         d = devs[i % copies]
         o = outs[i % copies]
         osdn.forward(d.q, d.k, d.v, d.beta, d.r, eta=d.eta, chunk=C, precond=precond,
+                     alpha=d.alpha if gated else None,
                      out=o if precond else {**o, "d_final": None}, workspace=ws)
 
     print("[bench] path=%s copies=%d" % (path, copies), file=sys.stderr, flush=True)
@@ -201,6 +204,9 @@ def main():
     phases = {}
     if args.only in ("all", "phases"):
         ms_dn = time_launches(lambda i: fwd(i, precond=False), args.steps, args.warmup, torch)
+        ms_g = time_launches(lambda i: fwd(i, gated=True), args.steps, args.warmup, torch)
+        ms_gdn = time_launches(lambda i: fwd(i, precond=False, gated=True), args.steps,
+                               args.warmup, torch)
         kts = [torch.empty_like(d.k) for d in devs]
         dfin = torch.empty((B, H, dk), dtype=torch.float32, device="cuda")
         lib = osdn.load()
@@ -221,7 +227,8 @@ def main():
             d = devs[i % copies]
             o = outs[i % copies]
             st = lib.osdn_chunk_fwd(d.q.data_ptr(), d.k.data_ptr(), kts[i % copies].data_ptr(),
-                                    d.v.data_ptr(), d.beta.data_ptr(), None, B, H, T, dk, dv, C,
+                                    d.v.data_ptr(), d.beta.data_ptr(), None, None, B, H, T, dk,
+                                    dv, C,
                                     code, o["o"].data_ptr(), o["S_final"].data_ptr(),
                                     cws.data_ptr() if (use_ws and cws_n) else None,
                                     cws_n if use_ws else 0, stream)
@@ -243,6 +250,10 @@ def main():
             "deltanet_mode": {"ms": ms_dn, "tokens_per_s": tokens / (ms_dn * 1e-3),
                               "traffic": stored_traffic("osdn_fused_deltanet", args.workload)},
             "precond_overhead": (ms - ms_dn) / ms,
+            "gated_forward": {"ms": ms_g, "tokens_per_s": tokens / (ms_g * 1e-3),
+                              "vs_ungated": ms_g / ms},
+            "gated_deltanet_mode": {"ms": ms_gdn, "tokens_per_s": tokens / (ms_gdn * 1e-3)},
+            "gated_precond_overhead": (ms_g - ms_gdn) / ms_g,
             "two_launch_scan_share": ms_scan / (ms_scan + ms_chunk),
         }
         result["phases"] = phases

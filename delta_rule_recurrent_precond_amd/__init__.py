@@ -92,11 +92,12 @@ def chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code) -> int:
     return int(n)
 
 
-def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64, *, workspace=True):
+def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64, *, alpha=None, workspace=True):
     """Phase 2 with a given write key k~.  Returns (o, S_final).
 
-    ``workspace``: True allocates the scratch that selects the chunk-parallel
-    path (when one exists for these shapes), a uint8 device tensor passes one,
+    ``alpha`` [B,H,T] fp32 is the optional state gate.  ``workspace``: True
+    allocates the scratch that selects the chunk-parallel path (when one exists
+    for these shapes; gated calls have none), a uint8 device tensor passes one,
     None runs the single-kernel pass."""
     _dev(q, "q")
     B, H, T, dk = q.shape
@@ -108,24 +109,28 @@ def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64, *, workspace=True):
         raise ValueError("v has shape %s, expected [%d,%d,%d,dv]" % (tuple(v.shape), B, H, T))
     dv = v.shape[3]
     _dev(beta, "beta", (B, H, T), torch.float32, dev)
+    _dev(alpha, "alpha", (B, H, T), torch.float32, dev)
     _dev(S0, "S0", (B, H, dv, dk), torch.float32, dev)
     o = torch.empty_like(v)
     S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if workspace is True and alpha is not None:
+        workspace = None
     if workspace is True:
         n = chunk_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), _dtype_code(q))
         workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
     ws_bytes = 0 if workspace is None else workspace.numel()
     st = _lib.load().osdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(k_tilde), _ptr(v), _ptr(beta),
-                                    _ptr(S0), B, H, T, dk, dv, int(chunk), _dtype_code(q),
+                                    _ptr(alpha), _ptr(S0), B, H, T, dk, dv, int(chunk), _dtype_code(q),
                                     _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes,
                                     _stream(dev))
     _lib.check("osdn_chunk_fwd", st)
     return o, S_final
 
 
-def step(q, k, v, beta, S, d, r=None, eta=0.05, *, o=None, want_log_ratio=False):
-    """One decoding step.  q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), beta, r
-    [B,H] fp32; S [B,H,dv,dk] and d [B,H,dk] fp32 are updated in place.
+def step(q, k, v, beta, S, d, r=None, eta=0.05, *, alpha=None, o=None, want_log_ratio=False):
+    """One decoding step.  q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), beta, r and
+    the optional state gate alpha [B,H] fp32; S [B,H,dv,dk] and d [B,H,dk] fp32
+    are updated in place.
     Returns dict(o[, log_ratio])."""
     _dev(q, "q")
     B, H, dk = q.shape
@@ -137,11 +142,13 @@ def step(q, k, v, beta, S, d, r=None, eta=0.05, *, o=None, want_log_ratio=False)
     dv = v.shape[2]
     _dev(beta, "beta", (B, H), torch.float32, dev)
     _dev(r, "r", (B, H), torch.float32, dev)
+    _dev(alpha, "alpha", (B, H), torch.float32, dev)
     _dev(S, "S", (B, H, dv, dk), torch.float32, dev)
     _dev(d, "d", (B, H, dk), torch.float32, dev)
     o = torch.empty_like(v) if o is None else o
     lr = torch.empty((B, H), dtype=torch.float32, device=dev) if want_log_ratio else None
-    st = _lib.load().osdn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), float(eta), B, H,
+    st = _lib.load().osdn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(alpha),
+                               float(eta), B, H,
                                dk, dv, _dtype_code(q), _ptr(S), _ptr(d), _ptr(o), _ptr(lr),
                                _stream(dev))
     _lib.check("osdn_step", st)
@@ -165,8 +172,11 @@ def forward_path(B, H, T, dk, dv, chunk, dtype_code, precond=True) -> str:
 
 
 def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond=True,
-            *, out=None, workspace=None):
+            *, alpha=None, out=None, workspace=None):
     """Both phases.  Returns dict(o, S_final, d_final, log_ratio_sum).
+
+    ``alpha`` [B,H,T] fp32 is the optional state gate (Gated DeltaNet backbone;
+    with precond=False, Gated DeltaNet itself).
 
     ``out`` may pass preallocated outputs (same keys) to keep the call free of
     allocations; ``workspace`` a uint8 device tensor of at least
@@ -182,6 +192,7 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond
     dv = v.shape[3]
     _dev(beta, "beta", (B, H, T), torch.float32, dev)
     _dev(r, "r", (B, H, T), torch.float32, dev)
+    _dev(alpha, "alpha", (B, H, T), torch.float32, dev)
     _dev(d0, "d0", (B, H, dk), torch.float32, dev)
     _dev(S0, "S0", (B, H, dv, dk), torch.float32, dev)
     code = _dtype_code(q)
@@ -199,7 +210,8 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.load().osdn_forward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(d0), _ptr(S0), float(eta),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(alpha), _ptr(d0), _ptr(S0),
+        float(eta),
         B, H, T, dk, dv, int(chunk), code, flags, _ptr(out["o"]), _ptr(out.get("S_final")),
         _ptr(out.get("d_final")), _ptr(out.get("log_ratio_sum")), _ptr(workspace), ws_bytes,
         _stream(dev))

@@ -10,6 +10,13 @@
 //   (I + A) X = diag(beta) (V - K S^T)            pseudo-values x_t = beta_t (v_t - S_{t-1} k_t)
 //   O  = Q S^T + lower(Q Kt^T) X                  o_t = S_t q_t (scores include t = s)
 //   S <- S + X^T Kt
+// With the optional state gate alpha (S_t = alpha_t S_{t-1} + beta_t (v_t -
+// alpha_t S_{t-1} k_t) kt_t^T) and gamma_t = prod_{m<=t} alpha_m within the
+// chunk: A_ts and the scores P_ts carry gamma_t / gamma_s, the residual reads
+// gamma_t S k_t, the output gamma_t S q_t, and S <- gamma_L S + sum_s
+// (gamma_L / gamma_s) x_s kt_s^T.  Decay ratios are 2^(lg_t - lg_s) with lg the
+// running sum of log2 alpha (clamped at -126 per token, so a zero gate gives
+// 2^-126 rather than an infinite logarithm).
 // This is the correctness path (used for fp32 data and for shapes the
 // matrix-core kernel does not cover).  One workgroup per (b, h, dv tile),
 // serial over chunks, everything of a chunk staged in LDS as fp32.
@@ -26,8 +33,8 @@ template <typename T, int DK, int DVT, int C>
 __global__ void __launch_bounds__(kThreads)
 chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ kt,
               const T *__restrict__ v, const float *__restrict__ beta,
-              const float *__restrict__ S0, int T_, int dv, T *__restrict__ o,
-              float *__restrict__ S_final) {
+              const float *__restrict__ alpha, const float *__restrict__ S0, int T_, int dv,
+              T *__restrict__ o, float *__restrict__ S_final) {
   constexpr int DKP = DK + 1;          // padded rows (bank spread)
   constexpr int CP = C + 1;
   constexpr int XP = DVT + 1;
@@ -41,6 +48,7 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
   __shared__ float sX[C * XP];    // V - K S^T scaled (R), then X
   __shared__ float sV[C * DVT];
   __shared__ float sB[C];
+  __shared__ float sLg[C];        // running sum of log2 alpha within the chunk
 
   const int tid = threadIdx.x;
   const long bh = blockIdx.x;
@@ -67,6 +75,13 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       sV[idx] = t < L ? Elem<T>::load(v + (tok0 + c0 + t) * (long)dv + j0 + j) : 0.0f;
     }
     for (int t = tid; t < C; t += kThreads) sB[t] = t < L ? beta[tok0 + c0 + t] : 0.0f;
+    if (tid == 0) {
+      float acc = 0.0f;
+      for (int t = 0; t < C; ++t) {
+        if (alpha && t < L) acc += fmaxf(log2f(alpha[tok0 + c0 + t]), -126.0f);
+        sLg[t] = acc;
+      }
+    }
     __syncthreads();
 
     // 2. mixed gram A and right-hand side R = diag(beta)(V - K S^T)
@@ -76,6 +91,7 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       if (s < t) {
         for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sKt[s * DKP + i];
         acc *= sB[t];
+        if (alpha) acc *= exp2f(sLg[t] - sLg[s]);
       }
       sA[t * CP + s] = acc;
     }
@@ -83,6 +99,7 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       const int t = idx / DVT, j = idx % DVT;
       float acc = 0.0f;
       for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sS[j * DKP + i];
+      if (alpha) acc *= exp2f(sLg[t]);
       sX[t * XP + j] = sB[t] * (sV[idx] - acc);
     }
     __syncthreads();
@@ -112,8 +129,10 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
     for (int idx = tid; idx < C * C; idx += kThreads) {
       const int t = idx / C, s = idx % C;
       float acc = 0.0f;
-      if (s <= t)
+      if (s <= t) {
         for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sKt[s * DKP + i];
+        if (alpha) acc *= exp2f(sLg[t] - sLg[s]);
+      }
       sA[t * CP + s] = acc;
     }
     __syncthreads();
@@ -124,6 +143,7 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       if (t < L) {
         float acc = 0.0f;
         for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sS[j * DKP + i];
+        if (alpha) acc *= exp2f(sLg[t]);
         for (int s = 0; s <= t; ++s) acc += sA[t * CP + s] * sX[s * XP + j];
         Elem<T>::store(o + (tok0 + c0 + t) * (long)dv + j0 + j, acc);
       }
@@ -134,7 +154,13 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
     for (int idx = tid; idx < DVT * DK; idx += kThreads) {
       const int j = idx / DK, i = idx % DK;
       float acc = sS[j * DKP + i];
-      for (int s = 0; s < L; ++s) acc += sX[s * XP + j] * sKt[s * DKP + i];
+      if (alpha) {
+        const float lgL = sLg[L - 1];
+        acc *= exp2f(lgL);
+        for (int s = 0; s < L; ++s) acc += exp2f(lgL - sLg[s]) * sX[s * XP + j] * sKt[s * DKP + i];
+      } else {
+        for (int s = 0; s < L; ++s) acc += sX[s * XP + j] * sKt[s * DKP + i];
+      }
       sS[j * DKP + i] = acc;
     }
     __syncthreads();
@@ -154,7 +180,8 @@ hipError_t launch_c(const ChunkArgs &a, hipStream_t s, dim3 grid) {
 #define OSDN_GEN_CASE(C_)                                                                      \
   case C_:                                                                                     \
     hipLaunchKernelGGL((chunk_generic<T, DK, DVT, C_>), grid, block, 0, s, (const T *)a.q,   \
-                       (const T *)a.k, (const T *)a.k_tilde, (const T *)a.v, a.beta, a.S0,   \
+                       (const T *)a.k, (const T *)a.k_tilde, (const T *)a.v, a.beta, a.alpha,\
+                       a.S0,                                                                   \
                        a.T, a.dv, (T *)a.o, a.S_final);                                       \
     break;
   switch (a.chunk) {

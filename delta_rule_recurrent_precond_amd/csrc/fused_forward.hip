@@ -93,19 +93,23 @@ struct Smem {
   float dsb[4];             // write-key scale [buf] (padded to keep 16-byte alignment)
   float r[C], n[C], bv[C], alpha[C], g[C], cc[C], w[C], rhs[C], acc[C];
   float lg[C + 4];          // lg[t] = sum_{m<t} log2 r_m
+  float al[C];              // state gates of the chunk being prepared
+  float lga[2][C + 4];      // [buf] lga[t] = sum_{m<=t} log2 alpha_m (state gate)
   float lgC;                // lg[L] of the chunk prepared last
   float red[15];
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget of one workgroup");
+static_assert(offsetof(Smem, lga) % 16 == 0, "16-byte reads of the gate prefix");
 
 // The kernel body.  Every LDS array comes in through its own restrict
 // pointer, which tells the compiler that a store to one array cannot change
 // another, so loads can be issued ahead of unrelated stores.
-template <int MODE>
+template <int MODE, bool GATED>
 __device__ __forceinline__ void fused_body(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const bf16 *__restrict__ kt_in, const bf16 *__restrict__ v,
                    const float *__restrict__ beta, const float *__restrict__ r,
+                   const float *__restrict__ alpha,
                    const float *__restrict__ d0, const float *__restrict__ S0, float eta,
                    int BH, int T_, bf16 *__restrict__ o, float *__restrict__ S_final,
                    float *__restrict__ d_final, float *__restrict__ log_ratio_sum, bf16 *__restrict__ kt_out,
@@ -119,7 +123,8 @@ __device__ __forceinline__ void fused_body(
            float *__restrict__ Lbv, float *__restrict__ Lalpha, float *__restrict__ Lg,
            float *__restrict__ Lcc, float *__restrict__ Lw, float *__restrict__ Lrhs,
            float *__restrict__ Lacc, float *__restrict__ Llg, float *__restrict__ LlgC,
-           float *__restrict__ Lred) {
+           float *__restrict__ Lred, float *__restrict__ Lal,
+           float (*__restrict__ Llga)[C + 4]) {
   constexpr int NTILE = MODE == kScan ? 1 : 128 / DVT;
 
   const int tid = threadIdx.x;
@@ -164,6 +169,14 @@ __device__ __forceinline__ void fused_body(
     ident[e] = (4 * g + e == c16) ? (f16)1.0f : (f16)0.0f;
     identb[e] = (4 * g + e == c16) ? (bf16)1.0f : (bf16)0.0f;
   }
+
+  // State-gate decays gamma_t / gamma_s = 2^(lga_t - lga_s) of buffer nb for
+  // rows t0..t0+3 and column s (only taken for s <= t, where they are <= 1).
+  auto gate_decay = [&](int nb, int t0, int s) {
+    const float4 lt = *(const float4 *)&Llga[nb][t0];
+    const float ls = Llga[nb][s];
+    return f32x4{fexp2(lt.x - ls), fexp2(lt.y - ls), fexp2(lt.z - ls), fexp2(lt.w - ls)};
+  };
 
   // ------------- prep work any wave can take (chunk in buffer nb) -------------
   // Write keys of i tile n (OSDN): D = Gamma d0 + R (c (.) P), kt = D (.) k / ds,
@@ -237,10 +250,12 @@ __device__ __forceinline__ void fused_body(
     for (int kk = 0; kk < 4; ++kk)
       acc = mma32(ld8(&LQp[(16 * rt + c16) * KP + 32 * kk + 8 * g]),
                   ld8(&Bsrc[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
+    f32x4 dec = {1.f, 1.f, 1.f, 1.f};
+    if (GATED) dec = gate_decay(nb, 16 * rt + 4 * g, 16 * ct + c16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * rt + 4 * g + e, col = 16 * ct + c16;
-      LP[nb][row * CP + col] = h(col <= row ? ds * acc[e] : 0.f);
+      LP[nb][row * CP + col] = h(col <= row ? ds * dec[e] * acc[e] : 0.f);
     }
   };
 
@@ -284,10 +299,12 @@ __device__ __forceinline__ void fused_body(
     for (int kk = 0; kk < 4; ++kk)
       acc = mma32(ld8(&LKp[(16 * rt + c16) * KP + 32 * kk + 8 * g]),
                   ld8(&Bsrc[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
+    f32x4 dec = {1.f, 1.f, 1.f, 1.f};
+    if (GATED) dec = gate_decay(nb, 16 * rt + 4 * g, 16 * ct + c16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * rt + 4 * g + e, col = 16 * ct + c16;
-      LF[row * AP + col] = Lbeta[nb][row] * ds * acc[e];
+      LF[row * AP + col] = Lbeta[nb][row] * ds * dec[e] * acc[e];
     }
   };
 
@@ -308,7 +325,7 @@ __device__ __forceinline__ void fused_body(
     // =====================================================================
     const int ptid = tid;
     uint4 pk[3], pq[3], pkt[3], pv;
-    float pb = 0.f, pr = 1.f;
+    float pb = 0.f, pr = 1.f, pal = 1.f;
     float lr_sum = 0.f;  // wave 0: sum over tokens of log rho_t
     // Global loads of a chunk by all prep waves: k and q (and given write keys)
     // as 1024 pieces of 8 elements, the value tile as 256 pieces, beta and r.
@@ -335,6 +352,7 @@ __device__ __forceinline__ void fused_body(
       const int tb = min(ptid & 63, L - 1);
       pb = beta[tok0 + c0 + tb];
       pr = (r ? r : beta)[tok0 + c0 + tb];  // replaced by 1 when staged if r is absent
+      if (GATED) pal = alpha[tok0 + c0 + tb];
     };
     if (nch > 0) prep_load(0);
     __syncthreads();
@@ -382,6 +400,7 @@ __device__ __forceinline__ void fused_body(
           if (ptid < C) {
             Lbeta[nb][ptid] = ptid < pL ? pb : 0.f;
             Lr[ptid] = (r && ptid < pL) ? pr : 1.f;
+            if (GATED) Lal[ptid] = ptid < pL ? pal : 1.f;
           }
           if (MODE == kGiven) {
 #pragma unroll
@@ -393,6 +412,16 @@ __device__ __forceinline__ void fused_body(
       __syncthreads();
 
       // ------------------------------ phase 2 ------------------------------
+      if (GATED && act && wave == 4) {
+        // lga[t] = sum_{m<=t} log2 alpha_m (clamped so that alpha = 0 stays finite)
+        float incl = fmaxf(flog2(Lal[lane]), -126.f);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(incl, off);
+          if (lane >= off) incl += y;
+        }
+        Llga[nb][lane] = incl;
+      }
       if (act && MODE != kGiven) {
         if (wave < 4) {
           // token statistics: wave w owns tokens 16w..16w+15, lane quarter g 32 dims
@@ -674,10 +703,12 @@ __device__ __forceinline__ void fused_body(
           for (int kk = 0; kk < 4; ++kk)
             acc = mma32(ld8(&LKp[(16 * b + c16) * KP + 32 * kk + 8 * g]),
                         ld8(&Bsrc[(16 * b + c16) * KP + 32 * kk + 8 * g]), acc);
+          f32x4 dec = {1.f, 1.f, 1.f, 1.f};
+          if (GATED) dec = gate_decay(nb, 16 * b + 4 * g, 16 * b + c16);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = 16 * b + 4 * g + e, col = 16 * b + c16;
-            LF[row * AP + col] = col < row ? Lbeta[nb][row] * ds * acc[e] : 0.f;
+            LF[row * AP + col] = col < row ? Lbeta[nb][row] * ds * dec[e] * acc[e] : 0.f;
           }
           wave_lds_sync();
           float x[4];
@@ -760,7 +791,7 @@ __device__ __forceinline__ void fused_body(
     // jcol, rows 16m + 4g + e).
     f32x4 KS[4], O[4];
     f16x4 V[4];
-    f16x8 Rb[2], Xb[2];
+    f16x8 Rb[2], Xb[2], Xs[2];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       KS[m] = O[m] = zero4();
@@ -785,6 +816,12 @@ __device__ __forceinline__ void fused_body(
         for (int m = 0; m < 4; ++m) {
           const float4 b4 = *(const float4 *)&Lbeta[cb][16 * m + 4 * g];
           const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+          if (GATED) {  // the entry state reaches token t decayed by gamma_t
+            const float4 l4 = *(const float4 *)&Llga[cb][16 * m + 4 * g];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) KS[m][e] *= fexp2(lv[e]);
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) rr[m][e] = h(bb[e] * ((float)V[m][e] - KS[m][e]));
         }
@@ -807,6 +844,19 @@ __device__ __forceinline__ void fused_body(
         }
         Xb[0] = cat(h4(X[0]), h4(X[1]));
         Xb[1] = cat(h4(X[2]), h4(X[3]));
+        if (GATED) {
+          // rows of X for the state update, decayed to the chunk end: gamma_L / gamma_s
+          const float lgL = Llga[cb][C - 1];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const float4 l4 = *(const float4 *)&Llga[cb][16 * m + 4 * g];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) X[m][e] *= fexp2(lgL - lv[e]);
+          }
+          Xs[0] = cat(h4(X[0]), h4(X[1]));
+          Xs[1] = cat(h4(X[2]), h4(X[3]));
+        }
       }
       if (pact && walk_mode(MODE)) key_gram_tile(8 + sn);
       if (pact && MODE != kScan) {
@@ -824,6 +874,12 @@ __device__ __forceinline__ void fused_body(
         // that a lane holds 4 consecutive channels of one token (8-byte stores)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
+          if (GATED) {
+            const float4 l4 = *(const float4 *)&Llga[cb][16 * m + 4 * g];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) O[m][e] *= fexp2(lv[e]);
+          }
           const f16 *row = &LP[cb][(16 * m + c16) * CP];
 #pragma unroll
           for (int qq = 0; qq <= (m >> 1); ++qq) O[m] = mma32(ldpk(row, 32 * qq, g), Xb[qq], O[m]);
@@ -841,13 +897,16 @@ __device__ __forceinline__ void fused_body(
       if (act) {
         // S^T += ds Kt^T X, then the fp16 copy for the next products
         const float ds = Ldsb[cb];
+        const float gL = GATED ? fexp2(Llga[cb][C - 1]) : 1.f;  // gamma_L
 #pragma unroll
         for (int i8 = 0; i8 < 8; ++i8) {
           f32x4 u = zero4();
 #pragma unroll
-          for (int qq = 0; qq < 2; ++qq) u = mma32(ld8(&LKtF[cb][i8][qq][lane][0]), Xb[qq], u);
+          for (int qq = 0; qq < 2; ++qq)
+            u = mma32(ld8(&LKtF[cb][i8][qq][lane][0]), GATED ? Xs[qq] : Xb[qq], u);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Sacc[i8][e] = fmaf(ds, u[e], Sacc[i8][e]);
+          for (int e = 0; e < 4; ++e)
+            Sacc[i8][e] = fmaf(ds, u[e], GATED ? gL * Sacc[i8][e] : Sacc[i8][e]);
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
@@ -902,11 +961,12 @@ __device__ __forceinline__ void fused_body(
   }
 }
 
-template <int MODE>
+template <int MODE, bool GATED>
 __global__ void __launch_bounds__(NTH)
 osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    const bf16 *__restrict__ kt_in, const bf16 *__restrict__ v,
                    const float *__restrict__ beta, const float *__restrict__ r,
+                   const float *__restrict__ alpha,
                    const float *__restrict__ d0, const float *__restrict__ S0, float eta,
                    int BH, int T_, bf16 *__restrict__ o, float *__restrict__ S_final,
                    float *__restrict__ d_final, float *__restrict__ log_ratio_sum,
@@ -914,26 +974,31 @@ osdn_fused_forward(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                    float *__restrict__ log_ratio) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
-  fused_body<MODE>(q, k, kt_in, v, beta, r, d0, S0, eta, BH, T_, o, S_final, d_final,
+  fused_body<MODE, GATED>(q, k, kt_in, v, beta, r, alpha, d0, S0, eta, BH, T_, o, S_final, d_final,
                    log_ratio_sum, kt_out, d_all, log_ratio, sm.Kp, sm.Qp, sm.Kt, sm.KtF, sm.Tm, sm.P, sm.F, sm.Td, sm.d_in,
                    sm.dpart, sm.beta, sm.dsb, sm.r, sm.n, sm.bv, sm.alpha, sm.g, sm.cc, sm.w,
-                   sm.rhs, sm.acc, sm.lg, &sm.lgC, sm.red);
+                   sm.rhs, sm.acc, sm.lg, &sm.lgC, sm.red, sm.al, sm.lga);
+}
+
+template <int MODE, bool GATED>
+hipError_t launch_mg(const FusedArgs &a, const void *kt, hipStream_t s) {
+  const int BH = a.B * a.H;
+  const dim3 grid((unsigned)(BH * (128 / DVT))), block(NTH);
+  const size_t shm = sizeof(Smem);
+  hipError_t e = hipFuncSetAttribute((const void *)osdn_fused_forward<MODE, GATED>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((osdn_fused_forward<MODE, GATED>), grid, block, shm, s, (const bf16 *)a.q,
+                     (const bf16 *)a.k, (const bf16 *)kt, (const bf16 *)a.v, a.beta,
+                     MODE == kOsdn ? a.r : nullptr, a.alpha, a.d0, a.S0, a.eta, BH, a.T, (bf16 *)a.o,
+                     a.S_final, a.d_final, a.log_ratio_sum, (bf16 *)nullptr, (float *)nullptr,
+                     (float *)nullptr);
+  return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_mode(const FusedArgs &a, const void *kt, hipStream_t s) {
-  const int BH = a.B * a.H;
-  const dim3 grid((unsigned)(BH * (128 / DVT))), block(NTH);
-  const size_t shm = sizeof(Smem);
-  hipError_t e = hipFuncSetAttribute((const void *)osdn_fused_forward<MODE>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(osdn_fused_forward<MODE>, grid, block, shm, s, (const bf16 *)a.q,
-                     (const bf16 *)a.k, (const bf16 *)kt, (const bf16 *)a.v, a.beta,
-                     MODE == kOsdn ? a.r : nullptr, a.d0, a.S0, a.eta, BH, a.T, (bf16 *)a.o,
-                     a.S_final, a.d_final, a.log_ratio_sum, (bf16 *)nullptr, (float *)nullptr,
-                     (float *)nullptr);
-  return hipGetLastError();
+  return a.alpha ? launch_mg<MODE, true>(a, kt, s) : launch_mg<MODE, false>(a, kt, s);
 }
 
 }  // namespace
@@ -953,12 +1018,12 @@ hipError_t launch_fused_scan(const ScanArgs &a, hipStream_t s) {
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
   const size_t shm = sizeof(Smem);
-  hipError_t e = hipFuncSetAttribute((const void *)osdn_fused_forward<kScan>,
+  hipError_t e = hipFuncSetAttribute((const void *)osdn_fused_forward<kScan, false>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(osdn_fused_forward<kScan>, dim3((unsigned)BH), dim3(NTH), shm, s,
+  hipLaunchKernelGGL((osdn_fused_forward<kScan, false>), dim3((unsigned)BH), dim3(NTH), shm, s,
                      (const bf16 *)nullptr, (const bf16 *)a.k, (const bf16 *)nullptr,
-                     (const bf16 *)nullptr, a.beta, a.r, a.d0, (const float *)nullptr, a.eta, BH,
+                     (const bf16 *)nullptr, a.beta, a.r, (const float *)nullptr, a.d0, (const float *)nullptr, a.eta, BH,
                      a.T, (bf16 *)nullptr, (float *)nullptr, a.d_final, a.log_ratio_sum,
                      (bf16 *)a.k_tilde, a.d_all, a.log_ratio);
   return hipGetLastError();
@@ -966,7 +1031,7 @@ hipError_t launch_fused_scan(const ScanArgs &a, hipStream_t s) {
 
 hipError_t launch_fused_chunk(const ChunkArgs &a, hipStream_t s) {
   if ((long)a.B * a.H == 0) return hipSuccess;
-  FusedArgs f{a.q, a.k, a.v, a.beta, nullptr, nullptr, a.S0, 0.f, a.B, a.H, a.T, a.dk, a.dv,
+  FusedArgs f{a.q, a.k, a.v, a.beta, nullptr, a.alpha, nullptr, a.S0, 0.f, a.B, a.H, a.T, a.dk, a.dv,
               a.chunk, a.dtype, 0, a.o, a.S_final, nullptr, nullptr};
   return launch_mode<kGiven>(f, a.k_tilde, s);
 }

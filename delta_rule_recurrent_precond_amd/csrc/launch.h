@@ -19,7 +19,7 @@ struct ScanArgs {
 
 struct ChunkArgs {
   const void *q, *k, *k_tilde, *v;
-  const float *beta, *S0;
+  const float *beta, *alpha, *S0;  // alpha: optional state gate
   int B, H, T, dk, dv, chunk, dtype;
   void *o;
   float *S_final;
@@ -27,7 +27,7 @@ struct ChunkArgs {
 
 struct FusedArgs {
   const void *q, *k, *v;
-  const float *beta, *r, *d0, *S0;
+  const float *beta, *r, *alpha, *d0, *S0;  // alpha: optional state gate
   float eta;
   int B, H, T, dk, dv, chunk, dtype;
   int precond_off;
@@ -37,7 +37,7 @@ struct FusedArgs {
 
 struct StepArgs {
   const void *q, *k, *v;
-  const float *beta, *r;
+  const float *beta, *r, *alpha;  // alpha: optional state gate
   float eta;
   int B, H, dk, dv, dtype;
   float *S, *d;   // updated in place

@@ -71,13 +71,13 @@ OSDN_EXPORT int osdn_precond_scan(const void *k, const float *beta, const float 
 }
 
 OSDN_EXPORT int osdn_step(const void *q, const void *k, const void *v, const float *beta,
-                          const float *r, float eta, int B, int H, int dk, int dv, int dtype,
+                          const float *r, const float *alpha, float eta, int B, int H, int dk, int dv, int dtype,
                           float *S, float *d, void *o, float *log_ratio, void *stream) {
   int st = check_sizes(B, H, 1, dk, dv, 16, dtype, true, false);
   if (st != OSDN_OK) return st;
   if ((long long)B * H == 0) return OSDN_OK;
   if (!q || !k || !v || !beta || !S || !d || !o) return OSDN_ERR_NULL;
-  osdn::StepArgs a{q, k, v, beta, r, eta, B, H, dk, dv, dtype, S, d, o, log_ratio};
+  osdn::StepArgs a{q, k, v, beta, r, alpha, eta, B, H, dk, dv, dtype, S, d, o, log_ratio};
   return hip_status(osdn::launch_step(a, (hipStream_t)stream));
 }
 
@@ -88,17 +88,19 @@ OSDN_EXPORT size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, i
 }
 
 OSDN_EXPORT int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde, const void *v,
-                               const float *beta, const float *S0, int B, int H, int T, int dk,
+                               const float *beta, const float *alpha, const float *S0, int B,
+                               int H, int T, int dk,
                                int dv, int chunk, int dtype, void *o, float *S_final,
                                void *workspace, size_t workspace_bytes, void *stream) {
   int st = check_sizes(B, H, T, dk, dv, chunk, dtype, true, true);
   if (st != OSDN_OK) return st;
   if ((long long)B * H == 0) return OSDN_OK;
   if (T > 0 && (!q || !k || !k_tilde || !v || !beta || !o)) return OSDN_ERR_NULL;
-  osdn::ChunkArgs a{q, k, k_tilde, v, beta, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
+  osdn::ChunkArgs a{q, k, k_tilde, v, beta, alpha, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
   hipStream_t s = (hipStream_t)stream;
   if (use_fused(dk, dv, chunk, dtype)) {
-    if (workspace && workspace_bytes >= osdn::split_workspace_bytes(B, H, T))
+    // the two-kernel pass has no state gate; a gated call runs the single kernel
+    if (!alpha && workspace && workspace_bytes >= osdn::split_workspace_bytes(B, H, T))
       return hip_status(osdn::launch_split_chunk(a, true, workspace, s));
     return hip_status(osdn::launch_fused_chunk(a, s));
   }
@@ -121,7 +123,7 @@ OSDN_EXPORT const char *osdn_forward_path(int B, int H, int T, int dk, int dv, i
 }
 
 OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
-                             const float *r, const float *d0, const float *S0, float eta, int B,
+                             const float *r, const float *alpha, const float *d0, const float *S0, float eta, int B,
                              int H, int T, int dk, int dv, int chunk, int dtype, unsigned flags,
                              void *o, float *S_final, float *d_final, float *log_ratio_sum,
                              void *workspace, size_t workspace_bytes, void *stream) {
@@ -134,7 +136,7 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   hipStream_t s = (hipStream_t)stream;
 
   if (use_fused(dk, dv, chunk, dtype)) {
-    osdn::FusedArgs a{q, k, v, beta, r, d0, S0, eta, B, H, T, dk, dv, chunk, dtype,
+    osdn::FusedArgs a{q, k, v, beta, r, alpha, d0, S0, eta, B, H, T, dk, dv, chunk, dtype,
                       off ? 1 : 0, o, S_final, d_final, log_ratio_sum};
     return hip_status(osdn::launch_fused_forward(a, s));
   }
@@ -157,6 +159,6 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
     st = hip_status(osdn::launch_precond_scan_serial(sa, s));
     if (st != OSDN_OK) return st;
   }
-  osdn::ChunkArgs ca{q, k, kt, v, beta, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
+  osdn::ChunkArgs ca{q, k, kt, v, beta, alpha, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
   return hip_status(osdn::launch_chunk_generic(ca, s));  // only shapes the fused kernel lacks
 }

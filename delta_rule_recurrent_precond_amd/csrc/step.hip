@@ -7,6 +7,7 @@
 // §2.3 (APF retention r), §3 (rho = (1 - beta a)^2) and the persistent (S, d)
 // state the efficiency claims rest on.  For one token:
 //   a = <d, k (.) k>,  n = ||k||^2,  kt = d (.) k
+//   S <- alpha S (optional state gate, Gated DeltaNet's decay)
 //   u = v - S k,  S <- S + beta u kt^T,  o = S q (after the write)
 //   rho = (1 - beta a)^2,  d <- r d + eta beta (1 - beta a) (k (.) k) / n  (0 if n = 0)
 //
@@ -25,7 +26,8 @@ constexpr int NT = 256;
 template <typename T, int DK>
 __global__ void __launch_bounds__(NT)
 osdn_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-                 const float *__restrict__ beta, const float *__restrict__ r, float eta, int dv,
+                 const float *__restrict__ beta, const float *__restrict__ r,
+                 const float *__restrict__ alpha, float eta, int dv,
                  float *__restrict__ S, float *__restrict__ d, T *__restrict__ o,
                  float *__restrict__ log_ratio) {
   constexpr int TPR = DK / 4;         // threads per row of S (4 columns each)
@@ -37,6 +39,7 @@ osdn_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long bh = blockIdx.x;
   const float bt = beta[bh];
+  const float at = alpha ? alpha[bh] : 1.0f;  // state gate
 
   // key statistics and the write key (fp32), one thread per dimension
   float pn = 0.f, pa = 0.f;
@@ -78,6 +81,7 @@ osdn_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   for (int j = tid / TPR; j < dv; j += RPP) {
     float *row = S + (bh * dv + j) * DK + c4;
     float4 s = *(const float4 *)row;
+    s.x *= at, s.y *= at, s.z *= at, s.w *= at;
     float sk = s.x * kc.x + s.y * kc.y + s.z * kc.z + s.w * kc.w;
     sk = group_sum<TPR>(sk);
     const float u = coef[0] * (Elem<T>::load(v + bh * dv + j) - sk);  // beta (v_j - (S k)_j)
@@ -107,7 +111,7 @@ hipError_t launch_t(const StepArgs &a, hipStream_t s) {
 #define OSDN_STEP(DKV)                                                                     \
   case DKV:                                                                                \
     hipLaunchKernelGGL((osdn_step_kernel<T, DKV>), dim3(BH), dim3(NT), 0, s, q, k, v,       \
-                       a.beta, a.r, a.eta, a.dv, a.S, a.d, o, a.log_ratio);                  \
+                       a.beta, a.r, a.alpha, a.eta, a.dv, a.S, a.d, o, a.log_ratio);                  \
     break;
   switch (a.dk) {
     OSDN_STEP(16)

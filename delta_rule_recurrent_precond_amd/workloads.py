@@ -7,8 +7,9 @@ L2-normalised per token in fp64, the gates go through a logistic sigmoid, and
 q/k/v are cast once (round-to-nearest-even) to the stored dtype.  Those stored
 bits are the inputs of every implementation.
 
-Draw order per seed: q, k, v, beta-logits, r-logits.  The recall workload
-draws its key pool, value pool and index sequence first.
+Draw order per seed: q, k, v, beta-logits, r-logits, alpha-logits (state
+gate, gated workloads only).  The recall workload draws its key pool, value
+pool and index sequence first.
 
 The pages measure on recall/perplexity datasets that are not available here;
 the repeated-key workload below stands in for the structure of their
@@ -42,6 +43,9 @@ class Workload:
     r_sigma: float = 1.0
     recall_pool: int = 0  # >0: repeated-key recall structure with this pool size
     seed: int = 0
+    gated: bool = False   # state gate alpha present (Gated DeltaNet backbone)
+    alpha_mu: float = 3.0
+    alpha_sigma: float = 1.0
 
     @property
     def tokens(self) -> int:
@@ -67,6 +71,11 @@ RECALL_VANILLA = Workload("recall x2 vanilla B2 H16 T16384 d128 C64 bf16", 2, 16
                           seed=1005)
 RECALL_APF = replace(RECALL_VANILLA, name="recall x2 APF B2 H16 T16384 d128 C64 bf16", apf=True)
 
+# The 1.3B-style layer on the Gated DeltaNet backbone: the same draws plus a
+# per-token state gate alpha = sigmoid(3 + N(0,1)) (mostly 0.88..0.98).
+L13B_APF_GATED = replace(L13B_APF, name="1.3B-layer APF gated B4 H16 T4096 d128 C64 bf16",
+                         gated=True)
+
 CONFIGS = {
     "tiny": TINY_F32,
     "340m": L340M_VANILLA,
@@ -74,6 +83,7 @@ CONFIGS = {
     "1.3b-apf": L13B_APF,
     "recall": RECALL_VANILLA,
     "recall-apf": RECALL_APF,
+    "1.3b-apf-gated": L13B_APF_GATED,
 }
 
 # The throughput metric is quoted on the 1.3B-style layer (H=16, dk=dv=128, T=4096).
@@ -115,11 +125,12 @@ class Inputs:
     r: Optional[torch.Tensor]  # [B,H,T] fp32 or None (no APF)
     eta: float
     workload: Workload
+    alpha: Optional[torch.Tensor] = None  # [B,H,T] fp32 state gate or None
 
     def to(self, device):
         mv = lambda t: None if t is None else t.to(device)
         return Inputs(mv(self.q), mv(self.k), mv(self.v), mv(self.beta), mv(self.r), self.eta,
-                      self.workload)
+                      self.workload, mv(self.alpha))
 
 
 def generate(w: Workload, seed: Optional[int] = None) -> Inputs:
@@ -145,7 +156,8 @@ def generate(w: Workload, seed: Optional[int] = None) -> Inputs:
         v = rng.standard_normal((B, H, T, dv))
     beta = _sigmoid(w.beta_mu + w.beta_sigma * rng.standard_normal((B, H, T)))
     r = _sigmoid(w.r_mu + w.r_sigma * rng.standard_normal((B, H, T))) if w.apf else None
-    return Inputs(_store(q, w.dtype), _store(k, w.dtype), _store(v, w.dtype),
-                  torch.from_numpy(beta).to(torch.float32),
-                  None if r is None else torch.from_numpy(r).to(torch.float32),
-                  float(w.eta), w)
+    alpha = (_sigmoid(w.alpha_mu + w.alpha_sigma * rng.standard_normal((B, H, T)))
+             if w.gated else None)
+    f32 = lambda x: None if x is None else torch.from_numpy(x).to(torch.float32)
+    return Inputs(_store(q, w.dtype), _store(k, w.dtype), _store(v, w.dtype), f32(beta), f32(r),
+                  float(w.eta), w, f32(alpha))

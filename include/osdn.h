@@ -40,6 +40,14 @@
  *    chunk (the last chunk is short).
  *  - Errors: every argument is checked before anything is enqueued; on error
  *    nothing is enqueued and a negative OSDN_ERR_* code is returned.
+ *  - State gate (osdn_chunk_fwd, osdn_forward, osdn_step): alpha [B][H][T]
+ *    fp32, or NULL for none.  The pages run OSDN on a Gated DeltaNet backbone
+ *    [summary §4] without printing its update; the plainest reading, used
+ *    here, decays the state before each token's read and write:
+ *      S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) kt_t^T.
+ *    alpha acts on S only; the preconditioner walk does not see it.  alpha = 1
+ *    gives the ungated results; alpha in [0, 1] is the intended range (decays
+ *    below 2^-126 over a chunk are flushed to zero).
  *  - Results are deterministic run to run (no floating-point atomics).
  *  - Non-finite inputs propagate; they are not checked.
  */
@@ -95,6 +103,11 @@ int osdn_precond_scan(const void *k, const float *beta, const float *r, const fl
  *   k_tilde   [B,H,T,dk] dtype   write-side keys (required if T > 0)
  *   v         [B,H,T,dv] dtype   values (required if T > 0)
  *   beta      [B,H,T]    fp32    (required if T > 0)
+ *   alpha     [B,H,T]    fp32    state gate; NULL means none.  With it, gamma_t
+ *                                the product of alpha over the chunk up to t:
+ *                                A_ts and the scores take gamma_t / gamma_s,
+ *                                K S^T and Q S^T take gamma_t, and
+ *                                S <- gamma_L S + sum_s (gamma_L / gamma_s) x_s kt_s^T
  *   S0        [B,H,dv,dk] fp32   initial state; NULL means zero
  *   chunk                        chunk length
  *   o         [B,H,T,dv] dtype   out: o_t = S_t q_t (required if T > 0)
@@ -102,12 +115,13 @@ int osdn_precond_scan(const void *k, const float *beta, const float *r, const fl
  *   workspace  optional device scratch.  When it holds at least
  *              osdn_chunk_fwd_workspace_bytes(...) bytes (a positive number),
  *              the per-chunk work runs chunk-parallel ahead of the sequential
- *              pass (faster); NULL selects the single-kernel pass.
+ *              pass (faster, ungated calls only); NULL selects the single-kernel
+ *              pass.
  */
 int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde, const void *v,
-                   const float *beta, const float *S0, int B, int H, int T, int dk, int dv,
-                   int chunk, int dtype, void *o, float *S_final, void *workspace,
-                   size_t workspace_bytes, void *stream);
+                   const float *beta, const float *alpha, const float *S0, int B, int H,
+                   int T, int dk, int dv, int chunk, int dtype, void *o, float *S_final,
+                   void *workspace, size_t workspace_bytes, void *stream);
 
 /* Scratch bytes that let osdn_chunk_fwd run its chunk-parallel path (0 when
  * no path for these arguments uses scratch); (size_t)-1 if the arguments are
@@ -116,7 +130,8 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
 
 /*
  * Both phases end to end [summary §2.2 two-phase implementation].
- *   q, k, v, beta, r, d0, S0, eta   as above
+ *   q, k, v, beta, r, alpha, d0, S0, eta   as above; with OSDN_PRECOND_OFF and
+ *                  alpha this is Gated DeltaNet itself
  *   flags          0 or OSDN_PRECOND_OFF
  *   o              [B,H,T,dv] dtype out (required if T > 0)
  *   S_final        [B,H,dv,dk] fp32 out (optional)
@@ -128,15 +143,16 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  *                  bytes (may be NULL when that is 0)
  */
 int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
-                 const float *r, const float *d0, const float *S0, float eta, int B, int H,
-                 int T, int dk, int dv, int chunk, int dtype, unsigned flags, void *o,
-                 float *S_final, float *d_final, float *log_ratio_sum, void *workspace,
-                 size_t workspace_bytes, void *stream);
+                 const float *r, const float *alpha, const float *d0, const float *S0,
+                 float eta, int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                 unsigned flags, void *o, float *S_final, float *d_final,
+                 float *log_ratio_sum, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decoding step with persistent state [summary §2.1-§2.3, §3; the
  * efficiency claims concern this per-token update]: for one token per (b,h),
- *   kt = d (.) k,  S <- S + beta (v - S k) kt^T,  o = S q  (after the write),
+ *   kt = d (.) k,  S <- alpha S (if gated),  S <- S + beta (v - S k) kt^T,
+ *   o = S q  (after the write),
  *   rho = (1 - beta <d, k (.) k>)^2,
  *   d <- r d + eta beta (1 - beta <d, k (.) k>) (k (.) k) / ||k||^2  (0 if k = 0).
  * Running it for t = 0..T-1 gives the same o, S and d as osdn_forward over the
@@ -145,6 +161,7 @@ int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
  *   v         [B,H,dv] dtype     value (required)
  *   beta      [B,H]    fp32      write gate (required)
  *   r         [B,H]    fp32      APF retention gate; NULL means r = 1
+ *   alpha     [B,H]    fp32      state gate; NULL means none
  *   S         [B,H,dv,dk] fp32   state, read and updated in place (required)
  *   d         [B,H,dk] fp32      preconditioner, read and updated in place (required)
  *   o         [B,H,dv] dtype     out: the readout (required)
@@ -152,7 +169,7 @@ int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
  * S, d and o must not overlap each other or the inputs.
  */
 int osdn_step(const void *q, const void *k, const void *v, const float *beta, const float *r,
-              float eta, int B, int H, int dk, int dv, int dtype, float *S, float *d, void *o,
+              const float *alpha, float eta, int B, int H, int dk, int dv, int dtype, float *S, float *d, void *o,
               float *log_ratio, void *stream);
 
 /* Scratch bytes osdn_forward needs for these arguments (0 when the fused

@@ -56,7 +56,7 @@ NULL = None
 
 def _fwd(lib, B=1, H=1, T=4, dk=16, dv=16, chunk=16, dtype=0, flags=0, ptr=1):
     p = ptr  # non-NULL dummy address: never dereferenced on these paths
-    return lib.osdn_forward(p, p, p, p, None, None, None, 0.1, B, H, T, dk, dv, chunk, dtype,
+    return lib.osdn_forward(p, p, p, p, None, None, None, None, 0.1, B, H, T, dk, dv, chunk, dtype,
                             flags, p, None, None, None, None, 0, None)
 
 
@@ -87,7 +87,7 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.osdn_forward_path(0, 4, 8, 16, 16, 16, 0, 0).decode() == "none"
     assert lib.osdn_precond_scan(None, None, None, None, 0.1, 3, 0, 5, 16, 0, None, None, None,
                                  None, None) == _lib.OSDN_OK
-    assert lib.osdn_chunk_fwd(None, None, None, None, None, None, 0, 2, 5, 16, 16, 16, 0, None,
+    assert lib.osdn_chunk_fwd(None, None, None, None, None, None, None, 0, 2, 5, 16, 16, 16, 0, None,
                               None, None, 0, None) == _lib.OSDN_OK
 
 
@@ -99,23 +99,23 @@ def test_scan_and_chunk_reject(lib):
                                  None) == _lib.OSDN_ERR_NULL
     assert lib.osdn_precond_scan(p, p, None, None, 0.1, 1, 1, 4, 16, 0, None, None, None, None,
                                  None) == _lib.OSDN_ERR_NULL
-    assert lib.osdn_chunk_fwd(p, p, None, p, p, None, 1, 1, 4, 16, 16, 16, 0, p, None,
+    assert lib.osdn_chunk_fwd(p, p, None, p, p, None, None, 1, 1, 4, 16, 16, 16, 0, p, None,
                               None, 0, None) == _lib.OSDN_ERR_NULL
-    assert lib.osdn_chunk_fwd(p, p, p, p, p, None, 1, 1, 4, 16, 16, 8, 0, p, None,
+    assert lib.osdn_chunk_fwd(p, p, p, p, p, None, None, 1, 1, 4, 16, 16, 8, 0, p, None,
                               None, 0, None) == _lib.OSDN_ERR_UNSUPPORTED
-    assert lib.osdn_chunk_fwd(p, p, p, p, p, None, 1, -1, 4, 16, 16, 16, 0, p, None,
+    assert lib.osdn_chunk_fwd(p, p, p, p, p, None, None, 1, -1, 4, 16, 16, 16, 0, p, None,
                               None, 0, None) == _lib.OSDN_ERR_SHAPE
 
 
 def test_step_rejects(lib):
     p = 1
-    assert lib.osdn_step(None, None, None, None, None, 0.1, 0, 4, 16, 16, 0, None, None, None,
+    assert lib.osdn_step(None, None, None, None, None, None, 0.1, 0, 4, 16, 16, 0, None, None, None,
                          None, None) == _lib.OSDN_OK
-    assert lib.osdn_step(p, p, p, p, None, 0.1, 1, 1, 16, 16, 0, None, p, p, None,
+    assert lib.osdn_step(p, p, p, p, None, None, 0.1, 1, 1, 16, 16, 0, None, p, p, None,
                          None) == _lib.OSDN_ERR_NULL
-    assert lib.osdn_step(p, p, p, p, None, 0.1, 1, 1, 24, 16, 0, p, p, p, None,
+    assert lib.osdn_step(p, p, p, p, None, None, 0.1, 1, 1, 24, 16, 0, p, p, p, None,
                          None) == _lib.OSDN_ERR_UNSUPPORTED
-    assert lib.osdn_step(p, p, p, p, None, 0.1, 1, -2, 16, 16, 0, p, p, p, None,
+    assert lib.osdn_step(p, p, p, p, None, None, 0.1, 1, -2, 16, 16, 0, p, p, p, None,
                          None) == _lib.OSDN_ERR_SHAPE
 
 
