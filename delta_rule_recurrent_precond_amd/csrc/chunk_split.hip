@@ -234,9 +234,11 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // ---------------------------------------------------------------------------
 // chunk_state: one workgroup of 8 waves per (b, h, 32 value channels),
 // sequential over chunks.  Waves 0 and 1 run the pass on channels 16w..16w+15
-// of the tile from one LDS buffer while waves 2-7 load the operands of the
-// next chunk and store them into the other (the loads are spread over six
-// waves so that enough of them are in flight).  One barrier per chunk.
+// of the tile from one LDS buffer while waves 2-7 store the operands of the
+// next chunk into the other.  The loaders keep two chunks of operands in
+// registers: the global loads of chunk c+2 are issued before chunk c+1 is
+// stored, so a load has two iterations to arrive (the latency of a burst of
+// loads from every CU is longer than one iteration).  One barrier per chunk.
 // ---------------------------------------------------------------------------
 constexpr int ST = 512;  // threads
 constexpr int VP = 40;   // padded row (halves) of the staged [64][32] value tile
@@ -293,42 +295,49 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
   // Loads are unconditional (a masked lane reads a valid address) and masked
   // values are zeroed when stored: a conditional load makes the compiler wait
   // for it at the end of its branch.
-  uint4 lkq[NKQ], lv, lr[NR];
-  float lb = 0.f;
-  int lL = 0;  // valid rows of the chunk in the registers
-  auto load = [&](int cc) {
+  struct Regs {
+    uint4 kq[NKQ], v, r[NR];
+    float b;
+    int L;  // valid rows of the chunk held
+  };
+  Regs ra, rb;
+  // chunk cc clamped to the last one: the loads past the end reread it
+  auto load = [&](Regs &R, int cc) {
+    cc = min(cc, NC - 1);
     const long t0 = (long)bh * T_ + (long)cc * C;
     const int L = min(C, T_ - cc * C);
-    lL = L;
+    R.L = L;
 #pragma unroll
     for (int u = 0; u < NKQ; ++u) {
       const int p = min(lt + NL * u, 2047), pp = p & 1023, t = min(pp >> 4, L - 1);
-      lkq[u] = *(const uint4 *)((p < 1024 ? k : q) + (t0 + t) * DK + (pp & 15) * 8);  // k or q
+      R.kq[u] = *(const uint4 *)((p < 1024 ? k : q) + (t0 + t) * DK + (pp & 15) * 8);  // k or q
     }
     {
       const int t = min((lt & 255) >> 2, L - 1);
-      lv = *(const uint4 *)(v + (t0 + t) * 128 + j0 + (lt & 3) * 8);
+      R.v = *(const uint4 *)(v + (t0 + t) * 128 + j0 + (lt & 3) * 8);
     }
     const uint4 *rs = (const uint4 *)(ws + ((long)bh * NC + cc) * REC);
 #pragma unroll
-    for (int u = 0; u < NR; ++u) lr[u] = rs[min(lt + NL * u, RECP - 1)];
-    lb = beta[t0 + min(lt & 63, L - 1)];
+    for (int u = 0; u < NR; ++u) R.r[u] = rs[min(lt + NL * u, RECP - 1)];
+    R.b = beta[t0 + min(lt & 63, L - 1)];
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](const Regs &R, int buf) {
     const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int u = 0; u < NKQ; ++u) {
       const int p = lt + NL * u, pp = p & 1023, t = pp >> 4, i0 = (pp & 15) * 8;
-      if (p < 2048) *(f16x8 *)&(p < 1024 ? sm.K : sm.Q)[buf][t * KP + i0] = t < lL ? cvt8(lkq[u]) : z8;
+      if (p < 2048)
+        *(f16x8 *)&(p < 1024 ? sm.K : sm.Q)[buf][t * KP + i0] = t < R.L ? cvt8(R.kq[u]) : z8;
     }
-    if (lt < 256) *(f16x8 *)&sm.V[buf][(lt >> 2) * VP + (lt & 3) * 8] = (lt >> 2) < lL ? cvt8(lv) : z8;
+    if (lt < 256)
+      *(f16x8 *)&sm.V[buf][(lt >> 2) * VP + (lt & 3) * 8] = (lt >> 2) < R.L ? cvt8(R.v) : z8;
     uint4 *rd = (uint4 *)sm.rec[buf];
 #pragma unroll
     for (int u = 0; u < NR; ++u) {
       const int p = lt + NL * u;
-      if (p < RECP) rd[p] = lr[u];
+      if (p < RECP) rd[p] = R.r[u];
     }
-    if (lt < C) sm.b[buf][lt] = lt < lL ? lb : 0.f;
+    if (lt < C) sm.b[buf][lt] = lt < R.L ? R.b : 0.f;
   };
 
   f32x4 Sacc[8];
@@ -346,87 +355,102 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
   for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
 
   if (NC > 0 && wave >= 2) {
-    load(0);
-    stash(0);
+    load(ra, 0);
+    load(rb, 1);
+    stash(ra, 0);
   }
   __syncthreads();
 
-  for (int c = 0; c < NC; ++c) {
-    const int cb = c & 1;
-    if (wave >= 2 && c + 1 < NC) load(c + 1);
-    if (wave < 2) {
-    const long tok0 = (long)bh * T_ + (long)c * C;
-    const int L = min(C, T_ - c * C);
-    const f16 *Kc = sm.K[cb], *Qc = sm.Q[cb];
-    const f16x8 *KtF = (const f16x8 *)(sm.rec[cb] + OFF_KTF);
-    const f16x8 *TmA = (const f16x8 *)(sm.rec[cb] + OFF_TM);
-    const f16x8 *PA = (const f16x8 *)(sm.rec[cb] + OFF_P);
-    const float ds = *(const float *)(sm.rec[cb] + OFF_DS);
-
-    // K S^T and Q S^T
-    f32x4 KS[4], O[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f16 *kr = &Kc[(16 * m + c16) * KP], *qr = &Qc[(16 * m + c16) * KP];
-      f32x4 a = zero4(), b = zero4();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        a = mma32(ldpk(kr, 32 * kk, g), Sb[kk], a);
-        b = mma32(ldpk(qr, 32 * kk, g), Sb[kk], b);
+  // Chunk c runs from LDS buffer c & 1.  Entering iteration c the loaders hold
+  // chunk c+1 in one register set; they load chunk c+2 into the other (freed by
+  // the previous store), then store chunk c+1.  The loaders' loop is written
+  // for two iterations so that the register sets keep fixed names; the two
+  // roles run separate loops with the same barrier count, so their registers
+  // are never live at the same time.
+  if (wave >= 2) {
+    for (int c = 0; c < NC; c += 2) {
+      load(ra, c + 2);
+      if (c + 1 < NC) stash(rb, 1);
+      __syncthreads();
+      if (c + 1 < NC) {
+        load(rb, c + 3);
+        if (c + 2 < NC) stash(ra, 0);
+        __syncthreads();
       }
-      KS[m] = a;
-      O[m] = b;
     }
-    // R = diag(beta)(V - K S^T), values turned into the result layout
-    f16x4 rr[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f16x4 vv =
-          h4(mma16(ld4(&sm.V[cb][(16 * m + c16) * VP + 16 * wave + 4 * g]), ident, zero4()));
-      const f32x4 b4 = *(const f32x4 *)&sm.b[cb][16 * m + 4 * g];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rr[m][e] = h(b4[e] * ((float)vv[e] - KS[m][e]));
-    }
-    const f16x8 Rb[2] = {cat(rr[0], rr[1]), cat(rr[2], rr[3])};
-    // X = T R
-    f32x4 X[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int qq = 0; qq <= (m >> 1); ++qq)
-        acc = mma32(TmA[op_index(m, qq) * 64 + lane], Rb[qq], acc);
-      X[m] = acc;
-    }
-    const f16x8 Xb[2] = {cat(h4(X[0]), h4(X[1])), cat(h4(X[2]), h4(X[3]))};
-    // S^T += ds Kt^T X
-#pragma unroll
-    for (int i8 = 0; i8 < 8; ++i8) {
-      f32x4 u = zero4();
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq) u = mma32(KtF[(i8 * 2 + qq) * 64 + lane], Xb[qq], u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Sacc[i8][e] = fmaf(ds, u[e], Sacc[i8][e]);
-    }
-    // O = Q S^T + P X, stored as bf16 through an identity transpose
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-      for (int qq = 0; qq <= (m >> 1); ++qq)
-        O[m] = mma32(PA[op_index(m, qq) * 64 + lane], Xb[qq], O[m]);
-      const bf16x4 ob = {(bf16)O[m][0], (bf16)O[m][1], (bf16)O[m][2], (bf16)O[m][3]};
-      const f32x4 ot = mma16bf(ob, identb, zero4());
-      const int t = 16 * m + c16;
-      if (t < L)
-        *(bf16x4 *)(o + (tok0 + t) * 128 + j0 + 16 * wave + 4 * g) =
-            bf16x4{(bf16)ot[0], (bf16)ot[1], (bf16)ot[2], (bf16)ot[3]};
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
-    }
+  } else {
+    for (int c = 0; c < NC; ++c) {
+      const int cb = c & 1;
+      const long tok0 = (long)bh * T_ + (long)c * C;
+      const int L = min(C, T_ - c * C);
+      const f16 *Kc = sm.K[cb], *Qc = sm.Q[cb];
+      const f16x8 *KtF = (const f16x8 *)(sm.rec[cb] + OFF_KTF);
+      const f16x8 *TmA = (const f16x8 *)(sm.rec[cb] + OFF_TM);
+      const f16x8 *PA = (const f16x8 *)(sm.rec[cb] + OFF_P);
+      const float ds = *(const float *)(sm.rec[cb] + OFF_DS);
 
-    if (wave >= 2 && c + 1 < NC) stash(cb ^ 1);
-    __syncthreads();
+      // K S^T and Q S^T
+      f32x4 KS[4], O[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f16 *kr = &Kc[(16 * m + c16) * KP], *qr = &Qc[(16 * m + c16) * KP];
+        f32x4 a = zero4(), b = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          a = mma32(ldpk(kr, 32 * kk, g), Sb[kk], a);
+          b = mma32(ldpk(qr, 32 * kk, g), Sb[kk], b);
+        }
+        KS[m] = a;
+        O[m] = b;
+      }
+      // R = diag(beta)(V - K S^T), values turned into the result layout
+      f16x4 rr[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f16x4 vv =
+            h4(mma16(ld4(&sm.V[cb][(16 * m + c16) * VP + 16 * wave + 4 * g]), ident, zero4()));
+        const f32x4 b4 = *(const f32x4 *)&sm.b[cb][16 * m + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rr[m][e] = h(b4[e] * ((float)vv[e] - KS[m][e]));
+      }
+      const f16x8 Rb[2] = {cat(rr[0], rr[1]), cat(rr[2], rr[3])};
+      // X = T R
+      f32x4 X[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int qq = 0; qq <= (m >> 1); ++qq)
+          acc = mma32(TmA[op_index(m, qq) * 64 + lane], Rb[qq], acc);
+        X[m] = acc;
+      }
+      const f16x8 Xb[2] = {cat(h4(X[0]), h4(X[1])), cat(h4(X[2]), h4(X[3]))};
+      // S^T += ds Kt^T X
+#pragma unroll
+      for (int i8 = 0; i8 < 8; ++i8) {
+        f32x4 u = zero4();
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) u = mma32(KtF[(i8 * 2 + qq) * 64 + lane], Xb[qq], u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[i8][e] = fmaf(ds, u[e], Sacc[i8][e]);
+      }
+      // O = Q S^T + P X, stored as bf16 through an identity transpose
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int qq = 0; qq <= (m >> 1); ++qq)
+          O[m] = mma32(PA[op_index(m, qq) * 64 + lane], Xb[qq], O[m]);
+        const bf16x4 ob = {(bf16)O[m][0], (bf16)O[m][1], (bf16)O[m][2], (bf16)O[m][3]};
+        const f32x4 ot = mma16bf(ob, identb, zero4());
+        const int t = 16 * m + c16;
+        if (t < L)
+          *(bf16x4 *)(o + (tok0 + t) * 128 + j0 + 16 * wave + 4 * g) =
+              bf16x4{(bf16)ot[0], (bf16)ot[1], (bf16)ot[2], (bf16)ot[3]};
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
+      __syncthreads();
+    }
   }
 
   if (S_final && wave < 2) {
