@@ -232,16 +232,25 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
-// chunk_state: one workgroup of 8 waves per (b, h, 32 value channels),
-// sequential over chunks.  Waves 0 and 1 run the pass on channels 16w..16w+15
-// of the tile from one LDS buffer while waves 2-7 store the operands of the
-// next chunk into the other.  The loaders keep two chunks of operands in
-// registers: the global loads of chunk c+2 are issued before chunk c+1 is
-// stored, so a load has two iterations to arrive (the latency of a burst of
-// loads from every CU is longer than one iteration).  One barrier per chunk.
+// chunk_state: one workgroup of 12 waves per (b, h, 32 value channels),
+// sequential over chunks, one barrier per chunk.  Per 16-channel sub-tile sn:
+//   wave sn (the state chain)  K S^T, R = diag(beta)(V - K S^T), X = T R,
+//                              S^T += ds Kt^T X; passes X and the new fp16 S^T
+//                              to the output wave through LDS
+//   wave 2 + sn (the outputs)  Q S^T of chunk c (from the S^T the chain wave
+//                              left), then in the next iteration
+//                              O = Q S^T + P X of chunk c and its stores
+//   waves 4-11 (loaders)       global loads of chunk c+2, LDS stores of c+1
+// The output wave keeps Q S^T and the score operands of chunk c in registers
+// so that the loaders may refill that chunk's LDS buffer.  The loaders keep two
+// chunks in registers: the loads of chunk c+2 are issued before chunk c+1 is
+// stored, so a burst of loads from every CU has two iterations to arrive.
+// Each role runs its own loop with the same barrier count (NC + 1), so the
+// registers of different roles are never live at the same time.
 // ---------------------------------------------------------------------------
-constexpr int ST = 512;  // threads
-constexpr int VP = 40;   // padded row (halves) of the staged [64][32] value tile
+constexpr int ST = 768;        // threads
+constexpr int NL = ST - 256;   // loader lanes
+constexpr int VP = 40;         // padded row (halves) of the staged [64][32] value tile
 
 struct StateSmem {
   f16 K[2][C * KP];
@@ -249,6 +258,8 @@ struct StateSmem {
   f16 V[2][C * VP];
   unsigned char rec[2][OFF_DS + 16];  // KtF, TmA, PA, ds of the chunk
   float b[2][C];
+  f16x8 Sx[2][2][4][64];  // fp16 S^T at a chunk's start [parity][sn][kk][lane], paired order
+  f16x8 Xx[2][2][2][64];  // X of a chunk [parity][sn][qq][lane], paired order
 };
 static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
 
@@ -274,8 +285,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       tile = b & 3;
     }
   }
-  const int j0 = 32 * tile;            // first channel of the tile
-  const int jcol = j0 + 16 * wave + c16;
+  const int j0 = 32 * tile;  // first channel of the tile
 
   f16x4 ident;
   bf16x4 identb;
@@ -285,89 +295,69 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     identb[e] = (4 * g + e == c16) ? (bf16)1.0f : (bf16)0.0f;
   }
 
-  // loader registers (waves 2-7, index lt): k and q as 2048 pieces of 8
-  // elements, the value tile as 256, the record as OFF_DS/16 + 1 = 1793 pieces
-  // of 16 bytes, beta
-  constexpr int NL = ST - 128;
-  constexpr int RECP = OFF_DS / 16 + 1;
-  constexpr int NKQ = (2048 + NL - 1) / NL, NR = (RECP + NL - 1) / NL;
-  const int lt = tid - 128;
-  // Loads are unconditional (a masked lane reads a valid address) and masked
-  // values are zeroed when stored: a conditional load makes the compiler wait
-  // for it at the end of its branch.
-  struct Regs {
-    uint4 kq[NKQ], v, r[NR];
-    float b;
-    int L;  // valid rows of the chunk held
-  };
-  Regs ra, rb;
-  // chunk cc clamped to the last one: the loads past the end reread it
-  auto load = [&](Regs &R, int cc) {
-    cc = min(cc, NC - 1);
-    const long t0 = (long)bh * T_ + (long)cc * C;
-    const int L = min(C, T_ - cc * C);
-    R.L = L;
+  if (wave >= 4) {
+    // ================================ loaders ================================
+    // k and q as 2048 pieces of 8 elements, the value tile as 256, the record as
+    // OFF_DS/16 + 1 = 1793 pieces of 16 bytes, beta.  Loads are unconditional (a
+    // masked lane reads a valid address) and masked values are zeroed when
+    // stored: a conditional load makes the compiler wait for it at the end of
+    // its branch.
+    constexpr int RECP = OFF_DS / 16 + 1;
+    constexpr int NKQ = (2048 + NL - 1) / NL, NR = (RECP + NL - 1) / NL;
+    const int lt = tid - 256;
+    struct Regs {
+      uint4 kq[NKQ], v, r[NR];
+      float b;
+      int L;  // valid rows of the chunk held
+    };
+    Regs ra, rb;
+    // chunk cc clamped to the last one: the loads past the end reread it
+    auto load = [&](Regs &R, int cc) {
+      cc = min(cc, NC - 1);
+      const long t0 = (long)bh * T_ + (long)cc * C;
+      const int L = min(C, T_ - cc * C);
+      R.L = L;
 #pragma unroll
-    for (int u = 0; u < NKQ; ++u) {
-      const int p = min(lt + NL * u, 2047), pp = p & 1023, t = min(pp >> 4, L - 1);
-      R.kq[u] = *(const uint4 *)((p < 1024 ? k : q) + (t0 + t) * DK + (pp & 15) * 8);  // k or q
+      for (int u = 0; u < NKQ; ++u) {
+        const int p = min(lt + NL * u, 2047), pp = p & 1023, t = min(pp >> 4, L - 1);
+        R.kq[u] = *(const uint4 *)((p < 1024 ? k : q) + (t0 + t) * DK + (pp & 15) * 8);
+      }
+      {
+        const int t = min((lt & 255) >> 2, L - 1);
+        R.v = *(const uint4 *)(v + (t0 + t) * 128 + j0 + (lt & 3) * 8);
+      }
+      const uint4 *rs = (const uint4 *)(ws + ((long)bh * NC + cc) * REC);
+#pragma unroll
+      for (int u = 0; u < NR; ++u) R.r[u] = rs[min(lt + NL * u, RECP - 1)];
+      R.b = beta[t0 + min(lt & 63, L - 1)];
+    };
+    auto stash = [&](const Regs &R, int buf) {
+      const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < NKQ; ++u) {
+        const int p = lt + NL * u, pp = p & 1023, t = pp >> 4, i0 = (pp & 15) * 8;
+        if (p < 2048)
+          *(f16x8 *)&(p < 1024 ? sm.K : sm.Q)[buf][t * KP + i0] = t < R.L ? cvt8(R.kq[u]) : z8;
+      }
+      if (lt < 256)
+        *(f16x8 *)&sm.V[buf][(lt >> 2) * VP + (lt & 3) * 8] = (lt >> 2) < R.L ? cvt8(R.v) : z8;
+      uint4 *rd = (uint4 *)sm.rec[buf];
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int p = lt + NL * u;
+        if (p < RECP) rd[p] = R.r[u];
+      }
+      if (lt < C) sm.b[buf][lt] = lt < R.L ? R.b : 0.f;
+    };
+    if (NC > 0) {
+      load(ra, 0);
+      load(rb, 1);
+      stash(ra, 0);
     }
-    {
-      const int t = min((lt & 255) >> 2, L - 1);
-      R.v = *(const uint4 *)(v + (t0 + t) * 128 + j0 + (lt & 3) * 8);
-    }
-    const uint4 *rs = (const uint4 *)(ws + ((long)bh * NC + cc) * REC);
-#pragma unroll
-    for (int u = 0; u < NR; ++u) R.r[u] = rs[min(lt + NL * u, RECP - 1)];
-    R.b = beta[t0 + min(lt & 63, L - 1)];
-  };
-  auto stash = [&](const Regs &R, int buf) {
-    const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int u = 0; u < NKQ; ++u) {
-      const int p = lt + NL * u, pp = p & 1023, t = pp >> 4, i0 = (pp & 15) * 8;
-      if (p < 2048)
-        *(f16x8 *)&(p < 1024 ? sm.K : sm.Q)[buf][t * KP + i0] = t < R.L ? cvt8(R.kq[u]) : z8;
-    }
-    if (lt < 256)
-      *(f16x8 *)&sm.V[buf][(lt >> 2) * VP + (lt & 3) * 8] = (lt >> 2) < R.L ? cvt8(R.v) : z8;
-    uint4 *rd = (uint4 *)sm.rec[buf];
-#pragma unroll
-    for (int u = 0; u < NR; ++u) {
-      const int p = lt + NL * u;
-      if (p < RECP) rd[p] = R.r[u];
-    }
-    if (lt < C) sm.b[buf][lt] = lt < R.L ? R.b : 0.f;
-  };
-
-  f32x4 Sacc[8];
-  f16x8 Sb[4];
-#pragma unroll
-  for (int i8 = 0; i8 < 8; ++i8) Sacc[i8] = zero4();
-  if (S0 && wave < 2) {
-#pragma unroll
-    for (int i8 = 0; i8 < 8; ++i8) {
-      const float4 s4 = *(const float4 *)(S0 + ((long)bh * 128 + jcol) * DK + 16 * i8 + 4 * g);
-      Sacc[i8] = f32x4{s4.x, s4.y, s4.z, s4.w};
-    }
-  }
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
-
-  if (NC > 0 && wave >= 2) {
-    load(ra, 0);
-    load(rb, 1);
-    stash(ra, 0);
-  }
-  __syncthreads();
-
-  // Chunk c runs from LDS buffer c & 1.  Entering iteration c the loaders hold
-  // chunk c+1 in one register set; they load chunk c+2 into the other (freed by
-  // the previous store), then store chunk c+1.  The loaders' loop is written
-  // for two iterations so that the register sets keep fixed names; the two
-  // roles run separate loops with the same barrier count, so their registers
-  // are never live at the same time.
-  if (wave >= 2) {
+    __syncthreads();
+    // Entering iteration c the loaders hold chunk c+1 in one register set; they
+    // load chunk c+2 into the other (freed by the previous store), then store
+    // chunk c+1.  Written for two iterations so that the sets keep fixed names.
     for (int c = 0; c < NC; c += 2) {
       load(ra, c + 2);
       if (c + 1 < NC) stash(rb, 1);
@@ -378,40 +368,49 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         __syncthreads();
       }
     }
-  } else {
+    __syncthreads();  // the output waves' last iteration
+  } else if (wave < 2) {
+    // ============================== state chain ==============================
+    const int sn = wave;
+    const int jcol = j0 + 16 * sn + c16;
+    f32x4 Sacc[8];  // S^T tiles: rows i = 16 i8 + 4g + e, column jcol
+    f16x8 Sb[4];    // S^T in the paired k order
+#pragma unroll
+    for (int i8 = 0; i8 < 8; ++i8) Sacc[i8] = zero4();
+    if (S0) {
+#pragma unroll
+      for (int i8 = 0; i8 < 8; ++i8) {
+        const float4 s4 = *(const float4 *)(S0 + ((long)bh * 128 + jcol) * DK + 16 * i8 + 4 * g);
+        Sacc[i8] = f32x4{s4.x, s4.y, s4.z, s4.w};
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
+      sm.Sx[0][sn][kk][lane] = Sb[kk];
+    }
+    __syncthreads();
+
     for (int c = 0; c < NC; ++c) {
       const int cb = c & 1;
-      const long tok0 = (long)bh * T_ + (long)c * C;
-      const int L = min(C, T_ - c * C);
-      const f16 *Kc = sm.K[cb], *Qc = sm.Q[cb];
+      const f16 *Kc = sm.K[cb];
       const f16x8 *KtF = (const f16x8 *)(sm.rec[cb] + OFF_KTF);
       const f16x8 *TmA = (const f16x8 *)(sm.rec[cb] + OFF_TM);
-      const f16x8 *PA = (const f16x8 *)(sm.rec[cb] + OFF_P);
       const float ds = *(const float *)(sm.rec[cb] + OFF_DS);
-
-      // K S^T and Q S^T
-      f32x4 KS[4], O[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f16 *kr = &Kc[(16 * m + c16) * KP], *qr = &Qc[(16 * m + c16) * KP];
-        f32x4 a = zero4(), b = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          a = mma32(ldpk(kr, 32 * kk, g), Sb[kk], a);
-          b = mma32(ldpk(qr, 32 * kk, g), Sb[kk], b);
-        }
-        KS[m] = a;
-        O[m] = b;
-      }
-      // R = diag(beta)(V - K S^T), values turned into the result layout
+      // K S^T, then R = diag(beta)(V - K S^T) with the values turned into the
+      // result layout
       f16x4 rr[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
+        const f16 *kr = &Kc[(16 * m + c16) * KP];
+        f32x4 a = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) a = mma32(ldpk(kr, 32 * kk, g), Sb[kk], a);
         const f16x4 vv =
-            h4(mma16(ld4(&sm.V[cb][(16 * m + c16) * VP + 16 * wave + 4 * g]), ident, zero4()));
+            h4(mma16(ld4(&sm.V[cb][(16 * m + c16) * VP + 16 * sn + 4 * g]), ident, zero4()));
         const f32x4 b4 = *(const f32x4 *)&sm.b[cb][16 * m + 4 * g];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rr[m][e] = h(b4[e] * ((float)vv[e] - KS[m][e]));
+        for (int e = 0; e < 4; ++e) rr[m][e] = h(b4[e] * ((float)vv[e] - a[e]));
       }
       const f16x8 Rb[2] = {cat(rr[0], rr[1]), cat(rr[2], rr[3])};
       // X = T R
@@ -425,6 +424,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         X[m] = acc;
       }
       const f16x8 Xb[2] = {cat(h4(X[0]), h4(X[1])), cat(h4(X[2]), h4(X[3]))};
+      sm.Xx[cb][sn][0][lane] = Xb[0];
+      sm.Xx[cb][sn][1][lane] = Xb[1];
       // S^T += ds Kt^T X
 #pragma unroll
       for (int i8 = 0; i8 < 8; ++i8) {
@@ -434,30 +435,68 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 #pragma unroll
         for (int e = 0; e < 4; ++e) Sacc[i8][e] = fmaf(ds, u[e], Sacc[i8][e]);
       }
-      // O = Q S^T + P X, stored as bf16 through an identity transpose
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-#pragma unroll
-        for (int qq = 0; qq <= (m >> 1); ++qq)
-          O[m] = mma32(PA[op_index(m, qq) * 64 + lane], Xb[qq], O[m]);
-        const bf16x4 ob = {(bf16)O[m][0], (bf16)O[m][1], (bf16)O[m][2], (bf16)O[m][3]};
-        const f32x4 ot = mma16bf(ob, identb, zero4());
-        const int t = 16 * m + c16;
-        if (t < L)
-          *(bf16x4 *)(o + (tok0 + t) * 128 + j0 + 16 * wave + 4 * g) =
-              bf16x4{(bf16)ot[0], (bf16)ot[1], (bf16)ot[2], (bf16)ot[3]};
+      for (int kk = 0; kk < 4; ++kk) {
+        Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
+        sm.Sx[cb ^ 1][sn][kk][lane] = Sb[kk];
       }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
       __syncthreads();
     }
-  }
+    __syncthreads();  // the output waves' last iteration
 
-  if (S_final && wave < 2) {
+    if (S_final) {
 #pragma unroll
-    for (int i8 = 0; i8 < 8; ++i8)
-      *(float4 *)(S_final + ((long)bh * 128 + jcol) * DK + 16 * i8 + 4 * g) =
-          float4{Sacc[i8][0], Sacc[i8][1], Sacc[i8][2], Sacc[i8][3]};
+      for (int i8 = 0; i8 < 8; ++i8)
+        *(float4 *)(S_final + ((long)bh * 128 + jcol) * DK + 16 * i8 + 4 * g) =
+            float4{Sacc[i8][0], Sacc[i8][1], Sacc[i8][2], Sacc[i8][3]};
+    }
+  } else {
+    // ================================ outputs ================================
+    const int sn = wave - 2;
+    f32x4 O[4];     // Q S^T of the chunk whose outputs are pending
+    f16x8 Pr[6];    // its score operands
+    __syncthreads();
+    for (int it = 0; it <= NC; ++it) {
+      if (it > 0) {
+        // O = Q S^T + P X of chunk it - 1, stored as bf16 through an identity
+        // transpose (a lane then holds 4 consecutive channels of one token)
+        const int c = it - 1;
+        const long tok0 = (long)bh * T_ + (long)c * C;
+        const int L = min(C, T_ - c * C);
+        const f16x8 Xb[2] = {sm.Xx[c & 1][sn][0][lane], sm.Xx[c & 1][sn][1][lane]};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+          for (int qq = 0; qq <= (m >> 1); ++qq) O[m] = mma32(Pr[op_index(m, qq)], Xb[qq], O[m]);
+          const bf16x4 ob = {(bf16)O[m][0], (bf16)O[m][1], (bf16)O[m][2], (bf16)O[m][3]};
+          const f32x4 ot = mma16bf(ob, identb, zero4());
+          const int t = 16 * m + c16;
+          if (t < L)
+            *(bf16x4 *)(o + (tok0 + t) * 128 + j0 + 16 * sn + 4 * g) =
+                bf16x4{(bf16)ot[0], (bf16)ot[1], (bf16)ot[2], (bf16)ot[3]};
+        }
+      }
+      if (it < NC) {
+        // Q S^T of chunk it from the S^T its chain wave left, and its scores
+        const int cb = it & 1;
+        f16x8 Sb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) Sb[kk] = sm.Sx[cb][sn][kk][lane];
+        const f16 *Qc = sm.Q[cb];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f16 *qr = &Qc[(16 * m + c16) * KP];
+          f32x4 a = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) a = mma32(ldpk(qr, 32 * kk, g), Sb[kk], a);
+          O[m] = a;
+        }
+        const f16x8 *PA = (const f16x8 *)(sm.rec[cb] + OFF_P);
+#pragma unroll
+        for (int x = 0; x < 6; ++x) Pr[x] = PA[x * 64 + lane];
+      }
+      __syncthreads();
+    }
   }
 }
 
