@@ -170,7 +170,6 @@ def main():
     copies = max(2, -(-2 * CACHE_BYTES // per_copy))
     devs = [host.to("cuda") for _ in range(copies)]
     B, H, T, dk, dv, C = w.B, w.H, w.T, w.dk, w.dv, w.chunk
-    path = osdn.forward_path(B, H, T, dk, dv, C, code)
     outs = [{
         "o": torch.empty_like(d.v),
         "S_final": torch.empty((B, H, dv, dk), dtype=torch.float32, device="cuda"),
@@ -179,13 +178,16 @@ def main():
     } for d in devs]
     ws_n = osdn.forward_workspace_bytes(B, H, T, dk, dv, C, code)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda") if ws_n else None
+    path = osdn.forward_path(B, H, T, dk, dv, C, code, workspace_bytes=ws_n)
 
-    def fwd(i, precond=True, gated=False):
+    def fwd(i, precond=True, gated=False, single=False):
+        # single: no optional scratch, so the one-kernel forward runs
         d = devs[i % copies]
         o = outs[i % copies]
         osdn.forward(d.q, d.k, d.v, d.beta, d.r, eta=d.eta, chunk=C, precond=precond,
                      alpha=d.alpha if gated else None,
-                     out=o if precond else {**o, "d_final": None}, workspace=ws)
+                     out=o if precond else {**o, "d_final": None},
+                     workspace=None if single else ws)
 
     print("[bench] path=%s copies=%d" % (path, copies), file=sys.stderr, flush=True)
     ms = time_launches(fwd, args.steps, args.warmup, torch)
@@ -194,7 +196,7 @@ def main():
         "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if (path == "fused" and w.dtype == "bf16") else "f32",
+        "dtype": "bf16" if (path in ("fused", "split") and w.dtype == "bf16") else "f32",
         "data": "synthetic (seeded generator; shapes and distributions of the workload)",
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C,
                    "eta": w.eta, "apf": w.apf, "storage": w.dtype, "path": path},
@@ -204,6 +206,9 @@ def main():
     phases = {}
     if args.only in ("all", "phases"):
         ms_dn = time_launches(lambda i: fwd(i, precond=False), args.steps, args.warmup, torch)
+        ms_single = time_launches(lambda i: fwd(i, single=True), args.steps, args.warmup, torch)
+        ms_dn_single = time_launches(lambda i: fwd(i, precond=False, single=True), args.steps,
+                                     args.warmup, torch)
         ms_g = time_launches(lambda i: fwd(i, gated=True), args.steps, args.warmup, torch)
         ms_gdn = time_launches(lambda i: fwd(i, precond=False, gated=True), args.steps,
                                args.warmup, torch)
@@ -212,12 +217,17 @@ def main():
         lib = osdn.load()
         stream = torch.cuda.current_stream().cuda_stream
 
-        def scan(i):
+        sws_n = osdn.precond_scan_workspace_bytes(B, H, T, dk, code)
+        sws = torch.empty(max(sws_n, 1), dtype=torch.uint8, device="cuda")
+
+        def scan(i, use_ws=True):
             d = devs[i % copies]
             st = lib.osdn_precond_scan(d.k.data_ptr(), d.beta.data_ptr(),
                                        None if d.r is None else d.r.data_ptr(), None,
                                        float(d.eta), B, H, T, dk, code, kts[i % copies].data_ptr(),
-                                       dfin.data_ptr(), None, None, stream)
+                                       dfin.data_ptr(), None, None,
+                                       sws.data_ptr() if (use_ws and sws_n) else None,
+                                       sws_n if use_ws else 0, stream)
             assert st == 0, st
 
         cws_n = osdn.chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, code)
@@ -235,20 +245,26 @@ def main():
             assert st == 0, st
 
         ms_scan = time_launches(scan, args.steps, args.warmup, torch)
+        ms_scan_single = time_launches(lambda i: scan(i, False), args.steps, args.warmup, torch)
         ms_chunk = time_launches(chunk, args.steps, args.warmup, torch)
         ms_chunk_single = time_launches(lambda i: chunk(i, False), args.steps, args.warmup, torch)
         phases = {
+            "forward_single_kernel": {"ms": ms_single, "tokens_per_s": tokens / (ms_single * 1e-3),
+                                      "traffic": stored_traffic("osdn_fused_forward",
+                                                                args.workload)},
+            "deltanet_mode_single_kernel": {"ms": ms_dn_single},
             "precond_scan": {"ms": ms_scan, "tokens_per_s": tokens / (ms_scan * 1e-3),
                              "hbm_frac": algorithmic_bytes(w, "scan") / (ms_scan * 1e-3)
                              / (HBM_PEAK_GBS * 1e9),
-                             "traffic": stored_traffic("osdn_fused_scan", args.workload)},
+                             "traffic": stored_traffic("osdn_precond_scan_split", args.workload)},
+            "precond_scan_single_kernel": {"ms": ms_scan_single},
             "chunk_fwd": {"ms": ms_chunk, "tokens_per_s": tokens / (ms_chunk * 1e-3),
                           "hbm_frac": algorithmic_bytes(w, "chunk") / (ms_chunk * 1e-3)
                           / (HBM_PEAK_GBS * 1e9),
-                          "traffic": stored_traffic("osdn_fused_chunk", args.workload)},
+                          "traffic": stored_traffic("osdn_chunk_fwd_split", args.workload)},
             "chunk_fwd_single_kernel": {"ms": ms_chunk_single},
             "deltanet_mode": {"ms": ms_dn, "tokens_per_s": tokens / (ms_dn * 1e-3),
-                              "traffic": stored_traffic("osdn_fused_deltanet", args.workload)},
+                              "traffic": stored_traffic("osdn_deltanet_split", args.workload)},
             "precond_overhead": (ms - ms_dn) / ms,
             "gated_forward": {"ms": ms_g, "tokens_per_s": tokens / (ms_g * 1e-3),
                               "vs_ungated": ms_g / ms},
@@ -260,9 +276,14 @@ def main():
         print("[bench] scan %.4f ms, chunk %.4f ms, deltanet %.4f ms" % (ms_scan, ms_chunk, ms_dn),
               file=sys.stderr, flush=True)
 
-    # Dominant kernel against the HBM roofline.  The fused path is one kernel per
-    # osdn_forward; the two-launch path is dominated by the chunkwise pass.
-    if path == "fused":
+    # Against the HBM roofline.  On the matrix-core shapes the unit is one
+    # osdn_forward call: the single fused kernel, or the pipeline of launches
+    # (walk_prep, walk, chunk_prep, chunk_state) timed as one call on its stream,
+    # with the method's algorithmic bytes (q, k, v, beta, r in; o out).  The
+    # two-launch path is dominated by the chunkwise pass.
+    if path == "split":
+        kname, kms, kbytes = "osdn_forward_split", ms, algorithmic_bytes(w, "fused")
+    elif path == "fused":
         kname, kms, kbytes = "osdn_fused_forward", ms, algorithmic_bytes(w, "fused")
     else:
         kname = "chunk_generic"

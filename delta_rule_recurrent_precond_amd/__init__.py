@@ -22,7 +22,8 @@ import torch
 from . import _lib
 from ._lib import OsdnError, load  # noqa: F401
 
-__all__ = ["precond_scan", "chunk_fwd", "forward", "forward_workspace_bytes", "forward_path",
+__all__ = ["precond_scan", "chunk_fwd", "forward", "step", "forward_workspace_bytes", "forward_path",
+           "precond_scan_workspace_bytes", "chunk_fwd_workspace_bytes",
            "OsdnError", "load"]
 
 
@@ -61,8 +62,20 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def precond_scan(k, beta, r=None, d0=None, eta=0.05, *, want_d_all=False, want_log_ratio=False):
-    """Phase 1.  Returns dict(k_tilde, d_final[, d_all][, log_ratio])."""
+def precond_scan_workspace_bytes(B, H, T, dk, dtype_code) -> int:
+    n = _lib.load().osdn_precond_scan_workspace_bytes(B, H, T, dk, dtype_code)
+    if n == (1 << 64) - 1:
+        raise ValueError("invalid arguments for osdn_precond_scan")
+    return int(n)
+
+
+def precond_scan(k, beta, r=None, d0=None, eta=0.05, *, want_d_all=False, want_log_ratio=False,
+                 workspace=True):
+    """Phase 1.  Returns dict(k_tilde, d_final[, d_all][, log_ratio]).
+
+    ``workspace``: True allocates the scratch that selects the three-launch
+    walk (when it exists for these shapes), a uint8 device tensor passes one,
+    None runs the single-kernel walk."""
     _dev(k, "k")
     B, H, T, dk = k.shape
     dev = k.device
@@ -77,10 +90,14 @@ def precond_scan(k, beta, r=None, d0=None, eta=0.05, *, want_d_all=False, want_l
         out["d_all"] = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev)
     if want_log_ratio:
         out["log_ratio"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    if workspace is True:
+        n = precond_scan_workspace_bytes(B, H, T, dk, _dtype_code(k))
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+    ws_bytes = 0 if workspace is None else workspace.numel()
     st = _lib.load().osdn_precond_scan(
         _ptr(k), _ptr(beta), _ptr(r), _ptr(d0), float(eta), B, H, T, dk, _dtype_code(k),
         _ptr(out["k_tilde"]), _ptr(out["d_final"]), _ptr(out.get("d_all")),
-        _ptr(out.get("log_ratio")), _stream(dev))
+        _ptr(out.get("log_ratio")), _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check("osdn_precond_scan", st)
     return out
 
@@ -166,21 +183,25 @@ def forward_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code, precond=True) ->
     return int(n)
 
 
-def forward_path(B, H, T, dk, dv, chunk, dtype_code, precond=True) -> str:
+def forward_path(B, H, T, dk, dv, chunk, dtype_code, precond=True, gated=False,
+                 workspace_bytes=0) -> str:
     flags = 0 if precond else _lib.OSDN_PRECOND_OFF
-    return _lib.load().osdn_forward_path(B, H, T, dk, dv, chunk, dtype_code, flags).decode()
+    return _lib.load().osdn_forward_path(B, H, T, dk, dv, chunk, dtype_code, flags, int(gated),
+                                         int(workspace_bytes)).decode()
 
 
 def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond=True,
-            *, alpha=None, out=None, workspace=None):
+            *, alpha=None, out=None, workspace=True):
     """Both phases.  Returns dict(o, S_final, d_final, log_ratio_sum).
 
     ``alpha`` [B,H,T] fp32 is the optional state gate (Gated DeltaNet backbone;
     with precond=False, Gated DeltaNet itself).
 
     ``out`` may pass preallocated outputs (same keys) to keep the call free of
-    allocations; ``workspace`` a uint8 device tensor of at least
-    forward_workspace_bytes(...) bytes.
+    allocations.  ``workspace``: True allocates the scratch of the fastest path
+    (forward_workspace_bytes), a uint8 device tensor passes one, None passes
+    only what the path requires (none on the shapes of the single fused
+    kernel, which then runs).
     """
     _dev(q, "q")
     B, H, T, dk = q.shape
@@ -205,9 +226,12 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond
                         if precond else None),
             "log_ratio_sum": torch.empty((B, H), dtype=torch.float32, device=dev),
         }
-    need = forward_workspace_bytes(B, H, T, dk, dv, chunk, code, precond)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    single = forward_path(B, H, T, dk, dv, chunk, code, precond) == "fused"
+    if workspace is True and alpha is not None and single:
+        workspace = None  # the multi-launch pipeline has no state gate
+    if workspace is True or (workspace is None and not single):
+        need = forward_workspace_bytes(B, H, T, dk, dv, chunk, code, precond)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.load().osdn_forward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(alpha), _ptr(d0), _ptr(S0),

@@ -31,7 +31,8 @@ P = ctypes.c_void_p
 I = ctypes.c_int
 F = ctypes.c_float
 SIGNATURES = {
-    "osdn_precond_scan": (I, [P, P, P, P, F, I, I, I, I, I, P, P, P, P, P]),
+    "osdn_precond_scan": (I, [P, P, P, P, F, I, I, I, I, I, P, P, P, P, P, ctypes.c_size_t, P]),
+    "osdn_precond_scan_workspace_bytes": (ctypes.c_size_t, [I, I, I, I, I]),
     "osdn_chunk_fwd": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, ctypes.c_size_t,
                            P]),
     "osdn_chunk_fwd_workspace_bytes": (ctypes.c_size_t, [I, I, I, I, I, I, I]),
@@ -40,7 +41,8 @@ SIGNATURES = {
                          P, P, P, P, P, ctypes.c_size_t, P]),
     "osdn_forward_workspace_bytes": (ctypes.c_size_t, [I, I, I, I, I, I, I, ctypes.c_uint]),
     "osdn_status_str": (ctypes.c_char_p, [I]),
-    "osdn_forward_path": (ctypes.c_char_p, [I, I, I, I, I, I, I, ctypes.c_uint]),
+    "osdn_forward_path": (ctypes.c_char_p, [I, I, I, I, I, I, I, ctypes.c_uint, I,
+                                            ctypes.c_size_t]),
 }
 
 

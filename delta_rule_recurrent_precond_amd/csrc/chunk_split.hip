@@ -22,16 +22,20 @@
 //   TmA  fp16 [6 ops][64 lanes][8]  rows of T as 16x16x32 A operands, paired k order
 //   PA   fp16 [6 ops][64 lanes][8]  rows of P ds as A operands, paired k order
 //   ds   fp32 write-key scale: kt is stored divided by ds, a power of two
+//   lr   fp32 (kt = k only) sum over the chunk of log rho_t, rho_t = (1 - beta_t ||k_t||^2)^2
 // op x = 0..5 is (row block m, t pair qq) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
 #include "device.h"
 #include "launch.h"
 #include "mfma.h"
+#include "walk.h"
 
 namespace osdn {
 
 namespace {
 
-enum PrepMode { kDeltaNet = 1, kGiven = 2 };  // kt = k, or kt read from memory
+// kOsdn: kt formed from the walk's results; kDeltaNet: kt = k; kGiven: kt read
+// from memory
+enum PrepMode { kOsdn = 0, kDeltaNet = 1, kGiven = 2 };
 
 constexpr int C = 64;
 constexpr int DK = 128;
@@ -40,6 +44,7 @@ constexpr size_t OFF_KTF = 0;
 constexpr size_t OFF_TM = 16384;
 constexpr size_t OFF_P = 22528;
 constexpr size_t OFF_DS = 28672;
+constexpr size_t OFF_LR = 28676;  // kt = k: sum over the chunk of log rho_t
 constexpr int LDT = 24;  // padded row (halves) of the 16x16 fp16 blocks in LDS
 constexpr int LDF = 20;  // padded row (floats) of the 16x16 fp32 blocks in LDS
 
@@ -52,11 +57,16 @@ __device__ __forceinline__ int op_index(int m, int qq) { return m < 2 ? m : 2 * 
 // ---------------------------------------------------------------------------
 constexpr int KP = 136;  // padded row (halves) of the staged [64][128] tiles
 
-template <int MODE>  // kGiven: kt from memory; kDeltaNet: kt = k
+// kOsdn: threads 0-127 run the in-chunk preconditioner recurrence
+// d_{t+1} = r_t d_t + c_t (k_t (.) k_t) from the chunk's entry d and the c_t
+// of the walk (one key dimension each, fp32), forming kt_t = d_t (.) k_t twice:
+// once for its largest magnitude (the scale ds), once to stage kt / ds.
+template <int MODE>
 __global__ void __launch_bounds__(256)
 chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
            const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
-           unsigned char *__restrict__ ws) {
+           unsigned char *__restrict__ ws, const float *__restrict__ r,
+           const float *__restrict__ wout) {
   __shared__ __align__(16) f16 Ks[C * KP];          // k
   __shared__ __align__(16) f16 Kts[C * KP];         // kt / ds (kt = k: unused)
   __shared__ __align__(16) f16 Qs[C * KP];          // q
@@ -64,6 +74,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   __shared__ __align__(16) f16 Aoff[6][16][LDT];   // off-diagonal blocks of A (fp16)
   __shared__ __align__(16) f16 Tdg[4][16][LDT];    // diagonal blocks of T (fp16)
   __shared__ float bs[C];
+  __shared__ float cs[C], rs[C];  // kOsdn: c_t and r_t
   __shared__ float red[4];
 
   const int tid = threadIdx.x;
@@ -73,7 +84,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
   unsigned char *rec = ws + ((long)bh * NC + c) * REC;
-  const f16 *Ktp = (MODE == kGiven) ? Kts : Ks;
+  const f16 *Ktp = (MODE == kDeltaNet) ? Ks : Kts;
 
   // ---- loads: 1024 pieces of 8 elements per tensor, 4 per thread
   uint4 rk[4], rq[4], rt[4];
@@ -87,6 +98,10 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (MODE == kGiven) rt[u] = ok ? *(const uint4 *)(kt_in + off) : uint4{0, 0, 0, 0};
   }
   if (tid < C) bs[tid] = tid < L ? beta[tok0 + tid] : 0.f;
+  if (MODE == kOsdn && tid < C) {
+    cs[tid] = tid < L ? wout[((long)bh * NC + c) * WOUT + DK + tid] : 0.f;
+    rs[tid] = (r && tid < L) ? r[tok0 + tid] : 1.0f;
+  }
 
   // write-key scale: a power of two >= max |kt| (given keys), 1 for kt = k
   float ds = 1.0f;
@@ -105,7 +120,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     km = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     ds = km > 0.f ? fexp2(ceilf(flog2(km))) : 1.0f;
   }
-  const float inv = 1.0f / ds;
+  float inv = 1.0f / ds;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
@@ -120,6 +135,34 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   }
   __syncthreads();
+
+  if (MODE == kOsdn) {
+    const float d_in = tid < DK ? wout[((long)bh * NC + c) * WOUT + tid] : 0.f;
+    auto recur = [&](auto &&emit) {
+      float d = d_in;
+      for (int t0 = 0; t0 < C; t0 += 4) {
+        const float4 c4 = *(const float4 *)&cs[t0], r4 = *(const float4 *)&rs[t0];
+        const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float kv = (float)Ks[(t0 + e) * KP + tid];
+          emit(t0 + e, d * kv);
+          d = fmaf(cv[e], kv * kv, rv[e] * d);
+        }
+      }
+    };
+    float km = 0.f;
+    if (tid < DK) recur([&](int, float x) { km = fmaxf(km, fabsf(x)); });
+#pragma unroll
+    for (int m_ = 1; m_ < 64; m_ <<= 1) km = fmaxf(km, __shfl_xor(km, m_));
+    if (lane == 0) red[wave] = km;
+    __syncthreads();
+    km = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    ds = km > 0.f ? fexp2(ceilf(flog2(km))) : 1.0f;
+    inv = 1.0f / ds;
+    if (tid < DK) recur([&](int t, float x) { Kts[t * KP + tid] = h(x * inv); });
+    __syncthreads();
+  }
 
   f16x4 ident;
 #pragma unroll
@@ -195,8 +238,30 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       *(f16x8 *)(rec + OFF_KTF + (((n * 2 + qq) * 64 + lane) * 8) * 2) = cat(tr[2 * qq], tr[2 * qq + 1]);
   }
   if (tid == 0) *(float *)(rec + OFF_DS) = ds;
+  if (MODE == kDeltaNet) {
+    // log rho_t with a_t = ||k_t||^2 from the stored values (16 threads per token)
+    float lr = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = tid + 256 * u, t = p >> 4;
+      const unsigned short *sv = (const unsigned short *)&rk[u];
+      float sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = bf2f(sv[e]);
+        sq = fmaf(x, x, sq);
+      }
+      sq = group_sum<16>(sq);
+      const float gd = 1.0f - bs[t] * sq;
+      if ((p & 15) == 0 && t < L) lr += logf(gd * gd);
+    }
+    lr = wave_sum(lr);
+    if (lane == 0) red[wave] = lr;
+  }
 
   __syncthreads();  // Tdg and Aoff complete
+  if (MODE == kDeltaNet && tid == 0)
+    *(float *)(rec + OFF_LR) = (red[0] + red[1]) + (red[2] + red[3]);
 
   // ---- T: the diagonal block of row block `wave` as an A-operand half, then
   // column `wave` below the diagonal: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
@@ -267,7 +332,7 @@ __global__ void __launch_bounds__(ST)
 chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
             const float *__restrict__ beta, const float *__restrict__ S0, int BH, int T_, int NC,
             const unsigned char *__restrict__ ws, bf16 *__restrict__ o,
-            float *__restrict__ S_final) {
+            float *__restrict__ S_final, float *__restrict__ log_ratio_sum) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   StateSmem &sm = *reinterpret_cast<StateSmem *>(smem_raw);
   const int tid = threadIdx.x;
@@ -450,6 +515,13 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         *(float4 *)(S_final + ((long)bh * 128 + jcol) * DK + 16 * i8 + 4 * g) =
             float4{Sacc[i8][0], Sacc[i8][1], Sacc[i8][2], Sacc[i8][3]};
     }
+    if (log_ratio_sum && tile == 0 && wave == 0) {
+      // the chunks' sums of log rho_t, in a fixed order
+      float acc = 0.f;
+      for (int c = lane; c < NC; c += 64) acc += *(const float *)(ws + ((long)bh * NC + c) * REC + OFF_LR);
+      acc = wave_sum(acc);
+      if (lane == 0) log_ratio_sum[bh] = acc;
+    }
   } else {
     // ================================ outputs ================================
     const int sn = wave - 2;
@@ -507,6 +579,62 @@ size_t split_workspace_bytes(int B, int H, int T) {
   return (size_t)B * H * nc * REC;
 }
 
+namespace {
+
+hipError_t launch_state(const ChunkArgs &a, int NC, const void *ws, float *log_ratio_sum,
+                        hipStream_t s) {
+  const int BH = a.B * a.H;
+  const size_t shm = sizeof(StateSmem);
+  hipError_t e = hipFuncSetAttribute((const void *)chunk_state,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_state, dim3((unsigned)(BH * 4)), dim3(ST), shm, s, (const bf16 *)a.q,
+                     (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.S0, BH, a.T, NC,
+                     (const unsigned char *)ws, (bf16 *)a.o, a.S_final, log_ratio_sum);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t split_forward_workspace_bytes(int B, int H, int T) {
+  // the walk's records live in the space the chunk records take later
+  const size_t nc = (size_t)((T + C - 1) / C);
+  return (size_t)B * H * nc * (REC + WOUT * sizeof(float));
+}
+
+hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
+  const int BH = a.B * a.H;
+  if (BH == 0) return hipSuccess;
+  const int NC = (a.T + C - 1) / C;
+  unsigned char *rec = (unsigned char *)ws;
+  ChunkArgs ca{a.q, a.k, nullptr, a.v, a.beta, nullptr, a.S0, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
+               a.dtype, a.o, a.S_final};
+  if (a.precond_off) {  // the plain delta rule: kt = k
+    if (NC > 0) {
+      hipLaunchKernelGGL(chunk_prep<kDeltaNet>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
+                         a.T, NC, rec, (const float *)nullptr, (const float *)nullptr);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return launch_state(ca, NC, ws, a.log_ratio_sum, s);
+  }
+  float *wout = (float *)(rec + (size_t)BH * NC * REC);
+  static_assert(WREC <= REC, "walk records fit in the chunk records' space");
+  ScanArgs sa{a.k, a.beta, a.r, a.d0, a.eta, a.B, a.H, a.T, a.dk, a.dtype, 0, nullptr,
+              a.d_final, nullptr, nullptr, a.log_ratio_sum};
+  hipError_t e = launch_walk(sa, rec, wout, s);
+  if (e != hipSuccess) return e;
+  if (NC > 0) {
+    hipLaunchKernelGGL(chunk_prep<kOsdn>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta, a.T,
+                       NC, rec, a.r, (const float *)wout);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_state(ca, NC, ws, nullptr, s);
+}
+
 hipError_t launch_split_chunk(const ChunkArgs &a, bool given, void *ws, hipStream_t s) {
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
@@ -515,22 +643,17 @@ hipError_t launch_split_chunk(const ChunkArgs &a, bool given, void *ws, hipStrea
     if (given)
       hipLaunchKernelGGL(chunk_prep<kGiven>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
                          (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.k_tilde, a.beta,
-                         a.T, NC, (unsigned char *)ws);
+                         a.T, NC, (unsigned char *)ws, (const float *)nullptr,
+                         (const float *)nullptr);
     else
       hipLaunchKernelGGL(chunk_prep<kDeltaNet>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
                          (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
-                         a.T, NC, (unsigned char *)ws);
+                         a.T, NC, (unsigned char *)ws, (const float *)nullptr,
+                         (const float *)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t shm = sizeof(StateSmem);
-  hipError_t e = hipFuncSetAttribute((const void *)chunk_state,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk_state, dim3((unsigned)(BH * 4)), dim3(ST), shm, s, (const bf16 *)a.q,
-                     (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.S0, BH, a.T, NC,
-                     (const unsigned char *)ws, (bf16 *)a.o, a.S_final);
-  return hipGetLastError();
+  return launch_state(a, NC, ws, nullptr, s);
 }
 
 }  // namespace osdn

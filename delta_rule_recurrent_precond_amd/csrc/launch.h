@@ -68,4 +68,21 @@ hipError_t launch_split_chunk(const ChunkArgs &a, bool given, void *ws, hipStrea
 bool fused_scan_supported(int dk, int dtype);
 hipError_t launch_fused_scan(const ScanArgs &a, hipStream_t s);
 
+// The walk in three launches (bf16 keys, dk = 128, chunk 64; walk.hip):
+// walk_prep + walk write per-chunk records (wrec, WREC bytes each) and the
+// entry d and c of every chunk (wout, WOUT floats each), plus d_final,
+// log_ratio and log_ratio_sum of `a`; launch_walk_scan adds walk_keys, which
+// writes a.k_tilde and a.d_all, with wrec and wout carved from ws
+// (walk_workspace_bytes).
+bool walk_supported(int dk, int dtype);
+size_t walk_workspace_bytes(int B, int H, int T);
+hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, float *wout, hipStream_t s);
+hipError_t launch_walk_scan(const ScanArgs &a, void *ws, hipStream_t s);
+
+// The forward in four launches (bf16, dk = dv = 128, chunk 64): the walk, then
+// the chunk-parallel pass forming the write keys from the walk's results, then
+// the state kernel; ws of split_forward_workspace_bytes.
+size_t split_forward_workspace_bytes(int B, int H, int T);
+hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s);
+
 }  // namespace osdn

@@ -35,10 +35,24 @@ bool use_fused(int dk, int dv, int chunk, int dtype) {
   return osdn::fused_supported(dk, dv, chunk, dtype);
 }
 
-size_t ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype, unsigned flags) {
-  if ((flags & OSDN_PRECOND_OFF) || use_fused(dk, dv, chunk, dtype)) return 0;
+// Scratch of the two-launch path (kt between the walk and the chunk pass).
+size_t two_phase_bytes(int B, int H, int T, int dk, int dtype, unsigned flags) {
+  if (flags & OSDN_PRECOND_OFF) return 0;
   const size_t n = (size_t)B * H * T * dk * elem_bytes(dtype);
   return (n + 255) & ~(size_t)255;
+}
+
+// Scratch that selects the fastest path: the split pipeline on the shapes of
+// the matrix-core kernels, else what the two-launch path needs.
+size_t ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype, unsigned flags) {
+  if (use_fused(dk, dv, chunk, dtype)) return osdn::split_forward_workspace_bytes(B, H, T);
+  return two_phase_bytes(B, H, T, dk, dtype, flags);
+}
+
+bool split_ok(int B, int H, int T, int dk, int dv, int chunk, int dtype, const float *alpha,
+              size_t workspace_bytes, const void *workspace) {
+  return use_fused(dk, dv, chunk, dtype) && !alpha && workspace &&
+         workspace_bytes >= osdn::split_forward_workspace_bytes(B, H, T);
 }
 
 }  // namespace
@@ -55,16 +69,25 @@ OSDN_EXPORT const char *osdn_status_str(int status) {
   }
 }
 
+OSDN_EXPORT size_t osdn_precond_scan_workspace_bytes(int B, int H, int T, int dk, int dtype) {
+  if (check_sizes(B, H, T, dk, 16, 16, dtype, false, false) != OSDN_OK) return (size_t)-1;
+  return osdn::walk_supported(dk, dtype) ? osdn::walk_workspace_bytes(B, H, T) : 0;
+}
+
 OSDN_EXPORT int osdn_precond_scan(const void *k, const float *beta, const float *r,
                                   const float *d0, float eta, int B, int H, int T, int dk,
                                   int dtype, void *k_tilde, float *d_final, float *d_all,
-                                  float *log_ratio, void *stream) {
+                                  float *log_ratio, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
   int st = check_sizes(B, H, T, dk, 16, 16, dtype, false, false);
   if (st != OSDN_OK) return st;
   if ((long long)B * H == 0) return OSDN_OK;
   if (T > 0 && (!k || !beta || !k_tilde)) return OSDN_ERR_NULL;
   osdn::ScanArgs a{k, beta, r, d0, eta, B, H, T, dk, dtype, 0, k_tilde,
                    d_final, d_all, log_ratio, nullptr};
+  if (osdn::walk_supported(dk, dtype) && workspace &&
+      workspace_bytes >= osdn::walk_workspace_bytes(B, H, T))
+    return hip_status(osdn::launch_walk_scan(a, workspace, (hipStream_t)stream));
   if (osdn::fused_scan_supported(dk, dtype))
     return hip_status(osdn::launch_fused_scan(a, (hipStream_t)stream));
   return hip_status(osdn::launch_precond_scan_serial(a, (hipStream_t)stream));
@@ -115,10 +138,14 @@ OSDN_EXPORT size_t osdn_forward_workspace_bytes(int B, int H, int T, int dk, int
 }
 
 OSDN_EXPORT const char *osdn_forward_path(int B, int H, int T, int dk, int dv, int chunk,
-                                          int dtype, unsigned flags) {
+                                          int dtype, unsigned flags, int gated,
+                                          size_t workspace_bytes) {
   if (check_sizes(B, H, T, dk, dv, chunk, dtype, true, true) != OSDN_OK) return "invalid";
   if (flags & ~OSDN_PRECOND_OFF) return "invalid";
   if ((long long)B * H == 0) return "none";
+  const float one = 1.0f;
+  if (split_ok(B, H, T, dk, dv, chunk, dtype, gated ? &one : nullptr, workspace_bytes, &one))
+    return "split";
   return use_fused(dk, dv, chunk, dtype) ? "fused" : "two-phase";
 }
 
@@ -138,12 +165,14 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   if (use_fused(dk, dv, chunk, dtype)) {
     osdn::FusedArgs a{q, k, v, beta, r, alpha, d0, S0, eta, B, H, T, dk, dv, chunk, dtype,
                       off ? 1 : 0, o, S_final, d_final, log_ratio_sum};
+    if (split_ok(B, H, T, dk, dv, chunk, dtype, alpha, workspace_bytes, workspace))
+      return hip_status(osdn::launch_split_forward(a, workspace, s));
     return hip_status(osdn::launch_fused_forward(a, s));
   }
 
   // Two launches: the preconditioner walk writes kt into the workspace, then
   // the chunkwise pass reads it.
-  const size_t need = ws_bytes(B, H, T, dk, dv, chunk, dtype, flags);
+  const size_t need = two_phase_bytes(B, H, T, dk, dtype, flags);
   if (need > 0 && (!workspace || workspace_bytes < need)) return OSDN_ERR_WORKSPACE;
   const void *kt = k;
   if (!off) {

@@ -1,0 +1,22 @@
+// Layout of the preconditioner walk's scratch records (walk.hip), shared with
+// the chunk-parallel pass that reads the walk's results (chunk_split.hip).
+#pragma once
+
+#include <stddef.h>
+
+namespace osdn {
+
+// Per (b, h, chunk of 64 tokens), written by walk_prep and read by walk:
+//   W_MINV  fp32 [64][64]  (I + M)^-1, row-major (zero above the diagonal)
+//   W_U     fp32 [64]      beta_t Gamma_t
+//   W_A     fp32 [64]      alpha_t = eta beta_t / n_t (0 if n_t = 0)
+//   W_WA    fp32 [64]      R_{L,t} alpha_t (0 past the end of the sequence)
+//   W_GL    fp32           Gamma_L
+constexpr size_t WREC = 17408;
+constexpr size_t W_MINV = 0, W_U = 16384, W_A = 16640, W_WA = 16896, W_GL = 17152;
+
+// Per (b, h, chunk), written by walk: the chunk's entry preconditioner d [128]
+// then c_t = alpha_t g_t [64], fp32.
+constexpr int WOUT = 192;
+
+}  // namespace osdn

@@ -87,11 +87,22 @@ extern "C" {
  *   d_final   [B,H,dk]   fp32    out: d_T (optional, NULL to skip)
  *   d_all     [B,H,T,dk] fp32    out: d_t, the value used at token t (optional)
  *   log_ratio [B,H,T]    fp32    out: log rho_t (optional; -inf where rho_t = 0)
+ *   workspace  optional device scratch.  With at least
+ *              osdn_precond_scan_workspace_bytes(...) bytes (positive for bf16
+ *              keys with dk = 128) the walk runs in three launches: the
+ *              d-independent part of every chunk (the (I + M)^-1 of the chunked
+ *              walk) in parallel, then a short sequential pass per (b,h), then
+ *              the keys of every chunk in parallel.  NULL selects a single
+ *              kernel per (b,h).
  */
 int osdn_precond_scan(const void *k, const float *beta, const float *r, const float *d0,
                       float eta, int B, int H, int T, int dk, int dtype,
                       void *k_tilde, float *d_final, float *d_all, float *log_ratio,
-                      void *stream);
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes that select osdn_precond_scan's three-launch walk (0 when no
+ * such path exists for these arguments); (size_t)-1 if they are invalid. */
+size_t osdn_precond_scan_workspace_bytes(int B, int H, int T, int dk, int dtype);
 
 /*
  * Phase 2: the chunkwise delta-rule pass with a given write key kt
@@ -139,8 +150,12 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  *   log_ratio_sum  [B,H] fp32 out: sum_t log rho_t (optional) -- the per-head
  *                  log of the product of token-local residual ratios of
  *                  [summary §3]; its mean over tokens gives log q_geo [summary §4.2]
- *   workspace      device scratch of at least osdn_forward_workspace_bytes(...)
- *                  bytes (may be NULL when that is 0)
+ *   workspace      device scratch.  With at least osdn_forward_workspace_bytes(...)
+ *                  bytes the fastest path runs; for bf16, dk = dv = 128, chunk 64
+ *                  that is a pipeline of launches (walk, chunk-parallel pass,
+ *                  sequential state pass; ungated calls), and less scratch (or
+ *                  NULL) selects the single fused kernel.  Other shapes need the
+ *                  scratch (the walk hands kt to the chunk pass through it).
  */
 int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
                  const float *r, const float *alpha, const float *d0, const float *S0,
@@ -172,19 +187,22 @@ int osdn_step(const void *q, const void *k, const void *v, const float *beta, co
               const float *alpha, float eta, int B, int H, int dk, int dv, int dtype, float *S, float *d, void *o,
               float *log_ratio, void *stream);
 
-/* Scratch bytes osdn_forward needs for these arguments (0 when the fused
- * single-kernel path applies); (size_t)-1 if the arguments are invalid. */
+/* Scratch bytes that select osdn_forward's fastest path for these arguments
+ * (required on the two-phase path, optional on the matrix-core shapes);
+ * (size_t)-1 if the arguments are invalid. */
 size_t osdn_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype,
                                     unsigned flags);
 
 /* Static, NUL-terminated description of a status code (host pointer). */
 const char *osdn_status_str(int status);
 
-/* Name of the kernel family osdn_forward would launch for these arguments
- * ("fused", "two-phase" or "none"); static host string, "invalid" on bad
- * arguments.  Lets callers and tests know which path they exercised. */
+/* Name of the kernel family osdn_forward would launch for these arguments,
+ * whether a state gate is passed (gated != 0) and the workspace size: "split"
+ * (the multi-launch pipeline), "fused" (one kernel), "two-phase" or "none";
+ * static host string, "invalid" on bad arguments.  Lets callers and tests
+ * know which path they exercised. */
 const char *osdn_forward_path(int B, int H, int T, int dk, int dv, int chunk, int dtype,
-                              unsigned flags);
+                              unsigned flags, int gated, size_t workspace_bytes);
 
 #ifdef __cplusplus
 }

@@ -129,7 +129,7 @@ def test_unit_gate_equals_ungated_bitwise(dtype, dk, chunk, precond):
     dev = inp.to("cuda")
     ones = torch.ones(w.B, w.H, w.T, device="cuda")
     a = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=inp.eta, chunk=chunk,
-                     precond=precond)
+                     precond=precond, workspace=None)  # the same kernel as the gated call
     b = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=inp.eta, chunk=chunk,
                      precond=precond, alpha=ones)
     torch.cuda.synchronize()

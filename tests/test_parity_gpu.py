@@ -62,16 +62,25 @@ def _log_ratio_tol(rho, eps_a=2e-5):
     return 2.0 * eps_a / g + 1e-6
 
 
-def _check_forward(w, inp, heads, precond=True, d0=None, S0=None, tol=None, label=""):
+def _ws_bytes(w, precond, ws):
+    code = 0 if w.dtype == "bf16" else 1
+    return osdn.forward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, code, precond) \
+        if ws is True else 0
+
+
+def _check_forward(w, inp, heads, precond=True, d0=None, S0=None, tol=None, label="", ws=True):
+    """ws=True: the fastest path (the multi-launch pipeline on the matrix-core
+    shapes); ws=None: no optional scratch (the single fused kernel there)."""
     tol = tol or TOL[w.dtype]
     dev = _to_dev(inp)
-    _log("forward %s heads=%d path=%s" % (label or w.name, len(heads),
-                                         osdn.forward_path(w.B, w.H, w.T, w.dk, w.dv, w.chunk,
-                                                           0 if w.dtype == "bf16" else 1,
-                                                           precond)))
+    code = 0 if w.dtype == "bf16" else 1
+    _log("forward %s heads=%d path=%s" % (
+        label or w.name, len(heads),
+        osdn.forward_path(w.B, w.H, w.T, w.dk, w.dv, w.chunk, code, precond,
+                          workspace_bytes=_ws_bytes(w, precond, ws))))
     out = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r,
                        None if d0 is None else d0.cuda(), None if S0 is None else S0.cuda(),
-                       eta=inp.eta, chunk=w.chunk, precond=precond)
+                       eta=inp.eta, chunk=w.chunk, precond=precond, workspace=ws)
     torch.cuda.synchronize()
     ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, d0, S0, eta=inp.eta,
                          mode="osdn" if precond else "deltanet", heads=heads,
@@ -135,15 +144,17 @@ def test_precond_scan_empty_sequence_copies_d0(dk):
     assert torch.equal(out["d_final"].cpu(), d0)
 
 
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 130])
-def test_precond_scan_chunk_boundaries(T):
-    """The chunked walk (bf16, dk = 128) around chunk boundaries, APF gates."""
+@pytest.mark.parametrize("ws", [True, None])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 200])
+def test_precond_scan_chunk_boundaries(T, ws):
+    """The chunked walk (bf16, dk = 128) around chunk boundaries, APF gates:
+    the three-launch walk (ws=True) and the single kernel per (b,h)."""
     w = W.custom(1, 2, T, 128, 128, 64, dtype="bf16", eta=0.2, apf=True, seed=300 + T)
     inp = W.generate(w)
     dev = _to_dev(inp)
-    _log("scan chunk boundaries T=%d" % T)
+    _log("scan chunk boundaries T=%d ws=%s" % (T, ws))
     out = osdn.precond_scan(dev.k, dev.beta, dev.r, None, inp.eta, want_d_all=True,
-                            want_log_ratio=True)
+                            want_log_ratio=True, workspace=ws)
     torch.cuda.synchronize()
     ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, None, None, eta=inp.eta,
                          want=("d", "d_all", "k_tilde", "rho"))
@@ -154,15 +165,17 @@ def test_precond_scan_chunk_boundaries(T):
     assert np.all(np.abs(lr - np.log(ref["rho"])) <= _log_ratio_tol(ref["rho"]))
 
 
+@pytest.mark.parametrize("ws", [True, None])
 @pytest.mark.parametrize("name", ["1.3b-apf", "recall-apf"])
-def test_precond_scan_full_size_sampled_heads(name):
+def test_precond_scan_full_size_sampled_heads(name, ws):
     """The standalone walk at a workload's full size, checked on sampled heads."""
     w = W.CONFIGS[name]
     inp = W.generate(w)
     heads = _heads(w, 3)
     dev = _to_dev(inp)
-    _log("scan full size %s heads=%s" % (name, heads))
-    out = osdn.precond_scan(dev.k, dev.beta, dev.r, None, inp.eta, want_log_ratio=True)
+    _log("scan full size %s heads=%s ws=%s" % (name, heads, ws))
+    out = osdn.precond_scan(dev.k, dev.beta, dev.r, None, inp.eta, want_log_ratio=True,
+                            workspace=ws)
     torch.cuda.synchronize()
     ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, None, None, eta=inp.eta,
                          heads=heads, want=("d", "k_tilde", "rho"))
@@ -238,20 +251,22 @@ def test_chunk_fwd_workspace_too_small_uses_single_kernel():
                                                (64, 64, 64, 190, True), (128, 128, 64, 333, True),
                                                (128, 128, 64, 256, False), (128, 64, 16, 71, True),
                                                (64, 128, 32, 64, False)])
-def test_forward_parity_small(dtype, dk, dv, chunk, T, apf):
+@pytest.mark.parametrize("ws", [True, None])
+def test_forward_parity_small(dtype, dk, dv, chunk, T, apf, ws):
     w = W.custom(2, 3, T, dk, dv, chunk, dtype=dtype, eta=0.1, apf=apf, seed=T + dk)
     inp = W.generate(w)
-    _check_forward(w, inp, _heads(w, 6))
+    _check_forward(w, inp, _heads(w, 6), ws=ws)
 
 
+@pytest.mark.parametrize("ws", [True, None])
 @pytest.mark.parametrize("precond", [True, False])
-def test_forward_with_initial_state(precond):
+def test_forward_with_initial_state(precond, ws):
     w = W.custom(1, 4, 200, 128, 128, 64, dtype="bf16", eta=0.05, apf=True, seed=42)
     inp = W.generate(w)
     g = torch.Generator().manual_seed(9)
     S0 = 0.05 * torch.randn(w.B, w.H, w.dv, w.dk, generator=g)
     d0 = 0.5 + torch.rand(w.B, w.H, w.dk, generator=g)
-    _check_forward(w, inp, _heads(w, 4), precond=precond, d0=d0, S0=S0)
+    _check_forward(w, inp, _heads(w, 4), precond=precond, d0=d0, S0=S0, ws=ws)
 
 
 def test_forward_deltanet_mode_small():
@@ -259,8 +274,9 @@ def test_forward_deltanet_mode_small():
     _check_forward(w, W.generate(w), _heads(w, 4), precond=False)
 
 
+@pytest.mark.parametrize("ws", [True, None])
 @pytest.mark.parametrize("T", [0, 1, 5, 64, 65])
-def test_forward_short_and_empty(T):
+def test_forward_short_and_empty(T, ws):
     w = W.custom(1, 2, T, 128, 128, 64, dtype="bf16", eta=0.1, apf=True, seed=11)
     inp = W.generate(w)
     g = torch.Generator().manual_seed(1)
@@ -268,49 +284,87 @@ def test_forward_short_and_empty(T):
     d0 = 0.5 + torch.rand(1, 2, 128, generator=g)
     dev = _to_dev(inp)
     out = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, d0.cuda(), S0.cuda(), eta=inp.eta,
-                       chunk=64)
+                       chunk=64, workspace=ws)
     torch.cuda.synchronize()
     if T == 0:
         assert torch.equal(out["S_final"].cpu(), S0)
         assert torch.equal(out["d_final"].cpu(), d0)
         assert torch.all(out["log_ratio_sum"].cpu() == 0)
     else:
-        _check_forward(w, inp, [0, 1], d0=d0, S0=S0)
+        _check_forward(w, inp, [0, 1], d0=d0, S0=S0, ws=ws)
 
 
 def test_eta_zero_equals_deltanet_mode_bitwise():
+    """Single fused kernel: eta = 0 runs the delta rule's operations exactly."""
     w = W.custom(2, 2, 200, 128, 128, 64, dtype="bf16", eta=0.0, apf=False, seed=21)
     dev = _to_dev(W.generate(w))
-    a = osdn.forward(dev.q, dev.k, dev.v, dev.beta, None, eta=0.0, chunk=64, precond=True)
-    b = osdn.forward(dev.q, dev.k, dev.v, dev.beta, None, eta=0.0, chunk=64, precond=False)
+    a = osdn.forward(dev.q, dev.k, dev.v, dev.beta, None, eta=0.0, chunk=64, precond=True,
+                     workspace=None)
+    b = osdn.forward(dev.q, dev.k, dev.v, dev.beta, None, eta=0.0, chunk=64, precond=False,
+                     workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(a["o"], b["o"]) and torch.equal(a["S_final"], b["S_final"])
     assert torch.all(a["d_final"] == 1.0)
 
 
-def test_deterministic_bitwise():
+def test_eta_zero_equals_deltanet_mode_split():
+    """Multi-launch pipeline: with eta = 0 the walk keeps d = 1 exactly and the
+    write keys are k scaled by a power of two, so the results match the delta
+    rule's to the rounding of fp16 subnormals."""
+    w = W.custom(2, 2, 200, 128, 128, 64, dtype="bf16", eta=0.0, apf=False, seed=21)
+    dev = _to_dev(W.generate(w))
+    a = osdn.forward(dev.q, dev.k, dev.v, dev.beta, None, eta=0.0, chunk=64, precond=True)
+    b = osdn.forward(dev.q, dev.k, dev.v, dev.beta, None, eta=0.0, chunk=64, precond=False)
+    torch.cuda.synchronize()
+    assert torch.all(a["d_final"] == 1.0)
+    assert rowwise_rel(a["o"], as_f64(b["o"])) <= 1e-3
+    assert matrix_rel(a["S_final"], as_f64(b["S_final"])) <= 1e-4
+    lr_a, lr_b = as_f64(a["log_ratio_sum"]), as_f64(b["log_ratio_sum"])
+    assert np.all(np.abs(lr_a - lr_b) <= 1e-4 * np.abs(lr_b) + 1e-3)
+
+
+def test_split_forward_matches_single_kernel():
+    """The multi-launch pipeline and the single fused kernel at a medium size:
+    both within the fp16-operand error of each other; d and the residual-ratio
+    sums to fp32 rounding."""
+    w = W.custom(2, 4, 700, 128, 128, 64, dtype="bf16", eta=0.05, apf=True, seed=77)
+    dev = _to_dev(W.generate(w))
+    a = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=0.05, chunk=64)
+    b = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=0.05, chunk=64, workspace=None)
+    torch.cuda.synchronize()
+    assert rowwise_rel(a["o"], as_f64(b["o"])) <= 2e-2
+    assert matrix_rel(a["S_final"], as_f64(b["S_final"])) <= 2e-2
+    assert rowwise_rel(a["d_final"], as_f64(b["d_final"])) <= 1e-5
+    lr_a, lr_b = as_f64(a["log_ratio_sum"]), as_f64(b["log_ratio_sum"])
+    assert np.all(np.abs(lr_a - lr_b) <= 1e-4 * np.abs(lr_b) + 1e-3)
+
+
+@pytest.mark.parametrize("ws", [True, None])
+def test_deterministic_bitwise(ws):
     w = W.custom(2, 4, 300, 128, 128, 64, dtype="bf16", eta=0.05, apf=True, seed=8)
     dev = _to_dev(W.generate(w))
-    runs = [osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=0.05, chunk=64)
+    runs = [osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=0.05, chunk=64, workspace=ws)
             for _ in range(2)]
     torch.cuda.synchronize()
     for key in ("o", "S_final", "d_final", "log_ratio_sum"):
         assert torch.equal(runs[0][key], runs[1][key]), key
 
 
+@pytest.mark.parametrize("ws", [True, None])
 @pytest.mark.parametrize("split", [128, 100])
-def test_continuation_through_state(split):
+def test_continuation_through_state(split, ws):
     """forward(0:T) vs forward(split:T) started from forward(0:split)'s (S, d)."""
     w = W.custom(1, 2, 256, 128, 128, 64, dtype="bf16", eta=0.05, apf=True, seed=31)
     inp = W.generate(w)
     dev = _to_dev(inp)
-    whole = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=0.05, chunk=64)
+    whole = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=0.05, chunk=64, workspace=ws)
     sl = lambda t, a, b: t[:, :, a:b].contiguous()
     first = osdn.forward(sl(dev.q, 0, split), sl(dev.k, 0, split), sl(dev.v, 0, split),
-                         sl(dev.beta, 0, split), sl(dev.r, 0, split), eta=0.05, chunk=64)
+                         sl(dev.beta, 0, split), sl(dev.r, 0, split), eta=0.05, chunk=64,
+                         workspace=ws)
     second = osdn.forward(sl(dev.q, split, 256), sl(dev.k, split, 256), sl(dev.v, split, 256),
                           sl(dev.beta, split, 256), sl(dev.r, split, 256), first["d_final"],
-                          first["S_final"], eta=0.05, chunk=64)
+                          first["S_final"], eta=0.05, chunk=64, workspace=ws)
     torch.cuda.synchronize()
     o = torch.cat([first["o"], second["o"]], dim=2)
     if split % 64 == 0:   # same chunk boundaries: identical operations
@@ -364,11 +418,12 @@ FULL = [("tiny", 1), ("340m", 4), ("340m-apf", 4), ("1.3b-apf", 4), ("recall", 3
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("ws", [True, None])
 @pytest.mark.parametrize("name,nheads", FULL)
-def test_workload_full_size(name, nheads):
+def test_workload_full_size(name, nheads, ws):
     w = W.CONFIGS[name]
     inp = W.generate(w)
-    out, ref, errs = _check_forward(w, inp, _heads(w, nheads), label=name)
+    out, ref, errs = _check_forward(w, inp, _heads(w, nheads), label=name, ws=ws)
     if name.startswith("recall") or name == "1.3b-apf":
         # q_geo over the sampled heads agrees with the oracle's
         heads = _heads(w, nheads)
