@@ -65,7 +65,7 @@ template <int MODE>
 __global__ void __launch_bounds__(256)
 chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
            const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
-           unsigned char *__restrict__ ws, const float *__restrict__ r,
+           int c0, int ncs, unsigned char *__restrict__ ws, const float *__restrict__ r,
            const float *__restrict__ wout) {
   __shared__ __align__(16) f16 Ks[C * KP];          // k
   __shared__ __align__(16) f16 Kts[C * KP];         // kt / ds (kt = k: unused)
@@ -80,7 +80,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+  const int bh = blockIdx.x / ncs, c = c0 + blockIdx.x % ncs;  // chunks c0 .. c0+ncs-1
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
   unsigned char *rec = ws + ((long)bh * NC + c) * REC;
@@ -602,25 +602,29 @@ size_t split_forward_workspace_bytes(int B, int H, int T) {
   return (size_t)B * H * nc * (REC + WOUT * sizeof(float));
 }
 
+// walk_prep, the walk's sequential pass, chunk_prep forming the write keys
+// from the walk's results, the state kernel -- in that order on one stream.
+// (Running chunk_prep of finished segments beside the walk on a second stream
+// was measured: the cross-stream waits and the sharing of CUs ate the overlap.)
 hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
   const int NC = (a.T + C - 1) / C;
   unsigned char *rec = (unsigned char *)ws;
+  float *wout = (float *)(rec + (size_t)BH * NC * REC);
+  static_assert(WREC <= REC, "walk records fit in the chunk records' space");
   ChunkArgs ca{a.q, a.k, nullptr, a.v, a.beta, nullptr, a.S0, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
                a.dtype, a.o, a.S_final};
   if (a.precond_off) {  // the plain delta rule: kt = k
     if (NC > 0) {
       hipLaunchKernelGGL(chunk_prep<kDeltaNet>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
                          (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
-                         a.T, NC, rec, (const float *)nullptr, (const float *)nullptr);
+                         a.T, NC, 0, NC, rec, (const float *)nullptr, (const float *)nullptr);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
     return launch_state(ca, NC, ws, a.log_ratio_sum, s);
   }
-  float *wout = (float *)(rec + (size_t)BH * NC * REC);
-  static_assert(WREC <= REC, "walk records fit in the chunk records' space");
   ScanArgs sa{a.k, a.beta, a.r, a.d0, a.eta, a.B, a.H, a.T, a.dk, a.dtype, 0, nullptr,
               a.d_final, nullptr, nullptr, a.log_ratio_sum};
   hipError_t e = launch_walk(sa, rec, wout, s);
@@ -628,7 +632,7 @@ hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   if (NC > 0) {
     hipLaunchKernelGGL(chunk_prep<kOsdn>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta, a.T,
-                       NC, rec, a.r, (const float *)wout);
+                       NC, 0, NC, rec, a.r, (const float *)wout);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -643,12 +647,12 @@ hipError_t launch_split_chunk(const ChunkArgs &a, bool given, void *ws, hipStrea
     if (given)
       hipLaunchKernelGGL(chunk_prep<kGiven>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
                          (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.k_tilde, a.beta,
-                         a.T, NC, (unsigned char *)ws, (const float *)nullptr,
+                         a.T, NC, 0, NC, (unsigned char *)ws, (const float *)nullptr,
                          (const float *)nullptr);
     else
       hipLaunchKernelGGL(chunk_prep<kDeltaNet>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
                          (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
-                         a.T, NC, (unsigned char *)ws, (const float *)nullptr,
+                         a.T, NC, 0, NC, (unsigned char *)ws, (const float *)nullptr,
                          (const float *)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

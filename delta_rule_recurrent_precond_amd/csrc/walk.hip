@@ -41,7 +41,7 @@ constexpr int FP = 68;   // padded row (floats) of [64][64] fp32 tiles in LDS
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const float *__restrict__ r,
-          float eta, int T_, int NC, unsigned char *__restrict__ wrec) {
+          float eta, int T_, int NC, int c0, int ncs, unsigned char *__restrict__ wrec) {
   // The fp16 keys are needed only for the key gram; (I + M)^-1 reuses their space.
   __shared__ __align__(16) float F[C * FP];           // key gram G, then M (strictly lower)
   __shared__ __align__(16) unsigned char KM[C * KP * 2];  // fp16 keys, then (I + M)^-1 [64][FP]
@@ -54,7 +54,7 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+  const int bh = blockIdx.x / ncs, c = c0 + blockIdx.x % ncs;  // chunks c0 .. c0+ncs-1
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
 
@@ -198,8 +198,9 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 }
 
 // ---------------------------------------------------------------------------
-// walk: one workgroup of 4 waves per (b, h), sequential over chunks, three
-// barriers per chunk:
+// walk: one workgroup of 4 waves per (b, h), sequential over chunks c0..c1-1
+// (the entry d of chunk c0 is d0, or what the launch before left in wout),
+// three barriers per chunk:
 //   A  b_t = <d, p_t> (4 threads per token), rhs_t = 1 - beta_t Gamma_t b_t
 //   B  g = (I + M)^-1 rhs (4 threads per token); c_t, w_t = R_{L,t} alpha_t g_t
 //   C  threads 0-127: d <- Gamma_L d + sum_t w_t p_t, one dimension each (kept
@@ -219,7 +220,7 @@ struct alignas(16) WalkSmem {
 
 __global__ void __launch_bounds__(256)
 walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
-     const float *__restrict__ d0, int T_, int NC, float *__restrict__ wout,
+     const float *__restrict__ d0, int T_, int NC, int c0, int c1, float *__restrict__ wout,
      float *__restrict__ d_final, float *__restrict__ log_ratio,
      float *__restrict__ log_ratio_sum) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -241,7 +242,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
   };
   Regs ra, rb;
   auto load = [&](Regs &R, int cc) {
-    cc = min(cc, NC - 1);
+    cc = min(cc, c1 - 1);
     const long t0 = (long)bh * T_ + (long)cc * C;
     const int L = min(C, T_ - cc * C);
     R.L = L;
@@ -276,13 +277,17 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
 
   float dreg = 0.f;  // owners: d of their dimension, entry value of the chunk in the pass
   if (owner) {
-    dreg = d0 ? d0[(long)bh * DK + tid] : 1.0f;
+    if (c0 == 0) {
+      dreg = d0 ? d0[(long)bh * DK + tid] : 1.0f;
+      if (NC > 0) wout[(long)bh * NC * WOUT + tid] = dreg;
+    } else {
+      dreg = wout[((long)bh * NC + c0) * WOUT + tid];
+    }
     sm.d[tid] = dreg;
-    if (NC > 0) wout[(long)bh * NC * WOUT + tid] = dreg;
-  } else if (NC > 0) {
-    load(ra, 0);
-    load(rb, 1);
-    stash(ra, 0);
+  } else if (c1 > c0) {
+    load(ra, c0);
+    load(rb, c0 + 1);
+    stash(ra, c0 & 1);
   }
   float lr_acc = 0.f;  // sum of log rho_t (threads 128-191)
   __syncthreads();
@@ -358,7 +363,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
       }
       dreg = fmaf(gl, dreg, a0 + a1);
       sm.d[tid] = dreg;
-      if (c + 1 < NC) wout[((long)bh * NC + c + 1) * WOUT + tid] = dreg;
+      if (c + 1 < NC) wout[((long)bh * NC + c + 1) * WOUT + tid] = dreg;  // next entry d
     } else {
       if (lt < C && lt < L) {
         const float gt = sm.g[lt];
@@ -366,21 +371,25 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
         lr_acc += lr;
         if (log_ratio) log_ratio[t0 + lt] = lr;
       }
-      if (c + 1 < NC) stash(next, cb ^ 1);
+      if (c + 1 < c1) stash(next, cb ^ 1);
     }
     __syncthreads();
   };
-  for (int c = 0; c < NC; c += 2) {
+  for (int c = c0; c < c1; c += 2) {
     iteration(c, rb, ra);
-    if (c + 1 < NC) iteration(c + 1, ra, rb);
+    if (c + 1 < c1) iteration(c + 1, ra, rb);
   }
 
-  if (d_final && owner) d_final[(long)bh * DK + tid] = dreg;
+  if (d_final && owner && c1 == NC) d_final[(long)bh * DK + tid] = dreg;
   if (log_ratio_sum) {
+    // this launch's chunks, added to the sums of the launches before it
     const float s = wave_sum(lr_acc);
     if ((tid & 63) == 0) sm.red[tid >> 6] = s;
     __syncthreads();
-    if (tid == 0) log_ratio_sum[bh] = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+    if (tid == 0) {
+      const float part = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+      log_ratio_sum[bh] = c0 == 0 ? part : log_ratio_sum[bh] + part;
+    }
   }
 }
 
@@ -447,20 +456,35 @@ size_t walk_workspace_bytes(int B, int H, int T) {
   return (size_t)B * H * nc * (WREC + WOUT * sizeof(float));
 }
 
-hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, float *wout, hipStream_t s) {
+hipError_t launch_walk_prep(const ScanArgs &a, int c0, int c1, unsigned char *wrec,
+                            hipStream_t s) {
+  const int BH = a.B * a.H;
+  const int NC = (a.T + C - 1) / C;
+  if (BH == 0 || c1 <= c0) return hipSuccess;
+  hipLaunchKernelGGL(walk_prep, dim3((unsigned)(BH * (c1 - c0))), dim3(256), 0, s,
+                     (const bf16 *)a.k, a.beta, a.r, a.eta, a.T, NC, c0, c1 - c0, wrec);
+  return hipGetLastError();
+}
+
+hipError_t launch_walk_pass(const ScanArgs &a, int c0, int c1, const unsigned char *wrec,
+                            float *wout, hipStream_t s) {
   const int BH = a.B * a.H;
   const int NC = (a.T + C - 1) / C;
   if (BH == 0) return hipSuccess;
-  if (NC > 0)
-    hipLaunchKernelGGL(walk_prep, dim3((unsigned)(BH * NC)), dim3(256), 0, s, (const bf16 *)a.k,
-                       a.beta, a.r, a.eta, a.T, NC, wrec);
+  constexpr size_t shm = sizeof(WalkSmem);
   hipError_t e = hipFuncSetAttribute((const void *)walk,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(WalkSmem));
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(walk, dim3((unsigned)BH), dim3(256), sizeof(WalkSmem), s, (const bf16 *)a.k,
-                     (const unsigned char *)wrec, a.d0, a.T, NC, wout, a.d_final, a.log_ratio,
-                     a.log_ratio_sum);
+  hipLaunchKernelGGL(walk, dim3((unsigned)BH), dim3(256), shm, s, (const bf16 *)a.k,
+                     wrec, a.d0, a.T, NC, c0, c1, wout, a.d_final, a.log_ratio, a.log_ratio_sum);
   return hipGetLastError();
+}
+
+hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, float *wout, hipStream_t s) {
+  const int NC = (a.T + C - 1) / C;
+  hipError_t e = launch_walk_prep(a, 0, NC, wrec, s);
+  if (e != hipSuccess) return e;
+  return launch_walk_pass(a, 0, NC, wrec, wout, s);
 }
 
 hipError_t launch_walk_scan(const ScanArgs &a, void *ws, hipStream_t s) {

@@ -129,7 +129,8 @@ def test_chunk_workspace_bytes(lib):
 
 
 def test_split_workspace_bytes(lib):
-    # matrix-core shapes: chunk records (32 KB) plus the walk's results (768 B)
+    # matrix-core shapes: chunk records (32 KB; the walk records of 17 KB use the same
+    # space first) and walk results (768 B)
     # per (b, h, chunk of 64); the walk alone: its records (17 KB) plus results
     assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 0) == 2 * 3 * 3 * (32768 + 768)
     assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 1) == 2 * 3 * 3 * (32768 + 768)
