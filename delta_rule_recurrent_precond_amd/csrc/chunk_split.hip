@@ -67,12 +67,16 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
            const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
            int c0, int ncs, unsigned char *__restrict__ ws, const float *__restrict__ r,
            const float *__restrict__ wout) {
+  // q is needed only for the scores, which are formed first; the blocks of A
+  // and T then reuse its space (53 KB in all: three workgroups per CU)
   __shared__ __align__(16) f16 Ks[C * KP];          // k
   __shared__ __align__(16) f16 Kts[C * KP];         // kt / ds (kt = k: unused)
-  __shared__ __align__(16) f16 Qs[C * KP];          // q
-  __shared__ __align__(16) float Fd[4][16][LDF];   // diagonal blocks of A (fp32)
-  __shared__ __align__(16) f16 Aoff[6][16][LDT];   // off-diagonal blocks of A (fp16)
-  __shared__ __align__(16) f16 Tdg[4][16][LDT];    // diagonal blocks of T (fp16)
+  __shared__ __align__(16) unsigned char QF[C * KP * 2];
+  f16 *Qs = (f16 *)QF;                                                 // q
+  float(*Fd)[16][LDF] = (float(*)[16][LDF])QF;                         // diagonal blocks of A
+  f16(*Aoff)[16][LDT] = (f16(*)[16][LDT])(QF + 4 * 16 * LDF * 4);       // off-diagonal blocks of A
+  f16(*Tdg)[16][LDT] = (f16(*)[16][LDT])(QF + 4 * 16 * LDF * 4 + 6 * 16 * LDT * 2);  // diag of T
+  static_assert(4 * 16 * LDF * 4 + 10 * 16 * LDT * 2 <= C * KP * 2, "A and T blocks fit");
   __shared__ float bs[C];
   __shared__ float cs[C], rs[C];  // kOsdn: c_t and r_t
   __shared__ float red[4];
@@ -86,16 +90,25 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   unsigned char *rec = ws + ((long)bh * NC + c) * REC;
   const f16 *Ktp = (MODE == kDeltaNet) ? Ks : Kts;
 
-  // ---- loads: 1024 pieces of 8 elements per tensor, 4 per thread
+  // ---- loads: 1024 pieces of 8 elements per tensor, 4 per thread.  Rows past
+  // the end reread the last row (a load under a condition would make the
+  // compiler wait for it where the branches join) and are zeroed here.
   uint4 rk[4], rq[4], rt[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = p >> 4;
-    const long off = (tok0 + t) * DK + (p & 15) * 8;
-    const bool ok = t < L;
-    rk[u] = ok ? *(const uint4 *)(k + off) : uint4{0, 0, 0, 0};
-    rq[u] = ok ? *(const uint4 *)(q + off) : uint4{0, 0, 0, 0};
-    if (MODE == kGiven) rt[u] = ok ? *(const uint4 *)(kt_in + off) : uint4{0, 0, 0, 0};
+    const long off = (tok0 + min(t, L - 1)) * DK + (p & 15) * 8;
+    rk[u] = *(const uint4 *)(k + off);
+    rq[u] = *(const uint4 *)(q + off);
+    if (MODE == kGiven) rt[u] = *(const uint4 *)(kt_in + off);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if ((tid + 256 * u) >> 4 >= L) {
+      rk[u] = uint4{0, 0, 0, 0};
+      rq[u] = uint4{0, 0, 0, 0};
+      if (MODE == kGiven) rt[u] = uint4{0, 0, 0, 0};
+    }
   }
   if (tid < C) bs[tid] = tid < L ? beta[tok0 + tid] : 0.f;
   if (MODE == kOsdn && tid < C) {
@@ -179,6 +192,19 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   };
   auto beta4 = [&](int rt_) { return *(const f32x4 *)&bs[16 * rt_ + 4 * g]; };
 
+  // ---- scores P = lower(Q Kt^T) ds, emitted as A operands (transposed tiles)
+  for (int idx = wave; idx < 10; idx += 4) {
+    int rt_, ct;
+    tri_tile(idx, rt_, ct);
+    const f32x4 acc = gram(Qs, rt_, ct);
+    f32x4 pv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = (16 * ct + c16 <= 16 * rt_ + 4 * g + e) ? ds * acc[e] : 0.f;
+    const f16x4 pt = h4(mma16(h4(pv), ident, zero4()));
+    *(f16x4 *)(rec + OFF_P + ((op_index(rt_, ct >> 1) * 64 + lane) * 8 + 4 * (ct & 1)) * 2) = pt;
+  }
+  __syncthreads();  // q is no longer read: its space takes the blocks of A and T
+
   // ---- A: diagonal block `wave` (then its inverse) and off-diagonal blocks
   {
     const f32x4 acc = gram(Ks, wave, wave);
@@ -205,17 +231,6 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int j = 0; j < 4; ++j) Tdg[wave][(lane & 3) + 4 * j][lane >> 2] = h(x[j]);
   }
 
-  // ---- scores P = lower(Q Kt^T) ds, emitted as A operands (transposed tiles)
-  for (int idx = wave; idx < 10; idx += 4) {
-    int rt_, ct;
-    tri_tile(idx, rt_, ct);
-    const f32x4 acc = gram(Qs, rt_, ct);
-    f32x4 pv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pv[e] = (16 * ct + c16 <= 16 * rt_ + 4 * g + e) ? ds * acc[e] : 0.f;
-    const f16x4 pt = h4(mma16(h4(pv), ident, zero4()));
-    *(f16x4 *)(rec + OFF_P + ((op_index(rt_, ct >> 1) * 64 + lane) * 8 + 4 * (ct & 1)) * 2) = pt;
-  }
   // the two zero halves of P and T: blocks (0,1) and (2,3)
   if (wave == 0) {
     const f16x4 z = {0, 0, 0, 0};
