@@ -1,15 +1,17 @@
-"""Measured HBM traffic and kernel-time summaries for the library's kernels.
+"""Measured HBM traffic and kernel-time summaries for the library's entry points.
 
-HBM bytes per launch come from two rocprofv3 counter passes over the same
+HBM bytes per call come from two rocprofv3 counter passes over the same
 program (the counter blocks cannot hold FETCH_SIZE and WRITE_SIZE in one pass),
 each scaled by what the same counter reads for a device-to-device copy of a
-known size run in the same process:
+known size run in the same process.  A call may launch several kernels (the
+split forward launches four); its bytes are the sum over every library kernel
+the program dispatched, divided by the number of calls:
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d D1 -o run -- \\
-        python3 -m delta_rule_recurrent_precond_amd.profiling run
+        python3 -m delta_rule_recurrent_precond_amd.profiling run --entry E
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d D2 -o run -- \\
-        python3 -m delta_rule_recurrent_precond_amd.profiling run
-    python3 -m delta_rule_recurrent_precond_amd.profiling record --fetch D1 --write D2
+        python3 -m delta_rule_recurrent_precond_amd.profiling run --entry E
+    python3 -m delta_rule_recurrent_precond_amd.profiling record --entry E --fetch D1 --write D2
 
 `record` writes profiles/traffic.json (read by bench.py; an entry only counts
 while the kernel sources are unchanged) and a text summary under profiles/.
@@ -29,9 +31,14 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CAL_BYTES = 1 << 30  # calibration copy: 1 GiB read, 1 GiB written
-# template argument of osdn_fused_forward -> the entry point it serves
-MODES = {"0": "osdn_fused_forward", "1": "osdn_fused_deltanet", "2": "osdn_fused_chunk",
-         "3": "osdn_fused_scan"}
+# entry -> the label bench.py looks up in traffic.json
+ENTRIES = {
+    "forward_split": "osdn_forward_split",
+    "forward_fused": "osdn_fused_forward",
+    "deltanet_split": "osdn_deltanet_split",
+    "scan_split": "osdn_precond_scan_split",
+    "chunk_split": "osdn_chunk_fwd_split",
+}
 
 
 def kernel_sources_hash() -> str:
@@ -41,19 +48,34 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _kernel_label(name: str):
-    """Entry-point label of an osdn kernel name (mangled or demangled), or None."""
-    if "osdn_fused_forward" not in name:
-        return None
-    for key, label in MODES.items():
-        if "ILi%sE" % key in name or "osdn_fused_forward<%s>" % key in name:
-            return label
-    return None
+def _is_library_kernel(name: str) -> bool:
+    """Kernels of libosdn.so (namespace osdn, mangled or demangled)."""
+    return "4osdn" in name or "osdn::" in name
 
 
-def run(workload: str, launches: int) -> None:
+def call(entry: str, dev, w):
+    """One call of the entry point on the device inputs."""
+    import delta_rule_recurrent_precond_amd as osdn
+
+    if entry == "forward_split":
+        osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=dev.eta, chunk=w.chunk)
+    elif entry == "forward_fused":
+        osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=dev.eta, chunk=w.chunk,
+                     workspace=None)
+    elif entry == "deltanet_split":
+        osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=dev.eta, chunk=w.chunk,
+                     precond=False)
+    elif entry == "scan_split":
+        osdn.precond_scan(dev.k, dev.beta, dev.r, None, dev.eta)
+    elif entry == "chunk_split":
+        osdn.chunk_fwd(dev.q, dev.k, dev.k, dev.v, dev.beta, chunk=w.chunk)
+    else:
+        raise SystemExit("unknown entry %s" % entry)
+
+
+def run(workload: str, launches: int, entry: str) -> None:
     """The program the counter passes profile: a calibration copy, then
-    `launches` calls of each fused entry point on the workload."""
+    `launches` calls of one entry point on the workload."""
     import torch
 
     import delta_rule_recurrent_precond_amd as osdn
@@ -69,14 +91,9 @@ def run(workload: str, launches: int) -> None:
     w = W.CONFIGS[workload]
     dev = W.generate(w).to("cuda")
     for _ in range(launches):
-        osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=dev.eta, chunk=w.chunk)
-        osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=dev.eta, chunk=w.chunk,
-                     precond=False)
-        sc = osdn.precond_scan(dev.k, dev.beta, dev.r, None, dev.eta)
-        osdn.chunk_fwd(dev.q, dev.k, sc["k_tilde"], dev.v, dev.beta, chunk=w.chunk)
+        call(entry, dev, w)
     torch.cuda.synchronize()
-    print("profiled program done: %s, %d launches per entry point" % (workload, launches),
-          flush=True)
+    print("profiled program done: %s, %s, %d calls" % (workload, entry, launches), flush=True)
 
 
 def _counter_rows(directory: str):
@@ -90,66 +107,66 @@ def _counter_rows(directory: str):
     return rows
 
 
-def _means(directory: str, counter: str):
-    """Mean counter value per dispatch for the calibration copy and each osdn kernel."""
-    sums, counts = {}, {}
+def _totals(directory: str, counter: str):
+    """Mean counter value per dispatch of the calibration copy (the three
+    largest copies), and the sum over every library kernel dispatch with the
+    per-kernel dispatch counts."""
+    per = {}
     for r in _counter_rows(directory):
         if r.get("Counter_Name", "").strip() != counter:
             continue
         name = r.get("Kernel_Name", "")
-        label = _kernel_label(name)
-        if label is None and "copy" in name.lower():
-            label = "copy"
-        if label is None:
-            continue
-        v = float(r["Counter_Value"])
-        # one row per dispatch and counter (values already summed over instances)
-        key = (label, r.get("Dispatch_Id", r.get("Correlation_Id")))
-        sums[key] = sums.get(key, 0.0) + v
-    per = {}
-    for (label, _), v in sums.items():
-        per.setdefault(label, []).append(v)
-    out = {}
-    for label, vs in per.items():
-        if label == "copy":
-            vs = sorted(vs)[-3:]  # the three 1 GiB copies are the largest
-        out[label] = (sum(vs) / len(vs), len(vs))
-    return out
+        key = (name, r.get("Dispatch_Id", r.get("Correlation_Id")))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])  # summed over instances
+    copies = sorted(v for (n, _), v in per.items() if "copy" in n.lower())[-3:]
+    lib = {}
+    for (n, _), v in per.items():
+        if _is_library_kernel(n):
+            tot, cnt = lib.get(n, (0.0, 0))
+            lib[n] = (tot + v, cnt + 1)
+    copy_mean = sum(copies) / len(copies) if copies else None
+    return copy_mean, lib
 
 
-def record(fetch_dir: str, write_dir: str, workload: str, cmd_fetch: str, cmd_write: str) -> None:
-    fetch = _means(fetch_dir, "FETCH_SIZE")
-    write = _means(write_dir, "WRITE_SIZE")
-    if "copy" not in fetch or "copy" not in write:
+def record(fetch_dir: str, write_dir: str, workload: str, entry: str, launches: int,
+           cmd_fetch: str, cmd_write: str) -> None:
+    copy_f, fetch = _totals(fetch_dir, "FETCH_SIZE")
+    copy_w, write = _totals(write_dir, "WRITE_SIZE")
+    if not copy_f or not copy_w:
         raise SystemExit("calibration copy not found in the counter output")
-    f_fetch = CAL_BYTES / fetch["copy"][0]
-    f_write = CAL_BYTES / write["copy"][0]
+    if not fetch or not write:
+        raise SystemExit("no library kernel in the counter output")
+    f_fetch = CAL_BYTES / copy_f
+    f_write = CAL_BYTES / copy_w
+    fb = sum(t for t, _ in fetch.values()) * f_fetch / launches
+    wb = sum(t for t, _ in write.values()) * f_write / launches
+    label = ENTRIES[entry]
     path = os.path.join(ROOT, "profiles", "traffic.json")
     db = json.load(open(path)) if os.path.exists(path) else {}
     src = kernel_sources_hash()
-    lines = ["HBM traffic per launch, workload %s (kernel sources %s)" % (workload, src), "",
+    db["%s|%s" % (label, workload)] = {
+        "sources": src, "bytes_per_launch": fb + wb, "fetch_bytes": fb, "write_bytes": wb,
+        "fetch_factor": f_fetch, "write_factor": f_write, "calls": launches}
+    json.dump(db, open(path, "w"), indent=1, sort_keys=True)
+    lines = ["HBM traffic per call of %s, workload %s (kernel sources %s)" % (label, workload, src),
+             "",
              "command (FETCH_SIZE pass): " + cmd_fetch,
              "command (WRITE_SIZE pass): " + cmd_write,
              "command (this summary): python3 -m delta_rule_recurrent_precond_amd.profiling "
-             "record --fetch <D1> --write <D2> --workload %s" % workload, "",
+             "record --entry %s --fetch <D1> --write <D2> --workload %s --launches %d"
+             % (entry, workload, launches), "",
              "calibration: device-to-device copy of %d bytes; FETCH_SIZE reads %.6g, "
-             "WRITE_SIZE reads %.6g per dispatch" % (CAL_BYTES, fetch["copy"][0], write["copy"][0]),
+             "WRITE_SIZE reads %.6g per dispatch" % (CAL_BYTES, copy_f, copy_w),
              "scale factors (bytes per counter unit): fetch %.4f, write %.4f" % (f_fetch, f_write),
              "",
-             "%-22s %9s %14s %14s %16s" % ("kernel", "launches", "FETCH_SIZE", "WRITE_SIZE",
-                                          "bytes/launch")]
-    for label in MODES.values():
-        if label not in fetch or label not in write:
-            continue
-        fb = fetch[label][0] * f_fetch
-        wb = write[label][0] * f_write
-        db["%s|%s" % (label, workload)] = {
-            "sources": src, "bytes_per_launch": fb + wb, "fetch_bytes": fb, "write_bytes": wb,
-            "fetch_factor": f_fetch, "write_factor": f_write}
-        lines.append("%-22s %9d %14.6g %14.6g %16.6g" % (label, fetch[label][1], fetch[label][0],
-                                                         write[label][0], fb + wb))
-    json.dump(db, open(path, "w"), indent=1, sort_keys=True)
-    txt = os.path.join(ROOT, "profiles", "traffic_fused_kernels_%s.txt" % workload)
+             "%-64s %9s %16s %16s" % ("kernel", "dispatches", "fetch bytes/call", "write bytes/call")]
+    for n in sorted(set(fetch) | set(write)):
+        tf, cf = fetch.get(n, (0.0, 0))
+        tw, _ = write.get(n, (0.0, 0))
+        lines.append("%-64s %9d %16.6g %16.6g" % (n[:64], cf, tf * f_fetch / launches,
+                                                  tw * f_write / launches))
+    lines += ["", "total bytes per call: %.6g (fetch %.6g, write %.6g)" % (fb + wb, fb, wb)]
+    txt = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (entry, workload))
     open(txt, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -177,10 +194,13 @@ def main(argv=None):
     p = sub.add_parser("run")
     p.add_argument("--workload", default="1.3b-apf")
     p.add_argument("--launches", type=int, default=3)
+    p.add_argument("--entry", choices=sorted(ENTRIES), required=True)
     p = sub.add_parser("record")
     p.add_argument("--fetch", required=True)
     p.add_argument("--write", required=True)
     p.add_argument("--workload", default="1.3b-apf")
+    p.add_argument("--launches", type=int, default=3)
+    p.add_argument("--entry", choices=sorted(ENTRIES), required=True)
     p.add_argument("--cmd-fetch", default="")
     p.add_argument("--cmd-write", default="")
     p = sub.add_parser("summary")
@@ -189,9 +209,9 @@ def main(argv=None):
     p.add_argument("--out")
     a = ap.parse_args(argv)
     if a.cmd == "run":
-        run(a.workload, a.launches)
+        run(a.workload, a.launches, a.entry)
     elif a.cmd == "record":
-        record(a.fetch, a.write, a.workload, a.cmd_fetch, a.cmd_write)
+        record(a.fetch, a.write, a.workload, a.entry, a.launches, a.cmd_fetch, a.cmd_write)
     else:
         text = summary(a.src, a.command)
         if a.out:

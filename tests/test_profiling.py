@@ -20,22 +20,48 @@ def _write(tmp_path, rows):
     return str(d)
 
 
-def test_kernel_labels():
-    assert profiling._kernel_label(MANGLED % 0) == "osdn_fused_forward"
-    assert profiling._kernel_label(MANGLED % 3) == "osdn_fused_scan"
-    assert profiling._kernel_label("osdn::osdn_fused_forward<2>(...)") == "osdn_fused_chunk"
-    assert profiling._kernel_label("__amd_rocclr_copyBuffer") is None
+def test_library_kernels():
+    assert profiling._is_library_kernel(MANGLED % 0)
+    assert profiling._is_library_kernel("osdn::(anonymous namespace)::chunk_state(...)")
+    assert not profiling._is_library_kernel("__amd_rocclr_copyBuffer")
+    assert not profiling._is_library_kernel("void at::native::vectorized_elementwise_kernel")
 
 
-def test_means_pick_the_three_largest_copies(tmp_path):
+def test_totals_sum_library_kernels_and_pick_the_three_largest_copies(tmp_path):
     rows = [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 7.0)]  # a small unrelated copy
     rows += [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 100.0)] * 3
     rows += [(MANGLED % 0, "FETCH_SIZE", 10.0), (MANGLED % 0, "FETCH_SIZE", 14.0),
-             (MANGLED % 1, "WRITE_SIZE", 99.0)]
-    m = profiling._means(_write(tmp_path, rows), "FETCH_SIZE")
-    assert m["copy"] == (100.0, 3)
-    assert m["osdn_fused_forward"] == (12.0, 2)
-    assert "osdn_fused_deltanet" not in m
+             ("osdn::walk(...)", "FETCH_SIZE", 5.0), (MANGLED % 1, "WRITE_SIZE", 99.0)]
+    copy_mean, lib = profiling._totals(_write(tmp_path, rows), "FETCH_SIZE")
+    assert copy_mean == 100.0
+    assert lib[MANGLED % 0] == (24.0, 2)
+    assert lib["osdn::walk(...)"] == (5.0, 1)
+    assert MANGLED % 1 not in lib
+
+
+def test_record_divides_by_calls(tmp_path, monkeypatch):
+    rows_f = [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 1024.0)] * 3
+    rows_f += [("osdn::walk(...)", "FETCH_SIZE", 64.0)] * 2
+    rows_w = [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 2048.0)] * 3
+    rows_w += [("osdn::walk(...)", "WRITE_SIZE", 8.0)] * 2
+    df = tmp_path / "f"
+    dw = tmp_path / "w"
+    df.mkdir()
+    dw.mkdir()
+    for d, rows in ((df, rows_f), (dw, rows_w)):
+        with open(d / "run_counter_collection.csv", "w", newline="") as f:
+            wr = csv.writer(f)
+            wr.writerow(HEADER)
+            for i, (name, counter, value) in enumerate(rows):
+                wr.writerow([i + 1, i + 1, name, counter, value])
+    monkeypatch.setattr(profiling, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    profiling.record(str(df), str(dw), "wl", "scan_split", 2, "cf", "cw")
+    import json
+    rec = json.load(open(tmp_path / "profiles" / "traffic.json"))["osdn_precond_scan_split|wl"]
+    # 2 dispatches x 64 units x (2^30 / 1024) bytes per unit, over 2 calls
+    assert rec["fetch_bytes"] == 64 * (1 << 30) / 1024
+    assert rec["write_bytes"] == 8 * (1 << 30) / 2048
 
 
 def test_summary_table(tmp_path):
