@@ -8,7 +8,9 @@ q/k/v are cast once (round-to-nearest-even) to the stored dtype.  Those stored
 bits are the inputs of every implementation.
 
 Draw order per seed: q, k, v, beta-logits, r-logits, alpha-logits (state
-gate, gated workloads only).  The recall workload draws its key pool, value
+gate, gated workloads only).  Raw workloads skip the normalisation and the
+sigmoids (the same draws, so their transforms give the plain workload's values
+before rounding).  The recall workload draws its key pool, value
 pool and index sequence first.
 
 The pages measure on recall/perplexity datasets that are not available here;
@@ -46,6 +48,7 @@ class Workload:
     gated: bool = False   # state gate alpha present (Gated DeltaNet backbone)
     alpha_mu: float = 3.0
     alpha_sigma: float = 1.0
+    raw: bool = False     # q, k not normalised and beta, r as logits (the kernels transform them)
 
     @property
     def tokens(self) -> int:
@@ -151,11 +154,14 @@ def generate(w: Workload, seed: Optional[int] = None) -> Inputs:
             v[b] = vals[:, idx[b], :]
         q = k.copy()                                           # queries are the keys
     else:
-        q = _l2n(rng.standard_normal((B, H, T, dk)))
-        k = _l2n(rng.standard_normal((B, H, T, dk)))
+        q = rng.standard_normal((B, H, T, dk))
+        k = rng.standard_normal((B, H, T, dk))
+        if not w.raw:
+            q, k = _l2n(q), _l2n(k)
         v = rng.standard_normal((B, H, T, dv))
-    beta = _sigmoid(w.beta_mu + w.beta_sigma * rng.standard_normal((B, H, T)))
-    r = _sigmoid(w.r_mu + w.r_sigma * rng.standard_normal((B, H, T))) if w.apf else None
+    gate = (lambda x: x) if w.raw else _sigmoid
+    beta = gate(w.beta_mu + w.beta_sigma * rng.standard_normal((B, H, T)))
+    r = gate(w.r_mu + w.r_sigma * rng.standard_normal((B, H, T))) if w.apf else None
     alpha = (_sigmoid(w.alpha_mu + w.alpha_sigma * rng.standard_normal((B, H, T)))
              if w.gated else None)
     f32 = lambda x: None if x is None else torch.from_numpy(x).to(torch.float32)

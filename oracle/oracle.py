@@ -18,6 +18,9 @@ chunked_state_pass the chunkwise (WY/UT) form of the state pass with K~ in
 chunked_dwalk      the preconditioner recurrence unrolled over a chunk
                    (affine in d, as the APF section notes)          [summary §2.3]
 q_geo              geometric mean of the token-local residual ratios [summary §3, §4.2]
+prepare_inputs     L2 normalisation of q and k per token and the logistic sigmoid
+                   of gate logits, the input transforms the measured workloads
+                   apply before the recurrence (plain definitions, fp64)
 
 Every function here is pinned by tests/test_oracle_*.py against closed forms,
 special cases, an exact-rational brute force or an independent formulation.
@@ -81,6 +84,29 @@ def _f64(x):
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def prepare_inputs(q, k, beta, r=None, norm_qk=True, gate_logits=True):
+    """The input transforms on the stored values, in fp64.
+
+    norm_qk: q_t <- q_t / ||q_t||_2 and k_t <- k_t / ||k_t||_2 per token (a zero
+    vector stays zero).  gate_logits: beta_t <- 1 / (1 + exp(-beta_t)), and the
+    same for r_t.  Returns (q, k, beta, r) as fp64 arrays (r None if absent).
+    """
+    q, k, beta, r = _f64(q), _f64(k), _f64(beta), _f64(r)
+    if norm_qk:
+        def unit(x):
+            n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+            return np.where(n > 0, x / np.where(n > 0, n, 1.0), 0.0)
+        q, k = unit(q), unit(k)
+    if gate_logits:
+        def sig(x):
+            if x is None:
+                return None
+            with np.errstate(over="ignore"):  # exp(-x) = inf gives 0 exactly
+                return 1.0 / (1.0 + np.exp(-x))
+        beta, r = sig(beta), sig(r)
+    return q, k, beta, r
 
 
 def default_threads() -> int:
