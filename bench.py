@@ -212,6 +212,28 @@ def main():
         ms_g = time_launches(lambda i: fwd(i, gated=True), args.steps, args.warmup, torch)
         ms_gdn = time_launches(lambda i: fwd(i, precond=False, gated=True), args.steps,
                                args.warmup, torch)
+        # raw inputs (q, k unnormalised, beta and r as logits): the transforms done
+        # inside the kernels, against separate elementwise passes before the call
+        raw_host = W.generate(dataclasses.replace(w, raw=True))
+        raws = [raw_host.to("cuda") for _ in range(copies)]
+        del raw_host
+
+        def fwd_raw(i, fused=True):
+            d = raws[i % copies]
+            o = outs[i % copies]
+            if fused:
+                osdn.forward(d.q, d.k, d.v, d.beta, d.r, eta=d.eta, chunk=C, out=o,
+                             workspace=ws, norm_qk=True, gate_logits=True)
+            else:
+                qn = torch.nn.functional.normalize(d.q.float(), dim=-1).to(d.q.dtype)
+                kn = torch.nn.functional.normalize(d.k.float(), dim=-1).to(d.k.dtype)
+                osdn.forward(qn, kn, d.v, torch.sigmoid(d.beta),
+                             None if d.r is None else torch.sigmoid(d.r), eta=d.eta, chunk=C,
+                             out=o, workspace=ws)
+
+        ms_raw = time_launches(fwd_raw, args.steps, args.warmup, torch)
+        ms_raw_sep = time_launches(lambda i: fwd_raw(i, False), args.steps, args.warmup, torch)
+        del raws
         kts = [torch.empty_like(d.k) for d in devs]
         dfin = torch.empty((B, H, dk), dtype=torch.float32, device="cuda")
         lib = osdn.load()
@@ -270,6 +292,10 @@ def main():
                               "vs_ungated": ms_g / ms},
             "gated_deltanet_mode": {"ms": ms_gdn, "tokens_per_s": tokens / (ms_gdn * 1e-3)},
             "gated_precond_overhead": (ms_g - ms_gdn) / ms_g,
+            "raw_inputs_transforms_in_kernels": {"ms": ms_raw,
+                                                 "tokens_per_s": tokens / (ms_raw * 1e-3)},
+            "raw_inputs_separate_torch_passes": {"ms": ms_raw_sep,
+                                                 "tokens_per_s": tokens / (ms_raw_sep * 1e-3)},
             "two_launch_scan_share": ms_scan / (ms_scan + ms_chunk),
         }
         result["phases"] = phases

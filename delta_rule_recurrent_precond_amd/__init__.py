@@ -144,10 +144,16 @@ def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64, *, alpha=None, workspac
     return o, S_final
 
 
-def step(q, k, v, beta, S, d, r=None, eta=0.05, *, alpha=None, o=None, want_log_ratio=False):
+def _transform_flags(norm_qk, gate_logits):
+    return (_lib.OSDN_NORM_QK if norm_qk else 0) | (_lib.OSDN_GATE_LOGITS if gate_logits else 0)
+
+
+def step(q, k, v, beta, S, d, r=None, eta=0.05, *, alpha=None, o=None, want_log_ratio=False,
+         norm_qk=False, gate_logits=False):
     """One decoding step.  q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), beta, r and
     the optional state gate alpha [B,H] fp32; S [B,H,dv,dk] and d [B,H,dk] fp32
-    are updated in place.
+    are updated in place.  ``norm_qk``: q, k are unnormalised (the kernel
+    divides them by their norms); ``gate_logits``: beta, r are logits.
     Returns dict(o[, log_ratio])."""
     _dev(q, "q")
     B, H, dk = q.shape
@@ -165,9 +171,9 @@ def step(q, k, v, beta, S, d, r=None, eta=0.05, *, alpha=None, o=None, want_log_
     o = torch.empty_like(v) if o is None else o
     lr = torch.empty((B, H), dtype=torch.float32, device=dev) if want_log_ratio else None
     st = _lib.load().osdn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(alpha),
-                               float(eta), B, H,
-                               dk, dv, _dtype_code(q), _ptr(S), _ptr(d), _ptr(o), _ptr(lr),
-                               _stream(dev))
+                               float(eta), B, H, dk, dv, _dtype_code(q),
+                               _transform_flags(norm_qk, gate_logits), _ptr(S), _ptr(d), _ptr(o),
+                               _ptr(lr), _stream(dev))
     _lib.check("osdn_step", st)
     out = {"o": o}
     if want_log_ratio:
@@ -191,8 +197,13 @@ def forward_path(B, H, T, dk, dv, chunk, dtype_code, precond=True, gated=False,
 
 
 def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond=True,
-            *, alpha=None, out=None, workspace=True):
+            *, alpha=None, out=None, workspace=True, norm_qk=False, gate_logits=False):
     """Both phases.  Returns dict(o, S_final, d_final, log_ratio_sum).
+
+    ``norm_qk``: q and k are unnormalised and the kernels divide each by its L2
+    norm; ``gate_logits``: beta and r are logits and the kernels take their
+    sigmoid (multi-launch and two-phase paths; not with alpha on the shapes of
+    the single fused kernel).
 
     ``alpha`` [B,H,T] fp32 is the optional state gate (Gated DeltaNet backbone;
     with precond=False, Gated DeltaNet itself).
@@ -217,7 +228,7 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond
     _dev(d0, "d0", (B, H, dk), torch.float32, dev)
     _dev(S0, "S0", (B, H, dv, dk), torch.float32, dev)
     code = _dtype_code(q)
-    flags = 0 if precond else _lib.OSDN_PRECOND_OFF
+    flags = (0 if precond else _lib.OSDN_PRECOND_OFF) | _transform_flags(norm_qk, gate_logits)
     if out is None:
         out = {
             "o": torch.empty_like(v),

@@ -23,6 +23,8 @@ OSDN_ERR_HIP = -5
 OSDN_BF16 = 0
 OSDN_F32 = 1
 OSDN_PRECOND_OFF = 1
+OSDN_NORM_QK = 2
+OSDN_GATE_LOGITS = 4
 
 _lib = None
 _lock = threading.Lock()
@@ -36,7 +38,7 @@ SIGNATURES = {
     "osdn_chunk_fwd": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, ctypes.c_size_t,
                            P]),
     "osdn_chunk_fwd_workspace_bytes": (ctypes.c_size_t, [I, I, I, I, I, I, I]),
-    "osdn_step": (I, [P, P, P, P, P, P, F, I, I, I, I, I, P, P, P, P, P]),
+    "osdn_step": (I, [P, P, P, P, P, P, F, I, I, I, I, I, ctypes.c_uint, P, P, P, P, P]),
     "osdn_forward": (I, [P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, ctypes.c_uint,
                          P, P, P, P, P, ctypes.c_size_t, P]),
     "osdn_forward_workspace_bytes": (ctypes.c_size_t, [I, I, I, I, I, I, I, ctypes.c_uint]),

@@ -34,7 +34,7 @@ __global__ void __launch_bounds__(kThreads)
 chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ kt,
               const T *__restrict__ v, const float *__restrict__ beta,
               const float *__restrict__ alpha, const float *__restrict__ S0, int T_, int dv,
-              T *__restrict__ o, float *__restrict__ S_final) {
+              T *__restrict__ o, float *__restrict__ S_final, unsigned xf) {
   constexpr int DKP = DK + 1;          // padded rows (bank spread)
   constexpr int CP = C + 1;
   constexpr int XP = DVT + 1;
@@ -55,6 +55,15 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
   const int j0 = blockIdx.y * DVT;  // first value channel of this tile
 
   const long tok0 = bh * (long)T_;
+  // q and k rows divided by their norms when they arrive unnormalised
+  auto normalise_rows = [&](float *X) {
+    for (int t = tid; t < C; t += kThreads) {
+      float n = 0.0f;
+      for (int i = 0; i < DK; ++i) n = fmaf(X[t * DKP + i], X[t * DKP + i], n);
+      const float sc = unit_scale(n);
+      for (int i = 0; i < DK; ++i) X[t * DKP + i] *= sc;
+    }
+  };
   for (int idx = tid; idx < DVT * DK; idx += kThreads) {
     const int j = idx / DK, i = idx % DK;
     sS[j * DKP + i] = S0 ? S0[(bh * dv + j0 + j) * DK + i] : 0.0f;
@@ -74,7 +83,10 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       const int t = idx / DVT, j = idx % DVT;
       sV[idx] = t < L ? Elem<T>::load(v + (tok0 + c0 + t) * (long)dv + j0 + j) : 0.0f;
     }
-    for (int t = tid; t < C; t += kThreads) sB[t] = t < L ? beta[tok0 + c0 + t] : 0.0f;
+    for (int t = tid; t < C; t += kThreads) {
+      const float bv = t < L ? beta[tok0 + c0 + t] : 0.0f;
+      sB[t] = (t < L && (xf & kGateLogits)) ? sigmoid_gate(bv) : bv;
+    }
     if (tid == 0) {
       float acc = 0.0f;
       for (int t = 0; t < C; ++t) {
@@ -83,6 +95,11 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       }
     }
     __syncthreads();
+    if (xf & kNormQK) {
+      normalise_rows(sK);
+      if (xf & kNormKt) normalise_rows(sKt);
+      __syncthreads();
+    }
 
     // 2. mixed gram A and right-hand side R = diag(beta)(V - K S^T)
     for (int idx = tid; idx < C * C; idx += kThreads) {
@@ -124,6 +141,10 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       }
     }
     __syncthreads();
+    if (xf & kNormQK) {
+      normalise_rows(sK);
+      __syncthreads();
+    }
 
     // 4. intra-chunk scores P = lower(Q Kt^T) (diagonal included) into sA
     for (int idx = tid; idx < C * C; idx += kThreads) {
@@ -182,7 +203,7 @@ hipError_t launch_c(const ChunkArgs &a, hipStream_t s, dim3 grid) {
     hipLaunchKernelGGL((chunk_generic<T, DK, DVT, C_>), grid, block, 0, s, (const T *)a.q,   \
                        (const T *)a.k, (const T *)a.k_tilde, (const T *)a.v, a.beta, a.alpha,\
                        a.S0,                                                                   \
-                       a.T, a.dv, (T *)a.o, a.S_final);                                       \
+                       a.T, a.dv, (T *)a.o, a.S_final, a.xf);                                 \
     break;
   switch (a.chunk) {
     OSDN_GEN_CASE(16)

@@ -23,6 +23,8 @@
 //   PA   fp16 [6 ops][64 lanes][8]  rows of P ds as A operands, paired k order
 //   ds   fp32 write-key scale: kt is stored divided by ds, a power of two
 //   lr   fp32 (kt = k only) sum over the chunk of log rho_t, rho_t = (1 - beta_t ||k_t||^2)^2
+//   sc   fp32 [2][64] (q, k given unnormalised) 1/||k_t|| and 1/||q_t||: the state
+//        kernel stages q and k as stored and scales the rows of K S^T and Q S^T
 // op x = 0..5 is (row block m, t pair qq) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
 #include "device.h"
 #include "launch.h"
@@ -45,6 +47,7 @@ constexpr size_t OFF_TM = 16384;
 constexpr size_t OFF_P = 22528;
 constexpr size_t OFF_DS = 28672;
 constexpr size_t OFF_LR = 28676;  // kt = k: sum over the chunk of log rho_t
+constexpr size_t OFF_SC = 28688;  // per-token 1/||k_t||, then 1/||q_t||
 constexpr int LDT = 24;  // padded row (halves) of the 16x16 fp16 blocks in LDS
 constexpr int LDF = 20;  // padded row (floats) of the 16x16 fp32 blocks in LDS
 
@@ -61,12 +64,17 @@ constexpr int KP = 136;  // padded row (halves) of the staged [64][128] tiles
 // d_{t+1} = r_t d_t + c_t (k_t (.) k_t) from the chunk's entry d and the c_t
 // of the walk (one key dimension each, fp32), forming kt_t = d_t (.) k_t twice:
 // once for its largest magnitude (the scale ds), once to stage kt / ds.
-template <int MODE>
+// NORM (forward only): q and k arrive unnormalised.  q is staged normalised;
+// for kOsdn k is staged as stored (exact) and its 1/||k_t|| enters the
+// recurrence and the rows of A in fp32; for kt = k it is staged normalised.
+// Both scales go to the record for the state kernel.  xf & kGateLogits: beta
+// and r arrive as logits.
+template <int MODE, bool NORM>
 __global__ void __launch_bounds__(256)
 chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
            const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
            int c0, int ncs, unsigned char *__restrict__ ws, const float *__restrict__ r,
-           const float *__restrict__ wout) {
+           const float *__restrict__ wout, unsigned xf) {
   // q is needed only for the scores, which are formed first; the blocks of A
   // and T then reuse its space (53 KB in all: three workgroups per CU)
   __shared__ __align__(16) f16 Ks[C * KP];          // k
@@ -79,6 +87,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   static_assert(4 * 16 * LDF * 4 + 10 * 16 * LDT * 2 <= C * KP * 2, "A and T blocks fit");
   __shared__ float bs[C];
   __shared__ float cs[C], rs[C];  // kOsdn: c_t and r_t
+  __shared__ float sk[C];         // kOsdn, NORM: 1 / ||k_t||
   __shared__ float red[4];
 
   const int tid = threadIdx.x;
@@ -110,10 +119,38 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (MODE == kGiven) rt[u] = uint4{0, 0, 0, 0};
     }
   }
-  if (tid < C) bs[tid] = tid < L ? beta[tok0 + tid] : 0.f;
+  if (tid < C) {
+    const float bv = beta[tok0 + min(tid, L - 1)];
+    bs[tid] = tid < L ? ((xf & kGateLogits) ? sigmoid_gate(bv) : bv) : 0.f;
+  }
   if (MODE == kOsdn && tid < C) {
     cs[tid] = tid < L ? wout[((long)bh * NC + c) * WOUT + DK + tid] : 0.f;
-    rs[tid] = (r && tid < L) ? r[tok0 + tid] : 1.0f;
+    const float rv = r ? r[tok0 + min(tid, L - 1)] : 1.0f;
+    rs[tid] = (r && tid < L) ? ((xf & kGateLogits) ? sigmoid_gate(rv) : rv) : 1.0f;
+  }
+  // per-token normalisation scales (16 threads per token hold its pieces)
+  float kscale[4] = {1.f, 1.f, 1.f, 1.f}, qscale[4] = {1.f, 1.f, 1.f, 1.f};
+  if (NORM) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const unsigned short *sk8 = (const unsigned short *)&rk[u];
+      const unsigned short *sq8 = (const unsigned short *)&rq[u];
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = bf2f(sk8[e]), y = bf2f(sq8[e]);
+        a = fmaf(x, x, a);
+        b = fmaf(y, y, b);
+      }
+      kscale[u] = unit_scale(group_sum<16>(a));
+      qscale[u] = unit_scale(group_sum<16>(b));
+      if ((tid & 15) == 0) {
+        const int t = (tid + 256 * u) >> 4;
+        if (MODE == kOsdn) sk[t] = kscale[u];
+        *(float *)(rec + OFF_SC + 4 * t) = kscale[u];
+        *(float *)(rec + OFF_SC + 4 * (C + t)) = qscale[u];
+      }
+    }
   }
 
   // write-key scale: a power of two >= max |kt| (given keys), 1 for kt = k
@@ -137,8 +174,8 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
-    *(f16x8 *)&Ks[t * KP + i0] = cvt8(rk[u]);
-    *(f16x8 *)&Qs[t * KP + i0] = cvt8(rq[u]);
+    *(f16x8 *)&Ks[t * KP + i0] = (NORM && MODE == kDeltaNet) ? cvt8s(rk[u], kscale[u]) : cvt8(rk[u]);
+    *(f16x8 *)&Qs[t * KP + i0] = NORM ? cvt8s(rq[u], qscale[u]) : cvt8(rq[u]);
     if (MODE == kGiven) {
       const unsigned short *s = (const unsigned short *)&rt[u];
       f16x8 hv;
@@ -156,11 +193,18 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       for (int t0 = 0; t0 < C; t0 += 4) {
         const float4 c4 = *(const float4 *)&cs[t0], r4 = *(const float4 *)&rs[t0];
         const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+        float sv[4] = {1.f, 1.f, 1.f, 1.f};
+        if (NORM) {
+          const float4 s4 = *(const float4 *)&sk[t0];
+          sv[0] = s4.x, sv[1] = s4.y, sv[2] = s4.z, sv[3] = s4.w;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          // the normalised key is kv * sv
           const float kv = (float)Ks[(t0 + e) * KP + tid];
-          emit(t0 + e, d * kv);
-          d = fmaf(cv[e], kv * kv, rv[e] * d);
+          const float kh = NORM ? kv * sv[e] : kv;
+          emit(t0 + e, d * kh);
+          d = fmaf(cv[e], kh * kh, rv[e] * d);
         }
       }
     };
@@ -191,6 +235,11 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     return acc;
   };
   auto beta4 = [&](int rt_) { return *(const f32x4 *)&bs[16 * rt_ + 4 * g]; };
+  // kOsdn, NORM stages k as stored: the rows of A take the keys' 1/||k||
+  auto krow4 = [&](int rt_) {
+    return (NORM && MODE == kOsdn) ? *(const f32x4 *)&sk[16 * rt_ + 4 * g]
+                                   : f32x4{1.f, 1.f, 1.f, 1.f};
+  };
 
   // ---- scores P = lower(Q Kt^T) ds, emitted as A operands (transposed tiles)
   for (int idx = wave; idx < 10; idx += 4) {
@@ -208,20 +257,21 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // ---- A: diagonal block `wave` (then its inverse) and off-diagonal blocks
   {
     const f32x4 acc = gram(Ks, wave, wave);
-    const f32x4 b4 = beta4(wave);
+    const f32x4 b4 = beta4(wave), f4 = krow4(wave);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 4 * g + e;
-      Fd[wave][row][c16] = c16 < row ? b4[e] * ds * acc[e] : 0.f;
+      Fd[wave][row][c16] = c16 < row ? (NORM ? b4[e] * ds * acc[e] * f4[e] : b4[e] * ds * acc[e]) : 0.f;
     }
   }
   for (int job = wave; job < 6; job += 4) {
     int rt_, ct;
     off_tile(job, rt_, ct);
     const f32x4 acc = gram(Ks, rt_, ct);
-    const f32x4 b4 = beta4(rt_);
+    const f32x4 b4 = beta4(rt_), f4 = krow4(rt_);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Aoff[job][4 * g + e][c16] = h(b4[e] * ds * acc[e]);
+    for (int e = 0; e < 4; ++e)
+      Aoff[job][4 * g + e][c16] = h(NORM ? b4[e] * ds * acc[e] * f4[e] : b4[e] * ds * acc[e]);
   }
   wave_lds_sync();
   {
@@ -267,6 +317,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         sq = fmaf(x, x, sq);
       }
       sq = group_sum<16>(sq);
+      if (NORM) sq *= kscale[u] * kscale[u];  // of the normalised key
       const float gd = 1.0f - bs[t] * sq;
       if ((p & 15) == 0 && t < L) lr += logf(gd * gd);
     }
@@ -327,6 +378,8 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // stored, so a burst of loads from every CU has two iterations to arrive.
 // Each role runs its own loop with the same barrier count (NC + 1), so the
 // registers of different roles are never live at the same time.
+// NORM: q and k are staged as stored; the record's per-token 1/||k_t|| and
+// 1/||q_t|| scale the rows of K S^T and Q S^T in fp32.
 // ---------------------------------------------------------------------------
 constexpr int ST = 768;        // threads
 constexpr int NL = ST - 256;   // loader lanes
@@ -336,18 +389,19 @@ struct StateSmem {
   f16 K[2][C * KP];
   f16 Q[2][C * KP];
   f16 V[2][C * VP];
-  unsigned char rec[2][OFF_DS + 16];  // KtF, TmA, PA, ds of the chunk
+  unsigned char rec[2][OFF_SC + 2 * C * 4];  // KtF, TmA, PA, ds, scales of the chunk
   float b[2][C];
   f16x8 Sx[2][2][4][64];  // fp16 S^T at a chunk's start [parity][sn][kk][lane], paired order
   f16x8 Xx[2][2][2][64];  // X of a chunk [parity][sn][qq][lane], paired order
 };
 static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
 
+template <bool NORM>
 __global__ void __launch_bounds__(ST)
 chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
             const float *__restrict__ beta, const float *__restrict__ S0, int BH, int T_, int NC,
             const unsigned char *__restrict__ ws, bf16 *__restrict__ o,
-            float *__restrict__ S_final, float *__restrict__ log_ratio_sum) {
+            float *__restrict__ S_final, float *__restrict__ log_ratio_sum, unsigned xf) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   StateSmem &sm = *reinterpret_cast<StateSmem *>(smem_raw);
   const int tid = threadIdx.x;
@@ -378,11 +432,11 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
   if (wave >= 4) {
     // ================================ loaders ================================
     // k and q as 2048 pieces of 8 elements, the value tile as 256, the record as
-    // OFF_DS/16 + 1 = 1793 pieces of 16 bytes, beta.  Loads are unconditional (a
-    // masked lane reads a valid address) and masked values are zeroed when
-    // stored: a conditional load makes the compiler wait for it at the end of
-    // its branch.
-    constexpr int RECP = OFF_DS / 16 + 1;
+    // OFF_DS/16 + 1 = 1793 pieces of 16 bytes (1825 with the scales), beta.
+    // Loads are unconditional (a masked lane reads a valid address) and masked
+    // values are zeroed when stored: a conditional load makes the compiler wait
+    // for it at the end of its branch.
+    constexpr int RECP = NORM ? (int)(OFF_SC / 16) + 2 * C * 4 / 16 : (int)(OFF_DS / 16) + 1;
     constexpr int NKQ = (2048 + NL - 1) / NL, NR = (RECP + NL - 1) / NL;
     const int lt = tid - 256;
     struct Regs {
@@ -427,7 +481,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         const int p = lt + NL * u;
         if (p < RECP) rd[p] = R.r[u];
       }
-      if (lt < C) sm.b[buf][lt] = lt < R.L ? R.b : 0.f;
+      if (lt < C)
+        sm.b[buf][lt] = lt < R.L ? ((xf & kGateLogits) ? sigmoid_gate(R.b) : R.b) : 0.f;
     };
     if (NC > 0) {
       load(ra, 0);
@@ -486,6 +541,11 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         f32x4 a = zero4();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) a = mma32(ldpk(kr, 32 * kk, g), Sb[kk], a);
+        if (NORM) {
+          const f32x4 s4 = *(const f32x4 *)(sm.rec[cb] + OFF_SC + 4 * (16 * m + 4 * g));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] *= s4[e];
+        }
         const f16x4 vv =
             h4(mma16(ld4(&sm.V[cb][(16 * m + c16) * VP + 16 * sn + 4 * g]), ident, zero4()));
         const f32x4 b4 = *(const f32x4 *)&sm.b[cb][16 * m + 4 * g];
@@ -576,6 +636,11 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
           f32x4 a = zero4();
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) a = mma32(ldpk(qr, 32 * kk, g), Sb[kk], a);
+          if (NORM) {
+            const f32x4 s4 = *(const f32x4 *)(sm.rec[cb] + OFF_SC + 4 * (C + 16 * m + 4 * g));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] *= s4[e];
+          }
           O[m] = a;
         }
         const f16x8 *PA = (const f16x8 *)(sm.rec[cb] + OFF_P);
@@ -600,12 +665,20 @@ hipError_t launch_state(const ChunkArgs &a, int NC, const void *ws, float *log_r
                         hipStream_t s) {
   const int BH = a.B * a.H;
   const size_t shm = sizeof(StateSmem);
-  hipError_t e = hipFuncSetAttribute((const void *)chunk_state,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  const bool norm = (a.xf & kNormQK) != 0;
+  const void *fn = norm ? (const void *)chunk_state<true> : (const void *)chunk_state<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk_state, dim3((unsigned)(BH * 4)), dim3(ST), shm, s, (const bf16 *)a.q,
-                     (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.S0, BH, a.T, NC,
-                     (const unsigned char *)ws, (bf16 *)a.o, a.S_final, log_ratio_sum);
+  if (norm)
+    hipLaunchKernelGGL(chunk_state<true>, dim3((unsigned)(BH * 4)), dim3(ST), shm, s,
+                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.S0, BH,
+                       a.T, NC, (const unsigned char *)ws, (bf16 *)a.o, a.S_final, log_ratio_sum,
+                       a.xf);
+  else
+    hipLaunchKernelGGL(chunk_state<false>, dim3((unsigned)(BH * 4)), dim3(ST), shm, s,
+                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.S0, BH,
+                       a.T, NC, (const unsigned char *)ws, (bf16 *)a.o, a.S_final, log_ratio_sum,
+                       a.xf);
   return hipGetLastError();
 }
 
@@ -629,25 +702,37 @@ hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   float *wout = (float *)(rec + (size_t)BH * NC * REC);
   static_assert(WREC <= REC, "walk records fit in the chunk records' space");
   ChunkArgs ca{a.q, a.k, nullptr, a.v, a.beta, nullptr, a.S0, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
-               a.dtype, a.o, a.S_final};
+               a.dtype, a.o, a.S_final, a.xf};
   if (a.precond_off) {  // the plain delta rule: kt = k
     if (NC > 0) {
-      hipLaunchKernelGGL(chunk_prep<kDeltaNet>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
-                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
-                         a.T, NC, 0, NC, rec, (const float *)nullptr, (const float *)nullptr);
+      if (a.xf & kNormQK)
+        hipLaunchKernelGGL((chunk_prep<kDeltaNet, true>), dim3((unsigned)(BH * NC)), dim3(256), 0,
+                           s, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
+                           a.T, NC, 0, NC, rec, (const float *)nullptr, (const float *)nullptr,
+                           a.xf);
+      else
+        hipLaunchKernelGGL((chunk_prep<kDeltaNet, false>), dim3((unsigned)(BH * NC)), dim3(256), 0,
+                           s, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
+                           a.T, NC, 0, NC, rec, (const float *)nullptr, (const float *)nullptr,
+                           a.xf);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
     return launch_state(ca, NC, ws, a.log_ratio_sum, s);
   }
   ScanArgs sa{a.k, a.beta, a.r, a.d0, a.eta, a.B, a.H, a.T, a.dk, a.dtype, 0, nullptr,
-              a.d_final, nullptr, nullptr, a.log_ratio_sum};
+              a.d_final, nullptr, nullptr, a.log_ratio_sum, a.xf};
   hipError_t e = launch_walk(sa, rec, wout, s);
   if (e != hipSuccess) return e;
   if (NC > 0) {
-    hipLaunchKernelGGL(chunk_prep<kOsdn>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
-                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta, a.T,
-                       NC, 0, NC, rec, a.r, (const float *)wout);
+    if (a.xf & kNormQK)
+      hipLaunchKernelGGL((chunk_prep<kOsdn, true>), dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta, a.T,
+                         NC, 0, NC, rec, a.r, (const float *)wout, a.xf);
+    else
+      hipLaunchKernelGGL((chunk_prep<kOsdn, false>), dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta, a.T,
+                         NC, 0, NC, rec, a.r, (const float *)wout, a.xf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -660,15 +745,15 @@ hipError_t launch_split_chunk(const ChunkArgs &a, bool given, void *ws, hipStrea
   const int NC = (a.T + C - 1) / C;
   if (NC > 0) {
     if (given)
-      hipLaunchKernelGGL(chunk_prep<kGiven>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+      hipLaunchKernelGGL((chunk_prep<kGiven, false>), dim3((unsigned)(BH * NC)), dim3(256), 0, s,
                          (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.k_tilde, a.beta,
                          a.T, NC, 0, NC, (unsigned char *)ws, (const float *)nullptr,
-                         (const float *)nullptr);
+                         (const float *)nullptr, 0u);
     else
-      hipLaunchKernelGGL(chunk_prep<kDeltaNet>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+      hipLaunchKernelGGL((chunk_prep<kDeltaNet, false>), dim3((unsigned)(BH * NC)), dim3(256), 0, s,
                          (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
                          a.T, NC, 0, NC, (unsigned char *)ws, (const float *)nullptr,
-                         (const float *)nullptr);
+                         (const float *)nullptr, 0u);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -43,6 +43,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Input transforms of the raw-input flags (include/osdn.h): the scale that
+// normalises a vector of squared norm n (a zero vector stays zero), and the
+// logistic sigmoid of a gate logit.
+__device__ __forceinline__ float unit_scale(float n) { return n > 0.f ? 1.0f / sqrtf(n) : 0.f; }
+__device__ __forceinline__ float sigmoid_gate(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+
 // Sum over aligned groups of G lanes (G = 2..64, power of two) with xor
 // shuffles; every lane of the group receives the group's total.
 template <int G>

@@ -7,6 +7,11 @@
 
 namespace osdn {
 
+// Bits of the input-transform flags the kernels take (the ABI's values):
+// q, k arrive unnormalised; beta, r arrive as logits; and (internal) the given
+// write keys are the unnormalised keys themselves.
+constexpr unsigned kNormQK = 2u, kGateLogits = 4u, kNormKt = 8u;
+
 struct ScanArgs {
   const void *k;
   const float *beta, *r, *d0;
@@ -15,6 +20,7 @@ struct ScanArgs {
   int mode_off;          // 1: plain delta rule (only the residual-ratio sums are produced)
   void *k_tilde;         // [B,H,T,dk] dtype (unused when mode_off)
   float *d_final, *d_all, *log_ratio, *log_ratio_sum;  // optional
+  unsigned xf;           // input transforms (kNormQK: k unnormalised; kGateLogits: beta, r logits)
 };
 
 struct ChunkArgs {
@@ -23,6 +29,7 @@ struct ChunkArgs {
   int B, H, T, dk, dv, chunk, dtype;
   void *o;
   float *S_final;
+  unsigned xf;  // input transforms of q, k and beta (kNormQK, kGateLogits)
 };
 
 struct FusedArgs {
@@ -33,6 +40,7 @@ struct FusedArgs {
   int precond_off;
   void *o;
   float *S_final, *d_final, *log_ratio_sum;
+  unsigned xf;  // input transforms (kNormQK, kGateLogits)
 };
 
 struct StepArgs {
@@ -43,6 +51,7 @@ struct StepArgs {
   float *S, *d;   // updated in place
   void *o;
   float *log_ratio;  // optional
+  unsigned xf;       // input transforms (kNormQK, kGateLogits)
 };
 
 // One decoding step with persistent (S, d), one workgroup per (b,h).

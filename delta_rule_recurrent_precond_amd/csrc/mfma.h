@@ -50,6 +50,25 @@ __device__ __forceinline__ f16x8 ld8(const f16 *p) { return *(const f16x8 *)p; }
 __device__ __forceinline__ f16x8 ldpk(const f16 *row, int kb, int g) {
   return cat(ld4(row + kb + 4 * g), ld4(row + kb + 16 + 4 * g));
 }
+// Sum of squares of 8 bf16 (16 bytes), fp32.
+__device__ __forceinline__ float sqsum8(const uint4 &u) {
+  const unsigned short *s = (const unsigned short *)&u;
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = bf2f(s[e]);
+    a = fmaf(x, x, a);
+  }
+  return a;
+}
+// 8 bf16 times a scale (fp32), rounded once to fp16.
+__device__ __forceinline__ f16x8 cvt8s(const uint4 &u, float sc) {
+  const unsigned short *s = (const unsigned short *)&u;
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = h(bf2f(s[e]) * sc);
+  return r;
+}
 // 8 bf16 (16 bytes) as fp16 (exact for |x| in fp16's normal range)
 __device__ __forceinline__ f16x8 cvt8(const uint4 &u) {
   const unsigned short *s = (const unsigned short *)&u;

@@ -49,6 +49,13 @@ size_t ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype, unsig
   return two_phase_bytes(B, H, T, dk, dtype, flags);
 }
 
+constexpr unsigned kFlags = OSDN_PRECOND_OFF | OSDN_NORM_QK | OSDN_GATE_LOGITS;
+// the kernels' transform bits from the ABI flags
+unsigned transforms(unsigned flags) {
+  return (flags & OSDN_NORM_QK ? osdn::kNormQK : 0u) |
+         (flags & OSDN_GATE_LOGITS ? osdn::kGateLogits : 0u);
+}
+
 bool split_ok(int B, int H, int T, int dk, int dv, int chunk, int dtype, const float *alpha,
               size_t workspace_bytes, const void *workspace) {
   return use_fused(dk, dv, chunk, dtype) && !alpha && workspace &&
@@ -94,13 +101,16 @@ OSDN_EXPORT int osdn_precond_scan(const void *k, const float *beta, const float 
 }
 
 OSDN_EXPORT int osdn_step(const void *q, const void *k, const void *v, const float *beta,
-                          const float *r, const float *alpha, float eta, int B, int H, int dk, int dv, int dtype,
-                          float *S, float *d, void *o, float *log_ratio, void *stream) {
+                          const float *r, const float *alpha, float eta, int B, int H, int dk,
+                          int dv, int dtype, unsigned flags, float *S, float *d, void *o,
+                          float *log_ratio, void *stream) {
   int st = check_sizes(B, H, 1, dk, dv, 16, dtype, true, false);
   if (st != OSDN_OK) return st;
+  if (flags & ~(OSDN_NORM_QK | OSDN_GATE_LOGITS)) return OSDN_ERR_UNSUPPORTED;
   if ((long long)B * H == 0) return OSDN_OK;
   if (!q || !k || !v || !beta || !S || !d || !o) return OSDN_ERR_NULL;
-  osdn::StepArgs a{q, k, v, beta, r, alpha, eta, B, H, dk, dv, dtype, S, d, o, log_ratio};
+  osdn::StepArgs a{q, k, v, beta, r, alpha, eta, B, H, dk, dv, dtype, S, d, o, log_ratio,
+                   transforms(flags)};
   return hip_status(osdn::launch_step(a, (hipStream_t)stream));
 }
 
@@ -133,7 +143,7 @@ OSDN_EXPORT int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde
 OSDN_EXPORT size_t osdn_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
                                                 int dtype, unsigned flags) {
   if (check_sizes(B, H, T, dk, dv, chunk, dtype, true, true) != OSDN_OK) return (size_t)-1;
-  if (flags & ~OSDN_PRECOND_OFF) return (size_t)-1;
+  if (flags & ~kFlags) return (size_t)-1;
   return ws_bytes(B, H, T, dk, dv, chunk, dtype, flags);
 }
 
@@ -141,12 +151,13 @@ OSDN_EXPORT const char *osdn_forward_path(int B, int H, int T, int dk, int dv, i
                                           int dtype, unsigned flags, int gated,
                                           size_t workspace_bytes) {
   if (check_sizes(B, H, T, dk, dv, chunk, dtype, true, true) != OSDN_OK) return "invalid";
-  if (flags & ~OSDN_PRECOND_OFF) return "invalid";
+  if (flags & ~kFlags) return "invalid";
   if ((long long)B * H == 0) return "none";
   const float one = 1.0f;
   if (split_ok(B, H, T, dk, dv, chunk, dtype, gated ? &one : nullptr, workspace_bytes, &one))
     return "split";
-  return use_fused(dk, dv, chunk, dtype) ? "fused" : "two-phase";
+  if (!use_fused(dk, dv, chunk, dtype)) return "two-phase";
+  return transforms(flags) ? "unsupported" : "fused";
 }
 
 OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
@@ -156,7 +167,12 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
                              void *workspace, size_t workspace_bytes, void *stream) {
   int st = check_sizes(B, H, T, dk, dv, chunk, dtype, true, true);
   if (st != OSDN_OK) return st;
-  if (flags & ~OSDN_PRECOND_OFF) return OSDN_ERR_UNSUPPORTED;
+  if (flags & ~kFlags) return OSDN_ERR_UNSUPPORTED;
+  const unsigned xf = transforms(flags);
+  // the single fused kernel takes its inputs prepared
+  if (xf && use_fused(dk, dv, chunk, dtype) &&
+      !split_ok(B, H, T, dk, dv, chunk, dtype, alpha, workspace_bytes, workspace))
+    return OSDN_ERR_UNSUPPORTED;
   if ((long long)B * H == 0) return OSDN_OK;
   if (T > 0 && (!q || !k || !v || !beta || !o)) return OSDN_ERR_NULL;
   const bool off = (flags & OSDN_PRECOND_OFF) != 0;
@@ -164,7 +180,7 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
 
   if (use_fused(dk, dv, chunk, dtype)) {
     osdn::FusedArgs a{q, k, v, beta, r, alpha, d0, S0, eta, B, H, T, dk, dv, chunk, dtype,
-                      off ? 1 : 0, o, S_final, d_final, log_ratio_sum};
+                      off ? 1 : 0, o, S_final, d_final, log_ratio_sum, xf};
     if (split_ok(B, H, T, dk, dv, chunk, dtype, alpha, workspace_bytes, workspace))
       return hip_status(osdn::launch_split_forward(a, workspace, s));
     return hip_status(osdn::launch_fused_forward(a, s));
@@ -177,17 +193,20 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   const void *kt = k;
   if (!off) {
     osdn::ScanArgs sa{k, beta, r, d0, eta, B, H, T, dk, dtype, 0, workspace,
-                      d_final, nullptr, nullptr, log_ratio_sum};
-    st = hip_status(osdn::fused_scan_supported(dk, dtype) ? osdn::launch_fused_scan(sa, s)
-                                                          : osdn::launch_precond_scan_serial(sa, s));
+                      d_final, nullptr, nullptr, log_ratio_sum, xf};
+    st = hip_status(osdn::fused_scan_supported(dk, dtype) && !xf
+                        ? osdn::launch_fused_scan(sa, s)
+                        : osdn::launch_precond_scan_serial(sa, s));
     if (st != OSDN_OK) return st;
     kt = workspace;
   } else if (log_ratio_sum) {
     osdn::ScanArgs sa{k, beta, nullptr, nullptr, 0.0f, B, H, T, dk, dtype, 1, nullptr,
-                      nullptr, nullptr, nullptr, log_ratio_sum};
+                      nullptr, nullptr, nullptr, log_ratio_sum, xf};
     st = hip_status(osdn::launch_precond_scan_serial(sa, s));
     if (st != OSDN_OK) return st;
   }
-  osdn::ChunkArgs ca{q, k, kt, v, beta, alpha, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
+  // with kt = k (the delta rule) unnormalised keys are normalised on both sides
+  osdn::ChunkArgs ca{q, k, kt, v, beta, alpha, S0, B, H, T, dk, dv, chunk, dtype, o, S_final,
+                     xf | (off && (xf & osdn::kNormQK) ? osdn::kNormKt : 0u)};
   return hip_status(osdn::launch_chunk_generic(ca, s));  // only shapes the fused kernel lacks
 }

@@ -8,7 +8,9 @@
 // One wave per (b,h).  Lane l holds EPL = max(1, dk/64) consecutive elements
 // of k_t and d; the two inner products per token (||k||^2 and <d, k (.) k>)
 // are wave reductions.  The chain that is serial over tokens is
-// d -> a -> c -> d; key loads run a block ahead of it.
+// d -> a -> c -> d; key loads run a block ahead of it.  xf: kNormQK -- the
+// keys arrive unnormalised and each is divided by its norm (one more wave
+// reduction per token); kGateLogits -- beta and r arrive as logits.
 #include "device.h"
 #include "launch.h"
 
@@ -24,7 +26,7 @@ precond_scan_serial(const T *__restrict__ k, const float *__restrict__ beta,
                     const float *__restrict__ r, const float *__restrict__ d0, float eta, int T_,
                     int mode_off, T *__restrict__ k_tilde, float *__restrict__ d_final,
                     float *__restrict__ d_all, float *__restrict__ log_ratio,
-                    float *__restrict__ log_ratio_sum) {
+                    float *__restrict__ log_ratio_sum, unsigned xf) {
   constexpr int EPL = DK >= 64 ? DK / 64 : 1;
   const int lane = threadIdx.x;
   const long bh = blockIdx.x;
@@ -52,8 +54,9 @@ precond_scan_serial(const T *__restrict__ k, const float *__restrict__ beta,
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
         kb[j][e] = (ok && active) ? Elem<T>::load(kh + (long)t * DK + e0 + e) : 0.0f;
-      bb[j] = ok ? bh_beta[t] : 0.0f;
-      rb[j] = (ok && bh_r) ? bh_r[t] : 1.0f;
+      const float bv = ok ? bh_beta[t] : 0.0f, rv = (ok && bh_r) ? bh_r[t] : 1.0f;
+      bb[j] = (ok && (xf & kGateLogits)) ? sigmoid_gate(bv) : bv;
+      rb[j] = (ok && bh_r && (xf & kGateLogits)) ? sigmoid_gate(rv) : rv;
     }
   };
   auto run_block = [&](const float (&kb)[kBlock][EPL], const float (&bb)[kBlock],
@@ -62,10 +65,20 @@ precond_scan_serial(const T *__restrict__ k, const float *__restrict__ beta,
     for (int j = 0; j < kBlock; ++j) {
       const int t = t0 + j;
       if (t >= T_) break;
-      float p[EPL], pn = 0.0f, pa = 0.0f;
+      float kk[EPL], p[EPL], pn = 0.0f, pa = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kk[e] = kb[j][e];
+      if (xf & kNormQK) {
+        float sq = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sq = fmaf(kk[e], kk[e], sq);
+        const float sc = unit_scale(wave_sum(sq));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) kk[e] *= sc;
+      }
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        p[e] = kb[j][e] * kb[j][e];
+        p[e] = kk[e] * kk[e];
         pn += p[e];
         pa += d[e] * p[e];
       }
@@ -77,7 +90,7 @@ precond_scan_serial(const T *__restrict__ k, const float *__restrict__ beta,
       if (!mode_off && active) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          Elem<T>::store(k_tilde + row * DK + e0 + e, d[e] * kb[j][e]);
+          Elem<T>::store(k_tilde + row * DK + e0 + e, d[e] * kk[e]);
           if (d_all) d_all[row * DK + e0 + e] = d[e];
         }
       }
@@ -115,7 +128,7 @@ hipError_t launch_serial_t(const ScanArgs &a, hipStream_t s) {
   case DK_:                                                                                     \
     hipLaunchKernelGGL((precond_scan_serial<T, DK_>), grid, block, 0, s, (const T *)a.k,      \
                        a.beta, a.r, a.d0, a.eta, a.T, a.mode_off, (T *)a.k_tilde, a.d_final,  \
-                       a.d_all, a.log_ratio, a.log_ratio_sum);                                 \
+                       a.d_all, a.log_ratio, a.log_ratio_sum, a.xf);                           \
     break;
   switch (a.dk) {
     OSDN_SCAN_CASE(16)

@@ -29,26 +29,45 @@ osdn_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
                  const float *__restrict__ beta, const float *__restrict__ r,
                  const float *__restrict__ alpha, float eta, int dv,
                  float *__restrict__ S, float *__restrict__ d, T *__restrict__ o,
-                 float *__restrict__ log_ratio) {
+                 float *__restrict__ log_ratio, unsigned xf) {
   constexpr int TPR = DK / 4;         // threads per row of S (4 columns each)
   constexpr int RPP = NT / TPR;       // rows per pass
   __shared__ float kt_s[DK], k_s[DK], q_s[DK];
-  __shared__ float red[NT / 64][2];
+  __shared__ float red[NT / 64][2], redn[NT / 64][2];
   __shared__ float coef[2];           // beta, c
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long bh = blockIdx.x;
-  const float bt = beta[bh];
+  const float bt = (xf & kGateLogits) ? sigmoid_gate(beta[bh]) : beta[bh];
   const float at = alpha ? alpha[bh] : 1.0f;  // state gate
 
   // key statistics and the write key (fp32), one thread per dimension
-  float pn = 0.f, pa = 0.f;
+  float pn = 0.f, pa = 0.f, kv = 0.f, qv = 0.f, dv_ = 0.f;
   if (tid < DK) {
-    const float kv = Elem<T>::load(k + bh * DK + tid);
-    const float dv_ = d[bh * DK + tid];
+    kv = Elem<T>::load(k + bh * DK + tid);
+    qv = Elem<T>::load(q + bh * DK + tid);
+    dv_ = d[bh * DK + tid];
+  }
+  if (xf & kNormQK) {  // q and k arrive unnormalised: divide by their norms
+    const float nk = wave_sum(kv * kv), nq = wave_sum(qv * qv);
+    if (lane == 0) {
+      redn[wave][0] = nk;
+      redn[wave][1] = nq;
+    }
+    __syncthreads();
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      sk += redn[w][0];
+      sq += redn[w][1];
+    }
+    kv *= unit_scale(sk);
+    qv *= unit_scale(sq);
+  }
+  if (tid < DK) {
     k_s[tid] = kv;
     kt_s[tid] = dv_ * kv;
-    q_s[tid] = Elem<T>::load(q + bh * DK + tid);
+    q_s[tid] = qv;
     pn = kv * kv;
     pa = dv_ * (kv * kv);
   }
@@ -97,7 +116,7 @@ osdn_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
 
   // d <- r d + c (k (.) k)
   if (tid < DK) {
-    const float rt = r ? r[bh] : 1.0f;
+    const float rt = r ? ((xf & kGateLogits) ? sigmoid_gate(r[bh]) : r[bh]) : 1.0f;
     const float kv = k_s[tid];
     d[bh * DK + tid] = fmaf(coef[1], kv * kv, rt * d[bh * DK + tid]);
   }
@@ -111,7 +130,7 @@ hipError_t launch_t(const StepArgs &a, hipStream_t s) {
 #define OSDN_STEP(DKV)                                                                     \
   case DKV:                                                                                \
     hipLaunchKernelGGL((osdn_step_kernel<T, DKV>), dim3(BH), dim3(NT), 0, s, q, k, v,       \
-                       a.beta, a.r, a.alpha, a.eta, a.dv, a.S, a.d, o, a.log_ratio);                  \
+                       a.beta, a.r, a.alpha, a.eta, a.dv, a.S, a.d, o, a.log_ratio, a.xf);                  \
     break;
   switch (a.dk) {
     OSDN_STEP(16)

@@ -41,12 +41,13 @@ constexpr int FP = 68;   // padded row (floats) of [64][64] fp32 tiles in LDS
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const float *__restrict__ r,
-          float eta, int T_, int NC, int c0, int ncs, unsigned char *__restrict__ wrec) {
+          float eta, int T_, int NC, int c0, int ncs, unsigned xf, unsigned char *__restrict__ wrec) {
   // The fp16 keys are needed only for the key gram; (I + M)^-1 reuses their space.
   __shared__ __align__(16) float F[C * FP];           // key gram G, then M (strictly lower)
   __shared__ __align__(16) unsigned char KM[C * KP * 2];  // fp16 keys, then (I + M)^-1 [64][FP]
   __shared__ float Yw[3][16][17];                     // per-wave staging of a block sum
   __shared__ float bs[C], al[C], nn[C], lg[C + 4];
+  __shared__ float ss[C];  // 1 / ||k_t||^2 for unnormalised keys, else 1
   static_assert(C * KP * 2 >= C * FP * 4, "the inverse fits in the keys' space");
   f16 *Kh = (f16 *)KM;
   float *Mi = (float *)KM;
@@ -67,10 +68,16 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
     rk[u] = *(const uint4 *)(k + (tok0 + t) * DK + (p & 15) * 8);
   }
   const int tb = min(lane, L - 1);
-  const float pb = beta[tok0 + tb];
-  const float pr = r ? r[tok0 + tb] : 1.0f;
+  float pb = beta[tok0 + tb];
+  float pr = r ? r[tok0 + tb] : 1.0f;
+  if (xf & kGateLogits) {
+    pb = sigmoid_gate(pb);
+    pr = sigmoid_gate(pr);
+  }
 
-  // stage the keys; n_t from the stored bf16 values (16 threads per token)
+  // stage the stored keys (exact in fp16); n_t from the stored bf16 values (16
+  // threads per token).  Unnormalised keys enter through the fp32 factor
+  // 1 / n_t on p_t (the normalised key's p is p_t / n_t), never through fp16.
   const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -85,7 +92,11 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
       sq = fmaf(x, x, sq);
     }
     sq = group_sum<16>(ok ? sq : 0.f);
-    if ((p & 15) == 0) nn[t] = sq;
+    if ((p & 15) == 0) {
+      const float sc = (xf & kNormQK) ? (sq > 0.f ? 1.0f / sq : 0.f) : 1.0f;
+      ss[t] = sc;
+      nn[t] = sq * sc;  // ||k_t||^2 of the key the recurrence sees
+    }
   }
   if (wave == 0) {
     bs[lane] = lane < L ? pb : 0.f;
@@ -122,7 +133,7 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   // and above the diagonal; the blocks of (I + M)^-1 above the diagonal are zero
   {
     const int t = tid >> 2, q = tid & 3;
-    const float bl = bs[t], lt = lg[t];
+    const float bl = bs[t], lt = lg[t], ssl = ss[t];
     float row[16];
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
@@ -132,7 +143,7 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int s = 16 * q + j;
-      row[j] = s < t ? bl * al[s] * fexp2(lt - lg[s + 1]) * row[j] : 0.f;
+      row[j] = s < t ? bl * al[s] * fexp2(lt - lg[s + 1]) * (ssl * ss[s]) * row[j] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
@@ -193,6 +204,7 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
     ((float *)(rec + W_U))[t] = bs[t] * fexp2(lg[t]);
     ((float *)(rec + W_A))[t] = al[t];
     ((float *)(rec + W_WA))[t] = t < L ? fexp2(lg[C] - lg[t + 1]) * al[t] : 0.f;
+    ((float *)(rec + W_S))[t] = ss[t];
   }
   if (tid == 0) *(float *)(rec + W_GL) = fexp2(lg[C]);
 }
@@ -211,7 +223,7 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 struct alignas(16) WalkSmem {
   bf16 K[2][C * KP];         // keys
   float Mi[2][C * FP];       // (I + M)^-1
-  float vec[2][3][C];        // u = beta Gamma, alpha, R_{L,t} alpha
+  float vec[2][4][C];        // u = beta Gamma, alpha, R_{L,t} alpha, the 1/||k||^2 factor
   float gL[2][4];            // Gamma_L
   float d[DK];               // entry d of the chunk in the pass
   float rhs[C], w[C], g[C];
@@ -232,7 +244,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
   const int lt = tid - DK;                 // loader index (threads 128-255)
 
   // loads of one chunk by threads 128-255: 1024 pieces of 8 keys, 8 each; the
-  // record as 1073 pieces of 16 bytes (1024 of the inverse, 48 of vectors,
+  // record as 1089 pieces of 16 bytes (1024 of the inverse, 64 of vectors,
   // Gamma_L), 9 each
   constexpr int RP = (W_GL + 16) / 16;
   constexpr int NRP = (RP + 127) / 128;
@@ -316,7 +328,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
         }
       }
       const float b = group_sum<4>(b0 + b1);
-      if (part == 0) sm.rhs[t] = 1.0f - sm.vec[cb][0][t] * b;
+      if (part == 0) sm.rhs[t] = 1.0f - sm.vec[cb][0][t] * (sm.vec[cb][3][t] * b);
     }
     __syncthreads();
     // B
@@ -334,7 +346,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
       }
       const float gt = group_sum<4>(ga + gb);
       if (part == 0) {
-        sm.w[t] = sm.vec[cb][2][t] * gt;
+        sm.w[t] = sm.vec[cb][2][t] * gt * sm.vec[cb][3][t];
         sm.g[t] = gt;
         wout[((long)bh * NC + c) * WOUT + DK + t] = sm.vec[cb][1][t] * gt;
       }
@@ -462,7 +474,7 @@ hipError_t launch_walk_prep(const ScanArgs &a, int c0, int c1, unsigned char *wr
   const int NC = (a.T + C - 1) / C;
   if (BH == 0 || c1 <= c0) return hipSuccess;
   hipLaunchKernelGGL(walk_prep, dim3((unsigned)(BH * (c1 - c0))), dim3(256), 0, s,
-                     (const bf16 *)a.k, a.beta, a.r, a.eta, a.T, NC, c0, c1 - c0, wrec);
+                     (const bf16 *)a.k, a.beta, a.r, a.eta, a.T, NC, c0, c1 - c0, a.xf, wrec);
   return hipGetLastError();
 }
 

@@ -74,6 +74,19 @@ extern "C" {
  * eta are ignored, d_final is not written, rho_t = (1 - beta_t ||k_t||^2)^2. */
 #define OSDN_PRECOND_OFF 1u
 
+/* Input transforms done inside the kernels as the inputs are staged, so no
+ * separate elementwise pass over them is needed (osdn_forward, osdn_step):
+ *   OSDN_NORM_QK      q and k arrive unnormalised; every q_t and k_t is divided
+ *                     by its L2 norm (fp32; a zero vector stays zero)
+ *   OSDN_GATE_LOGITS  beta and r arrive as logits; the kernels use
+ *                     1 / (1 + exp(-x)).  alpha is not transformed.
+ * The measured workloads apply exactly these transforms to their draws.
+ * osdn_forward takes them on the multi-launch path (bf16, dk = dv = 128,
+ * chunk 64, enough workspace, no alpha) and on the two-phase path; where the
+ * single fused kernel would run it returns OSDN_ERR_UNSUPPORTED. */
+#define OSDN_NORM_QK 2u
+#define OSDN_GATE_LOGITS 4u
+
 /*
  * Phase 1: the preconditioner scan over the key stream [summary §2.2 phase 1,
  * §2.3 APF].
@@ -143,7 +156,7 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  * Both phases end to end [summary §2.2 two-phase implementation].
  *   q, k, v, beta, r, alpha, d0, S0, eta   as above; with OSDN_PRECOND_OFF and
  *                  alpha this is Gated DeltaNet itself
- *   flags          0 or OSDN_PRECOND_OFF
+ *   flags          OSDN_PRECOND_OFF, OSDN_NORM_QK, OSDN_GATE_LOGITS, or'd
  *   o              [B,H,T,dv] dtype out (required if T > 0)
  *   S_final        [B,H,dv,dk] fp32 out (optional)
  *   d_final        [B,H,dk] fp32 out (optional)
@@ -181,11 +194,12 @@ int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
  *   d         [B,H,dk] fp32      preconditioner, read and updated in place (required)
  *   o         [B,H,dv] dtype     out: the readout (required)
  *   log_ratio [B,H]    fp32      out: log rho (optional)
+ *   flags     0, OSDN_NORM_QK, OSDN_GATE_LOGITS, or'd (the transforms above)
  * S, d and o must not overlap each other or the inputs.
  */
 int osdn_step(const void *q, const void *k, const void *v, const float *beta, const float *r,
-              const float *alpha, float eta, int B, int H, int dk, int dv, int dtype, float *S, float *d, void *o,
-              float *log_ratio, void *stream);
+              const float *alpha, float eta, int B, int H, int dk, int dv, int dtype,
+              unsigned flags, float *S, float *d, void *o, float *log_ratio, void *stream);
 
 /* Scratch bytes that select osdn_forward's fastest path for these arguments
  * (required on the two-phase path, optional on the matrix-core shapes);
@@ -198,7 +212,8 @@ const char *osdn_status_str(int status);
 
 /* Name of the kernel family osdn_forward would launch for these arguments,
  * whether a state gate is passed (gated != 0) and the workspace size: "split"
- * (the multi-launch pipeline), "fused" (one kernel), "two-phase" or "none";
+ * (the multi-launch pipeline), "fused" (one kernel), "two-phase", "none", or
+ * "unsupported" (input transforms where only the fused kernel could run);
  * static host string, "invalid" on bad arguments.  Lets callers and tests
  * know which path they exercised. */
 const char *osdn_forward_path(int B, int H, int T, int dk, int dv, int chunk, int dtype,

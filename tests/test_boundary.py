@@ -68,7 +68,7 @@ def _fwd(lib, B=1, H=1, T=4, dk=16, dv=16, chunk=16, dtype=0, flags=0, ptr=1):
     (dict(chunk=128), _lib.OSDN_ERR_UNSUPPORTED),
     (dict(chunk=0), _lib.OSDN_ERR_UNSUPPORTED),
     (dict(dtype=7), _lib.OSDN_ERR_UNSUPPORTED),
-    (dict(flags=4), _lib.OSDN_ERR_UNSUPPORTED),
+    (dict(flags=8), _lib.OSDN_ERR_UNSUPPORTED),
     (dict(ptr=None), _lib.OSDN_ERR_NULL),
     (dict(B=1 << 30, H=1 << 10), _lib.OSDN_ERR_SHAPE),
 ])
@@ -109,13 +109,13 @@ def test_scan_and_chunk_reject(lib):
 
 def test_step_rejects(lib):
     p = 1
-    assert lib.osdn_step(None, None, None, None, None, None, 0.1, 0, 4, 16, 16, 0, None, None, None,
+    assert lib.osdn_step(None, None, None, None, None, None, 0.1, 0, 4, 16, 16, 0, 0, None, None, None,
                          None, None) == _lib.OSDN_OK
-    assert lib.osdn_step(p, p, p, p, None, None, 0.1, 1, 1, 16, 16, 0, None, p, p, None,
+    assert lib.osdn_step(p, p, p, p, None, None, 0.1, 1, 1, 16, 16, 0, 0, None, p, p, None,
                          None) == _lib.OSDN_ERR_NULL
-    assert lib.osdn_step(p, p, p, p, None, None, 0.1, 1, 1, 24, 16, 0, p, p, p, None,
+    assert lib.osdn_step(p, p, p, p, None, None, 0.1, 1, 1, 24, 16, 0, 0, p, p, p, None,
                          None) == _lib.OSDN_ERR_UNSUPPORTED
-    assert lib.osdn_step(p, p, p, p, None, None, 0.1, 1, -2, 16, 16, 0, p, p, p, None,
+    assert lib.osdn_step(p, p, p, p, None, None, 0.1, 1, -2, 16, 16, 0, 0, p, p, p, None,
                          None) == _lib.OSDN_ERR_SHAPE
 
 
@@ -129,12 +129,12 @@ def test_chunk_workspace_bytes(lib):
 
 
 def test_split_workspace_bytes(lib):
-    # matrix-core shapes: chunk records (32 KB; the walk records of 17 KB use the same
+    # matrix-core shapes: chunk records (32 KB; the walk records of 17.25 KB use the same
     # space first) and walk results (768 B)
     # per (b, h, chunk of 64); the walk alone: its records (17 KB) plus results
     assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 0) == 2 * 3 * 3 * (32768 + 768)
     assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 1) == 2 * 3 * 3 * (32768 + 768)
-    assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 0) == 2 * 3 * 3 * (17408 + 768)
+    assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 0) == 2 * 3 * 3 * (17664 + 768)
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 64, 0) == 0
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 1) == 0
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 48, 0) == (1 << 64) - 1
@@ -163,3 +163,17 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError, match="no CPU path"):
         osdn.forward(q, q, q, torch.zeros(1, 1, 4))
+
+
+def test_transform_flags(lib):
+    """Input transforms: accepted where the multi-launch or two-phase path runs,
+    refused where only the single fused kernel could (validated before any launch;
+    the dummy pointers are never dereferenced on these paths)."""
+    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, 2, 0, 0).decode() == "unsupported"
+    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, 6, 1, 1 << 40).decode() == "unsupported"
+    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, 6, 0, 1 << 40).decode() == "split"
+    assert lib.osdn_forward_path(1, 1, 64, 64, 64, 64, 1, 7, 0, 0).decode() == "two-phase"
+    assert _fwd(lib, B=1, H=1, T=64, dk=128, dv=128, chunk=64, flags=2) == _lib.OSDN_ERR_UNSUPPORTED
+    assert lib.osdn_forward_workspace_bytes(1, 1, 64, 128, 128, 64, 0, 7) > 0
+    assert lib.osdn_step(1, 1, 1, 1, None, None, 0.1, 1, 1, 16, 16, 0, 8, 1, 1, 1, None,
+                         None) == _lib.OSDN_ERR_UNSUPPORTED
