@@ -212,6 +212,10 @@ def main():
         ms_g = time_launches(lambda i: fwd(i, gated=True), args.steps, args.warmup, torch)
         ms_gdn = time_launches(lambda i: fwd(i, precond=False, gated=True), args.steps,
                                args.warmup, torch)
+        ms_g_single = time_launches(lambda i: fwd(i, gated=True, single=True), args.steps,
+                                    args.warmup, torch)
+        ms_gdn_single = time_launches(lambda i: fwd(i, precond=False, gated=True, single=True),
+                                      args.steps, args.warmup, torch)
         # raw inputs (q, k unnormalised, beta and r as logits): the transforms done
         # inside the kernels, against separate elementwise passes before the call
         raw_host = W.generate(dataclasses.replace(w, raw=True))
@@ -291,6 +295,10 @@ def main():
             "gated_forward": {"ms": ms_g, "tokens_per_s": tokens / (ms_g * 1e-3),
                               "vs_ungated": ms_g / ms},
             "gated_deltanet_mode": {"ms": ms_gdn, "tokens_per_s": tokens / (ms_gdn * 1e-3)},
+            "gated_forward_single_kernel": {"ms": ms_g_single,
+                                            "tokens_per_s": tokens / (ms_g_single * 1e-3)},
+            "gated_deltanet_mode_single_kernel": {
+                "ms": ms_gdn_single, "tokens_per_s": tokens / (ms_gdn_single * 1e-3)},
             "gated_precond_overhead": (ms_g - ms_gdn) / ms_g,
             "raw_inputs_transforms_in_kernels": {"ms": ms_raw,
                                                  "tokens_per_s": tokens / (ms_raw * 1e-3)},

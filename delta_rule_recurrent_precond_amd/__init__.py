@@ -114,8 +114,8 @@ def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64, *, alpha=None, workspac
 
     ``alpha`` [B,H,T] fp32 is the optional state gate.  ``workspace``: True
     allocates the scratch that selects the chunk-parallel path (when one exists
-    for these shapes; gated calls have none), a uint8 device tensor passes one,
-    None runs the single-kernel pass."""
+    for these shapes), a uint8 device tensor passes one, None runs the
+    single-kernel pass."""
     _dev(q, "q")
     B, H, T, dk = q.shape
     dev = q.device
@@ -130,8 +130,6 @@ def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64, *, alpha=None, workspac
     _dev(S0, "S0", (B, H, dv, dk), torch.float32, dev)
     o = torch.empty_like(v)
     S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-    if workspace is True and alpha is not None:
-        workspace = None
     if workspace is True:
         n = chunk_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), _dtype_code(q))
         workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
@@ -189,10 +187,9 @@ def forward_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code, precond=True) ->
     return int(n)
 
 
-def forward_path(B, H, T, dk, dv, chunk, dtype_code, precond=True, gated=False,
-                 workspace_bytes=0) -> str:
+def forward_path(B, H, T, dk, dv, chunk, dtype_code, precond=True, workspace_bytes=0) -> str:
     flags = 0 if precond else _lib.OSDN_PRECOND_OFF
-    return _lib.load().osdn_forward_path(B, H, T, dk, dv, chunk, dtype_code, flags, int(gated),
+    return _lib.load().osdn_forward_path(B, H, T, dk, dv, chunk, dtype_code, flags,
                                          int(workspace_bytes)).decode()
 
 
@@ -202,8 +199,8 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond
 
     ``norm_qk``: q and k are unnormalised and the kernels divide each by its L2
     norm; ``gate_logits``: beta and r are logits and the kernels take their
-    sigmoid (multi-launch and two-phase paths; not with alpha on the shapes of
-    the single fused kernel).
+    sigmoid (multi-launch and two-phase paths; the single fused kernel refuses
+    them).
 
     ``alpha`` [B,H,T] fp32 is the optional state gate (Gated DeltaNet backbone;
     with precond=False, Gated DeltaNet itself).
@@ -238,8 +235,6 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond
             "log_ratio_sum": torch.empty((B, H), dtype=torch.float32, device=dev),
         }
     single = forward_path(B, H, T, dk, dv, chunk, code, precond) == "fused"
-    if workspace is True and alpha is not None and single:
-        workspace = None  # the multi-launch pipeline has no state gate
     if workspace is True or (workspace is None and not single):
         need = forward_workspace_bytes(B, H, T, dk, dv, chunk, code, precond)
         workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None

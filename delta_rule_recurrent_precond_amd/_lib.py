@@ -43,7 +43,7 @@ SIGNATURES = {
                          P, P, P, P, P, ctypes.c_size_t, P]),
     "osdn_forward_workspace_bytes": (ctypes.c_size_t, [I, I, I, I, I, I, I, ctypes.c_uint]),
     "osdn_status_str": (ctypes.c_char_p, [I]),
-    "osdn_forward_path": (ctypes.c_char_p, [I, I, I, I, I, I, I, ctypes.c_uint, I,
+    "osdn_forward_path": (ctypes.c_char_p, [I, I, I, I, I, I, I, ctypes.c_uint,
                                             ctypes.c_size_t]),
 }
 

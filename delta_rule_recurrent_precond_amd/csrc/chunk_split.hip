@@ -23,9 +23,19 @@
 //   PA   fp16 [6 ops][64 lanes][8]  rows of P ds as A operands, paired k order
 //   ds   fp32 write-key scale: kt is stored divided by ds, a power of two
 //   lr   fp32 (kt = k only) sum over the chunk of log rho_t, rho_t = (1 - beta_t ||k_t||^2)^2
-//   sc   fp32 [2][64] (q, k given unnormalised) 1/||k_t|| and 1/||q_t||: the state
-//        kernel stages q and k as stored and scales the rows of K S^T and Q S^T
+//   gL   fp32 (state gate) gamma_L, the decay of the chunk's entry state
+//   sc   fp32 [2][64] (unnormalised q, k or a state gate) per-token factors of the
+//        rows of K S^T and Q S^T: 1/||k_t|| gamma_t and 1/||q_t|| gamma_t
+//        (gamma_t: product of the gates of the chunk up to t; L: its last row)
 // op x = 0..5 is (row block m, t pair qq) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
+//
+// With the state gate alpha (OSDN on the Gated DeltaNet backbone, read as
+// S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) kt_t^T) the chunk
+// form takes the decays gamma_t / gamma_s = 2^(lg_t - lg_s), lg_t the running
+// sum of log2 alpha within the chunk, each term clamped at -126:
+//   A_ts and P_ts gain gamma_t / gamma_s, the rows of K S^T and Q S^T gamma_t,
+//   the S-update operand of token s gamma_L / gamma_s (applied to kt_s in fp32
+//   before its fp16 rounding), and S <- gamma_L S + ...
 #include "device.h"
 #include "launch.h"
 #include "mfma.h"
@@ -47,7 +57,9 @@ constexpr size_t OFF_TM = 16384;
 constexpr size_t OFF_P = 22528;
 constexpr size_t OFF_DS = 28672;
 constexpr size_t OFF_LR = 28676;  // kt = k: sum over the chunk of log rho_t
-constexpr size_t OFF_SC = 28688;  // per-token 1/||k_t||, then 1/||q_t||
+constexpr size_t OFF_GL = 28680;  // gamma_L
+constexpr size_t OFF_SC = 28688;  // per-token factors of the K rows, then of the Q rows
+constexpr size_t OFF_KF = OFF_SC, OFF_QF = OFF_SC + 256, OFF_END = OFF_SC + 512;
 constexpr int LDT = 24;  // padded row (halves) of the 16x16 fp16 blocks in LDS
 constexpr int LDF = 20;  // padded row (floats) of the 16x16 fp32 blocks in LDS
 
@@ -67,14 +79,16 @@ constexpr int KP = 136;  // padded row (halves) of the staged [64][128] tiles
 // NORM (forward only): q and k arrive unnormalised.  q is staged normalised;
 // for kOsdn k is staged as stored (exact) and its 1/||k_t|| enters the
 // recurrence and the rows of A in fp32; for kt = k it is staged normalised.
-// Both scales go to the record for the state kernel.  xf & kGateLogits: beta
-// and r arrive as logits.
-template <int MODE, bool NORM>
+// The scales go to the record for the state kernel.  GATED: the state gate's
+// decays enter A, P and the S-update operands, and its row factors go to the
+// record.  xf & kGateLogits:
+// beta and r arrive as logits.
+template <int MODE, bool NORM, bool GATED>
 __global__ void __launch_bounds__(256)
 chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
            const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
            int c0, int ncs, unsigned char *__restrict__ ws, const float *__restrict__ r,
-           const float *__restrict__ wout, unsigned xf) {
+           const float *__restrict__ wout, const float *__restrict__ alpha, unsigned xf) {
   // q is needed only for the scores, which are formed first; the blocks of A
   // and T then reuse its space (53 KB in all: three workgroups per CU)
   __shared__ __align__(16) f16 Ks[C * KP];          // k
@@ -87,7 +101,9 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   static_assert(4 * 16 * LDF * 4 + 10 * 16 * LDT * 2 <= C * KP * 2, "A and T blocks fit");
   __shared__ float bs[C];
   __shared__ float cs[C], rs[C];  // kOsdn: c_t and r_t
-  __shared__ float sk[C];         // kOsdn, NORM: 1 / ||k_t||
+  __shared__ float sk[C], sq[C];  // NORM: 1 / ||k_t||, 1 / ||q_t||
+  __shared__ float lga[C];        // GATED: lg_t, the running sum of log2 alpha
+  __shared__ float xdl[C];        // GATED: gamma_L / gamma_t
   __shared__ float red[4];
 
   const int tid = threadIdx.x;
@@ -146,11 +162,20 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       qscale[u] = unit_scale(group_sum<16>(b));
       if ((tid & 15) == 0) {
         const int t = (tid + 256 * u) >> 4;
-        if (MODE == kOsdn) sk[t] = kscale[u];
-        *(float *)(rec + OFF_SC + 4 * t) = kscale[u];
-        *(float *)(rec + OFF_SC + 4 * (C + t)) = qscale[u];
+        sk[t] = kscale[u];
+        sq[t] = qscale[u];
       }
     }
+  }
+  if (GATED && tid < C) {  // wave 0: an inclusive scan over the chunk's tokens
+    const float av = alpha[tok0 + min(tid, L - 1)];
+    float incl = fmaxf(flog2(tid < L ? av : 1.0f), -126.f);  // alpha = 0 stays finite
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    lga[tid] = incl;
   }
 
   // write-key scale: a power of two >= max |kt| (given keys), 1 for kt = k
@@ -185,6 +210,20 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   }
   __syncthreads();
+
+  // the state kernel's per-token factors
+  if ((NORM || GATED) && tid < C) {
+    float kf = NORM ? sk[tid] : 1.0f, qf = NORM ? sq[tid] : 1.0f;
+    if (GATED) {
+      const float gm = fexp2(lga[tid]), lgL = lga[C - 1];
+      kf *= gm;
+      qf *= gm;
+      xdl[tid] = fexp2(lgL - lga[tid]);
+      if (tid == 0) *(float *)(rec + OFF_GL) = fexp2(lgL);
+    }
+    *(float *)(rec + OFF_KF + 4 * tid) = kf;
+    *(float *)(rec + OFF_QF + 4 * tid) = qf;
+  }
 
   if (MODE == kOsdn) {
     const float d_in = tid < DK ? wout[((long)bh * NC + c) * WOUT + tid] : 0.f;
@@ -240,15 +279,34 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     return (NORM && MODE == kOsdn) ? *(const f32x4 *)&sk[16 * rt_ + 4 * g]
                                    : f32x4{1.f, 1.f, 1.f, 1.f};
   };
+  // GATED: gamma_t / gamma_s for rows t = 16 rt + 4g + e and column s (taken
+  // only where s <= t, where it is <= 1)
+  auto dec4 = [&](int rt_, int s) {
+    if (!GATED) return f32x4{1.f, 1.f, 1.f, 1.f};
+    const float4 lt = *(const float4 *)&lga[16 * rt_ + 4 * g];
+    const float ls = lga[s];
+    return f32x4{fexp2(lt.x - ls), fexp2(lt.y - ls), fexp2(lt.z - ls), fexp2(lt.w - ls)};
+  };
+  // an entry of A: beta_t ds [gamma_t / gamma_s] (k_t . kt_s) [/ ||k_t||]
+  auto a_entry = [&](float b, float dc, float acc, float f) {
+    float x = b * ds;
+    if (GATED) x *= dc;
+    x *= acc;
+    if (NORM) x *= f;
+    return x;
+  };
 
   // ---- scores P = lower(Q Kt^T) ds, emitted as A operands (transposed tiles)
   for (int idx = wave; idx < 10; idx += 4) {
     int rt_, ct;
     tri_tile(idx, rt_, ct);
     const f32x4 acc = gram(Qs, rt_, ct);
+    const f32x4 dc = dec4(rt_, 16 * ct + c16);
     f32x4 pv;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pv[e] = (16 * ct + c16 <= 16 * rt_ + 4 * g + e) ? ds * acc[e] : 0.f;
+    for (int e = 0; e < 4; ++e)
+      pv[e] = (16 * ct + c16 <= 16 * rt_ + 4 * g + e) ? (GATED ? ds * dc[e] * acc[e] : ds * acc[e])
+                                                     : 0.f;
     const f16x4 pt = h4(mma16(h4(pv), ident, zero4()));
     *(f16x4 *)(rec + OFF_P + ((op_index(rt_, ct >> 1) * 64 + lane) * 8 + 4 * (ct & 1)) * 2) = pt;
   }
@@ -257,21 +315,20 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // ---- A: diagonal block `wave` (then its inverse) and off-diagonal blocks
   {
     const f32x4 acc = gram(Ks, wave, wave);
-    const f32x4 b4 = beta4(wave), f4 = krow4(wave);
+    const f32x4 b4 = beta4(wave), f4 = krow4(wave), dc = dec4(wave, 16 * wave + c16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 4 * g + e;
-      Fd[wave][row][c16] = c16 < row ? (NORM ? b4[e] * ds * acc[e] * f4[e] : b4[e] * ds * acc[e]) : 0.f;
+      Fd[wave][row][c16] = c16 < row ? a_entry(b4[e], dc[e], acc[e], f4[e]) : 0.f;
     }
   }
   for (int job = wave; job < 6; job += 4) {
     int rt_, ct;
     off_tile(job, rt_, ct);
     const f32x4 acc = gram(Ks, rt_, ct);
-    const f32x4 b4 = beta4(rt_), f4 = krow4(rt_);
+    const f32x4 b4 = beta4(rt_), f4 = krow4(rt_), dc = dec4(rt_, 16 * ct + c16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      Aoff[job][4 * g + e][c16] = h(NORM ? b4[e] * ds * acc[e] * f4[e] : b4[e] * ds * acc[e]);
+    for (int e = 0; e < 4; ++e) Aoff[job][4 * g + e][c16] = h(a_entry(b4[e], dc[e], acc[e], f4[e]));
   }
   wave_lds_sync();
   {
@@ -290,14 +347,22 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     *(f16x4 *)(rec + OFF_TM + ((op_index(2, 1) * 64 + lane) * 8 + 4) * 2) = z;
   }
 
-  // ---- write keys as S-update operands: i tiles 2w, 2w+1
+  // ---- write keys as S-update operands: i tiles 2w, 2w+1 (a lane holds tokens
+  // 16m + 4g + e of key dimension 16n + c16); GATED: decayed to the chunk end
 #pragma unroll
   for (int nn = 0; nn < 2; ++nn) {
     const int n = 2 * wave + nn;
     f16x4 tr[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      tr[m] = h4(mma16(ld4(&Ktp[(16 * m + c16) * KP + 16 * n + 4 * g]), ident, zero4()));
+    for (int m = 0; m < 4; ++m) {
+      f32x4 tv = mma16(ld4(&Ktp[(16 * m + c16) * KP + 16 * n + 4 * g]), ident, zero4());
+      if (GATED) {
+        const f32x4 xd = *(const f32x4 *)&xdl[16 * m + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tv[e] *= xd[e];
+      }
+      tr[m] = h4(tv);
+    }
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
       *(f16x8 *)(rec + OFF_KTF + (((n * 2 + qq) * 64 + lane) * 8) * 2) = cat(tr[2 * qq], tr[2 * qq + 1]);
@@ -378,8 +443,9 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // stored, so a burst of loads from every CU has two iterations to arrive.
 // Each role runs its own loop with the same barrier count (NC + 1), so the
 // registers of different roles are never live at the same time.
-// NORM: q and k are staged as stored; the record's per-token 1/||k_t|| and
-// 1/||q_t|| scale the rows of K S^T and Q S^T in fp32.
+// SCALED (unnormalised q, k or a state gate): q and k are staged as stored and
+// the record's per-token factors scale the rows of K S^T and Q S^T in fp32.
+// GATED: S decays by the record's gamma_L (the update operands carry the rest).
 // ---------------------------------------------------------------------------
 constexpr int ST = 768;        // threads
 constexpr int NL = ST - 256;   // loader lanes
@@ -389,14 +455,14 @@ struct StateSmem {
   f16 K[2][C * KP];
   f16 Q[2][C * KP];
   f16 V[2][C * VP];
-  unsigned char rec[2][OFF_SC + 2 * C * 4];  // KtF, TmA, PA, ds, scales of the chunk
+  unsigned char rec[2][OFF_END];  // KtF, TmA, PA, ds, factors of the chunk
   float b[2][C];
   f16x8 Sx[2][2][4][64];  // fp16 S^T at a chunk's start [parity][sn][kk][lane], paired order
   f16x8 Xx[2][2][2][64];  // X of a chunk [parity][sn][qq][lane], paired order
 };
 static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
 
-template <bool NORM>
+template <bool SCALED, bool GATED>
 __global__ void __launch_bounds__(ST)
 chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
             const float *__restrict__ beta, const float *__restrict__ S0, int BH, int T_, int NC,
@@ -432,11 +498,11 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
   if (wave >= 4) {
     // ================================ loaders ================================
     // k and q as 2048 pieces of 8 elements, the value tile as 256, the record as
-    // OFF_DS/16 + 1 = 1793 pieces of 16 bytes (1825 with the scales), beta.
+    // OFF_DS/16 + 1 = 1793 pieces of 16 bytes (1825 with the row factors), beta.
     // Loads are unconditional (a masked lane reads a valid address) and masked
     // values are zeroed when stored: a conditional load makes the compiler wait
     // for it at the end of its branch.
-    constexpr int RECP = NORM ? (int)(OFF_SC / 16) + 2 * C * 4 / 16 : (int)(OFF_DS / 16) + 1;
+    constexpr int RECP = SCALED ? (int)(OFF_END / 16) : (int)(OFF_DS / 16) + 1;
     constexpr int NKQ = (2048 + NL - 1) / NL, NR = (RECP + NL - 1) / NL;
     const int lt = tid - 256;
     struct Regs {
@@ -541,8 +607,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         f32x4 a = zero4();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) a = mma32(ldpk(kr, 32 * kk, g), Sb[kk], a);
-        if (NORM) {
-          const f32x4 s4 = *(const f32x4 *)(sm.rec[cb] + OFF_SC + 4 * (16 * m + 4 * g));
+        if (SCALED) {
+          const f32x4 s4 = *(const f32x4 *)(sm.rec[cb] + OFF_KF + 4 * (16 * m + 4 * g));
 #pragma unroll
           for (int e = 0; e < 4; ++e) a[e] *= s4[e];
         }
@@ -566,14 +632,16 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       const f16x8 Xb[2] = {cat(h4(X[0]), h4(X[1])), cat(h4(X[2]), h4(X[3]))};
       sm.Xx[cb][sn][0][lane] = Xb[0];
       sm.Xx[cb][sn][1][lane] = Xb[1];
-      // S^T += ds Kt^T X
+      const float gL = GATED ? *(const float *)(sm.rec[cb] + OFF_GL) : 1.0f;
+      // S^T <- gamma_L S^T + ds Kt^T X
 #pragma unroll
       for (int i8 = 0; i8 < 8; ++i8) {
         f32x4 u = zero4();
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) u = mma32(KtF[(i8 * 2 + qq) * 64 + lane], Xb[qq], u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Sacc[i8][e] = fmaf(ds, u[e], Sacc[i8][e]);
+        for (int e = 0; e < 4; ++e)
+          Sacc[i8][e] = fmaf(ds, u[e], GATED ? gL * Sacc[i8][e] : Sacc[i8][e]);
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -636,8 +704,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
           f32x4 a = zero4();
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) a = mma32(ldpk(qr, 32 * kk, g), Sb[kk], a);
-          if (NORM) {
-            const f32x4 s4 = *(const f32x4 *)(sm.rec[cb] + OFF_SC + 4 * (C + 16 * m + 4 * g));
+          if (SCALED) {
+            const f32x4 s4 = *(const f32x4 *)(sm.rec[cb] + OFF_QF + 4 * (16 * m + 4 * g));
 #pragma unroll
             for (int e = 0; e < 4; ++e) a[e] *= s4[e];
           }
@@ -661,24 +729,53 @@ size_t split_workspace_bytes(int B, int H, int T) {
 
 namespace {
 
-hipError_t launch_state(const ChunkArgs &a, int NC, const void *ws, float *log_ratio_sum,
-                        hipStream_t s) {
+template <bool SCALED, bool GATED>
+hipError_t launch_state_t(const ChunkArgs &a, int NC, const void *ws, float *log_ratio_sum,
+                          hipStream_t s) {
   const int BH = a.B * a.H;
   const size_t shm = sizeof(StateSmem);
-  const bool norm = (a.xf & kNormQK) != 0;
-  const void *fn = norm ? (const void *)chunk_state<true> : (const void *)chunk_state<false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  hipError_t e = hipFuncSetAttribute((const void *)chunk_state<SCALED, GATED>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  if (norm)
-    hipLaunchKernelGGL(chunk_state<true>, dim3((unsigned)(BH * 4)), dim3(ST), shm, s,
-                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.S0, BH,
-                       a.T, NC, (const unsigned char *)ws, (bf16 *)a.o, a.S_final, log_ratio_sum,
-                       a.xf);
+  hipLaunchKernelGGL((chunk_state<SCALED, GATED>), dim3((unsigned)(BH * 4)), dim3(ST), shm, s,
+                     (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.S0, BH,
+                     a.T, NC, (const unsigned char *)ws, (bf16 *)a.o, a.S_final, log_ratio_sum,
+                     a.xf);
+  return hipGetLastError();
+}
+
+// the record carries row factors when q, k arrive unnormalised or a gate is given
+hipError_t launch_state(const ChunkArgs &a, int NC, const void *ws, float *log_ratio_sum,
+                        hipStream_t s) {
+  if (a.alpha) return launch_state_t<true, true>(a, NC, ws, log_ratio_sum, s);
+  if (a.xf & kNormQK) return launch_state_t<true, false>(a, NC, ws, log_ratio_sum, s);
+  return launch_state_t<false, false>(a, NC, ws, log_ratio_sum, s);
+}
+
+template <int MODE, bool NORM, bool GATED>
+void launch_prep_t(int BH, int NC, hipStream_t s, const void *q, const void *k, const void *kt,
+                   const float *beta, int T, unsigned char *rec, const float *r,
+                   const float *wout, const float *alpha, unsigned xf) {
+  hipLaunchKernelGGL((chunk_prep<MODE, NORM, GATED>), dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+                     (const bf16 *)q, (const bf16 *)k, (const bf16 *)kt, beta, T, NC, 0, NC, rec,
+                     r, wout, alpha, xf);
+}
+
+// chunk_prep over every chunk of every head; kGiven takes no input transforms
+template <int MODE>
+hipError_t launch_prep(int BH, int NC, hipStream_t s, const void *q, const void *k,
+                       const void *kt, const float *beta, int T, unsigned char *rec,
+                       const float *r, const float *wout, const float *alpha, unsigned xf) {
+  if (NC <= 0) return hipSuccess;
+  const bool norm = MODE != kGiven && (xf & kNormQK);
+  if (norm && alpha)
+    launch_prep_t<MODE, MODE != kGiven, true>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+  else if (norm)
+    launch_prep_t<MODE, MODE != kGiven, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+  else if (alpha)
+    launch_prep_t<MODE, false, true>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
   else
-    hipLaunchKernelGGL(chunk_state<false>, dim3((unsigned)(BH * 4)), dim3(ST), shm, s,
-                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.S0, BH,
-                       a.T, NC, (const unsigned char *)ws, (bf16 *)a.o, a.S_final, log_ratio_sum,
-                       a.xf);
+    launch_prep_t<MODE, false, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
   return hipGetLastError();
 }
 
@@ -701,41 +798,21 @@ hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   unsigned char *rec = (unsigned char *)ws;
   float *wout = (float *)(rec + (size_t)BH * NC * REC);
   static_assert(WREC <= REC, "walk records fit in the chunk records' space");
-  ChunkArgs ca{a.q, a.k, nullptr, a.v, a.beta, nullptr, a.S0, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
+  ChunkArgs ca{a.q, a.k, nullptr, a.v, a.beta, a.alpha, a.S0, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
                a.dtype, a.o, a.S_final, a.xf};
-  if (a.precond_off) {  // the plain delta rule: kt = k
-    if (NC > 0) {
-      if (a.xf & kNormQK)
-        hipLaunchKernelGGL((chunk_prep<kDeltaNet, true>), dim3((unsigned)(BH * NC)), dim3(256), 0,
-                           s, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
-                           a.T, NC, 0, NC, rec, (const float *)nullptr, (const float *)nullptr,
-                           a.xf);
-      else
-        hipLaunchKernelGGL((chunk_prep<kDeltaNet, false>), dim3((unsigned)(BH * NC)), dim3(256), 0,
-                           s, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
-                           a.T, NC, 0, NC, rec, (const float *)nullptr, (const float *)nullptr,
-                           a.xf);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+  if (a.precond_off) {  // the plain delta rule (Gated DeltaNet with alpha): kt = k
+    hipError_t e = launch_prep<kDeltaNet>(BH, NC, s, a.q, a.k, nullptr, a.beta, a.T, rec, nullptr,
+                                          nullptr, a.alpha, a.xf);
+    if (e != hipSuccess) return e;
     return launch_state(ca, NC, ws, a.log_ratio_sum, s);
   }
+  // the gate leaves the preconditioner walk unchanged
   ScanArgs sa{a.k, a.beta, a.r, a.d0, a.eta, a.B, a.H, a.T, a.dk, a.dtype, 0, nullptr,
               a.d_final, nullptr, nullptr, a.log_ratio_sum, a.xf};
   hipError_t e = launch_walk(sa, rec, wout, s);
   if (e != hipSuccess) return e;
-  if (NC > 0) {
-    if (a.xf & kNormQK)
-      hipLaunchKernelGGL((chunk_prep<kOsdn, true>), dim3((unsigned)(BH * NC)), dim3(256), 0, s,
-                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta, a.T,
-                         NC, 0, NC, rec, a.r, (const float *)wout, a.xf);
-    else
-      hipLaunchKernelGGL((chunk_prep<kOsdn, false>), dim3((unsigned)(BH * NC)), dim3(256), 0, s,
-                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta, a.T,
-                         NC, 0, NC, rec, a.r, (const float *)wout, a.xf);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  e = launch_prep<kOsdn>(BH, NC, s, a.q, a.k, nullptr, a.beta, a.T, rec, a.r, wout, a.alpha, a.xf);
+  if (e != hipSuccess) return e;
   return launch_state(ca, NC, ws, nullptr, s);
 }
 
@@ -743,21 +820,15 @@ hipError_t launch_split_chunk(const ChunkArgs &a, bool given, void *ws, hipStrea
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
   const int NC = (a.T + C - 1) / C;
-  if (NC > 0) {
-    if (given)
-      hipLaunchKernelGGL((chunk_prep<kGiven, false>), dim3((unsigned)(BH * NC)), dim3(256), 0, s,
-                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.k_tilde, a.beta,
-                         a.T, NC, 0, NC, (unsigned char *)ws, (const float *)nullptr,
-                         (const float *)nullptr, 0u);
-    else
-      hipLaunchKernelGGL((chunk_prep<kDeltaNet, false>), dim3((unsigned)(BH * NC)), dim3(256), 0, s,
-                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)nullptr, a.beta,
-                         a.T, NC, 0, NC, (unsigned char *)ws, (const float *)nullptr,
-                         (const float *)nullptr, 0u);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return launch_state(a, NC, ws, nullptr, s);
+  unsigned char *rec = (unsigned char *)ws;
+  hipError_t e = given ? launch_prep<kGiven>(BH, NC, s, a.q, a.k, a.k_tilde, a.beta, a.T, rec,
+                                             nullptr, nullptr, a.alpha, 0u)
+                       : launch_prep<kDeltaNet>(BH, NC, s, a.q, a.k, nullptr, a.beta, a.T, rec,
+                                                nullptr, nullptr, a.alpha, 0u);
+  if (e != hipSuccess) return e;
+  ChunkArgs b = a;
+  b.xf = 0u;
+  return launch_state(b, NC, ws, nullptr, s);
 }
 
 }  // namespace osdn

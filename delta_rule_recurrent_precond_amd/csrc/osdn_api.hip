@@ -56,9 +56,9 @@ unsigned transforms(unsigned flags) {
          (flags & OSDN_GATE_LOGITS ? osdn::kGateLogits : 0u);
 }
 
-bool split_ok(int B, int H, int T, int dk, int dv, int chunk, int dtype, const float *alpha,
-              size_t workspace_bytes, const void *workspace) {
-  return use_fused(dk, dv, chunk, dtype) && !alpha && workspace &&
+bool split_ok(int B, int H, int T, int dk, int dv, int chunk, int dtype, size_t workspace_bytes,
+              const void *workspace) {
+  return use_fused(dk, dv, chunk, dtype) && workspace &&
          workspace_bytes >= osdn::split_forward_workspace_bytes(B, H, T);
 }
 
@@ -132,8 +132,7 @@ OSDN_EXPORT int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde
   osdn::ChunkArgs a{q, k, k_tilde, v, beta, alpha, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
   hipStream_t s = (hipStream_t)stream;
   if (use_fused(dk, dv, chunk, dtype)) {
-    // the two-kernel pass has no state gate; a gated call runs the single kernel
-    if (!alpha && workspace && workspace_bytes >= osdn::split_workspace_bytes(B, H, T))
+    if (workspace && workspace_bytes >= osdn::split_workspace_bytes(B, H, T))
       return hip_status(osdn::launch_split_chunk(a, true, workspace, s));
     return hip_status(osdn::launch_fused_chunk(a, s));
   }
@@ -148,13 +147,13 @@ OSDN_EXPORT size_t osdn_forward_workspace_bytes(int B, int H, int T, int dk, int
 }
 
 OSDN_EXPORT const char *osdn_forward_path(int B, int H, int T, int dk, int dv, int chunk,
-                                          int dtype, unsigned flags, int gated,
+                                          int dtype, unsigned flags,
                                           size_t workspace_bytes) {
   if (check_sizes(B, H, T, dk, dv, chunk, dtype, true, true) != OSDN_OK) return "invalid";
   if (flags & ~kFlags) return "invalid";
   if ((long long)B * H == 0) return "none";
   const float one = 1.0f;
-  if (split_ok(B, H, T, dk, dv, chunk, dtype, gated ? &one : nullptr, workspace_bytes, &one))
+  if (split_ok(B, H, T, dk, dv, chunk, dtype, workspace_bytes, &one))
     return "split";
   if (!use_fused(dk, dv, chunk, dtype)) return "two-phase";
   return transforms(flags) ? "unsupported" : "fused";
@@ -171,7 +170,7 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   const unsigned xf = transforms(flags);
   // the single fused kernel takes its inputs prepared
   if (xf && use_fused(dk, dv, chunk, dtype) &&
-      !split_ok(B, H, T, dk, dv, chunk, dtype, alpha, workspace_bytes, workspace))
+      !split_ok(B, H, T, dk, dv, chunk, dtype, workspace_bytes, workspace))
     return OSDN_ERR_UNSUPPORTED;
   if ((long long)B * H == 0) return OSDN_OK;
   if (T > 0 && (!q || !k || !v || !beta || !o)) return OSDN_ERR_NULL;
@@ -181,7 +180,7 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   if (use_fused(dk, dv, chunk, dtype)) {
     osdn::FusedArgs a{q, k, v, beta, r, alpha, d0, S0, eta, B, H, T, dk, dv, chunk, dtype,
                       off ? 1 : 0, o, S_final, d_final, log_ratio_sum, xf};
-    if (split_ok(B, H, T, dk, dv, chunk, dtype, alpha, workspace_bytes, workspace))
+    if (split_ok(B, H, T, dk, dv, chunk, dtype, workspace_bytes, workspace))
       return hip_status(osdn::launch_split_forward(a, workspace, s));
     return hip_status(osdn::launch_fused_forward(a, s));
   }

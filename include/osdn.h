@@ -82,7 +82,7 @@ extern "C" {
  *                     1 / (1 + exp(-x)).  alpha is not transformed.
  * The measured workloads apply exactly these transforms to their draws.
  * osdn_forward takes them on the multi-launch path (bf16, dk = dv = 128,
- * chunk 64, enough workspace, no alpha) and on the two-phase path; where the
+ * chunk 64, enough workspace) and on the two-phase path; where the
  * single fused kernel would run it returns OSDN_ERR_UNSUPPORTED. */
 #define OSDN_NORM_QK 2u
 #define OSDN_GATE_LOGITS 4u
@@ -139,8 +139,7 @@ size_t osdn_precond_scan_workspace_bytes(int B, int H, int T, int dk, int dtype)
  *   workspace  optional device scratch.  When it holds at least
  *              osdn_chunk_fwd_workspace_bytes(...) bytes (a positive number),
  *              the per-chunk work runs chunk-parallel ahead of the sequential
- *              pass (faster, ungated calls only); NULL selects the single-kernel
- *              pass.
+ *              pass (faster); NULL selects the single-kernel pass.
  */
 int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde, const void *v,
                    const float *beta, const float *alpha, const float *S0, int B, int H,
@@ -166,7 +165,7 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  *   workspace      device scratch.  With at least osdn_forward_workspace_bytes(...)
  *                  bytes the fastest path runs; for bf16, dk = dv = 128, chunk 64
  *                  that is a pipeline of launches (walk, chunk-parallel pass,
- *                  sequential state pass; ungated calls), and less scratch (or
+ *                  sequential state pass), and less scratch (or
  *                  NULL) selects the single fused kernel.  Other shapes need the
  *                  scratch (the walk hands kt to the chunk pass through it).
  */
@@ -210,14 +209,14 @@ size_t osdn_forward_workspace_bytes(int B, int H, int T, int dk, int dv, int chu
 /* Static, NUL-terminated description of a status code (host pointer). */
 const char *osdn_status_str(int status);
 
-/* Name of the kernel family osdn_forward would launch for these arguments,
- * whether a state gate is passed (gated != 0) and the workspace size: "split"
+/* Name of the kernel family osdn_forward would launch for these arguments and
+ * the workspace size (every family takes the state gate): "split"
  * (the multi-launch pipeline), "fused" (one kernel), "two-phase", "none", or
  * "unsupported" (input transforms where only the fused kernel could run);
  * static host string, "invalid" on bad arguments.  Lets callers and tests
  * know which path they exercised. */
 const char *osdn_forward_path(int B, int H, int T, int dk, int dv, int chunk, int dtype,
-                              unsigned flags, int gated, size_t workspace_bytes);
+                              unsigned flags, size_t workspace_bytes);
 
 #ifdef __cplusplus
 }

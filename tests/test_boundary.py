@@ -78,13 +78,13 @@ def test_forward_rejects(lib, kw, code):
 
 def test_forward_needs_workspace_on_two_phase_path(lib):
     # fp32 data always takes the two-launch path, which stages k~ in the workspace
-    assert lib.osdn_forward_path(1, 1, 4, 16, 16, 16, 1, 0, 0, 0).decode() == "two-phase"
+    assert lib.osdn_forward_path(1, 1, 4, 16, 16, 16, 1, 0, 0).decode() == "two-phase"
     assert _fwd(lib, dtype=1) == _lib.OSDN_ERR_WORKSPACE
 
 
 def test_empty_batch_is_a_no_op(lib):
     assert _fwd(lib, B=0, ptr=None) == _lib.OSDN_OK
-    assert lib.osdn_forward_path(0, 4, 8, 16, 16, 16, 0, 0, 0, 0).decode() == "none"
+    assert lib.osdn_forward_path(0, 4, 8, 16, 16, 16, 0, 0, 0).decode() == "none"
     assert lib.osdn_precond_scan(None, None, None, None, 0.1, 3, 0, 5, 16, 0, None, None, None,
                                  None, None, 0, None) == _lib.OSDN_OK
     assert lib.osdn_chunk_fwd(None, None, None, None, None, None, None, 0, 2, 5, 16, 16, 16, 0, None,
@@ -139,22 +139,21 @@ def test_split_workspace_bytes(lib):
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 1) == 0
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 48, 0) == (1 << 64) - 1
     n = lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 0)
-    assert lib.osdn_forward_path(2, 3, 130, 128, 128, 64, 0, 0, 0, n).decode() == "split"
-    assert lib.osdn_forward_path(2, 3, 130, 128, 128, 64, 0, 0, 0, n - 1).decode() == "fused"
-    assert lib.osdn_forward_path(2, 3, 130, 128, 128, 64, 0, 0, 1, n).decode() == "fused"
-    assert lib.osdn_forward_path(2, 3, 130, 128, 128, 64, 0, 1, 0, n).decode() == "split"
+    assert lib.osdn_forward_path(2, 3, 130, 128, 128, 64, 0, 0, n).decode() == "split"
+    assert lib.osdn_forward_path(2, 3, 130, 128, 128, 64, 0, 0, n - 1).decode() == "fused"
+    assert lib.osdn_forward_path(2, 3, 130, 128, 128, 64, 0, 1, n).decode() == "split"
 
 
 def test_workspace_bytes(lib):
     n = lib.osdn_forward_workspace_bytes(2, 3, 100, 64, 32, 32, 1, 0)
-    path = lib.osdn_forward_path(2, 3, 100, 64, 32, 32, 1, 0, 0, 0).decode()
+    path = lib.osdn_forward_path(2, 3, 100, 64, 32, 32, 1, 0, 0).decode()
     if path == "two-phase":
         assert n >= 2 * 3 * 100 * 64 * 4 and n % 256 == 0
     else:
         assert n == 0
     assert lib.osdn_forward_workspace_bytes(2, 3, 100, 64, 32, 32, 1, 1) == 0
     assert lib.osdn_forward_workspace_bytes(2, 3, 100, 48, 32, 32, 1, 0) == ctypes.c_size_t(-1).value
-    assert lib.osdn_forward_path(2, 3, 100, 48, 32, 32, 1, 0, 0, 0).decode() == "invalid"
+    assert lib.osdn_forward_path(2, 3, 100, 48, 32, 32, 1, 0, 0).decode() == "invalid"
 
 
 def test_python_binding_refuses_cpu_tensors():
@@ -169,10 +168,9 @@ def test_transform_flags(lib):
     """Input transforms: accepted where the multi-launch or two-phase path runs,
     refused where only the single fused kernel could (validated before any launch;
     the dummy pointers are never dereferenced on these paths)."""
-    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, 2, 0, 0).decode() == "unsupported"
-    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, 6, 1, 1 << 40).decode() == "unsupported"
-    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, 6, 0, 1 << 40).decode() == "split"
-    assert lib.osdn_forward_path(1, 1, 64, 64, 64, 64, 1, 7, 0, 0).decode() == "two-phase"
+    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, 2, 0).decode() == "unsupported"
+    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, 6, 1 << 40).decode() == "split"
+    assert lib.osdn_forward_path(1, 1, 64, 64, 64, 64, 1, 7, 0).decode() == "two-phase"
     assert _fwd(lib, B=1, H=1, T=64, dk=128, dv=128, chunk=64, flags=2) == _lib.OSDN_ERR_UNSUPPORTED
     assert lib.osdn_forward_workspace_bytes(1, 1, 64, 128, 128, 64, 0, 7) > 0
     assert lib.osdn_step(1, 1, 1, 1, None, None, 0.1, 1, 1, 16, 16, 0, 8, 1, 1, 1, None,

@@ -9,8 +9,11 @@ cumulative decays gamma_t / gamma_s = 2^(lg_t - lg_s); the oracle runs the
 token recurrence.  Tolerances are the ungated ones (the decays are <= 1 and
 only shrink the terms they touch): fp32 data o, S 1e-4 and d 1e-5; bf16 data
 o, S 2e-2 and d 1e-5.  Inputs come from the seeded generators; expected values
-from the oracle only.
+from the oracle only.  The matrix-core shapes run both paths: the multi-launch
+pipeline (the default workspace) and the single fused kernel (workspace=None).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -55,14 +58,14 @@ def _select(x, heads, w):
     return x.reshape((w.B * w.H,) + x.shape[2:])[heads]
 
 
-def _check(w, inp, precond=True, S0=None, heads=None, alpha=None):
+def _check(w, inp, precond=True, S0=None, heads=None, alpha=None, ws=True):
     alpha = inp.alpha if alpha is None else alpha
     heads = heads if heads is not None else list(range(w.B * w.H))
     dev = inp.to("cuda")
-    _log("gated forward %s precond=%s heads=%d" % (w.name, precond, len(heads)))
+    _log("gated forward %s precond=%s heads=%d workspace=%s" % (w.name, precond, len(heads), ws))
     out = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, None,
                        None if S0 is None else S0.cuda(), eta=inp.eta, chunk=w.chunk,
-                       precond=precond, alpha=alpha.cuda())
+                       precond=precond, alpha=alpha.cuda(), workspace=ws)
     torch.cuda.synchronize()
     ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, None, S0, eta=inp.eta,
                          mode="osdn" if precond else "deltanet", heads=heads,
@@ -87,20 +90,25 @@ def _check(w, inp, precond=True, S0=None, heads=None, alpha=None):
     ("f32", 128, 128, 64, 130),
 ])
 @pytest.mark.parametrize("precond", [True, False])
-def test_forward_gated_parity(dtype, dk, dv, chunk, T, precond):
+@pytest.mark.parametrize("ws", [True, None])
+def test_forward_gated_parity(dtype, dk, dv, chunk, T, precond, ws):
+    if ws is None and dk != 128:
+        pytest.skip("only the matrix-core shapes have a second path")
     w = _gated(2, 2, T, dk, dv, chunk, dtype, seed=900 + dk + dv + T)
     inp = W.generate(w)
     S0 = 0.1 * torch.randn(w.B, w.H, dv, dk, generator=torch.Generator().manual_seed(4))
-    _check(w, inp, precond, S0=S0)
+    _check(w, inp, precond, S0=S0, ws=ws)
 
 
 @pytest.mark.parametrize("T", [1, 63, 64, 129])
-def test_forward_gated_chunk_boundaries(T):
+@pytest.mark.parametrize("ws", [True, None])
+def test_forward_gated_chunk_boundaries(T, ws):
     w = _gated(1, 2, T, 128, 128, 64, "bf16", seed=950 + T)
-    _check(w, W.generate(w))
+    _check(w, W.generate(w), ws=ws)
 
 
-def test_strong_decay_and_zero_gates():
+@pytest.mark.parametrize("ws", [True, None])
+def test_strong_decay_and_zero_gates(ws):
     """Gates spread over (0, 1) with some exact zeros (a state reset: the state
     before such a token is forgotten)."""
     w = _gated(2, 2, 200, 128, 128, 64, "bf16", seed=961, alpha_mu=0.0, alpha_sigma=2.0)
@@ -110,7 +118,13 @@ def test_strong_decay_and_zero_gates():
     alpha[:, :, 64] = 0.0     # first token of a chunk
     alpha[:, :, 127] = 0.0    # last token of a chunk
     S0 = torch.randn(w.B, w.H, 128, 128, generator=torch.Generator().manual_seed(5))
-    _check(w, inp, S0=S0, alpha=alpha)
+    _check(w, inp, S0=S0, alpha=alpha, ws=ws)
+    # every token resets the state: o_t = beta_t (q_t . kt_t) v_t.  With q = k the
+    # factor is sum_i d_i k_i^2 > 0, so no row of o is a cancelling dot product
+    # (whose row-relative error would measure one fp16 rounding, not the pass)
+    rec = dataclasses.replace(inp, q=inp.k)
+    for p in (True, False):
+        _check(w, rec, precond=p, S0=S0, alpha=torch.zeros_like(alpha), ws=ws)
     wf = _gated(1, 2, 90, 32, 32, 16, "f32", seed=962, alpha_mu=0.0, alpha_sigma=2.0)
     inpf = W.generate(wf)
     af = inpf.alpha.clone()
@@ -121,17 +135,20 @@ def test_strong_decay_and_zero_gates():
 
 @pytest.mark.parametrize("dtype,dk,chunk", [("bf16", 128, 64), ("f32", 32, 16)])
 @pytest.mark.parametrize("precond", [True, False])
-def test_unit_gate_equals_ungated_bitwise(dtype, dk, chunk, precond):
+@pytest.mark.parametrize("ws", [True, None])
+def test_unit_gate_equals_ungated_bitwise(dtype, dk, chunk, precond, ws):
     """alpha = 1 gives decays of exactly 1, so the gated kernels reproduce the
-    ungated results bit for bit."""
+    ungated results of the same path bit for bit."""
+    if ws is None and dtype == "f32":
+        pytest.skip("the fp32 path needs its workspace")
     w = W.custom(2, 2, 150, dk, dk, chunk, dtype=dtype, eta=0.1, apf=True, seed=970 + dk)
     inp = W.generate(w)
     dev = inp.to("cuda")
     ones = torch.ones(w.B, w.H, w.T, device="cuda")
     a = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=inp.eta, chunk=chunk,
-                     precond=precond, workspace=None)  # the same kernel as the gated call
+                     precond=precond, workspace=ws)
     b = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=inp.eta, chunk=chunk,
-                     precond=precond, alpha=ones)
+                     precond=precond, alpha=ones, workspace=ws)
     torch.cuda.synchronize()
     for name in ("o", "S_final", "d_final", "log_ratio_sum"):
         if a.get(name) is not None:
@@ -139,8 +156,10 @@ def test_unit_gate_equals_ungated_bitwise(dtype, dk, chunk, precond):
 
 
 @pytest.mark.parametrize("dtype,dk,dv,chunk,T", [("bf16", 128, 128, 64, 300),
+                                                 ("bf16", 128, 128, 64, 64),
                                                  ("f32", 64, 32, 32, 97)])
-def test_chunk_fwd_gated_given_ktilde(dtype, dk, dv, chunk, T):
+@pytest.mark.parametrize("ws", [True, None])
+def test_chunk_fwd_gated_given_ktilde(dtype, dk, dv, chunk, T, ws):
     w = _gated(2, 2, T, dk, dv, chunk, dtype, seed=980 + T)
     inp = W.generate(w)
     S0 = 0.1 * torch.randn(w.B, w.H, dv, dk, generator=torch.Generator().manual_seed(6))
@@ -150,7 +169,7 @@ def test_chunk_fwd_gated_given_ktilde(dtype, dk, dv, chunk, T):
     dev = inp.to("cuda")
     _log("gated chunk %s" % w.name)
     o, S = osdn.chunk_fwd(dev.q, dev.k, kt.cuda(), dev.v, dev.beta, S0.cuda(), chunk,
-                          alpha=dev.alpha)
+                          alpha=dev.alpha, workspace=ws)
     torch.cuda.synchronize()
     ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, None, None, S0, mode="given",
                          k_given=kt, want=("o", "S"), alpha=inp.alpha)
@@ -159,20 +178,20 @@ def test_chunk_fwd_gated_given_ktilde(dtype, dk, dv, chunk, T):
     assert matrix_rel(S, ref["S"]) <= tol["S"]
 
 
-def test_chunk_fwd_gated_ignores_workspace():
-    """A gated call given a workspace still runs (the chunk-parallel pass has no
-    gate) and matches the call without one bit for bit."""
+def test_chunk_fwd_gated_unit_gate_bitwise():
+    """The chunk-parallel pass with alpha = 1 reproduces its ungated results bit
+    for bit (given keys and kt = k alike)."""
     w = _gated(1, 2, 200, 128, 128, 64, "bf16", seed=985)
     inp = W.generate(w)
     dev = inp.to("cuda")
     n = osdn.chunk_fwd_workspace_bytes(w.B, w.H, w.T, 128, 128, 64, 0)
     ws = torch.empty(n, dtype=torch.uint8, device="cuda")
-    a = osdn.chunk_fwd(dev.q, dev.k, dev.k, dev.v, dev.beta, None, 64, alpha=dev.alpha,
-                       workspace=ws)
-    b = osdn.chunk_fwd(dev.q, dev.k, dev.k, dev.v, dev.beta, None, 64, alpha=dev.alpha,
-                       workspace=None)
-    torch.cuda.synchronize()
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    ones = torch.ones(w.B, w.H, w.T, device="cuda")
+    for kt in (dev.k, dev.q):
+        a = osdn.chunk_fwd(dev.q, dev.k, kt, dev.v, dev.beta, None, 64, alpha=ones, workspace=ws)
+        b = osdn.chunk_fwd(dev.q, dev.k, kt, dev.v, dev.beta, None, 64, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 @pytest.mark.parametrize("dtype,dk,dv", [("f32", 32, 64), ("bf16", 128, 128)])
@@ -220,8 +239,9 @@ def test_gated_steps_continue_a_gated_forward():
 
 
 @pytest.mark.slow
-def test_gated_workload_full_size():
+@pytest.mark.parametrize("ws", [True, None])
+def test_gated_workload_full_size(ws):
     """The gated 1.3B-style layer at full size, on sampled heads."""
     w = W.CONFIGS["1.3b-apf-gated"]
     inp = W.generate(w)
-    _check(w, inp, heads=_heads(w, 4))
+    _check(w, inp, heads=_heads(w, 4), ws=ws)

@@ -47,7 +47,8 @@ def _select(x, heads, w):
     return x.reshape((w.B * w.H,) + x.shape[2:])[heads]
 
 
-def _check(w, inp, precond=True, heads=None, S0=None, norm_qk=True, gate_logits=True):
+def _check(w, inp, precond=True, heads=None, S0=None, norm_qk=True, gate_logits=True,
+           gated=False):
     heads = heads if heads is not None else list(range(w.B * w.H))
     dev = inp.to("cuda")
     code = 0 if w.dtype == "bf16" else 1
@@ -57,12 +58,13 @@ def _check(w, inp, precond=True, heads=None, S0=None, norm_qk=True, gate_logits=
                                            workspace_bytes=ws_n)))
     out = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, None,
                        None if S0 is None else S0.cuda(), eta=inp.eta, chunk=w.chunk,
-                       precond=precond, norm_qk=norm_qk, gate_logits=gate_logits)
+                       precond=precond, norm_qk=norm_qk, gate_logits=gate_logits,
+                       alpha=dev.alpha if gated else None)
     torch.cuda.synchronize()
     q, k, b, r = oracle.prepare_inputs(inp.q, inp.k, inp.beta, inp.r, norm_qk, gate_logits)
     ref = oracle.forward(q, k, inp.v, b, r, None, S0, eta=inp.eta,
                          mode="osdn" if precond else "deltanet", heads=heads,
-                         want=("o", "S", "d", "rho"))
+                         want=("o", "S", "d", "rho"), alpha=inp.alpha if gated else None)
     tol = TOL[w.dtype]
     errs = {"o": rowwise_rel(_select(out["o"], heads, w), _select(ref["o"], heads, w)),
             "S": matrix_rel(_select(out["S_final"], heads, w), _select(ref["S"], heads, w))}
@@ -78,9 +80,9 @@ def _check(w, inp, precond=True, heads=None, S0=None, norm_qk=True, gate_logits=
     assert errs["lrs"] <= 1.0, errs
 
 
-def _raw(B, H, T, dk, dv, chunk, dtype, seed, apf=True):
+def _raw(B, H, T, dk, dv, chunk, dtype, seed, apf=True, gated=False):
     return dataclasses.replace(W.custom(B, H, T, dk, dv, chunk, dtype=dtype, eta=0.1, apf=apf,
-                                        seed=seed), raw=True)
+                                        seed=seed, gated=gated), raw=True)
 
 
 @pytest.mark.parametrize("precond", [True, False])
@@ -95,6 +97,19 @@ def test_forward_raw_inputs(dtype, dk, dv, chunk, T, precond):
     w = _raw(2, 2, T, dk, dv, chunk, dtype, seed=1100 + dk + T)
     S0 = 0.1 * torch.randn(2, 2, dv, dk, generator=torch.Generator().manual_seed(8))
     _check(w, W.generate(w), precond, S0=S0)
+
+
+@pytest.mark.parametrize("precond", [True, False])
+@pytest.mark.parametrize("dtype,dk,dv,chunk,T", [
+    ("bf16", 128, 128, 64, 300),   # multi-launch pipeline with the state gate
+    ("f32", 32, 64, 32, 77),       # two-phase path
+])
+def test_gated_forward_raw_inputs(dtype, dk, dv, chunk, T, precond):
+    """Raw inputs with the state gate (OSDN on Gated DeltaNet; Gated DeltaNet
+    itself without the preconditioner)."""
+    w = _raw(2, 2, T, dk, dv, chunk, dtype, seed=1190 + dk + T, gated=True)
+    S0 = 0.1 * torch.randn(2, 2, dv, dk, generator=torch.Generator().manual_seed(9))
+    _check(w, W.generate(w), precond, S0=S0, gated=True)
 
 
 @pytest.mark.parametrize("norm_qk,gate_logits", [(True, False), (False, True)])
