@@ -293,15 +293,18 @@ def main():
                               "traffic": stored_traffic("osdn_deltanet_split", args.workload)},
             "precond_overhead": (ms - ms_dn) / ms,
             "gated_forward": {"ms": ms_g, "tokens_per_s": tokens / (ms_g * 1e-3),
-                              "vs_ungated": ms_g / ms},
+                              "vs_ungated": ms_g / ms,
+                              "traffic": stored_traffic("osdn_forward_gated_split",
+                                                        args.workload)},
             "gated_deltanet_mode": {"ms": ms_gdn, "tokens_per_s": tokens / (ms_gdn * 1e-3)},
             "gated_forward_single_kernel": {"ms": ms_g_single,
                                             "tokens_per_s": tokens / (ms_g_single * 1e-3)},
             "gated_deltanet_mode_single_kernel": {
                 "ms": ms_gdn_single, "tokens_per_s": tokens / (ms_gdn_single * 1e-3)},
             "gated_precond_overhead": (ms_g - ms_gdn) / ms_g,
-            "raw_inputs_transforms_in_kernels": {"ms": ms_raw,
-                                                 "tokens_per_s": tokens / (ms_raw * 1e-3)},
+            "raw_inputs_transforms_in_kernels": {
+                "ms": ms_raw, "tokens_per_s": tokens / (ms_raw * 1e-3),
+                "traffic": stored_traffic("osdn_forward_raw_split", args.workload)},
             "raw_inputs_separate_torch_passes": {"ms": ms_raw_sep,
                                                  "tokens_per_s": tokens / (ms_raw_sep * 1e-3)},
             "two_launch_scan_share": ms_scan / (ms_scan + ms_chunk),

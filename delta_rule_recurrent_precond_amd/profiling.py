@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import dataclasses
 import glob
 import hashlib
 import json
@@ -38,7 +39,12 @@ ENTRIES = {
     "deltanet_split": "osdn_deltanet_split",
     "scan_split": "osdn_precond_scan_split",
     "chunk_split": "osdn_chunk_fwd_split",
+    "forward_gated_split": "osdn_forward_gated_split",
+    "forward_raw_split": "osdn_forward_raw_split",
 }
+# entries that profile another draw of the same workload: the state gate added,
+# or q, k unnormalised with beta, r as logits (the kernels transform them)
+DRAWS = {"forward_gated_split": {"gated": True}, "forward_raw_split": {"raw": True}}
 
 
 def kernel_sources_hash() -> str:
@@ -69,6 +75,12 @@ def call(entry: str, dev, w):
         osdn.precond_scan(dev.k, dev.beta, dev.r, None, dev.eta)
     elif entry == "chunk_split":
         osdn.chunk_fwd(dev.q, dev.k, dev.k, dev.v, dev.beta, chunk=w.chunk)
+    elif entry == "forward_gated_split":
+        osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=dev.eta, chunk=w.chunk,
+                     alpha=dev.alpha)
+    elif entry == "forward_raw_split":
+        osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=dev.eta, chunk=w.chunk,
+                     norm_qk=True, gate_logits=True)
     else:
         raise SystemExit("unknown entry %s" % entry)
 
@@ -88,7 +100,7 @@ def run(workload: str, launches: int, entry: str) -> None:
         b.copy_(a)
     torch.cuda.synchronize()
     del a, b
-    w = W.CONFIGS[workload]
+    w = dataclasses.replace(W.CONFIGS[workload], **DRAWS.get(entry, {}))
     dev = W.generate(w).to("cuda")
     for _ in range(launches):
         call(entry, dev, w)
