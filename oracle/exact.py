@@ -14,9 +14,10 @@ from fractions import Fraction as F
 
 
 def run(q, k, v, beta, r=None, d0=None, S0=None, eta=F(0), deltanet=False, alpha=None):
-    """Sequences of rationals: q,k [T][dk], v [T][dv], beta,r,alpha [T], d0 [dk],
+    """Sequences of rationals: q,k [T][dk], v [T][dv], beta,r [T], d0 [dk],
     S0 [dv][dk].  alpha is the optional state gate (the state is scaled by
-    alpha_t before token t reads and writes it).
+    alpha_t before token t reads and writes it): [T] scalars, or [T][dk] with one
+    gate per key dimension, which scales column i of the state by alpha_t[i].
     Returns dict(o [T][dv], S [dv][dk], d [dk], k_tilde [T][dk], rho [T])."""
     T = len(k)
     dk = len(k[0]) if T else (len(d0) if d0 is not None else 0)
@@ -34,7 +35,10 @@ def run(q, k, v, beta, r=None, d0=None, S0=None, eta=F(0), deltanet=False, alpha
         a = sum((di * si for di, si in zip(d, sq)), F(0))
         w = list(kt_vec) if deltanet else [di * ki for di, ki in zip(d, kt_vec)]
         kts.append(w)
-        if alpha is not None:
+        if alpha is not None and isinstance(alpha[t], (list, tuple)):
+            ag = [F(x) for x in alpha[t]]
+            S = [[ag[i] * row[i] for i in range(dk)] for row in S]
+        elif alpha is not None:
             at = F(alpha[t])
             S = [[at * x for x in row] for row in S]
         # state read with (the gated) S_{t-1}, then rank-one write

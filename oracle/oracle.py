@@ -67,7 +67,7 @@ def _load():
             lib.oracle_forward.argtypes = [
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 ctypes.c_int, ctypes.c_double,
-                P, P, P, P, P, P, P, P, P,  # q k v beta r d0 S0 k_given alpha
+                P, P, P, P, P, P, P, P, P, P,  # q k v beta r d0 S0 k_given alpha alpha_k
                 P, P, P, P, P, P,         # o S_final d_final k_tilde d_all rho
                 P, ctypes.c_long, ctypes.c_int]
             _lib = lib
@@ -123,6 +123,9 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.0, mode="osdn",
 
     ``alpha`` [B,H,T] is the optional state gate (Gated DeltaNet backbone):
     S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) kt_t^T.
+    ``alpha`` [B,H,T,dk] is the per-channel gate (Kimi Delta Attention
+    backbone): S_t = S_{t-1} D_t + beta_t (v_t - S_{t-1} D_t k_t) kt_t^T with
+    D_t = diag(alpha_t), which scales the key columns of S.
 
     Arrays are [B,H,T,dk] (q, k, k_given), [B,H,T,dv] (v), [B,H,T] (beta, r),
     [B,H,dk] (d0), [B,H,dv,dk] (S0); anything convertible (numpy, torch CPU)
@@ -144,6 +147,10 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.0, mode="osdn",
     k_given = _f64(k_given)
     alpha = _f64(alpha)
     assert v.shape == (B, H, T, dv) and beta.shape == (B, H, T)
+    alpha_k = None
+    if alpha is not None and alpha.ndim == 4:
+        assert alpha.shape == (B, H, T, dk)
+        alpha, alpha_k = None, alpha
     if alpha is not None:
         assert alpha.shape == (B, H, T)
     if q is not None:
@@ -173,7 +180,7 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.0, mode="osdn",
     nthr = threads if threads is not None else min(default_threads(), max(1, n_heads))
     rc = lib.oracle_forward(B, H, T, dk, dv, MODES[mode], float(eta),
                             _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(d0),
-                            _ptr(S0), _ptr(k_given), _ptr(alpha),
+                            _ptr(S0), _ptr(k_given), _ptr(alpha), _ptr(alpha_k),
                             _ptr(o), _ptr(Sf), _ptr(df), _ptr(kt), _ptr(da), _ptr(rho),
                             _ptr(hv), n_heads, int(nthr))
     if rc != 0:
@@ -243,8 +250,16 @@ def chunked_state_pass(q, k, k_tilde, v, beta, S0=None, C=64, alpha=None):
         (I + A) X = diag(beta) (V - diag(gamma) K S^T),
         O_t = gamma_t S q_t + sum_{s<=t} (gamma_t/gamma_s) (q_t . k~_s) x_s,
         S' = gamma_L S + sum_s (gamma_L/gamma_s) x_s k~_s^T.
-    Inputs: q, k, k_tilde [T,dk]; v [T,dv]; beta, alpha [T]; S0 [dv,dk].
-    Returns (o [T,dv], S_final [dv,dk]).
+    With a per-channel gate (alpha [T,dk], S_t = S_{t-1} D_t + x_t k~_t^T,
+    D_t = diag(alpha_t)) the decays are vectors g_t = prod_{m<=t} alpha_m, and
+    S_{t-1} D_t = S diag(g_t) + sum_{s<t} x_s (k~_s (.) g_t / g_s)^T gives
+        A_ts = beta_t <k_t (.) g_t, k~_s / g_s> (s < t),
+        (I + A) X = diag(beta) (V - (K (.) G) S^T),
+        O = (Q (.) G) S^T + lower_incl_diag((Q (.) G) (K~ / G)^T) X,
+        S' = S diag(g_L) + X^T (K~ (.) g_L / G).
+    (Plain fp64 division by g: for gates bounded away from zero.)
+    Inputs: q, k, k_tilde [T,dk]; v [T,dv]; beta [T]; alpha [T] or [T,dk];
+    S0 [dv,dk].  Returns (o [T,dv], S_final [dv,dk]).
     """
     q, k, kt, v, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, k_tilde, v, beta))
     T, dk = k.shape
@@ -255,6 +270,15 @@ def chunked_state_pass(q, k, k_tilde, v, beta, S0=None, C=64, alpha=None):
     for c0 in range(0, T, C):
         sl = slice(c0, min(T, c0 + C))
         Q, K, Kt, V, bt = q[sl], k[sl], kt[sl], v[sl], beta[sl]
+        if al.ndim == 2:  # one gate per key dimension
+            G = np.cumprod(al[sl], axis=0)
+            KG, QG, KtG = K * G, Q * G, Kt / G
+            A = np.tril(bt[:, None] * (KG @ KtG.T), k=-1)
+            rhs = bt[:, None] * (V - KG @ S.T)
+            X = np.linalg.solve(np.eye(len(bt)) + A, rhs)
+            o[sl] = QG @ S.T + np.tril(QG @ KtG.T) @ X
+            S = S * G[-1][None, :] + X.T @ (Kt * (G[-1][None, :] / G))
+            continue
         gam = np.cumprod(al[sl])
         ratio = gam[:, None] / gam[None, :]          # gamma_t / gamma_s
         A = np.tril(bt[:, None] * ratio * (K @ Kt.T), k=-1)

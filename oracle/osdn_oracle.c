@@ -39,6 +39,14 @@
  * i.e. S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) kt^T.  The
  * preconditioner walk and rho_t do not involve S and are unchanged.  NULL
  * alpha is alpha = 1.
+ *
+ * Optional per-channel gate alpha_k (Kimi Delta Attention backbone, also only
+ * named in [summary §4]; the plainest reading generalises the scalar gate to
+ * one gate per key dimension): each column i of S (key dimension i) decays by
+ * alpha_k[t][i] before the token's read and write,
+ *     S <- S diag(alpha_k_t),  then u = v_t - S k_t and S += beta_t u kt^T,
+ * i.e. S_t = S_{t-1} D_t + beta_t (v_t - S_{t-1} D_t k_t) kt^T, D_t = diag(alpha_k_t).
+ * A gate vector with equal entries is the scalar gate.
  */
 #include <math.h>
 #include <pthread.h>
@@ -50,7 +58,7 @@ enum { ORACLE_OSDN = 0, ORACLE_DELTANET = 1, ORACLE_GIVEN_KTILDE = 2 };
 typedef struct {
   int B, H, T, dk, dv, mode;
   double eta;
-  const double *q, *k, *v, *beta, *r, *d0, *S0, *k_given, *alpha;
+  const double *q, *k, *v, *beta, *r, *d0, *S0, *k_given, *alpha, *alpha_k;
   double *o, *S_final, *d_final, *k_tilde, *d_all, *rho;
   const long *heads; /* which flattened (b,h) indices to run */
   long n_heads;
@@ -105,6 +113,11 @@ static int run_head(const oracle_job *J, long bh) {
     if (J->alpha) {
       const double at = J->alpha[row];
       for (long x = 0; x < (long)dv * dk; ++x) S[x] *= at;
+    }
+    if (J->alpha_k) {
+      const double *ak = J->alpha_k + row * dk;
+      for (int j = 0; j < dv; ++j)
+        for (int i = 0; i < dk; ++i) S[(long)j * dk + i] *= ak[i];
     }
 
     /* residual against the state before this token's write */
@@ -172,7 +185,8 @@ static void *worker(void *arg) {
  * Run the recurrence over the heads listed in `heads` (flattened b*H+h; NULL
  * means all B*H heads) with up to n_threads threads (one head per task).
  * Shapes: q,k,k_given,k_tilde,d_all [B,H,T,dk]; v,o [B,H,T,dv];
- * beta,r,alpha,rho [B,H,T]; d0,d_final [B,H,dk]; S0,S_final [B,H,dv,dk].
+ * beta,r,alpha,rho [B,H,T]; alpha_k [B,H,T,dk]; d0,d_final [B,H,dk];
+ * S0,S_final [B,H,dv,dk].
  * Optional pointers may be NULL.  Returns 0, or -1 on bad arguments or
  * allocation failure.
  */
@@ -180,7 +194,7 @@ int oracle_forward(int B, int H, int T, int dk, int dv, int mode, double eta,
                    const double *q, const double *k, const double *v,
                    const double *beta, const double *r, const double *d0,
                    const double *S0, const double *k_given, const double *alpha,
-                   double *o, double *S_final, double *d_final,
+                   const double *alpha_k, double *o, double *S_final, double *d_final,
                    double *k_tilde, double *d_all, double *rho,
                    const long *heads, long n_heads, int n_threads) {
   if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
@@ -196,7 +210,7 @@ int oracle_forward(int B, int H, int T, int dk, int dv, int mode, double eta,
   memset(&J, 0, sizeof(J));
   J.B = B; J.H = H; J.T = T; J.dk = dk; J.dv = dv; J.mode = mode; J.eta = eta;
   J.q = q; J.k = k; J.v = v; J.beta = beta; J.r = r; J.d0 = d0; J.S0 = S0;
-  J.k_given = k_given; J.alpha = alpha; J.o = o; J.S_final = S_final; J.d_final = d_final;
+  J.k_given = k_given; J.alpha = alpha; J.alpha_k = alpha_k; J.o = o; J.S_final = S_final; J.d_final = d_final;
   J.k_tilde = k_tilde; J.d_all = d_all; J.rho = rho;
   J.heads = heads; J.n_heads = n_heads; J.next = 0; J.failed = 0;
   pthread_mutex_init(&J.lock, NULL);
