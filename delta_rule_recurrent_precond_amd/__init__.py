@@ -149,8 +149,8 @@ def _transform_flags(norm_qk, gate_logits):
 def step(q, k, v, beta, S, d, r=None, eta=0.05, *, alpha=None, o=None, want_log_ratio=False,
          norm_qk=False, gate_logits=False):
     """One decoding step.  q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), beta, r and
-    the optional state gate alpha [B,H] fp32; S [B,H,dv,dk] and d [B,H,dk] fp32
-    are updated in place.  ``norm_qk``: q, k are unnormalised (the kernel
+    the optional state gate alpha [B,H] fp32 (or [B,H,dk]: one gate per key
+    dimension); S [B,H,dv,dk] and d [B,H,dk] fp32 are updated in place.  ``norm_qk``: q, k are unnormalised (the kernel
     divides them by their norms); ``gate_logits``: beta, r are logits.
     Returns dict(o[, log_ratio])."""
     _dev(q, "q")
@@ -163,14 +163,17 @@ def step(q, k, v, beta, S, d, r=None, eta=0.05, *, alpha=None, o=None, want_log_
     dv = v.shape[2]
     _dev(beta, "beta", (B, H), torch.float32, dev)
     _dev(r, "r", (B, H), torch.float32, dev)
-    _dev(alpha, "alpha", (B, H), torch.float32, dev)
+    chan = alpha is not None and alpha.dim() == 3
+    _dev(alpha, "alpha", (B, H, dk) if chan else (B, H), torch.float32, dev)
     _dev(S, "S", (B, H, dv, dk), torch.float32, dev)
     _dev(d, "d", (B, H, dk), torch.float32, dev)
     o = torch.empty_like(v) if o is None else o
     lr = torch.empty((B, H), dtype=torch.float32, device=dev) if want_log_ratio else None
     st = _lib.load().osdn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(alpha),
                                float(eta), B, H, dk, dv, _dtype_code(q),
-                               _transform_flags(norm_qk, gate_logits), _ptr(S), _ptr(d), _ptr(o),
+                               _transform_flags(norm_qk, gate_logits)
+                               | (_lib.OSDN_GATE_PER_CHANNEL if chan else 0),
+                               _ptr(S), _ptr(d), _ptr(o),
                                _ptr(lr), _stream(dev))
     _lib.check("osdn_step", st)
     out = {"o": o}
@@ -179,16 +182,20 @@ def step(q, k, v, beta, S, d, r=None, eta=0.05, *, alpha=None, o=None, want_log_
     return out
 
 
-def forward_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code, precond=True) -> int:
-    flags = 0 if precond else _lib.OSDN_PRECOND_OFF
+def forward_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code, precond=True,
+                            per_channel=False) -> int:
+    flags = ((0 if precond else _lib.OSDN_PRECOND_OFF)
+             | (_lib.OSDN_GATE_PER_CHANNEL if per_channel else 0))
     n = _lib.load().osdn_forward_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code, flags)
     if n == (1 << 64) - 1:
         raise ValueError("invalid arguments for osdn_forward")
     return int(n)
 
 
-def forward_path(B, H, T, dk, dv, chunk, dtype_code, precond=True, workspace_bytes=0) -> str:
-    flags = 0 if precond else _lib.OSDN_PRECOND_OFF
+def forward_path(B, H, T, dk, dv, chunk, dtype_code, precond=True, workspace_bytes=0,
+                 per_channel=False) -> str:
+    flags = ((0 if precond else _lib.OSDN_PRECOND_OFF)
+             | (_lib.OSDN_GATE_PER_CHANNEL if per_channel else 0))
     return _lib.load().osdn_forward_path(B, H, T, dk, dv, chunk, dtype_code, flags,
                                          int(workspace_bytes)).decode()
 
@@ -203,7 +210,9 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond
     them).
 
     ``alpha`` [B,H,T] fp32 is the optional state gate (Gated DeltaNet backbone;
-    with precond=False, Gated DeltaNet itself).
+    with precond=False, Gated DeltaNet itself); [B,H,T,dk] is the per-channel
+    gate, one per key dimension (Kimi Delta Attention backbone), which runs on
+    the two-phase path.
 
     ``out`` may pass preallocated outputs (same keys) to keep the call free of
     allocations.  ``workspace``: True allocates the scratch of the fastest path
@@ -221,11 +230,13 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond
     dv = v.shape[3]
     _dev(beta, "beta", (B, H, T), torch.float32, dev)
     _dev(r, "r", (B, H, T), torch.float32, dev)
-    _dev(alpha, "alpha", (B, H, T), torch.float32, dev)
+    chan = alpha is not None and alpha.dim() == 4
+    _dev(alpha, "alpha", (B, H, T, dk) if chan else (B, H, T), torch.float32, dev)
     _dev(d0, "d0", (B, H, dk), torch.float32, dev)
     _dev(S0, "S0", (B, H, dv, dk), torch.float32, dev)
     code = _dtype_code(q)
-    flags = (0 if precond else _lib.OSDN_PRECOND_OFF) | _transform_flags(norm_qk, gate_logits)
+    flags = ((0 if precond else _lib.OSDN_PRECOND_OFF) | _transform_flags(norm_qk, gate_logits)
+             | (_lib.OSDN_GATE_PER_CHANNEL if chan else 0))
     if out is None:
         out = {
             "o": torch.empty_like(v),
@@ -234,9 +245,9 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond
                         if precond else None),
             "log_ratio_sum": torch.empty((B, H), dtype=torch.float32, device=dev),
         }
-    single = forward_path(B, H, T, dk, dv, chunk, code, precond) == "fused"
+    single = forward_path(B, H, T, dk, dv, chunk, code, precond, per_channel=chan) == "fused"
     if workspace is True or (workspace is None and not single):
-        need = forward_workspace_bytes(B, H, T, dk, dv, chunk, code, precond)
+        need = forward_workspace_bytes(B, H, T, dk, dv, chunk, code, precond, per_channel=chan)
         workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.load().osdn_forward(

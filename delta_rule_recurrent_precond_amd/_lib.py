@@ -25,6 +25,7 @@ OSDN_F32 = 1
 OSDN_PRECOND_OFF = 1
 OSDN_NORM_QK = 2
 OSDN_GATE_LOGITS = 4
+OSDN_GATE_PER_CHANNEL = 8
 
 _lib = None
 _lock = threading.Lock()

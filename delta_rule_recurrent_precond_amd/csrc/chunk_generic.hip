@@ -17,6 +17,13 @@
 // (gamma_L / gamma_s) x_s kt_s^T.  Decay ratios are 2^(lg_t - lg_s) with lg the
 // running sum of log2 alpha (clamped at -126 per token, so a zero gate gives
 // 2^-126 rather than an infinite logarithm).
+// With the per-channel gate (GK: alpha [T][DK], S_t = S_{t-1} diag(alpha_t) +
+// x_t kt_t^T) the decays are per key dimension i, 2^(lg_t,i - lg_s,i): they
+// enter every sum over i term by term (A_ts = beta_t sum_i k_ti kt_si
+// 2^(lg_ti - lg_si), the residual and the output read S (g_t (.) k_t) and
+// S (g_t (.) q_t), and S_ji <- 2^lg_Li S_ji + sum_s 2^(lg_Li - lg_si) x_sj kt_si).
+// Each exponent is a difference of running sums with s <= t, so it never
+// exceeds zero.
 // This is the correctness path (used for fp32 data and for shapes the
 // matrix-core kernel does not cover).  One workgroup per (b, h, dv tile),
 // serial over chunks, everything of a chunk staged in LDS as fp32.
@@ -29,7 +36,7 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <typename T, int DK, int DVT, int C>
+template <typename T, int DK, int DVT, int C, bool GK>
 __global__ void __launch_bounds__(kThreads)
 chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ kt,
               const T *__restrict__ v, const float *__restrict__ beta,
@@ -49,6 +56,7 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
   __shared__ float sV[C * DVT];
   __shared__ float sB[C];
   __shared__ float sLg[C];        // running sum of log2 alpha within the chunk
+  __shared__ float sLgk[GK ? C * DK : 1];  // GK: the same per key dimension, [t][i]
 
   const int tid = threadIdx.x;
   const long bh = blockIdx.x;
@@ -87,7 +95,15 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       const float bv = t < L ? beta[tok0 + c0 + t] : 0.0f;
       sB[t] = (t < L && (xf & kGateLogits)) ? sigmoid_gate(bv) : bv;
     }
-    if (tid == 0) {
+    if (GK) {
+      for (int i = tid; i < DK; i += kThreads) {
+        float acc = 0.0f;
+        for (int t = 0; t < C; ++t) {
+          if (t < L) acc += fmaxf(log2f(alpha[(tok0 + c0 + t) * DK + i]), -126.0f);
+          sLgk[t * DK + i] = acc;
+        }
+      }
+    } else if (tid == 0) {
       float acc = 0.0f;
       for (int t = 0; t < C; ++t) {
         if (alpha && t < L) acc += fmaxf(log2f(alpha[tok0 + c0 + t]), -126.0f);
@@ -106,17 +122,27 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       const int t = idx / C, s = idx % C;
       float acc = 0.0f;
       if (s < t) {
-        for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sKt[s * DKP + i];
-        acc *= sB[t];
-        if (alpha) acc *= exp2f(sLg[t] - sLg[s]);
+        if (GK) {
+          for (int i = 0; i < DK; ++i)
+            acc += sK[t * DKP + i] * sKt[s * DKP + i] * exp2f(sLgk[t * DK + i] - sLgk[s * DK + i]);
+          acc *= sB[t];
+        } else {
+          for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sKt[s * DKP + i];
+          acc *= sB[t];
+          if (alpha) acc *= exp2f(sLg[t] - sLg[s]);
+        }
       }
       sA[t * CP + s] = acc;
     }
     for (int idx = tid; idx < C * DVT; idx += kThreads) {
       const int t = idx / DVT, j = idx % DVT;
       float acc = 0.0f;
-      for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sS[j * DKP + i];
-      if (alpha) acc *= exp2f(sLg[t]);
+      if (GK) {
+        for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * exp2f(sLgk[t * DK + i]) * sS[j * DKP + i];
+      } else {
+        for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sS[j * DKP + i];
+        if (alpha) acc *= exp2f(sLg[t]);
+      }
       sX[t * XP + j] = sB[t] * (sV[idx] - acc);
     }
     __syncthreads();
@@ -151,8 +177,13 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       const int t = idx / C, s = idx % C;
       float acc = 0.0f;
       if (s <= t) {
-        for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sKt[s * DKP + i];
-        if (alpha) acc *= exp2f(sLg[t] - sLg[s]);
+        if (GK) {
+          for (int i = 0; i < DK; ++i)
+            acc += sK[t * DKP + i] * sKt[s * DKP + i] * exp2f(sLgk[t * DK + i] - sLgk[s * DK + i]);
+        } else {
+          for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sKt[s * DKP + i];
+          if (alpha) acc *= exp2f(sLg[t] - sLg[s]);
+        }
       }
       sA[t * CP + s] = acc;
     }
@@ -163,8 +194,13 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       const int t = idx / DVT, j = idx % DVT;
       if (t < L) {
         float acc = 0.0f;
-        for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sS[j * DKP + i];
-        if (alpha) acc *= exp2f(sLg[t]);
+        if (GK) {
+          for (int i = 0; i < DK; ++i)
+            acc += sK[t * DKP + i] * exp2f(sLgk[t * DK + i]) * sS[j * DKP + i];
+        } else {
+          for (int i = 0; i < DK; ++i) acc += sK[t * DKP + i] * sS[j * DKP + i];
+          if (alpha) acc *= exp2f(sLg[t]);
+        }
         for (int s = 0; s <= t; ++s) acc += sA[t * CP + s] * sX[s * XP + j];
         Elem<T>::store(o + (tok0 + c0 + t) * (long)dv + j0 + j, acc);
       }
@@ -175,7 +211,12 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
     for (int idx = tid; idx < DVT * DK; idx += kThreads) {
       const int j = idx / DK, i = idx % DK;
       float acc = sS[j * DKP + i];
-      if (alpha) {
+      if (GK) {
+        const float lgL = sLgk[(L - 1) * DK + i];
+        acc *= exp2f(lgL);
+        for (int s = 0; s < L; ++s)
+          acc += exp2f(lgL - sLgk[s * DK + i]) * sX[s * XP + j] * sKt[s * DKP + i];
+      } else if (alpha) {
         const float lgL = sLg[L - 1];
         acc *= exp2f(lgL);
         for (int s = 0; s < L; ++s) acc += exp2f(lgL - sLg[s]) * sX[s * XP + j] * sKt[s * DKP + i];
@@ -195,12 +236,12 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
   }
 }
 
-template <typename T, int DK, int DVT>
+template <typename T, int DK, int DVT, bool GK>
 hipError_t launch_c(const ChunkArgs &a, hipStream_t s, dim3 grid) {
   const dim3 block(kThreads);
 #define OSDN_GEN_CASE(C_)                                                                      \
   case C_:                                                                                     \
-    hipLaunchKernelGGL((chunk_generic<T, DK, DVT, C_>), grid, block, 0, s, (const T *)a.q,   \
+    hipLaunchKernelGGL((chunk_generic<T, DK, DVT, C_, GK>), grid, block, 0, s, (const T *)a.q, \
                        (const T *)a.k, (const T *)a.k_tilde, (const T *)a.v, a.beta, a.alpha,\
                        a.S0,                                                                   \
                        a.T, a.dv, (T *)a.o, a.S_final, a.xf);                                 \
@@ -216,22 +257,29 @@ hipError_t launch_c(const ChunkArgs &a, hipStream_t s, dim3 grid) {
   return hipGetLastError();
 }
 
-template <typename T, int DVT>
+template <typename T, int DVT, bool GK>
 hipError_t launch_dk(const ChunkArgs &a, hipStream_t s, dim3 grid) {
   switch (a.dk) {
-    case 16: return launch_c<T, 16, DVT>(a, s, grid);
-    case 32: return launch_c<T, 32, DVT>(a, s, grid);
-    case 64: return launch_c<T, 64, DVT>(a, s, grid);
-    case 128: return launch_c<T, 128, DVT>(a, s, grid);
+    case 16: return launch_c<T, 16, DVT, GK>(a, s, grid);
+    case 32: return launch_c<T, 32, DVT, GK>(a, s, grid);
+    case 64: return launch_c<T, 64, DVT, GK>(a, s, grid);
+    case 128: return launch_c<T, 128, DVT, GK>(a, s, grid);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
-hipError_t launch_t(const ChunkArgs &a, hipStream_t s) {
+template <typename T, bool GK>
+hipError_t launch_g(const ChunkArgs &a, hipStream_t s) {
   const int dvt = a.dv >= 32 ? 32 : 16;
   const dim3 grid((unsigned)(a.B * a.H), (unsigned)(a.dv / dvt));
-  return dvt == 32 ? launch_dk<T, 32>(a, s, grid) : launch_dk<T, 16>(a, s, grid);
+  return dvt == 32 ? launch_dk<T, 32, GK>(a, s, grid) : launch_dk<T, 16, GK>(a, s, grid);
+}
+
+// the per-channel gate takes its own instances (a [C][DK] table of decays)
+template <typename T>
+hipError_t launch_t(const ChunkArgs &a, hipStream_t s) {
+  if ((a.xf & kGateChannels) && a.alpha) return launch_g<T, true>(a, s);
+  return launch_g<T, false>(a, s);
 }
 
 }  // namespace

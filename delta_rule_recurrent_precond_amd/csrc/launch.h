@@ -7,10 +7,10 @@
 
 namespace osdn {
 
-// Bits of the input-transform flags the kernels take (the ABI's values):
-// q, k arrive unnormalised; beta, r arrive as logits; and (internal) the given
-// write keys are the unnormalised keys themselves.
-constexpr unsigned kNormQK = 2u, kGateLogits = 4u, kNormKt = 8u;
+// Bits of the flags the kernels take: q, k arrive unnormalised; beta, r arrive
+// as logits; (internal) the given write keys are the unnormalised keys
+// themselves; alpha holds one gate per key dimension.
+constexpr unsigned kNormQK = 2u, kGateLogits = 4u, kNormKt = 8u, kGateChannels = 16u;
 
 struct ScanArgs {
   const void *k;

@@ -45,20 +45,29 @@ size_t two_phase_bytes(int B, int H, int T, int dk, int dtype, unsigned flags) {
 // Scratch that selects the fastest path: the split pipeline on the shapes of
 // the matrix-core kernels, else what the two-launch path needs.
 size_t ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype, unsigned flags) {
-  if (use_fused(dk, dv, chunk, dtype)) return osdn::split_forward_workspace_bytes(B, H, T);
+  if (use_fused(dk, dv, chunk, dtype) && !(flags & OSDN_GATE_PER_CHANNEL))
+    return osdn::split_forward_workspace_bytes(B, H, T);
   return two_phase_bytes(B, H, T, dk, dtype, flags);
 }
 
-constexpr unsigned kFlags = OSDN_PRECOND_OFF | OSDN_NORM_QK | OSDN_GATE_LOGITS;
-// the kernels' transform bits from the ABI flags
+constexpr unsigned kFlags =
+    OSDN_PRECOND_OFF | OSDN_NORM_QK | OSDN_GATE_LOGITS | OSDN_GATE_PER_CHANNEL;
+// the kernels' bits from the ABI flags
 unsigned transforms(unsigned flags) {
   return (flags & OSDN_NORM_QK ? osdn::kNormQK : 0u) |
-         (flags & OSDN_GATE_LOGITS ? osdn::kGateLogits : 0u);
+         (flags & OSDN_GATE_LOGITS ? osdn::kGateLogits : 0u) |
+         (flags & OSDN_GATE_PER_CHANNEL ? osdn::kGateChannels : 0u);
 }
 
-bool split_ok(int B, int H, int T, int dk, int dv, int chunk, int dtype, size_t workspace_bytes,
-              const void *workspace) {
-  return use_fused(dk, dv, chunk, dtype) && workspace &&
+// the matrix-core kernels (split pipeline or single fused kernel) take the call;
+// the per-channel gate runs on the two-phase path
+bool matrix_core(int dk, int dv, int chunk, int dtype, unsigned flags) {
+  return use_fused(dk, dv, chunk, dtype) && !(flags & OSDN_GATE_PER_CHANNEL);
+}
+
+bool split_ok(int B, int H, int T, int dk, int dv, int chunk, int dtype, unsigned flags,
+              size_t workspace_bytes, const void *workspace) {
+  return matrix_core(dk, dv, chunk, dtype, flags) && workspace &&
          workspace_bytes >= osdn::split_forward_workspace_bytes(B, H, T);
 }
 
@@ -106,9 +115,11 @@ OSDN_EXPORT int osdn_step(const void *q, const void *k, const void *v, const flo
                           float *log_ratio, void *stream) {
   int st = check_sizes(B, H, 1, dk, dv, 16, dtype, true, false);
   if (st != OSDN_OK) return st;
-  if (flags & ~(OSDN_NORM_QK | OSDN_GATE_LOGITS)) return OSDN_ERR_UNSUPPORTED;
+  if (flags & ~(OSDN_NORM_QK | OSDN_GATE_LOGITS | OSDN_GATE_PER_CHANNEL))
+    return OSDN_ERR_UNSUPPORTED;
   if ((long long)B * H == 0) return OSDN_OK;
   if (!q || !k || !v || !beta || !S || !d || !o) return OSDN_ERR_NULL;
+  if ((flags & OSDN_GATE_PER_CHANNEL) && !alpha) return OSDN_ERR_NULL;
   osdn::StepArgs a{q, k, v, beta, r, alpha, eta, B, H, dk, dv, dtype, S, d, o, log_ratio,
                    transforms(flags)};
   return hip_status(osdn::launch_step(a, (hipStream_t)stream));
@@ -153,9 +164,9 @@ OSDN_EXPORT const char *osdn_forward_path(int B, int H, int T, int dk, int dv, i
   if (flags & ~kFlags) return "invalid";
   if ((long long)B * H == 0) return "none";
   const float one = 1.0f;
-  if (split_ok(B, H, T, dk, dv, chunk, dtype, workspace_bytes, &one))
+  if (split_ok(B, H, T, dk, dv, chunk, dtype, flags, workspace_bytes, &one))
     return "split";
-  if (!use_fused(dk, dv, chunk, dtype)) return "two-phase";
+  if (!matrix_core(dk, dv, chunk, dtype, flags)) return "two-phase";
   return transforms(flags) ? "unsupported" : "fused";
 }
 
@@ -168,19 +179,20 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   if (st != OSDN_OK) return st;
   if (flags & ~kFlags) return OSDN_ERR_UNSUPPORTED;
   const unsigned xf = transforms(flags);
+  const bool mc = matrix_core(dk, dv, chunk, dtype, flags);
   // the single fused kernel takes its inputs prepared
-  if (xf && use_fused(dk, dv, chunk, dtype) &&
-      !split_ok(B, H, T, dk, dv, chunk, dtype, workspace_bytes, workspace))
+  if (xf && mc && !split_ok(B, H, T, dk, dv, chunk, dtype, flags, workspace_bytes, workspace))
     return OSDN_ERR_UNSUPPORTED;
   if ((long long)B * H == 0) return OSDN_OK;
   if (T > 0 && (!q || !k || !v || !beta || !o)) return OSDN_ERR_NULL;
+  if (T > 0 && (flags & OSDN_GATE_PER_CHANNEL) && !alpha) return OSDN_ERR_NULL;
   const bool off = (flags & OSDN_PRECOND_OFF) != 0;
   hipStream_t s = (hipStream_t)stream;
 
-  if (use_fused(dk, dv, chunk, dtype)) {
+  if (mc) {
     osdn::FusedArgs a{q, k, v, beta, r, alpha, d0, S0, eta, B, H, T, dk, dv, chunk, dtype,
                       off ? 1 : 0, o, S_final, d_final, log_ratio_sum, xf};
-    if (split_ok(B, H, T, dk, dv, chunk, dtype, workspace_bytes, workspace))
+    if (split_ok(B, H, T, dk, dv, chunk, dtype, flags, workspace_bytes, workspace))
       return hip_status(osdn::launch_split_forward(a, workspace, s));
     return hip_status(osdn::launch_fused_forward(a, s));
   }
@@ -190,22 +202,23 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   const size_t need = two_phase_bytes(B, H, T, dk, dtype, flags);
   if (need > 0 && (!workspace || workspace_bytes < need)) return OSDN_ERR_WORKSPACE;
   const void *kt = k;
+  const unsigned sxf = xf & (osdn::kNormQK | osdn::kGateLogits);  // what the walk transforms
   if (!off) {
     osdn::ScanArgs sa{k, beta, r, d0, eta, B, H, T, dk, dtype, 0, workspace,
-                      d_final, nullptr, nullptr, log_ratio_sum, xf};
-    st = hip_status(osdn::fused_scan_supported(dk, dtype) && !xf
+                      d_final, nullptr, nullptr, log_ratio_sum, sxf};
+    st = hip_status(osdn::fused_scan_supported(dk, dtype) && !sxf
                         ? osdn::launch_fused_scan(sa, s)
                         : osdn::launch_precond_scan_serial(sa, s));
     if (st != OSDN_OK) return st;
     kt = workspace;
   } else if (log_ratio_sum) {
     osdn::ScanArgs sa{k, beta, nullptr, nullptr, 0.0f, B, H, T, dk, dtype, 1, nullptr,
-                      nullptr, nullptr, nullptr, log_ratio_sum, xf};
+                      nullptr, nullptr, nullptr, log_ratio_sum, sxf};
     st = hip_status(osdn::launch_precond_scan_serial(sa, s));
     if (st != OSDN_OK) return st;
   }
   // with kt = k (the delta rule) unnormalised keys are normalised on both sides
   osdn::ChunkArgs ca{q, k, kt, v, beta, alpha, S0, B, H, T, dk, dv, chunk, dtype, o, S_final,
                      xf | (off && (xf & osdn::kNormQK) ? osdn::kNormKt : 0u)};
-  return hip_status(osdn::launch_chunk_generic(ca, s));  // only shapes the fused kernel lacks
+  return hip_status(osdn::launch_chunk_generic(ca, s));
 }

@@ -7,7 +7,8 @@
 // §2.3 (APF retention r), §3 (rho = (1 - beta a)^2) and the persistent (S, d)
 // state the efficiency claims rest on.  For one token:
 //   a = <d, k (.) k>,  n = ||k||^2,  kt = d (.) k
-//   S <- alpha S (optional state gate, Gated DeltaNet's decay)
+//   S <- alpha S (optional state gate, Gated DeltaNet's decay), or
+//   S <- S diag(alpha) (per-channel gate, one per key dimension: KDA's decay)
 //   u = v - S k,  S <- S + beta u kt^T,  o = S q (after the write)
 //   rho = (1 - beta a)^2,  d <- r d + eta beta (1 - beta a) (k (.) k) / n  (0 if n = 0)
 //
@@ -39,7 +40,8 @@ osdn_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long bh = blockIdx.x;
   const float bt = (xf & kGateLogits) ? sigmoid_gate(beta[bh]) : beta[bh];
-  const float at = alpha ? alpha[bh] : 1.0f;  // state gate
+  const bool chan = (xf & kGateChannels) != 0;
+  const float at = (alpha && !chan) ? alpha[bh] : 1.0f;  // scalar state gate
 
   // key statistics and the write key (fp32), one thread per dimension
   float pn = 0.f, pa = 0.f, kv = 0.f, qv = 0.f, dv_ = 0.f;
@@ -97,10 +99,12 @@ osdn_step_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   const float4 kc = *(const float4 *)&k_s[c4];
   const float4 ktc = *(const float4 *)&kt_s[c4];
   const float4 qc = *(const float4 *)&q_s[c4];
+  // gates of this thread's four columns
+  const float4 ac = chan ? *(const float4 *)(alpha + bh * DK + c4) : float4{at, at, at, at};
   for (int j = tid / TPR; j < dv; j += RPP) {
     float *row = S + (bh * dv + j) * DK + c4;
     float4 s = *(const float4 *)row;
-    s.x *= at, s.y *= at, s.z *= at, s.w *= at;
+    s.x *= ac.x, s.y *= ac.y, s.z *= ac.z, s.w *= ac.w;
     float sk = s.x * kc.x + s.y * kc.y + s.z * kc.z + s.w * kc.w;
     sk = group_sum<TPR>(sk);
     const float u = coef[0] * (Elem<T>::load(v + bh * dv + j) - sk);  // beta (v_j - (S k)_j)

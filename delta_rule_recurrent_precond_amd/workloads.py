@@ -8,7 +8,7 @@ q/k/v are cast once (round-to-nearest-even) to the stored dtype.  Those stored
 bits are the inputs of every implementation.
 
 Draw order per seed: q, k, v, beta-logits, r-logits, alpha-logits (state
-gate, gated workloads only).  Raw workloads skip the normalisation and the
+gate, gated workloads only; one per key dimension for the per-channel gate).  Raw workloads skip the normalisation and the
 sigmoids (the same draws, so their transforms give the plain workload's values
 before rounding).  The recall workload draws its key pool, value
 pool and index sequence first.
@@ -48,6 +48,7 @@ class Workload:
     gated: bool = False   # state gate alpha present (Gated DeltaNet backbone)
     alpha_mu: float = 3.0
     alpha_sigma: float = 1.0
+    gate_channels: bool = False  # with gated: one gate per key dimension (KDA backbone)
     raw: bool = False     # q, k not normalised and beta, r as logits (the kernels transform them)
 
     @property
@@ -79,6 +80,11 @@ RECALL_APF = replace(RECALL_VANILLA, name="recall x2 APF B2 H16 T16384 d128 C64 
 L13B_APF_GATED = replace(L13B_APF, name="1.3B-layer APF gated B4 H16 T4096 d128 C64 bf16",
                          gated=True)
 
+# The same layer on the Kimi Delta Attention backbone: one gate per key
+# dimension, alpha[..., i] = sigmoid(3 + N(0,1)) drawn independently.
+L13B_APF_KDA = replace(L13B_APF, name="1.3B-layer APF per-channel gate B4 H16 T4096 d128 C64 bf16",
+                       gated=True, gate_channels=True)
+
 CONFIGS = {
     "tiny": TINY_F32,
     "340m": L340M_VANILLA,
@@ -87,6 +93,7 @@ CONFIGS = {
     "recall": RECALL_VANILLA,
     "recall-apf": RECALL_APF,
     "1.3b-apf-gated": L13B_APF_GATED,
+    "1.3b-apf-kda": L13B_APF_KDA,
 }
 
 # The throughput metric is quoted on the 1.3B-style layer (H=16, dk=dv=128, T=4096).
@@ -128,7 +135,7 @@ class Inputs:
     r: Optional[torch.Tensor]  # [B,H,T] fp32 or None (no APF)
     eta: float
     workload: Workload
-    alpha: Optional[torch.Tensor] = None  # [B,H,T] fp32 state gate or None
+    alpha: Optional[torch.Tensor] = None  # [B,H,T] (or [B,H,T,dk]) fp32 state gate or None
 
     def to(self, device):
         mv = lambda t: None if t is None else t.to(device)
@@ -162,7 +169,8 @@ def generate(w: Workload, seed: Optional[int] = None) -> Inputs:
     gate = (lambda x: x) if w.raw else _sigmoid
     beta = gate(w.beta_mu + w.beta_sigma * rng.standard_normal((B, H, T)))
     r = gate(w.r_mu + w.r_sigma * rng.standard_normal((B, H, T))) if w.apf else None
-    alpha = (_sigmoid(w.alpha_mu + w.alpha_sigma * rng.standard_normal((B, H, T)))
+    gshape = (B, H, T, dk) if w.gate_channels else (B, H, T)
+    alpha = (_sigmoid(w.alpha_mu + w.alpha_sigma * rng.standard_normal(gshape))
              if w.gated else None)
     f32 = lambda x: None if x is None else torch.from_numpy(x).to(torch.float32)
     return Inputs(_store(q, w.dtype), _store(k, w.dtype), _store(v, w.dtype), f32(beta), f32(r),

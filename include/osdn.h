@@ -48,6 +48,13 @@
  *    alpha acts on S only; the preconditioner walk does not see it.  alpha = 1
  *    gives the ungated results; alpha in [0, 1] is the intended range (decays
  *    below 2^-126 over a chunk are flushed to zero).
+ *  - Per-channel gate (osdn_forward, osdn_step with OSDN_GATE_PER_CHANNEL):
+ *    alpha is [B][H][T][dk] fp32 (step: [B][H][dk]), one gate per key
+ *    dimension.  The pages also run OSDN on a Kimi Delta Attention backbone
+ *    [summary §4] without printing its update; the reading used here
+ *    generalises the scalar gate:
+ *      S_t = S_{t-1} D_t + beta_t (v_t - S_{t-1} D_t k_t) kt_t^T,  D_t = diag(alpha_t),
+ *    i.e. column i of S (key dimension i) decays by alpha_t[i].
  *  - Results are deterministic run to run (no floating-point atomics).
  *  - Non-finite inputs propagate; they are not checked.
  */
@@ -86,6 +93,12 @@ extern "C" {
  * single fused kernel would run it returns OSDN_ERR_UNSUPPORTED. */
 #define OSDN_NORM_QK 2u
 #define OSDN_GATE_LOGITS 4u
+
+/* osdn_forward, osdn_step flag: alpha holds one gate per key dimension (the
+ * per-channel gate above; required with this flag).  osdn_forward runs it on
+ * the two-phase path for every supported shape, which needs the workspace
+ * osdn_forward_workspace_bytes reports for these flags. */
+#define OSDN_GATE_PER_CHANNEL 8u
 
 /*
  * Phase 1: the preconditioner scan over the key stream [summary §2.2 phase 1,
@@ -155,7 +168,8 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  * Both phases end to end [summary §2.2 two-phase implementation].
  *   q, k, v, beta, r, alpha, d0, S0, eta   as above; with OSDN_PRECOND_OFF and
  *                  alpha this is Gated DeltaNet itself
- *   flags          OSDN_PRECOND_OFF, OSDN_NORM_QK, OSDN_GATE_LOGITS, or'd
+ *   flags          OSDN_PRECOND_OFF, OSDN_NORM_QK, OSDN_GATE_LOGITS,
+ *                  OSDN_GATE_PER_CHANNEL, or'd
  *   o              [B,H,T,dv] dtype out (required if T > 0)
  *   S_final        [B,H,dv,dk] fp32 out (optional)
  *   d_final        [B,H,dk] fp32 out (optional)
@@ -193,7 +207,7 @@ int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
  *   d         [B,H,dk] fp32      preconditioner, read and updated in place (required)
  *   o         [B,H,dv] dtype     out: the readout (required)
  *   log_ratio [B,H]    fp32      out: log rho (optional)
- *   flags     0, OSDN_NORM_QK, OSDN_GATE_LOGITS, or'd (the transforms above)
+ *   flags     0, OSDN_NORM_QK, OSDN_GATE_LOGITS, OSDN_GATE_PER_CHANNEL, or'd
  * S, d and o must not overlap each other or the inputs.
  */
 int osdn_step(const void *q, const void *k, const void *v, const float *beta, const float *r,

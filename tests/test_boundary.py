@@ -68,7 +68,8 @@ def _fwd(lib, B=1, H=1, T=4, dk=16, dv=16, chunk=16, dtype=0, flags=0, ptr=1):
     (dict(chunk=128), _lib.OSDN_ERR_UNSUPPORTED),
     (dict(chunk=0), _lib.OSDN_ERR_UNSUPPORTED),
     (dict(dtype=7), _lib.OSDN_ERR_UNSUPPORTED),
-    (dict(flags=8), _lib.OSDN_ERR_UNSUPPORTED),
+    (dict(flags=16), _lib.OSDN_ERR_UNSUPPORTED),
+    (dict(flags=8), _lib.OSDN_ERR_NULL),   # the per-channel gate needs alpha
     (dict(ptr=None), _lib.OSDN_ERR_NULL),
     (dict(B=1 << 30, H=1 << 10), _lib.OSDN_ERR_SHAPE),
 ])
@@ -173,5 +174,20 @@ def test_transform_flags(lib):
     assert lib.osdn_forward_path(1, 1, 64, 64, 64, 64, 1, 7, 0).decode() == "two-phase"
     assert _fwd(lib, B=1, H=1, T=64, dk=128, dv=128, chunk=64, flags=2) == _lib.OSDN_ERR_UNSUPPORTED
     assert lib.osdn_forward_workspace_bytes(1, 1, 64, 128, 128, 64, 0, 7) > 0
-    assert lib.osdn_step(1, 1, 1, 1, None, None, 0.1, 1, 1, 16, 16, 0, 8, 1, 1, 1, None,
+    assert lib.osdn_step(1, 1, 1, 1, None, None, 0.1, 1, 1, 16, 16, 0, 16, 1, 1, 1, None,
                          None) == _lib.OSDN_ERR_UNSUPPORTED
+
+
+def test_per_channel_gate_flag(lib):
+    """OSDN_GATE_PER_CHANNEL: the two-phase path for every shape (the matrix-core
+    kernels do not take it), its workspace is the write-key buffer, and alpha is
+    required (validated before any launch)."""
+    PC = _lib.OSDN_GATE_PER_CHANNEL
+    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, PC, 1 << 40).decode() == "two-phase"
+    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, PC | 1, 0).decode() == "two-phase"
+    assert lib.osdn_forward_path(1, 1, 64, 32, 16, 16, 1, PC | 6, 0).decode() == "two-phase"
+    assert lib.osdn_forward_workspace_bytes(2, 3, 100, 128, 128, 64, 0, PC) == 2 * 3 * 100 * 128 * 2
+    assert lib.osdn_forward_workspace_bytes(2, 3, 100, 128, 128, 64, 0, PC | 1) == 0
+    assert _fwd(lib, B=1, H=1, T=64, dk=128, dv=128, chunk=64, flags=PC) == _lib.OSDN_ERR_NULL
+    assert lib.osdn_step(1, 1, 1, 1, None, None, 0.1, 1, 1, 16, 16, 0, PC, 1, 1, 1, None,
+                         None) == _lib.OSDN_ERR_NULL
