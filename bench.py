@@ -126,13 +126,22 @@ def bench_step(args, torch, osdn, W):
     o = torch.empty_like(tok[2])
     ms = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S, d, tok[4],
                                            eta=w.eta, o=o), args.steps, args.warmup, torch)
+    # the same step with one state gate per key dimension
+    ach = W.generate(dataclasses.replace(w, gated=True, gate_channels=True)).alpha[:, :, 0]
+    ach = ach.contiguous().to("cuda")
+    ms_ch = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S, d, tok[4],
+                                              eta=w.eta, o=o, alpha=ach),
+                          args.steps, args.warmup, torch)
     heads = w.B * w.H
     # S read and written (fp32), d read and written, q, k, v read and o written
     # (bf16), beta and r read
     nbytes = heads * (2 * w.dv * w.dk * 4 + 2 * w.dk * 4 + (2 * w.dk + 2 * w.dv) * 2 + 8)
     return {"workload": w.name, "ms": ms, "tokens_per_s": w.B / (ms * 1e-3),
             "algorithmic_bytes": nbytes,
-            "hbm_frac": nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+            "hbm_frac": nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "per_channel_gate": {"ms": ms_ch,
+                                 "hbm_frac": (nbytes + heads * w.dk * 4) / (ms_ch * 1e-3)
+                                 / (HBM_PEAK_GBS * 1e9)}}
 
 
 def gpu_clocks():
@@ -238,6 +247,27 @@ def main():
         ms_raw = time_launches(fwd_raw, args.steps, args.warmup, torch)
         ms_raw_sep = time_launches(lambda i: fwd_raw(i, False), args.steps, args.warmup, torch)
         del raws
+        # the per-channel gate (KDA backbone): the same draws with one gate per key
+        # dimension, on the two-phase path
+        kda_alpha = W.generate(dataclasses.replace(w, gated=True, gate_channels=True)).alpha
+        kalphas = [kda_alpha.to("cuda") for _ in range(2)]
+        del kda_alpha
+        kws_n = osdn.forward_workspace_bytes(B, H, T, dk, dv, C, code, per_channel=True)
+        kws = torch.empty(max(kws_n, 1), dtype=torch.uint8, device="cuda")
+        kda_path = osdn.forward_path(B, H, T, dk, dv, C, code, per_channel=True,
+                                     workspace_bytes=kws_n)
+
+        def fwd_kda(i, precond=True):
+            d = devs[i % copies]
+            o = outs[i % copies]
+            osdn.forward(d.q, d.k, d.v, d.beta, d.r, eta=d.eta, chunk=C, precond=precond,
+                         alpha=kalphas[i % 2], out=o if precond else {**o, "d_final": None},
+                         workspace=kws)
+
+        kda_steps = max(2, args.steps // 4)
+        ms_kda = time_launches(fwd_kda, kda_steps, 1, torch)
+        ms_kda_dn = time_launches(lambda i: fwd_kda(i, False), kda_steps, 1, torch)
+        del kalphas, kws
         kts = [torch.empty_like(d.k) for d in devs]
         dfin = torch.empty((B, H, dk), dtype=torch.float32, device="cuda")
         lib = osdn.load()
@@ -305,6 +335,10 @@ def main():
             "raw_inputs_transforms_in_kernels": {
                 "ms": ms_raw, "tokens_per_s": tokens / (ms_raw * 1e-3),
                 "traffic": stored_traffic("osdn_forward_raw_split", args.workload)},
+            "per_channel_gate_forward": {"ms": ms_kda, "tokens_per_s": tokens / (ms_kda * 1e-3),
+                                         "path": kda_path, "steps": kda_steps},
+            "per_channel_gate_deltanet_mode": {"ms": ms_kda_dn,
+                                               "tokens_per_s": tokens / (ms_kda_dn * 1e-3)},
             "raw_inputs_separate_torch_passes": {"ms": ms_raw_sep,
                                                  "tokens_per_s": tokens / (ms_raw_sep * 1e-3)},
             "two_launch_scan_share": ms_scan / (ms_scan + ms_chunk),

@@ -36,6 +36,24 @@
 //   A_ts and P_ts gain gamma_t / gamma_s, the rows of K S^T and Q S^T gamma_t,
 //   the S-update operand of token s gamma_L / gamma_s (applied to kt_s in fp32
 //   before its fp16 rounding), and S <- gamma_L S + ...
+//
+// With one gate per key dimension (GK; the Kimi Delta Attention backbone,
+// S_t = S_{t-1} diag(alpha_t) + beta_t (v_t - S_{t-1} diag(alpha_t) k_t) kt_t^T)
+// the decays g_t = prod_{m<=t} alpha_m are vectors and enter every sum over the
+// key dimension term by term:
+//   A_ts = beta_t <k_t (.) g_t, kt_s / g_s>,  P_ts = <q_t (.) g_t, kt_s / g_s>,
+//   K S^T -> (K (.) G) S^T,  Q S^T -> (Q (.) G) S^T,  S <- S diag(g_L) + X^T (Kt (.) g_L / G).
+// No ratio g_t / g_s is ever formed by division.  A and P are built from
+// products of alpha over the tokens between s and t:
+//   - a 16x16 tile below the diagonal (row block r > column block c) factors
+//     through the boundary of block r - 1, with both factors <= 1: the rows of
+//     block r take the product from the block's start to t, and the column
+//     operand takes the product from s + 1 to the end of block r - 1 (one
+//     operand copy per (r, c));
+//   - the diagonal 16x16 blocks are summed term by term on the vector ALU with
+//     a running product down the rows.
+// A zero gate therefore resets exactly.  The record then carries K (.) G and
+// Q (.) G (fp16, what the state kernel stages in place of k and q) and g_L.
 #include "device.h"
 #include "launch.h"
 #include "mfma.h"
@@ -60,6 +78,9 @@ constexpr size_t OFF_LR = 28676;  // kt = k: sum over the chunk of log rho_t
 constexpr size_t OFF_GL = 28680;  // gamma_L
 constexpr size_t OFF_SC = 28688;  // per-token factors of the K rows, then of the Q rows
 constexpr size_t OFF_KF = OFF_SC, OFF_QF = OFF_SC + 256, OFF_END = OFF_SC + 512;
+// the record with the per-channel gate: the above, then K (.) G and Q (.) G as
+// fp16 [64][128] row-major, then g_L fp32 [128]
+constexpr size_t OFF_KG = 32768, OFF_QG = 49152, OFF_GV = 65536, RECK = 66048;
 constexpr int LDT = 24;  // padded row (halves) of the 16x16 fp16 blocks in LDS
 constexpr int LDF = 20;  // padded row (floats) of the 16x16 fp32 blocks in LDS
 
@@ -81,9 +102,9 @@ constexpr int KP = 136;  // padded row (halves) of the staged [64][128] tiles
 // recurrence and the rows of A in fp32; for kt = k it is staged normalised.
 // The scales go to the record for the state kernel.  GATED: the state gate's
 // decays enter A, P and the S-update operands, and its row factors go to the
-// record.  xf & kGateLogits:
+// record.  GK: the per-channel gate, as described at the top.  xf & kGateLogits:
 // beta and r arrive as logits.
-template <int MODE, bool NORM, bool GATED>
+template <int MODE, bool NORM, bool GATED, bool GK>
 __global__ void __launch_bounds__(256)
 chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
            const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
@@ -104,6 +125,13 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   __shared__ float sk[C], sq[C];  // NORM: 1 / ||k_t||, 1 / ||q_t||
   __shared__ float lga[C];        // GATED: lg_t, the running sum of log2 alpha
   __shared__ float xdl[C];        // GATED: gamma_L / gamma_t
+  // GK: alpha [t][i] (fp32), later the column operands of the tiles below the
+  // diagonal (fp16, 6 tiles of 16 rows in off_tile order); the diagonal blocks
+  // of A and P (fp32 sums); the products of alpha over each 16-token block
+  __shared__ __align__(16) float Al[GK ? C * DK : 4];
+  __shared__ float Adg[GK ? 4 * 16 * LDF : 4], Pdg[GK ? 4 * 16 * LDF : 4];
+  __shared__ float Bk[GK ? 4 * DK : 4];
+  static_assert(!GK || 6 * 16 * KP * 2 <= C * DK * 4, "column operands fit in alpha's space");
   __shared__ float red[4];
 
   const int tid = threadIdx.x;
@@ -112,8 +140,9 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int bh = blockIdx.x / ncs, c = c0 + blockIdx.x % ncs;  // chunks c0 .. c0+ncs-1
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
-  unsigned char *rec = ws + ((long)bh * NC + c) * REC;
-  const f16 *Ktp = (MODE == kDeltaNet) ? Ks : Kts;
+  unsigned char *rec = ws + ((long)bh * NC + c) * (GK ? RECK : REC);
+  // the write keys (GK keeps a copy of k for kt = k: the rows of Ks are rescaled)
+  const f16 *Ktp = (MODE == kDeltaNet && !GK) ? Ks : Kts;
 
   // ---- loads: 1024 pieces of 8 elements per tensor, 4 per thread.  Rows past
   // the end reread the last row (a load under a condition would make the
@@ -143,6 +172,14 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     cs[tid] = tid < L ? wout[((long)bh * NC + c) * WOUT + DK + tid] : 0.f;
     const float rv = r ? r[tok0 + min(tid, L - 1)] : 1.0f;
     rs[tid] = (r && tid < L) ? ((xf & kGateLogits) ? sigmoid_gate(rv) : rv) : 1.0f;
+  }
+  if (GK) {  // alpha of the chunk; rows past the end are 1 (they change no product)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = tid + 256 * u, t = p >> 5, i4 = (p & 31) * 4;
+      const float4 a4 = *(const float4 *)(alpha + (tok0 + min(t, L - 1)) * DK + i4);
+      *(float4 *)&Al[t * DK + i4] = t < L ? a4 : float4{1.f, 1.f, 1.f, 1.f};
+    }
   }
   // per-token normalisation scales (16 threads per token hold its pieces)
   float kscale[4] = {1.f, 1.f, 1.f, 1.f}, qscale[4] = {1.f, 1.f, 1.f, 1.f};
@@ -208,11 +245,13 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       for (int e = 0; e < 8; ++e) hv[e] = h(bf2f(s[e]) * inv);
       *(f16x8 *)&Kts[t * KP + i0] = hv;
     }
+    if (GK && MODE == kDeltaNet)
+      *(f16x8 *)&Kts[t * KP + i0] = NORM ? cvt8s(rk[u], kscale[u]) : cvt8(rk[u]);
   }
   __syncthreads();
 
   // the state kernel's per-token factors
-  if ((NORM || GATED) && tid < C) {
+  if ((NORM || GATED) && !GK && tid < C) {
     float kf = NORM ? sk[tid] : 1.0f, qf = NORM ? sq[tid] : 1.0f;
     if (GATED) {
       const float gm = fexp2(lga[tid]), lgL = lga[C - 1];
@@ -260,6 +299,114 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     __syncthreads();
   }
 
+  if (GK) {
+    // (a) the diagonal blocks of A and P term by term: wave b takes block b, a
+    // lane column s = 16b + (lane & 15) and 32 key dimensions; e_i runs down the
+    // rows as the product of alpha_i over s+1 .. t (1 at t = s, 0 above it).
+    // The four lanes of a column add their partial sums.
+    const int b = wave, sl = lane & 15, i0 = 32 * (lane >> 4), s = 16 * b + sl;
+    float kts[32], e[32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16x8 v = ld8(&Kts[s * KP + i0 + 8 * j]);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        kts[8 * j + x] = (float)v[x];
+        e[8 * j + x] = 0.f;
+      }
+    }
+    for (int tl = 0; tl < 16; ++tl) {
+      const int t = 16 * b + tl;
+      float a = 0.f, pq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x8 kv = ld8(&Ks[t * KP + i0 + 8 * j]);
+        const f16x8 qv = ld8(&Qs[t * KP + i0 + 8 * j]);
+        const float4 a0 = *(const float4 *)&Al[t * DK + i0 + 8 * j];
+        const float4 a1 = *(const float4 *)&Al[t * DK + i0 + 8 * j + 4];
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int cc = 8 * j + x;
+          e[cc] = tl == sl ? 1.f : e[cc] * av[x];
+          const float w = kts[cc] * e[cc];
+          a = fmaf((float)kv[x], w, a);
+          pq = fmaf((float)qv[x], w, pq);
+        }
+      }
+      a += __shfl_xor(a, 16);
+      a += __shfl_xor(a, 32);
+      pq += __shfl_xor(pq, 16);
+      pq += __shfl_xor(pq, 32);
+      if (lane < 16) {
+        Adg[(16 * b + tl) * LDF + sl] = tl > sl ? a : 0.f;
+        Pdg[(16 * b + tl) * LDF + sl] = tl >= sl ? pq : 0.f;
+      }
+    }
+    // (b) per key dimension i (thread i, blocks 2hb and 2hb + 1): the products
+    // of alpha over each block, then
+    //   g_t = (product over the earlier blocks) * (product from the block start to t)
+    //   K (.) G and Q (.) G to the record; the rows of block r >= 1 of k and q
+    //   rescaled by the product from the block start to t (in place);
+    //   the column operand of tile (r, c): kt_s times the product over s+1 ..
+    //   end of block r-1; kt_s decayed to the chunk end (in place) for the S
+    //   update; g_L to the record.
+    const int i = tid & 127, hb = tid >> 7;
+    float av[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) av[u] = Al[(32 * hb + u) * DK + i];
+    float B0 = 1.f, B1 = 1.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      B0 *= av[u];
+      B1 *= av[16 + u];
+    }
+    Bk[(2 * hb) * DK + i] = B0;
+    Bk[(2 * hb + 1) * DK + i] = B1;
+    __syncthreads();  // alpha read everywhere (its space takes the column operands)
+    const float Bv[4] = {Bk[i], Bk[DK + i], Bk[2 * DK + i], Bk[3 * DK + i]};
+    f16 *KC = (f16 *)Al;
+    f16 *kg = (f16 *)(rec + OFF_KG), *qg = (f16 *)(rec + OFF_QG);
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int blk = 2 * hb + bb;
+      float G = 1.f, after = 1.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if (x < blk) G *= Bv[x];
+        if (x > blk) after *= Bv[x];
+      }
+      float pp = 1.f;
+      for (int tl = 0; tl < 16; ++tl) {
+        const int t = 16 * blk + tl;
+        pp *= av[16 * bb + tl];
+        const float g = G * pp;
+        const float kv = (float)Ks[t * KP + i], qv = (float)Qs[t * KP + i];
+        const float kh = (NORM && MODE == kOsdn) ? kv * sk[t] : kv;
+        kg[t * DK + i] = h(kh * g);
+        qg[t * DK + i] = h(qv * g);
+        if (blk > 0) {
+          Ks[t * KP + i] = h(kv * pp);
+          Qs[t * KP + i] = h(qv * pp);
+        }
+      }
+      float ss = 1.f;  // product over s+1 .. end of the block
+      for (int tl = 15; tl >= 0; --tl) {
+        const int s2 = 16 * blk + tl;
+        const float kt = (float)Kts[s2 * KP + i];
+        float f = ss;
+        for (int r = blk + 1; r < 4; ++r) {
+          KC[(16 * (r * (r - 1) / 2 + blk) + tl) * KP + i] = h(kt * f);
+          f *= Bv[r];
+        }
+        Kts[s2 * KP + i] = h(kt * (ss * after));
+        ss *= av[16 * bb + tl];
+      }
+    }
+    if (hb == 0) ((float *)(rec + OFF_GV))[i] = (Bv[0] * Bv[1]) * (Bv[2] * Bv[3]);
+    __syncthreads();
+  }
+
   f16x4 ident;
 #pragma unroll
   for (int e = 0; e < 4; ++e) ident[e] = (4 * g + e == c16) ? (f16)1.0f : (f16)0.0f;
@@ -271,6 +418,24 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int kk = 0; kk < 4; ++kk)
       acc = mma32(ld8(&xs[(16 * rt_ + c16) * KP + 32 * kk + 8 * g]),
                   ld8(&Ktp[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
+    return acc;
+  };
+  // GK: tile (rt, ct) below the diagonal from the rescaled rows of xs and the
+  // column operand of (rt, ct)
+  auto gramk = [&](const f16 *xs, int rt_, int ct) {
+    const f16 *kc = (const f16 *)Al + 16 * ((rt_ * (rt_ - 1)) / 2 + ct) * KP;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      acc = mma32(ld8(&xs[(16 * rt_ + c16) * KP + 32 * kk + 8 * g]),
+                  ld8(&kc[c16 * KP + 32 * kk + 8 * g]), acc);
+    return acc;
+  };
+  // GK: a diagonal block of A or P in the result layout
+  auto diag4 = [&](const float *D, int b_) {
+    f32x4 acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = D[(16 * b_ + 4 * g + e) * LDF + c16];
     return acc;
   };
   auto beta4 = [&](int rt_) { return *(const f32x4 *)&bs[16 * rt_ + 4 * g]; };
@@ -300,7 +465,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   for (int idx = wave; idx < 10; idx += 4) {
     int rt_, ct;
     tri_tile(idx, rt_, ct);
-    const f32x4 acc = gram(Qs, rt_, ct);
+    const f32x4 acc = !GK ? gram(Qs, rt_, ct) : rt_ == ct ? diag4(Pdg, rt_) : gramk(Qs, rt_, ct);
     const f32x4 dc = dec4(rt_, 16 * ct + c16);
     f32x4 pv;
 #pragma unroll
@@ -314,7 +479,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   // ---- A: diagonal block `wave` (then its inverse) and off-diagonal blocks
   {
-    const f32x4 acc = gram(Ks, wave, wave);
+    const f32x4 acc = GK ? diag4(Adg, wave) : gram(Ks, wave, wave);
     const f32x4 b4 = beta4(wave), f4 = krow4(wave), dc = dec4(wave, 16 * wave + c16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -325,7 +490,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   for (int job = wave; job < 6; job += 4) {
     int rt_, ct;
     off_tile(job, rt_, ct);
-    const f32x4 acc = gram(Ks, rt_, ct);
+    const f32x4 acc = GK ? gramk(Ks, rt_, ct) : gram(Ks, rt_, ct);
     const f32x4 b4 = beta4(rt_), f4 = krow4(rt_), dc = dec4(rt_, 16 * ct + c16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) Aoff[job][4 * g + e][c16] = h(a_entry(b4[e], dc[e], acc[e], f4[e]));
@@ -446,6 +611,9 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // SCALED (unnormalised q, k or a state gate): q and k are staged as stored and
 // the record's per-token factors scale the rows of K S^T and Q S^T in fp32.
 // GATED: S decays by the record's gamma_L (the update operands carry the rest).
+// GK (per-channel gate): q and k come from the record as K (.) G and Q (.) G
+// (fp16), and S decays per key dimension by the record's g_L (kept in the
+// factor slot of the LDS record).
 // ---------------------------------------------------------------------------
 constexpr int ST = 768;        // threads
 constexpr int NL = ST - 256;   // loader lanes
@@ -462,7 +630,7 @@ struct StateSmem {
 };
 static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
 
-template <bool SCALED, bool GATED>
+template <bool SCALED, bool GATED, bool GK>
 __global__ void __launch_bounds__(ST)
 chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
             const float *__restrict__ beta, const float *__restrict__ S0, int BH, int T_, int NC,
@@ -502,7 +670,11 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     // Loads are unconditional (a masked lane reads a valid address) and masked
     // values are zeroed when stored: a conditional load makes the compiler wait
     // for it at the end of its branch.
-    constexpr int RECP = SCALED ? (int)(OFF_END / 16) : (int)(OFF_DS / 16) + 1;
+    // GK: 32 more pieces, g_L, from OFF_GV into the factor slot (piece 1793 on)
+    constexpr int RP0 = (int)(OFF_DS / 16) + 1;
+    constexpr int RECP = (SCALED || GK) ? (int)(OFF_END / 16) : RP0;
+    static_assert(RP0 * 16 == (int)OFF_SC, "g_L lands in the factor slot");
+    constexpr size_t RB = GK ? RECK : REC;
     constexpr int NKQ = (2048 + NL - 1) / NL, NR = (RECP + NL - 1) / NL;
     const int lt = tid - 256;
     struct Regs {
@@ -517,18 +689,24 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       const long t0 = (long)bh * T_ + (long)cc * C;
       const int L = min(C, T_ - cc * C);
       R.L = L;
+      const unsigned char *rc = ws + ((long)bh * NC + cc) * RB;
 #pragma unroll
       for (int u = 0; u < NKQ; ++u) {
         const int p = min(lt + NL * u, 2047), pp = p & 1023, t = min(pp >> 4, L - 1);
-        R.kq[u] = *(const uint4 *)((p < 1024 ? k : q) + (t0 + t) * DK + (pp & 15) * 8);
+        if (GK)  // K (.) G, Q (.) G: fp16 rows of 256 bytes in the record
+          R.kq[u] = *(const uint4 *)(rc + (p < 1024 ? OFF_KG : OFF_QG) + t * 256 + (pp & 15) * 16);
+        else
+          R.kq[u] = *(const uint4 *)((p < 1024 ? k : q) + (t0 + t) * DK + (pp & 15) * 8);
       }
       {
         const int t = min((lt & 255) >> 2, L - 1);
         R.v = *(const uint4 *)(v + (t0 + t) * 128 + j0 + (lt & 3) * 8);
       }
-      const uint4 *rs = (const uint4 *)(ws + ((long)bh * NC + cc) * REC);
 #pragma unroll
-      for (int u = 0; u < NR; ++u) R.r[u] = rs[min(lt + NL * u, RECP - 1)];
+      for (int u = 0; u < NR; ++u) {
+        const int p = min(lt + NL * u, RECP - 1);
+        R.r[u] = *(const uint4 *)(rc + ((GK && p >= RP0) ? OFF_GV + (p - RP0) * 16 : p * 16));
+      }
       R.b = beta[t0 + min(lt & 63, L - 1)];
     };
     auto stash = [&](const Regs &R, int buf) {
@@ -537,7 +715,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       for (int u = 0; u < NKQ; ++u) {
         const int p = lt + NL * u, pp = p & 1023, t = pp >> 4, i0 = (pp & 15) * 8;
         if (p < 2048)
-          *(f16x8 *)&(p < 1024 ? sm.K : sm.Q)[buf][t * KP + i0] = t < R.L ? cvt8(R.kq[u]) : z8;
+          *(f16x8 *)&(p < 1024 ? sm.K : sm.Q)[buf][t * KP + i0] =
+              t < R.L ? (GK ? __builtin_bit_cast(f16x8, R.kq[u]) : cvt8(R.kq[u])) : z8;
       }
       if (lt < 256)
         *(f16x8 *)&sm.V[buf][(lt >> 2) * VP + (lt & 3) * 8] = (lt >> 2) < R.L ? cvt8(R.v) : z8;
@@ -633,15 +812,17 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       sm.Xx[cb][sn][0][lane] = Xb[0];
       sm.Xx[cb][sn][1][lane] = Xb[1];
       const float gL = GATED ? *(const float *)(sm.rec[cb] + OFF_GL) : 1.0f;
-      // S^T <- gamma_L S^T + ds Kt^T X
+      // S^T <- gamma_L S^T + ds Kt^T X (GK: row i of S^T decays by g_L[i])
 #pragma unroll
       for (int i8 = 0; i8 < 8; ++i8) {
         f32x4 u = zero4();
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) u = mma32(KtF[(i8 * 2 + qq) * 64 + lane], Xb[qq], u);
+        f32x4 gv = {gL, gL, gL, gL};
+        if (GK) gv = *(const f32x4 *)(sm.rec[cb] + OFF_SC + 4 * (16 * i8 + 4 * g));
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          Sacc[i8][e] = fmaf(ds, u[e], GATED ? gL * Sacc[i8][e] : Sacc[i8][e]);
+          Sacc[i8][e] = fmaf(ds, u[e], (GATED || GK) ? gv[e] * Sacc[i8][e] : Sacc[i8][e]);
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -661,7 +842,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     if (log_ratio_sum && tile == 0 && wave == 0) {
       // the chunks' sums of log rho_t, in a fixed order
       float acc = 0.f;
-      for (int c = lane; c < NC; c += 64) acc += *(const float *)(ws + ((long)bh * NC + c) * REC + OFF_LR);
+      for (int c = lane; c < NC; c += 64)
+        acc += *(const float *)(ws + ((long)bh * NC + c) * (GK ? RECK : REC) + OFF_LR);
       acc = wave_sum(acc);
       if (lane == 0) log_ratio_sum[bh] = acc;
     }
@@ -729,62 +911,74 @@ size_t split_workspace_bytes(int B, int H, int T) {
 
 namespace {
 
-template <bool SCALED, bool GATED>
+template <bool SCALED, bool GATED, bool GK>
 hipError_t launch_state_t(const ChunkArgs &a, int NC, const void *ws, float *log_ratio_sum,
                           hipStream_t s) {
   const int BH = a.B * a.H;
   const size_t shm = sizeof(StateSmem);
-  hipError_t e = hipFuncSetAttribute((const void *)chunk_state<SCALED, GATED>,
+  hipError_t e = hipFuncSetAttribute((const void *)chunk_state<SCALED, GATED, GK>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chunk_state<SCALED, GATED>), dim3((unsigned)(BH * 4)), dim3(ST), shm, s,
+  hipLaunchKernelGGL((chunk_state<SCALED, GATED, GK>), dim3((unsigned)(BH * 4)), dim3(ST), shm, s,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.S0, BH,
                      a.T, NC, (const unsigned char *)ws, (bf16 *)a.o, a.S_final, log_ratio_sum,
                      a.xf);
   return hipGetLastError();
 }
 
-// the record carries row factors when q, k arrive unnormalised or a gate is given
+bool per_channel(const float *alpha, unsigned xf) { return alpha && (xf & kGateChannels); }
+
+// the record carries row factors when q, k arrive unnormalised or a gate is
+// given; with the per-channel gate it carries K (.) G, Q (.) G and g_L instead
 hipError_t launch_state(const ChunkArgs &a, int NC, const void *ws, float *log_ratio_sum,
                         hipStream_t s) {
-  if (a.alpha) return launch_state_t<true, true>(a, NC, ws, log_ratio_sum, s);
-  if (a.xf & kNormQK) return launch_state_t<true, false>(a, NC, ws, log_ratio_sum, s);
-  return launch_state_t<false, false>(a, NC, ws, log_ratio_sum, s);
+  if (per_channel(a.alpha, a.xf)) return launch_state_t<false, false, true>(a, NC, ws, log_ratio_sum, s);
+  if (a.alpha) return launch_state_t<true, true, false>(a, NC, ws, log_ratio_sum, s);
+  if (a.xf & kNormQK) return launch_state_t<true, false, false>(a, NC, ws, log_ratio_sum, s);
+  return launch_state_t<false, false, false>(a, NC, ws, log_ratio_sum, s);
 }
 
-template <int MODE, bool NORM, bool GATED>
+template <int MODE, bool NORM, bool GATED, bool GK>
 void launch_prep_t(int BH, int NC, hipStream_t s, const void *q, const void *k, const void *kt,
                    const float *beta, int T, unsigned char *rec, const float *r,
                    const float *wout, const float *alpha, unsigned xf) {
-  hipLaunchKernelGGL((chunk_prep<MODE, NORM, GATED>), dim3((unsigned)(BH * NC)), dim3(256), 0, s,
-                     (const bf16 *)q, (const bf16 *)k, (const bf16 *)kt, beta, T, NC, 0, NC, rec,
-                     r, wout, alpha, xf);
+  hipLaunchKernelGGL((chunk_prep<MODE, NORM, GATED, GK>), dim3((unsigned)(BH * NC)), dim3(256), 0,
+                     s, (const bf16 *)q, (const bf16 *)k, (const bf16 *)kt, beta, T, NC, 0, NC,
+                     rec, r, wout, alpha, xf);
 }
 
 // chunk_prep over every chunk of every head; kGiven takes no input transforms
+// and no per-channel gate
 template <int MODE>
 hipError_t launch_prep(int BH, int NC, hipStream_t s, const void *q, const void *k,
                        const void *kt, const float *beta, int T, unsigned char *rec,
                        const float *r, const float *wout, const float *alpha, unsigned xf) {
   if (NC <= 0) return hipSuccess;
-  const bool norm = MODE != kGiven && (xf & kNormQK);
-  if (norm && alpha)
-    launch_prep_t<MODE, MODE != kGiven, true>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
-  else if (norm)
-    launch_prep_t<MODE, MODE != kGiven, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
-  else if (alpha)
-    launch_prep_t<MODE, false, true>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
-  else
-    launch_prep_t<MODE, false, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+  constexpr bool TX = MODE != kGiven;  // instances with the transforms and the per-channel gate
+  const bool norm = TX && (xf & kNormQK);
+  if (TX && per_channel(alpha, xf)) {
+    if (norm)
+      launch_prep_t<MODE, TX, false, TX>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+    else
+      launch_prep_t<MODE, false, false, TX>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+  } else if (norm && alpha) {
+    launch_prep_t<MODE, TX, true, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+  } else if (norm) {
+    launch_prep_t<MODE, TX, false, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+  } else if (alpha) {
+    launch_prep_t<MODE, false, true, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+  } else {
+    launch_prep_t<MODE, false, false, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t split_forward_workspace_bytes(int B, int H, int T) {
+size_t split_forward_workspace_bytes(int B, int H, int T, bool gate_channels) {
   // the walk's records live in the space the chunk records take later
   const size_t nc = (size_t)((T + C - 1) / C);
-  return (size_t)B * H * nc * (REC + WOUT * sizeof(float));
+  return (size_t)B * H * nc * ((gate_channels ? RECK : REC) + WOUT * sizeof(float));
 }
 
 // walk_prep, the walk's sequential pass, chunk_prep forming the write keys
@@ -796,8 +990,9 @@ hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   if (BH == 0) return hipSuccess;
   const int NC = (a.T + C - 1) / C;
   unsigned char *rec = (unsigned char *)ws;
-  float *wout = (float *)(rec + (size_t)BH * NC * REC);
-  static_assert(WREC <= REC, "walk records fit in the chunk records' space");
+  const size_t rb = per_channel(a.alpha, a.xf) ? RECK : REC;
+  float *wout = (float *)(rec + (size_t)BH * NC * rb);
+  static_assert(WREC <= REC && REC <= RECK, "walk records fit in the chunk records' space");
   ChunkArgs ca{a.q, a.k, nullptr, a.v, a.beta, a.alpha, a.S0, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
                a.dtype, a.o, a.S_final, a.xf};
   if (a.precond_off) {  // the plain delta rule (Gated DeltaNet with alpha): kt = k

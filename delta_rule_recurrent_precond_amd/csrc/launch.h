@@ -98,7 +98,8 @@ hipError_t launch_walk_scan(const ScanArgs &a, void *ws, hipStream_t s);
 // The forward in four launches (bf16, dk = dv = 128, chunk 64): the walk, then
 // the chunk-parallel pass forming the write keys from the walk's results, then
 // the state kernel; ws of split_forward_workspace_bytes.
-size_t split_forward_workspace_bytes(int B, int H, int T);
+// (larger with the per-channel gate, whose chunk records carry K (.) G and Q (.) G)
+size_t split_forward_workspace_bytes(int B, int H, int T, bool gate_channels);
 hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s);
 
 }  // namespace osdn

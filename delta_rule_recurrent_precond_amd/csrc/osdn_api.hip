@@ -45,8 +45,8 @@ size_t two_phase_bytes(int B, int H, int T, int dk, int dtype, unsigned flags) {
 // Scratch that selects the fastest path: the split pipeline on the shapes of
 // the matrix-core kernels, else what the two-launch path needs.
 size_t ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype, unsigned flags) {
-  if (use_fused(dk, dv, chunk, dtype) && !(flags & OSDN_GATE_PER_CHANNEL))
-    return osdn::split_forward_workspace_bytes(B, H, T);
+  if (use_fused(dk, dv, chunk, dtype))
+    return osdn::split_forward_workspace_bytes(B, H, T, (flags & OSDN_GATE_PER_CHANNEL) != 0);
   return two_phase_bytes(B, H, T, dk, dtype, flags);
 }
 
@@ -59,16 +59,20 @@ unsigned transforms(unsigned flags) {
          (flags & OSDN_GATE_PER_CHANNEL ? osdn::kGateChannels : 0u);
 }
 
-// the matrix-core kernels (split pipeline or single fused kernel) take the call;
-// the per-channel gate runs on the two-phase path
-bool matrix_core(int dk, int dv, int chunk, int dtype, unsigned flags) {
-  return use_fused(dk, dv, chunk, dtype) && !(flags & OSDN_GATE_PER_CHANNEL);
-}
-
 bool split_ok(int B, int H, int T, int dk, int dv, int chunk, int dtype, unsigned flags,
               size_t workspace_bytes, const void *workspace) {
-  return matrix_core(dk, dv, chunk, dtype, flags) && workspace &&
-         workspace_bytes >= osdn::split_forward_workspace_bytes(B, H, T);
+  return use_fused(dk, dv, chunk, dtype) && workspace &&
+         workspace_bytes >= osdn::split_forward_workspace_bytes(
+                                B, H, T, (flags & OSDN_GATE_PER_CHANNEL) != 0);
+}
+
+// the single fused kernel takes the call: its shapes, not enough scratch for
+// the split pipeline, and no per-channel gate (which then runs on the
+// two-phase path)
+bool fused_ok(int B, int H, int T, int dk, int dv, int chunk, int dtype, unsigned flags,
+              size_t workspace_bytes, const void *workspace) {
+  return use_fused(dk, dv, chunk, dtype) && !(flags & OSDN_GATE_PER_CHANNEL) &&
+         !split_ok(B, H, T, dk, dv, chunk, dtype, flags, workspace_bytes, workspace);
 }
 
 }  // namespace
@@ -166,7 +170,7 @@ OSDN_EXPORT const char *osdn_forward_path(int B, int H, int T, int dk, int dv, i
   const float one = 1.0f;
   if (split_ok(B, H, T, dk, dv, chunk, dtype, flags, workspace_bytes, &one))
     return "split";
-  if (!matrix_core(dk, dv, chunk, dtype, flags)) return "two-phase";
+  if (!fused_ok(B, H, T, dk, dv, chunk, dtype, flags, workspace_bytes, &one)) return "two-phase";
   return transforms(flags) ? "unsupported" : "fused";
 }
 
@@ -179,22 +183,21 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   if (st != OSDN_OK) return st;
   if (flags & ~kFlags) return OSDN_ERR_UNSUPPORTED;
   const unsigned xf = transforms(flags);
-  const bool mc = matrix_core(dk, dv, chunk, dtype, flags);
+  const bool split = split_ok(B, H, T, dk, dv, chunk, dtype, flags, workspace_bytes, workspace);
+  const bool fused = fused_ok(B, H, T, dk, dv, chunk, dtype, flags, workspace_bytes, workspace);
   // the single fused kernel takes its inputs prepared
-  if (xf && mc && !split_ok(B, H, T, dk, dv, chunk, dtype, flags, workspace_bytes, workspace))
-    return OSDN_ERR_UNSUPPORTED;
+  if (xf && fused) return OSDN_ERR_UNSUPPORTED;
   if ((long long)B * H == 0) return OSDN_OK;
   if (T > 0 && (!q || !k || !v || !beta || !o)) return OSDN_ERR_NULL;
   if (T > 0 && (flags & OSDN_GATE_PER_CHANNEL) && !alpha) return OSDN_ERR_NULL;
   const bool off = (flags & OSDN_PRECOND_OFF) != 0;
   hipStream_t s = (hipStream_t)stream;
 
-  if (mc) {
+  if (split || fused) {
     osdn::FusedArgs a{q, k, v, beta, r, alpha, d0, S0, eta, B, H, T, dk, dv, chunk, dtype,
                       off ? 1 : 0, o, S_final, d_final, log_ratio_sum, xf};
-    if (split_ok(B, H, T, dk, dv, chunk, dtype, flags, workspace_bytes, workspace))
-      return hip_status(osdn::launch_split_forward(a, workspace, s));
-    return hip_status(osdn::launch_fused_forward(a, s));
+    return hip_status(split ? osdn::launch_split_forward(a, workspace, s)
+                            : osdn::launch_fused_forward(a, s));
   }
 
   // Two launches: the preconditioner walk writes kt into the workspace, then

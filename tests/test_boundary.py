@@ -179,15 +179,18 @@ def test_transform_flags(lib):
 
 
 def test_per_channel_gate_flag(lib):
-    """OSDN_GATE_PER_CHANNEL: the two-phase path for every shape (the matrix-core
-    kernels do not take it), its workspace is the write-key buffer, and alpha is
-    required (validated before any launch)."""
+    """OSDN_GATE_PER_CHANNEL: the multi-launch pipeline on its shapes given its
+    (larger) workspace, else the two-phase path (never the single fused kernel);
+    alpha is required (validated before any launch)."""
     PC = _lib.OSDN_GATE_PER_CHANNEL
-    assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, PC, 1 << 40).decode() == "two-phase"
+    n = lib.osdn_forward_workspace_bytes(2, 3, 100, 128, 128, 64, 0, PC)
+    assert n == 2 * 3 * 2 * (66048 + 768)   # chunk records with K (.) G, Q (.) G and g_L
+    assert lib.osdn_forward_workspace_bytes(2, 3, 100, 128, 128, 64, 0, PC | 1) == n
+    assert lib.osdn_forward_path(2, 3, 100, 128, 128, 64, 0, PC, n).decode() == "split"
+    assert lib.osdn_forward_path(2, 3, 100, 128, 128, 64, 0, PC, n - 1).decode() == "two-phase"
     assert lib.osdn_forward_path(1, 1, 64, 128, 128, 64, 0, PC | 1, 0).decode() == "two-phase"
     assert lib.osdn_forward_path(1, 1, 64, 32, 16, 16, 1, PC | 6, 0).decode() == "two-phase"
-    assert lib.osdn_forward_workspace_bytes(2, 3, 100, 128, 128, 64, 0, PC) == 2 * 3 * 100 * 128 * 2
-    assert lib.osdn_forward_workspace_bytes(2, 3, 100, 128, 128, 64, 0, PC | 1) == 0
+    assert lib.osdn_forward_workspace_bytes(2, 3, 100, 64, 64, 64, 1, PC) == 2 * 3 * 100 * 64 * 4
     assert _fwd(lib, B=1, H=1, T=64, dk=128, dv=128, chunk=64, flags=PC) == _lib.OSDN_ERR_NULL
     assert lib.osdn_step(1, 1, 1, 1, None, None, 0.1, 1, 1, 16, 16, 0, PC, 1, 1, 1, None,
                          None) == _lib.OSDN_ERR_NULL

@@ -4,11 +4,13 @@ backbone) against the fp64 oracle, through the C ABI.
 The pages evaluate OSDN on KDA without printing its update; both sides
 implement the reading
     S_t = S_{t-1} D_t + beta_t (v_t - S_{t-1} D_t k_t) kt_t^T,  D_t = diag(alpha_t),
-with the preconditioner walk unchanged.  osdn_forward runs it on the
-two-phase path (the walk writes kt, the vector chunk kernel applies the
-per-channel decays 2^(lg_t,i - lg_s,i) term by term); osdn_step scales each
-column of S.  Tolerances are the gated ones: fp32 data o, S 1e-4 and d 1e-5;
-bf16 data o, S 2e-2 and d 1e-5.  Inputs come from the seeded generators;
+with the preconditioner walk unchanged.  On the matrix-core shapes
+osdn_forward runs the multi-launch pipeline given its workspace (tiles below
+the diagonal factored through block boundaries, diagonal blocks term by term)
+and the two-phase path given only the write-key buffer; on other shapes the
+two-phase path (the vector chunk kernel applies the per-channel decays term by
+term).  osdn_step scales each column of S.  Tolerances are the gated ones:
+fp32 data o, S 1e-4 and d 1e-5; bf16 data o, S 2e-2 and d 1e-5.  Inputs come from the seeded generators;
 expected values from the oracle only.
 """
 import dataclasses
@@ -58,19 +60,25 @@ def _select(x, heads, w):
 
 
 def _check(w, inp, precond=True, S0=None, heads=None, alpha=None, q=None, norm_qk=False,
-           gate_logits=False):
+           gate_logits=False, ws=True):
     alpha = inp.alpha if alpha is None else alpha
     q = inp.q if q is None else q
     heads = heads if heads is not None else list(range(w.B * w.H))
     dev = inp.to("cuda")
     code = 0 if w.dtype == "bf16" else 1
+    if ws == "two-phase":  # only the write-key buffer (what the two-phase path needs)
+        ws = torch.empty(w.B * w.H * w.T * w.dk * (2 if code == 0 else 4), dtype=torch.uint8,
+                         device="cuda")
+    nbytes = (osdn.forward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, code, precond,
+                                           per_channel=True) if ws is True else ws.numel())
     _log("per-channel forward %s precond=%s heads=%d path=%s" % (
         w.name, precond, len(heads),
-        osdn.forward_path(w.B, w.H, w.T, w.dk, w.dv, w.chunk, code, precond, per_channel=True)))
+        osdn.forward_path(w.B, w.H, w.T, w.dk, w.dv, w.chunk, code, precond,
+                          workspace_bytes=nbytes, per_channel=True)))
     out = osdn.forward(q.cuda(), dev.k, dev.v, dev.beta, dev.r, None,
                        None if S0 is None else S0.cuda(), eta=inp.eta, chunk=w.chunk,
                        precond=precond, alpha=alpha.cuda(), norm_qk=norm_qk,
-                       gate_logits=gate_logits)
+                       gate_logits=gate_logits, workspace=ws)
     torch.cuda.synchronize()
     qq, kk, bb, rr = oracle.prepare_inputs(q, inp.k, inp.beta, inp.r, norm_qk, gate_logits)
     ref = oracle.forward(qq, kk, inp.v, bb, rr, None, S0, eta=inp.eta,
@@ -100,16 +108,20 @@ def _check(w, inp, precond=True, S0=None, heads=None, alpha=None, q=None, norm_q
     ("f32", 128, 128, 64, 130),
 ])
 @pytest.mark.parametrize("precond", [True, False])
-def test_forward_per_channel_parity(dtype, dk, dv, chunk, T, precond):
+@pytest.mark.parametrize("ws", [True, "two-phase"])
+def test_forward_per_channel_parity(dtype, dk, dv, chunk, T, precond, ws):
+    if ws != True and not (dtype == "bf16" and dk == 128):  # noqa: E712
+        pytest.skip("only the matrix-core shapes have a second path")
     w = _kda(2, 2, T, dk, dv, chunk, dtype, seed=1200 + dk + dv + T)
     S0 = 0.1 * torch.randn(w.B, w.H, dv, dk, generator=torch.Generator().manual_seed(4))
-    _check(w, W.generate(w), precond, S0=S0)
+    _check(w, W.generate(w), precond, S0=S0, ws=ws)
 
 
 @pytest.mark.parametrize("T", [1, 63, 64, 129])
-def test_forward_per_channel_chunk_boundaries(T):
+@pytest.mark.parametrize("ws", [True, "two-phase"])
+def test_forward_per_channel_chunk_boundaries(T, ws):
     w = _kda(1, 2, T, 128, 128, 64, "bf16", seed=1250 + T)
-    _check(w, W.generate(w))
+    _check(w, W.generate(w), ws=ws)
 
 
 def test_strong_decay_and_zero_channel_gates():
@@ -127,8 +139,12 @@ def test_strong_decay_and_zero_channel_gates():
     wb = _kda(1, 2, 150, 128, 128, 64, "bf16", seed=1262, alpha_mu=0.0, alpha_sigma=2.0)
     inpb = W.generate(wb)
     ab = inpb.alpha.clone()
-    ab[:, :, 70, ::3] = 0.0
-    _check(wb, inpb, alpha=ab)
+    ab[:, :, 70, ::3] = 0.0       # some channels closed inside a 16-token block
+    ab[:, :, 80, 1::3] = 0.0      # first token of a block
+    ab[:, :, 127, :] = 0.0        # last token of a chunk, every channel
+    for ws in (True, "two-phase"):
+        for p in (True, False):
+            _check(wb, inpb, precond=p, alpha=ab, ws=ws)
 
 
 @pytest.mark.parametrize("dtype,dk", [("f32", 32), ("bf16", 128)])
@@ -152,10 +168,39 @@ def test_equal_channels_match_the_scalar_gate(dtype, dk):
 
 
 @pytest.mark.parametrize("precond", [True, False])
-def test_per_channel_raw_inputs(precond):
+@pytest.mark.parametrize("ws", [True, "two-phase"])
+def test_per_channel_raw_inputs(precond, ws):
     """Per-channel gate with the in-kernel input transforms."""
     w = dataclasses.replace(_kda(2, 2, 170, 128, 128, 64, "bf16", seed=1280), raw=True)
-    _check(w, W.generate(w), precond, norm_qk=True, gate_logits=True)
+    _check(w, W.generate(w), precond, norm_qk=True, gate_logits=True, ws=ws)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("precond", [True, False])
+def test_unit_channel_gates_equal_ungated_bitwise(dtype, precond):
+    """alpha = 1 in every channel: every decay product is exactly 1, so the
+    per-channel kernels agree with the ungated run of the same path up to
+    their own rounding (they sum the products in another order: fp32 rounding
+    on the vector path, fp16-operand rounding on the multi-launch pipeline),
+    and the preconditioner walk, which the gate does not reach, is bitwise
+    the same."""
+    dk = 128 if dtype == "bf16" else 32
+    w = W.custom(2, 2, 150, dk, dk, 64 if dtype == "bf16" else 32, dtype=dtype, eta=0.1,
+                 apf=True, seed=1285)
+    inp = W.generate(w)
+    dev = inp.to("cuda")
+    ones = torch.ones(w.B, w.H, w.T, dk, device="cuda")
+    a = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=inp.eta, chunk=w.chunk,
+                     precond=precond)
+    b = osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=inp.eta, chunk=w.chunk,
+                     precond=precond, alpha=ones)
+    torch.cuda.synchronize()
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    assert rowwise_rel(b["o"], a["o"]) <= tol
+    assert matrix_rel(b["S_final"], a["S_final"]) <= tol
+    if precond:
+        assert torch.equal(a["d_final"], b["d_final"])
+    assert torch.equal(a["log_ratio_sum"], b["log_ratio_sum"])
 
 
 @pytest.mark.parametrize("dtype,dk,dv", [("f32", 32, 64), ("bf16", 128, 128)])
@@ -203,8 +248,9 @@ def test_per_channel_steps_continue_a_forward():
 
 
 @pytest.mark.slow
-def test_per_channel_workload_full_size():
+@pytest.mark.parametrize("ws", [True, "two-phase"])
+def test_per_channel_workload_full_size(ws):
     """The 1.3B-style layer with per-channel gates at full size, on sampled heads."""
     w = W.CONFIGS["1.3b-apf-kda"]
     inp = W.generate(w)
-    _check(w, inp, heads=_heads(w, 4))
+    _check(w, inp, heads=_heads(w, 4), ws=ws)
