@@ -46,10 +46,11 @@
 // No ratio g_t / g_s is ever formed by division.  A and P are built from
 // products of alpha over the tokens between s and t:
 //   - a 16x16 tile below the diagonal (row block r > column block c) factors
-//     through the boundary of block r - 1, with both factors <= 1: the rows of
-//     block r take the product from the block's start to t, and the column
-//     operand takes the product from s + 1 to the end of block r - 1 (one
-//     operand copy per (r, c));
+//     through the block boundaries, every factor <= 1: the rows of block r
+//     take the product from the block's start to t (staged in place), the
+//     columns take the product from s + 1 to the end of block c (staged in
+//     place), and the products over the full blocks between c and r scale the
+//     row operand as it is loaded;
 //   - the diagonal 16x16 blocks are summed term by term on the vector ALU with
 //     a running product down the rows.
 // A zero gate therefore resets exactly.  The record then carries K (.) G and
@@ -125,13 +126,11 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   __shared__ float sk[C], sq[C];  // NORM: 1 / ||k_t||, 1 / ||q_t||
   __shared__ float lga[C];        // GATED: lg_t, the running sum of log2 alpha
   __shared__ float xdl[C];        // GATED: gamma_L / gamma_t
-  // GK: alpha [t][i] (fp32), later the column operands of the tiles below the
-  // diagonal (fp16, 6 tiles of 16 rows in off_tile order); the diagonal blocks
-  // of A and P (fp32 sums); the products of alpha over each 16-token block
-  __shared__ __align__(16) float Al[GK ? C * DK : 4];
+  // GK: the diagonal blocks of A and P (fp32 sums); the products of alpha over
+  // each 16-token block, per key dimension [block][i] (alpha itself is read
+  // from global memory where it is used)
   __shared__ float Adg[GK ? 4 * 16 * LDF : 4], Pdg[GK ? 4 * 16 * LDF : 4];
-  __shared__ float Bk[GK ? 4 * DK : 4];
-  static_assert(!GK || 6 * 16 * KP * 2 <= C * DK * 4, "column operands fit in alpha's space");
+  __shared__ __align__(16) float Bk[GK ? 4 * DK : 4];
   __shared__ float red[4];
 
   const int tid = threadIdx.x;
@@ -172,14 +171,6 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     cs[tid] = tid < L ? wout[((long)bh * NC + c) * WOUT + DK + tid] : 0.f;
     const float rv = r ? r[tok0 + min(tid, L - 1)] : 1.0f;
     rs[tid] = (r && tid < L) ? ((xf & kGateLogits) ? sigmoid_gate(rv) : rv) : 1.0f;
-  }
-  if (GK) {  // alpha of the chunk; rows past the end are 1 (they change no product)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int p = tid + 256 * u, t = p >> 5, i4 = (p & 31) * 4;
-      const float4 a4 = *(const float4 *)(alpha + (tok0 + min(t, L - 1)) * DK + i4);
-      *(float4 *)&Al[t * DK + i4] = t < L ? a4 : float4{1.f, 1.f, 1.f, 1.f};
-    }
   }
   // per-token normalisation scales (16 threads per token hold its pieces)
   float kscale[4] = {1.f, 1.f, 1.f, 1.f}, qscale[4] = {1.f, 1.f, 1.f, 1.f};
@@ -302,8 +293,8 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   if (GK) {
     // (a) the diagonal blocks of A and P term by term: wave b takes block b, a
     // lane column s = 16b + (lane & 15) and 32 key dimensions; e_i runs down the
-    // rows as the product of alpha_i over s+1 .. t (1 at t = s, 0 above it).
-    // The four lanes of a column add their partial sums.
+    // rows as the product of alpha_i over s+1 .. t (0 above t = s, where the
+    // added 1 starts it).  The four lanes of a column add their partial sums.
     const int b = wave, sl = lane & 15, i0 = 32 * (lane >> 4), s = 16 * b + sl;
     float kts[32], e[32];
 #pragma unroll
@@ -315,20 +306,37 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         e[8 * j + x] = 0.f;
       }
     }
+    // alpha of row t for this lane's 32 dimensions (rows past the end are 1:
+    // they change no product), one row ahead of its use
+    auto arow = [&](int t, float4 (&v)[8]) {
+      const float *src = alpha + (tok0 + min(t, L - 1)) * DK + i0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = *(const float4 *)(src + 4 * j);
+      if (t >= L) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = float4{1.f, 1.f, 1.f, 1.f};
+      }
+    };
+    float4 an[8];
+    arow(16 * b, an);
     for (int tl = 0; tl < 16; ++tl) {
       const int t = 16 * b + tl;
+      float4 ac[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ac[j] = an[j];
+      if (tl < 15) arow(t + 1, an);
+      const float start = tl == sl ? 1.f : 0.f;
       float a = 0.f, pq = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f16x8 kv = ld8(&Ks[t * KP + i0 + 8 * j]);
         const f16x8 qv = ld8(&Qs[t * KP + i0 + 8 * j]);
-        const float4 a0 = *(const float4 *)&Al[t * DK + i0 + 8 * j];
-        const float4 a1 = *(const float4 *)&Al[t * DK + i0 + 8 * j + 4];
+        const float4 a0 = ac[2 * j], a1 = ac[2 * j + 1];
         const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int cc = 8 * j + x;
-          e[cc] = tl == sl ? 1.f : e[cc] * av[x];
+          e[cc] = fmaf(e[cc], av[x], start);
           const float w = kts[cc] * e[cc];
           a = fmaf((float)kv[x], w, a);
           pq = fmaf((float)qv[x], w, pq);
@@ -343,67 +351,59 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         Pdg[(16 * b + tl) * LDF + sl] = tl >= sl ? pq : 0.f;
       }
     }
-    // (b) per key dimension i (thread i, blocks 2hb and 2hb + 1): the products
-    // of alpha over each block, then
+    // (b) per pair of key dimensions (thread: dimensions i2, i2 + 1 of block
+    // blk = wave): the products of alpha over each block, then
     //   g_t = (product over the earlier blocks) * (product from the block start to t)
     //   K (.) G and Q (.) G to the record; the rows of block r >= 1 of k and q
-    //   rescaled by the product from the block start to t (in place);
-    //   the column operand of tile (r, c): kt_s times the product over s+1 ..
-    //   end of block r-1; kt_s decayed to the chunk end (in place) for the S
-    //   update; g_L to the record.
-    const int i = tid & 127, hb = tid >> 7;
-    float av[32];
-#pragma unroll
-    for (int u = 0; u < 32; ++u) av[u] = Al[(32 * hb + u) * DK + i];
-    float B0 = 1.f, B1 = 1.f;
+    //   rescaled by the product from the block start to t, and kt_s by the
+    //   product from s + 1 to the block end (in place); g_L to the record.
+    const int blk = wave, i2 = 2 * lane;
+    float2 av[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      B0 *= av[u];
-      B1 *= av[16 + u];
+      const int t = 16 * blk + u;
+      const float2 a2 = *(const float2 *)(alpha + (tok0 + min(t, L - 1)) * DK + i2);
+      av[u] = t < L ? a2 : float2{1.f, 1.f};
     }
-    Bk[(2 * hb) * DK + i] = B0;
-    Bk[(2 * hb + 1) * DK + i] = B1;
-    __syncthreads();  // alpha read everywhere (its space takes the column operands)
-    const float Bv[4] = {Bk[i], Bk[DK + i], Bk[2 * DK + i], Bk[3 * DK + i]};
-    f16 *KC = (f16 *)Al;
+    float2 Bb = {1.f, 1.f};
+#pragma unroll
+    for (int u = 0; u < 16; ++u) Bb = float2{Bb.x * av[u].x, Bb.y * av[u].y};
+    *(float2 *)&Bk[blk * DK + i2] = Bb;
+    __syncthreads();  // block products visible; the diagonal sums have read k, q, kt
+    float2 Bv[4], G = {1.f, 1.f};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      Bv[x] = *(const float2 *)&Bk[x * DK + i2];
+      if (x < blk) G = float2{G.x * Bv[x].x, G.y * Bv[x].y};
+    }
     f16 *kg = (f16 *)(rec + OFF_KG), *qg = (f16 *)(rec + OFF_QG);
+    float2 pp = {1.f, 1.f};
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int blk = 2 * hb + bb;
-      float G = 1.f, after = 1.f;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        if (x < blk) G *= Bv[x];
-        if (x > blk) after *= Bv[x];
-      }
-      float pp = 1.f;
-      for (int tl = 0; tl < 16; ++tl) {
-        const int t = 16 * blk + tl;
-        pp *= av[16 * bb + tl];
-        const float g = G * pp;
-        const float kv = (float)Ks[t * KP + i], qv = (float)Qs[t * KP + i];
-        const float kh = (NORM && MODE == kOsdn) ? kv * sk[t] : kv;
-        kg[t * DK + i] = h(kh * g);
-        qg[t * DK + i] = h(qv * g);
-        if (blk > 0) {
-          Ks[t * KP + i] = h(kv * pp);
-          Qs[t * KP + i] = h(qv * pp);
-        }
-      }
-      float ss = 1.f;  // product over s+1 .. end of the block
-      for (int tl = 15; tl >= 0; --tl) {
-        const int s2 = 16 * blk + tl;
-        const float kt = (float)Kts[s2 * KP + i];
-        float f = ss;
-        for (int r = blk + 1; r < 4; ++r) {
-          KC[(16 * (r * (r - 1) / 2 + blk) + tl) * KP + i] = h(kt * f);
-          f *= Bv[r];
-        }
-        Kts[s2 * KP + i] = h(kt * (ss * after));
-        ss *= av[16 * bb + tl];
+    for (int tl = 0; tl < 16; ++tl) {
+      const int t = 16 * blk + tl;
+      pp = float2{pp.x * av[tl].x, pp.y * av[tl].y};
+      const f16x2 k2 = *(const f16x2 *)&Ks[t * KP + i2], q2 = *(const f16x2 *)&Qs[t * KP + i2];
+      const float kx = (float)k2[0], ky = (float)k2[1], qx = (float)q2[0], qy = (float)q2[1];
+      const float ks = (NORM && MODE == kOsdn) ? sk[t] : 1.f;
+      const float gx = G.x * pp.x, gy = G.y * pp.y;
+      *(f16x2 *)&kg[t * DK + i2] = f16x2{h((kx * ks) * gx), h((ky * ks) * gy)};
+      *(f16x2 *)&qg[t * DK + i2] = f16x2{h(qx * gx), h(qy * gy)};
+      if (blk > 0) {
+        *(f16x2 *)&Ks[t * KP + i2] = f16x2{h(kx * pp.x), h(ky * pp.y)};
+        *(f16x2 *)&Qs[t * KP + i2] = f16x2{h(qx * pp.x), h(qy * pp.y)};
       }
     }
-    if (hb == 0) ((float *)(rec + OFF_GV))[i] = (Bv[0] * Bv[1]) * (Bv[2] * Bv[3]);
+    float2 ss = {1.f, 1.f};  // product over s+1 .. end of the block
+#pragma unroll
+    for (int tl = 15; tl >= 0; --tl) {
+      const int s2 = 16 * blk + tl;
+      const f16x2 t2 = *(const f16x2 *)&Kts[s2 * KP + i2];
+      *(f16x2 *)&Kts[s2 * KP + i2] = f16x2{h((float)t2[0] * ss.x), h((float)t2[1] * ss.y)};
+      ss = float2{ss.x * av[tl].x, ss.y * av[tl].y};
+    }
+    if (blk == 0)
+      *(float2 *)(rec + OFF_GV + 4 * i2) = float2{(Bv[0].x * Bv[1].x) * (Bv[2].x * Bv[3].x),
+                                                  (Bv[0].y * Bv[1].y) * (Bv[2].y * Bv[3].y)};
     __syncthreads();
   }
 
@@ -420,15 +420,29 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                   ld8(&Ktp[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
     return acc;
   };
-  // GK: tile (rt, ct) below the diagonal from the rescaled rows of xs and the
-  // column operand of (rt, ct)
+  // GK: tile (rt, ct) below the diagonal: the rescaled rows of xs (times the
+  // products over the full blocks between ct and rt, per key dimension) and the
+  // rescaled rows of kt
   auto gramk = [&](const f16 *xs, int rt_, int ct) {
-    const f16 *kc = (const f16 *)Al + 16 * ((rt_ * (rt_ - 1)) / 2 + ct) * KP;
     f32x4 acc = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      acc = mma32(ld8(&xs[(16 * rt_ + c16) * KP + 32 * kk + 8 * g]),
-                  ld8(&kc[c16 * KP + 32 * kk + 8 * g]), acc);
+    for (int kk = 0; kk < 4; ++kk) {
+      f16x8 a = ld8(&xs[(16 * rt_ + c16) * KP + 32 * kk + 8 * g]);
+      if (rt_ > ct + 1) {
+        const int i0 = 32 * kk + 8 * g;
+        float m[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+        for (int bb = ct + 1; bb < rt_; ++bb) {
+          const float4 b0 = *(const float4 *)&Bk[bb * DK + i0];
+          const float4 b1 = *(const float4 *)&Bk[bb * DK + i0 + 4];
+          const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) m[j] *= bv[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = h((float)a[j] * m[j]);
+      }
+      acc = mma32(a, ld8(&Kts[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
+    }
     return acc;
   };
   // GK: a diagonal block of A or P in the result layout
@@ -525,6 +539,12 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const f32x4 xd = *(const f32x4 *)&xdl[16 * m + 4 * g];
 #pragma unroll
         for (int e = 0; e < 4; ++e) tv[e] *= xd[e];
+      }
+      if (GK && m < 3) {  // kt_s so far carries the product to its block end
+        float after = 1.f;
+        for (int bb = m + 1; bb < 4; ++bb) after *= Bk[bb * DK + 16 * n + c16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tv[e] *= after;
       }
       tr[m] = h4(tv);
     }

@@ -14,6 +14,7 @@
 namespace osdn {
 
 typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
