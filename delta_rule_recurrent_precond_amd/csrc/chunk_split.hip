@@ -621,11 +621,11 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 //   wave 2 + sn (the outputs)  Q S^T of chunk c (from the S^T the chain wave
 //                              left), then in the next iteration
 //                              O = Q S^T + P X of chunk c and its stores
-//   waves 4-11 (loaders)       global loads of chunk c+2, LDS stores of c+1
+//   waves 4-11 (loaders)       global loads of chunk c+2 (GK: c+3), LDS stores of c+1
 // The output wave keeps Q S^T and the score operands of chunk c in registers
 // so that the loaders may refill that chunk's LDS buffer.  The loaders keep two
-// chunks in registers: the loads of chunk c+2 are issued before chunk c+1 is
-// stored, so a burst of loads from every CU has two iterations to arrive.
+// chunks in registers (three with GK), so a chunk's loads are issued one
+// iteration (two) before it is stored.
 // Each role runs its own loop with the same barrier count (NC + 1), so the
 // registers of different roles are never live at the same time.
 // SCALED (unnormalised q, k or a state gate): q and k are staged as stored and
@@ -700,21 +700,19 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     struct Regs {
       uint4 kq[NKQ], v, r[NR];
       float b;
-      int L;  // valid rows of the chunk held
     };
-    Regs ra, rb;
+    Regs ra, rb, rc;
     // chunk cc clamped to the last one: the loads past the end reread it
     auto load = [&](Regs &R, int cc) {
       cc = min(cc, NC - 1);
       const long t0 = (long)bh * T_ + (long)cc * C;
       const int L = min(C, T_ - cc * C);
-      R.L = L;
-      const unsigned char *rc = ws + ((long)bh * NC + cc) * RB;
+      const unsigned char *rp = ws + ((long)bh * NC + cc) * RB;
 #pragma unroll
       for (int u = 0; u < NKQ; ++u) {
         const int p = min(lt + NL * u, 2047), pp = p & 1023, t = min(pp >> 4, L - 1);
         if (GK)  // K (.) G, Q (.) G: fp16 rows of 256 bytes in the record
-          R.kq[u] = *(const uint4 *)(rc + (p < 1024 ? OFF_KG : OFF_QG) + t * 256 + (pp & 15) * 16);
+          R.kq[u] = *(const uint4 *)(rp + (p < 1024 ? OFF_KG : OFF_QG) + t * 256 + (pp & 15) * 16);
         else
           R.kq[u] = *(const uint4 *)((p < 1024 ? k : q) + (t0 + t) * DK + (pp & 15) * 8);
       }
@@ -725,21 +723,23 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 #pragma unroll
       for (int u = 0; u < NR; ++u) {
         const int p = min(lt + NL * u, RECP - 1);
-        R.r[u] = *(const uint4 *)(rc + ((GK && p >= RP0) ? OFF_GV + (p - RP0) * 16 : p * 16));
+        R.r[u] = *(const uint4 *)(rp + ((GK && p >= RP0) ? OFF_GV + (p - RP0) * 16 : p * 16));
       }
       R.b = beta[t0 + min(lt & 63, L - 1)];
     };
-    auto stash = [&](const Regs &R, int buf) {
+    // chunk cc (< NC) from its register set into LDS buffer cc & 1
+    auto stash = [&](const Regs &R, int cc) {
+      const int buf = cc & 1, L = min(C, T_ - cc * C);
       const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int u = 0; u < NKQ; ++u) {
         const int p = lt + NL * u, pp = p & 1023, t = pp >> 4, i0 = (pp & 15) * 8;
         if (p < 2048)
           *(f16x8 *)&(p < 1024 ? sm.K : sm.Q)[buf][t * KP + i0] =
-              t < R.L ? (GK ? __builtin_bit_cast(f16x8, R.kq[u]) : cvt8(R.kq[u])) : z8;
+              t < L ? (GK ? __builtin_bit_cast(f16x8, R.kq[u]) : cvt8(R.kq[u])) : z8;
       }
       if (lt < 256)
-        *(f16x8 *)&sm.V[buf][(lt >> 2) * VP + (lt & 3) * 8] = (lt >> 2) < R.L ? cvt8(R.v) : z8;
+        *(f16x8 *)&sm.V[buf][(lt >> 2) * VP + (lt & 3) * 8] = (lt >> 2) < L ? cvt8(R.v) : z8;
       uint4 *rd = (uint4 *)sm.rec[buf];
 #pragma unroll
       for (int u = 0; u < NR; ++u) {
@@ -747,24 +747,54 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         if (p < RECP) rd[p] = R.r[u];
       }
       if (lt < C)
-        sm.b[buf][lt] = lt < R.L ? ((xf & kGateLogits) ? sigmoid_gate(R.b) : R.b) : 0.f;
+        sm.b[buf][lt] = lt < L ? ((xf & kGateLogits) ? sigmoid_gate(R.b) : R.b) : 0.f;
     };
+    if (!GK) {
+      // Entering iteration c the loaders hold chunk c+1 in one register set; they
+      // load chunk c+2 into the other (freed by the previous store), then store
+      // chunk c+1.  Written for two iterations so that the sets keep fixed names.
+      if (NC > 0) {
+        load(ra, 0);
+        load(rb, 1);
+        stash(ra, 0);
+      }
+      __syncthreads();
+      for (int c = 0; c < NC; c += 2) {
+        load(ra, c + 2);
+        if (c + 1 < NC) stash(rb, c + 1);
+        __syncthreads();
+        if (c + 1 < NC) {
+          load(rb, c + 3);
+          if (c + 2 < NC) stash(ra, c + 2);
+          __syncthreads();
+        }
+      }
+      __syncthreads();  // the output waves' last iteration
+      return;
+    }
+    // GK (larger records, which miss the last-level cache more often): three
+    // register sets.  Entering iteration c the loaders hold chunks c+1 and c+2;
+    // they load chunk c+3 into the third set (freed by the previous store), then
+    // store chunk c+1, so every load has two iterations to arrive.
     if (NC > 0) {
       load(ra, 0);
       load(rb, 1);
+      load(rc, 2);
       stash(ra, 0);
     }
     __syncthreads();
-    // Entering iteration c the loaders hold chunk c+1 in one register set; they
-    // load chunk c+2 into the other (freed by the previous store), then store
-    // chunk c+1.  Written for two iterations so that the sets keep fixed names.
-    for (int c = 0; c < NC; c += 2) {
-      load(ra, c + 2);
-      if (c + 1 < NC) stash(rb, 1);
+    for (int c = 0; c < NC; c += 3) {
+      load(ra, c + 3);
+      if (c + 1 < NC) stash(rb, c + 1);
       __syncthreads();
       if (c + 1 < NC) {
-        load(rb, c + 3);
-        if (c + 2 < NC) stash(ra, 0);
+        load(rb, c + 4);
+        if (c + 2 < NC) stash(rc, c + 2);
+        __syncthreads();
+      }
+      if (c + 2 < NC) {
+        load(rc, c + 5);
+        if (c + 3 < NC) stash(ra, c + 3);
         __syncthreads();
       }
     }
