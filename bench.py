@@ -336,7 +336,9 @@ def main():
                 "ms": ms_raw, "tokens_per_s": tokens / (ms_raw * 1e-3),
                 "traffic": stored_traffic("osdn_forward_raw_split", args.workload)},
             "per_channel_gate_forward": {"ms": ms_kda, "tokens_per_s": tokens / (ms_kda * 1e-3),
-                                         "path": kda_path, "steps": kda_steps},
+                                         "path": kda_path, "steps": kda_steps,
+                                         "traffic": stored_traffic("osdn_forward_kda_split",
+                                                                   args.workload)},
             "per_channel_gate_deltanet_mode": {"ms": ms_kda_dn,
                                                "tokens_per_s": tokens / (ms_kda_dn * 1e-3)},
             "raw_inputs_separate_torch_passes": {"ms": ms_raw_sep,

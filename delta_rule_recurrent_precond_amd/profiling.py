@@ -41,10 +41,12 @@ ENTRIES = {
     "chunk_split": "osdn_chunk_fwd_split",
     "forward_gated_split": "osdn_forward_gated_split",
     "forward_raw_split": "osdn_forward_raw_split",
+    "forward_kda_split": "osdn_forward_kda_split",
 }
 # entries that profile another draw of the same workload: the state gate added,
 # or q, k unnormalised with beta, r as logits (the kernels transform them)
-DRAWS = {"forward_gated_split": {"gated": True}, "forward_raw_split": {"raw": True}}
+DRAWS = {"forward_gated_split": {"gated": True}, "forward_raw_split": {"raw": True},
+         "forward_kda_split": {"gated": True, "gate_channels": True}}
 
 
 def kernel_sources_hash() -> str:
@@ -76,6 +78,9 @@ def call(entry: str, dev, w):
     elif entry == "chunk_split":
         osdn.chunk_fwd(dev.q, dev.k, dev.k, dev.v, dev.beta, chunk=w.chunk)
     elif entry == "forward_gated_split":
+        osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=dev.eta, chunk=w.chunk,
+                     alpha=dev.alpha)
+    elif entry == "forward_kda_split":  # one gate per key dimension
         osdn.forward(dev.q, dev.k, dev.v, dev.beta, dev.r, eta=dev.eta, chunk=w.chunk,
                      alpha=dev.alpha)
     elif entry == "forward_raw_split":
