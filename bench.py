@@ -295,7 +295,7 @@ def main():
             st = lib.osdn_chunk_fwd(d.q.data_ptr(), d.k.data_ptr(), kts[i % copies].data_ptr(),
                                     d.v.data_ptr(), d.beta.data_ptr(), None, None, B, H, T, dk,
                                     dv, C,
-                                    code, o["o"].data_ptr(), o["S_final"].data_ptr(),
+                                    code, 0, o["o"].data_ptr(), o["S_final"].data_ptr(),
                                     cws.data_ptr() if (use_ws and cws_n) else None,
                                     cws_n if use_ws else 0, stream)
             assert st == 0, st

@@ -102,8 +102,9 @@ def precond_scan(k, beta, r=None, d0=None, eta=0.05, *, want_d_all=False, want_l
     return out
 
 
-def chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code) -> int:
-    n = _lib.load().osdn_chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code)
+def chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code, per_channel=False) -> int:
+    n = _lib.load().osdn_chunk_fwd_workspace_bytes(
+        B, H, T, dk, dv, chunk, dtype_code, _lib.OSDN_GATE_PER_CHANNEL if per_channel else 0)
     if n == (1 << 64) - 1:
         raise ValueError("invalid arguments for osdn_chunk_fwd")
     return int(n)
@@ -112,7 +113,8 @@ def chunk_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype_code) -> int:
 def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64, *, alpha=None, workspace=True):
     """Phase 2 with a given write key k~.  Returns (o, S_final).
 
-    ``alpha`` [B,H,T] fp32 is the optional state gate.  ``workspace``: True
+    ``alpha`` [B,H,T] fp32 is the optional state gate ([B,H,T,dk]: one gate per
+    key dimension).  ``workspace``: True
     allocates the scratch that selects the chunk-parallel path (when one exists
     for these shapes), a uint8 device tensor passes one, None runs the
     single-kernel pass."""
@@ -126,16 +128,18 @@ def chunk_fwd(q, k, k_tilde, v, beta, S0=None, chunk=64, *, alpha=None, workspac
         raise ValueError("v has shape %s, expected [%d,%d,%d,dv]" % (tuple(v.shape), B, H, T))
     dv = v.shape[3]
     _dev(beta, "beta", (B, H, T), torch.float32, dev)
-    _dev(alpha, "alpha", (B, H, T), torch.float32, dev)
+    chan = alpha is not None and alpha.dim() == 4
+    _dev(alpha, "alpha", (B, H, T, dk) if chan else (B, H, T), torch.float32, dev)
     _dev(S0, "S0", (B, H, dv, dk), torch.float32, dev)
     o = torch.empty_like(v)
     S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     if workspace is True:
-        n = chunk_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), _dtype_code(q))
+        n = chunk_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), _dtype_code(q), chan)
         workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
     ws_bytes = 0 if workspace is None else workspace.numel()
     st = _lib.load().osdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(k_tilde), _ptr(v), _ptr(beta),
                                     _ptr(alpha), _ptr(S0), B, H, T, dk, dv, int(chunk), _dtype_code(q),
+                                    _lib.OSDN_GATE_PER_CHANNEL if chan else 0,
                                     _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes,
                                     _stream(dev))
     _lib.check("osdn_chunk_fwd", st)

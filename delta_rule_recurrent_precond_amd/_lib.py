@@ -36,9 +36,9 @@ F = ctypes.c_float
 SIGNATURES = {
     "osdn_precond_scan": (I, [P, P, P, P, F, I, I, I, I, I, P, P, P, P, P, ctypes.c_size_t, P]),
     "osdn_precond_scan_workspace_bytes": (ctypes.c_size_t, [I, I, I, I, I]),
-    "osdn_chunk_fwd": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, P, ctypes.c_size_t,
-                           P]),
-    "osdn_chunk_fwd_workspace_bytes": (ctypes.c_size_t, [I, I, I, I, I, I, I]),
+    "osdn_chunk_fwd": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_uint, P, P, P,
+                           ctypes.c_size_t, P]),
+    "osdn_chunk_fwd_workspace_bytes": (ctypes.c_size_t, [I, I, I, I, I, I, I, ctypes.c_uint]),
     "osdn_step": (I, [P, P, P, P, P, P, F, I, I, I, I, I, ctypes.c_uint, P, P, P, P, P]),
     "osdn_forward": (I, [P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, ctypes.c_uint,
                          P, P, P, P, P, ctypes.c_size_t, P]),

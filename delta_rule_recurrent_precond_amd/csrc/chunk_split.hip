@@ -954,9 +954,9 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 
 }  // namespace
 
-size_t split_workspace_bytes(int B, int H, int T) {
+size_t split_workspace_bytes(int B, int H, int T, bool gate_channels) {
   const long nc = (T + C - 1) / C;
-  return (size_t)B * H * nc * REC;
+  return (size_t)B * H * nc * (gate_channels ? RECK : REC);
 }
 
 namespace {
@@ -998,19 +998,18 @@ void launch_prep_t(int BH, int NC, hipStream_t s, const void *q, const void *k, 
 }
 
 // chunk_prep over every chunk of every head; kGiven takes no input transforms
-// and no per-channel gate
 template <int MODE>
 hipError_t launch_prep(int BH, int NC, hipStream_t s, const void *q, const void *k,
                        const void *kt, const float *beta, int T, unsigned char *rec,
                        const float *r, const float *wout, const float *alpha, unsigned xf) {
   if (NC <= 0) return hipSuccess;
-  constexpr bool TX = MODE != kGiven;  // instances with the transforms and the per-channel gate
+  constexpr bool TX = MODE != kGiven;  // instances with the input transforms
   const bool norm = TX && (xf & kNormQK);
-  if (TX && per_channel(alpha, xf)) {
+  if (per_channel(alpha, xf)) {
     if (norm)
-      launch_prep_t<MODE, TX, false, TX>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+      launch_prep_t<MODE, TX, false, true>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
     else
-      launch_prep_t<MODE, false, false, TX>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+      launch_prep_t<MODE, false, false, true>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
   } else if (norm && alpha) {
     launch_prep_t<MODE, TX, true, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
   } else if (norm) {
@@ -1066,13 +1065,14 @@ hipError_t launch_split_chunk(const ChunkArgs &a, bool given, void *ws, hipStrea
   if (BH == 0) return hipSuccess;
   const int NC = (a.T + C - 1) / C;
   unsigned char *rec = (unsigned char *)ws;
+  const unsigned xf = a.xf & kGateChannels;  // the only flag the given-keys pass takes
   hipError_t e = given ? launch_prep<kGiven>(BH, NC, s, a.q, a.k, a.k_tilde, a.beta, a.T, rec,
-                                             nullptr, nullptr, a.alpha, 0u)
+                                             nullptr, nullptr, a.alpha, xf)
                        : launch_prep<kDeltaNet>(BH, NC, s, a.q, a.k, nullptr, a.beta, a.T, rec,
-                                                nullptr, nullptr, a.alpha, 0u);
+                                                nullptr, nullptr, a.alpha, xf);
   if (e != hipSuccess) return e;
   ChunkArgs b = a;
-  b.xf = 0u;
+  b.xf = xf;
   return launch_state(b, NC, ws, nullptr, s);
 }
 

@@ -71,7 +71,7 @@ hipError_t launch_fused_chunk(const ChunkArgs &a, hipStream_t s);
 // Two-kernel chunkwise pass (bf16, dk = dv = 128, chunk 64): a chunk-parallel
 // prep kernel writes per-chunk operands into `ws` (split_workspace_bytes), a
 // state kernel runs the sequential pass.  given: kt from a.k_tilde, else kt = k.
-size_t split_workspace_bytes(int B, int H, int T);
+size_t split_workspace_bytes(int B, int H, int T, bool gate_channels);
 hipError_t launch_split_chunk(const ChunkArgs &a, bool given, void *ws, hipStream_t s);
 // The same kernel's chunked preconditioner walk alone (bf16, dk = 128).
 bool fused_scan_supported(int dk, int dtype);

@@ -130,26 +130,34 @@ OSDN_EXPORT int osdn_step(const void *q, const void *k, const void *v, const flo
 }
 
 OSDN_EXPORT size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
-                                                  int dtype) {
+                                                  int dtype, unsigned flags) {
   if (check_sizes(B, H, T, dk, dv, chunk, dtype, true, true) != OSDN_OK) return (size_t)-1;
-  return use_fused(dk, dv, chunk, dtype) ? osdn::split_workspace_bytes(B, H, T) : 0;
+  if (flags & ~OSDN_GATE_PER_CHANNEL) return (size_t)-1;
+  return use_fused(dk, dv, chunk, dtype)
+             ? osdn::split_workspace_bytes(B, H, T, (flags & OSDN_GATE_PER_CHANNEL) != 0)
+             : 0;
 }
 
 OSDN_EXPORT int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde, const void *v,
                                const float *beta, const float *alpha, const float *S0, int B,
                                int H, int T, int dk,
-                               int dv, int chunk, int dtype, void *o, float *S_final,
-                               void *workspace, size_t workspace_bytes, void *stream) {
+                               int dv, int chunk, int dtype, unsigned flags, void *o,
+                               float *S_final, void *workspace, size_t workspace_bytes,
+                               void *stream) {
   int st = check_sizes(B, H, T, dk, dv, chunk, dtype, true, true);
   if (st != OSDN_OK) return st;
+  if (flags & ~OSDN_GATE_PER_CHANNEL) return OSDN_ERR_UNSUPPORTED;
   if ((long long)B * H == 0) return OSDN_OK;
   if (T > 0 && (!q || !k || !k_tilde || !v || !beta || !o)) return OSDN_ERR_NULL;
-  osdn::ChunkArgs a{q, k, k_tilde, v, beta, alpha, S0, B, H, T, dk, dv, chunk, dtype, o, S_final};
+  const bool chan = (flags & OSDN_GATE_PER_CHANNEL) != 0;
+  if (T > 0 && chan && !alpha) return OSDN_ERR_NULL;
+  osdn::ChunkArgs a{q, k, k_tilde, v, beta, alpha, S0, B, H, T, dk, dv, chunk, dtype, o, S_final,
+                    transforms(flags)};
   hipStream_t s = (hipStream_t)stream;
   if (use_fused(dk, dv, chunk, dtype)) {
-    if (workspace && workspace_bytes >= osdn::split_workspace_bytes(B, H, T))
+    if (workspace && workspace_bytes >= osdn::split_workspace_bytes(B, H, T, chan))
       return hip_status(osdn::launch_split_chunk(a, true, workspace, s));
-    return hip_status(osdn::launch_fused_chunk(a, s));
+    if (!chan) return hip_status(osdn::launch_fused_chunk(a, s));
   }
   return hip_status(osdn::launch_chunk_generic(a, s));
 }

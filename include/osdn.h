@@ -149,20 +149,25 @@ size_t osdn_precond_scan_workspace_bytes(int B, int H, int T, int dk, int dtype)
  *   chunk                        chunk length
  *   o         [B,H,T,dv] dtype   out: o_t = S_t q_t (required if T > 0)
  *   S_final   [B,H,dv,dk] fp32   out: S_T (optional)
+ *   flags      0 or OSDN_GATE_PER_CHANNEL (alpha [B,H,T,dk], one gate per key
+ *              dimension, as for osdn_forward); the input transforms are not
+ *              taken here (OSDN_ERR_UNSUPPORTED)
  *   workspace  optional device scratch.  When it holds at least
  *              osdn_chunk_fwd_workspace_bytes(...) bytes (a positive number),
  *              the per-chunk work runs chunk-parallel ahead of the sequential
- *              pass (faster); NULL selects the single-kernel pass.
+ *              pass (faster); NULL selects the single-kernel pass (the vector
+ *              chunk kernel with the per-channel gate).
  */
 int osdn_chunk_fwd(const void *q, const void *k, const void *k_tilde, const void *v,
                    const float *beta, const float *alpha, const float *S0, int B, int H,
-                   int T, int dk, int dv, int chunk, int dtype, void *o, float *S_final,
-                   void *workspace, size_t workspace_bytes, void *stream);
+                   int T, int dk, int dv, int chunk, int dtype, unsigned flags, void *o,
+                   float *S_final, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Scratch bytes that let osdn_chunk_fwd run its chunk-parallel path (0 when
- * no path for these arguments uses scratch); (size_t)-1 if the arguments are
- * invalid. */
-size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+/* Scratch bytes that let osdn_chunk_fwd run its chunk-parallel path for these
+ * flags (0 when no path for these arguments uses scratch); (size_t)-1 if the
+ * arguments are invalid. */
+size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                                      unsigned flags);
 
 /*
  * Both phases end to end [summary §2.2 two-phase implementation].

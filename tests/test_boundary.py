@@ -88,8 +88,8 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.osdn_forward_path(0, 4, 8, 16, 16, 16, 0, 0, 0).decode() == "none"
     assert lib.osdn_precond_scan(None, None, None, None, 0.1, 3, 0, 5, 16, 0, None, None, None,
                                  None, None, 0, None) == _lib.OSDN_OK
-    assert lib.osdn_chunk_fwd(None, None, None, None, None, None, None, 0, 2, 5, 16, 16, 16, 0, None,
-                              None, None, 0, None) == _lib.OSDN_OK
+    assert lib.osdn_chunk_fwd(None, None, None, None, None, None, None, 0, 2, 5, 16, 16, 16, 0, 0,
+                              None, None, None, 0, None) == _lib.OSDN_OK
 
 
 def test_scan_and_chunk_reject(lib):
@@ -100,12 +100,18 @@ def test_scan_and_chunk_reject(lib):
                                  None) == _lib.OSDN_ERR_NULL
     assert lib.osdn_precond_scan(p, p, None, None, 0.1, 1, 1, 4, 16, 0, None, None, None, None, None, 0,
                                  None) == _lib.OSDN_ERR_NULL
-    assert lib.osdn_chunk_fwd(p, p, None, p, p, None, None, 1, 1, 4, 16, 16, 16, 0, p, None,
+    assert lib.osdn_chunk_fwd(p, p, None, p, p, None, None, 1, 1, 4, 16, 16, 16, 0, 0, p, None,
                               None, 0, None) == _lib.OSDN_ERR_NULL
-    assert lib.osdn_chunk_fwd(p, p, p, p, p, None, None, 1, 1, 4, 16, 16, 8, 0, p, None,
+    assert lib.osdn_chunk_fwd(p, p, p, p, p, None, None, 1, 1, 4, 16, 16, 8, 0, 0, p, None,
                               None, 0, None) == _lib.OSDN_ERR_UNSUPPORTED
-    assert lib.osdn_chunk_fwd(p, p, p, p, p, None, None, 1, -1, 4, 16, 16, 16, 0, p, None,
+    assert lib.osdn_chunk_fwd(p, p, p, p, p, None, None, 1, -1, 4, 16, 16, 16, 0, 0, p, None,
                               None, 0, None) == _lib.OSDN_ERR_SHAPE
+    # flags: only the per-channel gate, and it needs alpha
+    assert lib.osdn_chunk_fwd(p, p, p, p, p, None, None, 1, 1, 4, 16, 16, 16, 0, 2, p, None,
+                              None, 0, None) == _lib.OSDN_ERR_UNSUPPORTED
+    assert lib.osdn_chunk_fwd(p, p, p, p, p, None, None, 1, 1, 4, 16, 16, 16, 0,
+                              _lib.OSDN_GATE_PER_CHANNEL, p, None, None, 0,
+                              None) == _lib.OSDN_ERR_NULL
 
 
 def test_step_rejects(lib):
@@ -122,11 +128,14 @@ def test_step_rejects(lib):
 
 def test_chunk_workspace_bytes(lib):
     # one 32 KB record per (b, h, chunk of 64) on the bf16 dk = dv = 128 shapes
-    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 128, 128, 64, 0) == 2 * 3 * 3 * 32768
-    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 0, 128, 128, 64, 0) == 0
-    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 64, 128, 64, 0) == 0
-    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 128, 128, 64, 1) == 0
-    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 128, 128, 24, 0) == (1 << 64) - 1
+    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 0) == 2 * 3 * 3 * 32768
+    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 128, 128, 64, 0,
+                                              _lib.OSDN_GATE_PER_CHANNEL) == 2 * 3 * 3 * 66048
+    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 0, 128, 128, 64, 0, 0) == 0
+    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 64, 128, 64, 0, 0) == 0
+    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 128, 128, 64, 1, 0) == 0
+    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 128, 128, 24, 0, 0) == (1 << 64) - 1
+    assert lib.osdn_chunk_fwd_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 2) == (1 << 64) - 1
 
 
 def test_split_workspace_bytes(lib):

@@ -203,6 +203,31 @@ def test_unit_channel_gates_equal_ungated_bitwise(dtype, precond):
     assert torch.equal(a["log_ratio_sum"], b["log_ratio_sum"])
 
 
+@pytest.mark.parametrize("dtype,dk,dv,chunk,T", [("bf16", 128, 128, 64, 300),
+                                                 ("bf16", 128, 128, 64, 64),
+                                                 ("f32", 64, 32, 32, 97)])
+@pytest.mark.parametrize("ws", [True, None])
+def test_chunk_fwd_per_channel_given_ktilde(dtype, dk, dv, chunk, T, ws):
+    """osdn_chunk_fwd with the per-channel gate: the two-kernel pass given its
+    workspace, the vector chunk kernel without."""
+    w = _kda(2, 2, T, dk, dv, chunk, dtype, seed=1300 + T)
+    inp = W.generate(w)
+    S0 = 0.1 * torch.randn(w.B, w.H, dv, dk, generator=torch.Generator().manual_seed(6))
+    kt_ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, eta=inp.eta,
+                            want=("k_tilde",))["k_tilde"]
+    kt = torch.from_numpy(kt_ref).to(inp.k.dtype)
+    dev = inp.to("cuda")
+    _log("per-channel chunk %s workspace=%s" % (w.name, ws))
+    o, S = osdn.chunk_fwd(dev.q, dev.k, kt.cuda(), dev.v, dev.beta, S0.cuda(), chunk,
+                          alpha=dev.alpha, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, None, None, S0, mode="given",
+                         k_given=kt, want=("o", "S"), alpha=inp.alpha)
+    tol = TOL[dtype]
+    assert rowwise_rel(o, ref["o"]) <= tol["o"]
+    assert matrix_rel(S, ref["S"]) <= tol["S"]
+
+
 @pytest.mark.parametrize("dtype,dk,dv", [("f32", 32, 64), ("bf16", 128, 128)])
 def test_per_channel_steps_match_oracle(dtype, dk, dv):
     T = 12
