@@ -48,8 +48,8 @@
  *    alpha acts on S only; the preconditioner walk does not see it.  alpha = 1
  *    gives the ungated results; alpha in [0, 1] is the intended range (decays
  *    below 2^-126 over a chunk are flushed to zero).
- *  - Per-channel gate (osdn_forward, osdn_step with OSDN_GATE_PER_CHANNEL):
- *    alpha is [B][H][T][dk] fp32 (step: [B][H][dk]), one gate per key
+ *  - Per-channel gate (osdn_chunk_fwd, osdn_forward, osdn_step with
+ *    OSDN_GATE_PER_CHANNEL): alpha is [B][H][T][dk] fp32 (step: [B][H][dk]), one gate per key
  *    dimension.  The pages also run OSDN on a Kimi Delta Attention backbone
  *    [summary §4] without printing its update; the reading used here
  *    generalises the scalar gate:
@@ -94,10 +94,13 @@ extern "C" {
 #define OSDN_NORM_QK 2u
 #define OSDN_GATE_LOGITS 4u
 
-/* osdn_forward, osdn_step flag: alpha holds one gate per key dimension (the
- * per-channel gate above; required with this flag).  osdn_forward runs it on
- * the two-phase path for every supported shape, which needs the workspace
- * osdn_forward_workspace_bytes reports for these flags. */
+/* osdn_chunk_fwd, osdn_forward, osdn_step flag: alpha holds one gate per key
+ * dimension (the per-channel gate above; required with this flag).  Given the
+ * workspace osdn_forward_workspace_bytes (osdn_chunk_fwd_workspace_bytes)
+ * reports for these flags, the matrix-core shapes run the multi-launch
+ * pipeline; otherwise the forward runs the two-phase path (which needs the
+ * write-key buffer) and osdn_chunk_fwd the vector chunk kernel.  The single
+ * fused kernel does not take it. */
 #define OSDN_GATE_PER_CHANNEL 8u
 
 /*
