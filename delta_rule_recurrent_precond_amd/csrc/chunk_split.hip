@@ -637,12 +637,22 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // ---------------------------------------------------------------------------
 constexpr int ST = 768;        // threads
 constexpr int NL = ST - 256;   // loader lanes
-constexpr int VP = 40;         // padded row (halves) of the staged [64][32] value tile
+// k and q rows in the state kernel's LDS: 256 bytes, no padding, held in the
+// paired k order of the 16x16x32 products, so that each operand is one 16-byte
+// read.  16-byte chunk 4 kk + g of row t holds k slots 32 kk + 4 g .. +3 and
+// 32 kk + 16 + 4 g .. +3, stored at chunk (4 kk + g) ^ (t & 15): the sixteen rows
+// one read covers then spread over all banks.
+__device__ __forceinline__ int kq_chunk(int t, int chunk) { return t * 128 + 8 * (chunk ^ (t & 15)); }
+// value-tile row staged by loader lane lt < 256 (its channels: 8 ((lt >> 4) & 3) .. +7)
+__device__ __forceinline__ int vrow(int lt) {
+  const int w = lt >> 4, i = lt & 15;
+  return 32 * ((w >> 2) & 1) + 16 * (i >> 3) + 8 * (w >> 3) + (i & 7);
+}
 
 struct StateSmem {
-  f16 K[2][C * KP];
-  f16 Q[2][C * KP];
-  f16 V[2][C * VP];
+  f16 K[2][C * 128];  // kq_chunk layout
+  f16 Q[2][C * 128];
+  f16x8 V[2][2][2][64];  // value tile as operands [buf][sn][m >> 1][lane]: rows 16 m + c16, 4 channels
   unsigned char rec[2][OFF_END];  // KtF, TmA, PA, ds, factors of the chunk
   float b[2][C];
   f16x8 Sx[2][2][4][64];  // fp16 S^T at a chunk's start [parity][sn][kk][lane], paired order
@@ -717,8 +727,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
           R.kq[u] = *(const uint4 *)((p < 1024 ? k : q) + (t0 + t) * DK + (pp & 15) * 8);
       }
       {
-        const int t = min((lt & 255) >> 2, L - 1);
-        R.v = *(const uint4 *)(v + (t0 + t) * 128 + j0 + (lt & 3) * 8);
+        const int t = min(vrow(lt & 255), L - 1);
+        R.v = *(const uint4 *)(v + (t0 + t) * 128 + j0 + ((lt >> 4) & 3) * 8);
       }
 #pragma unroll
       for (int u = 0; u < NR; ++u) {
@@ -733,13 +743,32 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int u = 0; u < NKQ; ++u) {
-        const int p = lt + NL * u, pp = p & 1023, t = pp >> 4, i0 = (pp & 15) * 8;
-        if (p < 2048)
-          *(f16x8 *)&(p < 1024 ? sm.K : sm.Q)[buf][t * KP + i0] =
-              t < L ? (GK ? __builtin_bit_cast(f16x8, R.kq[u]) : cvt8(R.kq[u])) : z8;
+        // piece jp of row t (slots 8 jp .. +7) goes as two halves to chunks
+        // 4 kk + 2 (jp & 1) and the next one, in their half (jp >> 1) & 1.  LDS
+        // writes are served 16 lanes (128 bytes) a clock: pieces with jp >= 8
+        // write their second half first, so that each write of the 16 lanes
+        // of a row covers 8 chunks of distinct residue mod 8, all banks once.
+        const int p = lt + NL * u, pp = p & 1023, t = pp >> 4, jp = pp & 15;
+        const int c0 = 4 * (jp >> 2) + 2 * (jp & 1), hh = 4 * ((jp >> 1) & 1);
+        const bool sw = jp >= 8;
+        if (p < 2048) {
+          const f16x8 x = t < L ? (GK ? __builtin_bit_cast(f16x8, R.kq[u]) : cvt8(R.kq[u])) : z8;
+          const f16x4 lo = f16x4{x[0], x[1], x[2], x[3]}, hi = f16x4{x[4], x[5], x[6], x[7]};
+          f16 *base = (p < 1024 ? sm.K : sm.Q)[buf];
+          *(f16x4 *)&base[kq_chunk(t, c0 + sw) + hh] = sw ? hi : lo;
+          *(f16x4 *)&base[kq_chunk(t, c0 + !sw) + hh] = sw ? lo : hi;
+        }
       }
-      if (lt < 256)
-        *(f16x8 *)&sm.V[buf][(lt >> 2) * VP + (lt & 3) * 8] = (lt >> 2) < L ? cvt8(R.v) : z8;
+      if (lt < 256) {
+        // row r, channels 8 q .. +7 of the tile: the operands of sub-tile q >> 1,
+        // lanes r % 16 + 16 g for g = 2 (q & 1) and the next, half m & 1.  The
+        // 16 lanes of one write cover rows of 8 residues mod 8 and both m parities.
+        const int r = vrow(lt), q = (lt >> 4) & 3, m = r >> 4, g0 = 2 * (q & 1);
+        const f16x8 x = r < L ? cvt8(R.v) : z8;
+        f16 *vb = (f16 *)sm.V[buf][q >> 1][m >> 1];
+        *(f16x4 *)&vb[((r & 15) + 16 * g0) * 8 + 4 * (m & 1)] = f16x4{x[0], x[1], x[2], x[3]};
+        *(f16x4 *)&vb[((r & 15) + 16 * g0 + 16) * 8 + 4 * (m & 1)] = f16x4{x[4], x[5], x[6], x[7]};
+      }
       uint4 *rd = (uint4 *)sm.rec[buf];
 #pragma unroll
       for (int u = 0; u < NR; ++u) {
@@ -830,19 +859,21 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       // K S^T, then R = diag(beta)(V - K S^T) with the values turned into the
       // result layout
       f16x4 rr[4];
+      const f16x8 Vv[2] = {sm.V[cb][sn][0][lane], sm.V[cb][sn][1][lane]};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f16 *kr = &Kc[(16 * m + c16) * KP];
         f32x4 a = zero4();
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) a = mma32(ldpk(kr, 32 * kk, g), Sb[kk], a);
+        for (int kk = 0; kk < 4; ++kk)
+          a = mma32(ld8(&Kc[kq_chunk(16 * m + c16, 4 * kk + g)]), Sb[kk], a);
         if (SCALED) {
           const f32x4 s4 = *(const f32x4 *)(sm.rec[cb] + OFF_KF + 4 * (16 * m + 4 * g));
 #pragma unroll
           for (int e = 0; e < 4; ++e) a[e] *= s4[e];
         }
-        const f16x4 vv =
-            h4(mma16(ld4(&sm.V[cb][(16 * m + c16) * VP + 16 * sn + 4 * g]), ident, zero4()));
+        const f16x8 &vp = Vv[m >> 1];
+        const f16x4 vin = (m & 1) ? f16x4{vp[4], vp[5], vp[6], vp[7]} : f16x4{vp[0], vp[1], vp[2], vp[3]};
+        const f16x4 vv = h4(mma16(vin, ident, zero4()));
         const f32x4 b4 = *(const f32x4 *)&sm.b[cb][16 * m + 4 * g];
 #pragma unroll
         for (int e = 0; e < 4; ++e) rr[m][e] = h(b4[e] * ((float)vv[e] - a[e]));
@@ -932,10 +963,10 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         const f16 *Qc = sm.Q[cb];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const f16 *qr = &Qc[(16 * m + c16) * KP];
           f32x4 a = zero4();
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) a = mma32(ldpk(qr, 32 * kk, g), Sb[kk], a);
+          for (int kk = 0; kk < 4; ++kk)
+            a = mma32(ld8(&Qc[kq_chunk(16 * m + c16, 4 * kk + g)]), Sb[kk], a);
           if (SCALED) {
             const f32x4 s4 = *(const f32x4 *)(sm.rec[cb] + OFF_QF + 4 * (16 * m + 4 * g));
 #pragma unroll

@@ -210,27 +210,33 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 }
 
 // ---------------------------------------------------------------------------
-// walk: one workgroup of 4 waves per (b, h), sequential over chunks c0..c1-1
+// walk: one workgroup of 8 waves per (b, h), sequential over chunks c0..c1-1
 // (the entry d of chunk c0 is d0, or what the launch before left in wout),
-// three barriers per chunk:
-//   A  b_t = <d, p_t> (4 threads per token), rhs_t = 1 - beta_t Gamma_t b_t
-//   B  g = (I + M)^-1 rhs (4 threads per token); c_t, w_t = R_{L,t} alpha_t g_t
-//   C  threads 0-127: d <- Gamma_L d + sum_t w_t p_t, one dimension each (kept
-//      in a register); threads 128-255: log rho_t, and the LDS stores of the
-//      next chunk, whose keys and record they load two chunks ahead (two
-//      register sets), so the loads have two iterations to arrive
+// three barriers per chunk.  Waves 0-3 run the chain, reading p_t = k_t (.) k_t
+// in fp32 from LDS:
+//   A  b_t = <d, p_t> (4 threads per token), rhs_t = 1 - u_t s_t b_t
+//   B  g = (I + M)^-1 rhs (4 threads per token); c_t, w_t = R_{L,t} alpha_t s_t g_t
+//   C  d <- Gamma_L d + sum_t w_t p_t: wave v takes dimensions 32 v .. +31, its
+//      two lane halves one half of the tokens each, joined by a lane-half swap;
+//      lane l < 32 keeps d of its dimension in a register
+// Waves 4-7 keep the chain fed: they load the keys and the record three
+// chunks ahead (three register sets), square the keys into p (fp32) as they
+// store them, and compute log rho_t, so that none of this sits on the chain.
 // ---------------------------------------------------------------------------
+constexpr int PS = 144;  // row (floats) of p in LDS: 16 dwords past a multiple of 64
+                         // spreads the 16-byte reads of phase A over all banks
+constexpr int WT = 512;  // threads
+
 struct alignas(16) WalkSmem {
-  bf16 K[2][C * KP];         // keys
+  float P[2][C * PS];        // p_t = k_t (.) k_t
   float Mi[2][C * FP];       // (I + M)^-1
   float vec[2][4][C];        // u = beta Gamma, alpha, R_{L,t} alpha, the 1/||k||^2 factor
   float gL[2][4];            // Gamma_L
   float d[DK];               // entry d of the chunk in the pass
   float rhs[C], w[C], g[C];
-  float red[4];
 };
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(WT)
 walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
      const float *__restrict__ d0, int T_, int NC, int c0, int c1, float *__restrict__ wout,
      float *__restrict__ d_final, float *__restrict__ log_ratio,
@@ -239,100 +245,155 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
   WalkSmem &sm = *reinterpret_cast<WalkSmem *>(smem_raw);
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
-  const int t = tid >> 2, part = tid & 3;  // phases A and B
-  const bool owner = tid < DK;             // phase C: dimension tid
-  const int lt = tid - DK;                 // loader index (threads 128-255)
 
-  // loads of one chunk by threads 128-255: 1024 pieces of 8 keys, 8 each; the
-  // record as 1089 pieces of 16 bytes (1024 of the inverse, 64 of vectors,
-  // Gamma_L), 9 each
-  constexpr int RP = (W_GL + 16) / 16;
-  constexpr int NRP = (RP + 127) / 128;
-  struct Regs {
-    uint4 k[8], rr[NRP];
-    int L;
-  };
-  Regs ra, rb;
-  auto load = [&](Regs &R, int cc) {
-    cc = min(cc, c1 - 1);
-    const long t0 = (long)bh * T_ + (long)cc * C;
-    const int L = min(C, T_ - cc * C);
-    R.L = L;
+  if (tid >= 256) {
+    // ================================ loaders ================================
+    // a chunk: 1024 pieces of 8 keys (4 per lane) and the record as 1089
+    // pieces of 16 bytes (1024 of the inverse, 64 of vectors, Gamma_L)
+    const int lt = tid - 256;
+    constexpr int RP = (W_GL + 16) / 16;
+    constexpr int NRP = (RP + 255) / 256;
+    struct Regs {
+      uint4 k[4], rr[NRP];
+    };
+    Regs ra, rb, rc;
+    // chunk cc clamped to the last one of the launch: loads past it reread it
+    auto load = [&](Regs &R, int cc) {
+      cc = min(cc, c1 - 1);
+      const long t0 = (long)bh * T_ + (long)cc * C;
+      const int L = min(C, T_ - cc * C);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int p = lt + 128 * u, tt = min(p >> 4, L - 1);
-      R.k[u] = *(const uint4 *)(k + (t0 + tt) * DK + (p & 15) * 8);
-    }
-    const uint4 *rs = (const uint4 *)(wrec + ((long)bh * NC + cc) * WREC);
-#pragma unroll
-    for (int u = 0; u < NRP; ++u) R.rr[u] = rs[min(lt + 128 * u, RP - 1)];
-  };
-  auto stash = [&](const Regs &R, int buf) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int p = lt + 128 * u, tt = p >> 4, i0 = (p & 15) * 8;
-      *(uint4 *)&sm.K[buf][tt * KP + i0] = tt < R.L ? R.k[u] : uint4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < NRP; ++u) {
-      const int p = lt + 128 * u;
-      if (p < C * C / 4) {
-        *(uint4 *)&sm.Mi[buf][(p >> 4) * FP + (p & 15) * 4] = R.rr[u];
-      } else if (p < RP - 1) {
-        const int v = p - C * C / 4;  // 16 pieces per vector
-        *(uint4 *)&sm.vec[buf][v >> 4][(v & 15) * 4] = R.rr[u];
-      } else if (p == RP - 1) {
-        *(uint4 *)&sm.gL[buf][0] = R.rr[u];
+      for (int u = 0; u < 4; ++u) {
+        const int p = lt + 256 * u, tt = min(p >> 4, L - 1);
+        R.k[u] = *(const uint4 *)(k + (t0 + tt) * DK + (p & 15) * 8);
       }
-    }
-  };
-
-  float dreg = 0.f;  // owners: d of their dimension, entry value of the chunk in the pass
-  if (owner) {
-    if (c0 == 0) {
-      dreg = d0 ? d0[(long)bh * DK + tid] : 1.0f;
-      if (NC > 0) wout[(long)bh * NC * WOUT + tid] = dreg;
-    } else {
-      dreg = wout[((long)bh * NC + c0) * WOUT + tid];
-    }
-    sm.d[tid] = dreg;
-  } else if (c1 > c0) {
-    load(ra, c0);
-    load(rb, c0 + 1);
-    stash(ra, c0 & 1);
-  }
-  float lr_acc = 0.f;  // sum of log rho_t (threads 128-191)
-  __syncthreads();
-
-  auto iteration = [&](int c, Regs &next, Regs &free_) {
-    const int cb = c & 1;
-    const long t0 = (long)bh * T_ + (long)c * C;
-    const int L = min(C, T_ - c * C);
-    if (!owner) load(free_, c + 2);
-    // A
-    {
-      const bf16 *kr = &sm.K[cb][t * KP + 32 * part];
-      float b0 = 0.f, b1 = 0.f;
+      const uint4 *rs = (const uint4 *)(wrec + ((long)bh * NC + cc) * WREC);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 kv = *(const uint4 *)(kr + 8 * j);
-        const unsigned short *sv = (const unsigned short *)&kv;
-        const int i0 = 32 * part + 8 * j;
-        const float4 p0 = *(const float4 *)&sm.d[i0], p1 = *(const float4 *)&sm.d[i0 + 4];
-        const float dv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      for (int u = 0; u < NRP; ++u) R.rr[u] = rs[min(lt + 256 * u, RP - 1)];
+    };
+    // the record of chunk cc into LDS buffer cc & 1
+    auto stash_rec = [&](const Regs &R, int cc) {
+      const int buf = cc & 1;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float x0 = bf2f(sv[e]), x1 = bf2f(sv[e + 1]);
-          b0 = fmaf(dv[e], x0 * x0, b0);
-          b1 = fmaf(dv[e + 1], x1 * x1, b1);
+      for (int u = 0; u < NRP; ++u) {
+        const int p = lt + 256 * u;
+        if (p < C * C / 4) {
+          *(uint4 *)&sm.Mi[buf][(p >> 4) * FP + (p & 15) * 4] = R.rr[u];
+        } else if (p < RP - 1) {
+          const int v = p - C * C / 4;  // 16 pieces per vector
+          *(uint4 *)&sm.vec[buf][v >> 4][(v & 15) * 4] = R.rr[u];
+        } else if (p == RP - 1) {
+          *(uint4 *)&sm.gL[buf][0] = R.rr[u];
         }
       }
+    };
+    // the keys of chunk cc, squared, into LDS buffer cc & 1 (rows past the end
+    // zero).  A piece is stored as two 16-byte halves; pieces with bit 2 set
+    // store their second half first, so that the 8 lanes of one LDS write
+    // clock cover distinct banks.
+    auto stash_p = [&](const Regs &R, int cc) {
+      const int buf = cc & 1, L = min(C, T_ - cc * C);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = lt + 256 * u, tt = p >> 4, i0 = (p & 15) * 8;
+        const unsigned short *s = (const unsigned short *)&R.k[u];
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = bf2f(s[e]);
+          x[e] = tt < L ? y * y : 0.f;
+        }
+        const bool sw = (p & 4) != 0;
+        const float4 f = {sw ? x[4] : x[0], sw ? x[5] : x[1], sw ? x[6] : x[2], sw ? x[7] : x[3]};
+        const float4 n = {sw ? x[0] : x[4], sw ? x[1] : x[5], sw ? x[2] : x[6], sw ? x[3] : x[7]};
+        float *row = &sm.P[buf][tt * PS + i0];
+        *(float4 *)(row + (sw ? 4 : 0)) = f;
+        *(float4 *)(row + (sw ? 0 : 4)) = n;
+      }
+    };
+    float lr_acc = 0.f;  // sum of log rho_t (wave 4)
+    // log rho_t = log g_t^2 of chunk c (g from phase B), wave 4
+    auto log_rho = [&](int c) {
+      const int L = min(C, T_ - c * C);
+      if (lt < C && lt < L) {
+        const float gt = sm.g[lt];
+        const float lr = logf(gt * gt);
+        lr_acc += lr;
+        if (log_ratio) log_ratio[(long)bh * T_ + (long)c * C + lt] = lr;
+      }
+    };
+    // one iteration: loads of chunk c+3 into the set that held chunk c, the
+    // record of chunk c+1 (window A), its keys (window B), log rho of chunk c
+    // (window C)
+    auto iteration = [&](int c, Regs &free_, const Regs &next) {
+      load(free_, c + 3);
+      if (c + 1 < c1) stash_rec(next, c + 1);
+      __syncthreads();
+      if (c + 1 < c1) stash_p(next, c + 1);
+      __syncthreads();
+      log_rho(c);
+      __syncthreads();
+    };
+    if (c1 > c0) {
+      load(ra, c0);
+      load(rb, c0 + 1);
+      load(rc, c0 + 2);
+      stash_rec(ra, c0);
+      stash_p(ra, c0);
+    }
+    __syncthreads();
+    for (int c = c0; c < c1; c += 3) {
+      iteration(c, ra, rb);
+      if (c + 1 < c1) iteration(c + 1, rb, rc);
+      if (c + 2 < c1) iteration(c + 2, rc, ra);
+    }
+    if (log_ratio_sum && lt < 64) {
+      // this launch's chunks, added to the sums of the launches before it
+      const float s = wave_sum(lr_acc);
+      if (lt == 0) log_ratio_sum[bh] = c0 == 0 ? s : log_ratio_sum[bh] + s;
+    }
+    return;
+  }
+
+  // ================================= chain ==================================
+  const int t = tid >> 2, part = tid & 3;       // phases A and B
+  const int wv = tid >> 6, l = tid & 63;
+  const int dim = 32 * wv + (l & 31), half = l >> 5;  // phase C
+  float dreg = 0.f;  // lanes l < 32: d of dimension dim, entry value of the chunk in the pass
+  if (half == 0) {
+    if (c0 == 0) {
+      dreg = d0 ? d0[(long)bh * DK + dim] : 1.0f;
+      if (NC > 0) wout[(long)bh * NC * WOUT + dim] = dreg;
+    } else {
+      dreg = wout[((long)bh * NC + c0) * WOUT + dim];
+    }
+    sm.d[dim] = dreg;
+  }
+  __syncthreads();
+
+  for (int c = c0; c < c1; ++c) {
+    const int cb = c & 1;
+    // A
+    {
+      const float ut = sm.vec[cb][0][t], st = sm.vec[cb][3][t];
+      const float *pr = &sm.P[cb][t * PS];
+      float b0 = 0.f, b1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i0 = 4 * (part + 4 * j);
+        const float4 p4 = *(const float4 *)(pr + i0), d4 = *(const float4 *)&sm.d[i0];
+        b0 = fmaf(d4.x, p4.x, b0);
+        b1 = fmaf(d4.y, p4.y, b1);
+        b0 = fmaf(d4.z, p4.z, b0);
+        b1 = fmaf(d4.w, p4.w, b1);
+      }
       const float b = group_sum<4>(b0 + b1);
-      if (part == 0) sm.rhs[t] = 1.0f - sm.vec[cb][0][t] * (sm.vec[cb][3][t] * b);
+      if (part == 0) sm.rhs[t] = 1.0f - ut * (st * b);
     }
     __syncthreads();
     // B
     {
+      const float wa = sm.vec[cb][2][t], st = sm.vec[cb][3][t], at = sm.vec[cb][1][t];
       const float *mrow = &sm.Mi[cb][t * FP + 16 * part];
       const float *rv = &sm.rhs[16 * part];
       float ga = 0.f, gb = 0.f;
@@ -346,63 +407,40 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
       }
       const float gt = group_sum<4>(ga + gb);
       if (part == 0) {
-        sm.w[t] = sm.vec[cb][2][t] * gt * sm.vec[cb][3][t];
+        sm.w[t] = wa * gt * st;
         sm.g[t] = gt;
-        wout[((long)bh * NC + c) * WOUT + DK + t] = sm.vec[cb][1][t] * gt;
+        wout[((long)bh * NC + c) * WOUT + DK + t] = at * gt;
       }
     }
     __syncthreads();
-    // C
-    if (owner) {
-      // every read issued before the sum (the scheduling barrier keeps them there)
-      bf16 kx[C];
-      float4 wv[C / 4];
-#pragma unroll
-      for (int s = 0; s < C; ++s) kx[s] = sm.K[cb][s * KP + tid];
-#pragma unroll
-      for (int j = 0; j < C / 4; ++j) wv[j] = *(const float4 *)&sm.w[4 * j];
+    // C: tokens 8 j + 4 half + e of dimension dim
+    {
+      const float *pc = &sm.P[cb][dim];
       const float gl = sm.gL[cb][0];
-      __builtin_amdgcn_sched_barrier(0);
       float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < C / 4; ++j) {
-        const float x0 = (float)kx[4 * j], x1 = (float)kx[4 * j + 1];
-        const float x2 = (float)kx[4 * j + 2], x3 = (float)kx[4 * j + 3];
-        a0 = fmaf(wv[j].x, x0 * x0, a0);
-        a1 = fmaf(wv[j].y, x1 * x1, a1);
-        a0 = fmaf(wv[j].z, x2 * x2, a0);
-        a1 = fmaf(wv[j].w, x3 * x3, a1);
+      for (int j = 0; j < 8; ++j) {
+        const int s0 = 8 * j + 4 * half;
+        const float4 w4 = *(const float4 *)&sm.w[s0];
+        a0 = fmaf(w4.x, pc[s0 * PS], a0);
+        a1 = fmaf(w4.y, pc[(s0 + 1) * PS], a1);
+        a0 = fmaf(w4.z, pc[(s0 + 2) * PS], a0);
+        a1 = fmaf(w4.w, pc[(s0 + 3) * PS], a1);
       }
-      dreg = fmaf(gl, dreg, a0 + a1);
-      sm.d[tid] = dreg;
-      if (c + 1 < NC) wout[((long)bh * NC + c + 1) * WOUT + tid] = dreg;  // next entry d
-    } else {
-      if (lt < C && lt < L) {
-        const float gt = sm.g[lt];
-        const float lr = logf(gt * gt);  // log rho_t
-        lr_acc += lr;
-        if (log_ratio) log_ratio[t0 + lt] = lr;
+      const float a = a0 + a1;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a),
+                                                       false, false);
+      const float sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      if (half == 0) {
+        dreg = fmaf(gl, dreg, sum);
+        sm.d[dim] = dreg;
+        if (c + 1 < NC) wout[((long)bh * NC + c + 1) * WOUT + dim] = dreg;  // next entry d
       }
-      if (c + 1 < c1) stash(next, cb ^ 1);
     }
     __syncthreads();
-  };
-  for (int c = c0; c < c1; c += 2) {
-    iteration(c, rb, ra);
-    if (c + 1 < c1) iteration(c + 1, ra, rb);
   }
 
-  if (d_final && owner && c1 == NC) d_final[(long)bh * DK + tid] = dreg;
-  if (log_ratio_sum) {
-    // this launch's chunks, added to the sums of the launches before it
-    const float s = wave_sum(lr_acc);
-    if ((tid & 63) == 0) sm.red[tid >> 6] = s;
-    __syncthreads();
-    if (tid == 0) {
-      const float part = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
-      log_ratio_sum[bh] = c0 == 0 ? part : log_ratio_sum[bh] + part;
-    }
-  }
+  if (d_final && half == 0 && c1 == NC) d_final[(long)bh * DK + dim] = dreg;
 }
 
 // ---------------------------------------------------------------------------
@@ -487,7 +525,7 @@ hipError_t launch_walk_pass(const ScanArgs &a, int c0, int c1, const unsigned ch
   hipError_t e = hipFuncSetAttribute((const void *)walk,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(walk, dim3((unsigned)BH), dim3(256), shm, s, (const bf16 *)a.k,
+  hipLaunchKernelGGL(walk, dim3((unsigned)BH), dim3(WT), shm, s, (const bf16 *)a.k,
                      wrec, a.d0, a.T, NC, c0, c1, wout, a.d_final, a.log_ratio, a.log_ratio_sum);
   return hipGetLastError();
 }
