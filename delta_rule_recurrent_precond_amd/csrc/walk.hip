@@ -219,13 +219,19 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 //   C  d <- Gamma_L d + sum_t w_t p_t: wave v takes dimensions 32 v .. +31, its
 //      two lane halves one half of the tokens each, joined by a lane-half swap;
 //      lane l < 32 keeps d of its dimension in a register
-// Waves 4-7 keep the chain fed: they load the keys and the record three
-// chunks ahead (three register sets), square the keys into p (fp32) as they
-// store them, and compute log rho_t, so that none of this sits on the chain.
+// Waves 4-7 keep the chain fed: they load the keys and the record four
+// chunks ahead (four register sets: a load has over two iterations to
+// arrive), square the keys into p (fp32) as they store them, and compute
+// log rho_t, so that none of this sits on the chain.
 // ---------------------------------------------------------------------------
 constexpr int PS = 144;  // row (floats) of p in LDS: 16 dwords past a multiple of 64
                          // spreads the 16-byte reads of phase A over all banks
 constexpr int WT = 512;  // threads
+// Column of key dimension i in a row of p: 16-byte halves of each 32-byte piece
+// swapped in the pieces whose index has bit 2 set.  The loaders then store the
+// first half of every piece with one instruction and the 8 lanes of each LDS
+// write clock still cover distinct banks.
+__device__ __forceinline__ int p_slot(int i) { return i ^ ((i >> 3) & 4); }
 
 struct alignas(16) WalkSmem {
   float P[2][C * PS];        // p_t = k_t (.) k_t
@@ -256,16 +262,16 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
     struct Regs {
       uint4 k[4], rr[NRP];
     };
-    Regs ra, rb, rc;
+    Regs ra, rb, rc, rd;
     // chunk cc clamped to the last one of the launch: loads past it reread it
     auto load = [&](Regs &R, int cc) {
       cc = min(cc, c1 - 1);
-      const long t0 = (long)bh * T_ + (long)cc * C;
+      const bf16 *kc = k + ((long)bh * T_ + (long)cc * C) * DK;  // uniform base, 32-bit offsets
       const int L = min(C, T_ - cc * C);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int p = lt + 256 * u, tt = min(p >> 4, L - 1);
-        R.k[u] = *(const uint4 *)(k + (t0 + tt) * DK + (p & 15) * 8);
+        R.k[u] = *(const uint4 *)(kc + tt * DK + (p & 15) * 8);
       }
       const uint4 *rs = (const uint4 *)(wrec + ((long)bh * NC + cc) * WREC);
 #pragma unroll
@@ -287,28 +293,27 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
         }
       }
     };
-    // the keys of chunk cc, squared, into LDS buffer cc & 1 (rows past the end
-    // zero).  A piece is stored as two 16-byte halves; pieces with bit 2 set
-    // store their second half first, so that the 8 lanes of one LDS write
-    // clock cover distinct banks.
-    auto stash_p = [&](const Regs &R, int cc) {
+    // pieces u0, u0 + 1 of the keys of chunk cc, squared, into LDS buffer
+    // cc & 1 (rows past the end zero), in the p_slot layout
+    auto stash_p = [&](const Regs &R, int cc, int u0) {
       const int buf = cc & 1, L = min(C, T_ - cc * C);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = u0; u < u0 + 2; ++u) {
         const int p = lt + 256 * u, tt = p >> 4, i0 = (p & 15) * 8;
         const unsigned short *s = (const unsigned short *)&R.k[u];
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float y = bf2f(s[e]);
-          x[e] = tt < L ? y * y : 0.f;
+          x[e] = y * y;
         }
-        const bool sw = (p & 4) != 0;
-        const float4 f = {sw ? x[4] : x[0], sw ? x[5] : x[1], sw ? x[6] : x[2], sw ? x[7] : x[3]};
-        const float4 n = {sw ? x[0] : x[4], sw ? x[1] : x[5], sw ? x[2] : x[6], sw ? x[3] : x[7]};
-        float *row = &sm.P[buf][tt * PS + i0];
-        *(float4 *)(row + (sw ? 4 : 0)) = f;
-        *(float4 *)(row + (sw ? 0 : 4)) = n;
+        if (L < C && tt >= L) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+        float *row = &sm.P[buf][tt * PS];
+        *(float4 *)(row + p_slot(i0)) = float4{x[0], x[1], x[2], x[3]};
+        *(float4 *)(row + p_slot(i0 + 4)) = float4{x[4], x[5], x[6], x[7]};
       }
     };
     float lr_acc = 0.f;  // sum of log rho_t (wave 4)
@@ -322,30 +327,37 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
         if (log_ratio) log_ratio[(long)bh * T_ + (long)c * C + lt] = lr;
       }
     };
-    // one iteration: loads of chunk c+3 into the set that held chunk c, the
-    // record of chunk c+1 (window A), its keys (window B), log rho of chunk c
-    // (window C)
+    // one iteration, its work spread so that no window outlasts the chain's
+    // phase: the record of chunk c+1 and half its keys (window A), the other
+    // half (window B), log rho of chunk c and the loads of chunk c+4 into the
+    // set that held chunk c (window C)
     auto iteration = [&](int c, Regs &free_, const Regs &next) {
-      load(free_, c + 3);
-      if (c + 1 < c1) stash_rec(next, c + 1);
+      if (c + 1 < c1) {
+        stash_rec(next, c + 1);
+        stash_p(next, c + 1, 0);
+      }
       __syncthreads();
-      if (c + 1 < c1) stash_p(next, c + 1);
+      if (c + 1 < c1) stash_p(next, c + 1, 2);
       __syncthreads();
       log_rho(c);
+      load(free_, c + 4);
       __syncthreads();
     };
     if (c1 > c0) {
       load(ra, c0);
       load(rb, c0 + 1);
       load(rc, c0 + 2);
+      load(rd, c0 + 3);
       stash_rec(ra, c0);
-      stash_p(ra, c0);
+      stash_p(ra, c0, 0);
+      stash_p(ra, c0, 2);
     }
     __syncthreads();
-    for (int c = c0; c < c1; c += 3) {
+    for (int c = c0; c < c1; c += 4) {
       iteration(c, ra, rb);
       if (c + 1 < c1) iteration(c + 1, rb, rc);
-      if (c + 2 < c1) iteration(c + 2, rc, ra);
+      if (c + 2 < c1) iteration(c + 2, rc, rd);
+      if (c + 3 < c1) iteration(c + 3, rd, ra);
     }
     if (log_ratio_sum && lt < 64) {
       // this launch's chunks, added to the sums of the launches before it
@@ -381,7 +393,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i0 = 4 * (part + 4 * j);
-        const float4 p4 = *(const float4 *)(pr + i0), d4 = *(const float4 *)&sm.d[i0];
+        const float4 p4 = *(const float4 *)(pr + p_slot(i0)), d4 = *(const float4 *)&sm.d[i0];
         b0 = fmaf(d4.x, p4.x, b0);
         b1 = fmaf(d4.y, p4.y, b1);
         b0 = fmaf(d4.z, p4.z, b0);
@@ -415,7 +427,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
     __syncthreads();
     // C: tokens 8 j + 4 half + e of dimension dim
     {
-      const float *pc = &sm.P[cb][dim];
+      const float *pc = &sm.P[cb][p_slot(dim)];
       const float gl = sm.gL[cb][0];
       float a0 = 0.f, a1 = 0.f;
 #pragma unroll
