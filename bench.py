@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "OSDN fwd tokens/s (scan+chunk WY), H=16 dk=dv=128 T=4096; % of roofline"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix cores, TFLOP/s
 CACHE_BYTES = 256 << 20
 
 
@@ -65,10 +66,19 @@ def algorithmic_bytes(w, path: str) -> int:
     return th * per + heads * (w.dv * w.dk * 4 + w.dk * 4)
 
 
-def stored_traffic(kernel: str, workload: str):
-    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
-    for the current kernel sources (profiles/traffic.json)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def algorithmic_flops(w) -> int:
+    """Flops of one forward: per token-head the chunkwise pass (chunk form of
+    the gist.science summary, §2.1: gram K K~^T, (I + A)^-1, W and U, the pseudo-
+    values X, Q S^T, the scores Q K~^T and their product with X, the state
+    update) is 6 dk dv + 2 C (3 dk + 2 dv) + C^2 / 3, and the preconditioner
+    walk (§2.2) about 8 dk."""
+    C = w.chunk
+    per = 6 * w.dk * w.dv + 2 * C * (3 * w.dk + 2 * w.dv) + C * C / 3 + 8 * w.dk
+    return int(w.B * w.H * w.T * per)
+
+
+def _stored(name: str, kernel: str, workload: str):
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     try:
@@ -77,7 +87,33 @@ def stored_traffic(kernel: str, workload: str):
         return None
     if not rec or rec.get("sources") != kernel_sources_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def stored_mfma(kernel: str, workload: str):
+    """Matrix-core flops per call counted by rocprofv3 (profiles/mfma.json), if
+    taken for the current kernel sources."""
+    rec = _stored("mfma.json", kernel, workload)
+    if rec is None:
+        return None
+    return {"f16_flops": rec.get("f16_flops_per_call"), "f32_flops": rec.get("f32_flops_per_call")}
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
+    for the current kernel sources (profiles/traffic.json)."""
+    rec = _stored("traffic.json", kernel, workload)
+    return rec.get("bytes_per_launch") if rec else None
 
 
 def time_launches(fn, steps, warmup, torch):
@@ -112,7 +148,24 @@ def cpu_baseline(w, inp):
     tokens = len(heads) * w.T / w.H
     return {"value": reps * tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "whole workload (%d (b,h) sequences x T=%d), fp64 token-serial, %d runs, "
-                      "%.2f s wall on %d threads" % (len(heads), w.T, reps, wall, threads)}
+                      "%.2f s wall on %d threads" % (len(heads), w.T, reps, wall, threads),
+            "cpu_model": host_cpu_model()}
+
+
+def cpu_single_thread(W):
+    """The oracle on one host thread over the two smallest workloads (the tiny
+    fp32 one and the 340M-style layer), tokens/s."""
+    from oracle import oracle
+    res = {}
+    for key in ("tiny", "340m"):
+        w = W.CONFIGS[key]
+        inp = W.generate(w)
+        t0 = time.perf_counter()
+        oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.r, eta=inp.eta,
+                       heads=list(range(w.B * w.H)), want=("o", "S", "d"), threads=1)
+        dt = time.perf_counter() - t0
+        res[key] = {"workload": w.name, "tokens_per_s": w.B * w.T / dt, "seconds": dt}
+    return res
 
 
 def bench_step(args, torch, osdn, W):
@@ -367,6 +420,24 @@ def main():
                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                           "traffic": stored_traffic(kname, args.workload),
                           "kernel": kname, "algorithmic_bytes": kbytes, "kernel_ms": kms}
+    # the same call against the matrix cores: the method's flops over the time,
+    # beside what the counters saw the matrix cores do (fp16 operands)
+    flops = algorithmic_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    result["mfma"] = {"achieved": tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": tflops / MFMA_PEAK_TFLOPS, "algorithmic_flops": flops,
+                      "operands": "fp16, fp32 accumulation",
+                      "counters": stored_mfma(kname, args.workload)}
+    # geometric mean of the residual ratios rho_t over all (b, h, t), OSDN and
+    # the plain delta rule on the same inputs
+    qg = {}
+    for mode, pre in (("osdn", True), ("deltanet_mode", False)):
+        d = devs[0]
+        r = osdn.forward(d.q, d.k, d.v, d.beta, d.r, eta=d.eta, chunk=C, precond=pre,
+                         workspace=ws)
+        torch.cuda.synchronize()
+        qg[mode] = float(torch.exp(r["log_ratio_sum"].double().sum() / (B * H * T)))
+    result["q_geo"] = qg
 
     if args.only in ("all", "phases"):
         result["decode_step"] = bench_step(args, torch, osdn, W)
@@ -375,6 +446,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, host)
+        result["cpu_single_thread"] = cpu_single_thread(W)
 
     print(json.dumps(result), flush=True)
 

@@ -15,6 +15,8 @@ the program dispatched, divided by the number of calls:
 
 `record` writes profiles/traffic.json (read by bench.py; an entry only counts
 while the kernel sources are unchanged) and a text summary under profiles/.
+`mfma` does the same for one pass over MFMA_COUNTERS (matrix-core flops per
+call and busy share): profiles/mfma.json and profiles/mfma_<entry>_<workload>.txt.
 `summary` turns a rocprofv3 --kernel-trace --stats output (kernel_stats.csv or
 the SQLite database) into the text tables kept under profiles/.
 """
@@ -188,6 +190,62 @@ def record(fetch_dir: str, write_dir: str, workload: str, entry: str, launches: 
     print("\n".join(lines))
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES")
+
+
+def record_mfma(directory: str, workload: str, entry: str, launches: int, cmd: str) -> None:
+    """Matrix-core work per call from one counter pass over MFMA_COUNTERS.  The
+    MOPS counters count units of 512 flops.  The busy share is
+    SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES as the counters report them: it
+    counts cycles with matrix-core work in flight, so it exceeds the share of
+    peak throughput that the flops alone imply."""
+    per = {}
+    for r in _counter_rows(directory):
+        name = r.get("Kernel_Name", "")
+        if not _is_library_kernel(name):
+            continue
+        c = r.get("Counter_Name", "").strip()
+        key = (name, r.get("Dispatch_Id", r.get("Correlation_Id")))
+        per.setdefault(key, {}).setdefault(c, 0.0)
+        per[key][c] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit("no library kernel in the counter output")
+    kern = {}
+    for (name, _), cs in per.items():
+        k = kern.setdefault(name, {"dispatches": 0, **{c: 0.0 for c in MFMA_COUNTERS}})
+        k["dispatches"] += 1
+        for c in MFMA_COUNTERS:
+            k[c] += cs.get(c, 0.0)
+    label = ENTRIES[entry]
+    src = kernel_sources_hash()
+    f16 = sum(k["SQ_INSTS_VALU_MFMA_MOPS_F16"] for k in kern.values()) * 512 / launches
+    f32 = sum(k["SQ_INSTS_VALU_MFMA_MOPS_F32"] for k in kern.values()) * 512 / launches
+    path = os.path.join(ROOT, "profiles", "mfma.json")
+    db = json.load(open(path)) if os.path.exists(path) else {}
+    db["%s|%s" % (label, workload)] = {"sources": src, "f16_flops_per_call": f16,
+                                       "f32_flops_per_call": f32, "calls": launches}
+    json.dump(db, open(path, "w"), indent=1, sort_keys=True)
+    lines = ["Matrix-core work per call of %s, workload %s (kernel sources %s)" % (label, workload, src),
+             "", "command (counter pass): " + cmd,
+             "command (this summary): python3 -m delta_rule_recurrent_precond_amd.profiling "
+             "mfma --entry %s --dir <D> --workload %s --launches %d --command <the pass's command>" % (entry, workload, launches),
+             "", "MOPS counters count units of 512 flops; busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "SQ_BUSY_CU_CYCLES", "",
+             "%-64s %9s %14s %14s %8s" % ("kernel", "dispatches", "f16 flop/call", "f32 flop/call",
+                                          "busy")]
+    for n in sorted(kern):
+        k = kern[n]
+        busy = k["SQ_VALU_MFMA_BUSY_CYCLES"] / k["SQ_BUSY_CU_CYCLES"] if k["SQ_BUSY_CU_CYCLES"] else 0
+        lines.append("%-64s %9d %14.4g %14.4g %8.3f" % (
+            n[:64], k["dispatches"], k["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / launches,
+            k["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512 / launches, busy))
+    lines += ["", "total per call: f16 %.6g flop, f32 %.6g flop" % (f16, f32)]
+    txt = os.path.join(ROOT, "profiles", "mfma_%s_%s.txt" % (entry, workload))
+    open(txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summary(src: str, cmd: str) -> str:
     out = ["command: " + cmd, ""]
     if src.endswith(".db"):
@@ -220,6 +278,12 @@ def main(argv=None):
     p.add_argument("--entry", choices=sorted(ENTRIES), required=True)
     p.add_argument("--cmd-fetch", default="")
     p.add_argument("--cmd-write", default="")
+    p = sub.add_parser("mfma")
+    p.add_argument("--dir", required=True)
+    p.add_argument("--workload", default="1.3b-apf")
+    p.add_argument("--launches", type=int, default=3)
+    p.add_argument("--entry", choices=sorted(ENTRIES), required=True)
+    p.add_argument("--command", default="")
     p = sub.add_parser("summary")
     p.add_argument("src")
     p.add_argument("--command", required=True)
@@ -229,6 +293,8 @@ def main(argv=None):
         run(a.workload, a.launches, a.entry)
     elif a.cmd == "record":
         record(a.fetch, a.write, a.workload, a.entry, a.launches, a.cmd_fetch, a.cmd_write)
+    elif a.cmd == "mfma":
+        record_mfma(a.dir, a.workload, a.entry, a.launches, a.command)
     else:
         text = summary(a.src, a.command)
         if a.out:

@@ -73,3 +73,29 @@ def test_summary_table(tmp_path):
     text = profiling.summary(str(p), "cmd")
     assert text.startswith("command: cmd")
     assert "500.000" in text and " 4 " in text
+
+
+def test_record_mfma_counts_512_flop_units_per_call(tmp_path, monkeypatch):
+    rows = []
+    for disp, (name, f16, f32, busy, cu) in enumerate([("osdn::chunk_state(...)", 10.0, 0.0, 30.0, 60.0),
+                                                       ("osdn::chunk_state(...)", 14.0, 0.0, 30.0, 60.0),
+                                                       ("osdn::walk_prep(...)", 2.0, 4.0, 5.0, 50.0),
+                                                       ("__amd_rocclr_copyBuffer", 99.0, 99.0, 9.0, 9.0)]):
+        for c, v in zip(profiling.MFMA_COUNTERS, (f16, f32, busy, cu)):
+            rows.append((disp, name, c, v))
+    d = tmp_path / "m"
+    d.mkdir()
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(HEADER)
+        for i, (disp, name, counter, value) in enumerate(rows):
+            wr.writerow([i + 1, disp + 1, name, counter, value])
+    monkeypatch.setattr(profiling, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    profiling.record_mfma(str(d), "wl", "forward_split", 2, "cmd")
+    import json
+    rec = json.load(open(tmp_path / "profiles" / "mfma.json"))["osdn_forward_split|wl"]
+    assert rec["f16_flops_per_call"] == (10 + 14 + 2) * 512 / 2
+    assert rec["f32_flops_per_call"] == 4 * 512 / 2
+    text = open(tmp_path / "profiles" / "mfma_forward_split_wl.txt").read()
+    assert "0.500" in text and "0.100" in text  # busy shares 60/120 and 5/50
