@@ -155,6 +155,9 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     rq[u] = *(const uint4 *)(q + off);
     if (MODE == kGiven) rt[u] = *(const uint4 *)(kt_in + off);
   }
+  // kOsdn: the chunk's entry d of dimension tid (threads 0-127), loaded here so
+  // that its latency passes while the chunk is staged, not on the d chain
+  const float d_entry = MODE == kOsdn ? wout[((long)bh * NC + c) * WOUT + min(tid, DK - 1)] : 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     if ((tid + 256 * u) >> 4 >= L) {
@@ -216,8 +219,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
       for (int e = 0; e < 8; ++e) km = fmaxf(km, fabsf(bf2f(s[e])));
     }
-#pragma unroll
-    for (int m_ = 1; m_ < 64; m_ <<= 1) km = fmaxf(km, __shfl_xor(km, m_));
+    km = wave_max(km);
     if (lane == 0) red[wave] = km;
     __syncthreads();
     km = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -256,9 +258,17 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
 
   if (MODE == kOsdn) {
-    const float d_in = tid < DK ? wout[((long)bh * NC + c) * WOUT + tid] : 0.f;
-    auto recur = [&](auto &&emit) {
-      float d = d_in;
+    // One pass per key dimension (threads 0-127): x_t = d_t kh_t stays in
+    // registers for both the scale and the staged write keys.  The keys of the
+    // dimension are read first, so no LDS round trip sits on the d chain.
+    float xs[C];
+    float km = 0.f;
+    if (tid < DK) {
+      float d = d_entry;
+      f16 kc[C];
+#pragma unroll
+      for (int t = 0; t < C; ++t) kc[t] = Ks[t * KP + tid];
+#pragma unroll
       for (int t0 = 0; t0 < C; t0 += 4) {
         const float4 c4 = *(const float4 *)&cs[t0], r4 = *(const float4 *)&rs[t0];
         const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
@@ -270,23 +280,24 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // the normalised key is kv * sv
-          const float kv = (float)Ks[(t0 + e) * KP + tid];
+          const float kv = (float)kc[t0 + e];
           const float kh = NORM ? kv * sv[e] : kv;
-          emit(t0 + e, d * kh);
+          xs[t0 + e] = d * kh;
+          km = fmaxf(km, fabsf(xs[t0 + e]));
           d = fmaf(cv[e], kh * kh, rv[e] * d);
         }
       }
-    };
-    float km = 0.f;
-    if (tid < DK) recur([&](int, float x) { km = fmaxf(km, fabsf(x)); });
-#pragma unroll
-    for (int m_ = 1; m_ < 64; m_ <<= 1) km = fmaxf(km, __shfl_xor(km, m_));
+    }
+    km = wave_max(km);
     if (lane == 0) red[wave] = km;
     __syncthreads();
     km = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     ds = km > 0.f ? fexp2(ceilf(flog2(km))) : 1.0f;
     inv = 1.0f / ds;
-    if (tid < DK) recur([&](int t, float x) { Kts[t * KP + tid] = h(x * inv); });
+    if (tid < DK) {
+#pragma unroll
+      for (int t = 0; t < C; ++t) Kts[t * KP + tid] = h(xs[t] * inv);
+    }
     __syncthreads();
   }
 

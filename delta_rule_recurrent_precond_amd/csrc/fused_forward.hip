@@ -403,8 +403,7 @@ __device__ __forceinline__ void fused_body(
             if (GATED) Lal[ptid] = ptid < pL ? pal : 1.f;
           }
           if (MODE == kGiven) {
-#pragma unroll
-            for (int m_ = 1; m_ < 64; m_ <<= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, m_));
+            kmax = wave_max(kmax);
             if (lane == 0) Lred[wave] = kmax;
           }
         }
