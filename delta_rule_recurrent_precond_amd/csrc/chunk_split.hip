@@ -109,7 +109,7 @@ template <int MODE, bool NORM, bool GATED, bool GK>
 __global__ void __launch_bounds__(256)
 chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
            const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
-           int c0, int ncs, unsigned char *__restrict__ ws, const float *__restrict__ r,
+           unsigned char *__restrict__ ws, const float *__restrict__ r,
            const float *__restrict__ wout, const float *__restrict__ alpha, unsigned xf) {
   // q is needed only for the scores, which are formed first; the blocks of A
   // and T then reuse its space (53 KB in all: three workgroups per CU)
@@ -136,7 +136,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.x / ncs, c = c0 + blockIdx.x % ncs;  // chunks c0 .. c0+ncs-1
+  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
   unsigned char *rec = ws + ((long)bh * NC + c) * (GK ? RECK : REC);
@@ -1035,8 +1035,8 @@ void launch_prep_t(int BH, int NC, hipStream_t s, const void *q, const void *k, 
                    const float *beta, int T, unsigned char *rec, const float *r,
                    const float *wout, const float *alpha, unsigned xf) {
   hipLaunchKernelGGL((chunk_prep<MODE, NORM, GATED, GK>), dim3((unsigned)(BH * NC)), dim3(256), 0,
-                     s, (const bf16 *)q, (const bf16 *)k, (const bf16 *)kt, beta, T, NC, 0, NC,
-                     rec, r, wout, alpha, xf);
+                     s, (const bf16 *)q, (const bf16 *)k, (const bf16 *)kt, beta, T, NC, rec, r,
+                     wout, alpha, xf);
 }
 
 // chunk_prep over every chunk of every head; kGiven takes no input transforms

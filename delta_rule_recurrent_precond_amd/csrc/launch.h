@@ -86,13 +86,6 @@ hipError_t launch_fused_scan(const ScanArgs &a, hipStream_t s);
 bool walk_supported(int dk, int dtype);
 size_t walk_workspace_bytes(int B, int H, int T);
 hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, float *wout, hipStream_t s);
-// The two parts of launch_walk for chunks c0..c1-1 (the pass continues from the
-// entry d of chunk c0 that the pass over the chunks before left in wout, and
-// adds to a.log_ratio_sum after the first range).
-hipError_t launch_walk_prep(const ScanArgs &a, int c0, int c1, unsigned char *wrec,
-                            hipStream_t s);
-hipError_t launch_walk_pass(const ScanArgs &a, int c0, int c1, const unsigned char *wrec,
-                            float *wout, hipStream_t s);
 hipError_t launch_walk_scan(const ScanArgs &a, void *ws, hipStream_t s);
 
 // The forward in four launches (bf16, dk = dv = 128, chunk 64): the walk, then

@@ -41,7 +41,7 @@ constexpr int FP = 68;   // padded row (floats) of [64][64] fp32 tiles in LDS
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const float *__restrict__ r,
-          float eta, int T_, int NC, int c0, int ncs, unsigned xf, unsigned char *__restrict__ wrec) {
+          float eta, int T_, int NC, unsigned xf, unsigned char *__restrict__ wrec) {
   // The fp16 keys are needed only for the key gram; (I + M)^-1 reuses their space.
   __shared__ __align__(16) float F[C * FP];           // key gram G, then M (strictly lower)
   __shared__ __align__(16) unsigned char KM[C * KP * 2];  // fp16 keys, then (I + M)^-1 [64][FP]
@@ -55,7 +55,7 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.x / ncs, c = c0 + blockIdx.x % ncs;  // chunks c0 .. c0+ncs-1
+  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
 
@@ -210,9 +210,8 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 }
 
 // ---------------------------------------------------------------------------
-// walk: one workgroup of 8 waves per (b, h), sequential over chunks c0..c1-1
-// (the entry d of chunk c0 is d0, or what the launch before left in wout),
-// three barriers per chunk.  Waves 0-3 run the chain, reading p_t = k_t (.) k_t
+// walk: one workgroup of 8 waves per (b, h), sequential over the chunks from
+// the entry d0 (ones if none is given), three barriers per chunk.  Waves 0-3 run the chain, reading p_t = k_t (.) k_t
 // in fp32 from LDS:
 //   A  b_t = <d, p_t> (4 threads per token), rhs_t = 1 - u_t s_t b_t
 //   B  g = (I + M)^-1 rhs (4 threads per token); c_t, w_t = R_{L,t} alpha_t s_t g_t
@@ -244,7 +243,7 @@ struct alignas(16) WalkSmem {
 
 __global__ void __launch_bounds__(WT)
 walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
-     const float *__restrict__ d0, int T_, int NC, int c0, int c1, float *__restrict__ wout,
+     const float *__restrict__ d0, int T_, int NC, float *__restrict__ wout,
      float *__restrict__ d_final, float *__restrict__ log_ratio,
      float *__restrict__ log_ratio_sum) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -263,9 +262,9 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
       uint4 k[4], rr[NRP];
     };
     Regs ra, rb, rc, rd;
-    // chunk cc clamped to the last one of the launch: loads past it reread it
+    // chunk cc clamped to the last one: loads past it reread it
     auto load = [&](Regs &R, int cc) {
-      cc = min(cc, c1 - 1);
+      cc = min(cc, NC - 1);
       const bf16 *kc = k + ((long)bh * T_ + (long)cc * C) * DK;  // uniform base, 32-bit offsets
       const int L = min(C, T_ - cc * C);
 #pragma unroll
@@ -332,37 +331,36 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
     // half (window B), log rho of chunk c and the loads of chunk c+4 into the
     // set that held chunk c (window C)
     auto iteration = [&](int c, Regs &free_, const Regs &next) {
-      if (c + 1 < c1) {
+      if (c + 1 < NC) {
         stash_rec(next, c + 1);
         stash_p(next, c + 1, 0);
       }
       __syncthreads();
-      if (c + 1 < c1) stash_p(next, c + 1, 2);
+      if (c + 1 < NC) stash_p(next, c + 1, 2);
       __syncthreads();
       log_rho(c);
       load(free_, c + 4);
       __syncthreads();
     };
-    if (c1 > c0) {
-      load(ra, c0);
-      load(rb, c0 + 1);
-      load(rc, c0 + 2);
-      load(rd, c0 + 3);
-      stash_rec(ra, c0);
-      stash_p(ra, c0, 0);
-      stash_p(ra, c0, 2);
+    if (NC > 0) {
+      load(ra, 0);
+      load(rb, 1);
+      load(rc, 2);
+      load(rd, 3);
+      stash_rec(ra, 0);
+      stash_p(ra, 0, 0);
+      stash_p(ra, 0, 2);
     }
     __syncthreads();
-    for (int c = c0; c < c1; c += 4) {
+    for (int c = 0; c < NC; c += 4) {
       iteration(c, ra, rb);
-      if (c + 1 < c1) iteration(c + 1, rb, rc);
-      if (c + 2 < c1) iteration(c + 2, rc, rd);
-      if (c + 3 < c1) iteration(c + 3, rd, ra);
+      if (c + 1 < NC) iteration(c + 1, rb, rc);
+      if (c + 2 < NC) iteration(c + 2, rc, rd);
+      if (c + 3 < NC) iteration(c + 3, rd, ra);
     }
     if (log_ratio_sum && lt < 64) {
-      // this launch's chunks, added to the sums of the launches before it
       const float s = wave_sum(lr_acc);
-      if (lt == 0) log_ratio_sum[bh] = c0 == 0 ? s : log_ratio_sum[bh] + s;
+      if (lt == 0) log_ratio_sum[bh] = s;
     }
     return;
   }
@@ -373,17 +371,13 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
   const int dim = 32 * wv + (l & 31), half = l >> 5;  // phase C
   float dreg = 0.f;  // lanes l < 32: d of dimension dim, entry value of the chunk in the pass
   if (half == 0) {
-    if (c0 == 0) {
-      dreg = d0 ? d0[(long)bh * DK + dim] : 1.0f;
-      if (NC > 0) wout[(long)bh * NC * WOUT + dim] = dreg;
-    } else {
-      dreg = wout[((long)bh * NC + c0) * WOUT + dim];
-    }
+    dreg = d0 ? d0[(long)bh * DK + dim] : 1.0f;
+    if (NC > 0) wout[(long)bh * NC * WOUT + dim] = dreg;
     sm.d[dim] = dreg;
   }
   __syncthreads();
 
-  for (int c = c0; c < c1; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int cb = c & 1;
     // A
     {
@@ -452,7 +446,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
     __syncthreads();
   }
 
-  if (d_final && half == 0 && c1 == NC) d_final[(long)bh * DK + dim] = dreg;
+  if (d_final && half == 0) d_final[(long)bh * DK + dim] = dreg;
 }
 
 // ---------------------------------------------------------------------------
@@ -518,35 +512,20 @@ size_t walk_workspace_bytes(int B, int H, int T) {
   return (size_t)B * H * nc * (WREC + WOUT * sizeof(float));
 }
 
-hipError_t launch_walk_prep(const ScanArgs &a, int c0, int c1, unsigned char *wrec,
-                            hipStream_t s) {
-  const int BH = a.B * a.H;
-  const int NC = (a.T + C - 1) / C;
-  if (BH == 0 || c1 <= c0) return hipSuccess;
-  hipLaunchKernelGGL(walk_prep, dim3((unsigned)(BH * (c1 - c0))), dim3(256), 0, s,
-                     (const bf16 *)a.k, a.beta, a.r, a.eta, a.T, NC, c0, c1 - c0, a.xf, wrec);
-  return hipGetLastError();
-}
-
-hipError_t launch_walk_pass(const ScanArgs &a, int c0, int c1, const unsigned char *wrec,
-                            float *wout, hipStream_t s) {
+hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, float *wout, hipStream_t s) {
   const int BH = a.B * a.H;
   const int NC = (a.T + C - 1) / C;
   if (BH == 0) return hipSuccess;
+  if (NC > 0)
+    hipLaunchKernelGGL(walk_prep, dim3((unsigned)(BH * NC)), dim3(256), 0, s, (const bf16 *)a.k,
+                       a.beta, a.r, a.eta, a.T, NC, a.xf, wrec);
   constexpr size_t shm = sizeof(WalkSmem);
   hipError_t e = hipFuncSetAttribute((const void *)walk,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(walk, dim3((unsigned)BH), dim3(WT), shm, s, (const bf16 *)a.k,
-                     wrec, a.d0, a.T, NC, c0, c1, wout, a.d_final, a.log_ratio, a.log_ratio_sum);
+  hipLaunchKernelGGL(walk, dim3((unsigned)BH), dim3(WT), shm, s, (const bf16 *)a.k, wrec, a.d0,
+                     a.T, NC, wout, a.d_final, a.log_ratio, a.log_ratio_sum);
   return hipGetLastError();
-}
-
-hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, float *wout, hipStream_t s) {
-  const int NC = (a.T + C - 1) / C;
-  hipError_t e = launch_walk_prep(a, 0, NC, wrec, s);
-  if (e != hipSuccess) return e;
-  return launch_walk_pass(a, 0, NC, wrec, wout, s);
 }
 
 hipError_t launch_walk_scan(const ScanArgs &a, void *ws, hipStream_t s) {
