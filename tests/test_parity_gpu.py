@@ -145,10 +145,11 @@ def test_precond_scan_empty_sequence_copies_d0(dk):
 
 
 @pytest.mark.parametrize("ws", [True, None])
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 200])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 200, 257, 320])
 def test_precond_scan_chunk_boundaries(T, ws):
     """The chunked walk (bf16, dk = 128) around chunk boundaries, APF gates:
-    the three-launch walk (ws=True) and the single kernel per (b,h)."""
+    the three-launch walk (ws=True) and the single kernel per (b,h).  1 to 5
+    chunks: the walk's loaders cycle through four register sets."""
     w = W.custom(1, 2, T, 128, 128, 64, dtype="bf16", eta=0.2, apf=True, seed=300 + T)
     inp = W.generate(w)
     dev = _to_dev(inp)
