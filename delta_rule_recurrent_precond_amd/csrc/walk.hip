@@ -211,8 +211,8 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 
 // ---------------------------------------------------------------------------
 // walk: one workgroup of 8 waves per (b, h), sequential over the chunks from
-// the entry d0 (ones if none is given), three barriers per chunk.  Waves 0-3 run the chain, reading p_t = k_t (.) k_t
-// in fp32 from LDS:
+// the entry d0 (ones if none is given), three barriers per chunk.  Waves 0-3
+// run the chain, reading p_t = k_t (.) k_t in fp32 from LDS:
 //   A  b_t = <d, p_t> (4 threads per token), rhs_t = 1 - u_t s_t b_t
 //   B  g = (I + M)^-1 rhs (4 threads per token); c_t, w_t = R_{L,t} alpha_t s_t g_t
 //   C  d <- Gamma_L d + sum_t w_t p_t: wave v takes dimensions 32 v .. +31, its
