@@ -65,12 +65,23 @@ __device__ __forceinline__ float unit_scale(float n) { return n > 0.f ? 1.0f / s
 __device__ __forceinline__ float sigmoid_gate(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 
-// Sum over aligned groups of G lanes (G = 2..64, power of two) with xor
-// shuffles; every lane of the group receives the group's total.
+// Sum over aligned groups of G lanes (G = 2..64, power of two); every lane of
+// the group receives the group's total.  Steps within a 16-lane row are DPP
+// moves: quads by xor, then the half-row and row mirrors, which pair the same
+// partial sums as xor 4 and xor 8 once the quads (and half-rows) hold equal
+// values, so the result is the xor butterfly's bit for bit.  Wider steps are
+// xor shuffles.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
-  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
+  for (int m = 1; m < G; m <<= 1) {
+    if (m == 4)
+      v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    else if (m == 8)
+      v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    else
+      v += __shfl_xor(v, m, 64);
+  }
   return v;
 }
 

@@ -46,8 +46,8 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   __shared__ __align__(16) float F[C * FP];           // key gram G, then M (strictly lower)
   __shared__ __align__(16) unsigned char KM[C * KP * 2];  // fp16 keys, then (I + M)^-1 [64][FP]
   __shared__ float Yw[3][16][17];                     // per-wave staging of a block sum
-  __shared__ float bs[C], al[C], nn[C], lg[C + 4];
-  __shared__ float ss[C];  // 1 / ||k_t||^2 for unnormalised keys, else 1
+  __shared__ __align__(16) float bs[C], al[C], nn[C], lg[C + 4];
+  __shared__ __align__(16) float ss[C];  // 1 / ||k_t||^2 for unnormalised keys, else 1
   static_assert(C * KP * 2 >= C * FP * 4, "the inverse fits in the keys' space");
   f16 *Kh = (f16 *)KM;
   float *Mi = (float *)KM;
@@ -134,16 +134,25 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   {
     const int t = tid >> 2, q = tid & 3;
     const float bl = bs[t], lt = lg[t], ssl = ss[t];
-    float row[16];
+    // the columns' factors as 16-byte reads (lg from 16 q, used from 16 q + 1)
+    float row[16], alc[16], ssc[16], lgc[20];
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
       const float4 f4 = *(const float4 *)&F[t * FP + 16 * q + j];
       row[j] = f4.x, row[j + 1] = f4.y, row[j + 2] = f4.z, row[j + 3] = f4.w;
+      const float4 a4 = *(const float4 *)&al[16 * q + j], s4 = *(const float4 *)&ss[16 * q + j];
+      alc[j] = a4.x, alc[j + 1] = a4.y, alc[j + 2] = a4.z, alc[j + 3] = a4.w;
+      ssc[j] = s4.x, ssc[j + 1] = s4.y, ssc[j + 2] = s4.z, ssc[j + 3] = s4.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 20; j += 4) {
+      const float4 l4 = *(const float4 *)&lg[16 * q + j];
+      lgc[j] = l4.x, lgc[j + 1] = l4.y, lgc[j + 2] = l4.z, lgc[j + 3] = l4.w;
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int s = 16 * q + j;
-      row[j] = s < t ? bl * al[s] * fexp2(lt - lg[s + 1]) * (ssl * ss[s]) * row[j] : 0.f;
+      row[j] = s < t ? bl * alc[j] * fexp2(lt - lgc[j + 1]) * (ssl * ssc[j]) * row[j] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
