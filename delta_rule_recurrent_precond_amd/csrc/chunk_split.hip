@@ -353,10 +353,8 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           pq = fmaf((float)qv[x], w, pq);
         }
       }
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      pq += __shfl_xor(pq, 16);
-      pq += __shfl_xor(pq, 32);
+      a = column_sum4(a);
+      pq = column_sum4(pq);
       if (lane < 16) {
         Adg[(16 * b + tl) * LDF + sl] = tl > sl ? a : 0.f;
         Pdg[(16 * b + tl) * LDF + sl] = tl >= sl ? pq : 0.f;

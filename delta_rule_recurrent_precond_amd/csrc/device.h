@@ -58,6 +58,16 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Sum over the four lanes l % 16 + 16 r (r = 0..3) of a wave, every one of
+// them receiving it: the row swap then the lane-half swap (gfx950), adding
+// in the order of xor-16 then xor-32 shuffles.
+__device__ __forceinline__ float column_sum4(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+
 // Input transforms of the raw-input flags (include/osdn.h): the scale that
 // normalises a vector of squared norm n (a zero vector stays zero), and the
 // logistic sigmoid of a gate logit.
