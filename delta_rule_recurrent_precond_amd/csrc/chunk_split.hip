@@ -87,6 +87,10 @@ constexpr int LDF = 20;  // padded row (floats) of the 16x16 fp32 blocks in LDS
 
 __device__ __forceinline__ int op_index(int m, int qq) { return m < 2 ? m : 2 * m - 2 + qq; }
 
+// zeros that a lane loads in place of a row of alpha (per-channel gate: the
+// step of the diagonal sums that starts a column); never written
+__device__ __align__(16) float g_zero16[16];
+
 // ---------------------------------------------------------------------------
 // chunk_prep: one workgroup of 4 waves per (b, h, chunk).  k, kt and q are
 // loaded with all loads in flight at once, staged in LDS as fp16, and every
@@ -131,6 +135,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // from global memory where it is used)
   __shared__ float Adg[GK ? 4 * 16 * LDF : 4], Pdg[GK ? 4 * 16 * LDF : 4];
   __shared__ __align__(16) float Bk[GK ? 4 * DK : 4];
+  __shared__ __align__(16) f16 Zrow[GK ? DK : 8];  // GK: zeros
   __shared__ float red[4];
 
   const int tid = threadIdx.x;
@@ -166,6 +171,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (MODE == kGiven) rt[u] = uint4{0, 0, 0, 0};
     }
   }
+  if (GK && tid < DK / 8) *(uint4 *)&Zrow[8 * tid] = uint4{0, 0, 0, 0};
   if (tid < C) {
     const float bv = beta[tok0 + min(tid, L - 1)];
     bs[tid] = tid < L ? ((xf & kGateLogits) ? sigmoid_gate(bv) : bv) : 0.f;
@@ -207,6 +213,20 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (lane >= off) incl += y;
     }
     lga[tid] = incl;
+  }
+
+  // GK: alpha of the chunk for the block products (wave b: rows 16b .. 16b + 15,
+  // dimensions 2 lane, 2 lane + 1; rows past the end are 1), issued after the
+  // other loads so the waits for those leave them in flight.  They also bring
+  // the chunk's alpha into L2 ahead of the diagonal sums, which read it row by row.
+  float2 av[GK ? 16 : 1];
+  if (GK) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = 16 * wave + u;
+      const float2 a2 = *(const float2 *)(alpha + (tok0 + min(t, L - 1)) * DK + 2 * lane);
+      av[u] = t < L ? a2 : float2{1.f, 1.f};
+    }
   }
 
   // write-key scale: a power of two >= max |kt| (given keys), 1 for kt = k
@@ -302,62 +322,68 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
 
   if (GK) {
-    // (a) the diagonal blocks of A and P term by term: wave b takes block b, a
-    // lane column s = 16b + (lane & 15) and 32 key dimensions; e_i runs down the
-    // rows as the product of alpha_i over s+1 .. t (0 above t = s, where the
-    // added 1 starts it).  The four lanes of a column add their partial sums.
-    const int b = wave, sl = lane & 15, i0 = 32 * (lane >> 4), s = 16 * b + sl;
-    float kts[32], e[32];
+    // (a) the diagonal blocks of A and P term by term.  Wave b takes block b;
+    // only the 136 entries on and below the diagonal are summed.  Lane group
+    // pr = lane >> 3 (8 lanes, 16 key dimensions each from i0) walks column pr
+    // down rows pr .. 15, then column 15 - pr down rows 15 - pr .. 15: 17 steps
+    // for every group.  u_i is kt_s,i times the product of alpha_i over s+1 .. t,
+    // carried as u <- u alpha_t + z: a step that starts a column takes alpha = 0
+    // (a table of zeros) and z = kt_s (its staged row), every other step the
+    // row's alpha and z = 0 (a zero row), so the chain needs no select per
+    // dimension.  Rows past the end read the last row's alpha: their k and q
+    // rows are zero, so their entries are 0 whatever u is.  The 8 lanes of a
+    // group add their partial sums.
+    const int b = wave, pr = lane >> 3, i0 = 16 * (lane & 7);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f16x8 v = ld8(&Kts[s * KP + i0 + 8 * j]);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        kts[8 * j + x] = (float)v[x];
-        e[8 * j + x] = 0.f;
+    for (int x = 0; x < 4; ++x) {  // the entries above the diagonal are 0
+      const int pos = lane + 64 * x, tl = pos >> 4, sl = pos & 15;
+      if (sl > tl) {
+        Adg[(16 * b + tl) * LDF + sl] = 0.f;
+        Pdg[(16 * b + tl) * LDF + sl] = 0.f;
       }
     }
-    // alpha of row t for this lane's 32 dimensions (rows past the end are 1:
-    // they change no product), one row ahead of its use
-    auto arow = [&](int t, float4 (&v)[8]) {
-      const float *src = alpha + (tok0 + min(t, L - 1)) * DK + i0;
+    auto row_of = [&](int j) { return j < 16 - pr ? pr + j : j - 1; };
+    auto col_of = [&](int j) { return j < 16 - pr ? pr : 15 - pr; };
+    auto starts = [&](int j) { return j == 0 || j == 16 - pr; };
+    auto aload = [&](int j, float4 (&v)[4]) {
+      const float *src = starts(j) ? g_zero16 : alpha + (tok0 + min(16 * b + row_of(j), L - 1)) * DK + i0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = *(const float4 *)(src + 4 * j);
-      if (t >= L) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = float4{1.f, 1.f, 1.f, 1.f};
-      }
+      for (int x = 0; x < 4; ++x) v[x] = *(const float4 *)(src + 4 * x);
     };
-    float4 an[8];
-    arow(16 * b, an);
-    for (int tl = 0; tl < 16; ++tl) {
-      const int t = 16 * b + tl;
-      float4 ac[8];
+    float u[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ac[j] = an[j];
-      if (tl < 15) arow(t + 1, an);
-      const float start = tl == sl ? 1.f : 0.f;
+    for (int x = 0; x < 16; ++x) u[x] = 0.f;
+    float4 ab[3][4];  // alpha three steps ahead
+    aload(0, ab[0]);
+    aload(1, ab[1]);
+    aload(2, ab[2]);
+#pragma unroll
+    for (int j = 0; j < 17; ++j) {
+      const int tl = row_of(j), sl = col_of(j), t = 16 * b + tl;
+      float al[16];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        al[4 * x] = ab[j % 3][x].x, al[4 * x + 1] = ab[j % 3][x].y;
+        al[4 * x + 2] = ab[j % 3][x].z, al[4 * x + 3] = ab[j % 3][x].w;
+      }
+      if (j + 3 < 17) aload(j + 3, ab[j % 3]);
+      const f16 *zp = starts(j) ? &Kts[(16 * b + sl) * KP + i0] : &Zrow[i0];
+      const f16x8 z0 = ld8(zp), z1 = ld8(zp + 8);
+      const f16x8 k0 = ld8(&Ks[t * KP + i0]), k1 = ld8(&Ks[t * KP + i0 + 8]);
+      const f16x8 q0 = ld8(&Qs[t * KP + i0]), q1 = ld8(&Qs[t * KP + i0 + 8]);
       float a = 0.f, pq = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f16x8 kv = ld8(&Ks[t * KP + i0 + 8 * j]);
-        const f16x8 qv = ld8(&Qs[t * KP + i0 + 8 * j]);
-        const float4 a0 = ac[2 * j], a1 = ac[2 * j + 1];
-        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int cc = 8 * j + x;
-          e[cc] = fmaf(e[cc], av[x], start);
-          const float w = kts[cc] * e[cc];
-          a = fmaf((float)kv[x], w, a);
-          pq = fmaf((float)qv[x], w, pq);
-        }
+      for (int x = 0; x < 16; ++x) {
+        const float zx = (float)(x < 8 ? z0[x] : z1[x - 8]);
+        u[x] = fmaf(u[x], al[x], zx);
+        a = fmaf((float)(x < 8 ? k0[x] : k1[x - 8]), u[x], a);
+        pq = fmaf((float)(x < 8 ? q0[x] : q1[x - 8]), u[x], pq);
       }
-      a = column_sum4(a);
-      pq = column_sum4(pq);
-      if (lane < 16) {
-        Adg[(16 * b + tl) * LDF + sl] = tl > sl ? a : 0.f;
-        Pdg[(16 * b + tl) * LDF + sl] = tl >= sl ? pq : 0.f;
+      a = group_sum<8>(a);
+      pq = group_sum<8>(pq);
+      if ((lane & 7) == 0) {
+        Adg[t * LDF + sl] = tl > sl ? a : 0.f;
+        Pdg[t * LDF + sl] = pq;
       }
     }
     // (b) per pair of key dimensions (thread: dimensions i2, i2 + 1 of block
@@ -367,13 +393,6 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     //   rescaled by the product from the block start to t, and kt_s by the
     //   product from s + 1 to the block end (in place); g_L to the record.
     const int blk = wave, i2 = 2 * lane;
-    float2 av[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int t = 16 * blk + u;
-      const float2 a2 = *(const float2 *)(alpha + (tok0 + min(t, L - 1)) * DK + i2);
-      av[u] = t < L ? a2 : float2{1.f, 1.f};
-    }
     float2 Bb = {1.f, 1.f};
 #pragma unroll
     for (int u = 0; u < 16; ++u) Bb = float2{Bb.x * av[u].x, Bb.y * av[u].y};

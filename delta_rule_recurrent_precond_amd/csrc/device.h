@@ -77,15 +77,19 @@ __device__ __forceinline__ float sigmoid_gate(float x) { return 1.0f / (1.0f + e
 
 // Sum over aligned groups of G lanes (G = 2..64, power of two); every lane of
 // the group receives the group's total.  Steps within a 16-lane row are DPP
-// moves: quads by xor, then the half-row and row mirrors, which pair the same
-// partial sums as xor 4 and xor 8 once the quads (and half-rows) hold equal
-// values, so the result is the xor butterfly's bit for bit.  Wider steps are
-// xor shuffles.
+// moves: the quad permutations [1,0,3,2] and [2,3,0,1] (xor 1, xor 2), then the
+// half-row and row mirrors, which pair the same partial sums as xor 4 and xor 8
+// once the quads (and half-rows) hold equal values, so the result is the xor
+// butterfly's bit for bit.  Wider steps are xor shuffles.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
   for (int m = 1; m < G; m <<= 1) {
-    if (m == 4)
+    if (m == 1)
+      v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    else if (m == 2)
+      v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    else if (m == 4)
       v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
     else if (m == 8)
       v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
