@@ -405,12 +405,22 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (x < blk) G = float2{G.x * Bv[x].x, G.y * Bv[x].y};
     }
     f16 *kg = (f16 *)(rec + OFF_KG), *qg = (f16 *)(rec + OFF_QG);
+    // every row is read before any is rewritten in place, so no LDS read waits
+    // behind the previous row's stores
+    f16x2 k2s[16], q2s[16], t2s[16];
+#pragma unroll
+    for (int tl = 0; tl < 16; ++tl) {
+      const int t = 16 * blk + tl;
+      k2s[tl] = *(const f16x2 *)&Ks[t * KP + i2];
+      q2s[tl] = *(const f16x2 *)&Qs[t * KP + i2];
+      t2s[tl] = *(const f16x2 *)&Kts[t * KP + i2];
+    }
     float2 pp = {1.f, 1.f};
 #pragma unroll
     for (int tl = 0; tl < 16; ++tl) {
       const int t = 16 * blk + tl;
       pp = float2{pp.x * av[tl].x, pp.y * av[tl].y};
-      const f16x2 k2 = *(const f16x2 *)&Ks[t * KP + i2], q2 = *(const f16x2 *)&Qs[t * KP + i2];
+      const f16x2 k2 = k2s[tl], q2 = q2s[tl];
       const float kx = (float)k2[0], ky = (float)k2[1], qx = (float)q2[0], qy = (float)q2[1];
       const float ks = (NORM && MODE == kOsdn) ? sk[t] : 1.f;
       const float gx = G.x * pp.x, gy = G.y * pp.y;
@@ -425,7 +435,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
     for (int tl = 15; tl >= 0; --tl) {
       const int s2 = 16 * blk + tl;
-      const f16x2 t2 = *(const f16x2 *)&Kts[s2 * KP + i2];
+      const f16x2 t2 = t2s[tl];
       *(f16x2 *)&Kts[s2 * KP + i2] = f16x2{h((float)t2[0] * ss.x), h((float)t2[1] * ss.y)};
       ss = float2{ss.x * av[tl].x, ss.y * av[tl].y};
     }
