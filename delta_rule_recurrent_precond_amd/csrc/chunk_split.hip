@@ -278,23 +278,31 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
 
   if (MODE == kOsdn) {
-    // One pass per key dimension (threads 0-127): x_t = d_t kh_t stays in
-    // registers for both the scale and the staged write keys.  The keys of the
-    // dimension are read first, so no LDS round trip sits on the d chain.
-    float xs[C];
-    float km = 0.f;
-    if (tid < DK) {
-      float d = d_entry;
-      f16 kc[C];
+    // The in-chunk recurrence d_{t+1} = r_t d_t + c_t kh_t^2 in two halves at
+    // once: threads 0-127 take tokens 0-31 of dimension tid from the entry d,
+    // threads 128-255 tokens 32-63 of dimension tid - 128 from d = 0, carrying
+    // the product P_t of r over 32 .. t-1 as well; the second half's
+    // x_t = d_t kh_t is then P_t kh_t d_32 + e_t kh_t with the first half's
+    // d_32.  The keys of a dimension are read first, so no LDS round trip sits
+    // on the d chain; x_t stays in registers for the scale and the staging.
+    const int dim = tid & (DK - 1), t0h = C / 2 * (tid >> 7);
+    // d_32 passes through the start of Kts, which is written only after the
+    // barrier that follows its last read (one more array would cost the third
+    // workgroup per CU)
+    float *dmid = (float *)Kts;
+    float xa[C / 2], xb[C / 2];  // P_t kh_t and (d_t or e_t) kh_t
+    {
+      f16 kc[C / 2];
 #pragma unroll
-      for (int t = 0; t < C; ++t) kc[t] = Ks[t * KP + tid];
+      for (int t = 0; t < C / 2; ++t) kc[t] = Ks[(t0h + t) * KP + dim];
+      float d = t0h ? 0.f : d_entry, pr = 1.f;
 #pragma unroll
-      for (int t0 = 0; t0 < C; t0 += 4) {
-        const float4 c4 = *(const float4 *)&cs[t0], r4 = *(const float4 *)&rs[t0];
+      for (int t0 = 0; t0 < C / 2; t0 += 4) {
+        const float4 c4 = *(const float4 *)&cs[t0h + t0], r4 = *(const float4 *)&rs[t0h + t0];
         const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
         float sv[4] = {1.f, 1.f, 1.f, 1.f};
         if (NORM) {
-          const float4 s4 = *(const float4 *)&sk[t0];
+          const float4 s4 = *(const float4 *)&sk[t0h + t0];
           sv[0] = s4.x, sv[1] = s4.y, sv[2] = s4.z, sv[3] = s4.w;
         }
 #pragma unroll
@@ -302,11 +310,22 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           // the normalised key is kv * sv
           const float kv = (float)kc[t0 + e];
           const float kh = NORM ? kv * sv[e] : kv;
-          xs[t0 + e] = d * kh;
-          km = fmaxf(km, fabsf(xs[t0 + e]));
+          xa[t0 + e] = pr * kh;
+          xb[t0 + e] = d * kh;
           d = fmaf(cv[e], kh * kh, rv[e] * d);
+          pr *= rv[e];
         }
       }
+      if (tid < DK) dmid[dim] = d;  // d_32
+    }
+    __syncthreads();
+    // first half: x = 0 * xa + xb, exactly xb
+    const float dj = tid < DK ? 0.f : dmid[dim];
+    float km = 0.f;
+#pragma unroll
+    for (int t = 0; t < C / 2; ++t) {
+      xa[t] = fmaf(xa[t], dj, xb[t]);
+      km = fmaxf(km, fabsf(xa[t]));
     }
     km = wave_max(km);
     if (lane == 0) red[wave] = km;
@@ -314,10 +333,8 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     km = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     ds = km > 0.f ? fexp2(ceilf(flog2(km))) : 1.0f;
     inv = 1.0f / ds;
-    if (tid < DK) {
 #pragma unroll
-      for (int t = 0; t < C; ++t) Kts[t * KP + tid] = h(xs[t] * inv);
-    }
+    for (int t = 0; t < C / 2; ++t) Kts[(t0h + t) * KP + dim] = h(xa[t] * inv);
     __syncthreads();
   }
 
