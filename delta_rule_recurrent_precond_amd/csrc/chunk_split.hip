@@ -127,9 +127,15 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   static_assert(4 * 16 * LDF * 4 + 10 * 16 * LDT * 2 <= C * KP * 2, "A and T blocks fit");
   __shared__ float bs[C];
   __shared__ float cs[C], rs[C];  // kOsdn: c_t and r_t
-  __shared__ float sk[C], sq[C];  // NORM: 1 / ||k_t||, 1 / ||q_t||
+  __shared__ float sk[C], sq_[MODE == kOsdn ? 1 : C];  // NORM: 1 / ||k_t||, 1 / ||q_t||
   __shared__ float lga[C];        // GATED: lg_t, the running sum of log2 alpha
-  __shared__ float xdl[C];        // GATED: gamma_L / gamma_t
+  // Two arrays share space, so that the raw-input gated pass fits three
+  // workgroups per CU: 1 / ||q_t|| (last read by the record's factors) lies in
+  // kt's tile past the 512 bytes that carry d_32 (kOsdn writes kt only after
+  // the recurrence), and gamma_L / gamma_t is written over c_t once the
+  // recurrence is done.
+  float *const sq = MODE == kOsdn ? (float *)Kts + 128 : sq_;
+  float *const xdl = cs;          // GATED: gamma_L / gamma_t
   // GK: the diagonal blocks of A and P (fp32 sums); the products of alpha over
   // each 16-token block, per key dimension [block][i] (alpha itself is read
   // from global memory where it is used)
@@ -270,7 +276,6 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const float gm = fexp2(lga[tid]), lgL = lga[C - 1];
       kf *= gm;
       qf *= gm;
-      xdl[tid] = fexp2(lgL - lga[tid]);
       if (tid == 0) *(float *)(rec + OFF_GL) = fexp2(lgL);
     }
     *(float *)(rec + OFF_KF + 4 * tid) = kf;
@@ -337,6 +342,10 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int t = 0; t < C / 2; ++t) Kts[(t0h + t) * KP + dim] = h(xa[t] * inv);
     __syncthreads();
   }
+
+  // GATED: gamma_L / gamma_t for the S-update operands, over c_t now that the
+  // recurrence is done with it
+  if (GATED && !GK && tid < C) xdl[tid] = fexp2(lga[C - 1] - lga[tid]);
 
   if (GK) {
     // (a) the diagonal blocks of A and P term by term.  Wave b takes block b;
