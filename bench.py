@@ -1,7 +1,7 @@
 """Benchmark of the OSDN forward hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1.3b-apf]
-                    [--no-cpu-baseline] [--only forward|phases]
+                    [--no-cpu-baseline] [--only forward|phases|configs]
 
 A step is one osdn_forward call (preconditioner walk + chunkwise pass) over
 the whole workload, inputs already resident in HBM.  Several input copies
@@ -9,7 +9,9 @@ rotate so the working set exceeds the 256 MB last-level cache.  Prints ONE
 JSON line (rank 0).  Besides the end-to-end figure it times the standalone
 phases (osdn_precond_scan, osdn_chunk_fwd) and the plain delta rule
 (OSDN_PRECOND_OFF), reports the dominant kernel against the HBM roofline,
-and times the fp64 CPU oracle on the host as a reported baseline.
+measures every configuration (tokens/s, roofline fraction, q_geo), and times
+the fp64 CPU oracle on the host as a reported baseline.  Every time is the
+median of per-call HIP event times, reported with its mean, minimum and maximum.
 """
 from __future__ import annotations
 
@@ -36,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="1.3b-apf")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "forward", "phases"], default="all")
+    ap.add_argument("--only", choices=["all", "forward", "phases", "configs"], default="all")
     return ap.parse_args()
 
 
@@ -117,19 +119,32 @@ def stored_traffic(kernel: str, workload: str):
 
 
 def time_launches(fn, steps, warmup, torch):
-    """Average ms per call of fn(i) over `steps` calls, HIP events on the
-    current stream (the library launches on that stream)."""
+    """Per-call times of fn(i): `warmup` untimed calls, then `steps` calls, each
+    between two HIP events recorded on the current stream (the library launches
+    on that stream), the whole run bracketed by device synchronisations.
+    Returns dict(ms=median, mean, min, max, n) in milliseconds; `mean` is the
+    first start to the last end over the calls."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     for i in range(steps):
+        ev[i][0].record()
         fn(i)
-    end.record()
+        ev[i][1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    n = len(ts)
+    med = ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2])
+    return {"ms": med, "mean": ev[0][0].elapsed_time(ev[-1][1]) / n, "min": ts[0],
+            "max": ts[-1], "n": n}
+
+
+def timing_fields(t):
+    """The spread of a time_launches result, for the JSON line."""
+    return {"ms": t["ms"], "ms_mean": t["mean"], "ms_min": t["min"], "ms_max": t["max"],
+            "calls": t["n"]}
 
 
 def cpu_baseline(w, inp):
@@ -177,23 +192,23 @@ def bench_step(args, torch, osdn, W):
     d = 0.5 + torch.rand(w.B, w.H, w.dk, device="cuda", generator=g)
     tok = [t[:, :, 0].contiguous() for t in (dev.q, dev.k, dev.v, dev.beta, dev.r)]
     o = torch.empty_like(tok[2])
-    ms = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S, d, tok[4],
-                                           eta=w.eta, o=o), args.steps, args.warmup, torch)
+    t = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S, d, tok[4],
+                                          eta=w.eta, o=o), args.steps, args.warmup, torch)
     # the same step with one state gate per key dimension
     ach = W.generate(dataclasses.replace(w, gated=True, gate_channels=True)).alpha[:, :, 0]
     ach = ach.contiguous().to("cuda")
-    ms_ch = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S, d, tok[4],
-                                              eta=w.eta, o=o, alpha=ach),
-                          args.steps, args.warmup, torch)
+    t_ch = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S, d, tok[4],
+                                             eta=w.eta, o=o, alpha=ach),
+                         args.steps, args.warmup, torch)
     heads = w.B * w.H
     # S read and written (fp32), d read and written, q, k, v read and o written
     # (bf16), beta and r read
     nbytes = heads * (2 * w.dv * w.dk * 4 + 2 * w.dk * 4 + (2 * w.dk + 2 * w.dv) * 2 + 8)
-    return {"workload": w.name, "ms": ms, "tokens_per_s": w.B / (ms * 1e-3),
+    return {"workload": w.name, **timing_fields(t), "tokens_per_s": w.B / (t["ms"] * 1e-3),
             "algorithmic_bytes": nbytes,
-            "hbm_frac": nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-            "per_channel_gate": {"ms": ms_ch,
-                                 "hbm_frac": (nbytes + heads * w.dk * 4) / (ms_ch * 1e-3)
+            "hbm_frac": nbytes / (t["ms"] * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "per_channel_gate": {**timing_fields(t_ch),
+                                 "hbm_frac": (nbytes + heads * w.dk * 4) / (t_ch["ms"] * 1e-3)
                                  / (HBM_PEAK_GBS * 1e9)}}
 
 
@@ -207,6 +222,57 @@ def gpu_clocks():
         return {k: v for k, v in card.items() if "sclk" in k or "mclk" in k}
     except Exception:  # noqa: BLE001 - purely informational
         return None
+
+
+def q_geo_of(osdn, torch, d, w, precond, ws):
+    """exp of the mean of log rho_t over all (b, h, t) of one forward."""
+    r = osdn.forward(d.q, d.k, d.v, d.beta, d.r, eta=d.eta, chunk=w.chunk, precond=precond,
+                     workspace=ws)
+    torch.cuda.synchronize()
+    return float(torch.exp(r["log_ratio_sum"].double().sum() / (w.B * w.H * w.T)))
+
+
+def bench_config(key, args, torch, osdn, W, steps):
+    """One measured configuration: the forward on its fastest path (median of
+    `steps` event-timed calls over rotating input copies), its fraction of the
+    HBM roofline (algorithmic bytes), q_geo for OSDN and for the plain delta
+    rule on the same inputs, and the path that ran."""
+    w = W.CONFIGS[key]
+    host = W.generate(w)
+    per_copy = sum(t.numel() * t.element_size() for t in (host.q, host.k, host.v, host.beta))
+    copies = max(2, -(-2 * CACHE_BYTES // per_copy))
+    devs = [host.to("cuda") for _ in range(copies)]
+    del host
+    code = 0 if w.dtype == "bf16" else 1
+    B, H, T, dk, dv, C = w.B, w.H, w.T, w.dk, w.dv, w.chunk
+    ws_n = osdn.forward_workspace_bytes(B, H, T, dk, dv, C, code)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    path = osdn.forward_path(B, H, T, dk, dv, C, code, workspace_bytes=ws_n)
+    outs = [{
+        "o": torch.empty_like(d.v),
+        "S_final": torch.empty((B, H, dv, dk), dtype=torch.float32, device="cuda"),
+        "d_final": torch.empty((B, H, dk), dtype=torch.float32, device="cuda"),
+        "log_ratio_sum": torch.empty((B, H), dtype=torch.float32, device="cuda"),
+    } for d in devs]
+
+    def fwd(i):
+        d = devs[i % copies]
+        osdn.forward(d.q, d.k, d.v, d.beta, d.r, eta=d.eta, chunk=C, out=outs[i % copies],
+                     workspace=ws)
+
+    t = time_launches(fwd, steps, max(3, args.warmup), torch)
+    nbytes = algorithmic_bytes(w, "fused")
+    res = {"workload": w.name, "path": path, **timing_fields(t),
+           "tokens_per_s": B * T / (t["ms"] * 1e-3),
+           "hbm_frac": nbytes / (t["ms"] * 1e-3) / (HBM_PEAK_GBS * 1e9),
+           "algorithmic_bytes": nbytes,
+           "q_geo": q_geo_of(osdn, torch, devs[0], w, True, ws),
+           "q_geo_deltanet_mode": q_geo_of(osdn, torch, devs[0], w, False, ws)}
+    if key == "tiny":
+        res["note"] = "parity case (16 KB tensors): launch latency, not a roofline figure"
+    del devs, outs, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -242,6 +308,14 @@ def main():
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda") if ws_n else None
     path = osdn.forward_path(B, H, T, dk, dv, C, code, workspace_bytes=ws_n)
 
+    def fpath(precond=True, single=False, per_channel=False, n=None):
+        """The path osdn_forward takes for one timed variant."""
+        if n is None:
+            n = 0 if single else osdn.forward_workspace_bytes(B, H, T, dk, dv, C, code, precond,
+                                                              per_channel=per_channel)
+        return osdn.forward_path(B, H, T, dk, dv, C, code, precond, workspace_bytes=n,
+                                 per_channel=per_channel)
+
     def fwd(i, precond=True, gated=False, single=False):
         # single: no optional scratch, so the one-kernel forward runs
         d = devs[i % copies]
@@ -252,32 +326,35 @@ def main():
                      workspace=None if single else ws)
 
     print("[bench] path=%s copies=%d" % (path, copies), file=sys.stderr, flush=True)
-    ms = time_launches(fwd, args.steps, args.warmup, torch)
+    tf = time_launches(fwd, args.steps, args.warmup, torch)
+    ms = tf["ms"]
     tokens = B * T
     result = {
         "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "timing": {"statistic": "median of per-call HIP event times", **timing_fields(tf)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if (path in ("fused", "split") and w.dtype == "bf16") else "f32",
         "data": "synthetic (seeded generator; shapes and distributions of the workload)",
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C,
                    "eta": w.eta, "apf": w.apf, "storage": w.dtype, "path": path},
     }
-    print("[bench] forward %.4f ms/step" % ms, file=sys.stderr, flush=True)
+    print("[bench] forward %.4f ms/step (median; min %.4f max %.4f)" % (ms, tf["min"], tf["max"]),
+          file=sys.stderr, flush=True)
 
     phases = {}
     if args.only in ("all", "phases"):
-        ms_dn = time_launches(lambda i: fwd(i, precond=False), args.steps, args.warmup, torch)
-        ms_single = time_launches(lambda i: fwd(i, single=True), args.steps, args.warmup, torch)
-        ms_dn_single = time_launches(lambda i: fwd(i, precond=False, single=True), args.steps,
-                                     args.warmup, torch)
-        ms_g = time_launches(lambda i: fwd(i, gated=True), args.steps, args.warmup, torch)
-        ms_gdn = time_launches(lambda i: fwd(i, precond=False, gated=True), args.steps,
-                               args.warmup, torch)
-        ms_g_single = time_launches(lambda i: fwd(i, gated=True, single=True), args.steps,
+        t_dn = time_launches(lambda i: fwd(i, precond=False), args.steps, args.warmup, torch)
+        t_single = time_launches(lambda i: fwd(i, single=True), args.steps, args.warmup, torch)
+        t_dn_single = time_launches(lambda i: fwd(i, precond=False, single=True), args.steps,
                                     args.warmup, torch)
-        ms_gdn_single = time_launches(lambda i: fwd(i, precond=False, gated=True, single=True),
-                                      args.steps, args.warmup, torch)
+        t_g = time_launches(lambda i: fwd(i, gated=True), args.steps, args.warmup, torch)
+        t_gdn = time_launches(lambda i: fwd(i, precond=False, gated=True), args.steps,
+                              args.warmup, torch)
+        t_g_single = time_launches(lambda i: fwd(i, gated=True, single=True), args.steps,
+                                   args.warmup, torch)
+        t_gdn_single = time_launches(lambda i: fwd(i, precond=False, gated=True, single=True),
+                                     args.steps, args.warmup, torch)
         # raw inputs (q, k unnormalised, beta and r as logits): the transforms done
         # inside the kernels, against separate elementwise passes before the call
         raw_host = W.generate(dataclasses.replace(w, raw=True))
@@ -297,18 +374,17 @@ def main():
                              None if d.r is None else torch.sigmoid(d.r), eta=d.eta, chunk=C,
                              out=o, workspace=ws)
 
-        ms_raw = time_launches(fwd_raw, args.steps, args.warmup, torch)
-        ms_raw_sep = time_launches(lambda i: fwd_raw(i, False), args.steps, args.warmup, torch)
+        t_raw = time_launches(fwd_raw, args.steps, args.warmup, torch)
+        t_raw_sep = time_launches(lambda i: fwd_raw(i, False), args.steps, args.warmup, torch)
         del raws
         # the per-channel gate (KDA backbone): the same draws with one gate per key
-        # dimension, on the two-phase path
+        # dimension
         kda_alpha = W.generate(dataclasses.replace(w, gated=True, gate_channels=True)).alpha
         kalphas = [kda_alpha.to("cuda") for _ in range(2)]
         del kda_alpha
         kws_n = osdn.forward_workspace_bytes(B, H, T, dk, dv, C, code, per_channel=True)
         kws = torch.empty(max(kws_n, 1), dtype=torch.uint8, device="cuda")
-        kda_path = osdn.forward_path(B, H, T, dk, dv, C, code, per_channel=True,
-                                     workspace_bytes=kws_n)
+        kda_path = fpath(per_channel=True, n=kws_n)
 
         def fwd_kda(i, precond=True):
             d = devs[i % copies]
@@ -318,8 +394,8 @@ def main():
                          workspace=kws)
 
         kda_steps = max(2, args.steps // 4)
-        ms_kda = time_launches(fwd_kda, kda_steps, 1, torch)
-        ms_kda_dn = time_launches(lambda i: fwd_kda(i, False), kda_steps, 1, torch)
+        t_kda = time_launches(fwd_kda, kda_steps, 1, torch)
+        t_kda_dn = time_launches(lambda i: fwd_kda(i, False), kda_steps, 1, torch)
         del kalphas, kws
         kts = [torch.empty_like(d.k) for d in devs]
         dfin = torch.empty((B, H, dk), dtype=torch.float32, device="cuda")
@@ -353,49 +429,50 @@ def main():
                                     cws_n if use_ws else 0, stream)
             assert st == 0, st
 
-        ms_scan = time_launches(scan, args.steps, args.warmup, torch)
-        ms_scan_single = time_launches(lambda i: scan(i, False), args.steps, args.warmup, torch)
-        ms_chunk = time_launches(chunk, args.steps, args.warmup, torch)
-        ms_chunk_single = time_launches(lambda i: chunk(i, False), args.steps, args.warmup, torch)
+        t_scan = time_launches(scan, args.steps, args.warmup, torch)
+        t_scan_single = time_launches(lambda i: scan(i, False), args.steps, args.warmup, torch)
+        t_chunk = time_launches(chunk, args.steps, args.warmup, torch)
+        t_chunk_single = time_launches(lambda i: chunk(i, False), args.steps, args.warmup, torch)
+        ms_dn, ms_scan, ms_chunk = t_dn["ms"], t_scan["ms"], t_chunk["ms"]
+        ms_g, ms_gdn = t_g["ms"], t_gdn["ms"]
+
+        def entry(t, p, **kw):
+            return {**timing_fields(t), "tokens_per_s": tokens / (t["ms"] * 1e-3), "path": p,
+                    **kw}
+
         phases = {
-            "forward_single_kernel": {"ms": ms_single, "tokens_per_s": tokens / (ms_single * 1e-3),
-                                      "traffic": stored_traffic("osdn_fused_forward",
-                                                                args.workload)},
-            "deltanet_mode_single_kernel": {"ms": ms_dn_single},
-            "precond_scan": {"ms": ms_scan, "tokens_per_s": tokens / (ms_scan * 1e-3),
-                             "hbm_frac": algorithmic_bytes(w, "scan") / (ms_scan * 1e-3)
-                             / (HBM_PEAK_GBS * 1e9),
-                             "traffic": stored_traffic("osdn_precond_scan_split", args.workload)},
-            "precond_scan_single_kernel": {"ms": ms_scan_single},
-            "chunk_fwd": {"ms": ms_chunk, "tokens_per_s": tokens / (ms_chunk * 1e-3),
-                          "hbm_frac": algorithmic_bytes(w, "chunk") / (ms_chunk * 1e-3)
-                          / (HBM_PEAK_GBS * 1e9),
-                          "traffic": stored_traffic("osdn_chunk_fwd_split", args.workload)},
-            "chunk_fwd_single_kernel": {"ms": ms_chunk_single},
-            "deltanet_mode": {"ms": ms_dn, "tokens_per_s": tokens / (ms_dn * 1e-3),
-                              "traffic": stored_traffic("osdn_deltanet_split", args.workload)},
+            "forward_single_kernel": entry(t_single, fpath(single=True),
+                                           traffic=stored_traffic("osdn_fused_forward",
+                                                                  args.workload)),
+            "deltanet_mode_single_kernel": entry(t_dn_single, fpath(False, single=True)),
+            "precond_scan": entry(t_scan, "walk_prep+walk+walk_keys" if sws_n else "single",
+                                  hbm_frac=algorithmic_bytes(w, "scan") / (ms_scan * 1e-3)
+                                  / (HBM_PEAK_GBS * 1e9),
+                                  traffic=stored_traffic("osdn_precond_scan_split",
+                                                         args.workload)),
+            "precond_scan_single_kernel": entry(t_scan_single, "one kernel per (b,h)"),
+            "chunk_fwd": entry(t_chunk, "chunk_prep+chunk_state" if cws_n else "single",
+                               hbm_frac=algorithmic_bytes(w, "chunk") / (ms_chunk * 1e-3)
+                               / (HBM_PEAK_GBS * 1e9),
+                               traffic=stored_traffic("osdn_chunk_fwd_split", args.workload)),
+            "chunk_fwd_single_kernel": entry(t_chunk_single, "single fused kernel (given kt)"),
+            "deltanet_mode": entry(t_dn, fpath(False),
+                                   traffic=stored_traffic("osdn_deltanet_split", args.workload)),
             "precond_overhead": (ms - ms_dn) / ms,
-            "gated_forward": {"ms": ms_g, "tokens_per_s": tokens / (ms_g * 1e-3),
-                              "vs_ungated": ms_g / ms,
-                              "traffic": stored_traffic("osdn_forward_gated_split",
-                                                        args.workload)},
-            "gated_deltanet_mode": {"ms": ms_gdn, "tokens_per_s": tokens / (ms_gdn * 1e-3)},
-            "gated_forward_single_kernel": {"ms": ms_g_single,
-                                            "tokens_per_s": tokens / (ms_g_single * 1e-3)},
-            "gated_deltanet_mode_single_kernel": {
-                "ms": ms_gdn_single, "tokens_per_s": tokens / (ms_gdn_single * 1e-3)},
+            "gated_forward": entry(t_g, fpath(), vs_ungated=ms_g / ms,
+                                   traffic=stored_traffic("osdn_forward_gated_split",
+                                                          args.workload)),
+            "gated_deltanet_mode": entry(t_gdn, fpath(False)),
+            "gated_forward_single_kernel": entry(t_g_single, fpath(single=True)),
+            "gated_deltanet_mode_single_kernel": entry(t_gdn_single, fpath(False, single=True)),
             "gated_precond_overhead": (ms_g - ms_gdn) / ms_g,
-            "raw_inputs_transforms_in_kernels": {
-                "ms": ms_raw, "tokens_per_s": tokens / (ms_raw * 1e-3),
-                "traffic": stored_traffic("osdn_forward_raw_split", args.workload)},
-            "per_channel_gate_forward": {"ms": ms_kda, "tokens_per_s": tokens / (ms_kda * 1e-3),
-                                         "path": kda_path, "steps": kda_steps,
-                                         "traffic": stored_traffic("osdn_forward_kda_split",
-                                                                   args.workload)},
-            "per_channel_gate_deltanet_mode": {"ms": ms_kda_dn,
-                                               "tokens_per_s": tokens / (ms_kda_dn * 1e-3)},
-            "raw_inputs_separate_torch_passes": {"ms": ms_raw_sep,
-                                                 "tokens_per_s": tokens / (ms_raw_sep * 1e-3)},
+            "raw_inputs_transforms_in_kernels": entry(
+                t_raw, fpath(), traffic=stored_traffic("osdn_forward_raw_split", args.workload)),
+            "per_channel_gate_forward": entry(t_kda, kda_path,
+                                              traffic=stored_traffic("osdn_forward_kda_split",
+                                                                     args.workload)),
+            "per_channel_gate_deltanet_mode": entry(t_kda_dn, fpath(False, per_channel=True)),
+            "raw_inputs_separate_torch_passes": entry(t_raw_sep, fpath()),
             "two_launch_scan_share": ms_scan / (ms_scan + ms_chunk),
         }
         result["phases"] = phases
@@ -430,17 +507,22 @@ def main():
                       "counters": stored_mfma(kname, args.workload)}
     # geometric mean of the residual ratios rho_t over all (b, h, t), OSDN and
     # the plain delta rule on the same inputs
-    qg = {}
-    for mode, pre in (("osdn", True), ("deltanet_mode", False)):
-        d = devs[0]
-        r = osdn.forward(d.q, d.k, d.v, d.beta, d.r, eta=d.eta, chunk=C, precond=pre,
-                         workspace=ws)
-        torch.cuda.synchronize()
-        qg[mode] = float(torch.exp(r["log_ratio_sum"].double().sum() / (B * H * T)))
-    result["q_geo"] = qg
+    result["q_geo"] = {"osdn": q_geo_of(osdn, torch, devs[0], w, True, ws),
+                       "deltanet_mode": q_geo_of(osdn, torch, devs[0], w, False, ws)}
 
     if args.only in ("all", "phases"):
         result["decode_step"] = bench_step(args, torch, osdn, W)
+
+    if args.only in ("all", "configs"):
+        # every measured configuration on its fastest path (the metric one above
+        # included, re-timed in the same way)
+        del devs, outs, ws
+        torch.cuda.empty_cache()
+        cfg = {}
+        for key in ("tiny", "340m", "340m-apf", "1.3b-apf", "recall", "recall-apf"):
+            print("[bench] config %s" % key, file=sys.stderr, flush=True)
+            cfg[key] = bench_config(key, args, torch, osdn, W, max(20, args.steps // 2))
+        result["configs"] = cfg
 
     result["gpu_clocks"] = gpu_clocks()
     if not args.no_cpu_baseline:

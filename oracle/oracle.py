@@ -36,7 +36,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "osdn_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# OSDN_ORACLE_LIB names a prebuilt oracle library to load instead (the
+# sanitizer test builds one with AddressSanitizer and UndefinedBehaviorSanitizer)
+_LIB_ENV = os.environ.get("OSDN_ORACLE_LIB")
+_LIB_PATH = _LIB_ENV or os.path.join(_HERE, "liboracle.so")
 _lib = None
 _lib_lock = threading.Lock()
 
@@ -58,8 +61,8 @@ def _load():
     global _lib
     with _lib_lock:
         if _lib is None:
-            if not os.path.exists(_LIB_PATH) or (
-                    os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+            if not _LIB_ENV and (not os.path.exists(_LIB_PATH) or (
+                    os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))):
                 build(force=True)
             lib = ctypes.CDLL(_LIB_PATH)
             P = ctypes.c_void_p

@@ -241,7 +241,7 @@ def test_gated_steps_continue_a_gated_forward():
 @pytest.mark.slow
 @pytest.mark.parametrize("ws", [True, None])
 def test_gated_workload_full_size(ws):
-    """The gated 1.3B-style layer at full size, on sampled heads."""
+    """The gated 1.3B-style layer at full size, every (b,h) compared."""
     w = W.CONFIGS["1.3b-apf-gated"]
     inp = W.generate(w)
-    _check(w, inp, heads=_heads(w, 4), ws=ws)
+    _check(w, inp, heads=_heads(w, w.B * w.H), ws=ws)

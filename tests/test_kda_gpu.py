@@ -275,7 +275,7 @@ def test_per_channel_steps_continue_a_forward():
 @pytest.mark.slow
 @pytest.mark.parametrize("ws", [True, "two-phase"])
 def test_per_channel_workload_full_size(ws):
-    """The 1.3B-style layer with per-channel gates at full size, on sampled heads."""
+    """The 1.3B-style layer with per-channel gates at full size, every (b,h) compared."""
     w = W.CONFIGS["1.3b-apf-kda"]
     inp = W.generate(w)
-    _check(w, inp, heads=_heads(w, 4), ws=ws)
+    _check(w, inp, heads=_heads(w, w.B * w.H), ws=ws)

@@ -168,11 +168,11 @@ def test_precond_scan_chunk_boundaries(T, ws):
 
 @pytest.mark.parametrize("ws", [True, None])
 @pytest.mark.parametrize("name", ["1.3b-apf", "recall-apf"])
-def test_precond_scan_full_size_sampled_heads(name, ws):
-    """The standalone walk at a workload's full size, checked on sampled heads."""
+def test_precond_scan_full_size(name, ws):
+    """The standalone walk at a workload's full size, every (b,h) checked."""
     w = W.CONFIGS[name]
     inp = W.generate(w)
-    heads = _heads(w, 3)
+    heads = _heads(w, w.B * w.H)
     dev = _to_dev(inp)
     _log("scan full size %s heads=%s ws=%s" % (name, heads, ws))
     out = osdn.precond_scan(dev.k, dev.beta, dev.r, None, inp.eta, want_log_ratio=True,
@@ -268,6 +268,15 @@ def test_forward_with_initial_state(precond, ws):
     S0 = 0.05 * torch.randn(w.B, w.H, w.dv, w.dk, generator=g)
     d0 = 0.5 + torch.rand(w.B, w.H, w.dk, generator=g)
     _check_forward(w, inp, _heads(w, 4), precond=precond, d0=d0, S0=S0, ws=ws)
+
+
+@pytest.mark.parametrize("precond", [True, False])
+def test_forward_many_heads_every_head(precond):
+    """B*H = 24 and 40 (multiples of 8): the state kernel's grouping of a head's
+    channel tiles onto one XCD maps blocks past the first 32, every head compared."""
+    for B, H in ((3, 8), (5, 8)):
+        w = W.custom(B, H, 140, 128, 128, 64, dtype="bf16", eta=0.1, apf=True, seed=B * H)
+        _check_forward(w, W.generate(w), _heads(w, B * H), precond=precond)
 
 
 def test_forward_deltanet_mode_small():
@@ -411,23 +420,23 @@ def test_basis_keys_closed_form():
 
 
 # ---------------------------------------------------------------------------
-# the five measured workloads at full size (sampled heads)
+# the five measured workloads at full size, every (b,h) compared
 # ---------------------------------------------------------------------------
 
-FULL = [("tiny", 1), ("340m", 4), ("340m-apf", 4), ("1.3b-apf", 4), ("recall", 3),
-        ("recall-apf", 3)]
+FULL = ["tiny", "340m", "340m-apf", "1.3b-apf", "recall", "recall-apf"]
+EVERY = 1 << 30  # _heads(w, EVERY) is every (b,h) of the workload
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("ws", [True, None])
-@pytest.mark.parametrize("name,nheads", FULL)
-def test_workload_full_size(name, nheads, ws):
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full_size(name, ws):
     w = W.CONFIGS[name]
     inp = W.generate(w)
-    out, ref, errs = _check_forward(w, inp, _heads(w, nheads), label=name, ws=ws)
+    out, ref, errs = _check_forward(w, inp, _heads(w, EVERY), label=name, ws=ws)
     if name.startswith("recall") or name == "1.3b-apf":
-        # q_geo over the sampled heads agrees with the oracle's
-        heads = _heads(w, nheads)
+        # q_geo over every head agrees with the oracle's
+        heads = _heads(w, EVERY)
         lrs = _select(out["log_ratio_sum"], heads, w)
         q_gpu = float(np.exp(lrs.sum() / (len(heads) * w.T)))
         q_ref = oracle.q_geo(_select(ref["rho"], heads, w))

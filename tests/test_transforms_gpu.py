@@ -171,6 +171,6 @@ def test_step_raw_inputs(dtype, dk, dv):
 
 @pytest.mark.slow
 def test_raw_workload_full_size():
-    """The 1.3B-style layer drawn raw, at full size, on sampled heads."""
+    """The 1.3B-style layer drawn raw, at full size, every (b,h) compared."""
     w = dataclasses.replace(W.CONFIGS["1.3b-apf"], raw=True)
-    _check(w, W.generate(w), heads=_heads(w, 3))
+    _check(w, W.generate(w), heads=_heads(w, w.B * w.H))
