@@ -36,9 +36,10 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <typename T, int DK, int DVT, int C, bool GK>
+// KT: the type of the write keys (T, or fp32 from the two-phase forward's scratch)
+template <typename T, typename KT, int DK, int DVT, int C, bool GK>
 __global__ void __launch_bounds__(kThreads)
-chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ kt,
+chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const KT *__restrict__ kt,
               const T *__restrict__ v, const float *__restrict__ beta,
               const float *__restrict__ alpha, const float *__restrict__ S0, int T_, int dv,
               T *__restrict__ o, float *__restrict__ S_final, unsigned xf) {
@@ -85,7 +86,7 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
       const bool ok = t < L;
       const long g = (tok0 + c0 + t) * DK + i;
       sK[t * DKP + i] = ok ? Elem<T>::load(k + g) : 0.0f;
-      sKt[t * DKP + i] = ok ? Elem<T>::load(kt + g) : 0.0f;
+      sKt[t * DKP + i] = ok ? Elem<KT>::load(kt + g) : 0.0f;
     }
     for (int idx = tid; idx < C * DVT; idx += kThreads) {
       const int t = idx / DVT, j = idx % DVT;
@@ -236,15 +237,14 @@ chunk_generic(const T *__restrict__ q, const T *__restrict__ k, const T *__restr
   }
 }
 
-template <typename T, int DK, int DVT, bool GK>
+template <typename T, typename KT, int DK, int DVT, bool GK>
 hipError_t launch_c(const ChunkArgs &a, hipStream_t s, dim3 grid) {
   const dim3 block(kThreads);
 #define OSDN_GEN_CASE(C_)                                                                      \
   case C_:                                                                                     \
-    hipLaunchKernelGGL((chunk_generic<T, DK, DVT, C_, GK>), grid, block, 0, s, (const T *)a.q, \
-                       (const T *)a.k, (const T *)a.k_tilde, (const T *)a.v, a.beta, a.alpha,\
-                       a.S0,                                                                   \
-                       a.T, a.dv, (T *)a.o, a.S_final, a.xf);                                 \
+    hipLaunchKernelGGL((chunk_generic<T, KT, DK, DVT, C_, GK>), grid, block, 0, s,             \
+                       (const T *)a.q, (const T *)a.k, (const KT *)a.k_tilde, (const T *)a.v,  \
+                       a.beta, a.alpha, a.S0, a.T, a.dv, (T *)a.o, a.S_final, a.xf);          \
     break;
   switch (a.chunk) {
     OSDN_GEN_CASE(16)
@@ -257,36 +257,37 @@ hipError_t launch_c(const ChunkArgs &a, hipStream_t s, dim3 grid) {
   return hipGetLastError();
 }
 
-template <typename T, int DVT, bool GK>
+template <typename T, typename KT, int DVT, bool GK>
 hipError_t launch_dk(const ChunkArgs &a, hipStream_t s, dim3 grid) {
   switch (a.dk) {
-    case 16: return launch_c<T, 16, DVT, GK>(a, s, grid);
-    case 32: return launch_c<T, 32, DVT, GK>(a, s, grid);
-    case 64: return launch_c<T, 64, DVT, GK>(a, s, grid);
-    case 128: return launch_c<T, 128, DVT, GK>(a, s, grid);
+    case 16: return launch_c<T, KT, 16, DVT, GK>(a, s, grid);
+    case 32: return launch_c<T, KT, 32, DVT, GK>(a, s, grid);
+    case 64: return launch_c<T, KT, 64, DVT, GK>(a, s, grid);
+    case 128: return launch_c<T, KT, 128, DVT, GK>(a, s, grid);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, bool GK>
+template <typename T, typename KT, bool GK>
 hipError_t launch_g(const ChunkArgs &a, hipStream_t s) {
   const int dvt = a.dv >= 32 ? 32 : 16;
   const dim3 grid((unsigned)(a.B * a.H), (unsigned)(a.dv / dvt));
-  return dvt == 32 ? launch_dk<T, 32, GK>(a, s, grid) : launch_dk<T, 16, GK>(a, s, grid);
+  return dvt == 32 ? launch_dk<T, KT, 32, GK>(a, s, grid) : launch_dk<T, KT, 16, GK>(a, s, grid);
 }
 
 // the per-channel gate takes its own instances (a [C][DK] table of decays)
-template <typename T>
+template <typename T, typename KT>
 hipError_t launch_t(const ChunkArgs &a, hipStream_t s) {
-  if ((a.xf & kGateChannels) && a.alpha) return launch_g<T, true>(a, s);
-  return launch_g<T, false>(a, s);
+  if ((a.xf & kGateChannels) && a.alpha) return launch_g<T, KT, true>(a, s);
+  return launch_g<T, KT, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t s) {
   if ((long)a.B * a.H == 0) return hipSuccess;
-  return a.dtype == 0 ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
+  if (a.dtype != 0) return launch_t<float, float>(a, s);
+  return (a.xf & kKtF32) ? launch_t<bf16, float>(a, s) : launch_t<bf16, bf16>(a, s);
 }
 
 }  // namespace osdn

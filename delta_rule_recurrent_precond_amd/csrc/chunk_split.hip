@@ -25,8 +25,11 @@
 //   lr   fp32 (kt = k only) sum over the chunk of log rho_t, rho_t = (1 - beta_t ||k_t||^2)^2
 //   gL   fp32 (state gate) gamma_L, the decay of the chunk's entry state
 //   sc   fp32 [2][64] (unnormalised q, k or a state gate) per-token factors of the
-//        rows of K S^T and Q S^T: 1/||k_t|| gamma_t and 1/||q_t|| gamma_t
+//        rows of K S^T and Q S^T: e_k/||k_t|| gamma_t and e_q/||q_t|| gamma_t
 //        (gamma_t: product of the gates of the chunk up to t; L: its last row)
+//   e    fp32 [2] (unnormalised q, k) 1 / e_k and 1 / e_q: raw k and q are staged
+//        divided by these powers of two (>= the chunk's largest |k|, |q|), which
+//        keeps every stored value exact in fp16 whatever the inputs' scale
 // op x = 0..5 is (row block m, t pair qq) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
 //
 // With the state gate alpha (OSDN on the Gated DeltaNet backbone, read as
@@ -78,7 +81,10 @@ constexpr size_t OFF_DS = 28672;
 constexpr size_t OFF_LR = 28676;  // kt = k: sum over the chunk of log rho_t
 constexpr size_t OFF_GL = 28680;  // gamma_L
 constexpr size_t OFF_SC = 28688;  // per-token factors of the K rows, then of the Q rows
-constexpr size_t OFF_KF = OFF_SC, OFF_QF = OFF_SC + 256, OFF_END = OFF_SC + 512;
+constexpr size_t OFF_KF = OFF_SC, OFF_QF = OFF_SC + 256;
+// NORM: the powers of two that raw k and q are divided by when staged (fp32
+// 1 / e_k, 1 / e_q), then padding to a 16-byte piece
+constexpr size_t OFF_E = OFF_SC + 512, OFF_END = OFF_E + 16;
 // the record with the per-channel gate: the above, then K (.) G and Q (.) G as
 // fp16 [64][128] row-major, then g_L fp32 [128]
 constexpr size_t OFF_KG = 32768, OFF_QG = 49152, OFF_GV = 65536, RECK = 66048;
@@ -143,6 +149,9 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   __shared__ __align__(16) float Bk[GK ? 4 * DK : 4];
   __shared__ __align__(16) f16 Zrow[GK ? DK : 8];  // GK: zeros
   __shared__ float red[4];
+  // XN with kt = k: the chunk's largest |k| and |q| per wave (kOsdn passes them
+  // through its kt tile instead, which nothing writes before the staging)
+  __shared__ float nred_[(NORM && !GK && MODE != kOsdn) ? 8 : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -151,6 +160,12 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
   unsigned char *rec = ws + ((long)bh * NC + c) * (GK ? RECK : REC);
+  // XN: raw q and k are staged exactly, divided by a power of two per chunk,
+  // and their normalisation enters as fp32 row and column factors of the
+  // products (rounding the unit vectors to fp16 instead would put up to 2^-12
+  // relative error on every element, which a near-orthogonal q . kt -- the
+  // first token's output -- amplifies without bound)
+  constexpr bool XN = NORM && !GK;
   // the write keys (GK keeps a copy of k for kt = k: the rows of Ks are rescaled)
   const f16 *Ktp = (MODE == kDeltaNet && !GK) ? Ks : Kts;
 
@@ -187,9 +202,15 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const float rv = r ? r[tok0 + min(tid, L - 1)] : 1.0f;
     rs[tid] = (r && tid < L) ? ((xf & kGateLogits) ? sigmoid_gate(rv) : rv) : 1.0f;
   }
-  // per-token normalisation scales (16 threads per token hold its pieces)
+  // per-token normalisation scales (16 threads per token hold its pieces):
+  // kinv = 1 / ||k_t||; XN: ik = 1 / e_k, iq = 1 / e_q with e a power of two >= the
+  // chunk's largest |k| (|q|), and the factors kscale = e_k / ||k_t||, qscale =
+  // e_q / ||q_t|| that turn the staged rows into unit vectors
   float kscale[4] = {1.f, 1.f, 1.f, 1.f}, qscale[4] = {1.f, 1.f, 1.f, 1.f};
+  float kinv[4] = {1.f, 1.f, 1.f, 1.f};
+  float ik = 1.f, iq = 1.f;
   if (NORM) {
+    float mk = 0.f, mq = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const unsigned short *sk8 = (const unsigned short *)&rk[u];
@@ -200,9 +221,35 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const float x = bf2f(sk8[e]), y = bf2f(sq8[e]);
         a = fmaf(x, x, a);
         b = fmaf(y, y, b);
+        mk = fmaxf(mk, fabsf(x));
+        mq = fmaxf(mq, fabsf(y));
       }
-      kscale[u] = unit_scale(group_sum<16>(a));
+      kinv[u] = kscale[u] = unit_scale(group_sum<16>(a));
       qscale[u] = unit_scale(group_sum<16>(b));
+    }
+    if (XN) {
+      // the chunk's largest |k| and |q| per wave (kOsdn: through Kts, below
+      // which its d_32 and q-norm factors lie)
+      float *nred = MODE == kOsdn ? (float *)Kts + 256 : nred_;
+      mk = wave_max(mk);
+      mq = wave_max(mq);
+      if (lane == 0) {
+        nred[wave] = mk;
+        nred[4 + wave] = mq;
+      }
+      __syncthreads();
+      const float ek = pow2_above(fmaxf(fmaxf(nred[0], nred[1]), fmaxf(nred[2], nred[3])));
+      const float eq = pow2_above(fmaxf(fmaxf(nred[4], nred[5]), fmaxf(nred[6], nred[7])));
+      ik = 1.0f / ek;
+      iq = 1.0f / eq;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        kscale[u] *= ek;
+        qscale[u] *= eq;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       if ((tid & 15) == 0) {
         const int t = (tid + 256 * u) >> 4;
         sk[t] = kscale[u];
@@ -255,8 +302,10 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
-    *(f16x8 *)&Ks[t * KP + i0] = (NORM && MODE == kDeltaNet) ? cvt8s(rk[u], kscale[u]) : cvt8(rk[u]);
-    *(f16x8 *)&Qs[t * KP + i0] = NORM ? cvt8s(rq[u], qscale[u]) : cvt8(rq[u]);
+    *(f16x8 *)&Ks[t * KP + i0] = XN ? cvt8s(rk[u], ik)
+                                 : (NORM && MODE == kDeltaNet) ? cvt8s(rk[u], kscale[u])
+                                                               : cvt8(rk[u]);
+    *(f16x8 *)&Qs[t * KP + i0] = XN ? cvt8s(rq[u], iq) : NORM ? cvt8s(rq[u], qscale[u]) : cvt8(rq[u]);
     if (MODE == kGiven) {
       const unsigned short *s = (const unsigned short *)&rt[u];
       f16x8 hv;
@@ -280,6 +329,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
     *(float *)(rec + OFF_KF + 4 * tid) = kf;
     *(float *)(rec + OFF_QF + 4 * tid) = qf;
+    if (tid == 0) *(float2 *)(rec + OFF_E) = float2{ik, iq};  // 1 unless XN
   }
 
   if (MODE == kOsdn) {
@@ -312,11 +362,13 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // the normalised key is kv * sv
+          // the normalised key is kv * sv; XN stages the write key in the
+          // staged keys' frame, d_t kv, and its factor sv enters the products
           const float kv = (float)kc[t0 + e];
           const float kh = NORM ? kv * sv[e] : kv;
-          xa[t0 + e] = pr * kh;
-          xb[t0 + e] = d * kh;
+          const float kx = XN ? kv : kh;
+          xa[t0 + e] = pr * kx;
+          xb[t0 + e] = d * kx;
           d = fmaf(cv[e], kh * kh, rv[e] * d);
           pr *= rv[e];
         }
@@ -324,6 +376,9 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (tid < DK) dmid[dim] = d;  // d_32
     }
     __syncthreads();
+    // XN: the scores' query factors move from kt's tile (written below) to r's
+    // array, which the recurrence no longer reads
+    if (XN && tid < C) rs[tid] = sq[tid];
     // first half: x = 0 * xa + xb, exactly xb
     const float dj = tid < DK ? 0.f : dmid[dim];
     float km = 0.f;
@@ -518,10 +573,13 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   };
   auto beta4 = [&](int rt_) { return *(const f32x4 *)&bs[16 * rt_ + 4 * g]; };
   // kOsdn, NORM stages k as stored: the rows of A take the keys' 1/||k||
+  // (XN: e_k / ||k||; also the columns, through colf)
   auto krow4 = [&](int rt_) {
-    return (NORM && MODE == kOsdn) ? *(const f32x4 *)&sk[16 * rt_ + 4 * g]
-                                   : f32x4{1.f, 1.f, 1.f, 1.f};
+    return (NORM && (MODE == kOsdn || XN)) ? *(const f32x4 *)&sk[16 * rt_ + 4 * g]
+                                           : f32x4{1.f, 1.f, 1.f, 1.f};
   };
+  // XN: the factor of write key s (column s of A and of the scores)
+  auto colf = [&](int s) { return XN ? sk[s] : 1.0f; };
   // GATED: gamma_t / gamma_s for rows t = 16 rt + 4g + e and column s (taken
   // only where s <= t, where it is <= 1)
   auto dec4 = [&](int rt_, int s) {
@@ -543,7 +601,13 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   for (int idx = wave; idx < 10; idx += 4) {
     int rt_, ct;
     tri_tile(idx, rt_, ct);
-    const f32x4 acc = !GK ? gram(Qs, rt_, ct) : rt_ == ct ? diag4(Pdg, rt_) : gramk(Qs, rt_, ct);
+    f32x4 acc = !GK ? gram(Qs, rt_, ct) : rt_ == ct ? diag4(Pdg, rt_) : gramk(Qs, rt_, ct);
+    if (XN) {  // the query rows' and the write-key columns' factors
+      const f32x4 qf = *(const f32x4 *)&(MODE == kOsdn ? rs : sq)[16 * rt_ + 4 * g];
+      const float kc = colf(16 * ct + c16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = (acc[e] * qf[e]) * kc;
+    }
     const f32x4 dc = dec4(rt_, 16 * ct + c16);
     f32x4 pv;
 #pragma unroll
@@ -559,10 +623,11 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   {
     const f32x4 acc = GK ? diag4(Adg, wave) : gram(Ks, wave, wave);
     const f32x4 b4 = beta4(wave), f4 = krow4(wave), dc = dec4(wave, 16 * wave + c16);
+    const float kc = colf(16 * wave + c16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 4 * g + e;
-      Fd[wave][row][c16] = c16 < row ? a_entry(b4[e], dc[e], acc[e], f4[e]) : 0.f;
+      Fd[wave][row][c16] = c16 < row ? a_entry(b4[e], dc[e], acc[e] * kc, f4[e]) : 0.f;
     }
   }
   for (int job = wave; job < 6; job += 4) {
@@ -570,8 +635,10 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     off_tile(job, rt_, ct);
     const f32x4 acc = GK ? gramk(Ks, rt_, ct) : gram(Ks, rt_, ct);
     const f32x4 b4 = beta4(rt_), f4 = krow4(rt_), dc = dec4(rt_, 16 * ct + c16);
+    const float kc = colf(16 * ct + c16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Aoff[job][4 * g + e][c16] = h(a_entry(b4[e], dc[e], acc[e], f4[e]));
+    for (int e = 0; e < 4; ++e)
+      Aoff[job][4 * g + e][c16] = h(a_entry(b4[e], dc[e], acc[e] * kc, f4[e]));
   }
   wave_lds_sync();
   {
@@ -599,6 +666,11 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       f32x4 tv = mma16(ld4(&Ktp[(16 * m + c16) * KP + 16 * n + 4 * g]), ident, zero4());
+      if (XN) {  // tokens 16 m + 4 g + e: the write keys' factors
+        const f32x4 kf = *(const f32x4 *)&sk[16 * m + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tv[e] *= kf[e];
+      }
       if (GATED) {
         const f32x4 xd = *(const f32x4 *)&xdl[16 * m + 4 * g];
 #pragma unroll
@@ -631,7 +703,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         sq = fmaf(x, x, sq);
       }
       sq = group_sum<16>(sq);
-      if (NORM) sq *= kscale[u] * kscale[u];  // of the normalised key
+      if (NORM) sq *= kinv[u] * kinv[u];  // of the normalised key
       const float gd = 1.0f - bs[t] * sq;
       if ((p & 15) == 0 && t < L) lr += logf(gd * gd);
     }
@@ -716,11 +788,12 @@ __device__ __forceinline__ int vrow(int lt) {
 struct StateSmem {
   f16 K[2][C * 128];  // kq_chunk layout
   f16 Q[2][C * 128];
-  f16x8 V[2][2][2][64];  // value tile as operands [buf][sn][m >> 1][lane]: rows 16 m + c16, 4 channels
+  uint4 V[2][2][2][64];  // value tile (bf16, exact) as operands [buf][sn][m >> 1][lane]: rows 16 m + c16, 4 channels
   unsigned char rec[2][OFF_END];  // KtF, TmA, PA, ds, factors of the chunk
   float b[2][C];
   f16x8 Sx[2][2][4][64];  // fp16 S^T at a chunk's start [parity][sn][kk][lane], paired order
   f16x8 Xx[2][2][2][64];  // X of a chunk [parity][sn][qq][lane], paired order
+  float sig[2][2][2];     // [parity][sn]: the powers of two Sx and Xx are scaled down by
 };
 static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
 
@@ -764,9 +837,10 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     // Loads are unconditional (a masked lane reads a valid address) and masked
     // values are zeroed when stored: a conditional load makes the compiler wait
     // for it at the end of its branch.
-    // GK: 32 more pieces, g_L, from OFF_GV into the factor slot (piece 1793 on)
+    // GK: 32 more pieces, g_L, from OFF_GV into the factor slot (piece 1793 on);
+    // SCALED: the factors and the staging scales of raw k and q
     constexpr int RP0 = (int)(OFF_DS / 16) + 1;
-    constexpr int RECP = (SCALED || GK) ? (int)(OFF_END / 16) : RP0;
+    constexpr int RECP = GK ? RP0 + 32 : SCALED ? (int)(OFF_END / 16) : RP0;
     static_assert(RP0 * 16 == (int)OFF_SC, "g_L lands in the factor slot");
     constexpr size_t RB = GK ? RECK : REC;
     constexpr int NKQ = (2048 + NL - 1) / NL, NR = (RECP + NL - 1) / NL;
@@ -774,6 +848,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     struct Regs {
       uint4 kq[NKQ], v, r[NR];
       float b;
+      float2 e;  // SCALED: 1 / e_k, 1 / e_q
     };
     Regs ra, rb, rc;
     // chunk cc clamped to the last one: the loads past the end reread it
@@ -800,6 +875,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         R.r[u] = *(const uint4 *)(rp + ((GK && p >= RP0) ? OFF_GV + (p - RP0) * 16 : p * 16));
       }
       R.b = beta[t0 + min(lt & 63, L - 1)];
+      if (SCALED) R.e = *(const float2 *)(rp + OFF_E);
     };
     // chunk cc (< NC) from its register set into LDS buffer cc & 1
     auto stash = [&](const Regs &R, int cc) {
@@ -816,7 +892,10 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         const int c0 = 4 * (jp >> 2) + 2 * (jp & 1), hh = 4 * ((jp >> 1) & 1);
         const bool sw = jp >= 8;
         if (p < 2048) {
-          const f16x8 x = t < L ? (GK ? __builtin_bit_cast(f16x8, R.kq[u]) : cvt8(R.kq[u])) : z8;
+          const f16x8 x = t < L ? (GK       ? __builtin_bit_cast(f16x8, R.kq[u])
+                                   : SCALED ? cvt8s(R.kq[u], p < 1024 ? R.e.x : R.e.y)
+                                            : cvt8(R.kq[u]))
+                                : z8;
           const f16x4 lo = f16x4{x[0], x[1], x[2], x[3]}, hi = f16x4{x[4], x[5], x[6], x[7]};
           f16 *base = (p < 1024 ? sm.K : sm.Q)[buf];
           *(f16x4 *)&base[kq_chunk(t, c0 + sw) + hh] = sw ? hi : lo;
@@ -827,11 +906,12 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         // row r, channels 8 q .. +7 of the tile: the operands of sub-tile q >> 1,
         // lanes r % 16 + 16 g for g = 2 (q & 1) and the next, half m & 1.  The
         // 16 lanes of one write cover rows of 8 residues mod 8 and both m parities.
+        // The values stay bf16 (exact at any scale).
         const int r = vrow(lt), q = (lt >> 4) & 3, m = r >> 4, g0 = 2 * (q & 1);
-        const f16x8 x = r < L ? cvt8(R.v) : z8;
-        f16 *vb = (f16 *)sm.V[buf][q >> 1][m >> 1];
-        *(f16x4 *)&vb[((r & 15) + 16 * g0) * 8 + 4 * (m & 1)] = f16x4{x[0], x[1], x[2], x[3]};
-        *(f16x4 *)&vb[((r & 15) + 16 * g0 + 16) * 8 + 4 * (m & 1)] = f16x4{x[4], x[5], x[6], x[7]};
+        const uint4 x = r < L ? R.v : uint4{0, 0, 0, 0};
+        unsigned *vb = (unsigned *)sm.V[buf][q >> 1][m >> 1];
+        *(uint2 *)&vb[((r & 15) + 16 * g0) * 4 + 2 * (m & 1)] = uint2{x.x, x.y};
+        *(uint2 *)&vb[((r & 15) + 16 * g0 + 16) * 4 + 2 * (m & 1)] = uint2{x.z, x.w};
       }
       uint4 *rd = (uint4 *)sm.rec[buf];
 #pragma unroll
@@ -897,7 +977,31 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     const int sn = wave;
     const int jcol = j0 + 16 * sn + c16;
     f32x4 Sacc[8];  // S^T tiles: rows i = 16 i8 + 4g + e, column jcol
-    f16x8 Sb[4];    // S^T in the paired k order
+    f16x8 Sb[4];    // S^T / ss in the paired k order
+    float ss = 1.f; // ss: a power of two >= max |S| of the wave's channels
+    // the fp16 copy of S^T for the products, divided by ss (exact scaling), into
+    // LDS for the output wave with its scale
+    auto stage_S = [&](int parity) {
+      float mx = 0.f;
+#pragma unroll
+      for (int i8 = 0; i8 < 8; ++i8)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(Sacc[i8][e]));
+      ss = pow2_above(wave_max(mx));
+      const float is = 1.0f / ss;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        f32x4 a = Sacc[2 * kk], b = Sacc[2 * kk + 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] *= is;
+          b[e] *= is;
+        }
+        Sb[kk] = cat(h4(a), h4(b));
+        sm.Sx[parity][sn][kk][lane] = Sb[kk];
+      }
+      if (lane == 0) sm.sig[parity][sn][0] = ss;
+    };
 #pragma unroll
     for (int i8 = 0; i8 < 8; ++i8) Sacc[i8] = zero4();
     if (S0) {
@@ -907,11 +1011,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         Sacc[i8] = f32x4{s4.x, s4.y, s4.z, s4.w};
       }
     }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
-      sm.Sx[0][sn][kk][lane] = Sb[kk];
-    }
+    stage_S(0);
     __syncthreads();
 
     for (int c = 0; c < NC; ++c) {
@@ -921,29 +1021,43 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       const f16x8 *TmA = (const f16x8 *)(sm.rec[cb] + OFF_TM);
       const float ds = *(const float *)(sm.rec[cb] + OFF_DS);
       // K S^T, then R = diag(beta)(V - K S^T) with the values turned into the
-      // result layout
-      f16x4 rr[4];
-      const f16x8 Vv[2] = {sm.V[cb][sn][0][lane], sm.V[cb][sn][1][lane]};
+      // result layout (exactly: bf16 through the identity), then R / sr in fp16
+      // with sr a power of two >= max |R| of the wave's channels
+      f32x4 rf[4];
+      const uint4 Vv[2] = {sm.V[cb][sn][0][lane], sm.V[cb][sn][1][lane]};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         f32x4 a = zero4();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           a = mma32(ld8(&Kc[kq_chunk(16 * m + c16, 4 * kk + g)]), Sb[kk], a);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] *= ss;
         if (SCALED) {
           const f32x4 s4 = *(const f32x4 *)(sm.rec[cb] + OFF_KF + 4 * (16 * m + 4 * g));
 #pragma unroll
           for (int e = 0; e < 4; ++e) a[e] *= s4[e];
         }
-        const f16x8 &vp = Vv[m >> 1];
-        const f16x4 vin = (m & 1) ? f16x4{vp[4], vp[5], vp[6], vp[7]} : f16x4{vp[0], vp[1], vp[2], vp[3]};
-        const f16x4 vv = h4(mma16(vin, ident, zero4()));
+        const uint4 &vp = Vv[m >> 1];
+        const bf16x4 vin = __builtin_bit_cast(bf16x4, (m & 1) ? uint2{vp.z, vp.w} : uint2{vp.x, vp.y});
+        const f32x4 vv = mma16bf(vin, identb, zero4());
         const f32x4 b4 = *(const f32x4 *)&sm.b[cb][16 * m + 4 * g];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rr[m][e] = h(b4[e] * ((float)vv[e] - a[e]));
+        for (int e = 0; e < 4; ++e) rf[m][e] = b4[e] * (vv[e] - a[e]);
       }
+      float mr = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mr = fmaxf(mr, fabsf(rf[m][e]));
+      const float sr = pow2_above(wave_max(mr)), isr = 1.0f / sr;
+      f16x4 rr[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rr[m][e] = h(rf[m][e] * isr);
       const f16x8 Rb[2] = {cat(rr[0], rr[1]), cat(rr[2], rr[3])};
-      // X = T R
+      // X / sr = T (R / sr)
       f32x4 X[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -956,8 +1070,10 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       const f16x8 Xb[2] = {cat(h4(X[0]), h4(X[1])), cat(h4(X[2]), h4(X[3]))};
       sm.Xx[cb][sn][0][lane] = Xb[0];
       sm.Xx[cb][sn][1][lane] = Xb[1];
+      if (lane == 0) sm.sig[cb][sn][1] = sr;
       const float gL = GATED ? *(const float *)(sm.rec[cb] + OFF_GL) : 1.0f;
-      // S^T <- gamma_L S^T + ds Kt^T X (GK: row i of S^T decays by g_L[i])
+      // S^T <- gamma_L S^T + ds sr Kt^T (X / sr) (GK: row i of S^T decays by g_L[i])
+      const float dsr = ds * sr;
 #pragma unroll
       for (int i8 = 0; i8 < 8; ++i8) {
         f32x4 u = zero4();
@@ -967,13 +1083,9 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         if (GK) gv = *(const f32x4 *)(sm.rec[cb] + OFF_SC + 4 * (16 * i8 + 4 * g));
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          Sacc[i8][e] = fmaf(ds, u[e], (GATED || GK) ? gv[e] * Sacc[i8][e] : Sacc[i8][e]);
+          Sacc[i8][e] = fmaf(dsr, u[e], (GATED || GK) ? gv[e] * Sacc[i8][e] : Sacc[i8][e]);
       }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
-        sm.Sx[cb ^ 1][sn][kk][lane] = Sb[kk];
-      }
+      stage_S(cb ^ 1);
       __syncthreads();
     }
     __syncthreads();  // the output waves' last iteration
@@ -1006,10 +1118,16 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         const long tok0 = (long)bh * T_ + (long)c * C;
         const int L = min(C, T_ - c * C);
         const f16x8 Xb[2] = {sm.Xx[c & 1][sn][0][lane], sm.Xx[c & 1][sn][1][lane]};
+        // X is stored divided by sr: O = sr (Q S^T / sr + P (X / sr))
+        const float sr = sm.sig[c & 1][sn][1], isr = 1.0f / sr;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
 #pragma unroll
+          for (int e = 0; e < 4; ++e) O[m][e] *= isr;
+#pragma unroll
           for (int qq = 0; qq <= (m >> 1); ++qq) O[m] = mma32(Pr[op_index(m, qq)], Xb[qq], O[m]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) O[m][e] *= sr;
           const bf16x4 ob = {(bf16)O[m][0], (bf16)O[m][1], (bf16)O[m][2], (bf16)O[m][3]};
           const f32x4 ot = mma16bf(ob, identb, zero4());
           const int t = 16 * m + c16;
@@ -1024,6 +1142,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         f16x8 Sb[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) Sb[kk] = sm.Sx[cb][sn][kk][lane];
+        const float ss = sm.sig[cb][sn][0];  // Sb holds S^T / ss
         const f16 *Qc = sm.Q[cb];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -1031,6 +1150,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
             a = mma32(ld8(&Qc[kq_chunk(16 * m + c16, 4 * kk + g)]), Sb[kk], a);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] *= ss;
           if (SCALED) {
             const f32x4 s4 = *(const f32x4 *)(sm.rec[cb] + OFF_QF + 4 * (16 * m + 4 * g));
 #pragma unroll

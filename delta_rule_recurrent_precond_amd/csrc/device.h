@@ -68,6 +68,16 @@ __device__ __forceinline__ float column_sum4(float v) {
   return __uint_as_float(h[0]) + __uint_as_float(h[1]);
 }
 
+// A power of two >= x (x >= 0 and finite; 1 for 0).  Values divided by it keep
+// their significand exactly, so it moves a vector into fp16's normal range
+// without changing how it rounds.
+__device__ __forceinline__ float pow2_above(float x) {
+  if (!(x > 0.f)) return 1.0f;
+  int e;
+  frexpf(x, &e);  // x = f 2^e with f in [0.5, 1)
+  return ldexpf(1.0f, e);
+}
+
 // Input transforms of the raw-input flags (include/osdn.h): the scale that
 // normalises a vector of squared norm n (a zero vector stays zero), and the
 // logistic sigmoid of a gate logit.

@@ -393,9 +393,9 @@ __device__ __forceinline__ void fused_body(
               }
             }
           }
-          if (MODE != kScan && ptid < 4 * C) {  // the value tile passes through Kt
+          if (MODE != kScan && ptid < 4 * C) {  // the value tile passes through Kt, in bf16
             const int t = ptid >> 2, j = (ptid & 3) * 8;
-            *(f16x8 *)&LKt[t * KP + j] = t < pL ? cvt8(pv) : z8;
+            *(uint4 *)&LKt[t * KP + j] = t < pL ? pv : uint4{0, 0, 0, 0};
           }
           if (ptid < C) {
             Lbeta[nb][ptid] = ptid < pL ? pb : 0.f;
@@ -771,7 +771,28 @@ __device__ __forceinline__ void fused_body(
     const int sn = wave - NPREP;          // 16-channel sub-tile
     const int jcol = j0 + 16 * sn + c16;  // value channel of this lane
     f32x4 Sacc[8];                        // S^T tiles: rows i = 16 i8 + 4g + e, col jcol
-    f16x8 Sb[4];                          // S^T in the paired k order (K S^T, Q S^T operand)
+    f16x8 Sb[4];                          // S^T / ss in the paired k order (K S^T, Q S^T operand)
+    float ss = 1.f;                       // a power of two >= max |S| of the wave's channels
+    // the fp16 copy of S^T, divided by ss (exact scaling: any state magnitude)
+    auto stage_S = [&]() {
+      float mx = 0.f;
+#pragma unroll
+      for (int i8 = 0; i8 < 8; ++i8)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(Sacc[i8][e]));
+      ss = pow2_above(wave_max(mx));
+      const float is = 1.0f / ss;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        f32x4 a = Sacc[2 * kk], b = Sacc[2 * kk + 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] *= is;
+          b[e] *= is;
+        }
+        Sb[kk] = cat(h4(a), h4(b));
+      }
+    };
 #pragma unroll
     for (int i8 = 0; i8 < 8; ++i8) Sacc[i8] = zero4();
     if (S0) {
@@ -781,21 +802,17 @@ __device__ __forceinline__ void fused_body(
         Sacc[i8] = f32x4{s4.x, s4.y, s4.z, s4.w};
       }
     }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
+    stage_S();
     __syncthreads();
 
     // Carried from the iteration that prepared the chunk to the one that runs
     // it: K S^T, Q S^T and the values, all in the result layout (lane: column
     // jcol, rows 16m + 4g + e).
-    f32x4 KS[4], O[4];
-    f16x4 V[4];
+    f32x4 KS[4], O[4], V[4];
     f16x8 Rb[2], Xb[2], Xs[2];
+    float sr = 1.f;  // R and X are held divided by sr, a power of two >= max |R|
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      KS[m] = O[m] = zero4();
-      V[m] = f16x4{0, 0, 0, 0};
-    }
+    for (int m = 0; m < 4; ++m) KS[m] = O[m] = V[m] = zero4();
 
     for (int it = 0; nch > 0 && it <= nch; ++it) {
       refresh_lane();
@@ -809,8 +826,9 @@ __device__ __forceinline__ void fused_body(
 
       // ------------------------------ phase 1 ------------------------------
       if (act) {
-        // R = diag(beta)(V - K S^T), in the paired k order for Tinv R
-        f16x4 rr[4];
+        // R = diag(beta)(V - K S^T), then R / sr in fp16, in the paired k order
+        // for Tinv R
+        f32x4 rf[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const float4 b4 = *(const float4 *)&Lbeta[cb][16 * m + 4 * g];
@@ -822,8 +840,20 @@ __device__ __forceinline__ void fused_body(
             for (int e = 0; e < 4; ++e) KS[m][e] *= fexp2(lv[e]);
           }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) rr[m][e] = h(bb[e] * ((float)V[m][e] - KS[m][e]));
+          for (int e = 0; e < 4; ++e) rf[m][e] = bb[e] * (V[m][e] - KS[m][e]);
         }
+        float mr = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mr = fmaxf(mr, fabsf(rf[m][e]));
+        sr = pow2_above(wave_max(mr));
+        const float isr = 1.0f / sr;
+        f16x4 rr[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rr[m][e] = h(rf[m][e] * isr);
         Rb[0] = cat(rr[0], rr[1]);
         Rb[1] = cat(rr[2], rr[3]);
       }
@@ -831,7 +861,7 @@ __device__ __forceinline__ void fused_body(
 
       // ------------------------------ phase 2 ------------------------------
       if (act) {
-        // X = Tinv R (row blocks m need t pairs 0..m/2), in the paired k order
+        // X / sr = Tinv (R / sr) (row blocks m need t pairs 0..m/2), in the paired k order
         f32x4 X[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -859,10 +889,12 @@ __device__ __forceinline__ void fused_body(
       }
       if (pact && walk_mode(MODE)) key_gram_tile(8 + sn);
       if (pact && MODE != kScan) {
-        // values of the chunk being prepared (staged row-major in Kt), transposed
+        // values of the chunk being prepared (staged row-major in Kt as bf16),
+        // transposed exactly
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          V[m] = h4(mma16(ld4(&LKt[(16 * m + c16) * KP + 16 * sn + 4 * g]), ident, zero4()));
+          V[m] = mma16bf(*(const bf16x4 *)&LKt[(16 * m + c16) * KP + 16 * sn + 4 * g], identb,
+                         zero4());
       }
       __syncthreads();
 
@@ -880,8 +912,14 @@ __device__ __forceinline__ void fused_body(
             for (int e = 0; e < 4; ++e) O[m][e] *= fexp2(lv[e]);
           }
           const f16 *row = &LP[cb][(16 * m + c16) * CP];
+          // X is held divided by sr: O = sr (Q S^T / sr + P (X / sr))
+          const float isr = 1.0f / sr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) O[m][e] *= isr;
 #pragma unroll
           for (int qq = 0; qq <= (m >> 1); ++qq) O[m] = mma32(ldpk(row, 32 * qq, g), Xb[qq], O[m]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) O[m][e] *= sr;
           const bf16x4 ob = {(bf16)O[m][0], (bf16)O[m][1], (bf16)O[m][2], (bf16)O[m][3]};
           const f32x4 ot = mma16bf(ob, identb, zero4());
           const int t = 16 * m + c16;
@@ -894,8 +932,8 @@ __device__ __forceinline__ void fused_body(
 
       // ------------------------------ phase 4 ------------------------------
       if (act) {
-        // S^T += ds Kt^T X, then the fp16 copy for the next products
-        const float ds = Ldsb[cb];
+        // S^T += ds sr Kt^T (X / sr), then the fp16 copy for the next products
+        const float ds = Ldsb[cb] * sr;
         const float gL = GATED ? fexp2(Llga[cb][C - 1]) : 1.f;  // gamma_L
 #pragma unroll
         for (int i8 = 0; i8 < 8; ++i8) {
@@ -907,8 +945,7 @@ __device__ __forceinline__ void fused_body(
           for (int e = 0; e < 4; ++e)
             Sacc[i8][e] = fmaf(ds, u[e], GATED ? gL * Sacc[i8][e] : Sacc[i8][e]);
         }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) Sb[kk] = cat(h4(Sacc[2 * kk]), h4(Sacc[2 * kk + 1]));
+        stage_S();
       }
       __syncthreads();
 
@@ -943,6 +980,8 @@ __device__ __forceinline__ void fused_body(
             const f16 *row = &src[(16 * m + c16) * KP];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) acc = mma32(ldpk(row, 32 * kk, g), Sb[kk], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] *= ss;  // Sb holds S^T / ss
             if (dist == 1) KS[m] = acc;
             else O[m] = acc;
           }

@@ -9,8 +9,12 @@ namespace osdn {
 
 // Bits of the flags the kernels take: q, k arrive unnormalised; beta, r arrive
 // as logits; (internal) the given write keys are the unnormalised keys
-// themselves; alpha holds one gate per key dimension.
-constexpr unsigned kNormQK = 2u, kGateLogits = 4u, kNormKt = 8u, kGateChannels = 16u;
+// themselves; alpha holds one gate per key dimension; (internal) the write
+// keys kt are fp32 whatever the data type (the two-phase forward keeps them
+// in its scratch at full precision: rounded to bf16 they would cost up to
+// 2^-9 relative per element, which near-orthogonal q . kt products amplify).
+constexpr unsigned kNormQK = 2u, kGateLogits = 4u, kNormKt = 8u, kGateChannels = 16u,
+                   kKtF32 = 32u;
 
 struct ScanArgs {
   const void *k;
@@ -20,7 +24,8 @@ struct ScanArgs {
   int mode_off;          // 1: plain delta rule (only the residual-ratio sums are produced)
   void *k_tilde;         // [B,H,T,dk] dtype (unused when mode_off)
   float *d_final, *d_all, *log_ratio, *log_ratio_sum;  // optional
-  unsigned xf;           // input transforms (kNormQK: k unnormalised; kGateLogits: beta, r logits)
+  unsigned xf;           // input transforms (kNormQK: k unnormalised; kGateLogits: beta, r logits);
+                         // kKtF32: k_tilde is fp32
 };
 
 struct ChunkArgs {
@@ -29,7 +34,7 @@ struct ChunkArgs {
   int B, H, T, dk, dv, chunk, dtype;
   void *o;
   float *S_final;
-  unsigned xf;  // input transforms of q, k and beta (kNormQK, kGateLogits)
+  unsigned xf;  // input transforms of q, k and beta (kNormQK, kGateLogits); kKtF32: k_tilde fp32
 };
 
 struct FusedArgs {

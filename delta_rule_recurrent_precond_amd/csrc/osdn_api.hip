@@ -12,7 +12,6 @@ namespace {
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
-size_t elem_bytes(int dtype) { return dtype == OSDN_BF16 ? 2 : 4; }
 
 // Sizes common to every entry point.
 int check_sizes(int B, int H, int T, int dk, int dv, int chunk, int dtype, bool need_dv,
@@ -35,11 +34,17 @@ bool use_fused(int dk, int dv, int chunk, int dtype) {
   return osdn::fused_supported(dk, dv, chunk, dtype);
 }
 
-// Scratch of the two-launch path (kt between the walk and the chunk pass).
+// Scratch of the two-launch path: kt between the walk and the chunk pass, in
+// fp32 whatever the data type, then (bf16 keys, dk = 128) the chunked walk's
+// records.
+size_t two_phase_kt_bytes(int B, int H, int T, int dk) {
+  const size_t n = (size_t)B * H * T * dk * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
 size_t two_phase_bytes(int B, int H, int T, int dk, int dtype, unsigned flags) {
   if (flags & OSDN_PRECOND_OFF) return 0;
-  const size_t n = (size_t)B * H * T * dk * elem_bytes(dtype);
-  return (n + 255) & ~(size_t)255;
+  return two_phase_kt_bytes(B, H, T, dk) +
+         (osdn::walk_supported(dk, dtype) ? osdn::walk_workspace_bytes(B, H, T) : 0);
 }
 
 // Scratch that selects the fastest path: the split pipeline on the shapes of
@@ -215,10 +220,13 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   const void *kt = k;
   const unsigned sxf = xf & (osdn::kNormQK | osdn::kGateLogits);  // what the walk transforms
   if (!off) {
+    // kt in fp32 (osdn::kKtF32): the chunked walk (bf16 keys, dk = 128) with
+    // its records after kt, else the token-serial walk
     osdn::ScanArgs sa{k, beta, r, d0, eta, B, H, T, dk, dtype, 0, workspace,
-                      d_final, nullptr, nullptr, log_ratio_sum, sxf};
-    st = hip_status(osdn::fused_scan_supported(dk, dtype) && !sxf
-                        ? osdn::launch_fused_scan(sa, s)
+                      d_final, nullptr, nullptr, log_ratio_sum, sxf | osdn::kKtF32};
+    st = hip_status(osdn::walk_supported(dk, dtype)
+                        ? osdn::launch_walk_scan(
+                              sa, (unsigned char *)workspace + two_phase_kt_bytes(B, H, T, dk), s)
                         : osdn::launch_precond_scan_serial(sa, s));
     if (st != OSDN_OK) return st;
     kt = workspace;
@@ -230,6 +238,6 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   }
   // with kt = k (the delta rule) unnormalised keys are normalised on both sides
   osdn::ChunkArgs ca{q, k, kt, v, beta, alpha, S0, B, H, T, dk, dv, chunk, dtype, o, S_final,
-                     xf | (off && (xf & osdn::kNormQK) ? osdn::kNormKt : 0u)};
+                     xf | (off ? ((xf & osdn::kNormQK) ? osdn::kNormKt : 0u) : osdn::kKtF32)};
   return hip_status(osdn::launch_chunk_generic(ca, s));
 }

@@ -20,11 +20,12 @@ namespace {
 
 constexpr int kBlock = 16;  // tokens per prefetch block
 
-template <typename T, int DK>
+// KT: the type of the write keys written (T, or fp32 for the two-phase forward)
+template <typename T, typename KT, int DK>
 __global__ void __launch_bounds__(64)
 precond_scan_serial(const T *__restrict__ k, const float *__restrict__ beta,
                     const float *__restrict__ r, const float *__restrict__ d0, float eta, int T_,
-                    int mode_off, T *__restrict__ k_tilde, float *__restrict__ d_final,
+                    int mode_off, KT *__restrict__ k_tilde, float *__restrict__ d_final,
                     float *__restrict__ d_all, float *__restrict__ log_ratio,
                     float *__restrict__ log_ratio_sum, unsigned xf) {
   constexpr int EPL = DK >= 64 ? DK / 64 : 1;
@@ -90,7 +91,7 @@ precond_scan_serial(const T *__restrict__ k, const float *__restrict__ beta,
       if (!mode_off && active) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          Elem<T>::store(k_tilde + row * DK + e0 + e, d[e] * kk[e]);
+          Elem<KT>::store(k_tilde + row * DK + e0 + e, d[e] * kk[e]);
           if (d_all) d_all[row * DK + e0 + e] = d[e];
         }
       }
@@ -121,13 +122,13 @@ precond_scan_serial(const T *__restrict__ k, const float *__restrict__ beta,
   if (log_ratio_sum && lane == 0) log_ratio_sum[bh] = lsum;
 }
 
-template <typename T>
+template <typename T, typename KT>
 hipError_t launch_serial_t(const ScanArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.H)), block(64);
 #define OSDN_SCAN_CASE(DK_)                                                                     \
   case DK_:                                                                                     \
-    hipLaunchKernelGGL((precond_scan_serial<T, DK_>), grid, block, 0, s, (const T *)a.k,      \
-                       a.beta, a.r, a.d0, a.eta, a.T, a.mode_off, (T *)a.k_tilde, a.d_final,  \
+    hipLaunchKernelGGL((precond_scan_serial<T, KT, DK_>), grid, block, 0, s, (const T *)a.k,  \
+                       a.beta, a.r, a.d0, a.eta, a.T, a.mode_off, (KT *)a.k_tilde, a.d_final, \
                        a.d_all, a.log_ratio, a.log_ratio_sum, a.xf);                           \
     break;
   switch (a.dk) {
@@ -146,7 +147,8 @@ hipError_t launch_serial_t(const ScanArgs &a, hipStream_t s) {
 
 hipError_t launch_precond_scan_serial(const ScanArgs &a, hipStream_t s) {
   if ((long)a.B * a.H == 0) return hipSuccess;
-  return a.dtype == 0 ? launch_serial_t<bf16>(a, s) : launch_serial_t<float>(a, s);
+  if (a.dtype != 0) return launch_serial_t<float, float>(a, s);
+  return (a.xf & kKtF32) ? launch_serial_t<bf16, float>(a, s) : launch_serial_t<bf16, bf16>(a, s);
 }
 
 }  // namespace osdn

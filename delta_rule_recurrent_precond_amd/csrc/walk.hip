@@ -75,15 +75,32 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
     pr = sigmoid_gate(pr);
   }
 
-  // stage the stored keys (exact in fp16); n_t from the stored bf16 values (16
-  // threads per token).  Unnormalised keys enter through the fp32 factor
-  // 1 / n_t on p_t (the normalised key's p is p_t / n_t), never through fp16.
+  // stage the stored keys divided by e, a power of two >= the chunk's largest
+  // |k| (exact in fp16 at any scale, and their squares stay in range); the
+  // key gram then carries 1 / e^4, put back in fp32 below.  n_t from the stored
+  // bf16 values (16 threads per token).  Unnormalised keys enter through the
+  // fp32 factor 1 / n_t on p_t (the normalised key's p is p_t / n_t).
+  float ek;
+  {
+    float mk = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const unsigned short *s8 = (const unsigned short *)&rk[u];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mk = fmaxf(mk, fabsf(bf2f(s8[e])));
+    }
+    mk = wave_max(mk);
+    if (lane == 0) Yw[0][0][wave] = mk;
+    __syncthreads();
+    ek = pow2_above(fmaxf(fmaxf(Yw[0][0][0], Yw[0][0][1]), fmaxf(Yw[0][0][2], Yw[0][0][3])));
+  }
+  const float ike = 1.0f / ek, e4 = (ek * ek) * (ek * ek);
   const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
     const bool ok = t < L;
-    *(f16x8 *)&Kh[t * KP + i0] = ok ? cvt8(rk[u]) : z8;
+    *(f16x8 *)&Kh[t * KP + i0] = ok ? cvt8s(rk[u], ike) : z8;
     const unsigned short *s = (const unsigned short *)&rk[u];
     float sq = 0.f;
 #pragma unroll
@@ -152,7 +169,7 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int s = 16 * q + j;
-      row[j] = s < t ? bl * alc[j] * fexp2(lt - lgc[j + 1]) * (ssl * ssc[j]) * row[j] : 0.f;
+      row[j] = s < t ? bl * alc[j] * fexp2(lt - lgc[j + 1]) * (ssl * ssc[j]) * (e4 * row[j]) : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
@@ -461,15 +478,20 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
 // ---------------------------------------------------------------------------
 // walk_keys: one workgroup per (b, h, chunk).  Threads 0-127 run the in-chunk
 // recurrence for one key dimension each; then all threads store kt rows with
-// 16-byte stores.
+// 16-byte stores.  KT is the type of kt (bf16, or fp32 for the two-phase
+// forward); xf: kNormQK -- kt is formed from the normalised key k_t / ||k_t||
+// (the scale from the stored values, fp32); kGateLogits -- r arrives as logits.
 // ---------------------------------------------------------------------------
+template <typename KT>
 __global__ void __launch_bounds__(256)
 walk_keys(const bf16 *__restrict__ k, const float *__restrict__ r,
-          const float *__restrict__ wout, int T_, int NC, bf16 *__restrict__ k_tilde,
-          float *__restrict__ d_all) {
+          const float *__restrict__ wout, int T_, int NC, KT *__restrict__ k_tilde,
+          float *__restrict__ d_all, unsigned xf) {
+  constexpr int KTP = 16 / sizeof(KT);  // elements of kt per 16-byte piece
+  constexpr int KTR = DK + KTP;         // padded kt row in LDS
   __shared__ __align__(16) bf16 Kb[C * KP];
-  __shared__ __align__(16) bf16 Kt[C * KP];
-  __shared__ float cs[C], rs[C];
+  __shared__ __align__(16) KT Kt[C * KTR];
+  __shared__ float cs[C], rs[C], sc[C];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
   const long tok0 = (long)bh * T_ + (long)c * C;
@@ -479,13 +501,17 @@ walk_keys(const bf16 *__restrict__ k, const float *__restrict__ r,
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
     const uint4 kv = *(const uint4 *)(k + (tok0 + min(t, L - 1)) * DK + i0);
-    *(uint4 *)&Kb[t * KP + i0] = t < L ? kv : uint4{0, 0, 0, 0};
+    const uint4 kz = t < L ? kv : uint4{0, 0, 0, 0};
+    *(uint4 *)&Kb[t * KP + i0] = kz;
+    // 1 / ||k_t|| from the 16 threads that hold row t (a zero row stays zero)
+    const float n = group_sum<16>(sqsum8(kz));
+    if ((p & 15) == 0) sc[t] = (xf & kNormQK) ? unit_scale(n) : 1.0f;
   }
   if (tid < C) {
     const int tb = min(tid, L - 1);
     const float cv = wo[DK + tid], rv = r ? r[tok0 + tb] : 1.0f;
     cs[tid] = tid < L ? cv : 0.f;
-    rs[tid] = (r && tid < L) ? rv : 1.0f;
+    rs[tid] = (r && tid < L) ? ((xf & kGateLogits) ? sigmoid_gate(rv) : rv) : 1.0f;
   }
   __syncthreads();
   if (tid < DK) {
@@ -493,22 +519,25 @@ walk_keys(const bf16 *__restrict__ k, const float *__restrict__ r,
     float d = wo[i];
     for (int t0 = 0; t0 < C; t0 += 4) {
       const float4 c4 = *(const float4 *)&cs[t0], r4 = *(const float4 *)&rs[t0];
+      const float4 s4 = *(const float4 *)&sc[t0];
       const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = t0 + e;
-        const float kv = (float)Kb[t * KP + i];
-        Kt[t * KP + i] = (bf16)(d * kv);
+        const float kv = (float)Kb[t * KP + i] * sv[e];
+        Elem<KT>::store(&Kt[t * KTR + i], d * kv);
         if (d_all && t < L) d_all[(tok0 + t) * DK + i] = d;
         d = fmaf(cv[e], kv * kv, rv[e] * d);
       }
     }
   }
   __syncthreads();
+  constexpr int PIECES = C * DK / KTP;  // 16-byte pieces of the chunk's kt
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
-    if (t < L) *(uint4 *)(k_tilde + (tok0 + t) * DK + i0) = *(const uint4 *)&Kt[t * KP + i0];
+  for (int u = 0; u < PIECES / 256; ++u) {
+    const int p = tid + 256 * u, t = p / (DK / KTP), i0 = (p % (DK / KTP)) * KTP;
+    if (t < L) *(uint4 *)(k_tilde + (tok0 + t) * DK + i0) = *(const uint4 *)&Kt[t * KTR + i0];
   }
 }
 
@@ -545,8 +574,14 @@ hipError_t launch_walk_scan(const ScanArgs &a, void *ws, hipStream_t s) {
   float *wout = (float *)(wrec + (size_t)BH * NC * WREC);
   hipError_t e = launch_walk(a, wrec, wout, s);
   if (e != hipSuccess || NC == 0) return e;
-  hipLaunchKernelGGL(walk_keys, dim3((unsigned)(BH * NC)), dim3(256), 0, s, (const bf16 *)a.k,
-                     a.r, (const float *)wout, a.T, NC, (bf16 *)a.k_tilde, a.d_all);
+  if (a.xf & kKtF32)
+    hipLaunchKernelGGL(walk_keys<float>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+                       (const bf16 *)a.k, a.r, (const float *)wout, a.T, NC, (float *)a.k_tilde,
+                       a.d_all, a.xf);
+  else
+    hipLaunchKernelGGL(walk_keys<bf16>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,
+                       (const bf16 *)a.k, a.r, (const float *)wout, a.T, NC, (bf16 *)a.k_tilde,
+                       a.d_all, a.xf);
   return hipGetLastError();
 }
 

@@ -189,7 +189,10 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  *                  that is a pipeline of launches (walk, chunk-parallel pass,
  *                  sequential state pass), and less scratch (or
  *                  NULL) selects the single fused kernel.  Other shapes need the
- *                  scratch (the walk hands kt to the chunk pass through it).
+ *                  scratch: the walk hands kt to the chunk pass through it, in
+ *                  fp32 whatever the data type (a bf16 kt would cost up to 2^-9
+ *                  relative per element before the chunk pass), followed for
+ *                  bf16 keys with dk = 128 by the chunked walk's records.
  */
 int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
                  const float *r, const float *alpha, const float *d0, const float *S0,

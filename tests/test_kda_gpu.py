@@ -7,7 +7,7 @@ implement the reading
 with the preconditioner walk unchanged.  On the matrix-core shapes
 osdn_forward runs the multi-launch pipeline given its workspace (tiles below
 the diagonal factored through block boundaries, diagonal blocks term by term)
-and the two-phase path given only the write-key buffer; on other shapes the
+and the two-phase path given less scratch than that pipeline needs; on other shapes the
 two-phase path (the vector chunk kernel applies the per-channel decays term by
 term).  osdn_step scales each column of S.  Tolerances are the gated ones:
 fp32 data o, S 1e-4 and d 1e-5; bf16 data o, S 2e-2 and d 1e-5.  Inputs come from the seeded generators;
@@ -66,9 +66,10 @@ def _check(w, inp, precond=True, S0=None, heads=None, alpha=None, q=None, norm_q
     heads = heads if heads is not None else list(range(w.B * w.H))
     dev = inp.to("cuda")
     code = 0 if w.dtype == "bf16" else 1
-    if ws == "two-phase":  # only the write-key buffer (what the two-phase path needs)
-        ws = torch.empty(w.B * w.H * w.T * w.dk * (2 if code == 0 else 4), dtype=torch.uint8,
-                         device="cuda")
+    if ws == "two-phase":  # one byte short of the split pipeline's scratch: the two-phase path
+        n = osdn.forward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, code, precond,
+                                         per_channel=True)
+        ws = torch.empty(max(n - 1, 1), dtype=torch.uint8, device="cuda")
     nbytes = (osdn.forward_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, code, precond,
                                            per_channel=True) if ws is True else ws.numel())
     _log("per-channel forward %s precond=%s heads=%d path=%s" % (
