@@ -22,7 +22,8 @@ import torch
 from . import _lib
 from ._lib import OsdnError, load  # noqa: F401
 
-__all__ = ["precond_scan", "chunk_fwd", "forward", "step", "forward_workspace_bytes", "forward_path",
+__all__ = ["precond_scan", "chunk_fwd", "forward", "forward_noalloc", "step",
+           "forward_workspace_bytes", "forward_path",
            "precond_scan_workspace_bytes", "chunk_fwd_workspace_bytes",
            "OsdnError", "load"]
 
@@ -261,4 +262,43 @@ def forward(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond
         _ptr(out.get("d_final")), _ptr(out.get("log_ratio_sum")), _ptr(workspace), ws_bytes,
         _stream(dev))
     _lib.check("osdn_forward", st)
+    return out
+
+
+def forward_noalloc(q, k, v, beta, r=None, d0=None, S0=None, eta=0.05, chunk=64, precond=True,
+                    *, alpha=None, out=None, norm_qk=False, gate_logits=False):
+    """osdn_forward_noalloc: the forward with its scratch in the library's fixed
+    device array (OSDN_NOALLOC_MAX_BYTES per GPU) instead of a workspace.  Same
+    arguments and results as forward(); with ``out`` given the call allocates
+    nothing.  Calls that overlap on one GPU race on that array."""
+    _dev(q, "q")
+    B, H, T, dk = q.shape
+    dev = q.device
+    _dev(k, "k", q.shape, q.dtype, dev)
+    _dev(v, "v", None, q.dtype, dev)
+    if v.shape[:3] != (B, H, T):
+        raise ValueError("v has shape %s, expected [%d,%d,%d,dv]" % (tuple(v.shape), B, H, T))
+    dv = v.shape[3]
+    _dev(beta, "beta", (B, H, T), torch.float32, dev)
+    _dev(r, "r", (B, H, T), torch.float32, dev)
+    chan = alpha is not None and alpha.dim() == 4
+    _dev(alpha, "alpha", (B, H, T, dk) if chan else (B, H, T), torch.float32, dev)
+    _dev(d0, "d0", (B, H, dk), torch.float32, dev)
+    _dev(S0, "S0", (B, H, dv, dk), torch.float32, dev)
+    flags = ((0 if precond else _lib.OSDN_PRECOND_OFF) | _transform_flags(norm_qk, gate_logits)
+             | (_lib.OSDN_GATE_PER_CHANNEL if chan else 0))
+    if out is None:
+        out = {
+            "o": torch.empty_like(v),
+            "S_final": torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev),
+            "d_final": (torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+                        if precond else None),
+            "log_ratio_sum": torch.empty((B, H), dtype=torch.float32, device=dev),
+        }
+    st = _lib.load().osdn_forward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(alpha), _ptr(d0), _ptr(S0),
+        float(eta), B, H, T, dk, dv, int(chunk), _dtype_code(q), flags, _ptr(out["o"]),
+        _ptr(out.get("S_final")), _ptr(out.get("d_final")), _ptr(out.get("log_ratio_sum")),
+        _stream(dev))
+    _lib.check("osdn_forward_noalloc", st)
     return out

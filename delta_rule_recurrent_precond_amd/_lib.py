@@ -20,6 +20,8 @@ OSDN_ERR_SHAPE = -2
 OSDN_ERR_UNSUPPORTED = -3
 OSDN_ERR_WORKSPACE = -4
 OSDN_ERR_HIP = -5
+OSDN_ERR_TOO_LARGE = -6
+OSDN_NOALLOC_MAX_BYTES = 64 << 20
 OSDN_BF16 = 0
 OSDN_F32 = 1
 OSDN_PRECOND_OFF = 1
@@ -43,6 +45,8 @@ SIGNATURES = {
     "osdn_forward": (I, [P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, ctypes.c_uint,
                          P, P, P, P, P, ctypes.c_size_t, P]),
     "osdn_forward_workspace_bytes": (ctypes.c_size_t, [I, I, I, I, I, I, I, ctypes.c_uint]),
+    "osdn_forward_noalloc": (I, [P, P, P, P, P, P, P, P, F, I, I, I, I, I, I, I, ctypes.c_uint,
+                                 P, P, P, P, P]),
     "osdn_status_str": (ctypes.c_char_p, [I]),
     "osdn_forward_path": (ctypes.c_char_p, [I, I, I, I, I, I, I, ctypes.c_uint,
                                             ctypes.c_size_t]),

@@ -3,10 +3,20 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/osdn.h"
 #include "launch.h"
 
 #define OSDN_EXPORT extern "C" __attribute__((visibility("default")))
+
+// Scratch of osdn_forward_noalloc: one fixed array in device memory, in place
+// of a workspace argument.  Every GPU the library runs on holds its own copy
+// for the life of the process.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): it uses the device
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = OSDN_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -29,6 +39,29 @@ int check_sizes(int B, int H, int T, int dk, int dv, int chunk, int dtype, bool 
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? OSDN_OK : OSDN_ERR_HIP; }
+
+// The device address of `scratch` on the current device, resolved with
+// hipGetSymbolAddress the first time a call runs on that device and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_addr[kMaxDevices];
+
+hipError_t scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
 
 bool use_fused(int dk, int dv, int chunk, int dtype) {
   return osdn::fused_supported(dk, dv, chunk, dtype);
@@ -90,6 +123,7 @@ OSDN_EXPORT const char *osdn_status_str(int status) {
     case OSDN_ERR_UNSUPPORTED: return "dtype, dk, dv or chunk outside the supported set";
     case OSDN_ERR_WORKSPACE: return "workspace is NULL or smaller than required";
     case OSDN_ERR_HIP: return "the HIP runtime rejected a launch";
+    case OSDN_ERR_TOO_LARGE: return "the call needs more scratch than the library's fixed array holds";
     default: return "unknown status";
   }
 }
@@ -240,4 +274,26 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
   osdn::ChunkArgs ca{q, k, kt, v, beta, alpha, S0, B, H, T, dk, dv, chunk, dtype, o, S_final,
                      xf | (off ? ((xf & osdn::kNormQK) ? osdn::kNormKt : 0u) : osdn::kKtF32)};
   return hip_status(osdn::launch_chunk_generic(ca, s));
+}
+
+OSDN_EXPORT int osdn_forward_noalloc(const void *q, const void *k, const void *v,
+                                     const float *beta, const float *r, const float *alpha,
+                                     const float *d0, const float *S0, float eta, int B, int H,
+                                     int T, int dk, int dv, int chunk, int dtype, unsigned flags,
+                                     void *o, float *S_final, float *d_final,
+                                     float *log_ratio_sum, void *stream) {
+  int st = check_sizes(B, H, T, dk, dv, chunk, dtype, true, true);
+  if (st != OSDN_OK) return st;
+  if (flags & ~kFlags) return OSDN_ERR_UNSUPPORTED;
+  // the scratch of the fastest path, as osdn_forward_workspace_bytes reports it;
+  // every byte of it is written before it is read, so nothing is cleared
+  const size_t need = ws_bytes(B, H, T, dk, dv, chunk, dtype, flags);
+  if (need > kScratchBytes) return OSDN_ERR_TOO_LARGE;
+  void *ws = nullptr;
+  if (need > 0 && (long long)B * H > 0 && T > 0) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return OSDN_ERR_HIP;
+  }
+  return osdn_forward(q, k, v, beta, r, alpha, d0, S0, eta, B, H, T, dk, dv, chunk, dtype, flags,
+                      o, S_final, d_final, log_ratio_sum, ws, ws ? need : 0, stream);
 }

@@ -73,6 +73,10 @@ extern "C" {
 #define OSDN_ERR_UNSUPPORTED (-3) /* dtype, dk, dv or chunk outside the supported set */
 #define OSDN_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than required */
 #define OSDN_ERR_HIP (-5)         /* the HIP runtime rejected a launch */
+#define OSDN_ERR_TOO_LARGE (-6)   /* osdn_forward_noalloc: more scratch than its fixed array holds */
+
+/* Size in bytes of osdn_forward_noalloc's fixed scratch array (one per GPU). */
+#define OSDN_NOALLOC_MAX_BYTES ((size_t)64 << 20)
 
 #define OSDN_BF16 0
 #define OSDN_F32 1
@@ -224,6 +228,27 @@ int osdn_forward(const void *q, const void *k, const void *v, const float *beta,
 int osdn_step(const void *q, const void *k, const void *v, const float *beta, const float *r,
               const float *alpha, float eta, int B, int H, int dk, int dv, int dtype,
               unsigned flags, float *S, float *d, void *o, float *log_ratio, void *stream);
+
+/*
+ * osdn_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, kernels and results as osdn_forward given the workspace of
+ * osdn_forward_workspace_bytes, but the scratch is a fixed array of
+ * OSDN_NOALLOC_MAX_BYTES (64 MiB) that the library keeps in
+ * device memory, one per GPU, for the life of the process: nothing is
+ * allocated, freed or cleared on the call.  A call needing more (more than
+ * about 2,000 (b, h, 64-token chunk) triples on the split pipeline, e.g. 16
+ * heads x 8,000 tokens) returns OSDN_ERR_TOO_LARGE before anything is
+ * enqueued.  The first call on a device resolves the array's address there
+ * (hipGetSymbolAddress); the stream must belong to the current device.  Every
+ * call on one GPU uses the same array: calls that overlap on that GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ */
+int osdn_forward_noalloc(const void *q, const void *k, const void *v, const float *beta,
+                         const float *r, const float *alpha, const float *d0, const float *S0,
+                         float eta, int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                         unsigned flags, void *o, float *S_final, float *d_final,
+                         float *log_ratio_sum, void *stream);
 
 /* Scratch bytes that select osdn_forward's fastest path for these arguments
  * (required on the two-phase path, optional on the matrix-core shapes);

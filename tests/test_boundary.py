@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         s = lib.osdn_status_str(code).decode()
         assert s and s != "unknown status"
     assert lib.osdn_status_str(12345).decode() == "unknown status"
@@ -203,3 +203,17 @@ def test_per_channel_gate_flag(lib):
     assert _fwd(lib, B=1, H=1, T=64, dk=128, dv=128, chunk=64, flags=PC) == _lib.OSDN_ERR_NULL
     assert lib.osdn_step(1, 1, 1, 1, None, None, 0.1, 1, 1, 16, 16, 0, PC, 1, 1, 1, None,
                          None) == _lib.OSDN_ERR_NULL
+
+
+def test_noalloc_rejects_calls_beyond_its_fixed_scratch(lib):
+    """osdn_forward_noalloc refuses, before touching the HIP runtime, a call whose
+    scratch would exceed OSDN_NOALLOC_MAX_BYTES (dummy pointers: never dereferenced)."""
+    p = 1
+    need = lib.osdn_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 0, 0)
+    assert need > _lib.OSDN_NOALLOC_MAX_BYTES
+    st = lib.osdn_forward_noalloc(p, p, p, p, None, None, None, None, 0.05, 4, 16, 4096, 128, 128,
+                                  64, 0, 0, p, None, None, None, None)
+    assert st == _lib.OSDN_ERR_TOO_LARGE
+    # argument checks come first, as on every entry point
+    assert lib.osdn_forward_noalloc(p, p, p, p, None, None, None, None, 0.05, 1, 1, 64, 48, 128,
+                                    64, 0, 0, p, None, None, None, None) == _lib.OSDN_ERR_UNSUPPORTED
