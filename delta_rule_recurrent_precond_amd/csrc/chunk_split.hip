@@ -156,7 +156,11 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+  // chunk-major, last chunk first, heads innermost: the state kernel reads every
+  // head's chunk 0 first, which is then the freshest data in the caches; with
+  // B*H a multiple of 8 a head runs on the XCD its state-kernel tiles use
+  const int BHn = gridDim.x / NC;
+  const int c = NC - 1 - (int)(blockIdx.x / BHn), bh = blockIdx.x % BHn;
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
   unsigned char *rec = ws + ((long)bh * NC + c) * (GK ? RECK : REC);

@@ -55,7 +55,10 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+  // chunk-major, last chunk first, heads innermost (as chunk_prep): the walk
+  // reads every head's chunk 0 first
+  const int BHn = gridDim.x / NC;
+  const int c = NC - 1 - (int)(blockIdx.x / BHn), bh = blockIdx.x % BHn;
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
 
