@@ -254,7 +254,8 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 // ---------------------------------------------------------------------------
 constexpr int PS = 144;  // row (floats) of p in LDS: 16 dwords past a multiple of 64
                          // spreads the 16-byte reads of phase A over all banks
-constexpr int WT = 512;  // threads
+constexpr int WT = 768;  // threads: the chain (waves 0-3), the loaders (waves 4-11)
+constexpr int NLD = WT - 256;  // loader lanes
 // Column of key dimension i in a row of p: 16-byte halves of each 32-byte piece
 // swapped in the pieces whose index has bit 2 set.  The loaders then store the
 // first half of every piece with one instruction and the 8 lanes of each LDS
@@ -282,75 +283,85 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
 
   if (tid >= 256) {
     // ================================ loaders ================================
-    // a chunk: 1024 pieces of 8 keys (4 per lane) and the record as 1089
-    // pieces of 16 bytes (1024 of the inverse, 64 of vectors, Gamma_L)
+    // a chunk: 1024 pieces of 8 keys (2 per lane) and the record as 705
+    // pieces of 16 bytes: the inverse's ten 16x16 blocks on and below the
+    // diagonal (piece q: block q >> 6, row (q >> 2) & 15, columns 4 (q & 3)
+    // .. +3), then 64 of the vectors and Gamma_L.  The blocks above the
+    // diagonal are zero in both LDS buffers from the start and never written.
     const int lt = tid - 256;
-    constexpr int RP = (W_GL + 16) / 16;
-    constexpr int NRP = (RP + 255) / 256;
+    constexpr int NMI = 640, RP = NMI + 65;
+    constexpr int NRP = (RP + NLD - 1) / NLD;
     struct Regs {
-      uint4 k[4], rr[NRP];
+      uint4 k[2], rr[NRP];
     };
     Regs ra, rb, rc, rd;
+    // byte offset in the record of piece q (< RP)
+    auto rec_off = [&](int q) {
+      if (q >= NMI) return (int)W_U + 16 * (q - NMI);  // the vectors, then Gamma_L
+      int bi, bj;
+      tri_tile(q >> 6, bi, bj);
+      return (int)W_MINV + 4 * ((16 * bi + ((q >> 2) & 15)) * C + 16 * bj + 4 * (q & 3));
+    };
     // chunk cc clamped to the last one: loads past it reread it
     auto load = [&](Regs &R, int cc) {
       cc = min(cc, NC - 1);
       const bf16 *kc = k + ((long)bh * T_ + (long)cc * C) * DK;  // uniform base, 32-bit offsets
       const int L = min(C, T_ - cc * C);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int p = lt + 256 * u, tt = min(p >> 4, L - 1);
+      for (int u = 0; u < 2; ++u) {
+        const int p = lt + NLD * u, tt = min(p >> 4, L - 1);
         R.k[u] = *(const uint4 *)(kc + tt * DK + (p & 15) * 8);
       }
-      const uint4 *rs = (const uint4 *)(wrec + ((long)bh * NC + cc) * WREC);
+      const unsigned char *rs = wrec + ((long)bh * NC + cc) * WREC;
 #pragma unroll
-      for (int u = 0; u < NRP; ++u) R.rr[u] = rs[min(lt + 256 * u, RP - 1)];
+      for (int u = 0; u < NRP; ++u) R.rr[u] = *(const uint4 *)(rs + rec_off(min(lt + NLD * u, RP - 1)));
     };
     // the record of chunk cc into LDS buffer cc & 1
     auto stash_rec = [&](const Regs &R, int cc) {
       const int buf = cc & 1;
 #pragma unroll
       for (int u = 0; u < NRP; ++u) {
-        const int p = lt + 256 * u;
-        if (p < C * C / 4) {
-          *(uint4 *)&sm.Mi[buf][(p >> 4) * FP + (p & 15) * 4] = R.rr[u];
-        } else if (p < RP - 1) {
-          const int v = p - C * C / 4;  // 16 pieces per vector
+        const int q = lt + NLD * u;
+        if (q < NMI) {
+          int bi, bj;
+          tri_tile(q >> 6, bi, bj);
+          *(uint4 *)&sm.Mi[buf][(16 * bi + ((q >> 2) & 15)) * FP + 16 * bj + 4 * (q & 3)] = R.rr[u];
+        } else if (q < RP - 1) {
+          const int v = q - NMI;  // 16 pieces per vector
           *(uint4 *)&sm.vec[buf][v >> 4][(v & 15) * 4] = R.rr[u];
-        } else if (p == RP - 1) {
+        } else if (q == RP - 1) {
           *(uint4 *)&sm.gL[buf][0] = R.rr[u];
         }
       }
     };
-    // pieces u0, u0 + 1 of the keys of chunk cc, squared, into LDS buffer
-    // cc & 1 (rows past the end zero), in the p_slot layout
-    auto stash_p = [&](const Regs &R, int cc, int u0) {
+    // piece u of the keys of chunk cc (tokens 32 u .. +31), squared, into LDS
+    // buffer cc & 1 (rows past the end zero), in the p_slot layout
+    auto stash_p = [&](const Regs &R, int cc, int u) {
       const int buf = cc & 1, L = min(C, T_ - cc * C);
+      const int p = lt + NLD * u, tt = p >> 4, i0 = (p & 15) * 8;
+      const unsigned short *s = (const unsigned short *)&R.k[u];
+      float x[8];
 #pragma unroll
-      for (int u = u0; u < u0 + 2; ++u) {
-        const int p = lt + 256 * u, tt = p >> 4, i0 = (p & 15) * 8;
-        const unsigned short *s = (const unsigned short *)&R.k[u];
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float y = bf2f(s[e]);
-          x[e] = y * y;
-        }
-        if (L < C && tt >= L) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.f;
-        }
-        float *row = &sm.P[buf][tt * PS];
-        *(float4 *)(row + p_slot(i0)) = float4{x[0], x[1], x[2], x[3]};
-        *(float4 *)(row + p_slot(i0 + 4)) = float4{x[4], x[5], x[6], x[7]};
+      for (int e = 0; e < 8; ++e) {
+        const float y = bf2f(s[e]);
+        x[e] = y * y;
       }
+      if (L < C && tt >= L) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+      float *row = &sm.P[buf][tt * PS];
+      *(float4 *)(row + p_slot(i0)) = float4{x[0], x[1], x[2], x[3]};
+      *(float4 *)(row + p_slot(i0 + 4)) = float4{x[4], x[5], x[6], x[7]};
     };
     float lr_acc = 0.f;  // sum of log rho_t (wave 4)
-    // log rho_t = log g_t^2 of chunk c (g from phase B), wave 4
+    // log rho_t = log g_t^2 of chunk c (g from phase B), wave 4; the hardware
+    // logarithm (about one ulp of log2)
     auto log_rho = [&](int c) {
       const int L = min(C, T_ - c * C);
       if (lt < C && lt < L) {
         const float gt = sm.g[lt];
-        const float lr = logf(gt * gt);
+        const float lr = __logf(gt * gt);
         lr_acc += lr;
         if (log_ratio) log_ratio[(long)bh * T_ + (long)c * C + lt] = lr;
       }
@@ -365,12 +376,19 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
         stash_p(next, c + 1, 0);
       }
       __syncthreads();
-      if (c + 1 < NC) stash_p(next, c + 1, 2);
+      if (c + 1 < NC) stash_p(next, c + 1, 1);
       __syncthreads();
       log_rho(c);
       load(free_, c + 4);
       __syncthreads();
     };
+    // zeros into the six blocks above the diagonal of both buffers (768 pieces)
+    for (int i = lt; i < 2 * 6 * 64; i += NLD) {
+      int bi, bj;
+      off_tile((i >> 6) % 6, bj, bi);  // (bj, bi) below the diagonal: (bi, bj) above it
+      *(float4 *)&sm.Mi[i / 384][(16 * bi + ((i >> 2) & 15)) * FP + 16 * bj + 4 * (i & 3)] =
+          float4{0.f, 0.f, 0.f, 0.f};
+    }
     if (NC > 0) {
       load(ra, 0);
       load(rb, 1);
@@ -378,7 +396,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
       load(rd, 3);
       stash_rec(ra, 0);
       stash_p(ra, 0, 0);
-      stash_p(ra, 0, 2);
+      stash_p(ra, 0, 1);
     }
     __syncthreads();
     for (int c = 0; c < NC; c += 4) {
@@ -395,6 +413,11 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
   }
 
   // ================================= chain ==================================
+  // The operands from the chunk's LDS buffers (p, the inverse, the per-token
+  // factors) are read into registers ahead of their phase, right after an
+  // earlier phase's own reads (B's and C's in phase A, the next chunk's A in
+  // phase C): a phase then waits only for the vector it contracts with (d, rhs
+  // or w), which the previous phase wrote.
   const int t = tid >> 2, part = tid & 3;       // phases A and B
   const int wv = tid >> 6, l = tid & 63;
   const int dim = 32 * wv + (l & 31), half = l >> 5;  // phase C
@@ -404,45 +427,87 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
     if (NC > 0) wout[(long)bh * NC * WOUT + dim] = dreg;
     sm.d[dim] = dreg;
   }
+  float pa[32];    // A: p_t at dimensions 4 (part + 4 j) .. +3
+  float mr[16];    // B: row t of (I + M)^-1, columns 16 part .. +15
+  float pcol[32];  // C: p of tokens 8 j + 4 half + e at dimension dim
+  float ut = 0.f, sta = 0.f;            // A: u_t, s_t
+  float wa = 0.f, stb = 0.f, at = 0.f;  // B: R_{L,t} alpha_t, s_t, alpha_t
+  float gl = 0.f;                       // C: Gamma_L
+  auto read_a = [&](int cb) {
+    const float *pr = &sm.P[cb][t * PS];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 p4 = *(const float4 *)(pr + p_slot(4 * (part + 4 * j)));
+      pa[4 * j] = p4.x, pa[4 * j + 1] = p4.y, pa[4 * j + 2] = p4.z, pa[4 * j + 3] = p4.w;
+    }
+    ut = sm.vec[cb][0][t];
+    sta = sm.vec[cb][3][t];
+  };
+  auto read_b = [&](int cb) {
+    const float *mrow = &sm.Mi[cb][t * FP + 16 * part];
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      const float4 m4 = *(const float4 *)(mrow + j);
+      mr[j] = m4.x, mr[j + 1] = m4.y, mr[j + 2] = m4.z, mr[j + 3] = m4.w;
+    }
+    wa = sm.vec[cb][2][t];
+    stb = sm.vec[cb][3][t];
+    at = sm.vec[cb][1][t];
+  };
+  auto read_c = [&](int cb) {
+    const float *pc = &sm.P[cb][p_slot(dim)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pcol[4 * j + e] = pc[(8 * j + 4 * half + e) * PS];
+    gl = sm.gL[cb][0];
+  };
   __syncthreads();
+  if (NC > 0) read_a(0);
 
   for (int c = 0; c < NC; ++c) {
     const int cb = c & 1;
     // A
     {
-      const float ut = sm.vec[cb][0][t], st = sm.vec[cb][3][t];
-      const float *pr = &sm.P[cb][t * PS];
-      float b0 = 0.f, b1 = 0.f;
+      float4 dv[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i0 = 4 * (part + 4 * j);
-        const float4 p4 = *(const float4 *)(pr + p_slot(i0)), d4 = *(const float4 *)&sm.d[i0];
-        b0 = fmaf(d4.x, p4.x, b0);
-        b1 = fmaf(d4.y, p4.y, b1);
-        b0 = fmaf(d4.z, p4.z, b0);
-        b1 = fmaf(d4.w, p4.w, b1);
+      for (int j = 0; j < 8; ++j) dv[j] = *(const float4 *)&sm.d[4 * (part + 4 * j)];
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(cb);
+      read_c(cb);
+      __builtin_amdgcn_sched_barrier(0);
+      float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        b0 = fmaf(dv[j].x, pa[4 * j], b0);
+        b1 = fmaf(dv[j].y, pa[4 * j + 1], b1);
+        b2 = fmaf(dv[j].z, pa[4 * j + 2], b2);
+        b3 = fmaf(dv[j].w, pa[4 * j + 3], b3);
+        b0 = fmaf(dv[j + 1].x, pa[4 * j + 4], b0);
+        b1 = fmaf(dv[j + 1].y, pa[4 * j + 5], b1);
+        b2 = fmaf(dv[j + 1].z, pa[4 * j + 6], b2);
+        b3 = fmaf(dv[j + 1].w, pa[4 * j + 7], b3);
       }
-      const float b = group_sum<4>(b0 + b1);
-      if (part == 0) sm.rhs[t] = 1.0f - ut * (st * b);
+      const float b = group_sum<4>((b0 + b1) + (b2 + b3));
+      if (part == 0) sm.rhs[t] = 1.0f - ut * (sta * b);
     }
     __syncthreads();
     // B
     {
-      const float wa = sm.vec[cb][2][t], st = sm.vec[cb][3][t], at = sm.vec[cb][1][t];
-      const float *mrow = &sm.Mi[cb][t * FP + 16 * part];
-      const float *rv = &sm.rhs[16 * part];
-      float ga = 0.f, gb = 0.f;
+      float4 rv[4];
 #pragma unroll
-      for (int j = 0; j < 16; j += 4) {
-        const float4 m4 = *(const float4 *)(mrow + j), r4 = *(const float4 *)(rv + j);
-        ga = fmaf(m4.x, r4.x, ga);
-        gb = fmaf(m4.y, r4.y, gb);
-        ga = fmaf(m4.z, r4.z, ga);
-        gb = fmaf(m4.w, r4.w, gb);
+      for (int j = 0; j < 4; ++j) rv[j] = *(const float4 *)&sm.rhs[16 * part + 4 * j];
+      float ga = 0.f, gb = 0.f, gc = 0.f, gd = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ga = fmaf(mr[4 * j], rv[j].x, ga);
+        gb = fmaf(mr[4 * j + 1], rv[j].y, gb);
+        gc = fmaf(mr[4 * j + 2], rv[j].z, gc);
+        gd = fmaf(mr[4 * j + 3], rv[j].w, gd);
       }
-      const float gt = group_sum<4>(ga + gb);
+      const float gt = group_sum<4>((ga + gb) + (gc + gd));
       if (part == 0) {
-        sm.w[t] = wa * gt * st;
+        sm.w[t] = wa * gt * stb;
         sm.g[t] = gt;
         wout[((long)bh * NC + c) * WOUT + DK + t] = at * gt;
       }
@@ -450,19 +515,21 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
     __syncthreads();
     // C: tokens 8 j + 4 half + e of dimension dim
     {
-      const float *pc = &sm.P[cb][p_slot(dim)];
-      const float gl = sm.gL[cb][0];
-      float a0 = 0.f, a1 = 0.f;
+      float4 wv4[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wv4[j] = *(const float4 *)&sm.w[8 * j + 4 * half];
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(cb ^ 1);  // past the last chunk: a stale buffer, never used
+      __builtin_amdgcn_sched_barrier(0);
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int s0 = 8 * j + 4 * half;
-        const float4 w4 = *(const float4 *)&sm.w[s0];
-        a0 = fmaf(w4.x, pc[s0 * PS], a0);
-        a1 = fmaf(w4.y, pc[(s0 + 1) * PS], a1);
-        a0 = fmaf(w4.z, pc[(s0 + 2) * PS], a0);
-        a1 = fmaf(w4.w, pc[(s0 + 3) * PS], a1);
+        a0 = fmaf(wv4[j].x, pcol[4 * j], a0);
+        a1 = fmaf(wv4[j].y, pcol[4 * j + 1], a1);
+        a2 = fmaf(wv4[j].z, pcol[4 * j + 2], a2);
+        a3 = fmaf(wv4[j].w, pcol[4 * j + 3], a3);
       }
-      const float a = a0 + a1;
+      const float a = (a0 + a1) + (a2 + a3);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a),
                                                        false, false);
       const float sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
