@@ -239,18 +239,18 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 }
 
 // ---------------------------------------------------------------------------
-// walk: one workgroup of 8 waves per (b, h), sequential over the chunks from
+// walk: one workgroup of 12 waves per (b, h), sequential over the chunks from
 // the entry d0 (ones if none is given), three barriers per chunk.  Waves 0-3
 // run the chain, reading p_t = k_t (.) k_t in fp32 from LDS:
 //   A  b_t = <d, p_t> (4 threads per token), rhs_t = 1 - u_t s_t b_t
 //   B  g = (I + M)^-1 rhs (4 threads per token); c_t, w_t = R_{L,t} alpha_t s_t g_t
 //   C  d <- Gamma_L d + sum_t w_t p_t: wave v takes dimensions 32 v .. +31, its
 //      two lane halves one half of the tokens each, joined by a lane-half swap;
-//      lane l < 32 keeps d of its dimension in a register
-// Waves 4-7 keep the chain fed: they load the keys and the record four
+//      lane l < 32 keeps d of its dimension in a register; then log rho_t
+// Waves 4-11 keep the chain fed: they load the keys and the record four
 // chunks ahead (four register sets: a load has over two iterations to
-// arrive), square the keys into p (fp32) as they store them, and compute
-// log rho_t, so that none of this sits on the chain.
+// arrive) and square the keys into p (fp32) as they store them, so that none
+// of this sits on the chain.
 // ---------------------------------------------------------------------------
 constexpr int PS = 144;  // row (floats) of p in LDS: 16 dwords past a multiple of 64
                          // spreads the 16-byte reads of phase A over all banks
@@ -267,6 +267,7 @@ struct alignas(16) WalkSmem {
   float Mi[2][C * FP];       // (I + M)^-1
   float vec[2][4][C];        // u = beta Gamma, alpha, R_{L,t} alpha, the 1/||k||^2 factor
   float gL[2][4];            // Gamma_L
+  float pad[4];              // where loader lanes without a record piece store
   float d[DK];               // entry d of the chunk in the pass
   float rhs[C], w[C], g[C];
 };
@@ -295,12 +296,25 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
       uint4 k[2], rr[NRP];
     };
     Regs ra, rb, rc, rd;
-    // byte offset in the record of piece q (< RP)
+    // Piece q's byte offsets in the record and in the WalkSmem of buffer buf
+    // (the pad past the last piece).  Arithmetic only: the loaders take no
+    // divergent branch, whose two paths would leave the loads in flight
+    // differently and make the waits after them drain every load.
     auto rec_off = [&](int q) {
-      if (q >= NMI) return (int)W_U + 16 * (q - NMI);  // the vectors, then Gamma_L
       int bi, bj;
-      tri_tile(q >> 6, bi, bj);
-      return (int)W_MINV + 4 * ((16 * bi + ((q >> 2) & 15)) * C + 16 * bj + 4 * (q & 3));
+      tri_tile(min(q >> 6, 9), bi, bj);
+      const int mi = (int)W_MINV + 4 * ((16 * bi + ((q >> 2) & 15)) * C + 16 * bj + 4 * (q & 3));
+      return q < NMI ? mi : (int)W_U + 16 * (q - NMI);  // the vectors, then Gamma_L
+    };
+    auto lds_off = [&](int q, int buf) {
+      int bi, bj;
+      tri_tile(min(q >> 6, 9), bi, bj);
+      const int v = q - NMI;  // 16 pieces per vector
+      const int mi = (int)offsetof(WalkSmem, Mi) +
+                     4 * (buf * C * FP + (16 * bi + ((q >> 2) & 15)) * FP + 16 * bj + 4 * (q & 3));
+      const int ve = (int)offsetof(WalkSmem, vec) + 4 * (buf * 4 * C + (v >> 4) * C + (v & 15) * 4);
+      const int gv = (int)offsetof(WalkSmem, gL) + 16 * buf;
+      return q < NMI ? mi : q < RP - 1 ? ve : q == RP - 1 ? gv : (int)offsetof(WalkSmem, pad);
     };
     // chunk cc clamped to the last one: loads past it reread it
     auto load = [&](Regs &R, int cc) {
@@ -320,19 +334,8 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
     auto stash_rec = [&](const Regs &R, int cc) {
       const int buf = cc & 1;
 #pragma unroll
-      for (int u = 0; u < NRP; ++u) {
-        const int q = lt + NLD * u;
-        if (q < NMI) {
-          int bi, bj;
-          tri_tile(q >> 6, bi, bj);
-          *(uint4 *)&sm.Mi[buf][(16 * bi + ((q >> 2) & 15)) * FP + 16 * bj + 4 * (q & 3)] = R.rr[u];
-        } else if (q < RP - 1) {
-          const int v = q - NMI;  // 16 pieces per vector
-          *(uint4 *)&sm.vec[buf][v >> 4][(v & 15) * 4] = R.rr[u];
-        } else if (q == RP - 1) {
-          *(uint4 *)&sm.gL[buf][0] = R.rr[u];
-        }
-      }
+      for (int u = 0; u < NRP; ++u)
+        *(uint4 *)(smem_raw + lds_off(lt + NLD * u, buf)) = R.rr[u];
     };
     // piece u of the keys of chunk cc (tokens 32 u .. +31), squared, into LDS
     // buffer cc & 1 (rows past the end zero), in the p_slot layout
@@ -344,41 +347,29 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float y = bf2f(s[e]);
-        x[e] = y * y;
-      }
-      if (L < C && tt >= L) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        x[e] = tt < L ? y * y : 0.f;
       }
       float *row = &sm.P[buf][tt * PS];
       *(float4 *)(row + p_slot(i0)) = float4{x[0], x[1], x[2], x[3]};
       *(float4 *)(row + p_slot(i0 + 4)) = float4{x[4], x[5], x[6], x[7]};
     };
-    float lr_acc = 0.f;  // sum of log rho_t (wave 4)
-    // log rho_t = log g_t^2 of chunk c (g from phase B), wave 4; the hardware
-    // logarithm (about one ulp of log2)
-    auto log_rho = [&](int c) {
-      const int L = min(C, T_ - c * C);
-      if (lt < C && lt < L) {
-        const float gt = sm.g[lt];
-        const float lr = __logf(gt * gt);
-        lr_acc += lr;
-        if (log_ratio) log_ratio[(long)bh * T_ + (long)c * C + lt] = lr;
-      }
-    };
     // one iteration, its work spread so that no window outlasts the chain's
     // phase: the record of chunk c+1 and half its keys (window A), the other
-    // half (window B), log rho of chunk c and the loads of chunk c+4 into the
-    // set that held chunk c (window C)
+    // half (window B), the loads of chunk c+4 into the set that held chunk c
+    // (window C).  The loaders store nothing to global memory: a store would
+    // share the load counter, whose waits then could no longer count the
+    // loads in flight and would drain them.
+    // (Unconditional: past the last chunk the stores put the last chunk's
+    // reread record and zero keys into a buffer that only the chain's idle
+    // iterations read.  A conditional iteration would leave the loads in
+    // flight differently on its two paths, and the waits after them would
+    // then drain every load.)
     auto iteration = [&](int c, Regs &free_, const Regs &next) {
-      if (c + 1 < NC) {
-        stash_rec(next, c + 1);
-        stash_p(next, c + 1, 0);
-      }
+      stash_rec(next, c + 1);
+      stash_p(next, c + 1, 0);
       __syncthreads();
-      if (c + 1 < NC) stash_p(next, c + 1, 1);
+      stash_p(next, c + 1, 1);
       __syncthreads();
-      log_rho(c);
       load(free_, c + 4);
       __syncthreads();
     };
@@ -401,13 +392,9 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
     __syncthreads();
     for (int c = 0; c < NC; c += 4) {
       iteration(c, ra, rb);
-      if (c + 1 < NC) iteration(c + 1, rb, rc);
-      if (c + 2 < NC) iteration(c + 2, rc, rd);
-      if (c + 3 < NC) iteration(c + 3, rd, ra);
-    }
-    if (log_ratio_sum && lt < 64) {
-      const float s = wave_sum(lr_acc);
-      if (lt == 0) log_ratio_sum[bh] = s;
+      iteration(c + 1, rb, rc);
+      iteration(c + 2, rc, rd);
+      iteration(c + 3, rd, ra);
     }
     return;
   }
@@ -415,9 +402,10 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
   // ================================= chain ==================================
   // The operands from the chunk's LDS buffers (p, the inverse, the per-token
   // factors) are read into registers ahead of their phase, right after an
-  // earlier phase's own reads (B's and C's in phase A, the next chunk's A in
-  // phase C): a phase then waits only for the vector it contracts with (d, rhs
-  // or w), which the previous phase wrote.
+  // earlier phase's own reads (B's and C's in phase A, which has time to
+  // spare while the loaders store, the next chunk's A in phase C): a phase
+  // then waits only for the vector it contracts with (d, rhs or w), which the
+  // previous phase wrote.
   const int t = tid >> 2, part = tid & 3;       // phases A and B
   const int wv = tid >> 6, l = tid & 63;
   const int dim = 32 * wv + (l & 31), half = l >> 5;  // phase C
@@ -433,6 +421,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
   float ut = 0.f, sta = 0.f;            // A: u_t, s_t
   float wa = 0.f, stb = 0.f, at = 0.f;  // B: R_{L,t} alpha_t, s_t, alpha_t
   float gl = 0.f;                       // C: Gamma_L
+  float lr_acc = 0.f;  // wave 0: sum of log rho_t over token tid
   auto read_a = [&](int cb) {
     const float *pr = &sm.P[cb][t * PS];
 #pragma unroll
@@ -454,10 +443,11 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
     stb = sm.vec[cb][3][t];
     at = sm.vec[cb][1][t];
   };
-  auto read_c = [&](int cb) {
+  // tokens 8 j + 4 half + e of C's operand for j in [j0, j0 + 4)
+  auto read_c = [&](int cb, int j0) {
     const float *pc = &sm.P[cb][p_slot(dim)];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = j0; j < j0 + 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) pcol[4 * j + e] = pc[(8 * j + 4 * half + e) * PS];
     gl = sm.gL[cb][0];
@@ -465,7 +455,10 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
   __syncthreads();
   if (NC > 0) read_a(0);
 
-  for (int c = 0; c < NC; ++c) {
+  // whole groups of four chunks, as the loaders run; past the last chunk an
+  // iteration changes no d and stores nothing
+  const int NC4 = (NC + 3) & ~3;
+  for (int c = 0; c < NC4; ++c) {
     const int cb = c & 1;
     // A
     {
@@ -474,7 +467,8 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
       for (int j = 0; j < 8; ++j) dv[j] = *(const float4 *)&sm.d[4 * (part + 4 * j)];
       __builtin_amdgcn_sched_barrier(0);
       read_b(cb);
-      read_c(cb);
+      read_c(cb, 0);
+      read_c(cb, 4);
       __builtin_amdgcn_sched_barrier(0);
       float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
 #pragma unroll
@@ -509,7 +503,7 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
       if (part == 0) {
         sm.w[t] = wa * gt * stb;
         sm.g[t] = gt;
-        wout[((long)bh * NC + c) * WOUT + DK + t] = at * gt;
+        if (c < NC) wout[((long)bh * NC + c) * WOUT + DK + t] = at * gt;
       }
     }
     __syncthreads();
@@ -533,13 +527,25 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a),
                                                        false, false);
       const float sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      if (half == 0) {
+      if (half == 0 && c < NC) {
         dreg = fmaf(gl, dreg, sum);
         sm.d[dim] = dreg;
         if (c + 1 < NC) wout[((long)bh * NC + c + 1) * WOUT + dim] = dreg;  // next entry d
       }
+      // log rho_t = log g_t^2 of the chunk (g from phase B), wave 0; the
+      // hardware logarithm (about one ulp of log2)
+      if (tid < C && tid < min(C, T_ - c * C)) {
+        const float gt = sm.g[tid];
+        const float lr = __logf(gt * gt);
+        lr_acc += lr;
+        if (log_ratio) log_ratio[(long)bh * T_ + (long)c * C + tid] = lr;
+      }
     }
     __syncthreads();
+  }
+  if (log_ratio_sum && tid < 64) {
+    const float s = wave_sum(lr_acc);
+    if (tid == 0) log_ratio_sum[bh] = s;
   }
 
   if (d_final && half == 0) d_final[(long)bh * DK + dim] = dreg;
