@@ -847,7 +847,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     constexpr int RECP = GK ? RP0 + 32 : SCALED ? (int)(OFF_END / 16) : RP0;
     static_assert(RP0 * 16 == (int)OFF_SC, "g_L lands in the factor slot");
     constexpr size_t RB = GK ? RECK : REC;
-    constexpr int NKQ = (2048 + NL - 1) / NL, NR = (RECP + NL - 1) / NL;
+    constexpr int NKQ = 2048 / NL, NR = (RECP + NL - 1) / NL;
+    static_assert(NKQ * NL == 2048, "every lane stages whole pieces of k and q");
     const int lt = tid - 256;
     struct Regs {
       uint4 kq[NKQ], v, r[NR];
@@ -895,17 +896,19 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         const int p = lt + NL * u, pp = p & 1023, t = pp >> 4, jp = pp & 15;
         const int c0 = 4 * (jp >> 2) + 2 * (jp & 1), hh = 4 * ((jp >> 1) & 1);
         const bool sw = jp >= 8;
-        if (p < 2048) {
-          const f16x8 x = t < L ? (GK       ? __builtin_bit_cast(f16x8, R.kq[u])
-                                   : SCALED ? cvt8s(R.kq[u], p < 1024 ? R.e.x : R.e.y)
-                                            : cvt8(R.kq[u]))
-                                : z8;
-          const f16x4 lo = f16x4{x[0], x[1], x[2], x[3]}, hi = f16x4{x[4], x[5], x[6], x[7]};
-          f16 *base = (p < 1024 ? sm.K : sm.Q)[buf];
-          *(f16x4 *)&base[kq_chunk(t, c0 + sw) + hh] = sw ? hi : lo;
-          *(f16x4 *)&base[kq_chunk(t, c0 + !sw) + hh] = sw ? lo : hi;
-        }
+        const f16x8 x = t < L ? (GK       ? __builtin_bit_cast(f16x8, R.kq[u])
+                                 : SCALED ? cvt8s(R.kq[u], p < 1024 ? R.e.x : R.e.y)
+                                          : cvt8(R.kq[u]))
+                              : z8;
+        const f16x4 lo = f16x4{x[0], x[1], x[2], x[3]}, hi = f16x4{x[4], x[5], x[6], x[7]};
+        f16 *base = (p < 1024 ? sm.K : sm.Q)[buf];
+        *(f16x4 *)&base[kq_chunk(t, c0 + sw) + hh] = sw ? hi : lo;
+        *(f16x4 *)&base[kq_chunk(t, c0 + !sw) + hh] = sw ? lo : hi;
       }
+      arrived(R.v);  // (the stores below sit in a branch)
+      arrived(R.b);
+#pragma unroll
+      for (int u = 0; u < NR; ++u) arrived(R.r[u]);
       if (lt < 256) {
         // row r, channels 8 q .. +7 of the tile: the operands of sub-tile q >> 1,
         // lanes r % 16 + 16 g for g = 2 (q & 1) and the next, half m & 1.  The
@@ -926,6 +929,10 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       if (lt < C)
         sm.b[buf][lt] = lt < L ? ((xf & kGateLogits) ? sigmoid_gate(R.b) : R.b) : 0.f;
     };
+    // The loop bodies hold no condition: a store guarded by one would leave
+    // the loads in flight differently on its two paths, and the waits after
+    // the join would then drain every load.  A store of the chunk past the
+    // last (zeros, the last record reread) goes to a buffer no one reads.
     if (!GK) {
       // Entering iteration c the loaders hold chunk c+1 in one register set; they
       // load chunk c+2 into the other (freed by the previous store), then store
@@ -936,16 +943,16 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         stash(ra, 0);
       }
       __syncthreads();
-      for (int c = 0; c < NC; c += 2) {
+      int c = 0;
+      for (; c + 1 < NC; c += 2) {
         load(ra, c + 2);
-        if (c + 1 < NC) stash(rb, c + 1);
+        stash(rb, c + 1);
         __syncthreads();
-        if (c + 1 < NC) {
-          load(rb, c + 3);
-          if (c + 2 < NC) stash(ra, c + 2);
-          __syncthreads();
-        }
+        load(rb, c + 3);
+        stash(ra, c + 2);
+        __syncthreads();
       }
+      if (c < NC) __syncthreads();  // the last iteration of an odd count: nothing to store
       __syncthreads();  // the output waves' last iteration
       return;
     }
@@ -960,20 +967,23 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       stash(ra, 0);
     }
     __syncthreads();
-    for (int c = 0; c < NC; c += 3) {
+    int c = 0;
+    for (; c + 2 < NC; c += 3) {
       load(ra, c + 3);
+      stash(rb, c + 1);
+      __syncthreads();
+      load(rb, c + 4);
+      stash(rc, c + 2);
+      __syncthreads();
+      load(rc, c + 5);
+      stash(ra, c + 3);
+      __syncthreads();
+    }
+    // the last one or two iterations (chunks c, c+1): chunk c+1 still to store
+    if (c < NC) {
       if (c + 1 < NC) stash(rb, c + 1);
       __syncthreads();
-      if (c + 1 < NC) {
-        load(rb, c + 4);
-        if (c + 2 < NC) stash(rc, c + 2);
-        __syncthreads();
-      }
-      if (c + 2 < NC) {
-        load(rc, c + 5);
-        if (c + 3 < NC) stash(ra, c + 3);
-        __syncthreads();
-      }
+      if (c + 1 < NC) __syncthreads();
     }
     __syncthreads();  // the output waves' last iteration
   } else if (wave < 2) {
@@ -1028,13 +1038,20 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       // result layout (exactly: bf16 through the identity), then R / sr in fp16
       // with sr a power of two >= max |R| of the wave's channels
       f32x4 rf[4];
+      // every operand read is issued before the first product, so that the
+      // products do not wait on LDS latency one read at a time
+      f16x8 ka[16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[4 * m + kk] = ld8(&Kc[kq_chunk(16 * m + c16, 4 * kk + g)]);
       const uint4 Vv[2] = {sm.V[cb][sn][0][lane], sm.V[cb][sn][1][lane]};
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         f32x4 a = zero4();
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          a = mma32(ld8(&Kc[kq_chunk(16 * m + c16, 4 * kk + g)]), Sb[kk], a);
+        for (int kk = 0; kk < 4; ++kk) a = mma32(ka[4 * m + kk], Sb[kk], a);
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[e] *= ss;
         if (SCALED) {
@@ -1078,11 +1095,15 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       const float gL = GATED ? *(const float *)(sm.rec[cb] + OFF_GL) : 1.0f;
       // S^T <- gamma_L S^T + ds sr Kt^T (X / sr) (GK: row i of S^T decays by g_L[i])
       const float dsr = ds * sr;
+      f16x8 kf[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) kf[x] = KtF[x * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i8 = 0; i8 < 8; ++i8) {
         f32x4 u = zero4();
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) u = mma32(KtF[(i8 * 2 + qq) * 64 + lane], Xb[qq], u);
+        for (int qq = 0; qq < 2; ++qq) u = mma32(kf[i8 * 2 + qq], Xb[qq], u);
         f32x4 gv = {gL, gL, gL, gL};
         if (GK) gv = *(const f32x4 *)(sm.rec[cb] + OFF_SC + 4 * (16 * i8 + 4 * g));
 #pragma unroll
@@ -1148,12 +1169,17 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         for (int kk = 0; kk < 4; ++kk) Sb[kk] = sm.Sx[cb][sn][kk][lane];
         const float ss = sm.sig[cb][sn][0];  // Sb holds S^T / ss
         const f16 *Qc = sm.Q[cb];
+        f16x8 qa[16];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) qa[4 * m + kk] = ld8(&Qc[kq_chunk(16 * m + c16, 4 * kk + g)]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           f32x4 a = zero4();
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            a = mma32(ld8(&Qc[kq_chunk(16 * m + c16, 4 * kk + g)]), Sb[kk], a);
+          for (int kk = 0; kk < 4; ++kk) a = mma32(qa[4 * m + kk], Sb[kk], a);
 #pragma unroll
           for (int e = 0; e < 4; ++e) a[e] *= ss;
           if (SCALED) {

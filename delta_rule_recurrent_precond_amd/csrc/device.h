@@ -71,6 +71,13 @@ __device__ __forceinline__ float column_sum4(float v) {
 // A power of two >= x (x >= 0 and finite; 1 for 0).  Values divided by it keep
 // their significand exactly, so it moves a vector into fp16's normal range
 // without changing how it rounds.
+// Waits here for a load into x's registers to arrive (an empty asm that reads
+// them), so that a branch that uses x after this point holds no wait of its own.
+__device__ __forceinline__ void arrived(const uint4 &x) {
+  asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+}
+__device__ __forceinline__ void arrived(float x) { asm volatile("" ::"v"(x)); }
+
 __device__ __forceinline__ float pow2_above(float x) {
   if (!(x > 0.f)) return 1.0f;
   int e;
