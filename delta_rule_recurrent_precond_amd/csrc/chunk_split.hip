@@ -116,20 +116,27 @@ constexpr int KP = 136;  // padded row (halves) of the staged [64][128] tiles
 // record.  GK: the per-channel gate, as described at the top.  xf & kGateLogits:
 // beta and r arrive as logits.
 template <int MODE, bool NORM, bool GATED, bool GK>
-__global__ void __launch_bounds__(256)
+// Four workgroups per CU where the LDS allows it (the two-tile instances) and
+// the registers fit a quarter of the file without spilling (not with raw q, k)
+__global__ void __launch_bounds__(256, (!GK && !NORM && MODE != kDeltaNet) ? 4 : 1)
 chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
            const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
            unsigned char *__restrict__ ws, const float *__restrict__ r,
            const float *__restrict__ wout, const float *__restrict__ alpha, unsigned xf) {
-  // q is needed only for the scores, which are formed first; the blocks of A
-  // and T then reuse its space (53 KB in all: three workgroups per CU)
-  __shared__ __align__(16) f16 Ks[C * KP];          // k
+  // q is needed only for the scores; the blocks of A and T then reuse its
+  // space.  QT (write keys of their own, no per-channel gate): the products of
+  // k with kt are formed first and held in registers, then q takes k's tile,
+  // then the blocks take it: two [64][128] tiles in all (36 KB, four
+  // workgroups per CU, where a tile of its own for q allows three)
+  constexpr bool QT = !GK && MODE != kDeltaNet;
+  __shared__ __align__(16) f16 Ks[C * KP];          // k (QT: then q, then the blocks)
   __shared__ __align__(16) f16 Kts[C * KP];         // kt / ds (kt = k: unused)
-  __shared__ __align__(16) unsigned char QF[C * KP * 2];
-  f16 *Qs = (f16 *)QF;                                                 // q
-  float(*Fd)[16][LDF] = (float(*)[16][LDF])QF;                         // diagonal blocks of A
-  f16(*Aoff)[16][LDT] = (f16(*)[16][LDT])(QF + 4 * 16 * LDF * 4);       // off-diagonal blocks of A
-  f16(*Tdg)[16][LDT] = (f16(*)[16][LDT])(QF + 4 * 16 * LDF * 4 + 6 * 16 * LDT * 2);  // diag of T
+  __shared__ __align__(16) unsigned char QF[QT ? 16 : C * KP * 2];
+  f16 *Qs = QT ? Ks : (f16 *)QF;                                       // q
+  unsigned char *const Bl = QT ? (unsigned char *)Ks : QF;
+  float(*Fd)[16][LDF] = (float(*)[16][LDF])Bl;                         // diagonal blocks of A
+  f16(*Aoff)[16][LDT] = (f16(*)[16][LDT])(Bl + 4 * 16 * LDF * 4);       // off-diagonal blocks of A
+  f16(*Tdg)[16][LDT] = (f16(*)[16][LDT])(Bl + 4 * 16 * LDF * 4 + 6 * 16 * LDT * 2);  // diag of T
   static_assert(4 * 16 * LDF * 4 + 10 * 16 * LDT * 2 <= C * KP * 2, "A and T blocks fit");
   __shared__ float bs[C];
   __shared__ float cs[C], rs[C];  // kOsdn: c_t and r_t
@@ -309,7 +316,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     *(f16x8 *)&Ks[t * KP + i0] = XN ? cvt8s(rk[u], ik)
                                  : (NORM && MODE == kDeltaNet) ? cvt8s(rk[u], kscale[u])
                                                                : cvt8(rk[u]);
-    *(f16x8 *)&Qs[t * KP + i0] = XN ? cvt8s(rq[u], iq) : NORM ? cvt8s(rq[u], qscale[u]) : cvt8(rq[u]);
+    if (!QT) *(f16x8 *)&Qs[t * KP + i0] = XN ? cvt8s(rq[u], iq) : NORM ? cvt8s(rq[u], qscale[u]) : cvt8(rq[u]);
     if (MODE == kGiven) {
       const unsigned short *s = (const unsigned short *)&rt[u];
       f16x8 hv;
@@ -349,7 +356,9 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // barrier that follows its last read (one more array would cost the third
     // workgroup per CU)
     float *dmid = (float *)Kts;
-    float xa[C / 2], xb[C / 2];  // P_t kh_t and (d_t or e_t) kh_t
+    // (d_t or e_t) kx_t; the second half's P_t kx_t is formed again after the
+    // barrier from the keys and r, in the same order (fewer registers held)
+    float xb[C / 2];
     {
       f16 kc[C / 2];
 #pragma unroll
@@ -371,7 +380,6 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           const float kv = (float)kc[t0 + e];
           const float kh = NORM ? kv * sv[e] : kv;
           const float kx = XN ? kv : kh;
-          xa[t0 + e] = pr * kx;
           xb[t0 + e] = d * kx;
           d = fmaf(cv[e], kh * kh, rv[e] * d);
           pr *= rv[e];
@@ -381,24 +389,42 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
     __syncthreads();
     // XN: the scores' query factors move from kt's tile (written below) to r's
-    // array, which the recurrence no longer reads
-    if (XN && tid < C) rs[tid] = sq[tid];
-    // first half: x = 0 * xa + xb, exactly xb
-    const float dj = tid < DK ? 0.f : dmid[dim];
+    // array once the second half below has read r
+    const float sqv = (XN && tid < C) ? sq[tid] : 0.f;
+    // second half: x_t = (P_t kx_t) d_32 + e_t kx_t (the first half's x is xb)
     float km = 0.f;
+    if (t0h) {
+      const float dj = dmid[dim];
+      float pr = 1.f;
 #pragma unroll
-    for (int t = 0; t < C / 2; ++t) {
-      xa[t] = fmaf(xa[t], dj, xb[t]);
-      km = fmaxf(km, fabsf(xa[t]));
+      for (int t0 = 0; t0 < C / 2; t0 += 4) {
+        const float4 r4 = *(const float4 *)&rs[t0h + t0];
+        const float rv[4] = {r4.x, r4.y, r4.z, r4.w};
+        float sv[4] = {1.f, 1.f, 1.f, 1.f};
+        if (NORM) {
+          const float4 s4 = *(const float4 *)&sk[t0h + t0];
+          sv[0] = s4.x, sv[1] = s4.y, sv[2] = s4.z, sv[3] = s4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float kv = (float)Ks[(t0h + t0 + e) * KP + dim];
+          const float kx = XN ? kv : (NORM ? kv * sv[e] : kv);
+          xb[t0 + e] = fmaf(pr * kx, dj, xb[t0 + e]);
+          pr *= rv[e];
+        }
+      }
     }
+#pragma unroll
+    for (int t = 0; t < C / 2; ++t) km = fmaxf(km, fabsf(xb[t]));
     km = wave_max(km);
     if (lane == 0) red[wave] = km;
     __syncthreads();
+    if (XN && tid < C) rs[tid] = sqv;
     km = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     ds = km > 0.f ? fexp2(ceilf(flog2(km))) : 1.0f;
     inv = 1.0f / ds;
 #pragma unroll
-    for (int t = 0; t < C / 2; ++t) Kts[(t0h + t) * KP + dim] = h(xa[t] * inv);
+    for (int t = 0; t < C / 2; ++t) Kts[(t0h + t) * KP + dim] = h(xb[t] * inv);
     __syncthreads();
   }
 
@@ -601,6 +627,29 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     return x;
   };
 
+  // QT: the products of k with kt for A (the diagonal block `wave`, then the
+  // off-diagonal jobs wave and wave + 4) into registers; then q into k's tile
+  f32x4 aD = zero4(), aO[2] = {zero4(), zero4()};
+  if (QT) {
+    aD = gram(Ks, wave, wave);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int job = wave + 4 * j;
+      if (job < 6) {
+        int rt_, ct;
+        off_tile(job, rt_, ct);
+        aO[j] = gram(Ks, rt_, ct);
+      }
+    }
+    __syncthreads();  // k is no longer read
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
+      *(f16x8 *)&Qs[t * KP + i0] = XN ? cvt8s(rq[u], iq) : NORM ? cvt8s(rq[u], qscale[u]) : cvt8(rq[u]);
+    }
+    __syncthreads();
+  }
+
   // ---- scores P = lower(Q Kt^T) ds, emitted as A operands (transposed tiles)
   for (int idx = wave; idx < 10; idx += 4) {
     int rt_, ct;
@@ -625,7 +674,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   // ---- A: diagonal block `wave` (then its inverse) and off-diagonal blocks
   {
-    const f32x4 acc = GK ? diag4(Adg, wave) : gram(Ks, wave, wave);
+    const f32x4 acc = GK ? diag4(Adg, wave) : QT ? aD : gram(Ks, wave, wave);
     const f32x4 b4 = beta4(wave), f4 = krow4(wave), dc = dec4(wave, 16 * wave + c16);
     const float kc = colf(16 * wave + c16);
 #pragma unroll
@@ -634,10 +683,13 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       Fd[wave][row][c16] = c16 < row ? a_entry(b4[e], dc[e], acc[e] * kc, f4[e]) : 0.f;
     }
   }
-  for (int job = wave; job < 6; job += 4) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int job = wave + 4 * j;
+    if (job >= 6) break;
     int rt_, ct;
     off_tile(job, rt_, ct);
-    const f32x4 acc = GK ? gramk(Ks, rt_, ct) : gram(Ks, rt_, ct);
+    const f32x4 acc = GK ? gramk(Ks, rt_, ct) : QT ? aO[j] : gram(Ks, rt_, ct);
     const f32x4 b4 = beta4(rt_), f4 = krow4(rt_), dc = dec4(rt_, 16 * ct + c16);
     const float kc = colf(16 * ct + c16);
 #pragma unroll
