@@ -7,7 +7,8 @@
 namespace osdn {
 
 // Per (b, h, chunk of 64 tokens), written by walk_prep and read by walk:
-//   W_MINV  fp32 [64][64]  (I + M)^-1, row-major (zero above the diagonal)
+//   W_MINV  fp32 [64][64]  (I + M)^-1, row-major; only its ten 16x16 blocks on
+//                          and below the diagonal are written (and read)
 //   W_U     fp32 [64]      beta_t Gamma_t
 //   W_A     fp32 [64]      alpha_t = eta beta_t / n_t (0 if n_t = 0)
 //   W_WA    fp32 [64]      R_{L,t} alpha_t (0 past the end of the sequence)

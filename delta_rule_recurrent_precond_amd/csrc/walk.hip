@@ -223,11 +223,17 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
     }
   }
 
-  // the record
+  // the record: the inverse's ten 16x16 blocks on and below the diagonal (the
+  // walk reads no other; piece q: block q >> 6, row (q >> 2) & 15, columns
+  // 4 (q & 3) .. +3), then the vectors
   unsigned char *rec = wrec + ((long)bh * NC + c) * WREC;
   float4 *dst = (float4 *)(rec + W_MINV);
-  for (int idx = tid; idx < C * C / 4; idx += 256)
-    dst[idx] = *(const float4 *)&Mi[(idx >> 4) * FP + (idx & 15) * 4];
+  for (int q = tid; q < 640; q += 256) {
+    int bi, bj;
+    tri_tile(q >> 6, bi, bj);
+    const int row = 16 * bi + ((q >> 2) & 15), col = 16 * bj + 4 * (q & 3);
+    dst[(row * C + col) >> 2] = *(const float4 *)&Mi[row * FP + col];
+  }
   if (tid < C) {
     const int t = tid;
     ((float *)(rec + W_U))[t] = bs[t] * fexp2(lg[t]);
