@@ -132,8 +132,10 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   }
   __syncthreads();
 
-  if (tid < C) al[tid] = nn[tid] > 0.f ? eta * bs[tid] / nn[tid] : 0.f;
-  // lower tiles of the key gram G = P P^T with P = k (.) k in fp16
+  if (tid < C) al[tid] = nn[tid] > 0.f ? eta * bs[tid] / nn[tid] : 0.f;  // for the record
+  // lower tiles of the key gram G = P P^T with P = k (.) k in fp16, turned into
+  // M in the result registers: M_ts = beta_t alpha_s R_{t,s} s_t s_s e^4 G_ts for
+  // s < t, zero on and above the diagonal (alpha_s formed here as for al)
   for (int job = wave; job < 10; job += 4) {
     int rt, ct;
     tri_tile(job, rt, ct);
@@ -144,41 +146,16 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
       const f16x8 b = ld8(&Kh[(16 * ct + c16) * KP + 32 * kk + 8 * g]);
       acc = mma32(a * a, b * b, acc);
     }
+    const int s = 16 * ct + c16, t0 = 16 * rt + 4 * g;
+    const float als = nn[s] > 0.f ? eta * bs[s] / nn[s] : 0.f, lgs = lg[s + 1], sss = ss[s];
+    const float4 b4 = *(const float4 *)&bs[t0], l4 = *(const float4 *)&lg[t0];
+    const float4 s4 = *(const float4 *)&ss[t0];
+    const float bt[4] = {b4.x, b4.y, b4.z, b4.w}, lt[4] = {l4.x, l4.y, l4.z, l4.w};
+    const float st[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) F[(16 * rt + 4 * g + e) * FP + 16 * ct + c16] = acc[e];
-  }
-  __syncthreads();
-
-  // M in place: thread (row t, quarter q) scales columns 16q..16q+15, zero on
-  // and above the diagonal; the blocks of (I + M)^-1 above the diagonal are zero
-  {
-    const int t = tid >> 2, q = tid & 3;
-    const float bl = bs[t], lt = lg[t], ssl = ss[t];
-    // the columns' factors as 16-byte reads (lg from 16 q, used from 16 q + 1)
-    float row[16], alc[16], ssc[16], lgc[20];
-#pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-      const float4 f4 = *(const float4 *)&F[t * FP + 16 * q + j];
-      row[j] = f4.x, row[j + 1] = f4.y, row[j + 2] = f4.z, row[j + 3] = f4.w;
-      const float4 a4 = *(const float4 *)&al[16 * q + j], s4 = *(const float4 *)&ss[16 * q + j];
-      alc[j] = a4.x, alc[j + 1] = a4.y, alc[j + 2] = a4.z, alc[j + 3] = a4.w;
-      ssc[j] = s4.x, ssc[j + 1] = s4.y, ssc[j + 2] = s4.z, ssc[j + 3] = s4.w;
-    }
-#pragma unroll
-    for (int j = 0; j < 20; j += 4) {
-      const float4 l4 = *(const float4 *)&lg[16 * q + j];
-      lgc[j] = l4.x, lgc[j + 1] = l4.y, lgc[j + 2] = l4.z, lgc[j + 3] = l4.w;
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int s = 16 * q + j;
-      row[j] = s < t ? bl * alc[j] * fexp2(lt - lgc[j + 1]) * (ssl * ssc[j]) * (e4 * row[j]) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-      *(float4 *)&F[t * FP + 16 * q + j] = float4{row[j], row[j + 1], row[j + 2], row[j + 3]};
-      if (16 * q > t) *(float4 *)&Mi[t * FP + 16 * q + j] = float4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int e = 0; e < 4; ++e)
+      F[(t0 + e) * FP + s] =
+          s < t0 + e ? bt[e] * als * fexp2(lt[e] - lgs) * (st[e] * sss) * (e4 * acc[e]) : 0.f;
   }
   __syncthreads();
 
