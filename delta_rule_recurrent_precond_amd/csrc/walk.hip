@@ -36,6 +36,15 @@ constexpr int DK = 128;
 constexpr int KP = 136;  // padded row (halves) of [64][128] tiles in LDS
 constexpr int FP = 68;   // padded row (floats) of [64][64] fp32 tiles in LDS
 
+// The maximum over each row of 16 lanes (DPP); every lane of the row receives it.
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // walk_prep: one workgroup of 4 waves per (b, h, chunk).
 // ---------------------------------------------------------------------------
@@ -48,6 +57,7 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   __shared__ float Yw[3][16][17];                     // per-wave staging of a block sum
   __shared__ __align__(16) float bs[C], al[C], nn[C], lg[C + 4];
   __shared__ __align__(16) float ss[C];  // 1 / ||k_t||^2 for unnormalised keys, else 1
+  __shared__ __align__(16) float e2[C];  // e_t^2: the square of row t's staging scale
   static_assert(C * KP * 2 >= C * FP * 4, "the inverse fits in the keys' space");
   f16 *Kh = (f16 *)KM;
   float *Mi = (float *)KM;
@@ -78,44 +88,33 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
     pr = sigmoid_gate(pr);
   }
 
-  // stage the stored keys divided by e, a power of two >= the chunk's largest
-  // |k| (exact in fp16 at any scale, and their squares stay in range); the
-  // key gram then carries 1 / e^4, put back in fp32 below.  n_t from the stored
-  // bf16 values (16 threads per token).  Unnormalised keys enter through the
-  // fp32 factor 1 / n_t on p_t (the normalised key's p is p_t / n_t).
-  float ek;
-  {
-    float mk = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const unsigned short *s8 = (const unsigned short *)&rk[u];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mk = fmaxf(mk, fabsf(bf2f(s8[e])));
-    }
-    mk = wave_max(mk);
-    if (lane == 0) Yw[0][0][wave] = mk;
-    __syncthreads();
-    ek = pow2_above(fmaxf(fmaxf(Yw[0][0][0], Yw[0][0][1]), fmaxf(Yw[0][0][2], Yw[0][0][3])));
-  }
-  const float ike = 1.0f / ek, e4 = (ek * ek) * (ek * ek);
+  // stage the stored keys of row t divided by e_t, a power of two >= the
+  // row's largest |k| (exact in fp16 at any scale, and their squares stay in
+  // range); entry (t, s) of the key gram then carries 1 / (e_t^2 e_s^2), put back
+  // in fp32 when M is formed.  n_t from the stored bf16 values (16 threads per
+  // token).  Unnormalised keys enter through the fp32 factor 1 / n_t on p_t
+  // (the normalised key's p is p_t / n_t).
   const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
     const bool ok = t < L;
-    *(f16x8 *)&Kh[t * KP + i0] = ok ? cvt8s(rk[u], ike) : z8;
     const unsigned short *s = (const unsigned short *)&rk[u];
-    float sq = 0.f;
+    float sq = 0.f, mk = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = bf2f(s[e]);
       sq = fmaf(x, x, sq);
+      mk = fmaxf(mk, fabsf(x));
     }
     sq = group_sum<16>(ok ? sq : 0.f);
+    const float er = pow2_above(row_max16(mk));
+    *(f16x8 *)&Kh[t * KP + i0] = ok ? cvt8s(rk[u], 1.0f / er) : z8;
     if ((p & 15) == 0) {
       const float sc = (xf & kNormQK) ? (sq > 0.f ? 1.0f / sq : 0.f) : 1.0f;
       ss[t] = sc;
       nn[t] = sq * sc;  // ||k_t||^2 of the key the recurrence sees
+      e2[t] = er * er;
     }
   }
   if (wave == 0) {
@@ -134,8 +133,8 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 
   if (tid < C) al[tid] = nn[tid] > 0.f ? eta * bs[tid] / nn[tid] : 0.f;  // for the record
   // lower tiles of the key gram G = P P^T with P = k (.) k in fp16, turned into
-  // M in the result registers: M_ts = beta_t alpha_s R_{t,s} s_t s_s e^4 G_ts for
-  // s < t, zero on and above the diagonal (alpha_s formed here as for al)
+  // M in the result registers: M_ts = beta_t alpha_s R_{t,s} s_t s_s e_t^2 e_s^2 G_ts
+  // for s < t, zero on and above the diagonal (alpha_s formed here as for al)
   for (int job = wave; job < 10; job += 4) {
     int rt, ct;
     tri_tile(job, rt, ct);
@@ -148,14 +147,16 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
     }
     const int s = 16 * ct + c16, t0 = 16 * rt + 4 * g;
     const float als = nn[s] > 0.f ? eta * bs[s] / nn[s] : 0.f, lgs = lg[s + 1], sss = ss[s];
+    const float e2s = e2[s];
     const float4 b4 = *(const float4 *)&bs[t0], l4 = *(const float4 *)&lg[t0];
-    const float4 s4 = *(const float4 *)&ss[t0];
+    const float4 s4 = *(const float4 *)&ss[t0], x4 = *(const float4 *)&e2[t0];
     const float bt[4] = {b4.x, b4.y, b4.z, b4.w}, lt[4] = {l4.x, l4.y, l4.z, l4.w};
-    const float st[4] = {s4.x, s4.y, s4.z, s4.w};
+    const float st[4] = {s4.x, s4.y, s4.z, s4.w}, et[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      F[(t0 + e) * FP + s] =
-          s < t0 + e ? bt[e] * als * fexp2(lt[e] - lgs) * (st[e] * sss) * (e4 * acc[e]) : 0.f;
+      F[(t0 + e) * FP + s] = s < t0 + e ? bt[e] * als * fexp2(lt[e] - lgs) * (st[e] * sss) *
+                                              ((et[e] * e2s) * acc[e])
+                                        : 0.f;
   }
   __syncthreads();
 
