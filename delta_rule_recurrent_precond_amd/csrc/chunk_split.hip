@@ -183,13 +183,14 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // ---- loads: 1024 pieces of 8 elements per tensor, 4 per thread.  Rows past
   // the end reread the last row (a load under a condition would make the
   // compiler wait for it where the branches join) and are zeroed here.
+  // k (and the given kt) first, q last: the staging of k then waits for k
+  // alone, and q's loads stay in flight until q is staged
   uint4 rk[4], rq[4], rt[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = p >> 4;
     const long off = (tok0 + min(t, L - 1)) * DK + (p & 15) * 8;
     rk[u] = *(const uint4 *)(k + off);
-    rq[u] = *(const uint4 *)(q + off);
     if (MODE == kGiven) rt[u] = *(const uint4 *)(kt_in + off);
   }
   // kOsdn: the chunk's entry d of dimension tid (threads 0-127), loaded here so
@@ -197,9 +198,15 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const float d_entry = MODE == kOsdn ? wout[((long)bh * NC + c) * WOUT + min(tid, DK - 1)] : 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
+    const int p = tid + 256 * u, t = p >> 4;
+    rq[u] = *(const uint4 *)(q + (tok0 + min(t, L - 1)) * DK + (p & 15) * 8);
+  }
+  // (q's rows past the end are zeroed where q is staged: a write to its
+  // registers here would wait for its loads)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
     if ((tid + 256 * u) >> 4 >= L) {
       rk[u] = uint4{0, 0, 0, 0};
-      rq[u] = uint4{0, 0, 0, 0};
       if (MODE == kGiven) rt[u] = uint4{0, 0, 0, 0};
     }
   }
@@ -316,7 +323,11 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     *(f16x8 *)&Ks[t * KP + i0] = XN ? cvt8s(rk[u], ik)
                                  : (NORM && MODE == kDeltaNet) ? cvt8s(rk[u], kscale[u])
                                                                : cvt8(rk[u]);
-    if (!QT) *(f16x8 *)&Qs[t * KP + i0] = XN ? cvt8s(rq[u], iq) : NORM ? cvt8s(rq[u], qscale[u]) : cvt8(rq[u]);
+    if (!QT)
+      *(f16x8 *)&Qs[t * KP + i0] = t >= L   ? f16x8{0, 0, 0, 0, 0, 0, 0, 0}
+                                   : XN     ? cvt8s(rq[u], iq)
+                                   : NORM   ? cvt8s(rq[u], qscale[u])
+                                            : cvt8(rq[u]);
     if (MODE == kGiven) {
       const unsigned short *s = (const unsigned short *)&rt[u];
       f16x8 hv;
@@ -645,7 +656,10 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
-      *(f16x8 *)&Qs[t * KP + i0] = XN ? cvt8s(rq[u], iq) : NORM ? cvt8s(rq[u], qscale[u]) : cvt8(rq[u]);
+      *(f16x8 *)&Qs[t * KP + i0] = t >= L   ? f16x8{0, 0, 0, 0, 0, 0, 0, 0}
+                                   : XN     ? cvt8s(rq[u], iq)
+                                   : NORM   ? cvt8s(rq[u], qscale[u])
+                                            : cvt8(rq[u]);
     }
     __syncthreads();
   }
