@@ -201,13 +201,13 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  * The path follows from the shapes and the scratch alone, silently;
  * osdn_forward_path names it.  What each costs, measured on MI355X for
  * B = 4, H = 16, T = 4096, dk = dv = 128, chunk 64, bf16:
- *   "split"      0.32 ms (the scratch of osdn_forward_workspace_bytes:
+ *   "split"      about 0.3 ms (the scratch of osdn_forward_workspace_bytes:
  *                about 137 MB there, 32.75 KiB per (b, h, 64-token chunk))
  *   "fused"      about 0.5 ms: one kernel redoes each chunk's preparation for
  *                every 32-channel tile of the values
  *   "two-phase"  for the per-channel gate (OSDN_GATE_PER_CHANNEL) with less
  *                scratch than "split" needs (65.25 KiB per chunk): about 22 ms,
- *                some 50 times the 0.43 ms of its split path, because the chunk
+ *                some 50 times the 0.45 ms of its split path, because the chunk
  *                pass then runs on vector kernels; give such calls the scratch.
  *                Other shapes run only here (vector kernels, fp32 kt).
  */
