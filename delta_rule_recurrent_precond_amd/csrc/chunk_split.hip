@@ -1068,7 +1068,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(Sacc[i8][e]));
       ss = pow2_above(wave_max(mx));
-      const float is = 1.0f / ss;
+      const float is = pow2_inv(ss);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         f32x4 a = Sacc[2 * kk], b = Sacc[2 * kk + 1];
@@ -1113,11 +1113,21 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         for (int kk = 0; kk < 4; ++kk) ka[4 * m + kk] = ld8(&Kc[kq_chunk(16 * m + c16, 4 * kk + g)]);
       const uint4 Vv[2] = {sm.V[cb][sn][0][lane], sm.V[cb][sn][1][lane]};
       __builtin_amdgcn_sched_barrier(0);
+      f32x4 ks[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        f32x4 a = zero4();
+        ks[m] = zero4();
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) a = mma32(ka[4 * m + kk], Sb[kk], a);
+        for (int kk = 0; kk < 4; ++kk) ks[m] = mma32(ka[4 * m + kk], Sb[kk], ks[m]);
+      }
+      // the operands of T R, on their way while R and its scale are formed
+      f16x8 tm[6];
+#pragma unroll
+      for (int x = 0; x < 6; ++x) tm[x] = TmA[x * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4 a = ks[m];
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[e] *= ss;
         if (SCALED) {
@@ -1132,12 +1142,17 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 #pragma unroll
         for (int e = 0; e < 4; ++e) rf[m][e] = b4[e] * (vv[e] - a[e]);
       }
+      // the S update's operands, on their way while R's scale and X are formed
+      f16x8 kf[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) kf[x] = KtF[x * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
       float mr = 0.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mr = fmaxf(mr, fabsf(rf[m][e]));
-      const float sr = pow2_above(wave_max(mr)), isr = 1.0f / sr;
+      const float sr = pow2_above(wave_max(mr)), isr = pow2_inv(sr);
       f16x4 rr[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
@@ -1150,8 +1165,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       for (int m = 0; m < 4; ++m) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int qq = 0; qq <= (m >> 1); ++qq)
-          acc = mma32(TmA[op_index(m, qq) * 64 + lane], Rb[qq], acc);
+        for (int qq = 0; qq <= (m >> 1); ++qq) acc = mma32(tm[op_index(m, qq)], Rb[qq], acc);
         X[m] = acc;
       }
       const f16x8 Xb[2] = {cat(h4(X[0]), h4(X[1])), cat(h4(X[2]), h4(X[3]))};
@@ -1161,10 +1175,6 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       const float gL = GATED ? *(const float *)(sm.rec[cb] + OFF_GL) : 1.0f;
       // S^T <- gamma_L S^T + ds sr Kt^T (X / sr) (GK: row i of S^T decays by g_L[i])
       const float dsr = ds * sr;
-      f16x8 kf[16];
-#pragma unroll
-      for (int x = 0; x < 16; ++x) kf[x] = KtF[x * 64 + lane];
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i8 = 0; i8 < 8; ++i8) {
         f32x4 u = zero4();
@@ -1209,8 +1219,11 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         const long tok0 = (long)bh * T_ + (long)c * C;
         const int L = min(C, T_ - c * C);
         const f16x8 Xb[2] = {sm.Xx[c & 1][sn][0][lane], sm.Xx[c & 1][sn][1][lane]};
-        // X is stored divided by sr: O = sr (Q S^T / sr + P (X / sr))
-        const float sr = sm.sig[c & 1][sn][1], isr = 1.0f / sr;
+        // X is stored divided by sr: O = sr (Q S^T / sr + P (X / sr)).  The
+        // four tiles are formed before any is stored, so that their products
+        // overlap (a store's condition would split them apart)
+        const float sr = sm.sig[c & 1][sn][1], isr = pow2_inv(sr);
+        f32x4 ot[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -1220,11 +1233,14 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 #pragma unroll
           for (int e = 0; e < 4; ++e) O[m][e] *= sr;
           const bf16x4 ob = {(bf16)O[m][0], (bf16)O[m][1], (bf16)O[m][2], (bf16)O[m][3]};
-          const f32x4 ot = mma16bf(ob, identb, zero4());
+          ot[m] = mma16bf(ob, identb, zero4());
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
           const int t = 16 * m + c16;
           if (t < L)
             *(bf16x4 *)(o + (tok0 + t) * 128 + j0 + 16 * sn + 4 * g) =
-                bf16x4{(bf16)ot[0], (bf16)ot[1], (bf16)ot[2], (bf16)ot[3]};
+                bf16x4{(bf16)ot[m][0], (bf16)ot[m][1], (bf16)ot[m][2], (bf16)ot[m][3]};
         }
       }
       if (it < NC) {

@@ -85,6 +85,14 @@ __device__ __forceinline__ float pow2_above(float x) {
   return ldexpf(1.0f, e);
 }
 
+// 1 / p for p a power of two, exactly (the bits 1.0f / p gives, without the
+// division's refinement steps)
+__device__ __forceinline__ float pow2_inv(float p) {
+  int e;
+  frexpf(p, &e);  // p = 0.5 * 2^e
+  return ldexpf(1.0f, 1 - e);
+}
+
 // Input transforms of the raw-input flags (include/osdn.h): the scale that
 // normalises a vector of squared norm n (a zero vector stays zero), and the
 // logistic sigmoid of a gate logit.

@@ -781,7 +781,7 @@ __device__ __forceinline__ void fused_body(
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(Sacc[i8][e]));
       ss = pow2_above(wave_max(mx));
-      const float is = 1.0f / ss;
+      const float is = pow2_inv(ss);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         f32x4 a = Sacc[2 * kk], b = Sacc[2 * kk + 1];
@@ -848,7 +848,7 @@ __device__ __forceinline__ void fused_body(
 #pragma unroll
           for (int e = 0; e < 4; ++e) mr = fmaxf(mr, fabsf(rf[m][e]));
         sr = pow2_above(wave_max(mr));
-        const float isr = 1.0f / sr;
+        const float isr = pow2_inv(sr);
         f16x4 rr[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -913,7 +913,7 @@ __device__ __forceinline__ void fused_body(
           }
           const f16 *row = &LP[cb][(16 * m + c16) * CP];
           // X is held divided by sr: O = sr (Q S^T / sr + P (X / sr))
-          const float isr = 1.0f / sr;
+          const float isr = pow2_inv(sr);
 #pragma unroll
           for (int e = 0; e < 4; ++e) O[m][e] *= isr;
 #pragma unroll
