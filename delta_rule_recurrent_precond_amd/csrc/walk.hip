@@ -51,15 +51,16 @@ __device__ __forceinline__ float row_max16(float v) {
 __global__ void __launch_bounds__(256)
 walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const float *__restrict__ r,
           float eta, int T_, int NC, unsigned xf, unsigned char *__restrict__ wrec) {
-  // The fp16 keys are needed only for the key gram; (I + M)^-1 reuses their space.
+  // The fp16 squared keys are needed only for the key gram; (I + M)^-1 reuses
+  // their space.
   __shared__ __align__(16) float F[C * FP];           // key gram G, then M (strictly lower)
-  __shared__ __align__(16) unsigned char KM[C * KP * 2];  // fp16 keys, then (I + M)^-1 [64][FP]
+  __shared__ __align__(16) unsigned char KM[C * KP * 2];  // fp16 p_t / e_t^2, then (I + M)^-1 [64][FP]
   __shared__ float Yw[3][16][17];                     // per-wave staging of a block sum
   __shared__ __align__(16) float bs[C], al[C], nn[C], lg[C + 4];
   __shared__ __align__(16) float ss[C];  // 1 / ||k_t||^2 for unnormalised keys, else 1
   __shared__ __align__(16) float e2[C];  // e_t^2: the square of row t's staging scale
   static_assert(C * KP * 2 >= C * FP * 4, "the inverse fits in the keys' space");
-  f16 *Kh = (f16 *)KM;
+  f16 *Ph = (f16 *)KM;
   float *Mi = (float *)KM;
 
   const int tid = threadIdx.x;
@@ -72,14 +73,17 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
 
-  // loads: 1024 pieces of 8 keys, 4 per thread; rows past the end reread the
-  // last row and are zeroed when staged
+  // loads: 1024 pieces of 8 keys, 4 per thread, and beta of each piece's row;
+  // rows past the end reread the last row and are zeroed when staged
   uint4 rk[4];
+  float rb[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = min(p >> 4, L - 1);
     rk[u] = *(const uint4 *)(k + (tok0 + t) * DK + (p & 15) * 8);
   }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) rb[u] = beta[tok0 + min((tid + 256 * u) >> 4, L - 1)];
   const int tb = min(lane, L - 1);
   float pb = beta[tok0 + tb];
   float pr = r ? r[tok0 + tb] : 1.0f;
@@ -88,32 +92,44 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
     pr = sigmoid_gate(pr);
   }
 
-  // stage the stored keys of row t divided by e_t, a power of two >= the
-  // row's largest |k| (exact in fp16 at any scale, and their squares stay in
-  // range); entry (t, s) of the key gram then carries 1 / (e_t^2 e_s^2), put back
-  // in fp32 when M is formed.  n_t from the stored bf16 values (16 threads per
-  // token).  Unnormalised keys enter through the fp32 factor 1 / n_t on p_t
-  // (the normalised key's p is p_t / n_t).
+  // stage p_t = k_t (.) k_t of the stored keys divided by e_t^2, with e_t a
+  // power of two >= the row's largest |k|, in fp16: (k / e_t)^2 is exact in
+  // fp32 (8 significant bits squared), so this is the one rounding the fp16
+  // product of two fp16 copies of k / e_t would make, done once per row
+  // instead of once per gram tile.  Entry (t, s) of the key gram then carries
+  // 1 / (e_t^2 e_s^2), put back in fp32 when M is formed.  n_t from the stored
+  // bf16 values (16 threads per token), and alpha_t with it.  Unnormalised keys
+  // enter through the fp32 factor 1 / n_t on p_t (the normalised key's p is
+  // p_t / n_t).
   const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
     const bool ok = t < L;
     const unsigned short *s = (const unsigned short *)&rk[u];
-    float sq = 0.f, mk = 0.f;
+    float x[8], sq = 0.f, mk = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = bf2f(s[e]);
-      sq = fmaf(x, x, sq);
-      mk = fmaxf(mk, fabsf(x));
+      x[e] = bf2f(s[e]);
+      sq = fmaf(x[e], x[e], sq);
+      mk = fmaxf(mk, fabsf(x[e]));
     }
     sq = group_sum<16>(ok ? sq : 0.f);
-    const float er = pow2_above(row_max16(mk));
-    *(f16x8 *)&Kh[t * KP + i0] = ok ? cvt8s(rk[u], 1.0f / er) : z8;
+    const float er = pow2_above(row_max16(mk)), ie = pow2_inv(er);
+    f16x8 ph;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = x[e] * ie;
+      ph[e] = h(y * y);
+    }
+    *(f16x8 *)&Ph[t * KP + i0] = ok ? ph : z8;
     if ((p & 15) == 0) {
       const float sc = (xf & kNormQK) ? (sq > 0.f ? 1.0f / sq : 0.f) : 1.0f;
+      const float bt = ok ? ((xf & kGateLogits) ? sigmoid_gate(rb[u]) : rb[u]) : 0.f;
+      const float n = sq * sc;  // ||k_t||^2 of the key the recurrence sees
       ss[t] = sc;
-      nn[t] = sq * sc;  // ||k_t||^2 of the key the recurrence sees
+      nn[t] = n;
+      al[t] = n > 0.f ? eta * bt / n : 0.f;
       e2[t] = er * er;
     }
   }
@@ -131,22 +147,19 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   }
   __syncthreads();
 
-  if (tid < C) al[tid] = nn[tid] > 0.f ? eta * bs[tid] / nn[tid] : 0.f;  // for the record
   // lower tiles of the key gram G = P P^T with P = k (.) k in fp16, turned into
   // M in the result registers: M_ts = beta_t alpha_s R_{t,s} s_t s_s e_t^2 e_s^2 G_ts
-  // for s < t, zero on and above the diagonal (alpha_s formed here as for al)
+  // for s < t, zero on and above the diagonal
   for (int job = wave; job < 10; job += 4) {
     int rt, ct;
     tri_tile(job, rt, ct);
     f32x4 acc = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const f16x8 a = ld8(&Kh[(16 * rt + c16) * KP + 32 * kk + 8 * g]);
-      const f16x8 b = ld8(&Kh[(16 * ct + c16) * KP + 32 * kk + 8 * g]);
-      acc = mma32(a * a, b * b, acc);
-    }
+    for (int kk = 0; kk < 4; ++kk)
+      acc = mma32(ld8(&Ph[(16 * rt + c16) * KP + 32 * kk + 8 * g]),
+                  ld8(&Ph[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
     const int s = 16 * ct + c16, t0 = 16 * rt + 4 * g;
-    const float als = nn[s] > 0.f ? eta * bs[s] / nn[s] : 0.f, lgs = lg[s + 1], sss = ss[s];
+    const float als = al[s], lgs = lg[s + 1], sss = ss[s];
     const float e2s = e2[s];
     const float4 b4 = *(const float4 *)&bs[t0], l4 = *(const float4 *)&lg[t0];
     const float4 s4 = *(const float4 *)&ss[t0], x4 = *(const float4 *)&e2[t0];
