@@ -36,12 +36,12 @@ constexpr int DK = 128;
 constexpr int KP = 136;  // padded row (halves) of [64][128] tiles in LDS
 constexpr int FP = 68;   // padded row (floats) of [64][64] fp32 tiles in LDS
 
-// The maximum over each row of 16 lanes (DPP); every lane of the row receives it.
-__device__ __forceinline__ float row_max16(float v) {
+// The maximum over each aligned group of 8 lanes (DPP); every lane of the
+// group receives it.
+__device__ __forceinline__ float group_max8(float v) {
   v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
   v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
   v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
   return v;
 }
 
@@ -73,65 +73,27 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
 
-  // loads: 1024 pieces of 8 keys, 4 per thread, and beta of each piece's row;
-  // rows past the end reread the last row and are zeroed when staged
-  uint4 rk[4];
-  float rb[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int p = tid + 256 * u, t = min(p >> 4, L - 1);
-    rk[u] = *(const uint4 *)(k + (tok0 + t) * DK + (p & 15) * 8);
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) rb[u] = beta[tok0 + min((tid + 256 * u) >> 4, L - 1)];
+  // loads: beta and r of token `lane` first (the log-gate scan needs only
+  // these), beta of the two rows the thread stages, then their keys: row
+  // t = (tid >> 3) + 32 u, keys 8 (tid & 7) + 64 j .. +7 for j = 0, 1 (the 8
+  // threads of a row read, and write to LDS, 128 contiguous bytes per j).
+  // Rows past the end reread the last row and are zeroed when staged.
   const int tb = min(lane, L - 1);
   float pb = beta[tok0 + tb];
   float pr = r ? r[tok0 + tb] : 1.0f;
+  float rb[2];
+  uint4 rk[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) rb[u] = beta[tok0 + min((tid >> 3) + 32 * u, L - 1)];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = min((tid >> 3) + 32 * u, L - 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) rk[u][j] = *(const uint4 *)(k + (tok0 + t) * DK + 8 * (tid & 7) + 64 * j);
+  }
   if (xf & kGateLogits) {
     pb = sigmoid_gate(pb);
     pr = sigmoid_gate(pr);
-  }
-
-  // stage p_t = k_t (.) k_t of the stored keys divided by e_t^2, with e_t a
-  // power of two >= the row's largest |k|, in fp16: (k / e_t)^2 is exact in
-  // fp32 (8 significant bits squared), so this is the one rounding the fp16
-  // product of two fp16 copies of k / e_t would make, done once per row
-  // instead of once per gram tile.  Entry (t, s) of the key gram then carries
-  // 1 / (e_t^2 e_s^2), put back in fp32 when M is formed.  n_t from the stored
-  // bf16 values (16 threads per token), and alpha_t with it.  Unnormalised keys
-  // enter through the fp32 factor 1 / n_t on p_t (the normalised key's p is
-  // p_t / n_t).
-  const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int p = tid + 256 * u, t = p >> 4, i0 = (p & 15) * 8;
-    const bool ok = t < L;
-    const unsigned short *s = (const unsigned short *)&rk[u];
-    float x[8], sq = 0.f, mk = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[e] = bf2f(s[e]);
-      sq = fmaf(x[e], x[e], sq);
-      mk = fmaxf(mk, fabsf(x[e]));
-    }
-    sq = group_sum<16>(ok ? sq : 0.f);
-    const float er = pow2_above(row_max16(mk)), ie = pow2_inv(er);
-    f16x8 ph;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float y = x[e] * ie;
-      ph[e] = h(y * y);
-    }
-    *(f16x8 *)&Ph[t * KP + i0] = ok ? ph : z8;
-    if ((p & 15) == 0) {
-      const float sc = (xf & kNormQK) ? (sq > 0.f ? 1.0f / sq : 0.f) : 1.0f;
-      const float bt = ok ? ((xf & kGateLogits) ? sigmoid_gate(rb[u]) : rb[u]) : 0.f;
-      const float n = sq * sc;  // ||k_t||^2 of the key the recurrence sees
-      ss[t] = sc;
-      nn[t] = n;
-      al[t] = n > 0.f ? eta * bt / n : 0.f;
-      e2[t] = er * er;
-    }
   }
   if (wave == 0) {
     bs[lane] = lane < L ? pb : 0.f;
@@ -144,6 +106,55 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
     }
     lg[lane + 1] = incl;
     if (lane == 0) lg[0] = 0.f;
+  }
+
+  // stage p_t = k_t (.) k_t of the stored keys divided by e_t^2, with e_t a
+  // power of two >= the row's largest |k|, in fp16: (k / e_t)^2 is exact in
+  // fp32 (8 significant bits squared), so this is the one rounding the fp16
+  // product of two fp16 copies of k / e_t would make, done once per row
+  // instead of once per gram tile.  Entry (t, s) of the key gram then carries
+  // 1 / (e_t^2 e_s^2), put back in fp32 when M is formed.  n_t from the stored
+  // bf16 values (8 threads per token), and alpha_t with it.  Unnormalised keys
+  // enter through the fp32 factor 1 / n_t on p_t (the normalised key's p is
+  // p_t / n_t).
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = (tid >> 3) + 32 * u, i0 = 8 * (tid & 7);
+    const bool ok = t < L;
+    float x[16], sq = 0.f, mk = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const unsigned short *s = (const unsigned short *)&rk[u][j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[8 * j + e] = bf2f(s[e]);
+        sq = fmaf(x[8 * j + e], x[8 * j + e], sq);
+        mk = fmaxf(mk, fabsf(x[8 * j + e]));
+      }
+    }
+    sq = group_sum<8>(ok ? sq : 0.f);
+    const float er = pow2_above(group_max8(mk));
+    const float ie = pow2_inv(er);
+    const f16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f16x8 ph;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = x[8 * j + e] * ie;
+        ph[e] = h(y * y);
+      }
+      *(f16x8 *)&Ph[t * KP + i0 + 64 * j] = ok ? ph : z8;  // a padded row stages zeros
+    }
+    if ((tid & 7) == 0) {
+      const float sc = (xf & kNormQK) ? (sq > 0.f ? 1.0f / sq : 0.f) : 1.0f;
+      const float bt = ok ? ((xf & kGateLogits) ? sigmoid_gate(rb[u]) : rb[u]) : 0.f;
+      const float n = sq * sc;  // ||k_t||^2 of the key the recurrence sees
+      ss[t] = sc;
+      nn[t] = n;
+      al[t] = n > 0.f ? eta * bt / n : 0.f;
+      e2[t] = er * er;
+    }
   }
   __syncthreads();
 
