@@ -160,27 +160,46 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 
   // lower tiles of the key gram G = P P^T with P = k (.) k in fp16, turned into
   // M in the result registers: M_ts = beta_t alpha_s R_{t,s} s_t s_s e_t^2 e_s^2 G_ts
-  // for s < t, zero on and above the diagonal
-  for (int job = wave; job < 10; job += 4) {
-    int rt, ct;
-    tri_tile(job, rt, ct);
-    f32x4 acc = zero4();
+  // for s < t, zero on and above the diagonal.  Wave w forms tiles w, w + 4 and
+  // w + 8 of the ten; waves 2 and 3 run a third pass on tile 9 whose entries
+  // go to their own rows of Yw (unused until the off-diagonal blocks), so that
+  // every pass is the same branch-free code: each tile's vectors are read
+  // before its products and the next tile's operands while its entries are
+  // formed.
+  {
+    f16x8 opa[4], opb[4];
+    auto read_ops = [&](int job) {
+      int rt, ct;
+      tri_tile(min(job, 9), rt, ct);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      acc = mma32(ld8(&Ph[(16 * rt + c16) * KP + 32 * kk + 8 * g]),
-                  ld8(&Ph[(16 * ct + c16) * KP + 32 * kk + 8 * g]), acc);
-    const int s = 16 * ct + c16, t0 = 16 * rt + 4 * g;
-    const float als = al[s], lgs = lg[s + 1], sss = ss[s];
-    const float e2s = e2[s];
-    const float4 b4 = *(const float4 *)&bs[t0], l4 = *(const float4 *)&lg[t0];
-    const float4 s4 = *(const float4 *)&ss[t0], x4 = *(const float4 *)&e2[t0];
-    const float bt[4] = {b4.x, b4.y, b4.z, b4.w}, lt[4] = {l4.x, l4.y, l4.z, l4.w};
-    const float st[4] = {s4.x, s4.y, s4.z, s4.w}, et[4] = {x4.x, x4.y, x4.z, x4.w};
+      for (int kk = 0; kk < 4; ++kk) {
+        opa[kk] = ld8(&Ph[(16 * rt + c16) * KP + 32 * kk + 8 * g]);
+        opb[kk] = ld8(&Ph[(16 * ct + c16) * KP + 32 * kk + 8 * g]);
+      }
+    };
+    read_ops(wave);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      F[(t0 + e) * FP + s] = s < t0 + e ? bt[e] * als * fexp2(lt[e] - lgs) * (st[e] * sss) *
-                                              ((et[e] * e2s) * acc[e])
-                                        : 0.f;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int job = wave + 4 * pass;
+      int rt, ct;
+      tri_tile(min(job, 9), rt, ct);
+      const int s = 16 * ct + c16, t0 = 16 * rt + 4 * g;
+      const float als = al[s], lgs = lg[s + 1], sss = ss[s], e2s = e2[s];
+      const float4 b4 = *(const float4 *)&bs[t0], l4 = *(const float4 *)&lg[t0];
+      const float4 s4 = *(const float4 *)&ss[t0], x4 = *(const float4 *)&e2[t0];
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mma32(opa[kk], opb[kk], acc);
+      if (pass < 2) read_ops(job + 4);
+      const float bt[4] = {b4.x, b4.y, b4.z, b4.w}, lt[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float st[4] = {s4.x, s4.y, s4.z, s4.w}, et[4] = {x4.x, x4.y, x4.z, x4.w};
+      float *dst = job < 10 ? &F[t0 * FP + s] : &Yw[wave - 2][0][0] + 4 * lane;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // (above the diagonal R may overflow: not stored)
+        const float m = bt[e] * als * fexp2(lt[e] - lgs) * (st[e] * sss) * ((et[e] * e2s) * acc[e]);
+        dst[job < 10 ? e * FP : e] = s < t0 + e ? m : 0.f;
+      }
+    }
   }
   __syncthreads();
 
