@@ -864,8 +864,36 @@ struct StateSmem {
   f16x8 Sx[2][2][4][64];  // fp16 S^T at a chunk's start [parity][sn][kk][lane], paired order
   f16x8 Xx[2][2][2][64];  // X of a chunk [parity][sn][qq][lane], paired order
   float sig[2][2][2];     // [parity][sn]: the powers of two Sx and Xx are scaled down by
+  // progress counters (see chunk_state): [0] loader-wave chunk stores, [1 + sn]
+  // chunks done by chain wave sn (+1 for the first S), [4 + sn] output passes
+  // done by output wave sn
+  int cnt[8];
 };
 static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
+
+// Bounded wait until the LDS counter *p reaches target (every lane reads the
+// same word; the value is taken as wave-uniform).  The waves of one workgroup
+// hand chunks to each other through these counters: a wave's LDS operations
+// reach the LDS in issue order, so data it stored before incrementing a
+// counter is in place for any wave that then sees the increment.  The empty
+// asm statements keep the compiler from moving LDS accesses across a wait or
+// an increment.  The bound (about 2^22 sleeps of 64 cycles) only ensures the
+// wave ends if a counter were never reached; the protocol reaches every one.
+__device__ __forceinline__ void lds_wait_geq(const int *p, int target) {
+  asm volatile("" ::: "memory");
+  for (int i = 0; i < (1 << 22); ++i) {
+    const int v = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (v >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void lds_count(int *p, int lane) {
+  asm volatile("" ::: "memory");
+  if (lane == 0) __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  asm volatile("" ::: "memory");
+}
 
 template <bool SCALED, bool GATED, bool GK>
 __global__ void __launch_bounds__(ST)
@@ -995,6 +1023,26 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       if (lt < C)
         sm.b[buf][lt] = lt < L ? ((xf & kGateLogits) ? sigmoid_gate(R.b) : R.b) : 0.f;
     };
+    // Chunk cc goes into buffer cc & 1 once every loader wave has stored chunk
+    // cc - 1 (no loader wave is then more than one chunk ahead of another, so a
+    // count of 8 (cc + 1) means all eight have stored chunk cc), both chain waves
+    // are done with chunk cc - 2 and both output waves with their pass over it.
+    auto put = [&](const Regs &R, int cc) __attribute__((always_inline)) {
+      asm volatile("" ::: "memory");
+      for (int i = 0; i < (1 << 22); ++i) {
+        const int l = __hip_atomic_load(&sm.cnt[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int h0 = __hip_atomic_load(&sm.cnt[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int h1 = __hip_atomic_load(&sm.cnt[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int o0 = __hip_atomic_load(&sm.cnt[4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int o1 = __hip_atomic_load(&sm.cnt[5], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const bool ok = l >= 8 * cc && min(h0, h1) >= cc && min(o0, o1) >= cc - 1;
+        if (__builtin_amdgcn_readfirstlane((int)ok)) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      asm volatile("" ::: "memory");
+      stash(R, cc);
+      lds_count(&sm.cnt[0], lane);
+    };
     // The loop bodies hold no condition: a store guarded by one would leave
     // the loads in flight differently on its two paths, and the waits after
     // the join would then drain every load.  A store of the chunk past the
@@ -1009,17 +1057,12 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         stash(ra, 0);
       }
       __syncthreads();
-      int c = 0;
-      for (; c + 1 < NC; c += 2) {
+      for (int c = 0; c + 1 < NC; c += 2) {
         load(ra, c + 2);
-        stash(rb, c + 1);
-        __syncthreads();
+        put(rb, c + 1);
         load(rb, c + 3);
-        stash(ra, c + 2);
-        __syncthreads();
+        put(ra, c + 2);
       }
-      if (c < NC) __syncthreads();  // the last iteration of an odd count: nothing to store
-      __syncthreads();  // the output waves' last iteration
       return;
     }
     // GK (larger records, which miss the last-level cache more often): three
@@ -1036,22 +1079,14 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     int c = 0;
     for (; c + 2 < NC; c += 3) {
       load(ra, c + 3);
-      stash(rb, c + 1);
-      __syncthreads();
+      put(rb, c + 1);
       load(rb, c + 4);
-      stash(rc, c + 2);
-      __syncthreads();
+      put(rc, c + 2);
       load(rc, c + 5);
-      stash(ra, c + 3);
-      __syncthreads();
+      put(ra, c + 3);
     }
-    // the last one or two iterations (chunks c, c+1): chunk c+1 still to store
-    if (c < NC) {
-      if (c + 1 < NC) stash(rb, c + 1);
-      __syncthreads();
-      if (c + 1 < NC) __syncthreads();
-    }
-    __syncthreads();  // the output waves' last iteration
+    // the last one or two chunks (c, c+1): chunk c+1 still to store
+    if (c + 1 < NC) put(rb, c + 1);
   } else if (wave < 2) {
     // ============================== state chain ==============================
     const int sn = wave;
@@ -1082,6 +1117,12 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       }
       if (lane == 0) sm.sig[parity][sn][0] = ss;
     };
+    // chunk 0 is stored and the first S staged before the barrier below
+    if (tid == 0) {
+      sm.cnt[0] = 8;
+      sm.cnt[1] = sm.cnt[2] = 1;
+      sm.cnt[4] = sm.cnt[5] = 0;
+    }
 #pragma unroll
     for (int i8 = 0; i8 < 8; ++i8) Sacc[i8] = zero4();
     if (S0) {
@@ -1096,6 +1137,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 
     for (int c = 0; c < NC; ++c) {
       const int cb = c & 1;
+      lds_wait_geq(&sm.cnt[0], 8 * (c + 1));  // chunk c stored by every loader wave
       const f16 *Kc = sm.K[cb];
       const f16x8 *KtF = (const f16x8 *)(sm.rec[cb] + OFF_KTF);
       const f16x8 *TmA = (const f16x8 *)(sm.rec[cb] + OFF_TM);
@@ -1169,6 +1211,9 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         X[m] = acc;
       }
       const f16x8 Xb[2] = {cat(h4(X[0]), h4(X[1])), cat(h4(X[2]), h4(X[3]))};
+      // X of chunk c - 2 and S at the start of chunk c - 1, in the slots written
+      // below, are read by the output wave's pass c - 1
+      lds_wait_geq(&sm.cnt[4 + sn], c);
       sm.Xx[cb][sn][0][lane] = Xb[0];
       sm.Xx[cb][sn][1][lane] = Xb[1];
       if (lane == 0) sm.sig[cb][sn][1] = sr;
@@ -1187,9 +1232,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
           Sacc[i8][e] = fmaf(dsr, u[e], (GATED || GK) ? gv[e] * Sacc[i8][e] : Sacc[i8][e]);
       }
       stage_S(cb ^ 1);
-      __syncthreads();
+      lds_count(&sm.cnt[1 + sn], lane);
     }
-    __syncthreads();  // the output waves' last iteration
 
     if (S_final) {
 #pragma unroll
@@ -1212,6 +1256,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     f16x8 Pr[6];    // its score operands
     __syncthreads();
     for (int it = 0; it <= NC; ++it) {
+      // X of chunk it - 1 and S at the start of chunk it, from chain wave sn
+      lds_wait_geq(&sm.cnt[1 + sn], it + 1);
       if (it > 0) {
         // O = Q S^T + P X of chunk it - 1, stored as bf16 through an identity
         // transpose (a lane then holds 4 consecutive channels of one token)
@@ -1245,6 +1291,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       }
       if (it < NC) {
         // Q S^T of chunk it from the S^T its chain wave left, and its scores
+        lds_wait_geq(&sm.cnt[0], 8 * (it + 1));  // chunk it stored by every loader wave
         const int cb = it & 1;
         f16x8 Sb[4];
 #pragma unroll
@@ -1275,7 +1322,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 #pragma unroll
         for (int x = 0; x < 6; ++x) Pr[x] = PA[x * 64 + lane];
       }
-      __syncthreads();
+      lds_count(&sm.cnt[4 + sn], lane);
     }
   }
 }
