@@ -864,11 +864,16 @@ struct StateSmem {
   f16x8 Sx[2][2][4][64];  // fp16 S^T at a chunk's start [parity][sn][kk][lane], paired order
   f16x8 Xx[2][2][2][64];  // X of a chunk [parity][sn][qq][lane], paired order
   float sig[2][2][2];     // [parity][sn]: the powers of two Sx and Xx are scaled down by
+  // a chunk's outputs in bf16 on their way to global memory [token][OSP]:
+  // channel 16 sn + j of the tile at slot j (rows of 80 bytes, 16-byte aligned)
+  bf16 Ost[C * 40];
   // progress counters (see chunk_state): [0] loader-wave chunk stores, [1 + sn]
   // chunks done by chain wave sn (+1 for the first S), [4 + sn] output passes
-  // done by output wave sn
+  // done by output wave sn, [6] output tiles staged and [7] output tiles read
+  // (both output waves)
   int cnt[8];
 };
+constexpr int OSP = 40;  // row of Ost (bf16)
 static_assert(sizeof(StateSmem) <= 160 * 1024, "LDS budget");
 
 // Bounded wait until the LDS counter *p reaches target (every lane reads the
@@ -1121,7 +1126,7 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
     if (tid == 0) {
       sm.cnt[0] = 8;
       sm.cnt[1] = sm.cnt[2] = 1;
-      sm.cnt[4] = sm.cnt[5] = 0;
+      sm.cnt[4] = sm.cnt[5] = sm.cnt[6] = sm.cnt[7] = 0;
     }
 #pragma unroll
     for (int i8 = 0; i8 < 8; ++i8) Sacc[i8] = zero4();
@@ -1267,8 +1272,11 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         const f16x8 Xb[2] = {sm.Xx[c & 1][sn][0][lane], sm.Xx[c & 1][sn][1][lane]};
         // X is stored divided by sr: O = sr (Q S^T / sr + P (X / sr)).  The
         // four tiles are formed before any is stored, so that their products
-        // overlap (a store's condition would split them apart)
+        // overlap.  Both output waves stage their 16 channels in LDS; each then
+        // stores 32 tokens of all 32 channels, 64 contiguous bytes a token (half
+        // the write requests of 32-byte pieces)
         const float sr = sm.sig[c & 1][sn][1], isr = pow2_inv(sr);
+        bf16 *stg = sm.Ost;
         f32x4 ot[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -1281,13 +1289,21 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
           const bf16x4 ob = {(bf16)O[m][0], (bf16)O[m][1], (bf16)O[m][2], (bf16)O[m][3]};
           ot[m] = mma16bf(ob, identb, zero4());
         }
+        // both output waves have read the staging of chunk c - 1 (count 2 (it - 1))
+        lds_wait_geq(&sm.cnt[7], 2 * (it - 1));
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int t = 16 * m + c16;
-          if (t < L)
-            *(bf16x4 *)(o + (tok0 + t) * 128 + j0 + 16 * sn + 4 * g) =
-                bf16x4{(bf16)ot[m][0], (bf16)ot[m][1], (bf16)ot[m][2], (bf16)ot[m][3]};
+        for (int m = 0; m < 4; ++m)
+          *(bf16x4 *)&stg[(16 * m + c16) * OSP + 16 * sn + 4 * g] =
+              bf16x4{(bf16)ot[m][0], (bf16)ot[m][1], (bf16)ot[m][2], (bf16)ot[m][3]};
+        lds_count(&sm.cnt[6], lane);
+        lds_wait_geq(&sm.cnt[6], 2 * it);  // both have staged chunk c
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int t = 32 * sn + 16 * j + (lane >> 2);
+          const uint4 ov = *(const uint4 *)&stg[t * OSP + 8 * (lane & 3)];
+          if (t < L) *(uint4 *)(o + (tok0 + t) * 128 + j0 + 8 * (lane & 3)) = ov;
         }
+        lds_count(&sm.cnt[7], lane);
       }
       if (it < NC) {
         // Q S^T of chunk it from the S^T its chain wave left, and its scores
