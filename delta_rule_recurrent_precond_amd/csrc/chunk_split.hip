@@ -820,20 +820,25 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
 // ---------------------------------------------------------------------------
 // chunk_state: one workgroup of 12 waves per (b, h, 32 value channels),
-// sequential over chunks, one barrier per chunk.  Per 16-channel sub-tile sn:
+// sequential over chunks.  Per 16-channel sub-tile sn:
 //   wave sn (the state chain)  K S^T, R = diag(beta)(V - K S^T), X = T R,
 //                              S^T += ds Kt^T X; passes X and the new fp16 S^T
 //                              to the output wave through LDS
 //   wave 2 + sn (the outputs)  Q S^T of chunk c (from the S^T the chain wave
-//                              left), then in the next iteration
-//                              O = Q S^T + P X of chunk c and its stores
+//                              left), then in the next pass O = Q S^T + P X of
+//                              chunk c, staged in LDS with the other output
+//                              wave's channels and stored 64 bytes a token
 //   waves 4-11 (loaders)       global loads of chunk c+2 (GK: c+3), LDS stores of c+1
 // The output wave keeps Q S^T and the score operands of chunk c in registers
 // so that the loaders may refill that chunk's LDS buffer.  The loaders keep two
 // chunks in registers (three with GK), so a chunk's loads are issued one
-// iteration (two) before it is stored.
-// Each role runs its own loop with the same barrier count (NC + 1), so the
-// registers of different roles are never live at the same time.
+// chunk (two) before it is stored.
+// The roles meet at one barrier, after the first chunk is stored and the first
+// S staged; from then on they hand chunks to each other through counters in
+// LDS (StateSmem::cnt), each role waiting only for the buffers it reads or is
+// about to overwrite, so that no role waits for the slowest of the others each
+// chunk.  Each role runs its own loop, so the registers of different roles are
+// never live at the same time.
 // SCALED (unnormalised q, k or a state gate): q and k are staged as stored and
 // the record's per-token factors scale the rows of K S^T and Q S^T in fp32.
 // GATED: S decays by the record's gamma_L (the update operands carry the rest).
