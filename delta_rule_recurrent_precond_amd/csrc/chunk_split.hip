@@ -1449,7 +1449,11 @@ hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   // the gate leaves the preconditioner walk unchanged
   ScanArgs sa{a.k, a.beta, a.r, a.d0, a.eta, a.B, a.H, a.T, a.dk, a.dtype, 0, nullptr,
               a.d_final, nullptr, nullptr, a.log_ratio_sum, a.xf};
-  hipError_t e = launch_walk(sa, rec, wout, s);
+  // the walk's ready flags sit past its records, in space the chunk records
+  // take only later
+  unsigned long long *flags = (unsigned long long *)(rec + (size_t)BH * NC * WREC);
+  static_assert(WREC % 8 == 0 && REC - WREC >= 8, "flags fit past the walk records");
+  hipError_t e = launch_walk(sa, rec, wout, s, flags);
   if (e != hipSuccess) return e;
   e = launch_prep<kOsdn>(BH, NC, s, a.q, a.k, nullptr, a.beta, a.T, rec, a.r, wout, a.alpha, a.xf);
   if (e != hipSuccess) return e;

@@ -145,8 +145,8 @@ OSDN_EXPORT int osdn_precond_scan(const void *k, const float *beta, const float 
   osdn::ScanArgs a{k, beta, r, d0, eta, B, H, T, dk, dtype, 0, k_tilde,
                    d_final, d_all, log_ratio, nullptr};
   if (osdn::walk_supported(dk, dtype) && workspace &&
-      workspace_bytes >= osdn::walk_workspace_bytes(B, H, T))
-    return hip_status(osdn::launch_walk_scan(a, workspace, (hipStream_t)stream));
+      workspace_bytes >= osdn::walk_workspace_min_bytes(B, H, T))
+    return hip_status(osdn::launch_walk_scan(a, workspace, workspace_bytes, (hipStream_t)stream));
   if (osdn::fused_scan_supported(dk, dtype))
     return hip_status(osdn::launch_fused_scan(a, (hipStream_t)stream));
   return hip_status(osdn::launch_precond_scan_serial(a, (hipStream_t)stream));
@@ -260,7 +260,8 @@ OSDN_EXPORT int osdn_forward(const void *q, const void *k, const void *v, const 
                       d_final, nullptr, nullptr, log_ratio_sum, sxf | osdn::kKtF32};
     st = hip_status(osdn::walk_supported(dk, dtype)
                         ? osdn::launch_walk_scan(
-                              sa, (unsigned char *)workspace + two_phase_kt_bytes(B, H, T, dk), s)
+                              sa, (unsigned char *)workspace + two_phase_kt_bytes(B, H, T, dk),
+                              workspace_bytes - two_phase_kt_bytes(B, H, T, dk), s)
                         : osdn::launch_precond_scan_serial(sa, s));
     if (st != OSDN_OK) return st;
     kt = workspace;

@@ -22,6 +22,10 @@
 //              and, if asked, d_t
 // The chunk-parallel pass of the forward (chunk_prep) runs the same in-chunk
 // recurrence to form its write keys.
+#include <atomic>
+#include <chrono>
+#include <random>
+
 #include "device.h"
 #include "launch.h"
 #include "mfma.h"
@@ -35,6 +39,7 @@ constexpr int C = 64;
 constexpr int DK = 128;
 constexpr int KP = 136;  // padded row (halves) of [64][128] tiles in LDS
 constexpr int FP = 68;   // padded row (floats) of [64][64] fp32 tiles in LDS
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // The maximum over each aligned group of 8 lanes (DPP); every lane of the
 // group receives it.
@@ -46,51 +51,88 @@ __device__ __forceinline__ float group_max8(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// walk_prep: one workgroup of 4 waves per (b, h, chunk).
+// walk_prep: the record of one (b, h, chunk), formed by 4 waves (tid 0..255
+// of the caller's 256 threads).  Every thread of the workgroup takes part in
+// the same barriers, so several instances may share a workgroup as long as
+// each runs this once per round.  COH: the record is written with device-scope
+// stores (sc1), which reach memory without an L2 writeback, so that another
+// workgroup of the same launch can read it with device-scope loads once a
+// flag says it is complete; `store` false computes without writing.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const float *__restrict__ r,
-          float eta, int T_, int NC, unsigned xf, unsigned char *__restrict__ wrec) {
+struct alignas(16) PrepSmem {
   // The fp16 squared keys are needed only for the key gram; (I + M)^-1 reuses
   // their space.
-  __shared__ __align__(16) float F[C * FP];           // key gram G, then M (strictly lower)
-  __shared__ __align__(16) unsigned char KM[C * KP * 2];  // fp16 p_t / e_t^2, then (I + M)^-1 [64][FP]
-  __shared__ float Yw[3][16][17];                     // per-wave staging of a block sum
-  __shared__ __align__(16) float bs[C], al[C], nn[C], lg[C + 4];
-  __shared__ __align__(16) float ss[C];  // 1 / ||k_t||^2 for unnormalised keys, else 1
-  __shared__ __align__(16) float e2[C];  // e_t^2: the square of row t's staging scale
-  static_assert(C * KP * 2 >= C * FP * 4, "the inverse fits in the keys' space");
-  f16 *Ph = (f16 *)KM;
-  float *Mi = (float *)KM;
+  float F[C * FP];                // key gram G, then M (strictly lower)
+  unsigned char KM[C * KP * 2];   // fp16 p_t / e_t^2, then (I + M)^-1 [64][FP]
+  float Yw[3][16][17];            // per-wave staging of a block sum
+  float bs[C], al[C], nn[C], lg[C + 4];
+  float ss[C];  // 1 / ||k_t||^2 for unnormalised keys, else 1
+  float e2[C];  // e_t^2: the square of row t's staging scale
+};
+static_assert(C * KP * 2 >= C * FP * 4, "the inverse fits in the keys' space");
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  // chunk-major, last chunk first, heads innermost (as chunk_prep): the walk
-  // reads every head's chunk 0 first
-  const int BHn = gridDim.x / NC;
-  const int c = NC - 1 - (int)(blockIdx.x / BHn), bh = blockIdx.x % BHn;
+// a buffer resource over n bytes at p (raw buffer: offsets in bytes; accesses
+// past n read zero and write nothing)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_over(const void *p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n, 0x00020000);
+}
+constexpr int kSc1 = 16;  // cache policy of a device-scope (sc1) buffer access
+
+// The global loads of one chunk (prep_load), apart from the rest so that a
+// caller can issue the next chunk's while it works on this one: beta and r of
+// token `lane` (the log-gate scan needs only these), beta of the two rows the
+// thread stages, then their keys: row t = (tid >> 3) + 32 u, keys 8 (tid & 7)
+// + 64 j .. +7 for j = 0, 1 (the 8 threads of a row read, and write to LDS,
+// 128 contiguous bytes per j).  Rows past the end reread the last row and are
+// zeroed when staged.
+struct PrepIn {
+  float pb, pr, rb[2];
+  uint4 rk[2][2];
+};
+
+__device__ __forceinline__ PrepIn prep_load(const int tid, const int bh, const int c,
+                                            const bf16 *__restrict__ k,
+                                            const float *__restrict__ beta,
+                                            const float *__restrict__ r, int T_) {
+  PrepIn in;
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
-
-  // loads: beta and r of token `lane` first (the log-gate scan needs only
-  // these), beta of the two rows the thread stages, then their keys: row
-  // t = (tid >> 3) + 32 u, keys 8 (tid & 7) + 64 j .. +7 for j = 0, 1 (the 8
-  // threads of a row read, and write to LDS, 128 contiguous bytes per j).
-  // Rows past the end reread the last row and are zeroed when staged.
-  const int tb = min(lane, L - 1);
-  float pb = beta[tok0 + tb];
-  float pr = r ? r[tok0 + tb] : 1.0f;
-  float rb[2];
-  uint4 rk[2][2];
+  const int tb = min(tid & 63, L - 1);
+  in.pb = beta[tok0 + tb];
+  in.pr = r ? r[tok0 + tb] : 1.0f;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) rb[u] = beta[tok0 + min((tid >> 3) + 32 * u, L - 1)];
+  for (int u = 0; u < 2; ++u) in.rb[u] = beta[tok0 + min((tid >> 3) + 32 * u, L - 1)];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int t = min((tid >> 3) + 32 * u, L - 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) rk[u][j] = *(const uint4 *)(k + (tok0 + t) * DK + 8 * (tid & 7) + 64 * j);
+    for (int j = 0; j < 2; ++j)
+      in.rk[u][j] = *(const uint4 *)(k + (tok0 + t) * DK + 8 * (tid & 7) + 64 * j);
   }
+  return in;
+}
+
+// staged(): called by every thread right after the barrier that ends the
+// staging.  COH: every wave's earlier global stores are complete at that
+// barrier (a caller writes the previous chunk's flag from staged()).
+template <bool COH, typename Staged>
+__device__ __forceinline__ void prep_chunk(PrepSmem &sm, const PrepIn &in, const int tid,
+                                           const int bh, const int c, const bool store,
+                                           const float *__restrict__ r, float eta, int T_, int NC,
+                                           unsigned xf, unsigned char *__restrict__ wrec,
+                                           Staged &&staged) {
+  float *F = sm.F;
+  float(*Yw)[16][17] = sm.Yw;
+  float *bs = sm.bs, *al = sm.al, *nn = sm.nn, *lg = sm.lg, *ss = sm.ss, *e2 = sm.e2;
+  f16 *Ph = (f16 *)sm.KM;
+  float *Mi = (float *)sm.KM;
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+  const int L = min(C, T_ - c * C);
+  float pb = in.pb, pr = in.pr;
+  const float *rb = in.rb;
+  const uint4(*rk)[2] = in.rk;
   if (xf & kGateLogits) {
     pb = sigmoid_gate(pb);
     pr = sigmoid_gate(pr);
@@ -156,7 +198,9 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
       e2[t] = er * er;
     }
   }
+  if (COH) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  staged();
 
   // lower tiles of the key gram G = P P^T with P = k (.) k in fp16, turned into
   // M in the result registers: M_ts = beta_t alpha_s R_{t,s} s_t s_s e_t^2 e_s^2 G_ts
@@ -247,22 +291,48 @@ walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   // the record: the inverse's ten 16x16 blocks on and below the diagonal (the
   // walk reads no other; piece q: block q >> 6, row (q >> 2) & 15, columns
   // 4 (q & 3) .. +3), then the vectors
+  if (!store) return;
   unsigned char *rec = wrec + ((long)bh * NC + c) * WREC;
-  float4 *dst = (float4 *)(rec + W_MINV);
+  const __amdgpu_buffer_rsrc_t rr = rsrc_over(rec, (int)WREC);
+  auto put = [&](float v, size_t off) {
+    if (COH)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rr, (int)off, 0, kSc1);
+    else
+      *(float *)(rec + off) = v;
+  };
   for (int q = tid; q < 640; q += 256) {
     int bi, bj;
     tri_tile(q >> 6, bi, bj);
     const int row = 16 * bi + ((q >> 2) & 15), col = 16 * bj + 4 * (q & 3);
-    dst[(row * C + col) >> 2] = *(const float4 *)&Mi[row * FP + col];
+    const float4 m = *(const float4 *)&Mi[row * FP + col];
+    const size_t off = W_MINV + 4 * (size_t)(row * C + col);
+    if (COH)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{__float_as_uint(m.x), __float_as_uint(m.y), __float_as_uint(m.z), __float_as_uint(m.w)},
+          rr, (int)off, 0, kSc1);
+    else
+      *(float4 *)(rec + off) = m;
   }
   if (tid < C) {
     const int t = tid;
-    ((float *)(rec + W_U))[t] = bs[t] * fexp2(lg[t]);
-    ((float *)(rec + W_A))[t] = al[t];
-    ((float *)(rec + W_WA))[t] = t < L ? fexp2(lg[C] - lg[t + 1]) * al[t] : 0.f;
-    ((float *)(rec + W_S))[t] = ss[t];
+    put(bs[t] * fexp2(lg[t]), W_U + 4 * t);
+    put(al[t], W_A + 4 * t);
+    put(t < L ? fexp2(lg[C] - lg[t + 1]) * al[t] : 0.f, W_WA + 4 * t);
+    put(ss[t], W_S + 4 * t);
   }
-  if (tid == 0) *(float *)(rec + W_GL) = fexp2(lg[C]);
+  if (tid == 0) put(fexp2(lg[C]), W_GL);
+}
+
+__global__ void __launch_bounds__(256)
+walk_prep(const bf16 *__restrict__ k, const float *__restrict__ beta, const float *__restrict__ r,
+          float eta, int T_, int NC, unsigned xf, unsigned char *__restrict__ wrec) {
+  __shared__ PrepSmem sm;
+  // chunk-major, last chunk first, heads innermost (as chunk_prep): the walk
+  // reads every head's chunk 0 first
+  const int BHn = gridDim.x / NC;
+  const int c = NC - 1 - (int)(blockIdx.x / BHn), bh = blockIdx.x % BHn;
+  prep_chunk<false>(sm, prep_load(threadIdx.x, bh, c, k, beta, r, T_), threadIdx.x, bh, c, true,
+                    r, eta, T_, NC, xf, wrec, [] {});
 }
 
 // ---------------------------------------------------------------------------
@@ -297,17 +367,34 @@ struct alignas(16) WalkSmem {
   float pad[4];              // where loader lanes without a record piece store
   float d[DK];               // entry d of the chunk in the pass
   float rhs[C], w[C], g[C];
+  int bad;                   // set if a record never became ready (PIPE)
 };
 
-__global__ void __launch_bounds__(WT)
-walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
-     const float *__restrict__ d0, int T_, int NC, float *__restrict__ wout,
-     float *__restrict__ d_final, float *__restrict__ log_ratio,
-     float *__restrict__ log_ratio_sum) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+// Bound on the polls of a record's ready flag (each a memory round trip plus
+// a sleep: about a third of a second in all); the protocol sets every flag
+// within the time the records take to prepare.  A wave gives up at most once.
+constexpr int kPollLimit = 1 << 18;
+
+// The walk of head bh.  PIPE: the records are written by other workgroups of
+// the same launch while the walk runs; flag[bh * NC + c] holds `epoch` once
+// the record of chunk c is complete, and the records are read with
+// device-scope loads (see prep_chunk).
+template <bool PIPE>
+__device__ __forceinline__ void walk_body(unsigned char *smem_raw, const int bh,
+                                          const bf16 *__restrict__ k,
+                                          const unsigned char *__restrict__ wrec,
+                                          const float *__restrict__ d0, int T_, int NC,
+                                          float *__restrict__ wout, float *__restrict__ d_final,
+                                          float *__restrict__ log_ratio,
+                                          float *__restrict__ log_ratio_sum,
+                                          const unsigned long long *__restrict__ flags,
+                                          unsigned long long epoch) {
   WalkSmem &sm = *reinterpret_cast<WalkSmem *>(smem_raw);
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x;
+  if (PIPE) {
+    if (tid == 0) sm.bad = 0;
+    __syncthreads();
+  }
 
   if (tid >= 256) {
     // ================================ loaders ================================
@@ -354,15 +441,52 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
         R.k[u] = *(const uint4 *)(kc + tt * DK + (p & 15) * 8);
       }
       const unsigned char *rs = wrec + ((long)bh * NC + cc) * WREC;
+      const __amdgpu_buffer_rsrc_t rr = rsrc_over(rs, (int)WREC);
 #pragma unroll
-      for (int u = 0; u < NRP; ++u) R.rr[u] = *(const uint4 *)(rs + rec_off(min(lt + NLD * u, RP - 1)));
+      for (int u = 0; u < NRP; ++u) {
+        const int off = rec_off(min(lt + NLD * u, RP - 1));
+        if (PIPE) {
+          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, kSc1);
+          R.rr[u] = uint4{x.x, x.y, x.z, x.w};
+        } else {
+          R.rr[u] = *(const uint4 *)(rs + off);
+        }
+      }
     };
-    // the record of chunk cc into LDS buffer cc & 1
+    // PIPE: wait until the records of chunks 0 .. cc are all ready (a
+    // wave-uniform call).  `ready` counts the chunks from 0 known to be
+    // ready; each poll reads the flags of the 64 chunks from there on.  false
+    // if the bound ran out, then and in every later call.
+    int ready = 0;
+    bool gave_up = false;
+    auto await = [&](int cc) {
+      cc = min(cc, NC - 1);
+      if (gave_up) return false;
+      const int lane = tid & 63;
+      const unsigned long long *f = flags + (long)bh * NC;
+      for (int i = 0; i < kPollLimit; ++i) {
+        if (cc < ready) return true;
+        const unsigned long long v = __hip_atomic_load(f + min(ready + lane, NC - 1),
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long set = __ballot(v == epoch);
+        ready += ~set == 0ull ? 64 : __builtin_ctzll(~set);
+        if (cc < ready) return true;
+        __builtin_amdgcn_s_sleep(8);
+      }
+      gave_up = true;
+      return false;
+    };
+    // the record of chunk cc into LDS buffer cc & 1.  PIPE: once a record was
+    // missing, the lane that stores Gamma_L overwrites it with NaN, so that d
+    // and everything after it turn NaN (a branch around an LDS store only:
+    // one around a loaded register would make the loads' waits drain them).
     auto stash_rec = [&](const Regs &R, int cc) {
       const int buf = cc & 1;
 #pragma unroll
       for (int u = 0; u < NRP; ++u)
         *(uint4 *)(smem_raw + lds_off(lt + NLD * u, buf)) = R.rr[u];
+      static_assert(NRP == 2 && RP - 1 >= NLD, "Gamma_L is the second piece of one lane");
+      if (PIPE && lt == RP - 1 - NLD && sm.bad != 0) sm.gL[buf][0] = __uint_as_float(0x7fc00000u);
     };
     // piece u of the keys of chunk cc (tokens 32 u .. +31), squared, into LDS
     // buffer cc & 1 (rows past the end zero), in the p_slot layout
@@ -391,11 +515,15 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
     // iterations read.  A conditional iteration would leave the loads in
     // flight differently on its two paths, and the waits after them would
     // then drain every load.)
+    // PIPE: loader wave 4 alone makes sure that chunk c+4's record is ready
+    // before the barrier after which all loaders load it (a poll waits for
+    // the wave's loads in flight; the other loader waves keep theirs).
     auto iteration = [&](int c, Regs &free_, const Regs &next) {
       stash_rec(next, c + 1);
       stash_p(next, c + 1, 0);
       __syncthreads();
       stash_p(next, c + 1, 1);
+      if (PIPE && (tid >> 6) == 4 && !await(c + 4)) sm.bad = 1;
       __syncthreads();
       load(free_, c + 4);
       __syncthreads();
@@ -408,6 +536,8 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
           float4{0.f, 0.f, 0.f, 0.f};
     }
     if (NC > 0) {
+      // PIPE: every loader wave waits for the first four records itself
+      if (PIPE && !await(3)) sm.bad = 1;
       load(ra, 0);
       load(rb, 1);
       load(rc, 2);
@@ -578,6 +708,92 @@ walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
   if (d_final && half == 0) d_final[(long)bh * DK + dim] = dreg;
 }
 
+__global__ void __launch_bounds__(WT)
+walk(const bf16 *__restrict__ k, const unsigned char *__restrict__ wrec,
+     const float *__restrict__ d0, int T_, int NC, float *__restrict__ wout,
+     float *__restrict__ d_final, float *__restrict__ log_ratio,
+     float *__restrict__ log_ratio_sum) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  walk_body<false>(smem_raw, blockIdx.x, k, wrec, d0, T_, NC, wout, d_final, log_ratio,
+                   log_ratio_sum, nullptr, 0);
+}
+
+// ---------------------------------------------------------------------------
+// walk_pipe: walk_prep and the walk in one launch.  Workgroups 0 .. BH-1 walk
+// (one per (b, h), as `walk`); the others prepare the records meanwhile, three
+// chunks at a time (one per 256 threads, in lockstep), in the order the walks
+// read them: chunk-major from chunk 0, heads innermost, workgroup j taking
+// rounds j, j + NPW, ... of 3 NPW chunks.  A finished record is announced by
+// writing `epoch` (a value no earlier call used) to its flag.  The preparing
+// workgroups never wait, so the walks, which wait only for them, always
+// finish; being launched first, the walks' workgroups are placed first.
+// ---------------------------------------------------------------------------
+constexpr size_t kPipeSmem = sizeof(WalkSmem) > 3 * sizeof(PrepSmem) ? sizeof(WalkSmem)
+                                                                       : 3 * sizeof(PrepSmem);
+
+__global__ void __launch_bounds__(WT)
+walk_pipe(const bf16 *__restrict__ k, const float *__restrict__ beta, const float *__restrict__ r,
+          float eta, unsigned xf, unsigned char *__restrict__ wrec, const float *__restrict__ d0,
+          int T_, int NC, int BH, float *__restrict__ wout, float *__restrict__ d_final,
+          float *__restrict__ log_ratio, float *__restrict__ log_ratio_sum,
+          unsigned long long *__restrict__ flags, unsigned long long epoch) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  if ((int)blockIdx.x < BH) {
+    walk_body<true>(smem_raw, blockIdx.x, k, wrec, d0, T_, NC, wout, d_final, log_ratio,
+                    log_ratio_sum, flags, epoch);
+    return;
+  }
+  const int j = blockIdx.x - BH, NPW = gridDim.x - BH;
+  // instance inst takes waves 4 inst .. +3; its wave roles are rotated by
+  // inst, so that the waves with the most work in the inverse's later levels
+  // (roles 0 and 1) of the three instances sit on different SIMDs (waves w,
+  // w + 4 and w + 8 of a workgroup share one)
+  const int inst = threadIdx.x >> 8;
+  const int it = ((((threadIdx.x >> 6) & 3) + inst) & 3) * 64 + (threadIdx.x & 63);
+  PrepSmem &ps = reinterpret_cast<PrepSmem *>(smem_raw)[inst];
+  const int total = BH * NC;
+  int base = 3 * j;
+  if (base >= total) return;
+  auto item_at = [&](int b, int &bh, int &c) {
+    const int ii = min(b + inst, total - 1);
+    c = ii / BH;
+    bh = ii % BH;
+  };
+  int bh, c, pbh = 0, pc = 0;
+  bool pvalid = false;  // the previous round's chunk, whose flag is still to be written
+  item_at(base, bh, c);
+  PrepIn cur = prep_load(it, bh, c, k, beta, r, T_), nxt;
+  for (; base < total; base += 3 * NPW) {
+    item_at(base, bh, c);
+    const bool valid = base + inst < total;
+    // Once this round's staging is done, the previous round's record stores
+    // are complete (prep_chunk waits for them before that barrier): its flag
+    // goes out, and the next round's loads (past the last chunk they reread
+    // it).
+    prep_chunk<true>(ps, cur, it, bh, c, valid, r, eta, T_, NC, xf, wrec, [&] {
+      if (pvalid && it == 0)
+        __hip_atomic_store(&flags[(long)pbh * NC + pc], epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      int nbh, ncc;
+      item_at(base + 3 * NPW, nbh, ncc);
+      nxt = prep_load(it, nbh, ncc, k, beta, r, T_);
+    });
+    // the record's stores read the inverse and the vectors from LDS, which the
+    // next round's staging overwrites: every wave is past them first
+    __syncthreads();
+    cur = nxt;
+    pvalid = valid;
+    pbh = bh;
+    pc = c;
+  }
+  // the last round's flag
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (pvalid && it == 0)
+    __hip_atomic_store(&flags[(long)pbh * NC + pc], epoch, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------------------
 // walk_keys: one workgroup per (b, h, chunk).  Threads 0-127 run the in-chunk
 // recurrence for one key dimension each; then all threads store kt rows with
@@ -648,15 +864,65 @@ walk_keys(const bf16 *__restrict__ k, const float *__restrict__ r,
 
 bool walk_supported(int dk, int dtype) { return dk == DK && dtype == 0; }
 
-size_t walk_workspace_bytes(int B, int H, int T) {
+size_t walk_workspace_min_bytes(int B, int H, int T) {
   const size_t nc = (size_t)((T + C - 1) / C);
   return (size_t)B * H * nc * (WREC + WOUT * sizeof(float));
 }
 
-hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, float *wout, hipStream_t s) {
+size_t walk_workspace_bytes(int B, int H, int T) {
+  const size_t nc = (size_t)((T + C - 1) / C);
+  return walk_workspace_min_bytes(B, H, T) + (size_t)B * H * nc * sizeof(unsigned long long);
+}
+
+namespace {
+
+// compute units of the current device (cached per device)
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// A value no earlier walk_pipe launch of this process used, and that memory
+// left by anything else holds only by a 2^-64 chance: a random start, then
+// one step per launch.
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> ctr{[] {
+    std::random_device rd;
+    const unsigned long long t =
+        (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    return (((unsigned long long)rd() << 32) ^ rd()) ^ (t * 0x9E3779B97F4A7C15ull);
+  }()};
+  unsigned long long e;
+  do e = ctr.fetch_add(1, std::memory_order_relaxed); while (e == 0);
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, float *wout, hipStream_t s,
+                       unsigned long long *flags) {
   const int BH = a.B * a.H;
   const int NC = (a.T + C - 1) / C;
   if (BH == 0) return hipSuccess;
+  // One launch when at least as many compute units are left to prepare the
+  // records as there are walks: one workgroup per compute unit.
+  const int cus = device_cus();
+  if (flags && NC > 0 && 2 * BH <= cus) {
+    hipError_t e = hipFuncSetAttribute((const void *)walk_pipe,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPipeSmem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(walk_pipe, dim3((unsigned)cus), dim3(WT), kPipeSmem, s, (const bf16 *)a.k,
+                       a.beta, a.r, a.eta, a.xf, wrec, a.d0, a.T, NC, BH, wout, a.d_final,
+                       a.log_ratio, a.log_ratio_sum, flags, next_epoch());
+    return hipGetLastError();
+  }
   if (NC > 0)
     hipLaunchKernelGGL(walk_prep, dim3((unsigned)(BH * NC)), dim3(256), 0, s, (const bf16 *)a.k,
                        a.beta, a.r, a.eta, a.T, NC, a.xf, wrec);
@@ -669,13 +935,18 @@ hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, float *wout, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_walk_scan(const ScanArgs &a, void *ws, hipStream_t s) {
+hipError_t launch_walk_scan(const ScanArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
   const int BH = a.B * a.H;
   const int NC = (a.T + C - 1) / C;
   if (BH == 0) return hipSuccess;
   unsigned char *wrec = (unsigned char *)ws;
   float *wout = (float *)(wrec + (size_t)BH * NC * WREC);
-  hipError_t e = launch_walk(a, wrec, wout, s);
+  // the ready flags past wout, if the workspace holds them
+  unsigned long long *flags =
+      ws_bytes >= walk_workspace_bytes(a.B, a.H, a.T)
+          ? (unsigned long long *)(wrec + walk_workspace_min_bytes(a.B, a.H, a.T))
+          : nullptr;
+  hipError_t e = launch_walk(a, wrec, wout, s, flags);
   if (e != hipSuccess || NC == 0) return e;
   if (a.xf & kKtF32)
     hipLaunchKernelGGL(walk_keys<float>, dim3((unsigned)(BH * NC)), dim3(256), 0, s,

@@ -122,19 +122,26 @@ extern "C" {
  *   log_ratio [B,H,T]    fp32    out: log rho_t (optional; -inf where rho_t = 0)
  *   workspace  optional device scratch.  With at least
  *              osdn_precond_scan_workspace_bytes(...) bytes (positive for bf16
- *              keys with dk = 128) the walk runs in three launches: the
- *              d-independent part of every chunk (the (I + M)^-1 of the chunked
- *              walk) in parallel, then a short sequential pass per (b,h), then
- *              the keys of every chunk in parallel.  NULL selects a single
- *              kernel per (b,h).
+ *              keys with dk = 128) the walk runs in two launches: one in which
+ *              some workgroups prepare the d-independent part of every chunk
+ *              (the (I + M)^-1 of the chunked walk) while one workgroup per
+ *              (b,h) walks the chunks as they become ready (handed over through
+ *              8-byte flags at the end of the workspace; when B*H exceeds half
+ *              the device's compute units the preparation runs as a launch of
+ *              its own first), then the keys of every chunk in parallel.  With
+ *              8 * B * H * ceil(T / 64) bytes less, the preparation always runs
+ *              as a launch of its own (three launches).  NULL, or less,
+ *              selects a single kernel per (b,h).  Results are bitwise the
+ *              same on all the multi-launch forms.
  */
 int osdn_precond_scan(const void *k, const float *beta, const float *r, const float *d0,
                       float eta, int B, int H, int T, int dk, int dtype,
                       void *k_tilde, float *d_final, float *d_all, float *log_ratio,
                       void *workspace, size_t workspace_bytes, void *stream);
 
-/* Scratch bytes that select osdn_precond_scan's three-launch walk (0 when no
- * such path exists for these arguments); (size_t)-1 if they are invalid. */
+/* Scratch bytes that select osdn_precond_scan's fastest multi-launch walk (0
+ * when no such path exists for these arguments); (size_t)-1 if they are
+ * invalid. */
 size_t osdn_precond_scan_workspace_bytes(int B, int H, int T, int dk, int dtype);
 
 /*
@@ -191,7 +198,9 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  *   workspace      device scratch.  With at least osdn_forward_workspace_bytes(...)
  *                  bytes the fastest path runs; for bf16, dk = dv = 128, chunk 64
  *                  that is a pipeline of launches (walk, chunk-parallel pass,
- *                  sequential state pass), and less scratch (or
+ *                  sequential state pass; the walk and the preparation of its
+ *                  chunks share one launch when B*H is at most half the
+ *                  device's compute units), and less scratch (or
  *                  NULL) selects the single fused kernel.  Other shapes need the
  *                  scratch: the walk hands kt to the chunk pass through it, in
  *                  fp32 whatever the data type (a bf16 kt would cost up to 2^-9
@@ -201,7 +210,7 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  * The path follows from the shapes and the scratch alone, silently;
  * osdn_forward_path names it.  What each costs, measured on MI355X for
  * B = 4, H = 16, T = 4096, dk = dv = 128, chunk 64, bf16:
- *   "split"      about 0.3 ms (the scratch of osdn_forward_workspace_bytes:
+ *   "split"      about 0.27 ms (the scratch of osdn_forward_workspace_bytes:
  *                about 137 MB there, 32.75 KiB per (b, h, 64-token chunk))
  *   "fused"      about 0.5 ms: one kernel redoes each chunk's preparation for
  *                every 32-channel tile of the values

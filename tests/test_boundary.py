@@ -142,9 +142,10 @@ def test_split_workspace_bytes(lib):
     # matrix-core shapes: chunk records (32 KB; the walk records of 17.25 KB use the same
     # space first) and walk results (768 B)
     # per (b, h, chunk of 64); the walk alone: its records (17 KB) plus results
+    # plus an 8-byte ready flag
     assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 0) == 2 * 3 * 3 * (32768 + 768)
     assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 1) == 2 * 3 * 3 * (32768 + 768)
-    assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 0) == 2 * 3 * 3 * (17664 + 768)
+    assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 0) == 2 * 3 * 3 * (17664 + 768 + 8)
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 64, 0) == 0
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 1) == 0
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 48, 0) == (1 << 64) - 1
