@@ -1,4 +1,4 @@
-// The preconditioner walk in three launches (bf16 keys, dk = 128, chunk 64).
+// The preconditioner walk in two or three launches (bf16 keys, dk = 128, chunk 64).
 //
 // Source: gist.science technical summary of "OSDN: Improving Delta Rule with
 // Provable Online Preconditioning in Linear Attention" -- §2.2 (the surrogate
@@ -17,6 +17,10 @@
 //   walk_prep  chunk-parallel: (I + M)^-1 in fp32 and the per-token factors
 //   walk       one workgroup per (b, h), sequential over chunks: three small
 //              products per chunk give g, c_t = alpha_t g_t and the next d_in
+//   walk_pipe  the two in one launch: the walks run on some compute units
+//              while the others prepare the records in the order the walks
+//              read them, handing each over through a flag (the walk, being
+//              sequential, leaves most of the device idle)
 //   walk_keys  chunk-parallel: d_t token by token from the chunk's entry value
 //              and c (the recurrence itself, in fp32), writing kt_t = d_t (.) k_t
 //              and, if asked, d_t
