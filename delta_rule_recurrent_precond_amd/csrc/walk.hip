@@ -756,39 +756,48 @@ walk_pipe(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
   const int it = ((((threadIdx.x >> 6) & 3) + inst) & 3) * 64 + (threadIdx.x & 63);
   PrepSmem &ps = reinterpret_cast<PrepSmem *>(smem_raw)[inst];
   const int total = BH * NC;
-  int base = 3 * j;
-  if (base >= total) return;
-  auto item_at = [&](int b, int &bh, int &c) {
-    const int ii = min(b + inst, total - 1);
-    c = ii / BH;
-    bh = ii % BH;
+  // Round q takes chunks 3 (NPW q + j) + inst: chunk-major, heads innermost.
+  auto item_of = [&](int q) { return 3 * (NPW * q + j) + inst; };
+  auto busy = [&](int q) { return 3 * (NPW * q + j) < total; };
+  auto locate = [&](int item, int &bh_, int &c_) {
+    const int ii = min(item, total - 1);  // past the last chunk: reread it, store nothing
+    c_ = ii / BH;
+    bh_ = ii % BH;
   };
   int bh, c, pbh = 0, pc = 0;
   bool pvalid = false;  // the previous round's chunk, whose flag is still to be written
-  item_at(base, bh, c);
+  locate(item_of(0), bh, c);
   PrepIn cur = prep_load(it, bh, c, k, beta, r, T_), nxt;
-  for (; base < total; base += 3 * NPW) {
-    item_at(base, bh, c);
-    const bool valid = base + inst < total;
+  for (int q = 0; busy(q); ++q) {
+    const int item = item_of(q);
+    const bool valid = item < total;
+    locate(item, bh, c);
     // Once this round's staging is done, the previous round's record stores
     // are complete (prep_chunk waits for them before that barrier): its flag
-    // goes out, and the next round's loads (past the last chunk they reread
-    // it).
+    // goes out, and the next round's loads.
     prep_chunk<true>(ps, cur, it, bh, c, valid, r, eta, T_, NC, xf, wrec, [&] {
       if (pvalid && it == 0)
         __hip_atomic_store(&flags[(long)pbh * NC + pc], epoch, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       int nbh, ncc;
-      item_at(base + 3 * NPW, nbh, ncc);
+      locate(item_of(q + 1), nbh, ncc);
       nxt = prep_load(it, nbh, ncc, k, beta, r, T_);
     });
-    // the record's stores read the inverse and the vectors from LDS, which the
-    // next round's staging overwrites: every wave is past them first
-    __syncthreads();
     cur = nxt;
-    pvalid = valid;
-    pbh = bh;
-    pc = c;
+    // the record's stores read the inverse and the vectors from LDS, which the
+    // next round's staging overwrites: every wave is past them first.  The
+    // first round's flags go out at once: the walks are waiting for them.
+    if (q == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (q == 0) {
+      if (valid && it == 0)
+        __hip_atomic_store(&flags[(long)bh * NC + c], epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      pvalid = valid;
+      pbh = bh;
+      pc = c;
+    }
   }
   // the last round's flag
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
