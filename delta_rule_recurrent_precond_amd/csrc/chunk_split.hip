@@ -62,6 +62,7 @@
 #include "launch.h"
 #include "mfma.h"
 #include "walk.h"
+#include "walk_device.h"
 
 namespace osdn {
 
@@ -115,33 +116,63 @@ constexpr int KP = 136;  // padded row (halves) of the staged [64][128] tiles
 // decays enter A, P and the S-update operands, and its row factors go to the
 // record.  GK: the per-channel gate, as described at the top.  xf & kGateLogits:
 // beta and r arrive as logits.
+// The LDS of one chunk_prep instance.  q is needed only for the scores; the
+// blocks of A and T then reuse its space.  QT (write keys of their own, no
+// per-channel gate): the products of k with kt are formed first and held in
+// registers, then q takes k's tile, then the blocks take it: two [64][128]
+// tiles in all (36 KB, four workgroups per CU, where a tile of its own for q
+// allows three)
 template <int MODE, bool NORM, bool GATED, bool GK>
-// Four workgroups per CU where the LDS allows it (the two-tile instances) and
-// the registers fit a quarter of the file without spilling (not with raw q, k)
-__global__ void __launch_bounds__(256, (!GK && !NORM && MODE != kDeltaNet) ? 4 : 1)
-chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
-           const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
-           unsigned char *__restrict__ ws, const float *__restrict__ r,
-           const float *__restrict__ wout, const float *__restrict__ alpha, unsigned xf) {
-  // q is needed only for the scores; the blocks of A and T then reuse its
-  // space.  QT (write keys of their own, no per-channel gate): the products of
-  // k with kt are formed first and held in registers, then q takes k's tile,
-  // then the blocks take it: two [64][128] tiles in all (36 KB, four
-  // workgroups per CU, where a tile of its own for q allows three)
-  constexpr bool QT = !GK && MODE != kDeltaNet;
-  __shared__ __align__(16) f16 Ks[C * KP];          // k (QT: then q, then the blocks)
-  __shared__ __align__(16) f16 Kts[C * KP];         // kt / ds (kt = k: unused)
-  __shared__ __align__(16) unsigned char QF[QT ? 16 : C * KP * 2];
+struct alignas(16) PrepLds {
+  static constexpr bool QT = !GK && MODE != kDeltaNet;
+  // (arrays an instance does not use keep a token size)
+  f16 Ks[C * KP];                                        // k (QT: then q, then the blocks)
+  f16 Kts[(MODE == kDeltaNet && !GK) ? 8 : C * KP];      // kt / ds
+  alignas(16) unsigned char QF[QT ? 16 : C * KP * 2];
+  float bs[C];
+  float cs[(MODE == kOsdn || GATED) ? C : 4];            // kOsdn: c_t (GATED: then xdl)
+  float rs[MODE == kOsdn ? C : 4];                       // kOsdn: r_t
+  float sk[NORM ? C : 4], sq_[(NORM && MODE != kOsdn) ? C : 4];  // 1 / ||k_t||, 1 / ||q_t||
+  float lga[GATED ? C : 4];                              // GATED: lg_t, the running sum of log2 alpha
+  // GK: the diagonal blocks of A and P (fp32 sums); the products of alpha over
+  // each 16-token block, per key dimension [block][i] (alpha itself is read
+  // from global memory where it is used)
+  float Adg[GK ? 4 * 16 * LDF : 4], Pdg[GK ? 4 * 16 * LDF : 4];
+  alignas(16) float Bk[GK ? 4 * DK : 4];
+  alignas(16) f16 Zrow[GK ? DK : 8];  // GK: zeros
+  float red[4];
+  // XN with kt = k: the chunk's largest |k| and |q| per wave (kOsdn passes them
+  // through its kt tile instead, which nothing writes before the staging)
+  float nred_[(NORM && !GK && MODE != kOsdn) ? 8 : 1];
+};
+
+// One chunk (bh, c) by the 256 threads tid = 0..255 of the caller (every
+// thread of the workgroup takes part in the same barriers, so several
+// instances may share a workgroup).  COH: the walk's results (wout) are read
+// with device-scope loads, the walk having written them in the same launch;
+// poison: they are not known to be complete (the chunk's keys turn NaN).
+template <int MODE, bool NORM, bool GATED, bool GK, bool COH>
+__device__ __forceinline__ void chunk_prep_body(
+    PrepLds<MODE, NORM, GATED, GK> &Ld, const int tid, const int bh, const int c,
+    const bool poison, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+    const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
+    unsigned char *__restrict__ ws, const float *__restrict__ r, const float *__restrict__ wout,
+    const float *__restrict__ alpha, unsigned xf) {
+  constexpr bool QT = PrepLds<MODE, NORM, GATED, GK>::QT;
+  f16 *const Ks = Ld.Ks;
+  f16 *const Kts = Ld.Kts;
+  unsigned char *const QF = Ld.QF;
   f16 *Qs = QT ? Ks : (f16 *)QF;                                       // q
   unsigned char *const Bl = QT ? (unsigned char *)Ks : QF;
   float(*Fd)[16][LDF] = (float(*)[16][LDF])Bl;                         // diagonal blocks of A
   f16(*Aoff)[16][LDT] = (f16(*)[16][LDT])(Bl + 4 * 16 * LDF * 4);       // off-diagonal blocks of A
   f16(*Tdg)[16][LDT] = (f16(*)[16][LDT])(Bl + 4 * 16 * LDF * 4 + 6 * 16 * LDT * 2);  // diag of T
   static_assert(4 * 16 * LDF * 4 + 10 * 16 * LDT * 2 <= C * KP * 2, "A and T blocks fit");
-  __shared__ float bs[C];
-  __shared__ float cs[C], rs[C];  // kOsdn: c_t and r_t
-  __shared__ float sk[C], sq_[MODE == kOsdn ? 1 : C];  // NORM: 1 / ||k_t||, 1 / ||q_t||
-  __shared__ float lga[C];        // GATED: lg_t, the running sum of log2 alpha
+  float *const bs = Ld.bs, *const cs = Ld.cs, *const rs = Ld.rs;
+  float *const sk = Ld.sk, *const sq_ = Ld.sq_, *const lga = Ld.lga;
+  float *const Adg = Ld.Adg, *const Pdg = Ld.Pdg, *const Bk = Ld.Bk;
+  f16 *const Zrow = Ld.Zrow;
+  float *const red = Ld.red, *const nred_ = Ld.nred_;
   // Two arrays share space, so that the raw-input gated pass fits three
   // workgroups per CU: 1 / ||q_t|| (last read by the record's factors) lies in
   // kt's tile past the 512 bytes that carry d_32 (kOsdn writes kt only after
@@ -149,25 +180,12 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // recurrence is done.
   float *const sq = MODE == kOsdn ? (float *)Kts + 128 : sq_;
   float *const xdl = cs;          // GATED: gamma_L / gamma_t
-  // GK: the diagonal blocks of A and P (fp32 sums); the products of alpha over
-  // each 16-token block, per key dimension [block][i] (alpha itself is read
-  // from global memory where it is used)
-  __shared__ float Adg[GK ? 4 * 16 * LDF : 4], Pdg[GK ? 4 * 16 * LDF : 4];
-  __shared__ __align__(16) float Bk[GK ? 4 * DK : 4];
-  __shared__ __align__(16) f16 Zrow[GK ? DK : 8];  // GK: zeros
-  __shared__ float red[4];
-  // XN with kt = k: the chunk's largest |k| and |q| per wave (kOsdn passes them
-  // through its kt tile instead, which nothing writes before the staging)
-  __shared__ float nred_[(NORM && !GK && MODE != kOsdn) ? 8 : 1];
+  auto ld_wout = [&](const float *p) {
+    return COH ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *p;
+  };
 
-  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  // chunk-major, last chunk first, heads innermost: the state kernel reads every
-  // head's chunk 0 first, which is then the freshest data in the caches; with
-  // B*H a multiple of 8 a head runs on the XCD its state-kernel tiles use
-  const int BHn = gridDim.x / NC;
-  const int c = NC - 1 - (int)(blockIdx.x / BHn), bh = blockIdx.x % BHn;
   const long tok0 = (long)bh * T_ + (long)c * C;
   const int L = min(C, T_ - c * C);
   unsigned char *rec = ws + ((long)bh * NC + c) * (GK ? RECK : REC);
@@ -195,7 +213,9 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
   // kOsdn: the chunk's entry d of dimension tid (threads 0-127), loaded here so
   // that its latency passes while the chunk is staged, not on the d chain
-  const float d_entry = MODE == kOsdn ? wout[((long)bh * NC + c) * WOUT + min(tid, DK - 1)] : 0.f;
+  const float d_entry = MODE != kOsdn ? 0.f
+                        : poison    ? __uint_as_float(0x7fc00000u)
+                                    : ld_wout(&wout[((long)bh * NC + c) * WOUT + min(tid, DK - 1)]);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = tid + 256 * u, t = p >> 4;
@@ -216,7 +236,7 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     bs[tid] = tid < L ? ((xf & kGateLogits) ? sigmoid_gate(bv) : bv) : 0.f;
   }
   if (MODE == kOsdn && tid < C) {
-    cs[tid] = tid < L ? wout[((long)bh * NC + c) * WOUT + DK + tid] : 0.f;
+    cs[tid] = tid < L ? ld_wout(&wout[((long)bh * NC + c) * WOUT + DK + tid]) : 0.f;
     const float rv = r ? r[tok0 + min(tid, L - 1)] : 1.0f;
     rs[tid] = (r && tid < L) ? ((xf & kGateLogits) ? sigmoid_gate(rv) : rv) : 1.0f;
   }
@@ -818,6 +838,92 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
 }
 
+// One workgroup of 4 waves per (b, h, chunk), chunk-major, last chunk first,
+// heads innermost: the state kernel reads every head's chunk 0 first, which is
+// then the freshest data in the caches; with B*H a multiple of 8 a head runs on
+// the XCD its state-kernel tiles use.  The grid may cover only the last chunks
+// of every head (BHn heads): the others were prepared elsewhere.
+template <int MODE, bool NORM, bool GATED, bool GK>
+// Four workgroups per CU where the LDS allows it (the two-tile instances) and
+// the registers fit a quarter of the file without spilling (not with raw q, k)
+__global__ void __launch_bounds__(256, (!GK && !NORM && MODE != kDeltaNet) ? 4 : 1)
+chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+           const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
+           int BHn, unsigned char *__restrict__ ws, const float *__restrict__ r,
+           const float *__restrict__ wout, const float *__restrict__ alpha, unsigned xf) {
+  __shared__ PrepLds<MODE, NORM, GATED, GK> Ld;
+  const int c = NC - 1 - (int)(blockIdx.x / BHn), bh = blockIdx.x % BHn;
+  chunk_prep_body<MODE, NORM, GATED, GK, false>(Ld, threadIdx.x, bh, c, false, q, k, kt_in, beta,
+                                                T_, NC, ws, r, wout, alpha, xf);
+}
+
+// ---------------------------------------------------------------------------
+// walk_chunk_pipe: the one-launch walk (the walks in workgroups 0 .. BH-1, the
+// others preparing their records) in which the preparing workgroups, once
+// their records are done, run chunk_prep for the first NCP chunks of every
+// head while the walks finish: the walks leave most of the device idle at
+// their end.  A walk publishes its results (device-scope stores, and a flag
+// per chunk once a chunk's are complete); a chunk is prepared once its flag is
+// set.  The walk records lie in the chunk records' slots (stride REC), with
+// their two flags past them: chunk_prep overwrites a slot only after the walk
+// has passed its chunk, when nothing reads the walk record or the flags any
+// more.  chunk_prep's own launch then covers chunks NCP .. NC-1.  The
+// chunk_prep items (chunk-major, heads innermost) continue the walk records'
+// sequence of rounds from the next multiple of three: round q of workgroup j
+// takes items 3 (NPW q + j) + inst of the whole sequence, so every workgroup
+// runs about the same number of rounds.  A round whose items run past the
+// last one repeats it (the same bytes written twice).  Only the plain forward
+// (no input transforms, no state gate) takes this form.
+// ---------------------------------------------------------------------------
+using TailLds = PrepLds<kOsdn, false, false, false>;
+constexpr size_t kTailSmem =
+    wd::kPipeSmem > 3 * sizeof(TailLds) ? wd::kPipeSmem : 3 * sizeof(TailLds);
+
+__global__ void __launch_bounds__(wd::WT)
+walk_chunk_pipe(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+                const float *__restrict__ beta, const float *__restrict__ r, float eta,
+                unsigned xf, unsigned char *__restrict__ ws, const float *__restrict__ d0, int T_,
+                int NC, int NCP, int BH, float *__restrict__ wout, float *__restrict__ d_final,
+                float *__restrict__ log_ratio_sum, unsigned long long epoch) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  unsigned long long *flags = (unsigned long long *)(ws + WREC);
+  constexpr int fstride = (int)(REC / 8);
+  if ((int)blockIdx.x < BH) {
+    wd::walk_body<true, true>(smem_raw, blockIdx.x, k, ws, REC, d0, T_, NC, wout, d_final,
+                              nullptr, log_ratio_sum, flags, fstride, epoch);
+    return;
+  }
+  const int j = blockIdx.x - BH, NPW = gridDim.x - BH;
+  const int q0 =
+      wd::pipe_prep(smem_raw, j, NPW, BH, k, beta, r, eta, xf, ws, REC, T_, NC, flags, fstride, epoch);
+  const int inst = threadIdx.x >> 8;
+  TailLds &Ld = reinterpret_cast<TailLds *>(smem_raw)[inst];
+  const int first = (BH * NC + 2) / 3 * 3;  // where the chunk_prep items start in the sequence
+  const int total = BH * NCP;
+  for (int qr = q0; 3 * (NPW * qr + j) - first < total; ++qr) {
+    const int ii = min(3 * (NPW * qr + j) - first + inst, total - 1);
+    const int c = ii / BH, bh = ii % BH;
+    // the walk past chunk c (a bounded wait; the walk is far ahead by now)
+    bool ok = false;
+    const unsigned long long *f = &flags[((long)bh * NC + c) * fstride + 1];
+    for (int i = 0; i < wd::kPollLimit; ++i) {
+      if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) {
+        ok = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    // (the thread index through an opaque copy each round, so that the
+    // compiler does not hoist the body's lane-dependent addresses out of the
+    // loop and keep them live across it)
+    int tid = threadIdx.x & 255;
+    asm volatile("" : "+v"(tid));
+    chunk_prep_body<kOsdn, false, false, false, true>(Ld, tid, bh, c, !ok, q, k, nullptr, beta, T_,
+                                                      NC, ws, r, wout, nullptr, xf);
+    __syncthreads();  // the next round's staging overwrites this round's LDS
+  }
+}
+
 // ---------------------------------------------------------------------------
 // chunk_state: one workgroup of 12 waves per (b, h, 32 value channels),
 // sequential over chunks.  Per 16-channel sub-tile sn:
@@ -1385,35 +1491,39 @@ hipError_t launch_state(const ChunkArgs &a, int NC, const void *ws, float *log_r
 }
 
 template <int MODE, bool NORM, bool GATED, bool GK>
-void launch_prep_t(int BH, int NC, hipStream_t s, const void *q, const void *k, const void *kt,
-                   const float *beta, int T, unsigned char *rec, const float *r,
+void launch_prep_t(int BH, int NC, int nck, hipStream_t s, const void *q, const void *k,
+                   const void *kt, const float *beta, int T, unsigned char *rec, const float *r,
                    const float *wout, const float *alpha, unsigned xf) {
-  hipLaunchKernelGGL((chunk_prep<MODE, NORM, GATED, GK>), dim3((unsigned)(BH * NC)), dim3(256), 0,
-                     s, (const bf16 *)q, (const bf16 *)k, (const bf16 *)kt, beta, T, NC, rec, r,
+  if (nck <= 0) return;
+  hipLaunchKernelGGL((chunk_prep<MODE, NORM, GATED, GK>), dim3((unsigned)(BH * nck)), dim3(256), 0,
+                     s, (const bf16 *)q, (const bf16 *)k, (const bf16 *)kt, beta, T, NC, BH, rec, r,
                      wout, alpha, xf);
 }
 
-// chunk_prep over every chunk of every head; kGiven takes no input transforms
+// chunk_prep over the last nck chunks (all by default) of every head; kGiven
+// takes no input transforms
 template <int MODE>
 hipError_t launch_prep(int BH, int NC, hipStream_t s, const void *q, const void *k,
                        const void *kt, const float *beta, int T, unsigned char *rec,
-                       const float *r, const float *wout, const float *alpha, unsigned xf) {
+                       const float *r, const float *wout, const float *alpha, unsigned xf,
+                       int nck = -1) {
   if (NC <= 0) return hipSuccess;
+  if (nck < 0) nck = NC;
   constexpr bool TX = MODE != kGiven;  // instances with the input transforms
   const bool norm = TX && (xf & kNormQK);
   if (per_channel(alpha, xf)) {
     if (norm)
-      launch_prep_t<MODE, TX, false, true>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+      launch_prep_t<MODE, TX, false, true>(BH, NC, nck, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
     else
-      launch_prep_t<MODE, false, false, true>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+      launch_prep_t<MODE, false, false, true>(BH, NC, nck, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
   } else if (norm && alpha) {
-    launch_prep_t<MODE, TX, true, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+    launch_prep_t<MODE, TX, true, false>(BH, NC, nck, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
   } else if (norm) {
-    launch_prep_t<MODE, TX, false, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+    launch_prep_t<MODE, TX, false, false>(BH, NC, nck, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
   } else if (alpha) {
-    launch_prep_t<MODE, false, true, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+    launch_prep_t<MODE, false, true, false>(BH, NC, nck, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
   } else {
-    launch_prep_t<MODE, false, false, false>(BH, NC, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
+    launch_prep_t<MODE, false, false, false>(BH, NC, nck, s, q, k, kt, beta, T, rec, r, wout, alpha, xf);
   }
   return hipGetLastError();
 }
@@ -1430,6 +1540,24 @@ size_t split_forward_workspace_bytes(int B, int H, int T, bool gate_channels) {
 // from the walk's results, the state kernel -- in that order on one stream.
 // (Running chunk_prep of finished segments beside the walk on a second stream
 // was measured: the cross-stream waits and the sharing of CUs ate the overlap.)
+// How many of every head's first chunks walk_chunk_pipe prepares: what its
+// preparing workgroups can do between finishing the walk's records and the
+// walks' end.  In units of a round of preparation (three chunks per
+// workgroup, about 8 us on MI355X; the walk takes about 1.05 us a chunk and
+// about 10 us to start), less one round of margin.
+int tail_chunks(int BH, int NC, int cus) {
+#ifdef OSDN_TAIL_CHUNKS
+  return min(OSDN_TAIL_CHUNKS, max(NC - 2, 0));
+#else
+  const int npw = cus - BH;
+  const double round_us = 8.0, walk_us = 10.0 + 1.05 * NC;
+  const double prep_rounds = (double)BH * NC / (3.0 * npw);
+  const double tail_rounds = walk_us / round_us - prep_rounds - 1.0;
+  if (tail_rounds <= 0) return 0;
+  return min((int)(tail_rounds * 3.0 * npw / BH), max(NC - 2, 0));
+#endif
+}
+
 hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
@@ -1449,13 +1577,30 @@ hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   // the gate leaves the preconditioner walk unchanged
   ScanArgs sa{a.k, a.beta, a.r, a.d0, a.eta, a.B, a.H, a.T, a.dk, a.dtype, 0, nullptr,
               a.d_final, nullptr, nullptr, a.log_ratio_sum, a.xf};
-  // the walk's ready flags sit past its records, in space the chunk records
-  // take only later
-  unsigned long long *flags = (unsigned long long *)(rec + (size_t)BH * NC * WREC);
-  static_assert(WREC % 8 == 0 && REC - WREC >= 8, "flags fit past the walk records");
-  hipError_t e = launch_walk(sa, rec, wout, s, flags);
+  // The walk's records take the chunk records' slots (stride REC), each with
+  // its ready flag and its walked flag past it: chunk_prep overwrites a slot
+  // only once the walk is done with it.
+  static_assert(WREC % 8 == 0 && REC - WREC >= 16, "the flags fit past a walk record");
+  unsigned long long *flags = (unsigned long long *)(rec + WREC);
+  const int cus = device_cus();
+  const bool one_launch = NC > 0 && 2 * BH <= cus;
+  const int ncp = one_launch && !a.alpha && !(a.xf & (kNormQK | kGateLogits)) ? tail_chunks(BH, NC, cus)
+                                                                              : 0;
+  hipError_t e;
+  if (ncp > 0) {
+    e = hipFuncSetAttribute((const void *)walk_chunk_pipe,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTailSmem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(walk_chunk_pipe, dim3((unsigned)cus), dim3(wd::WT), kTailSmem, s,
+                       (const bf16 *)a.q, (const bf16 *)a.k, a.beta, a.r, a.eta, a.xf, rec, a.d0,
+                       a.T, NC, ncp, BH, wout, a.d_final, a.log_ratio_sum, next_epoch());
+    e = hipGetLastError();
+  } else {
+    e = launch_walk(sa, rec, REC, wout, s, flags, (int)(REC / 8));
+  }
   if (e != hipSuccess) return e;
-  e = launch_prep<kOsdn>(BH, NC, s, a.q, a.k, nullptr, a.beta, a.T, rec, a.r, wout, a.alpha, a.xf);
+  e = launch_prep<kOsdn>(BH, NC, s, a.q, a.k, nullptr, a.beta, a.T, rec, a.r, wout, a.alpha, a.xf,
+                         NC - ncp);
   if (e != hipSuccess) return e;
   return launch_state(ca, NC, ws, nullptr, s);
 }

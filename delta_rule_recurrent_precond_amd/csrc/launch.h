@@ -88,14 +88,19 @@ hipError_t launch_fused_scan(const ScanArgs &a, hipStream_t s);
 // log_ratio and log_ratio_sum of `a`; launch_walk_scan adds walk_keys, which
 // writes a.k_tilde and a.d_all, with wrec and wout carved from ws (at least
 // walk_workspace_min_bytes; with walk_workspace_bytes the flags follow them).
-// flags: if given (B*H*ceil(T/64) 8-byte words, any contents), walk_prep and
-// the walk may run as one launch (walk_pipe) in which the records are
-// announced through these flags.
+// The record of (b h, chunk c) lies at wrec + (bh NC + c) rstride (rstride >=
+// WREC).  flags: if given (words flags[(bh NC + c) fstride], any contents),
+// walk_prep and the walk may run as one launch (walk_pipe) in which the
+// records are announced through these flags.
 bool walk_supported(int dk, int dtype);
 size_t walk_workspace_bytes(int B, int H, int T);
 size_t walk_workspace_min_bytes(int B, int H, int T);
-hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, float *wout, hipStream_t s,
-                       unsigned long long *flags = nullptr);
+hipError_t launch_walk(const ScanArgs &a, unsigned char *wrec, size_t rstride, float *wout,
+                       hipStream_t s, unsigned long long *flags = nullptr, int fstride = 1);
+// compute units of the current device; a value no earlier one-launch walk of
+// this process used (for its flags)
+int device_cus();
+unsigned long long next_epoch();
 hipError_t launch_walk_scan(const ScanArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
 
 // The forward in four launches (bf16, dk = dv = 128, chunk 64): the walk, then
