@@ -445,7 +445,7 @@ def main():
                                            traffic=stored_traffic("osdn_fused_forward",
                                                                   args.workload)),
             "deltanet_mode_single_kernel": entry(t_dn_single, fpath(False, single=True)),
-            "precond_scan": entry(t_scan, "walk_prep+walk+walk_keys" if sws_n else "single",
+            "precond_scan": entry(t_scan, "walk_pipe+walk_keys" if sws_n else "single",
                                   hbm_frac=algorithmic_bytes(w, "scan") / (ms_scan * 1e-3)
                                   / (HBM_PEAK_GBS * 1e9),
                                   traffic=stored_traffic("osdn_precond_scan_split",
@@ -481,7 +481,8 @@ def main():
 
     # Against the HBM roofline.  On the matrix-core shapes the unit is one
     # osdn_forward call: the single fused kernel, or the pipeline of launches
-    # (walk_prep, walk, chunk_prep, chunk_state) timed as one call on its stream,
+    # (the walk with its preparation, chunk_prep, chunk_state) timed as one call
+    # on its stream,
     # with the method's algorithmic bytes (q, k, v, beta, r in; o out).  The
     # two-launch path is dominated by the chunkwise pass.
     if path == "split":
