@@ -94,6 +94,9 @@ walk_pipe(const bf16 *__restrict__ k, const float *__restrict__ beta, const floa
 // 16-byte stores.  KT is the type of kt (bf16, or fp32 for the two-phase
 // forward); xf: kNormQK -- kt is formed from the normalised key k_t / ||k_t||
 // (the scale from the stored values, fp32); kGateLogits -- r arrives as logits.
+// A bf16 kt is written over the staged keys (each element by the thread that
+// read it, after reading it): 17 KB of LDS, so that eight workgroups fit on a
+// CU and hide each other's load latency.
 // ---------------------------------------------------------------------------
 template <typename KT>
 __global__ void __launch_bounds__(256)
@@ -102,8 +105,11 @@ walk_keys(const bf16 *__restrict__ k, const float *__restrict__ r,
           float *__restrict__ d_all, unsigned xf) {
   constexpr int KTP = 16 / sizeof(KT);  // elements of kt per 16-byte piece
   constexpr int KTR = DK + KTP;         // padded kt row in LDS
-  __shared__ __align__(16) bf16 Kb[C * KP];
-  __shared__ __align__(16) KT Kt[C * KTR];
+  constexpr bool IN_PLACE = sizeof(KT) == sizeof(bf16);
+  static_assert(!IN_PLACE || KTR == KP, "kt rows lie over the key rows");
+  __shared__ __align__(16) unsigned char kbuf[C * KP * sizeof(bf16) + (IN_PLACE ? 0 : C * KTR * sizeof(KT))];
+  bf16 *Kb = (bf16 *)kbuf;
+  KT *Kt = IN_PLACE ? (KT *)kbuf : (KT *)(kbuf + C * KP * sizeof(bf16));
   __shared__ float cs[C], rs[C], sc[C];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
