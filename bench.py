@@ -141,6 +141,16 @@ def time_launches(fn, steps, warmup, torch):
             "max": ts[-1], "n": n}
 
 
+def scan_path(w, ws_bytes):
+    """The launches osdn_precond_scan runs: one (walk_scan_pipe) when the
+    scratch holds the flags and B*H is at most half the compute units, three
+    with the scratch otherwise, else one kernel per (b,h)."""
+    if not ws_bytes:
+        return "single"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return "walk_scan_pipe" if 2 * w.B * w.H <= cus else "walk_prep+walk+walk_keys"
+
+
 def timing_fields(t):
     """The spread of a time_launches result, for the JSON line."""
     return {"ms": t["ms"], "ms_mean": t["mean"], "ms_min": t["min"], "ms_max": t["max"],
@@ -445,7 +455,7 @@ def main():
                                            traffic=stored_traffic("osdn_fused_forward",
                                                                   args.workload)),
             "deltanet_mode_single_kernel": entry(t_dn_single, fpath(False, single=True)),
-            "precond_scan": entry(t_scan, "walk_pipe+walk_keys" if sws_n else "single",
+            "precond_scan": entry(t_scan, scan_path(w, sws_n),
                                   hbm_frac=algorithmic_bytes(w, "scan") / (ms_scan * 1e-3)
                                   / (HBM_PEAK_GBS * 1e9),
                                   traffic=stored_traffic("osdn_precond_scan_split",

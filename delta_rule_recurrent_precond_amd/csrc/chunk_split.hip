@@ -900,19 +900,21 @@ walk_chunk_pipe(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   TailLds &Ld = reinterpret_cast<TailLds *>(smem_raw)[inst];
   const int first = (BH * NC + 2) / 3 * 3;  // where the chunk_prep items start in the sequence
   const int total = BH * NCP;
+  bool gave_up = false;  // once a wait ran out, later items do not wait
   for (int qr = q0; 3 * (NPW * qr + j) - first < total; ++qr) {
     const int ii = min(3 * (NPW * qr + j) - first + inst, total - 1);
     const int c = ii / BH, bh = ii % BH;
     // the walk past chunk c (a bounded wait; the walk is far ahead by now)
     bool ok = false;
     const unsigned long long *f = &flags[((long)bh * NC + c) * fstride + 1];
-    for (int i = 0; i < wd::kPollLimit; ++i) {
+    for (int i = 0; !gave_up && i < wd::kPollLimit; ++i) {
       if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) {
         ok = true;
         break;
       }
       __builtin_amdgcn_s_sleep(8);
     }
+    gave_up = !ok;
     // (the thread index through an opaque copy each round, so that the
     // compiler does not hoist the body's lane-dependent addresses out of the
     // loop and keep them live across it)

@@ -87,7 +87,8 @@ hipError_t launch_fused_scan(const ScanArgs &a, hipStream_t s);
 // entry d and c of every chunk (wout, WOUT floats each), plus d_final,
 // log_ratio and log_ratio_sum of `a`; launch_walk_scan adds walk_keys, which
 // writes a.k_tilde and a.d_all, with wrec and wout carved from ws (at least
-// walk_workspace_min_bytes; with walk_workspace_bytes the flags follow them).
+// walk_workspace_min_bytes; with walk_workspace_bytes two flags per chunk
+// follow them, and the three may run as one launch, walk_scan_pipe).
 // The record of (b h, chunk c) lies at wrec + (bh NC + c) rstride (rstride >=
 // WREC).  flags: if given (words flags[(bh NC + c) fstride], any contents),
 // walk_prep and the walk may run as one launch (walk_pipe) in which the

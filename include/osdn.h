@@ -122,15 +122,15 @@ extern "C" {
  *   log_ratio [B,H,T]    fp32    out: log rho_t (optional; -inf where rho_t = 0)
  *   workspace  optional device scratch.  With at least
  *              osdn_precond_scan_workspace_bytes(...) bytes (positive for bf16
- *              keys with dk = 128) the walk runs in two launches: one in which
- *              some workgroups prepare the d-independent part of every chunk
- *              (the (I + M)^-1 of the chunked walk) while one workgroup per
- *              (b,h) walks the chunks as they become ready (handed over through
- *              8-byte flags at the end of the workspace; when B*H exceeds half
- *              the device's compute units the preparation runs as a launch of
- *              its own first), then the keys of every chunk in parallel.  With
- *              8 * B * H * ceil(T / 64) bytes less, the preparation always runs
- *              as a launch of its own (three launches).  NULL, or less,
+ *              keys with dk = 128) the walk runs in one launch: some
+ *              workgroups prepare the d-independent part of every chunk (the
+ *              (I + M)^-1 of the chunked walk) while one workgroup per (b,h)
+ *              walks the chunks as they become ready, and the preparing
+ *              workgroups then write the keys of each chunk the walk has
+ *              passed (handed over through two 8-byte flags per chunk at the
+ *              end of the workspace).  When B*H exceeds half the device's
+ *              compute units, or with 16 * B * H * ceil(T / 64) bytes less,
+ *              the three run as launches of their own.  NULL, or less,
  *              selects a single kernel per (b,h).  Results are bitwise the
  *              same on all the multi-launch forms.
  */

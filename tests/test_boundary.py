@@ -145,7 +145,7 @@ def test_split_workspace_bytes(lib):
     # plus an 8-byte ready flag
     assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 0) == 2 * 3 * 3 * (32768 + 768)
     assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 1) == 2 * 3 * 3 * (32768 + 768)
-    assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 0) == 2 * 3 * 3 * (17664 + 768 + 8)
+    assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 0) == 2 * 3 * 3 * (17664 + 768 + 16)
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 64, 0) == 0
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 1) == 0
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 48, 0) == (1 << 64) - 1

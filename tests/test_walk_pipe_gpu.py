@@ -1,13 +1,14 @@
-"""The walk's one-launch form (walk_prep and the walk in one launch, the
-records handed over through ready flags in the workspace) against the
-two-launch walk: the same arithmetic, so every output agrees bit for bit.
+"""The walk's one-launch forms against the walk in three launches (walk_prep,
+the walk, walk_keys): the same arithmetic, so every output agrees bit for bit.
 
-osdn_precond_scan takes the one-launch form with the workspace of
-osdn_precond_scan_workspace_bytes and the two-launch form with 8 bytes per
-(b, h, chunk) less; its d_all and k_tilde expose the walk's result for every
-chunk.  Also calls that reuse one workspace, whose flags then hold earlier
-calls' values, and repeated calls (a race between the launch's workgroups
-would show as a difference between them)."""
+osdn_precond_scan runs in one launch (walk_prep, the walk and walk_keys, the
+records and the walk's results handed over through two flags per chunk in
+the workspace) with the workspace of osdn_precond_scan_workspace_bytes, and
+in three launches with 16 bytes per (b, h, chunk) less; its d_all and k_tilde
+expose the walk's result for every chunk.  osdn_forward runs walk_prep and the
+walk in one launch.  Also calls that reuse one workspace, whose flags then
+hold earlier calls' values, and repeated calls (a race between the launch's
+workgroups would show as a difference between them)."""
 import pytest
 import torch
 
@@ -33,18 +34,20 @@ def _inputs(B, H, T, seed, apf=True):
     return W.generate(w).to("cuda")
 
 
-def _scan(dev, one_launch):
+def _scan(dev, one_launch, want=True, ws=None):
     B, H, T, dk = dev.k.shape
-    full = osdn.precond_scan_workspace_bytes(B, H, T, dk, 0)
-    n = full if one_launch else full - 8 * B * H * ((T + 63) // 64)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
-    return osdn.precond_scan(dev.k, dev.beta, dev.r, eta=0.05, want_d_all=True,
-                             want_log_ratio=True, workspace=ws)
+    if ws is None:
+        full = osdn.precond_scan_workspace_bytes(B, H, T, dk, 0)
+        n = full if one_launch else full - 16 * B * H * ((T + 63) // 64)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    return osdn.precond_scan(dev.k, dev.beta, dev.r, eta=0.05, want_d_all=want,
+                             want_log_ratio=want, workspace=ws)
 
 
 def _equal(a, b, label):
     for key in ("k_tilde", "d_final", "d_all", "log_ratio"):
-        assert torch.equal(a[key], b[key]), (label, key)
+        if key in a or key in b:
+            assert torch.equal(a[key], b[key]), (label, key)
 
 
 # (B, H, T): one chunk, a single token, ragged tails, fewer chunks than the
@@ -62,6 +65,27 @@ def test_one_launch_walk_matches_two_launch_bitwise(B, H, T):
     b = _scan(dev, False)
     torch.cuda.synchronize()
     _equal(a, b, (B, H, T))
+
+
+@pytest.mark.parametrize("B,H,T", [(4, 16, 4096), (2, 3, 1000), (1, 1, 1)])
+def test_one_launch_scan_without_optional_outputs(B, H, T):
+    """k_tilde and d_final alone (no d_all, no log rho_t), as the bench calls it."""
+    _log("scan pipe, no optional outputs, B=%d H=%d T=%d" % (B, H, T))
+    dev = _inputs(B, H, T, seed=3 + T)
+    _equal(_scan(dev, True, want=False), _scan(dev, False, want=False), (B, H, T))
+    torch.cuda.synchronize()
+
+
+def test_one_launch_scan_reused_workspace():
+    """Three inputs through one precond_scan workspace, then the first again:
+    every call equals the three-launch walk (stale flags never pass)."""
+    shape = (2, 8, 1000)
+    n = osdn.precond_scan_workspace_bytes(*shape, 128, 0)
+    ws = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
+    devs = [_inputs(*shape, seed=s) for s in (15, 16, 17)]
+    for i in (0, 1, 2, 0, 2):
+        _equal(_scan(devs[i], True, ws=ws), _scan(devs[i], False), i)
+    torch.cuda.synchronize()
 
 
 def test_one_launch_walk_repeated():
