@@ -147,6 +147,7 @@ def scan_path(w, ws_bytes):
     with the scratch otherwise, else one kernel per (b,h)."""
     if not ws_bytes:
         return "single"
+    import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     return "walk_scan_pipe" if 2 * w.B * w.H <= cus else "walk_prep+walk+walk_keys"
 
