@@ -223,11 +223,12 @@ walk_keys(const bf16 *__restrict__ k, const float *__restrict__ r,
 // publish their results (device-scope stores, and a second flag per chunk
 // once a chunk's are complete), and the preparing workgroups, once their
 // records are done, go on with walk_keys for every chunk, each instance of
-// 256 threads taking one (b, h, chunk) once its flag is set.  The walk_keys
-// items (chunk-major, heads innermost, the order in which the walks finish
-// them) continue the records' sequence of rounds from the next multiple of
-// three, so every workgroup runs about the same number of rounds; a round
-// whose items run past the last one repeats it (the same bytes written twice).
+// 256 threads taking kTailNI (b, h, chunk) items a round once their flags are
+// set.  The walk_keys items (chunk-major, heads innermost, the order in which
+// the walks finish them) continue the records' sequence of rounds from the
+// next multiple of three, so every workgroup runs about the same number of
+// rounds; a round whose items run past the last one repeats it (the same
+// bytes written twice; walk_keys overwrites nothing that a wait reads).
 // Two flags per chunk: flags[2 (bh NC + c)] the record, + 1 the walk's results.
 // ---------------------------------------------------------------------------
 // walk_keys items per instance and round in the tail: two with a bf16 kt (the
