@@ -872,19 +872,26 @@ chunk_prep(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 // sequence of rounds from the next multiple of three: round q of workgroup j
 // takes items 3 (NPW q + j) + inst of the whole sequence, so every workgroup
 // runs about the same number of rounds.  A round whose items run past the
-// last one repeats it (the same bytes written twice).  Only the plain forward
-// (no input transforms, no state gate) takes this form.
+// last one repeats it (the same bytes written twice, by instances of one
+// workgroup, whose flag waits all end before the body's first barrier).  NORM
+// and GATED as chunk_prep's (raw q and k, the state gate alpha); the
+// per-channel gate, whose chunk_prep needs more LDS, does not take this form.
 // ---------------------------------------------------------------------------
-using TailLds = PrepLds<kOsdn, false, false, false>;
-constexpr size_t kTailSmem =
-    wd::kPipeSmem > 3 * sizeof(TailLds) ? wd::kPipeSmem : 3 * sizeof(TailLds);
+template <bool NORM, bool GATED>
+using TailLds = PrepLds<kOsdn, NORM, GATED, false>;
+template <bool NORM, bool GATED>
+constexpr size_t kTailSmem = wd::kPipeSmem > 3 * sizeof(TailLds<NORM, GATED>)
+                                 ? wd::kPipeSmem
+                                 : 3 * sizeof(TailLds<NORM, GATED>);
 
+template <bool NORM, bool GATED>
 __global__ void __launch_bounds__(wd::WT)
 walk_chunk_pipe(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 const float *__restrict__ beta, const float *__restrict__ r, float eta,
                 unsigned xf, unsigned char *__restrict__ ws, const float *__restrict__ d0, int T_,
                 int NC, int NCP, int BH, float *__restrict__ wout, float *__restrict__ d_final,
-                float *__restrict__ log_ratio_sum, unsigned long long epoch) {
+                float *__restrict__ log_ratio_sum, const float *__restrict__ alpha,
+                unsigned long long epoch) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   unsigned long long *flags = (unsigned long long *)(ws + WREC);
   constexpr int fstride = (int)(REC / 8);
@@ -897,7 +904,7 @@ walk_chunk_pipe(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int q0 =
       wd::pipe_prep(smem_raw, j, NPW, BH, k, beta, r, eta, xf, ws, REC, T_, NC, flags, fstride, epoch);
   const int inst = threadIdx.x >> 8;
-  TailLds &Ld = reinterpret_cast<TailLds *>(smem_raw)[inst];
+  TailLds<NORM, GATED> &Ld = reinterpret_cast<TailLds<NORM, GATED> *>(smem_raw)[inst];
   const int first = (BH * NC + 2) / 3 * 3;  // where the chunk_prep items start in the sequence
   const int total = BH * NCP;
   bool gave_up = false;  // once a wait ran out, later items do not wait
@@ -920,8 +927,8 @@ walk_chunk_pipe(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // loop and keep them live across it)
     int tid = threadIdx.x & 255;
     asm volatile("" : "+v"(tid));
-    chunk_prep_body<kOsdn, false, false, false, true>(Ld, tid, bh, c, !ok, q, k, nullptr, beta, T_,
-                                                      NC, ws, r, wout, nullptr, xf);
+    chunk_prep_body<kOsdn, NORM, GATED, false, true>(Ld, tid, bh, c, !ok, q, k, nullptr, beta, T_,
+                                                     NC, ws, r, wout, alpha, xf);
     __syncthreads();  // the next round's staging overwrites this round's LDS
   }
 }
@@ -1560,6 +1567,19 @@ int tail_chunks(int BH, int NC, int cus) {
 #endif
 }
 
+template <bool NORM, bool GATED>
+hipError_t launch_walk_chunk_pipe(const FusedArgs &a, unsigned char *rec, float *wout, int NC,
+                                  int ncp, int BH, int cus, hipStream_t s) {
+  constexpr size_t shm = kTailSmem<NORM, GATED>;
+  hipError_t e = hipFuncSetAttribute((const void *)walk_chunk_pipe<NORM, GATED>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((walk_chunk_pipe<NORM, GATED>), dim3((unsigned)cus), dim3(wd::WT), shm, s,
+                     (const bf16 *)a.q, (const bf16 *)a.k, a.beta, a.r, a.eta, a.xf, rec, a.d0,
+                     a.T, NC, ncp, BH, wout, a.d_final, a.log_ratio_sum, a.alpha, next_epoch());
+  return hipGetLastError();
+}
+
 hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
@@ -1586,17 +1606,14 @@ hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   unsigned long long *flags = (unsigned long long *)(rec + WREC);
   const int cus = device_cus();
   const bool one_launch = NC > 0 && 2 * BH <= cus;
-  const int ncp = one_launch && !a.alpha && !(a.xf & (kNormQK | kGateLogits)) ? tail_chunks(BH, NC, cus)
-                                                                              : 0;
+  const int ncp = one_launch && !per_channel(a.alpha, a.xf) ? tail_chunks(BH, NC, cus) : 0;
   hipError_t e;
   if (ncp > 0) {
-    e = hipFuncSetAttribute((const void *)walk_chunk_pipe,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTailSmem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(walk_chunk_pipe, dim3((unsigned)cus), dim3(wd::WT), kTailSmem, s,
-                       (const bf16 *)a.q, (const bf16 *)a.k, a.beta, a.r, a.eta, a.xf, rec, a.d0,
-                       a.T, NC, ncp, BH, wout, a.d_final, a.log_ratio_sum, next_epoch());
-    e = hipGetLastError();
+    const bool norm = (a.xf & kNormQK) != 0, gated = a.alpha != nullptr;
+    e = norm ? (gated ? launch_walk_chunk_pipe<true, true>(a, rec, wout, NC, ncp, BH, cus, s)
+                      : launch_walk_chunk_pipe<true, false>(a, rec, wout, NC, ncp, BH, cus, s))
+             : (gated ? launch_walk_chunk_pipe<false, true>(a, rec, wout, NC, ncp, BH, cus, s)
+                      : launch_walk_chunk_pipe<false, false>(a, rec, wout, NC, ncp, BH, cus, s));
   } else {
     e = launch_walk(sa, rec, REC, wout, s, flags, (int)(REC / 8));
   }

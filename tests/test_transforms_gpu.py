@@ -102,6 +102,7 @@ def test_forward_raw_inputs(dtype, dk, dv, chunk, T, precond):
 @pytest.mark.parametrize("precond", [True, False])
 @pytest.mark.parametrize("dtype,dk,dv,chunk,T", [
     ("bf16", 128, 128, 64, 300),   # multi-launch pipeline with the state gate
+    ("bf16", 128, 128, 64, 2048),  # the same, 30 of 32 chunks prepared in the walk's launch
     ("f32", 32, 64, 32, 77),       # two-phase path
 ])
 def test_gated_forward_raw_inputs(dtype, dk, dv, chunk, T, precond):
