@@ -51,10 +51,11 @@ def _equal(a, b, label):
 
 
 # (B, H, T): one chunk, a single token, ragged tails, fewer chunks than the
-# walk keeps in flight, the workloads' shapes, and head counts past the
-# one-launch limit (half the compute units), which take the two-launch walk
+# walk keeps in flight, the workloads' shapes, head counts at the one-launch
+# limit (B*H = half of MI355X's 256 compute units: as many preparing workgroups
+# as walks) and past it, which take the walk in three launches
 SHAPES = [(1, 1, 64), (1, 1, 1), (1, 3, 65), (2, 2, 200), (1, 4, 257), (2, 3, 1000),
-          (4, 16, 4096), (8, 8, 2048), (2, 16, 16384), (8, 20, 300)]
+          (4, 16, 4096), (8, 8, 2048), (2, 16, 16384), (8, 16, 700), (8, 20, 300)]
 
 
 @pytest.mark.parametrize("B,H,T", SHAPES)
@@ -98,7 +99,7 @@ def test_one_launch_walk_repeated():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("B,H,T", [(4, 16, 4096), (2, 3, 1000), (1, 1, 1)])
+@pytest.mark.parametrize("B,H,T", [(4, 16, 4096), (2, 3, 1000), (1, 1, 1), (8, 16, 700)])
 def test_forward_walk_matches_precond_scan(B, H, T):
     """osdn_forward runs the one-launch walk inside its pipeline: its d_final
     equals the scan's."""
