@@ -199,23 +199,30 @@ def bench_step(args, torch, osdn, W):
     w = W.DECODE
     dev = W.generate(w).to("cuda")
     g = torch.Generator(device="cuda").manual_seed(5)
-    S = 0.1 * torch.randn(w.B, w.H, w.dv, w.dk, device="cuda", generator=g)
-    d = 0.5 + torch.rand(w.B, w.H, w.dk, device="cuda", generator=g)
+    # enough copies of the state (S and d) that the calls rotate through at least
+    # twice the 256 MB last-level cache: each call's state comes from HBM
+    state_bytes = w.B * w.H * (w.dv + 1) * w.dk * 4
+    copies = max(2, -(-2 * CACHE_BYTES // state_bytes))
+    S = [0.1 * torch.randn(w.B, w.H, w.dv, w.dk, device="cuda", generator=g)
+         for _ in range(copies)]
+    d = [0.5 + torch.rand(w.B, w.H, w.dk, device="cuda", generator=g) for _ in range(copies)]
     tok = [t[:, :, 0].contiguous() for t in (dev.q, dev.k, dev.v, dev.beta, dev.r)]
     o = torch.empty_like(tok[2])
-    t = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S, d, tok[4],
-                                          eta=w.eta, o=o), args.steps, args.warmup, torch)
+    t = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S[i % copies],
+                                          d[i % copies], tok[4], eta=w.eta, o=o),
+                      args.steps, args.warmup, torch)
     # the same step with one state gate per key dimension
     ach = W.generate(dataclasses.replace(w, gated=True, gate_channels=True)).alpha[:, :, 0]
     ach = ach.contiguous().to("cuda")
-    t_ch = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S, d, tok[4],
-                                             eta=w.eta, o=o, alpha=ach),
+    t_ch = time_launches(lambda i: osdn.step(tok[0], tok[1], tok[2], tok[3], S[i % copies],
+                                             d[i % copies], tok[4], eta=w.eta, o=o, alpha=ach),
                          args.steps, args.warmup, torch)
     heads = w.B * w.H
     # S read and written (fp32), d read and written, q, k, v read and o written
     # (bf16), beta and r read
     nbytes = heads * (2 * w.dv * w.dk * 4 + 2 * w.dk * 4 + (2 * w.dk + 2 * w.dv) * 2 + 8)
-    return {"workload": w.name, **timing_fields(t), "tokens_per_s": w.B / (t["ms"] * 1e-3),
+    return {"workload": w.name, "state_copies": copies, **timing_fields(t),
+            "tokens_per_s": w.B / (t["ms"] * 1e-3),
             "algorithmic_bytes": nbytes,
             "hbm_frac": nbytes / (t["ms"] * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "per_channel_gate": {**timing_fields(t_ch),
