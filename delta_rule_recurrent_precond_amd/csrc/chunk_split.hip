@@ -146,18 +146,42 @@ struct alignas(16) PrepLds {
   float nred_[(NORM && !GK && MODE != kOsdn) ? 8 : 1];
 };
 
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+// A store into a chunk record at byte offset off: plain, or (PUB) a
+// device-scope (sc1) store for readers in other workgroups of the same launch.
+// rec is wave-uniform.
+template <bool PUB, typename T>
+__device__ __forceinline__ void rec_put(unsigned char *rec, int off, const T &v) {
+  if constexpr (!PUB) {
+    *(T *)(rec + off) = v;
+  } else {
+    const __amdgpu_buffer_rsrc_t rr = wd::rsrc_over(rec, (int)REC);
+    if constexpr (sizeof(T) == 4)
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), rr, off, 0, wd::kSc1);
+    else if constexpr (sizeof(T) == 8)
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rr, off, 0, wd::kSc1);
+    else {
+      static_assert(sizeof(T) == 16, "records are stored 4, 8 or 16 bytes at a time");
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(wd::u32x4, v), rr, off, 0,
+                                             wd::kSc1);
+    }
+  }
+}
+
 // One chunk (bh, c) by the 256 threads tid = 0..255 of the caller (every
 // thread of the workgroup takes part in the same barriers, so several
 // instances may share a workgroup).  COH: the walk's results (wout) are read
 // with device-scope loads, the walk having written them in the same launch;
 // poison: they are not known to be complete (the chunk's keys turn NaN).
-template <int MODE, bool NORM, bool GATED, bool GK, bool COH>
+template <int MODE, bool NORM, bool GATED, bool GK, bool COH, bool PUB = false>
 __device__ __forceinline__ void chunk_prep_body(
     PrepLds<MODE, NORM, GATED, GK> &Ld, const int tid, const int bh, const int c,
     const bool poison, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ kt_in, const float *__restrict__ beta, int T_, int NC,
     unsigned char *__restrict__ ws, const float *__restrict__ r, const float *__restrict__ wout,
-    const float *__restrict__ alpha, unsigned xf) {
+    const float *__restrict__ alpha, unsigned xf, unsigned long long *__restrict__ pflag = nullptr,
+    unsigned long long epoch = 0) {
+  static_assert(!PUB || !GK, "the published records are the two-tile ones");
   constexpr bool QT = PrepLds<MODE, NORM, GATED, GK>::QT;
   f16 *const Ks = Ld.Ks;
   f16 *const Kts = Ld.Kts;
@@ -367,11 +391,11 @@ __device__ __forceinline__ void chunk_prep_body(
       const float gm = fexp2(lga[tid]), lgL = lga[C - 1];
       kf *= gm;
       qf *= gm;
-      if (tid == 0) *(float *)(rec + OFF_GL) = fexp2(lgL);
+      if (tid == 0) rec_put<PUB>(rec, (int)OFF_GL, fexp2(lgL));
     }
-    *(float *)(rec + OFF_KF + 4 * tid) = kf;
-    *(float *)(rec + OFF_QF + 4 * tid) = qf;
-    if (tid == 0) *(float2 *)(rec + OFF_E) = float2{ik, iq};  // 1 unless XN
+    rec_put<PUB>(rec, (int)OFF_KF + 4 * tid, kf);
+    rec_put<PUB>(rec, (int)OFF_QF + 4 * tid, qf);
+    if (tid == 0) rec_put<PUB>(rec, (int)OFF_E, float2{ik, iq});  // 1 unless XN
   }
 
   if (MODE == kOsdn) {
@@ -702,7 +726,7 @@ __device__ __forceinline__ void chunk_prep_body(
       pv[e] = (16 * ct + c16 <= 16 * rt_ + 4 * g + e) ? (GATED ? ds * dc[e] * acc[e] : ds * acc[e])
                                                      : 0.f;
     const f16x4 pt = h4(mma16(h4(pv), ident, zero4()));
-    *(f16x4 *)(rec + OFF_P + ((op_index(rt_, ct >> 1) * 64 + lane) * 8 + 4 * (ct & 1)) * 2) = pt;
+    rec_put<PUB>(rec, (int)OFF_P + ((op_index(rt_, ct >> 1) * 64 + lane) * 8 + 4 * (ct & 1)) * 2, pt);
   }
   __syncthreads();  // q is no longer read: its space takes the blocks of A and T
 
@@ -741,10 +765,10 @@ __device__ __forceinline__ void chunk_prep_body(
   // the two zero halves of P and T: blocks (0,1) and (2,3)
   if (wave == 0) {
     const f16x4 z = {0, 0, 0, 0};
-    *(f16x4 *)(rec + OFF_P + ((op_index(0, 0) * 64 + lane) * 8 + 4) * 2) = z;
-    *(f16x4 *)(rec + OFF_P + ((op_index(2, 1) * 64 + lane) * 8 + 4) * 2) = z;
-    *(f16x4 *)(rec + OFF_TM + ((op_index(0, 0) * 64 + lane) * 8 + 4) * 2) = z;
-    *(f16x4 *)(rec + OFF_TM + ((op_index(2, 1) * 64 + lane) * 8 + 4) * 2) = z;
+    rec_put<PUB>(rec, (int)OFF_P + ((op_index(0, 0) * 64 + lane) * 8 + 4) * 2, z);
+    rec_put<PUB>(rec, (int)OFF_P + ((op_index(2, 1) * 64 + lane) * 8 + 4) * 2, z);
+    rec_put<PUB>(rec, (int)OFF_TM + ((op_index(0, 0) * 64 + lane) * 8 + 4) * 2, z);
+    rec_put<PUB>(rec, (int)OFF_TM + ((op_index(2, 1) * 64 + lane) * 8 + 4) * 2, z);
   }
 
   // ---- write keys as S-update operands: i tiles 2w, 2w+1 (a lane holds tokens
@@ -776,9 +800,9 @@ __device__ __forceinline__ void chunk_prep_body(
     }
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
-      *(f16x8 *)(rec + OFF_KTF + (((n * 2 + qq) * 64 + lane) * 8) * 2) = cat(tr[2 * qq], tr[2 * qq + 1]);
+      rec_put<PUB>(rec, (int)OFF_KTF + (((n * 2 + qq) * 64 + lane) * 8) * 2, cat(tr[2 * qq], tr[2 * qq + 1]));
   }
-  if (tid == 0) *(float *)(rec + OFF_DS) = ds;
+  if (tid == 0) rec_put<PUB>(rec, (int)OFF_DS, ds);
   if (MODE == kDeltaNet) {
     // log rho_t with a_t = ||k_t||^2 from the stored values (16 threads per token)
     float lr = 0.f;
@@ -803,14 +827,14 @@ __device__ __forceinline__ void chunk_prep_body(
 
   __syncthreads();  // Tdg and Aoff complete
   if (MODE == kDeltaNet && tid == 0)
-    *(float *)(rec + OFF_LR) = (red[0] + red[1]) + (red[2] + red[3]);
+    rec_put<PUB>(rec, (int)OFF_LR, (red[0] + red[1]) + (red[2] + red[3]));
 
   // ---- T: the diagonal block of row block `wave` as an A-operand half, then
   // column `wave` below the diagonal: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
   {
     const int m = wave;
-    *(f16x4 *)(rec + OFF_TM + ((op_index(m, m >> 1) * 64 + lane) * 8 + 4 * (m & 1)) * 2) =
-        ld4(&Tdg[m][c16][4 * g]);
+    rec_put<PUB>(rec, (int)OFF_TM + ((op_index(m, m >> 1) * 64 + lane) * 8 + 4 * (m & 1)) * 2,
+                 ld4(&Tdg[m][c16][4 * g]));
   }
   if (wave < 3) {
     const int bj = wave;
@@ -833,8 +857,13 @@ __device__ __forceinline__ void chunk_prep_body(
       for (int e = 0; e < 4; ++e) nz[e] = -z[e];
       tcol[bi] = h4(nz);
       const f16x4 tt = h4(mma16(tcol[bi], ident, zero4()));
-      *(f16x4 *)(rec + OFF_TM + ((op_index(bi, bj >> 1) * 64 + lane) * 8 + 4 * (bj & 1)) * 2) = tt;
+      rec_put<PUB>(rec, (int)OFF_TM + ((op_index(bi, bj >> 1) * 64 + lane) * 8 + 4 * (bj & 1)) * 2, tt);
     }
+  }
+  if (PUB) {  // every wave's record stores complete, then the chunk's flag
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(pflag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1020,13 +1049,20 @@ __device__ __forceinline__ void lds_count(int *p, int lane) {
   asm volatile("" ::: "memory");
 }
 
-template <bool SCALED, bool GATED, bool GK>
-__global__ void __launch_bounds__(ST)
-chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-            const float *__restrict__ beta, const float *__restrict__ S0, int BH, int T_, int NC,
-            const unsigned char *__restrict__ ws, bf16 *__restrict__ o,
-            float *__restrict__ S_final, float *__restrict__ log_ratio_sum, unsigned xf) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+// The state pass of state workgroup b (head and 32-channel tile; see chunk_state).
+// PIPE: the chunk records are written by other workgroups of the same launch,
+// each announced by pflags[(bh NC + c) pfstride] = epoch once complete; the
+// loaders read a record only after its flag (the records' space is written
+// once in the launch, so plain loads then see the record).  A loader wave
+// whose wait runs out stages NaN keys, so that the outputs turn NaN.
+template <bool SCALED, bool GATED, bool GK, bool PIPE>
+__device__ __forceinline__ void state_body(
+    unsigned char *smem_raw, const int b, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+    const bf16 *__restrict__ v, const float *__restrict__ beta, const float *__restrict__ S0,
+    int BH, int T_, int NC, const unsigned char *__restrict__ ws, bf16 *__restrict__ o,
+    float *__restrict__ S_final, float *__restrict__ log_ratio_sum, unsigned xf,
+    const unsigned long long *__restrict__ pflags, int pfstride, unsigned long long epoch) {
+  static_assert(!PIPE || (!GK && !SCALED), "the one-launch forward has the plain records");
   StateSmem &sm = *reinterpret_cast<StateSmem *>(smem_raw);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1034,7 +1070,6 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
   // (head, 32-channel tile); the four tiles of a head share one XCD (and its L2)
   int bh, tile;
   {
-    const int b = blockIdx.x;
     if ((BH & 7) == 0) {
       bh = 8 * (b >> 5) + (b & 7);
       tile = (b >> 3) & 3;
@@ -1075,9 +1110,31 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
       float2 e;  // SCALED: 1 / e_k, 1 / e_q
     };
     Regs ra, rb, rc;
+    // PIPE: wait until the records of chunks 0 .. cc are all announced (a
+    // wave-uniform call).  `ready` counts the chunks from 0 known to be ready;
+    // a poll reads the flags of the 64 chunks from there on.  Once the bound
+    // ran out the wave stops waiting and stages NaN keys.
+    int ready = 0;
+    bool bad = false;
+    auto await = [&](int cc) {
+      if (bad) return;
+      const unsigned long long *f = pflags + (long)bh * NC * pfstride;
+      for (int i = 0; i < wd::kPollLimit; ++i) {
+        if (cc < ready) return;
+        const unsigned long long fv =
+            __hip_atomic_load(f + (long)min(ready + lane, NC - 1) * pfstride, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long set = __ballot(fv == epoch);
+        ready += ~set == 0ull ? 64 : __builtin_ctzll(~set);
+        if (cc < ready) return;
+        __builtin_amdgcn_s_sleep(8);
+      }
+      bad = true;
+    };
     // chunk cc clamped to the last one: the loads past the end reread it
     auto load = [&](Regs &R, int cc) {
       cc = min(cc, NC - 1);
+      if (PIPE) await(cc);
       const long t0 = (long)bh * T_ + (long)cc * C;
       const int L = min(C, T_ - cc * C);
       const unsigned char *rp = ws + ((long)bh * NC + cc) * RB;
@@ -1115,10 +1172,12 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
         const int p = lt + NL * u, pp = p & 1023, t = pp >> 4, jp = pp & 15;
         const int c0 = 4 * (jp >> 2) + 2 * (jp & 1), hh = 4 * ((jp >> 1) & 1);
         const bool sw = jp >= 8;
-        const f16x8 x = t < L ? (GK       ? __builtin_bit_cast(f16x8, R.kq[u])
-                                 : SCALED ? cvt8s(R.kq[u], p < 1024 ? R.e.x : R.e.y)
-                                          : cvt8(R.kq[u]))
-                              : z8;
+        const f16x8 x0 = t < L ? (GK       ? __builtin_bit_cast(f16x8, R.kq[u])
+                                  : SCALED ? cvt8s(R.kq[u], p < 1024 ? R.e.x : R.e.y)
+                                           : cvt8(R.kq[u]))
+                               : z8;
+        const f16 qnan = __builtin_bit_cast(f16, (unsigned short)0x7e00);
+        const f16x8 x = (PIPE && bad) ? f16x8{qnan, qnan, qnan, qnan, qnan, qnan, qnan, qnan} : x0;
         const f16x4 lo = f16x4{x[0], x[1], x[2], x[3]}, hi = f16x4{x[4], x[5], x[6], x[7]};
         f16 *base = (p < 1024 ? sm.K : sm.Q)[buf];
         *(f16x4 *)&base[kq_chunk(t, c0 + sw) + hh] = sw ? hi : lo;
@@ -1463,6 +1522,101 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
   }
 }
 
+template <bool SCALED, bool GATED, bool GK>
+__global__ void __launch_bounds__(ST)
+chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+            const float *__restrict__ beta, const float *__restrict__ S0, int BH, int T_, int NC,
+            const unsigned char *__restrict__ ws, bf16 *__restrict__ o,
+            float *__restrict__ S_final, float *__restrict__ log_ratio_sum, unsigned xf) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  state_body<SCALED, GATED, GK, false>(smem_raw, blockIdx.x, q, k, v, beta, S0, BH, T_, NC, ws, o,
+                                       S_final, log_ratio_sum, xf, nullptr, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// walk_state_pipe: the plain forward in one launch, for few heads (B*H at most
+// an eighth of the compute units), where the walks, sequential over long
+// sequences, would otherwise leave most of the device idle and the state pass
+// after them would occupy only half of it.  The grid is the resident one
+// (NRES workgroups, one per CU) followed by the 4 B*H state workgroups:
+//   - workgroups 0 .. BH-1 walk (as in walk_pipe) and publish their results;
+//   - the next NRES - BH prepare the walk's records (pipe_prep), which never
+//     waits; then the first NRES - 5 BH of them run chunk_prep for every chunk
+//     (chunk-major, three chunks a round, each once the walk has passed it),
+//     publishing each record with device-scope stores and a flag, while the
+//     other 4 B*H end, freeing their compute units;
+//   - the state workgroups, dispatched after the resident ones onto the
+//     compute units so freed, run the state pass (state_body), each chunk
+//     once its record's flag is set.
+// No workgroup waits for one dispatched after it, and every wait is bounded.
+// Workspace: the chunk records (stride REC, as the split forward), wout, the
+// walk's records (stride WREC), then three flags per chunk (the walk record
+// ready, the walk past the chunk, the chunk record ready); each region is
+// written once in a launch, so plain loads of a record after its flag see it.
+// ---------------------------------------------------------------------------
+constexpr size_t kStatePipeSmem =
+    kTailSmem<false, false> > sizeof(StateSmem) ? kTailSmem<false, false> : sizeof(StateSmem);
+
+__global__ void __launch_bounds__(wd::WT)
+walk_state_pipe(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+                const bf16 *__restrict__ v, const float *__restrict__ beta,
+                const float *__restrict__ r, float eta, unsigned xf,
+                unsigned char *__restrict__ ws, unsigned char *__restrict__ wrec,
+                const float *__restrict__ d0, const float *__restrict__ S0, int T_, int NC,
+                int BH, float *__restrict__ wout, float *__restrict__ d_final,
+                float *__restrict__ log_ratio_sum, bf16 *__restrict__ o,
+                float *__restrict__ S_final, unsigned long long *__restrict__ flags,
+                unsigned long long epoch) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  constexpr int fstride = 3;
+  const int NRES = (int)gridDim.x - 4 * BH, b = blockIdx.x;
+  if (b < BH) {
+    wd::walk_body<true, true>(smem_raw, b, k, wrec, WREC, d0, T_, NC, wout, d_final, nullptr,
+                              log_ratio_sum, flags, fstride, epoch);
+    return;
+  }
+  if (b >= NRES) {
+    static_assert(ST == wd::WT, "the state pass runs in the walk's workgroup size");
+    state_body<false, false, false, true>(smem_raw, b - NRES, q, k, v, beta, S0, BH, T_, NC, ws,
+                                          o, S_final, nullptr, xf, flags + 2, fstride, epoch);
+    return;
+  }
+  const int j = b - BH, NPW = NRES - BH;
+  wd::pipe_prep(smem_raw, j, NPW, BH, k, beta, r, eta, xf, wrec, WREC, T_, NC, flags, fstride,
+                epoch);
+  const int PT = NPW - 4 * BH;  // the workgroups that go on with chunk_prep
+  if (j >= PT) return;
+  const int inst = threadIdx.x >> 8;
+  TailLds<false, false> &Ld = reinterpret_cast<TailLds<false, false> *>(smem_raw)[inst];
+  const int total = BH * NC;
+  bool gave_up = false;  // once a wait ran out, later items do not wait
+  // round m of workgroup j: items 3 m + inst, m = j, j + PT, ...
+  for (int m = j; 3 * m < total; m += PT) {
+    const int ii = min(3 * m + inst, total - 1);
+    const int c = ii / BH, bh = ii % BH;
+    // the walk past chunk c (a bounded wait)
+    bool ok = false;
+    const unsigned long long *f = &flags[((long)bh * NC + c) * fstride + 1];
+    for (int i = 0; !gave_up && i < wd::kPollLimit; ++i) {
+      if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) {
+        ok = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    gave_up = !ok;
+    // (the thread index through an opaque copy each round, so that the
+    // compiler does not hoist the body's lane-dependent addresses out of the
+    // loop and keep them live across it)
+    int tid = threadIdx.x & 255;
+    asm volatile("" : "+v"(tid));
+    chunk_prep_body<kOsdn, false, false, false, true, true>(
+        Ld, tid, bh, c, !ok, q, k, nullptr, beta, T_, NC, ws, r, wout, nullptr, xf,
+        &flags[((long)bh * NC + c) * fstride + 2], epoch);
+    __syncthreads();  // the next round's staging overwrites this round's LDS
+  }
+}
+
 }  // namespace
 
 size_t split_workspace_bytes(int B, int H, int T, bool gate_channels) {
@@ -1539,10 +1693,19 @@ hipError_t launch_prep(int BH, int NC, hipStream_t s, const void *q, const void 
 
 }  // namespace
 
+// Heads up to which the forward may run in one launch (walk_state_pipe): an
+// eighth of MI355X's 256 compute units.  The launch itself also checks the
+// device's count.
+constexpr int kStatePipeHeads = 32;
+
 size_t split_forward_workspace_bytes(int B, int H, int T, bool gate_channels) {
-  // the walk's records live in the space the chunk records take later
-  const size_t nc = (size_t)((T + C - 1) / C);
-  return (size_t)B * H * nc * ((gate_channels ? RECK : REC) + WOUT * sizeof(float));
+  // the walk's records live in the space the chunk records take later; with
+  // few heads they get their own space after wout, then three flags per chunk
+  // (walk_state_pipe)
+  const size_t nc = (size_t)((T + C - 1) / C), BH = (size_t)B * H;
+  size_t n = BH * nc * ((gate_channels ? RECK : REC) + WOUT * sizeof(float));
+  if (!gate_channels && BH <= (size_t)kStatePipeHeads) n += BH * nc * (WREC + 3 * sizeof(unsigned long long));
+  return n;
 }
 
 // walk_prep, the walk's sequential pass, chunk_prep forming the write keys
@@ -1605,6 +1768,20 @@ hipError_t launch_split_forward(const FusedArgs &a, void *ws, hipStream_t s) {
   static_assert(WREC % 8 == 0 && REC - WREC >= 16, "the flags fit past a walk record");
   unsigned long long *flags = (unsigned long long *)(rec + WREC);
   const int cus = device_cus();
+  if (NC > 0 && !a.alpha && !(a.xf & kNormQK) && BH <= kStatePipeHeads && 8 * BH <= cus) {
+    // the whole forward in one launch (the workspace has the space for it)
+    unsigned char *wr = (unsigned char *)(wout + (size_t)BH * NC * WOUT);
+    unsigned long long *fl = (unsigned long long *)(wr + (size_t)BH * NC * WREC);
+    hipError_t e = hipFuncSetAttribute((const void *)walk_state_pipe,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kStatePipeSmem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(walk_state_pipe, dim3((unsigned)(cus + 4 * BH)), dim3(wd::WT),
+                       kStatePipeSmem, s, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+                       a.beta, a.r, a.eta, a.xf, rec, wr, a.d0, a.S0, a.T, NC, BH, wout,
+                       a.d_final, a.log_ratio_sum, (bf16 *)a.o, a.S_final, fl, next_epoch());
+    return hipGetLastError();
+  }
   const bool one_launch = NC > 0 && 2 * BH <= cus;
   const int ncp = one_launch && !per_channel(a.alpha, a.xf) ? tail_chunks(BH, NC, cus) : 0;
   hipError_t e;

@@ -140,11 +140,14 @@ def test_chunk_workspace_bytes(lib):
 
 def test_split_workspace_bytes(lib):
     # matrix-core shapes: chunk records (32 KB; the walk records of 17.25 KB use the same
-    # space first) and walk results (768 B)
-    # per (b, h, chunk of 64); the walk alone: its records (17 KB) plus results
-    # plus an 8-byte ready flag
-    assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 0) == 2 * 3 * 3 * (32768 + 768)
-    assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 1) == 2 * 3 * 3 * (32768 + 768)
+    # space first) and walk results (768 B) per (b, h, chunk of 64); with at most 32
+    # heads the walk records get their own space and three 8-byte flags per chunk
+    # follow (the one-launch forward); the walk alone: its records (17 KB) plus
+    # results plus two 8-byte flags
+    few = 17664 + 24
+    assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 0) == 2 * 3 * 3 * (32768 + 768 + few)
+    assert lib.osdn_forward_workspace_bytes(2, 3, 130, 128, 128, 64, 0, 1) == 2 * 3 * 3 * (32768 + 768 + few)
+    assert lib.osdn_forward_workspace_bytes(4, 9, 130, 128, 128, 64, 0, 0) == 4 * 9 * 3 * (32768 + 768)
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 0) == 2 * 3 * 3 * (17664 + 768 + 16)
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 64, 0) == 0
     assert lib.osdn_precond_scan_workspace_bytes(2, 3, 130, 128, 1) == 0
