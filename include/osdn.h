@@ -200,7 +200,11 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  *                  that is a pipeline of launches (walk, chunk-parallel pass,
  *                  sequential state pass; the walk and the preparation of its
  *                  chunks share one launch when B*H is at most half the
- *                  device's compute units), and less scratch (or
+ *                  device's compute units).  With at most 32 heads (B*H) and
+ *                  neither a state gate nor OSDN_NORM_QK, on a device with at
+ *                  least 8 B*H compute units, the whole forward runs as one
+ *                  launch; the scratch then holds the walk's records apart
+ *                  (17.3 KiB more per chunk, and 256 bytes).  Less scratch (or
  *                  NULL) selects the single fused kernel.  Other shapes need the
  *                  scratch: the walk hands kt to the chunk pass through it, in
  *                  fp32 whatever the data type (a bf16 kt would cost up to 2^-9
