@@ -1548,7 +1548,10 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 //   - the state workgroups, dispatched after the resident ones onto the
 //     compute units so freed, run the state pass (state_body), each chunk
 //     once its record's flag is set.
-// No workgroup waits for one dispatched after it, and every wait is bounded.
+// The walks wait only for the preparing workgroups, which never wait while
+// they prepare the records; every other wait is for a workgroup dispatched
+// earlier, and every wait is bounded.  So the launch completes whatever number
+// of its workgroups the device holds at once.
 // Workspace: the chunk records (stride REC, as the split forward), wout, the
 // walk's records (stride WREC), then three flags per chunk (the walk record
 // ready, the walk past the chunk, the chunk record ready); each region is
