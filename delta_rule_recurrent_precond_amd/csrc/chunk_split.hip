@@ -1550,8 +1550,8 @@ chunk_state(const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *
 //     once its record's flag is set.
 // The walks wait only for the preparing workgroups, which never wait while
 // they prepare the records; every other wait is for a workgroup dispatched
-// earlier, and every wait is bounded.  So the launch completes whatever number
-// of its workgroups the device holds at once.
+// earlier, and every wait is bounded.  So the launch needs only more of its
+// workgroups resident at once than there are walks.
 // Workspace: the chunk records (stride REC, as the split forward), wout, the
 // walk's records (stride WREC), then three flags per chunk (the walk record
 // ready, the walk past the chunk, the chunk record ready); each region is
