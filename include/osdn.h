@@ -204,7 +204,7 @@ size_t osdn_chunk_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int c
  *                  neither a state gate nor OSDN_NORM_QK, on a device with at
  *                  least 8 B*H compute units, the whole forward runs as one
  *                  launch; the scratch then holds the walk's records apart
- *                  (17.3 KiB more per chunk, and 256 bytes).  Less scratch (or
+ *                  (17.3 KiB more per chunk).  Less scratch (or
  *                  NULL) selects the single fused kernel.  Other shapes need the
  *                  scratch: the walk hands kt to the chunk pass through it, in
  *                  fp32 whatever the data type (a bf16 kt would cost up to 2^-9
